@@ -1,0 +1,323 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+Each test fixes the oracle against something other than itself: a library
+routine, a closed form on tiny hand inputs, an invariant of the recurrence, or
+an independently written formulation (tests/kda_independent.py).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from gated_delta_rule_act_amd import workloads as W
+from tests import kda_independent as ind
+
+
+def bf(x):
+    return W.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def exact_bf(x):
+    b = bf(x)
+    assert np.array_equal(W.bf16_bits_to_f32(b).astype(np.float64), np.asarray(x, np.float64)), \
+        "hand value not exactly representable in bf16"
+    return b
+
+
+def run(d, **kw):
+    flags = (oracle.FLAG_QK_L2NORM if d.get("l2norm", True) else 0) | \
+            (oracle.FLAG_BETA_IS_PROB if d.get("beta_is_prob") else 0)
+    return oracle.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d.get("A_log"), d.get("dt_bias"),
+                      scale=d["scale"], lower_bound=d["lower_bound"], gate_mode=d["gate_mode"],
+                      flags=flags, initial_state=d.get("h0"), cu_seqlens=d.get("cu_seqlens"), **kw)
+
+
+def as_dict(inp: W.KdaInputs):
+    return dict(q=inp.q, k=inp.k, v=inp.v, g=inp.g, beta=inp.beta, A_log=inp.A_log,
+                dt_bias=inp.dt_bias, gate_mode=inp.gate_mode, lower_bound=inp.lower_bound,
+                scale=inp.scale, cu_seqlens=inp.cu_seqlens, h0=inp.initial_state_f64())
+
+
+def small(K=8, V=8, **kw):
+    base = dict(B=2, T=150, Hqk=2, K=K, V=V, seed=11)
+    base.update(kw)
+    return W.make_inputs(**base)
+
+
+# ---------------------------------------------------------------- gate, beta, norm
+def test_softplus_gate_matches_torch():
+    x = np.linspace(-60, 60, 2001)
+    for A in (-4.0, 0.0, 1.3, 6.0):
+        got = oracle.gate(oracle.GATE_SOFTPLUS, x, A_log=A)
+        ref = (-math.exp(A) * F.softplus(torch.tensor(x, dtype=torch.float64), beta=1.0,
+                                         threshold=1e9)).numpy()
+        np.testing.assert_allclose(got, ref, rtol=1e-14, atol=0)
+        assert np.all(got < 0)
+
+
+def test_safe_gate_matches_torch_and_saturates():
+    x = np.linspace(-30, 30, 1201)
+    for lb in (-5.0, -1.0, -1e-30):
+        for A in (-4.0, 0.0, 2.0):
+            got = oracle.gate(oracle.GATE_SAFE_SIGMOID, x, A_log=A, lower_bound=lb)
+            ref = lb * torch.sigmoid(math.exp(A) * torch.tensor(x, dtype=torch.float64)).numpy()
+            np.testing.assert_allclose(got, ref, rtol=1e-14, atol=0)
+            assert np.all(got <= 0) and np.all(got >= lb)
+    # saturated sigmoid: A_log = 20 gives exactly lb above zero, exactly 0 below, lb/2 at 0
+    got = oracle.gate(oracle.GATE_SAFE_SIGMOID, np.array([-0.5, 0.0, 0.5]), A_log=20.0, lower_bound=-5.0)
+    assert got[0] == 0.0 and got[1] == -2.5 and got[2] == -5.0
+
+
+def test_pregated_gate_is_identity():
+    x = np.array([-3.0, -0.25, 0.0])
+    assert np.array_equal(oracle.gate(oracle.GATE_PREGATED, x), x)
+
+
+def test_l2norm_closed_form():
+    y = oracle.l2norm([3.0, 4.0, 0.0, 0.0])
+    np.testing.assert_allclose(y, [0.6, 0.8, 0.0, 0.0], rtol=1e-7)
+    np.testing.assert_allclose(y, np.array([3, 4, 0, 0]) / math.sqrt(25 + 1e-6), rtol=1e-15)
+    assert np.array_equal(oracle.l2norm([0.0, 0.0]), [0.0, 0.0])
+
+
+# ---------------------------------------------------------------- closed forms
+def _tiny(q, k, v, g, beta_logit, *, h0=None, A_log=0.0, dt=None, mode=0, lb=-1.0, scale=0.75,
+          l2norm=True, beta_is_prob=False):
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
+    T, K = q.shape
+    V = v.shape[1]
+    d = dict(q=exact_bf(q).reshape(1, T, 1, K), k=exact_bf(k).reshape(1, T, 1, K),
+             v=exact_bf(v).reshape(1, T, 1, V), g=exact_bf(g).reshape(1, T, 1, K),
+             beta=exact_bf(beta_logit).reshape(1, T, 1), A_log=np.array([A_log], np.float32),
+             dt_bias=None if dt is None else np.asarray(dt, np.float32).reshape(1, K),
+             gate_mode=mode, lower_bound=lb, scale=scale, l2norm=l2norm, beta_is_prob=beta_is_prob,
+             h0=None if h0 is None else np.asarray(h0, np.float64).reshape(1, 1, V, K))
+    return d
+
+
+def test_hand_worked_example_exact():
+    # K = V = 2, no normalisation, beta given as 0.5, pre-gated zero decay:
+    # S0 = [[1,2],[3,4]], k = (1,0), q = (0,1), v = (5,6)
+    # read r = S0 k = (1,3); write S = S0 + 0.5 (v - r) k^T = [[3,2],[4.5,4]]
+    # output o = S q = (2,4)
+    d = _tiny([[0, 1]], [[1, 0]], [[5, 6]], [[0, 0]], [0.5], h0=[[1, 2], [3, 4]], mode=2,
+              scale=1.0, l2norm=False, beta_is_prob=True)
+    o, s = run(d)
+    assert np.array_equal(o.reshape(2), [2.0, 4.0])
+    assert np.array_equal(s.reshape(2, 2), [[3.0, 2.0], [4.5, 4.0]])
+
+
+def test_single_token_zero_state_closed_form():
+    # K=2, V=3 so that a transposed state cannot pass.
+    q, k, v = [[3.0, 4.0]], [[0.0, 2.0]], [[1.0, -2.0, 0.5]]
+    d = _tiny(q, k, v, [[0.5, -1.0]], [0.0], A_log=1.0, dt=[0.1, -0.2])
+    o, s = run(d)
+    qh = np.array([3.0, 4.0]) / math.sqrt(25 + 1e-6)
+    kh = np.array([0.0, 2.0]) / math.sqrt(4 + 1e-6)
+    vv = np.array([1.0, -2.0, 0.5])
+    beta = 0.5
+    np.testing.assert_allclose(s.reshape(3, 2), beta * np.outer(vv, kh), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(o.reshape(3), 0.75 * beta * (kh @ qh) * vv, rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_single_token_with_state_closed_form(mode):
+    q, k, v = [[1.0, -2.0]], [[0.5, 1.5]], [[2.0, 0.25, -1.0]]
+    g, dt, A, lb = [[0.75, -1.25]], [0.5, -0.125], 0.3, -2.0
+    S0 = np.array([[0.5, -1.0], [2.0, 0.25], [-0.75, 1.0]])
+    d = _tiny(q, k, v, g, [1.0], h0=S0, A_log=A, dt=dt, mode=mode, lb=lb)
+    o, s = run(d)
+    A = float(np.float32(A))                            # A_log is passed as fp32
+    x = np.array(g[0]) + np.array(dt)
+    a = (-math.exp(A) * np.log1p(np.exp(x))) if mode == 0 else lb / (1 + np.exp(-math.exp(A) * x))
+    qh = np.array(q[0]) / math.sqrt(5 + 1e-6)
+    kh = np.array(k[0]) / math.sqrt(2.5 + 1e-6)
+    beta = 1 / (1 + math.exp(-1.0))
+    Sp = S0 * np.exp(a)[None, :]                        # decay first
+    wr = beta * (np.array(v[0]) - Sp @ kh)              # then read and write
+    np.testing.assert_allclose(s.reshape(3, 2), Sp + np.outer(wr, kh), rtol=1e-13)
+    np.testing.assert_allclose(o.reshape(3), 0.75 * (Sp @ qh + wr * (kh @ qh)), rtol=1e-13)
+
+
+def test_two_tokens_matrix_form():
+    rng = np.random.default_rng(5)
+    vals = lambda *s: W.bf16_bits_to_f32(bf(rng.standard_normal(s))).astype(np.float64)
+    d = _tiny(vals(2, 3), vals(2, 3), vals(2, 4), vals(2, 3), vals(2), h0=rng.standard_normal((4, 3)),
+              A_log=0.4, dt=[0.1, 0.0, -0.3], mode=0)
+    o, s = run(d)
+    o2, s2 = ind.matrix_form_fwd(d)
+    np.testing.assert_allclose(o, o2, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(s, s2, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- invariants
+def test_beta_zero_is_pure_decay():
+    # pre-gated log decay (a = g exactly), beta = 0: no write at all
+    inp = small(K=6, V=5, T=90, B=1, Hqk=1, init_state_dtype=W.STATE_F32, h0_std=1.0)
+    d = as_dict(inp)
+    d.update(gate_mode=2, beta_is_prob=True, beta=np.zeros_like(inp.beta), dt_bias=None,
+             g=bf(-np.abs(W.bf16_bits_to_f32(inp.g)) * 0.1))
+    o, s = run(d)
+    a = W.bf16_bits_to_f32(d["g"][0, :, 0]).astype(np.float64)
+    Gam = np.cumsum(a, axis=0)
+    S0 = d["h0"][0, 0]
+    qh = ind.normalise_rows(W.bf16_bits_to_f32(inp.q[0, :, 0]).astype(np.float64))
+    np.testing.assert_allclose(s[0, 0], S0 * np.exp(Gam[-1])[None, :], rtol=1e-12)
+    ref_o = np.stack([inp.scale * (S0 * np.exp(Gam[t])[None, :]) @ qh[t] for t in range(90)])
+    np.testing.assert_allclose(o[0, :, 0], ref_o, rtol=1e-11, atol=1e-15)
+
+
+def _ungated_delta_rule(d):
+    q = ind.normalise_rows(W.bf16_bits_to_f32(d["q"][0, :, 0]).astype(np.float64))
+    k = ind.normalise_rows(W.bf16_bits_to_f32(d["k"][0, :, 0]).astype(np.float64))
+    v = W.bf16_bits_to_f32(d["v"][0, :, 0]).astype(np.float64)
+    beta = 1 / (1 + np.exp(-W.bf16_bits_to_f32(d["beta"][0, :, 0]).astype(np.float64)))
+    S = d["h0"][0, 0].copy()
+    outs = []
+    for t in range(q.shape[0]):
+        S = S @ (np.eye(S.shape[1]) - beta[t] * np.outer(k[t], k[t])) + beta[t] * np.outer(v[t], k[t])
+        outs.append(d["scale"] * S @ q[t])
+    return np.stack(outs), S
+
+
+def test_zero_activation_is_ungated_delta_rule():
+    inp = small(K=8, V=6, T=120, B=1, Hqk=1, init_state_dtype=W.STATE_F32, h0_std=0.5)
+    d = as_dict(inp)
+    ref_o, ref_s = _ungated_delta_rule(d)
+    # exact: pre-gated mode with zero log decay
+    d0 = dict(d, gate_mode=2, g=np.zeros_like(inp.g), dt_bias=None)
+    o, s = run(d0)
+    np.testing.assert_allclose(o[0, :, 0], ref_o, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(s[0, 0], ref_s, rtol=1e-12, atol=1e-15)
+    # g -> 0 through the softplus gate: A_log = -40 makes the activation ~1e-17
+    d1 = dict(d, gate_mode=0, A_log=np.full(1, -40.0, np.float32))
+    o, s = run(d1)
+    np.testing.assert_allclose(o[0, :, 0], ref_o, rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(s[0, 0], ref_s, rtol=1e-10, atol=1e-14)
+
+
+def test_complete_forgetting():
+    inp = small(K=8, V=4, T=40, B=1, Hqk=1, init_state_dtype=W.STATE_F32)
+    d = as_dict(inp)
+    d.update(gate_mode=0, A_log=np.full(1, 20.0, np.float32))
+    o, s = run(d)
+    q = ind.normalise_rows(W.bf16_bits_to_f32(inp.q[0, :, 0]).astype(np.float64))
+    k = ind.normalise_rows(W.bf16_bits_to_f32(inp.k[0, :, 0]).astype(np.float64))
+    v = W.bf16_bits_to_f32(inp.v[0, :, 0]).astype(np.float64)
+    beta = 1 / (1 + np.exp(-W.bf16_bits_to_f32(inp.beta[0, :, 0]).astype(np.float64)))
+    np.testing.assert_allclose(s[0, 0], beta[-1] * np.outer(v[-1], k[-1]), rtol=1e-13)
+    ref_o = inp.scale * (beta * np.einsum("tc,tc->t", k, q))[:, None] * v
+    np.testing.assert_allclose(o[0, :, 0], ref_o, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("mode,lb", [(0, -1.0), (1, -5.0)])
+def test_split_sequence_equals_one_call(mode, lb):
+    inp = small(K=8, V=8, T=200, B=1, Hqk=2, gate_mode=mode, lower_bound=lb,
+                init_state_dtype=W.STATE_F32)
+    d = as_dict(inp)
+    o, s = run(d)
+    cut = 77
+    d1 = dict(d, q=inp.q[:, :cut], k=inp.k[:, :cut], v=inp.v[:, :cut], g=inp.g[:, :cut], beta=inp.beta[:, :cut])
+    o1, s1 = run(d1)
+    d2 = dict(d, q=inp.q[:, cut:], k=inp.k[:, cut:], v=inp.v[:, cut:], g=inp.g[:, cut:],
+              beta=inp.beta[:, cut:], h0=s1)
+    o2, s2 = run(d2)
+    assert np.array_equal(np.concatenate([o1, o2], axis=1), o)
+    assert np.array_equal(s2, s)
+
+
+def test_packed_equals_separate_calls():
+    lengths = [1, 0, 63, 64, 65, 130]
+    inp = W.make_inputs(B=1, T=None, Hqk=2, Hv=4, K=8, V=8, seed=3, lengths=lengths,
+                        init_state_dtype=W.STATE_F32)
+    d = as_dict(inp)
+    o, s = run(d)
+    cu = inp.cu_seqlens
+    for n in range(len(lengths)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        dn = dict(d, q=inp.q[:, a:b], k=inp.k[:, a:b], v=inp.v[:, a:b], g=inp.g[:, a:b],
+                  beta=inp.beta[:, a:b], cu_seqlens=None, h0=d["h0"][n:n + 1])
+        on, sn = run(dn)
+        assert np.array_equal(on, o[:, a:b])
+        assert np.array_equal(sn[0], s[n])
+    # an empty sequence hands its initial state straight through
+    assert np.array_equal(s[1], d["h0"][1])
+
+
+def test_gva_equals_mha_with_repeated_qk():
+    inp = small(K=8, V=8, T=70, B=2, Hqk=2, Hv=6)
+    d = as_dict(inp)
+    o, s = run(d)
+    dm = dict(d, q=np.repeat(inp.q, 3, axis=2), k=np.repeat(inp.k, 3, axis=2))
+    om, sm = run(dm)
+    assert np.array_equal(o, om) and np.array_equal(s, sm)
+
+
+def test_thread_count_does_not_change_results():
+    d = as_dict(small(T=100))
+    o1, s1 = run(d, nthreads=1)
+    o4, s4 = run(d, nthreads=4)
+    assert np.array_equal(o1, o4) and np.array_equal(s1, s4)
+
+
+# ---------------------------------------------------------------- extremes
+def test_extreme_gates_finite():
+    for mode, lb, A_rng, gstd in [(1, -5.0, (20.0, 20.0), 3.0), (1, -5.0, (-4.0, 6.0), 3.0),
+                                  (0, -1.0, (-40.0, -40.0), 1.0), (0, -1.0, (6.0, 6.0), 3.0),
+                                  (0, -1.0, (20.0, 20.0), 1.0)]:
+        inp = small(K=16, V=16, T=130, gate_mode=mode, lower_bound=lb, A_log_range=A_rng, g_std=gstd,
+                    init_state_dtype=W.STATE_F32)
+        o, s = run(as_dict(inp))
+        assert np.isfinite(o).all() and np.isfinite(s).all()
+
+
+def test_saturated_lower_bound_gives_exact_decay():
+    # lb = -5 with a saturated sigmoid: every channel decays by exactly e^-5 per token
+    inp = small(K=4, V=3, T=10, B=1, Hqk=1, gate_mode=1, lower_bound=-5.0, init_state_dtype=W.STATE_F32)
+    d = as_dict(inp)
+    d.update(A_log=np.full(1, 20.0, np.float32), dt_bias=None, g=bf(np.full(inp.g.shape, 2.0)),
+             beta_is_prob=True, beta=np.zeros_like(inp.beta))
+    o, s = run(d)
+    np.testing.assert_allclose(s[0, 0], d["h0"][0, 0] * math.exp(-50.0), rtol=1e-13)
+
+
+def test_long_cumulative_decay_underflows_cleanly():
+    # T = 131072 at lb = -1 accumulates about -6.5e4 of log decay: the state must
+    # reach exactly zero without NaN when nothing is written.
+    inp = W.make_inputs(B=1, T=131072, Hqk=1, K=4, V=4, seed=9, gate_mode=1, lower_bound=-1.0,
+                        init_state_dtype=W.STATE_F32, h0_std=1.0)
+    d = as_dict(inp)
+    d.update(beta_is_prob=True, beta=np.zeros_like(inp.beta))
+    o, s = run(d)
+    assert np.isfinite(o).all()
+    assert np.array_equal(s, np.zeros_like(s))
+    assert np.abs(o[0, -1000:]).max() == 0.0
+
+
+# ---------------------------------------------------------------- second formulation
+@pytest.mark.parametrize("mode,lb,gstd,Arng", [(0, -1.0, 1.0, (0.0, math.log(16))),
+                                               (1, -5.0, 3.0, (-4.0, 6.0)),
+                                               (1, -1.0, 1.0, (0.0, math.log(16))),
+                                               (0, -1.0, 1.0, (-8.0, -6.0))])
+def test_chunked_formulation_agrees(mode, lb, gstd, Arng):
+    inp = W.make_inputs(B=2, T=200, Hqk=1, Hv=2, K=16, V=12, seed=21, gate_mode=mode, lower_bound=lb,
+                        g_std=gstd, A_log_range=Arng, init_state_dtype=W.STATE_F32)
+    d = as_dict(inp)
+    o, s = run(d)
+    oc, sc = ind.chunked_fwd(d)
+    np.testing.assert_allclose(o, oc, rtol=1e-9, atol=1e-13)
+    assert np.linalg.norm(s - sc) / np.linalg.norm(s) < 1e-12
+    assert np.linalg.norm(o - oc) / np.linalg.norm(o) < 1e-12
+
+
+def test_chunked_formulation_packed_full_width():
+    inp = W.make_inputs(B=1, T=None, Hqk=1, Hv=1, K=128, V=128, seed=4, lengths=[70, 129],
+                        gate_mode=0, init_state_dtype=W.STATE_BF16)
+    d = as_dict(inp)
+    o, s = run(d)
+    oc, sc = ind.chunked_fwd(d)
+    assert np.linalg.norm(s - sc) / np.linalg.norm(s) < 1e-12
+    assert np.linalg.norm(o - oc) / np.linalg.norm(o) < 1e-12
