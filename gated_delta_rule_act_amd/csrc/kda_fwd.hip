@@ -1,0 +1,954 @@
+// Chunked Kimi Delta Attention forward for MI355X (gfx950, CDNA4).
+//
+// What is computed (contract in include/kda.h): per sequence and v-head, the
+// per-key-channel gated delta rule with state S in R^{V x K}
+//     S <- S Diag(e^{a_t});  S <- S + b_t (v_t - S k_t) k_t^T;  o_t = scale S q_t
+// with the in-kernel gate activations of the fla-kda SKILL.md ("Gate
+// contracts") and the tensor layout of the FlashKDA page ("Tensor shapes and
+// dtypes").  It is evaluated in the chunked WY form: 64-token chunks made of
+// 16-token sub-chunks, as the fla-kda SKILL.md "Numerical invariants" and
+// "Code map" sections describe the intra / inter split.
+//
+// Two launches (plus a tiny chunk-map launch for packed sequences):
+//   kda_intra_kernel  one workgroup per (chunk, v-head), fully parallel.
+//       gate activation + chunk-local cumulative log2-decay Gamma;
+//       Akk = diag(b) (K Kt . 2^(Gi-Gj)) strictly lower and
+//       Aqk = (Q Kt . 2^(Gi-Gj)) lower incl. diagonal, on 16x16 sub-chunk
+//       blocks: off-diagonal blocks factor through the last row before the
+//       row block (both exponents <= 0), diagonal blocks either through the
+//       sub-chunk midpoint (safe gate: exponent span bounded by 8*|lb|) or
+//       pairwise on the VALU (softplus gate: unbounded per-token decay);
+//       T = (I + Akk)^-1 by 16x16 forward substitution plus fp32-MFMA block
+//       merges; WY factors W = T diag(b) (K . 2^G) and T diag(b) for u.
+//   kda_state_kernel  one workgroup per (sequence, v-head, 32-wide V slice),
+//       sequential over that sequence's chunks with the fp32 state slice in
+//       registers:  U = T diag(b) V - W S^T,  O = (Q . 2^G) S^T + Aqk U,
+//       S <- S Diag(2^G_last) + U^T (K . 2^(G_last - G)).
+//
+// Precision: 16-bit MFMA operands with fp32 accumulation; the contraction that
+// writes the state (U^T Kd) uses a 3-product fp16 hi/lo split, the diagonal
+// midpoint blocks (exponents up to 2^58) use bf16 with a hi/lo split on Akk,
+// and T is computed in fp32.  The exp2 operands are always differences of
+// Gamma values, never ratios of exponentials.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kda.h"
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 64;      // chunk length
+constexpr int DK = 128;     // key dim
+constexpr int DV = 128;     // value dim
+constexpr int VS = 32;      // V slice per state workgroup
+constexpr int NSLICE = DV / VS;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kL2Eps = 1e-6f;
+// Per-token log2 decay floor.  Any decay below 2^-1e4 is already exactly zero
+// in fp32; the floor only keeps Gamma finite so differences never form inf-inf.
+constexpr float kMinLog2Decay = -1.0e4f;
+
+// Per (v-head, chunk) workspace block, written by the intra kernel and read by
+// the state kernel.  All matrices are row-major in the orientation the state
+// kernel feeds to the MFMA, so its operand loads are 16-byte vectors.
+constexpr size_t OFF_WN = 0;        // -W          fp16 [64 t][128 k]
+constexpr size_t OFF_QG = 16384;    // Q . 2^G     fp16 [64 t][128 k]   (raw q)
+constexpr size_t OFF_KDH = 32768;   // (K . 2^(GL-G))^T hi fp16 [128 k][64 t]  (raw k)
+constexpr size_t OFF_KDL = 49152;   // ... lo
+constexpr size_t OFF_TBH = 65536;   // T diag(b)   bf16 [64 t][64 s] hi
+constexpr size_t OFF_TBL = 73728;   // ... lo
+constexpr size_t OFF_AQK = 81920;   // scale rq_t (Q Kt . 2^(Gt-Gs)) fp16 [64][64], lower incl diag
+constexpr size_t OFF_GN = 90112;    // 2^G_last    fp32 [128]
+constexpr size_t OFF_QS = 90624;    // scale rq_t  fp32 [64]
+constexpr size_t OFF_RK = 90880;    // rk_t        fp32 [64]
+constexpr size_t BLOCK = 91136;
+static_assert(BLOCK % 256 == 0, "workspace block alignment");
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ float wave_xor_sum16(float v) {
+  // sum across the 16 lanes that share (lane >> 4)
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+
+struct ChunkPos {
+  int n;          // sequence
+  int c;          // chunk index within the sequence
+  int64_t row0;   // first token row (row = b*T + t, or packed offset)
+  int len;        // valid tokens in this chunk (1..64)
+};
+
+__device__ __forceinline__ float gate_log2(int mode, float x, float A_exp, float lb) {
+  float a;
+  if (mode == KDA_GATE_SOFTPLUS) {
+    float sp = fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x)));
+    a = -A_exp * sp;
+  } else {
+    a = lb / (1.0f + __expf(-A_exp * x));
+  }
+  return fmaxf(a * kLog2e, kMinLog2Decay);
+}
+
+// ---------------------------------------------------------------------------
+// chunk map for packed sequences: chunk_off[n] = sum_{m<n} ceil(L_m / 64)
+__global__ void kda_chunk_map_kernel(const int64_t* __restrict__ cu, int N, int* __restrict__ chunk_off) {
+  const int lane = threadIdx.x;  // one wave of 64
+  int carry = 0;
+  if (lane == 0) chunk_off[0] = 0;
+  for (int base = 0; base < N; base += 64) {
+    int n = base + lane;
+    int cnt = 0;
+    if (n < N) {
+      int64_t L = cu[n + 1] - cu[n];
+      cnt = (int)((L + CH - 1) / CH);
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    if (n < N) chunk_off[n + 1] = carry + incl;
+    carry += __shfl(incl, 63);
+  }
+}
+
+__device__ __forceinline__ bool chunk_pos(int x, int B, int T, int N, const int64_t* cu,
+                                          const int* chunk_off, ChunkPos& cp) {
+  if (cu == nullptr) {
+    const int nc = (T + CH - 1) / CH;
+    if (x >= B * nc) return false;
+    cp.n = x / nc;
+    cp.c = x % nc;
+    cp.row0 = (int64_t)cp.n * T + (int64_t)cp.c * CH;
+    cp.len = min(CH, T - cp.c * CH);
+    return true;
+  }
+  if (x >= chunk_off[N]) return false;
+  int lo = 0, hi = N;  // find n: chunk_off[n] <= x < chunk_off[n+1]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (chunk_off[mid] <= x) lo = mid; else hi = mid;
+  }
+  cp.n = lo;
+  cp.c = x - chunk_off[lo];
+  cp.row0 = cu[lo] + (int64_t)cp.c * CH;
+  cp.len = (int)min((int64_t)CH, cu[lo + 1] - cp.row0);
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// intra-chunk kernel
+// LDS plan (bytes): phase A  sG f32[64][132] | sQ bf16[64][136] | sK bf16[64][136]
+//                   phase B  sA f32[64][68] | sAq f32[64][68] | sT f32[64][68] | sKEt f16[128][72]
+//                   always   sRq, sRk, sBeta f32[64]
+constexpr int GS = 132, QS = 136, AS = 68, KES = 72, WSS = 136;
+constexpr int L_SG = 0, L_SQ = L_SG + 64 * GS * 4, L_SK = L_SQ + 64 * QS * 2, L_PA_END = L_SK + 64 * QS * 2;
+constexpr int L_SA = 0, L_SAQ = L_SA + 64 * AS * 4, L_ST = L_SAQ + 64 * AS * 4, L_SKE = L_ST + 64 * AS * 4,
+              L_PB_END = L_SKE + 128 * KES * 2;
+constexpr int L_VEC = (L_PA_END > L_PB_END ? L_PA_END : L_PB_END);
+constexpr int INTRA_LDS = L_VEC + 3 * 64 * 4;
+static_assert(64 * WSS * 2 <= 128 * KES * 2, "W staging fits in the KE^T region");
+
+__global__ void __launch_bounds__(256)
+kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                 const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta,
+                 const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+                 const int64_t* __restrict__ cu, const int* __restrict__ chunk_off,
+                 int B, int T, int N, int Hqk, int Hv, int max_chunks,
+                 float scale, float lower_bound, int gate_mode, uint8_t* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[INTRA_LDS];
+  float* sG = reinterpret_cast<float*>(smem + L_SG);
+  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + L_SQ);
+  uint16_t* sK = reinterpret_cast<uint16_t*>(smem + L_SK);
+  float* sA = reinterpret_cast<float*>(smem + L_SA);
+  float* sAq = reinterpret_cast<float*>(smem + L_SAQ);
+  float* sT = reinterpret_cast<float*>(smem + L_ST);
+  _Float16* sKEt = reinterpret_cast<_Float16*>(smem + L_SKE);
+  _Float16* sW = sKEt;  // staging for -W after the W products
+  float* sRq = reinterpret_cast<float*>(smem + L_VEC);
+  float* sRk = sRq + 64;
+  float* sBeta = sRk + 64;
+
+  const int x = blockIdx.x, h = blockIdx.y;
+  ChunkPos cp;
+  if (!chunk_pos(x, B, T, N, cu, chunk_off, cp)) return;
+  const int hq = h / (Hv / Hqk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  uint8_t* blk = ws + ((size_t)h * max_chunks + x) * BLOCK;
+
+  // ---- S1: load g -> log2 decay; q, k raw; row norms; beta
+  {
+    const int cg = tid & 15, rg = tid >> 4;
+    const float A_exp = expf(A_log[h]);
+    float dtb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dtb[e] = dt_bias[(size_t)h * DK + cg * 8 + e];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = rg + 16 * rr;
+      float gv[8];
+      uint4 qr = make_uint4(0, 0, 0, 0), kr = make_uint4(0, 0, 0, 0);
+      if (r < cp.len) {
+        const int64_t row = cp.row0 + r;
+        uint4 gr = *reinterpret_cast<const uint4*>(g + ((size_t)row * Hv + h) * DK + cg * 8);
+        unpack_bf16x8(gr, gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[e] = gate_log2(gate_mode, gv[e] + dtb[e], A_exp, lower_bound);
+        qr = *reinterpret_cast<const uint4*>(q + ((size_t)row * Hqk + hq) * DK + cg * 8);
+        kr = *reinterpret_cast<const uint4*>(k + ((size_t)row * Hqk + hq) * DK + cg * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[e] = 0.0f;
+      }
+      float4* gdst = reinterpret_cast<float4*>(sG + r * GS + cg * 8);
+      gdst[0] = make_float4(gv[0], gv[1], gv[2], gv[3]);
+      gdst[1] = make_float4(gv[4], gv[5], gv[6], gv[7]);
+      *reinterpret_cast<uint4*>(sQ + r * QS + cg * 8) = qr;
+      *reinterpret_cast<uint4*>(sK + r * QS + cg * 8) = kr;
+      float qf[8], kf[8];
+      unpack_bf16x8(qr, qf);
+      unpack_bf16x8(kr, kf);
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { sq += qf[e] * qf[e]; sk += kf[e] * kf[e]; }
+      sq = wave_xor_sum16(sq);
+      sk = wave_xor_sum16(sk);
+      if (cg == 0) {
+        sRq[r] = 1.0f / sqrtf(sq + kL2Eps);
+        sRk[r] = 1.0f / sqrtf(sk + kL2Eps);
+      }
+    }
+    if (tid < 64) {
+      float bt = 0.0f;
+      if (tid < cp.len) {
+        const int64_t row = cp.row0 + tid;
+        float bl = bf2f(beta[(size_t)row * Hv + h]);
+        bt = 1.0f / (1.0f + __expf(-bl));
+      }
+      sBeta[tid] = bt;
+    }
+  }
+  __syncthreads();
+  // ---- S2: chunk-local cumulative sum down each channel (two halves of 32 rows)
+  {
+    const int c = tid & 127, hf = tid >> 7;
+    float acc = 0.0f;
+    for (int r = 32 * hf; r < 32 * hf + 32; ++r) {
+      acc += sG[r * GS + c];
+      sG[r * GS + c] = acc;
+    }
+    __syncthreads();
+    if (hf == 1) {
+      const float base = sG[31 * GS + c];
+      for (int r = 32; r < 64; ++r) sG[r * GS + c] += base;
+    }
+  }
+  __syncthreads();
+
+  // ---- S3: Akk / Aqk sub-chunk blocks for row block I = wave
+  const int I = wave;
+  f32x4 acc_kk[4], acc_qk[4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) { acc_kk[J] = f32x4{0, 0, 0, 0}; acc_qk[J] = f32x4{0, 0, 0, 0}; }
+  {
+    const int r = 16 * I + li;  // this lane's row (A operand) / column row (B operand)
+    for (int kb = 0; kb < 4; ++kb) {
+      const int c0 = 32 * kb + 8 * lg;
+      float Gr[8], kr[8], qr[8];
+      {
+        const float4* p = reinterpret_cast<const float4*>(sG + r * GS + c0);
+        float4 a0 = p[0], a1 = p[1];
+        Gr[0] = a0.x; Gr[1] = a0.y; Gr[2] = a0.z; Gr[3] = a0.w;
+        Gr[4] = a1.x; Gr[5] = a1.y; Gr[6] = a1.z; Gr[7] = a1.w;
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + r * QS + c0), kr);
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(sQ + r * QS + c0), qr);
+      }
+      if (gate_mode == KDA_GATE_SAFE_SIGMOID) {
+        // diagonal block through the sub-chunk midpoint row m
+        const int m = 16 * I + 8;
+        bf16x8 dKh, dKl, dQ, bKh, bKl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float d = Gr[e] - sG[m * GS + c0 + e];
+          const float df = fast_exp2(d), cf = fast_exp2(-d);
+          const float xk = kr[e] * df, xq = qr[e] * df, xb = kr[e] * cf;
+          const __bf16 hk = (__bf16)xk, hb = (__bf16)xb;
+          dKh[e] = hk; dKl[e] = (__bf16)(xk - (float)hk);
+          dQ[e] = (__bf16)xq;
+          bKh[e] = hb; bKl[e] = (__bf16)(xb - (float)hb);
+        }
+        f32x4 a = acc_kk[I];
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dKh, bKh, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dKh, bKl, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dKl, bKh, a, 0, 0, 0);
+        acc_kk[I] = a;
+        acc_qk[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dQ, bKh, acc_qk[I], 0, 0, 0);
+      }
+      if (I > 0) {
+        // off-diagonal blocks (I, J<I) through p = last row of block I-1
+        const int p = 16 * I - 1;
+        half8 aK, aQ;
+        float Gp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          Gp[e] = sG[p * GS + c0 + e];
+          const float rf = fast_exp2(Gr[e] - Gp[e]);
+          aK[e] = (_Float16)(kr[e] * rf);
+          aQ[e] = (_Float16)(qr[e] * rf);
+        }
+        for (int J = 0; J < I; ++J) {
+          const int s = 16 * J + li;
+          float Gs[8], ks[8];
+          const float4* ps = reinterpret_cast<const float4*>(sG + s * GS + c0);
+          float4 b0 = ps[0], b1 = ps[1];
+          Gs[0] = b0.x; Gs[1] = b0.y; Gs[2] = b0.z; Gs[3] = b0.w;
+          Gs[4] = b1.x; Gs[5] = b1.y; Gs[6] = b1.z; Gs[7] = b1.w;
+          unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + s * QS + c0), ks);
+          half8 bK;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bK[e] = (_Float16)(ks[e] * fast_exp2(Gp[e] - Gs[e]));
+          acc_kk[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aK, bK, acc_kk[J], 0, 0, 0);
+          acc_qk[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aQ, bK, acc_qk[J], 0, 0, 0);
+        }
+      }
+    }
+    if (gate_mode == KDA_GATE_SOFTPLUS) {
+      // diagonal block pairwise: rows i = 16I + 4*lg + rr, column row s = 16I + li
+      const int s = 16 * I + li;
+      float kk[4] = {0, 0, 0, 0}, qk[4] = {0, 0, 0, 0};
+      for (int c0 = 0; c0 < DK; c0 += 8) {
+        float Gs[8], ks[8];
+        const float4* ps = reinterpret_cast<const float4*>(sG + s * GS + c0);
+        float4 b0 = ps[0], b1 = ps[1];
+        Gs[0] = b0.x; Gs[1] = b0.y; Gs[2] = b0.z; Gs[3] = b0.w;
+        Gs[4] = b1.x; Gs[5] = b1.y; Gs[6] = b1.z; Gs[7] = b1.w;
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + s * QS + c0), ks);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int ri = 16 * I + 4 * lg + rr;
+          float Gi[8], ki[8], qi[8];
+          const float4* pi = reinterpret_cast<const float4*>(sG + ri * GS + c0);
+          float4 a0 = pi[0], a1 = pi[1];
+          Gi[0] = a0.x; Gi[1] = a0.y; Gi[2] = a0.z; Gi[3] = a0.w;
+          Gi[4] = a1.x; Gi[5] = a1.y; Gi[6] = a1.z; Gi[7] = a1.w;
+          unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + ri * QS + c0), ki);
+          unpack_bf16x8(*reinterpret_cast<const uint4*>(sQ + ri * QS + c0), qi);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float ex = fast_exp2(fminf(Gi[e] - Gs[e], 0.0f));
+            const float kse = ks[e] * ex;
+            kk[rr] += ki[e] * kse;
+            qk[rr] += qi[e] * kse;
+          }
+        }
+      }
+      acc_kk[I] = f32x4{kk[0], kk[1], kk[2], kk[3]};
+      acc_qk[I] = f32x4{qk[0], qk[1], qk[2], qk[3]};
+    }
+  }
+
+  // ---- S4: elementwise products straight from Gamma: Q . 2^G (row-major),
+  //          K . 2^G (kept for W), (K . 2^(G_last - G))^T hi/lo, 2^G_last
+  half8 keReg[4];
+  {
+    // Qg rows: item (t, 8 channels)
+    for (int it = 0; it < 4; ++it) {
+      const int item = tid + 256 * it;        // 0..1023
+      const int t = item >> 4, c0 = (item & 15) * 8;
+      float Gt[8], qf[8];
+      const float4* p = reinterpret_cast<const float4*>(sG + t * GS + c0);
+      float4 a0 = p[0], a1 = p[1];
+      Gt[0] = a0.x; Gt[1] = a0.y; Gt[2] = a0.z; Gt[3] = a0.w;
+      Gt[4] = a1.x; Gt[5] = a1.y; Gt[6] = a1.z; Gt[7] = a1.w;
+      unpack_bf16x8(*reinterpret_cast<const uint4*>(sQ + t * QS + c0), qf);
+      half8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (_Float16)(qf[e] * fast_exp2(Gt[e]));
+      *reinterpret_cast<half8*>(blk + OFF_QG + ((size_t)t * DK + c0) * 2) = o;
+    }
+    // transposed items (channel c, 8 consecutive t)
+    for (int it = 0; it < 4; ++it) {
+      const int c = tid & 127, tb = (tid >> 7) + 2 * it;  // tb 0..7
+      const float GL = sG[63 * GS + c];
+      half8 ke, kdh, kdl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = tb * 8 + e;
+        const float Gt = sG[t * GS + c];
+        const float kf = bf2f(sK[t * QS + c]);
+        ke[e] = (_Float16)(kf * fast_exp2(Gt));
+        const float kd = kf * fast_exp2(GL - Gt);
+        const _Float16 hi = (_Float16)kd;
+        kdh[e] = hi;
+        kdl[e] = (_Float16)(kd - (float)hi);
+      }
+      keReg[it] = ke;
+      *reinterpret_cast<half8*>(blk + OFF_KDH + ((size_t)c * CH + tb * 8) * 2) = kdh;
+      *reinterpret_cast<half8*>(blk + OFF_KDL + ((size_t)c * CH + tb * 8) * 2) = kdl;
+    }
+    if (tid < 128) reinterpret_cast<float*>(blk + OFF_GN)[tid] = fast_exp2(sG[63 * GS + tid]);
+    if (tid < 64) {
+      reinterpret_cast<float*>(blk + OFF_QS)[tid] = scale * sRq[tid];
+      reinterpret_cast<float*>(blk + OFF_RK)[tid] = sRk[tid];
+    }
+  }
+  __syncthreads();  // phase A LDS is dead from here
+
+  // ---- S5: Akk, Aqk into LDS (masks, beta, norms); K . 2^G transposed; T = 0
+  {
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = 16 * I + 4 * lg + rr, col = 16 * J + li;
+        float akk = 0.0f, aqk = 0.0f;
+        if (J <= I) {
+          if (row > col) akk = acc_kk[J][rr] * sBeta[row] * sRk[row] * sRk[col];
+          if (row >= col) aqk = acc_qk[J][rr] * scale * sRq[row];
+        }
+        sA[row * AS + col] = akk;
+        sAq[row * AS + col] = aqk;
+      }
+    }
+    for (int it = 0; it < 4; ++it) {
+      const int c = tid & 127, tb = (tid >> 7) + 2 * it;
+      *reinterpret_cast<half8*>(sKEt + c * KES + tb * 8) = keReg[it];
+    }
+    for (int i = tid; i < 64 * AS; i += 256) sT[i] = 0.0f;
+  }
+  __syncthreads();
+
+  // ---- S6: T = (I + Akk)^-1
+  if (lane < 16) {
+    // forward substitution on the diagonal block of this wave, column j = lane
+    const int j = lane, o = 16 * wave;
+    float xcol[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = (i == j) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s -= sA[(o + i) * AS + o + m] * xcol[m];
+      xcol[i] = s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sT[(o + i) * AS + o + j] = xcol[i];
+  }
+  __syncthreads();
+  for (int d = 1; d < 4; ++d) {
+    if (wave < 4 - d) {
+      const int Ib = wave + d, Jb = wave;
+      f32x4 z = f32x4{0, 0, 0, 0};
+      for (int Kb = Jb; Kb < Ib; ++Kb) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const float a = sA[(16 * Ib + li) * AS + 16 * Kb + 4 * kb + lg];
+          const float b = sT[(16 * Kb + 4 * kb + lg) * AS + 16 * Jb + li];
+          z = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, z, 0, 0, 0);
+        }
+      }
+      f32x4 y = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = sT[(16 * Ib + li) * AS + 16 * Ib + 4 * lg + r];
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, z[r], y, 0, 0, 0);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sT[(16 * Ib + 4 * lg + rr) * AS + 16 * Jb + li] = -y[rr];
+    }
+    __syncthreads();
+  }
+
+  // ---- S7: W = T diag(b rk) (K . 2^G); T diag(b) hi/lo; Aqk
+  {
+    f32x4 accw[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) accw[nt] = f32x4{0, 0, 0, 0};
+    const int t = 16 * wave + li;
+    const int nkb = (wave >= 2) ? 2 : 1;
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int s0 = 32 * kb + 8 * lg;
+      half8 a;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = (_Float16)(sT[t * AS + s0 + e] * sBeta[s0 + e] * sRk[s0 + e]);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const half8 b = *reinterpret_cast<const half8*>(sKEt + (16 * nt + li) * KES + s0);
+        accw[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, accw[nt], 0, 0, 0);
+      }
+    }
+    // T diag(b) and Aqk to global while the products drain
+    for (int it = 0; it < 2; ++it) {
+      const int item = tid + 256 * it;  // 0..511 : (row, 8 columns)
+      const int row = item >> 3, c0 = (item & 7) * 8;
+      bf16x8 th, tl;
+      half8 aq;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = sT[row * AS + c0 + e] * sBeta[c0 + e];
+        const __bf16 hv = (__bf16)v;
+        th[e] = hv;
+        tl[e] = (__bf16)(v - (float)hv);
+        aq[e] = (_Float16)sAq[row * AS + c0 + e];
+      }
+      *reinterpret_cast<bf16x8*>(blk + OFF_TBH + ((size_t)row * CH + c0) * 2) = th;
+      *reinterpret_cast<bf16x8*>(blk + OFF_TBL + ((size_t)row * CH + c0) * 2) = tl;
+      *reinterpret_cast<half8*>(blk + OFF_AQK + ((size_t)row * CH + c0) * 2) = aq;
+    }
+    __syncthreads();  // all waves are done reading K . 2^G
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        sW[(16 * wave + 4 * lg + rr) * WSS + 16 * nt + li] = (_Float16)(-accw[nt][rr]);
+    __syncthreads();
+    for (int it = 0; it < 4; ++it) {
+      const int item = tid + 256 * it;  // (row, 8 columns) of 64 x 128
+      const int row = item >> 4, c0 = (item & 15) * 8;
+      *reinterpret_cast<half8*>(blk + OFF_WN + ((size_t)row * DK + c0) * 2) =
+          *reinterpret_cast<const half8*>(sW + row * WSS + c0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// inter-chunk state kernel
+constexpr int SSS = 136;  // sS row stride (fp16), S^T slice stored as [v][k]
+constexpr int SUS = 72;   // sU / sVt row stride
+
+struct StateOps {
+  half8 wn[4], qg[4], aq[2];
+  half8 kdh[2][2], kdl[2][2];
+  bf16x8 tbh[2], tbl[2];
+  f32x4 gn[2], qs, rk;
+  uint4 vraw;
+};
+
+__device__ __forceinline__ void load_ops(StateOps& o, const uint8_t* blk, int wave, int li, int lg,
+                                         const uint16_t* __restrict__ v, int64_t row0, int len,
+                                         int Hv, int h, int v0, int tid) {
+  const int t = 16 * wave + li;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    o.wn[kb] = *reinterpret_cast<const half8*>(blk + OFF_WN + ((size_t)t * DK + 32 * kb + 8 * lg) * 2);
+    o.qg[kb] = *reinterpret_cast<const half8*>(blk + OFF_QG + ((size_t)t * DK + 32 * kb + 8 * lg) * 2);
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    o.aq[kb] = *reinterpret_cast<const half8*>(blk + OFF_AQK + ((size_t)t * CH + 32 * kb + 8 * lg) * 2);
+    o.tbh[kb] = *reinterpret_cast<const bf16x8*>(blk + OFF_TBH + ((size_t)t * CH + 32 * kb + 8 * lg) * 2);
+    o.tbl[kb] = *reinterpret_cast<const bf16x8*>(blk + OFF_TBL + ((size_t)t * CH + 32 * kb + 8 * lg) * 2);
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int kr = 32 * wave + 16 * mt + li;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      o.kdh[mt][kb] = *reinterpret_cast<const half8*>(blk + OFF_KDH + ((size_t)kr * CH + 32 * kb + 8 * lg) * 2);
+      o.kdl[mt][kb] = *reinterpret_cast<const half8*>(blk + OFF_KDL + ((size_t)kr * CH + 32 * kb + 8 * lg) * 2);
+    }
+    o.gn[mt] = *reinterpret_cast<const f32x4*>(blk + OFF_GN + (size_t)(32 * wave + 16 * mt + 4 * lg) * 4);
+  }
+  o.qs = *reinterpret_cast<const f32x4*>(blk + OFF_QS + (size_t)(16 * wave + 4 * lg) * 4);
+  o.rk = *reinterpret_cast<const f32x4*>(blk + OFF_RK + (size_t)(16 * wave + 4 * lg) * 4);
+  // V slice: thread -> (row s = tid >> 2, 8 columns)
+  const int s = tid >> 2, cq = tid & 3;
+  if (s < len) o.vraw = *reinterpret_cast<const uint4*>(v + ((size_t)(row0 + s) * Hv + h) * DV + v0 + 8 * cq);
+  else o.vraw = make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void store_vt(uint16_t* sVt, const uint4& vr, int tid) {
+  const int s = tid >> 2, cq = tid & 3;
+  const uint32_t w[4] = {vr.x, vr.y, vr.z, vr.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sVt[(8 * cq + 2 * i) * SUS + s] = (uint16_t)(w[i] & 0xffffu);
+    sVt[(8 * cq + 2 * i + 1) * SUS + s] = (uint16_t)(w[i] >> 16);
+  }
+}
+
+struct StateCtx {
+  const uint16_t* __restrict__ v;
+  uint16_t* __restrict__ out;
+  const uint8_t* wsh;
+  int64_t bos, seqlen;
+  int x0, nc, Hv, h, v0, tid, wave, li, lg;
+  _Float16* sS;
+  _Float16* sUh;
+  _Float16* sUl;
+  uint16_t* sVt;
+};
+
+// One chunk of the state chain: consumes `cur`, prefetches chunk c+1 into `nxt`.
+__device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2], StateOps& cur, StateOps& nxt,
+                                            const int c) {
+  const uint16_t* __restrict__ v = x.v;
+  uint16_t* __restrict__ out = x.out;
+  const int64_t bos = x.bos, seqlen = x.seqlen;
+  const int x0 = x.x0, nc = x.nc, Hv = x.Hv, h = x.h, v0 = x.v0, tid = x.tid, wave = x.wave, li = x.li, lg = x.lg;
+  _Float16* sS = x.sS;
+  _Float16* sUh = x.sUh;
+  _Float16* sUl = x.sUl;
+  uint16_t* sVt = x.sVt;
+  const uint8_t* wsh = x.wsh;
+    const int64_t row0 = bos + (int64_t)c * CH;
+    const int len = (int)min((int64_t)CH, seqlen - (int64_t)c * CH);
+    if (c + 1 < nc) {
+      const int64_t r1 = row0 + CH;
+      load_ops(nxt, wsh + (size_t)(x0 + c + 1) * BLOCK, wave, li, lg, v, r1,
+               (int)min((int64_t)CH, seqlen - (int64_t)(c + 1) * CH), Hv, h, v0, tid);
+    }
+    // S^T slice -> LDS as fp16 [v][k]
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int kk = 32 * wave + 16 * mt + 4 * lg, vv = 16 * nt + li;
+        _Float16* d = sS + vv * SSS + kk;
+        typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+        half4 hv = {(_Float16)S[mt][nt][0], (_Float16)S[mt][nt][1], (_Float16)S[mt][nt][2], (_Float16)S[mt][nt][3]};
+        *reinterpret_cast<half4*>(d) = hv;
+      }
+    __syncthreads();  // B1
+    // U = T diag(b) V - W S^T ;  O = (Q . 2^G) S^T   for rows t = 16*wave + ...
+    f32x4 U[2], O[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x4 u = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(sVt + (16 * nt + li) * SUS + 32 * kb + 8 * lg);
+        u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.tbh[kb], b, u, 0, 0, 0);
+        u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.tbl[kb], b, u, 0, 0, 0);
+      }
+      f32x4 o = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const half8 b = *reinterpret_cast<const half8*>(sS + (16 * nt + li) * SSS + 32 * kb + 8 * lg);
+        u = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.wn[kb], b, u, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.qg[kb], b, o, 0, 0, 0);
+      }
+      U[nt] = u;
+      O[nt] = o;
+    }
+    // U' = rk . U  -> LDS hi/lo, transposed [v][t]
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+      half4 hi, lo;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float up = U[nt][rr] * cur.rk[rr];
+        const _Float16 hh = (_Float16)up;
+        hi[rr] = hh;
+        lo[rr] = (_Float16)(up - (float)hh);
+      }
+      const int vv = 16 * nt + li, tt = 16 * wave + 4 * lg;
+      *reinterpret_cast<half4*>(sUh + vv * SUS + tt) = hi;
+      *reinterpret_cast<half4*>(sUl + vv * SUS + tt) = lo;
+    }
+    __syncthreads();  // B2
+    if (c + 1 < nc) store_vt(sVt, nxt.vraw, tid);
+    // S <- S Diag(2^G_last) + U'^T (K . 2^(G_last - G))
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      half8 uh[2], ul[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        uh[kb] = *reinterpret_cast<const half8*>(sUh + (16 * nt + li) * SUS + 32 * kb + 8 * lg);
+        ul[kb] = *reinterpret_cast<const half8*>(sUl + (16 * nt + li) * SUS + 32 * kb + 8 * lg);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x4 s = S[mt][nt] * cur.gn[mt];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.kdh[mt][kb], uh[kb], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.kdh[mt][kb], ul[kb], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.kdl[mt][kb], uh[kb], s, 0, 0, 0);
+        }
+        S[mt][nt] = s;
+      }
+      // O = qs . (Q . 2^G) S^T + Aqk U'
+      f32x4 o = O[nt] * cur.qs;
+      const int nkb = (wave >= 2) ? 2 : 1;
+      for (int kb = 0; kb < nkb; ++kb) o = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.aq[kb], uh[kb], o, 0, 0, 0);
+      // store valid rows
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int t = 16 * wave + 4 * lg + rr;
+        if (t < len) {
+          const __bf16 ob = (__bf16)o[rr];
+          out[((size_t)(row0 + t) * Hv + h) * DV + v0 + 16 * nt + li] = *reinterpret_cast<const uint16_t*>(&ob);
+        }
+      }
+    }
+}
+
+__global__ void __launch_bounds__(256)
+kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
+                 const int* __restrict__ chunk_off, const void* __restrict__ h0, void* __restrict__ hT,
+                 uint16_t* __restrict__ out, const uint8_t* __restrict__ ws,
+                 int B, int T, int N, int Hv, int max_chunks, int init_dtype, int final_dtype) {
+  __shared__ __attribute__((aligned(16))) _Float16 sS[VS * SSS];
+  __shared__ __attribute__((aligned(16))) _Float16 sUh[VS * SUS];
+  __shared__ __attribute__((aligned(16))) _Float16 sUl[VS * SUS];
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[VS * SUS];
+
+  // XCD-aware decode: the NSLICE slices of one chain share (id mod 8), so they
+  // are dispatched to the same XCD and share its L2 for the chain's operands.
+  const int id = blockIdx.x;
+  const int chain = (id / (8 * NSLICE)) * 8 + (id & 7);
+  const int slice = (id >> 3) % NSLICE;
+  if (chain >= N * Hv) return;
+  const int n = chain / Hv, h = chain % Hv;
+  const int v0 = VS * slice;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+
+  int64_t bos, seqlen;
+  int x0, nc;
+  if (cu == nullptr) {
+    bos = (int64_t)n * T; seqlen = T;
+    const int ncs = (T + CH - 1) / CH;
+    x0 = n * ncs; nc = ncs;
+  } else {
+    bos = cu[n]; seqlen = cu[n + 1] - cu[n];
+    x0 = chunk_off[n]; nc = chunk_off[n + 1] - x0;
+  }
+
+  // state tiles: S^T[k][v], k = 32*wave + 16*mt + 4*lg + r, v = v0 + 16*nt + li
+  f32x4 S[2][2];
+  const size_t sbase = ((size_t)n * Hv + h) * DV * DK;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int kk = 32 * wave + 16 * mt + 4 * lg, vv = v0 + 16 * nt + li;
+      f32x4 s = f32x4{0, 0, 0, 0};
+      if (init_dtype == KDA_STATE_F32) {
+        s = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(h0) + sbase + (size_t)vv * DK + kk);
+      } else if (init_dtype == KDA_STATE_BF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(h0) + sbase + (size_t)vv * DK + kk);
+        s = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+      }
+      S[mt][nt] = s;
+    }
+
+  const uint8_t* wsh = ws + (size_t)h * max_chunks * BLOCK;
+  StateOps opA, opB;
+  if (nc > 0) {
+    load_ops(opA, wsh + (size_t)x0 * BLOCK, wave, li, lg, v, bos, (int)min((int64_t)CH, seqlen), Hv, h, v0, tid);
+    store_vt(sVt, opA.vraw, tid);
+  }
+  StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, li, lg, sS, sUh, sUl, sVt};
+  for (int c = 0; c < nc; c += 2) {
+    state_chunk(ctx, S, opA, opB, c);
+    if (c + 1 < nc) state_chunk(ctx, S, opB, opA, c + 1);
+  }
+
+  if (final_dtype != KDA_STATE_NONE) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int kk = 32 * wave + 16 * mt + 4 * lg, vv = v0 + 16 * nt + li;
+        if (final_dtype == KDA_STATE_F32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(hT) + sbase + (size_t)vv * DK + kk) = S[mt][nt];
+        } else {
+          __bf16 b[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) b[r] = (__bf16)S[mt][nt][r];
+          uint2 u;
+          u.x = (uint32_t)(*reinterpret_cast<uint16_t*>(&b[0])) | ((uint32_t)(*reinterpret_cast<uint16_t*>(&b[1])) << 16);
+          u.y = (uint32_t)(*reinterpret_cast<uint16_t*>(&b[2])) | ((uint32_t)(*reinterpret_cast<uint16_t*>(&b[3])) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(hT) + sbase + (size_t)vv * DK + kk) = u;
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+thread_local char g_last_error[512] = "";
+
+kda_status fail(kda_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kda_status fail(kda_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+int64_t max_chunks_of(const kda_fwd_params* p, bool packed) {
+  const int64_t nc = ((int64_t)p->T + CH - 1) / CH;
+  return packed ? nc + p->num_seqs : (int64_t)p->B * nc;
+}
+
+size_t header_bytes(const kda_fwd_params* p) {
+  size_t b = (size_t)(p->num_seqs + 1) * sizeof(int);
+  return (b + 255) & ~(size_t)255;
+}
+
+kda_status check_params(const kda_fwd_params* p, bool packed) {
+  if (!p) return fail(KDA_ERR_NULL, "params is NULL");
+  if (p->K != DK || p->V != DV) return fail(KDA_ERR_SHAPE, "K and V must both be 128 (got K=%d, V=%d)", p->K, p->V);
+  if (p->B <= 0 || p->T < 0 || p->H_qk <= 0 || p->H_v <= 0)
+    return fail(KDA_ERR_SHAPE, "need B > 0, T >= 0, H_qk > 0, H_v > 0");
+  if (p->H_v % p->H_qk != 0) return fail(KDA_ERR_SHAPE, "H_v (%d) must be a multiple of H_qk (%d)", p->H_v, p->H_qk);
+  if (packed) {
+    if (p->B != 1) return fail(KDA_ERR_SHAPE, "with cu_seqlens, B must be 1 (got %d)", p->B);
+    if (p->num_seqs <= 0) return fail(KDA_ERR_SHAPE, "with cu_seqlens, num_seqs must be > 0");
+  } else if (p->num_seqs != p->B) {
+    return fail(KDA_ERR_SHAPE, "without cu_seqlens, num_seqs (%d) must equal B (%d)", p->num_seqs, p->B);
+  }
+  if ((int64_t)p->B * p->T * (int64_t)p->H_v > ((int64_t)1 << 40))
+    return fail(KDA_ERR_SHAPE, "B*T*H_v too large");
+  if (max_chunks_of(p, packed) * (int64_t)p->H_v > ((int64_t)1 << 30))
+    return fail(KDA_ERR_SHAPE, "too many chunks");
+  if ((int64_t)p->num_seqs * p->H_v > ((int64_t)1 << 26))
+    return fail(KDA_ERR_SHAPE, "too many (sequence, head) pairs");
+  if (p->gate_mode != KDA_GATE_SOFTPLUS && p->gate_mode != KDA_GATE_SAFE_SIGMOID)
+    return fail(KDA_ERR_UNSUPPORTED, "unknown gate_mode %d", p->gate_mode);
+  if (p->flags != KDA_FLAG_QK_L2NORM)
+    return fail(KDA_ERR_UNSUPPORTED, "flags must be KDA_FLAG_QK_L2NORM (got %d)", p->flags);
+  if (p->gate_mode == KDA_GATE_SAFE_SIGMOID && !(p->lower_bound >= -5.0f && p->lower_bound < 0.0f))
+    return fail(KDA_ERR_RANGE, "safe gate needs -5 <= lower_bound < 0 (got %g)", (double)p->lower_bound);
+  if (!(p->scale == p->scale) || p->scale > 3.0e38f || p->scale < -3.0e38f)
+    return fail(KDA_ERR_RANGE, "scale must be finite");
+  const int sd[2] = {p->init_state_dtype, p->final_state_dtype};
+  for (int i = 0; i < 2; ++i)
+    if (sd[i] != KDA_STATE_NONE && sd[i] != KDA_STATE_F32 && sd[i] != KDA_STATE_BF16)
+      return fail(KDA_ERR_DTYPE, "unknown state dtype code %d", sd[i]);
+  if (p->init_state_dtype != KDA_STATE_NONE && p->final_state_dtype != KDA_STATE_NONE &&
+      p->init_state_dtype != p->final_state_dtype)
+    return fail(KDA_ERR_DTYPE, "initial_state and final_state dtypes must match when both are given");
+  return KDA_OK;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_fwd_workspace_size(const kda_fwd_params* p) {
+  if (!p) return 0;
+  // packed or dense cannot be told from params alone; size for the larger
+  const bool packed = p->B == 1 && p->num_seqs >= 1;
+  if (check_params(p, false) != KDA_OK && check_params(p, true) != KDA_OK) return 0;
+  const int64_t mc = max_chunks_of(p, packed);
+  return header_bytes(p) + (size_t)p->H_v * (size_t)mc * BLOCK;
+}
+
+kda_status kda_fwd_check(const kda_fwd_params* p, const void* q, const void* k, const void* v,
+                         const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                         const int64_t* cu_seqlens, const void* initial_state, const void* final_state,
+                         const void* out, const void* workspace, size_t workspace_bytes) {
+  g_last_error[0] = 0;
+  const bool packed = cu_seqlens != nullptr;
+  kda_status s = check_params(p, packed);
+  if (s != KDA_OK) return s;
+  const bool empty = (int64_t)p->B * p->T == 0;
+  if (!empty) {
+    const void* req[] = {q, k, v, g, beta, A_log, dt_bias, out};
+    const char* names[] = {"q", "k", "v", "g", "beta", "A_log", "dt_bias", "out"};
+    for (int i = 0; i < 8; ++i)
+      if (!req[i]) return fail(KDA_ERR_NULL, "%s is NULL", names[i]);
+    const void* al[] = {q, k, v, g, out};
+    const char* aln[] = {"q", "k", "v", "g", "out"};
+    for (int i = 0; i < 5; ++i)
+      if (!aligned16(al[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", aln[i]);
+  }
+  if (p->init_state_dtype != KDA_STATE_NONE) {
+    if (!initial_state) return fail(KDA_ERR_NULL, "initial_state is NULL but init_state_dtype is set");
+    if (!aligned16(initial_state)) return fail(KDA_ERR_ALIGN, "initial_state is not 16-byte aligned");
+  }
+  if (p->final_state_dtype != KDA_STATE_NONE) {
+    if (!final_state) return fail(KDA_ERR_NULL, "final_state is NULL but final_state_dtype is set");
+    if (!aligned16(final_state)) return fail(KDA_ERR_ALIGN, "final_state is not 16-byte aligned");
+  }
+  const size_t need = kda_fwd_workspace_size(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(KDA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  return KDA_OK;
+}
+
+kda_status kda_fwd(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                   const void* beta, const float* A_log, const float* dt_bias, const int64_t* cu_seqlens,
+                   const void* initial_state, void* final_state, void* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  kda_status s = kda_fwd_check(p, q, k, v, g, beta, A_log, dt_bias, cu_seqlens, initial_state, final_state,
+                               out, workspace, workspace_bytes);
+  if (s != KDA_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool packed = cu_seqlens != nullptr;
+  const int64_t mc = max_chunks_of(p, packed);
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
+  int* chunk_off = reinterpret_cast<int*>(wsb);
+  uint8_t* blocks = wsb + header_bytes(p);
+  (void)hipGetLastError();
+  if (packed) {
+    hipLaunchKernelGGL(kda_chunk_map_kernel, dim3(1), dim3(64), 0, st, cu_seqlens, p->num_seqs, chunk_off);
+  }
+  if (mc > 0) {
+    hipLaunchKernelGGL(kda_intra_kernel, dim3((unsigned)mc, (unsigned)p->H_v), dim3(256), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)g, (const uint16_t*)beta,
+                       A_log, dt_bias, cu_seqlens, chunk_off, p->B, p->T, p->num_seqs, p->H_qk, p->H_v,
+                       (int)mc, p->scale, p->lower_bound, p->gate_mode, blocks);
+  }
+  const int chains = p->num_seqs * p->H_v;
+  const int groups = (chains + 7) / 8;
+  hipLaunchKernelGGL(kda_state_kernel, dim3((unsigned)(groups * 8 * NSLICE)), dim3(256), 0, st,
+                     (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out,
+                     (const uint8_t*)blocks, p->B, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype,
+                     p->final_state_dtype);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL";
+    case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE";
+    case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE";
+    case KDA_ERR_RANGE: return "KDA_ERR_RANGE";
+    case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) chunked Kimi Delta Attention forward.
+ *
+ * The call contract follows the "FlashKDA Delta Attention" skill page
+ * (atskills.one/aradotso): section "Core Kernel API", the "Tensor shapes and
+ * dtypes" table and "Constraints":
+ *   q, k, g  [B, T, H, K] bf16     (K must be 128; g are gate logits)
+ *   v        [B, T, H, V] bf16     (V must be 128)
+ *   beta     [B, T, H]    bf16     logits, sigmoid applied inside
+ *   A_log    [H] fp32, dt_bias [H, K] fp32, scale, lower_bound
+ *   out      [B, T, H, V] bf16, allocated by the caller
+ *   initial_state / final_state [N, H, V, K] bf16 or fp32 or absent
+ *     (note the V-before-K orientation); dtypes must match when both given
+ *   cu_seqlens [N+1] int64 for packed variable-length batches (then B == 1
+ *     and T is the total token count)
+ * Grouped value heads (several v/gate/beta heads sharing one q/k head) are
+ * the "grouped value heads" axis of the fla-kda SKILL.md "Validation"
+ * section: H_v = G * H_qk, and v-head h reads q/k head h / G.
+ *
+ * Gate activations ("fla-kda" skill listing and fla-kda SKILL.md, "Gate
+ * contracts"):
+ *   KDA_GATE_SOFTPLUS     a = -exp(A_log[h]) * softplus(g + dt_bias[h])
+ *   KDA_GATE_SAFE_SIGMOID a = lower_bound * sigmoid(exp(A_log[h]) * (g + dt_bias[h])),
+ *                         with -5 <= lower_bound < 0
+ * The recurrence (per sequence and v-head, state S in R^{V x K}, q and k
+ * L2-normalised in the kernel):
+ *   S <- S Diag(e^{a_t});  S <- S + sigmoid(beta_t) (v_t - S k_t) k_t^T;
+ *   o_t = scale * S q_t.
+ *
+ * Ownership: every buffer is allocated and owned by the caller.  The library
+ * allocates no device memory, keeps no mutable global state except a
+ * thread-local error string, and never synchronises: kda_fwd returns once its
+ * kernels are enqueued on `stream`.  Calls that use distinct workspaces are
+ * independent; two calls in flight must not share a workspace.
+ *
+ * Errors: all argument predicates are checked on the host before anything is
+ * enqueued; on error nothing is launched and nothing is written.  The values
+ * inside device tensors (e.g. that cu_seqlens is non-decreasing and ends at
+ * T) are not validated.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,        /* a required pointer is NULL */
+  KDA_ERR_SHAPE = -2,       /* a size is out of the supported set */
+  KDA_ERR_DTYPE = -3,       /* unknown or mismatched state dtype code */
+  KDA_ERR_RANGE = -4,       /* scalar outside its allowed range */
+  KDA_ERR_ALIGN = -5,       /* a tensor base is not 16-byte aligned */
+  KDA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than kda_fwd_workspace_size */
+  KDA_ERR_LAUNCH = -7,      /* the HIP runtime rejected a launch */
+  KDA_ERR_UNSUPPORTED = -8  /* unknown gate mode or flag */
+} kda_status;
+
+typedef enum { KDA_GATE_SOFTPLUS = 0, KDA_GATE_SAFE_SIGMOID = 1 } kda_gate_mode;
+typedef enum { KDA_STATE_NONE = 0, KDA_STATE_F32 = 1, KDA_STATE_BF16 = 2 } kda_state_dtype;
+
+/* flags: the only supported configuration normalises q and k in the kernel,
+ * so KDA_FLAG_QK_L2NORM must be set. */
+enum { KDA_FLAG_QK_L2NORM = 1 };
+
+typedef struct {
+  int32_t B, T;               /* batch rows and tokens per row (total tokens when packed) */
+  int32_t H_qk, H_v;          /* q/k heads and v/gate/beta heads; H_v % H_qk == 0 */
+  int32_t K, V;               /* head dims; both must be 128 */
+  int32_t num_seqs;           /* N: equals B without cu_seqlens; else the packed count */
+  float scale;                /* output scale (typically 1/sqrt(K)) */
+  float lower_bound;          /* safe gate only: -5 <= lower_bound < 0 */
+  int32_t gate_mode;          /* kda_gate_mode */
+  int32_t init_state_dtype;   /* kda_state_dtype of initial_state (NONE: zero state) */
+  int32_t final_state_dtype;  /* kda_state_dtype of final_state (NONE: not written) */
+  int32_t flags;              /* must be KDA_FLAG_QK_L2NORM */
+} kda_fwd_params;
+
+/* Bytes of device workspace kda_fwd needs for these parameters; host only,
+ * no HIP calls.  Returns 0 if the parameters are invalid. */
+size_t kda_fwd_workspace_size(const kda_fwd_params* p);
+
+/* Validates parameters and pointers exactly as kda_fwd does, without
+ * launching anything; host only, no HIP calls.  Pointers are device
+ * pointers (never dereferenced here).  initial_state / final_state /
+ * cu_seqlens may be NULL as the parameters allow.  Returns KDA_OK or the
+ * first failing predicate's code (detail in kda_last_error()). */
+kda_status kda_fwd_check(const kda_fwd_params* p,
+                         const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* A_log, const float* dt_bias,
+                         const int64_t* cu_seqlens, const void* initial_state,
+                         const void* final_state, const void* out,
+                         const void* workspace, size_t workspace_bytes);
+
+/* Chunked KDA forward.  All pointers are device pointers:
+ *   q, k      bf16 [B, T, H_qk, 128]       v, g  bf16 [B, T, H_v, 128]
+ *   beta      bf16 [B, T, H_v] (logits)
+ *   A_log     fp32 [H_v]                    dt_bias fp32 [H_v, 128]
+ *   cu_seqlens int64 [num_seqs + 1] or NULL (dense: sequence n is batch row n)
+ *   initial_state [num_seqs, H_v, 128, 128] of init_state_dtype, or NULL
+ *   final_state   [num_seqs, H_v, 128, 128] of final_state_dtype, or NULL
+ *   out       bf16 [B, T, H_v, 128] -- every element is written
+ *   workspace at least kda_fwd_workspace_size(p) bytes, 256-byte aligned
+ *   stream    a hipStream_t (NULL: the default stream)
+ * Tensors are dense row-major.  Returns after enqueueing; KDA_ERR_LAUNCH if
+ * the runtime reports a launch error. */
+kda_status kda_fwd(const kda_fwd_params* p,
+                   const void* q, const void* k, const void* v, const void* g,
+                   const void* beta, const float* A_log, const float* dt_bias,
+                   const int64_t* cu_seqlens, const void* initial_state, void* final_state,
+                   void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static name of a status code. */
+const char* kda_status_string(kda_status s);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,146 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/kda.h declares, and
+reject each invalid argument with its documented status before anything is
+launched.  kda_fwd_check dereferences nothing, so fake aligned addresses
+stand in for device pointers.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_act_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 256-byte aligned stand-in address, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load_library()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert set(names) == set(kda.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in kda._STATUS.items():
+        assert lib.kda_status_string(code).decode() == name
+    assert lib.kda_status_string(-99).decode() == "KDA_ERR_UNKNOWN"
+
+
+def base_params(**kw):
+    d = dict(B=2, T=300, H_qk=4, H_v=4, scale=0.125, lower_bound=-1.0, gate_mode=kda.GATE_SOFTPLUS,
+             init_state_dtype=kda.STATE_F32, final_state_dtype=kda.STATE_F32)
+    d.update(kw)
+    return kda.make_params(**d)
+
+
+def check(lib, p, ws=None, cu=None, drop=None, shift=None):
+    ptrs = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, cu=cu,
+                h0=FAKE if p.init_state_dtype else None, hT=FAKE if p.final_state_dtype else None,
+                out=FAKE, ws=FAKE)
+    if drop:
+        ptrs[drop] = None
+    if shift:
+        ptrs[shift] = ptrs[shift] + 2
+    need = lib.kda_fwd_workspace_size(ctypes.byref(p))
+    order = ["q", "k", "v", "g", "beta", "A_log", "dt_bias", "cu", "h0", "hT", "out", "ws"]
+    args = [None if ptrs[n] is None else ctypes.c_void_p(ptrs[n]) for n in order]
+    return lib.kda_fwd_check(ctypes.byref(p), *args, ctypes.c_size_t(need if ws is None else ws))
+
+
+def test_valid_dense_and_packed(lib):
+    assert check(lib, base_params()) == kda.KDA_OK
+    p = base_params(B=1, T=1000, num_seqs=7)
+    assert check(lib, p, cu=FAKE) == kda.KDA_OK
+
+
+@pytest.mark.parametrize("field,bad,code", [
+    ("K", 64, -2), ("V", 256, -2), ("K", 129, -2), ("H_v", 6, -2), ("B", 0, -2), ("T", -1, -2),
+    ("num_seqs", 3, -2), ("gate_mode", 2, -8), ("flags", 0, -8), ("flags", 3, -8),
+    ("init_state_dtype", 3, -3), ("final_state_dtype", -1, -3),
+])
+def test_shape_dtype_mode_rejections(lib, field, bad, code):
+    p = base_params()
+    setattr(p, field, bad)
+    assert check(lib, p) == code, kda.last_error()
+    assert kda.last_error() != ""
+
+
+def test_gva_head_ratio(lib):
+    assert check(lib, base_params(H_qk=2, H_v=6)) == kda.KDA_OK
+    assert check(lib, base_params(H_qk=4, H_v=6)) == -2
+
+
+def test_packed_requires_single_row(lib):
+    p = base_params(B=2, T=100, num_seqs=2)
+    assert check(lib, p, cu=FAKE) == -2
+    p = base_params(B=1, T=100, num_seqs=0)
+    assert check(lib, p, cu=FAKE) == -2
+
+
+@pytest.mark.parametrize("lb,ok", [(-5.0, True), (-5.0001, False), (-4.9999, True), (0.0, False),
+                                   (0.1, False), (-1e-30, True), (float("nan"), False),
+                                   (float("-inf"), False)])
+def test_lower_bound_range_safe_gate(lib, lb, ok):
+    p = base_params(gate_mode=kda.GATE_SAFE_SIGMOID, lower_bound=lb)
+    assert (check(lib, p) == kda.KDA_OK) == ok
+    if not ok:
+        assert check(lib, p) == -4
+
+
+def test_lower_bound_ignored_for_softplus(lib):
+    assert check(lib, base_params(gate_mode=kda.GATE_SOFTPLUS, lower_bound=7.0)) == kda.KDA_OK
+
+
+def test_state_dtypes_must_match(lib):
+    assert check(lib, base_params(init_state_dtype=1, final_state_dtype=2)) == -3
+    assert check(lib, base_params(init_state_dtype=2, final_state_dtype=2)) == kda.KDA_OK
+    assert check(lib, base_params(init_state_dtype=0, final_state_dtype=2)) == kda.KDA_OK
+    assert check(lib, base_params(init_state_dtype=1, final_state_dtype=0)) == kda.KDA_OK
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "A_log", "dt_bias", "out", "h0", "hT", "ws"])
+def test_null_pointers(lib, name):
+    code = check(lib, base_params(), drop=name)
+    assert code == (-6 if name == "ws" else -1)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "out", "h0", "hT"])
+def test_misaligned(lib, name):
+    assert check(lib, base_params(), shift=name) == -5
+
+
+def test_workspace_too_small(lib):
+    p = base_params()
+    need = lib.kda_fwd_workspace_size(ctypes.byref(p))
+    assert check(lib, p, ws=need) == kda.KDA_OK
+    assert check(lib, p, ws=need - 1) == -6
+
+
+def test_workspace_size_monotone(lib):
+    size = lambda **kw: lib.kda_fwd_workspace_size(ctypes.byref(base_params(**kw)))
+    # whole 64-token chunks: equal within a chunk, growing across a boundary
+    assert size(T=1) == size(T=63) == size(T=64) < size(T=65) < size(T=1000) < size(T=8192)
+    assert lib.kda_fwd_workspace_size(ctypes.byref(base_params(H_v=8, H_qk=4))) > \
+        lib.kda_fwd_workspace_size(ctypes.byref(base_params()))
+    bad = base_params(K=64)
+    assert lib.kda_fwd_workspace_size(ctypes.byref(bad)) == 0
+
+
+def test_empty_input_needs_no_tensors(lib):
+    p = base_params(T=0)
+    assert check(lib, p, drop="q") == kda.KDA_OK

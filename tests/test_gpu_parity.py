@@ -1,0 +1,203 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases are compared element by element (several 64-token chunks plus a
+ragged tail, every gate mode, packed sequences, grouped heads, state dtypes);
+the five measured workloads are run at full size in the same launch
+configuration the benchmark times, and compared on sampled (sequence, head)
+pairs that the oracle evaluates one by one, plus properties that hold at any
+size (every output written, finite).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_act_amd import workloads as W
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def small(**kw):
+    base = dict(B=2, T=300, Hqk=4, seed=101, init_state_dtype=W.STATE_F32)
+    base.update(kw)
+    return W.make_inputs(**base)
+
+
+CASES = {
+    "softplus_dense": dict(),
+    "softplus_no_state": dict(init_state_dtype=W.STATE_NONE, T=257),
+    "safe_lb5_extremes": dict(gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-5.0, A_log_range=(-4.0, 6.0),
+                              g_std=3.0),
+    "safe_lb1_gva": dict(gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-1.0, Hqk=2, Hv=6, T=200),
+    "softplus_gva": dict(Hqk=1, Hv=3, T=130),
+    "single_partial_chunk": dict(T=37, B=3),
+    "one_token": dict(T=1, B=2),
+    "exact_chunks": dict(T=256, B=1, Hqk=2),
+    "bf16_state": dict(init_state_dtype=W.STATE_BF16, final_state_dtype=W.STATE_BF16, T=150),
+    "no_final_state": dict(final_state_dtype=W.STATE_NONE, T=100),
+    "safe_lb_tiny": dict(gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-1e-30, T=140),
+    "softplus_long_memory": dict(A_log_range=(-8.0, -6.0), T=400, B=1),
+    "softplus_strong_decay": dict(A_log_range=(3.0, 6.0), g_std=3.0, T=200),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_small_elementwise(name):
+    inp = small(**CASES[name])
+    U.log(f"[gpu] small case {name}: B={inp.B} T={inp.T} Hqk={inp.Hqk} Hv={inp.Hv} gate={inp.gate_mode}")
+    o, s = U.run_gpu(inp)
+    o_ref, s_ref = U.run_oracle(inp)
+    assert torch.isfinite(o.float()).all()
+    if s is None:
+        U.assert_parity(U.errors(U.as_f64(o), o_ref), name)
+        return
+    assert torch.isfinite(s.float()).all()
+    U.assert_parity(U.errors(U.as_f64(o), o_ref, U.as_f64(s), s_ref,
+                             state_bf16=(inp.final_state_dtype == W.STATE_BF16)), name)
+
+
+@pytest.mark.parametrize("lengths,state", [
+    ([1, 63, 64, 65, 200, 130], W.STATE_F32),
+    ([0, 5, 0, 129], W.STATE_F32),
+    ([70, 1, 1, 300, 64], W.STATE_BF16),
+])
+def test_packed_elementwise(lengths, state):
+    inp = W.make_inputs(B=1, T=None, Hqk=2, Hv=4, seed=7, lengths=lengths, init_state_dtype=state,
+                        final_state_dtype=state)
+    U.log(f"[gpu] packed lengths={lengths} state={state}")
+    o, s = U.run_gpu(inp)
+    o_ref, s_ref = U.run_oracle(inp)
+    U.assert_parity(U.errors(U.as_f64(o), o_ref, U.as_f64(s), s_ref, state_bf16=(state == W.STATE_BF16)),
+                    f"packed {lengths}")
+    # an empty sequence returns its initial state
+    for n, L in enumerate(lengths):
+        if L == 0:
+            init = torch.from_numpy(inp.initial_state_f64()[n]).float()
+            assert torch.equal(s[n].float().cpu(), init.to(s.dtype).float())
+
+
+def test_empty_dense_returns_initial_state():
+    inp = small(T=0, B=2)
+    U.log("[gpu] empty dense T=0")
+    o, s = U.run_gpu(inp)
+    assert o.numel() == 0
+    assert torch.equal(s.cpu(), torch.from_numpy(inp.initial_state))
+
+
+# ---------------------------------------------------------------- invariants on the GPU
+def test_deterministic_bitwise():
+    inp = small(T=333)
+    U.log("[gpu] determinism")
+    d = U.to_device(inp)
+    o1, s1 = U.run_gpu(inp, d)
+    o2, s2 = U.run_gpu(inp, d)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(s1, s2)
+
+
+def test_split_sequence_matches_one_call():
+    inp = small(T=320, B=1)
+    U.log("[gpu] split = one call")
+    o, s = U.run_gpu(inp)
+    cut = 130
+    part = lambda a, lo, hi: np.ascontiguousarray(a[:, lo:hi])
+    i1 = W.KdaInputs(**{**inp.__dict__, "q": part(inp.q, 0, cut), "k": part(inp.k, 0, cut),
+                        "v": part(inp.v, 0, cut), "g": part(inp.g, 0, cut), "beta": part(inp.beta, 0, cut)})
+    o1, s1 = U.run_gpu(i1)
+    i2 = W.KdaInputs(**{**inp.__dict__, "q": part(inp.q, cut, 320), "k": part(inp.k, cut, 320),
+                        "v": part(inp.v, cut, 320), "g": part(inp.g, cut, 320),
+                        "beta": part(inp.beta, cut, 320), "initial_state": s1.cpu().numpy()})
+    o2, s2 = U.run_gpu(i2)
+    oc = torch.cat([o1, o2], dim=1).float()
+    assert (oc - o.float()).abs().max().item() <= U.OUT_MAX_ABS
+    rel = ((s2 - s).norm() / s.norm()).item()
+    assert rel <= U.STATE_REL, rel
+
+
+def test_packed_matches_separate_calls():
+    lengths = [90, 1, 200, 64]
+    inp = W.make_inputs(B=1, T=None, Hqk=2, Hv=2, seed=17, lengths=lengths, init_state_dtype=W.STATE_F32)
+    U.log("[gpu] packed = separate calls")
+    o, s = U.run_gpu(inp)
+    cu = inp.cu_seqlens
+    for n in range(len(lengths)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sl = lambda x: np.ascontiguousarray(x[:, a:b])
+        i1 = W.KdaInputs(**{**inp.__dict__, "q": sl(inp.q), "k": sl(inp.k), "v": sl(inp.v), "g": sl(inp.g),
+                            "beta": sl(inp.beta), "cu_seqlens": None,
+                            "initial_state": np.ascontiguousarray(inp.initial_state[n:n + 1])})
+        o1, s1 = U.run_gpu(i1)
+        assert torch.equal(o1.view(torch.int16), o[:, a:b].view(torch.int16)), n
+        assert torch.equal(s1[0], s[n]), n
+
+
+def test_gva_matches_mha_with_repeated_qk():
+    inp = small(Hqk=2, Hv=4, T=150)
+    U.log("[gpu] GVA = MHA")
+    o, s = U.run_gpu(inp)
+    rep = W.KdaInputs(**{**inp.__dict__, "q": np.repeat(inp.q, 2, axis=2), "k": np.repeat(inp.k, 2, axis=2)})
+    o2, s2 = U.run_gpu(rep)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(s, s2)
+
+
+def test_beta_near_zero_is_pure_decay():
+    inp = small(T=200, B=1)
+    inp.beta = W.f32_to_bf16_bits(np.full(inp.beta.shape, -30.0, np.float32))
+    U.log("[gpu] beta ~ 0")
+    o, s = U.run_gpu(inp)
+    o_ref, s_ref = U.run_oracle(inp)
+    U.assert_parity(U.errors(U.as_f64(o), o_ref, U.as_f64(s), s_ref), "beta~0")
+
+
+@pytest.mark.parametrize("A", [-40.0, -4.0, 6.0, 20.0])
+def test_extreme_A_log(A):
+    for mode, lb in ((W.GATE_SOFTPLUS, -1.0), (W.GATE_SAFE_SIGMOID, -5.0)):
+        inp = small(T=200, B=1, gate_mode=mode, lower_bound=lb, A_log_range=(A, A), g_std=3.0)
+        U.log(f"[gpu] extreme A_log={A} gate={mode}")
+        o, s = U.run_gpu(inp)
+        assert torch.isfinite(o.float()).all() and torch.isfinite(s).all()
+        o_ref, s_ref = U.run_oracle(inp)
+        U.assert_parity(U.errors(U.as_f64(o), o_ref, U.as_f64(s), s_ref), f"A_log={A} gate={mode}")
+
+
+def test_long_cumulative_decay_no_write():
+    # lb = -1 over 131072 tokens (Sum a ~ -6.5e4) with beta ~ 0: the state decays to
+    # zero without NaN; checked on one head at full length
+    inp = W.make_inputs(B=1, T=131072, Hqk=1, seed=5, gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-1.0,
+                        init_state_dtype=W.STATE_F32, h0_std=1.0)
+    inp.beta = W.f32_to_bf16_bits(np.full(inp.beta.shape, -30.0, np.float32))
+    U.log("[gpu] long cumulative decay")
+    o, s = U.run_gpu(inp)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(s).all()
+    assert s.abs().max().item() < 1e-30
+
+
+# ---------------------------------------------------------------- the five measured workloads
+SAMPLES = {1: None, 2: [(0, 0), (1, 5), (3, 15), (2, 9)], 3: [(0, 0), (1, 31), (0, 17), (1, 6)],
+           4: [(0, 0), (5, 31), (11, 7), (15, 20)], 5: [(0, 0), (0, 1), (0, 17), (0, 30)]}
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_measured_workload(idx):
+    inp = W.workload(idx)
+    U.log(f"[gpu] workload {idx} {inp.name}: B={inp.B} T={inp.T} Hqk={inp.Hqk} Hv={inp.Hv} N={inp.N}")
+    o, s = U.run_gpu(inp)
+    assert not torch.isnan(o.float()).any(), "some output element was not written"
+    assert torch.isfinite(o.float()).all() and torch.isfinite(s.float()).all()
+    bf = inp.final_state_dtype == W.STATE_BF16
+    if SAMPLES[idx] is None:
+        o_ref, s_ref = U.run_oracle(inp)
+        U.assert_parity(U.errors(U.as_f64(o), o_ref, U.as_f64(s), s_ref, state_bf16=bf), inp.name)
+        return
+    refs = U.oracle_pairs(inp, SAMPLES[idx])
+    for (n, h), (o_ref, s_ref) in refs.items():
+        if inp.cu_seqlens is None:
+            og = o[n, :, h]
+        else:
+            a, b = int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
+            og = o[0, a:b, h]
+        U.assert_parity(U.errors(U.as_f64(og), o_ref, U.as_f64(s[n, h]), s_ref, state_bf16=bf),
+                        f"{inp.name} pair n={n} h={h}")
