@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Chunked KDA forward benchmark on one MI355X.
+
+One step = one full forward (kda_fwd: intra-chunk kernel + state-chain
+kernel) over the safe-gate workload B=2, T=8192, H=32, K=V=128 (lower_bound
+-5, fp32 initial and final state), inputs resident in HBM.  Prints one JSON
+line: tokens/s, the dominant kernel's roofline from HIP events recorded
+around each stage on the launch stream, the path's fraction of the HBM and
+bf16 MFMA peaks, and the fp64 CPU oracle timed on this host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunk_kda fwd tokens/s (H=32,K=V=128,T=8192) + % bf16 MFMA peak, 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+# Method work per token-head (dense 64-token tiles): 5 x 2*64*128 for Akk, Aqk,
+# w, u, Aqk.U plus 3 x 2*128*128 for W.S, Q.S, K^T.U.
+FLOP_PER_TOKEN_HEAD = 5 * 2 * 64 * 128 + 3 * 2 * 128 * 128
+BLOCK_BYTES = 91136  # per (v-head, chunk) intermediates written by the intra kernel
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "gated_delta_rule_act_amd", "csrc", "kda_fwd.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel, workload_name):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"source_sha:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def bytes_model(inp):
+    """Compulsory bytes per launch of each kernel given the two-kernel dataflow,
+    and the method's own minimum for the whole path."""
+    B, T, Hqk, Hv, K, V = inp.B, inp.T, inp.Hqk, inp.Hv, inp.K, inp.V
+    nchunks = B * ((T + 63) // 64) if inp.cu_seqlens is None else sum(
+        (int(inp.cu_seqlens[n + 1] - inp.cu_seqlens[n]) + 63) // 64 for n in range(inp.N))
+    tok = B * T
+    st = {0: 0, 1: 4, 2: 2}
+    h0 = inp.N * Hv * V * K * st[inp.init_state_dtype]
+    hT = inp.N * Hv * V * K * st[inp.final_state_dtype]
+    inter = nchunks * Hv * BLOCK_BYTES
+    intra = tok * Hqk * K * 2 * 2 + tok * Hv * K * 2 + tok * Hv * 2 + inter
+    state = inter + tok * Hv * V * 2 + tok * Hv * V * 2 + h0 + hT
+    path = tok * Hqk * K * 2 * 2 + tok * Hv * (K * 2 + V * 2 + 2 + V * 2) + h0 + hT
+    return {"intra": intra, "state": state, "path": path}
+
+
+def cpu_baseline(inp, out_gpu, state_gpu, budget_s=30.0):
+    """Time the fp64 oracle on this host (all cores) on the same inputs; also
+    report the GPU result's parity against it."""
+    import numpy as np
+    import oracle
+    from tests import gpu_util as U
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    # calibrate on one head to keep the run bounded (10-30 s of CPU work)
+    t0 = time.perf_counter()
+    U.oracle_pair(inp, 0, 0, inp.initial_state_f64())
+    one = time.perf_counter() - t0
+    est_full = one * inp.N * inp.Hv / max(1, threads)
+    heads = inp.Hv
+    if est_full > budget_s:
+        heads = max(threads, int(inp.Hv * budget_s / est_full) // threads * threads)
+        heads = min(heads, inp.Hv)
+    sub = inp
+    if heads < inp.Hv:
+        G = inp.Hv // inp.Hqk
+        hq = max(1, heads // G)
+        heads = hq * G
+        import dataclasses
+        sub = dataclasses.replace(inp, q=np.ascontiguousarray(inp.q[:, :, :hq]), k=np.ascontiguousarray(inp.k[:, :, :hq]),
+                                  v=np.ascontiguousarray(inp.v[:, :, :heads]), g=np.ascontiguousarray(inp.g[:, :, :heads]),
+                                  beta=np.ascontiguousarray(inp.beta[:, :, :heads]), A_log=inp.A_log[:heads],
+                                  dt_bias=inp.dt_bias[:heads],
+                                  initial_state=None if inp.initial_state is None else
+                                  np.ascontiguousarray(inp.initial_state[:, :heads]))
+    t0 = time.perf_counter()
+    o_ref, s_ref = U.run_oracle(sub, nthreads=threads)
+    dt = time.perf_counter() - t0
+    tokens_per_s = inp.B * inp.T * (heads / inp.Hv) / dt
+    og = U.as_f64(out_gpu[:, :, :heads])
+    e = U.errors(og, o_ref, U.as_f64(state_gpu[:, :heads]), s_ref)
+    cpu = {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{inp.name}: all {inp.B * inp.T} tokens of {heads} of {inp.Hv} v-heads "
+                     f"(fp64 token recurrence, {dt:.1f} s; tokens/s scaled to all heads)",
+           "seconds": dt}
+    parity = {"out_max_abs": e["out_max_abs"], "out_rel_rms": e["out_rel_rms"], "state_rel": e["state_rel"],
+              "heads_checked": heads, "tol_out_max_abs": U.OUT_MAX_ABS, "tol_state_rel": U.STATE_REL}
+    return cpu, parity
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="measured workload index (the bench line is 3)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="instead of the forward, run N plain 1 GiB device copies (traffic counter scale)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); "
+              "multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_act_amd import kda, workloads as W
+    from tests import gpu_util as U
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.copy_calibration):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": {"read": 1 << 30, "write": 1 << 30},
+                          "copies": args.copy_calibration}))
+        return
+
+    t_gen = time.perf_counter()
+    inp = W.workload(args.workload)
+    d = U.to_device(inp)
+    fdt = U.final_dtype_of(inp)
+    out = torch.empty((inp.B, inp.T, inp.Hv, inp.V), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((inp.N, inp.Hv, inp.V, inp.K), dtype=fdt, device=dev)
+    p = kda.make_params(B=inp.B, T=inp.T, H_qk=inp.Hqk, H_v=inp.Hv, num_seqs=inp.N, scale=inp.scale,
+                        lower_bound=inp.lower_bound, gate_mode=inp.gate_mode,
+                        init_state_dtype=inp.init_state_dtype, final_state_dtype=inp.final_state_dtype)
+    ws = torch.empty(kda.workspace_size(p), dtype=torch.uint8, device=dev)
+    print(f"[bench] workload {inp.name} ready in {time.perf_counter() - t_gen:.1f} s; "
+          f"workspace {ws.numel() / 2**30:.2f} GiB", file=sys.stderr, flush=True)
+
+    def step(stage=None):
+        kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"], inp.scale, inp.lower_bound,
+                inp.gate_mode, initial_state=d["h0"], cu_seqlens=d["cu_seqlens"], out=out, final_state=fs,
+                final_state_dtype=fdt, workspace=ws, stage=stage)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` full forwards
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+    # per-kernel durations: events around each stage on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        e[0].record()
+        step("intra")
+        e[1].record()
+        step("state")
+        e[2].record()
+    torch.cuda.synchronize()
+    t_intra = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_state = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    tokens = inp.B * inp.T
+    value = tokens / (ms_per_step * 1e-3)
+    bm = bytes_model(inp)
+    kern = {"intra": t_intra, "state": t_state}
+    dom = max(kern, key=kern.get)
+    achieved = bm[dom] / (kern[dom] * 1e-3) / 1e9
+    traffic = profiled_traffic(dom, inp.name)
+    path_gbps = bm["path"] / (ms_per_step * 1e-3) / 1e9
+    mfma_tflops = FLOP_PER_TOKEN_HEAD * tokens * inp.Hv / (ms_per_step * 1e-3) / 1e12
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded numpy PCG64, see DESIGN.md)",
+        "config": {"workload": inp.name, "B": inp.B, "T": inp.T, "H_qk": inp.Hqk, "H_v": inp.Hv, "K": inp.K,
+                   "V": inp.V, "gate": ["softplus", "safe_sigmoid"][inp.gate_mode],
+                   "lower_bound": inp.lower_bound, "chunk": 64, "sub_chunk": 16,
+                   "initial_state": ["none", "fp32", "bf16"][inp.init_state_dtype],
+                   "final_state": ["none", "fp32", "bf16"][inp.final_state_dtype],
+                   "packed": inp.cu_seqlens is not None},
+        "roofline": {"bound": "hbm", "kernel": f"kda_{dom}_kernel", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": bm[dom],
+                     "avg_launch_ms": kern[dom]},
+        "kernels_ms": {"kda_intra_kernel": t_intra, "kda_state_kernel": t_state},
+        "path": {"min_bytes_per_step": bm["path"], "achieved_GBps": path_gbps,
+                 "hbm_frac": path_gbps / HBM_PEAK_GBPS, "mfma_algorithmic_TFLOPs": mfma_tflops,
+                 "mfma_pct_bf16_peak": 100.0 * mfma_tflops / BF16_PEAK_TFLOPS,
+                 "flop_per_token_head": FLOP_PER_TOKEN_HEAD},
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu, parity = cpu_baseline(inp, out, fs)
+        rec["cpu_baseline"] = cpu
+        rec["parity"] = parity
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

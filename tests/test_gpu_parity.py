@@ -144,7 +144,9 @@ def test_gva_matches_mha_with_repeated_qk():
 
 
 def test_beta_near_zero_is_pure_decay():
-    inp = small(T=200, B=1)
+    # weak decay so the surviving initial state stays O(1) and the relative
+    # state error is well conditioned
+    inp = small(T=200, B=1, A_log_range=(-8.0, -6.0), h0_std=1.0)
     inp.beta = W.f32_to_bf16_bits(np.full(inp.beta.shape, -30.0, np.float32))
     U.log("[gpu] beta ~ 0")
     o, s = U.run_gpu(inp)
