@@ -99,17 +99,6 @@ struct ChunkPos {
   int len;        // valid tokens in this chunk (1..64)
 };
 
-__device__ __forceinline__ float gate_log2(int mode, float x, float A_exp, float lb) {
-  float a;
-  if (mode == KDA_GATE_SOFTPLUS) {
-    float sp = fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x)));
-    a = -A_exp * sp;
-  } else {
-    a = lb / (1.0f + __expf(-A_exp * x));
-  }
-  return fmaxf(a * kLog2e, kMinLog2Decay);
-}
-
 // ---------------------------------------------------------------------------
 // chunk map for packed sequences: chunk_off[n] = sum_{m<n} ceil(L_m / 64)
 __global__ void kda_chunk_map_kernel(const int64_t* __restrict__ cu, int N, int* __restrict__ chunk_off) {
@@ -160,36 +149,128 @@ __device__ __forceinline__ bool chunk_pos(int x, int B, int T, int N, const int6
 
 // ---------------------------------------------------------------------------
 // intra-chunk kernel
-// LDS plan (bytes): phase A  sG f32[64][132] | sQ bf16[64][136] | sK bf16[64][136]
-//                   phase B  sA f32[64][68] | sAq f32[64][68] | sT f32[64][68] | sKEt f16[128][72]
-//                   always   sRq, sRk, sBeta f32[64]
-constexpr int GS = 132, QS = 136, AS = 68, KES = 72, WSS = 136;
-constexpr int L_SG = 0, L_SQ = L_SG + 64 * GS * 4, L_SK = L_SQ + 64 * QS * 2, L_PA_END = L_SK + 64 * QS * 2;
-constexpr int L_SA = 0, L_SAQ = L_SA + 64 * AS * 4, L_ST = L_SAQ + 64 * AS * 4, L_SKE = L_ST + 64 * AS * 4,
-              L_PB_END = L_SKE + 128 * KES * 2;
-constexpr int L_VEC = (L_PA_END > L_PB_END ? L_PA_END : L_PB_END);
-constexpr int INTRA_LDS = L_VEC + 3 * 64 * 4;
-static_assert(64 * WSS * 2 <= 128 * KES * 2, "W staging fits in the KE^T region");
+//
+// Register layout: wave w owns the 16-row sub-chunk I = w (rows 16I..16I+15);
+// lane l = (i = l & 15, g = l >> 4) holds row r = 16I + i and the 32 channels
+// c = 32*kb + 8*g + e (kb = 0..3, e = 0..7).  This is exactly the operand
+// layout of v_mfma_*_16x16x32 (A: row i, B: column-row i, slots 8g..8g+7 of
+// each 32-channel k-block), so every per-element factor is formed in
+// registers and fed to the MFMA without moving it.
+//
+// Exponent safety.  With p = last row of sub-chunk I-1 (Gamma_p = 0 for I = 0)
+// and e = last row of sub-chunk I, every element needs only
+//     R = 2^(Gamma_r - Gamma_p) <= 1   and   C = 2^(Gamma_e - Gamma_r) <= 1.
+// All other factors are per-channel vectors, computed once per chunk:
+//     P_I  = 2^Gamma_p            (Q . 2^Gamma = qR P_I, K . 2^Gamma = kR P_I)
+//     L_I  = 2^(Gamma_63 - Gamma_e)   (K . 2^(Gamma_63 - Gamma) = kC L_I)
+//     D_IJ = 2^(Gamma_p(I) - Gamma_e(J)), I >= J + 2 (off-diagonal columns)
+//     Mr_I = 2^(Gamma_p - Gamma_m), Mc_I = 2^(Gamma_m - Gamma_e), m = 16I + 8
+// Off-diagonal block (I, J < I): rows qR, kR against columns kC D_IJ -- all
+// factors <= 1, fp16 MFMA.  Diagonal block, safe gate: rows kR Mr against
+// columns kC Mc, i.e. both sides offset by the sub-chunk midpoint, with
+// exponents within 8 * |lower_bound| * log2(e) of zero (at most 2^58), on the
+// fp32 MFMA.  Diagonal block, softplus gate: the per-token decay is unbounded,
+// so the 136 pairs of the block are evaluated pairwise on the VALU.
+constexpr int AS = 68;      // fp32 row stride of Akk / T
+constexpr int AQS = 72;     // fp16 row stride of Aqk
+constexpr int KES = 72;     // fp16 row stride of the transposed K . 2^G / Kd tiles
+constexpr int WSS = 136;    // fp16 row stride of the W staging tile
+constexpr int GS = 132;     // fp32 row stride of Gamma (softplus pairwise only)
+constexpr int QS = 136;     // bf16 row stride of raw q, k (softplus pairwise only)
+constexpr int NVEC = 19;    // per-channel vectors: P0..3, L0..3, D20, D30, D31, Mr0..3, Mc0..3
+constexpr int V_P = 0, V_L = 4, V_D20 = 8, V_D30 = 9, V_D31 = 10, V_MR = 11, V_MC = 15;
 
+// LDS plan (bytes).  Region X is reused: mailbox (phases 3-4), Kd staging
+// (phase 4b), then Akk fp32 / W staging (phases 5-7).  Region T holds the
+// sub-chunk totals, midpoints and per-channel vectors until phase 3, then T.
+constexpr int MB_BYTES = 6 * 4 * 64 * 16;               // 6 (I,J) pairs x 4 k-blocks x 64 lanes x 16 B
+constexpr int X_BYTES = MB_BYTES;
+constexpr int L_X = 0;
+constexpr int L_T = L_X + X_BYTES;
+constexpr int T_BYTES = 64 * AS * 4;
+constexpr int L_TOT = L_T;                              // [4][128] f32, inside region T
+constexpr int L_MID = L_TOT + 4 * 128 * 4;              // [4][128] f32
+constexpr int L_VEC = L_MID + 4 * 128 * 4;              // [NVEC][128] f32
+constexpr int L_KE = L_T + T_BYTES;
+constexpr int L_AQ = L_KE + 128 * KES * 2;
+constexpr int L_RQ = L_AQ + 64 * AQS * 2;
+constexpr int L_RK = L_RQ + 64 * 4;
+constexpr int L_BETA = L_RK + 64 * 4;
+constexpr int L_END = L_BETA + 64 * 4;
+// softplus only: Gamma and raw q, k rows for the pairwise diagonal
+constexpr int L_PG = L_END;
+constexpr int L_PQ = L_PG + 64 * GS * 4;
+constexpr int L_PK = L_PQ + 64 * QS * 2;
+constexpr int L_END_SP = L_PK + 64 * QS * 2;
+static_assert(L_VEC + NVEC * 128 * 4 <= L_T + T_BYTES, "vectors fit in region T");
+static_assert(64 * AS * 4 <= X_BYTES, "Akk fits in region X");
+static_assert(64 * WSS * 2 <= X_BYTES, "W staging fits in region X");
+static_assert(X_BYTES >= 128 * KES * 2, "Kd staging fits in region X");
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_shr(float x) {
+  // lane i of each 16-lane row reads lane i - k of the same row; lanes with
+  // no source keep `old` = 0
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float scan16(float x) {
+  x += dpp_row_shr<0x111>(x);
+  x += dpp_row_shr<0x112>(x);
+  x += dpp_row_shr<0x114>(x);
+  x += dpp_row_shr<0x118>(x);
+  return x;
+}
+
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// log2-domain gate activation of x = g + dt_bias (A_exp = exp(A_log)).
+template <int MODE>
+__device__ __forceinline__ float gate2(float x, float A_exp, float lb_log2e) {
+  if (MODE == KDA_GATE_SAFE_SIGMOID) {
+    // lb * sigmoid(A x) * log2(e)
+    return lb_log2e * fast_rcp(1.0f + fast_exp2(-(A_exp * kLog2e) * x));
+  } else {
+    // -A * softplus(x) * log2(e), softplus(x) = max(x, 0) + log1p(e^-|x|)
+    const float ex = fast_exp2(-kLog2e * fabsf(x));
+    const float l1p = (ex < 0.0078125f) ? ex * (1.0f - ex * (0.5f - ex * (1.0f / 3.0f)))
+                                        : fast_log2(1.0f + ex) * 0.6931471805599453f;
+    const float a2 = -(A_exp * kLog2e) * (fmaxf(x, 0.0f) + l1p);
+    return fmaxf(a2, kMinLog2Decay);
+  }
+}
+
+__device__ __forceinline__ half8 to_half8(const float* v) {
+  half8 h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = (_Float16)v[e];
+  return h;
+}
+
+template <int MODE>
 __global__ void __launch_bounds__(256)
 kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta,
                  const float* __restrict__ A_log, const float* __restrict__ dt_bias,
                  const int64_t* __restrict__ cu, const int* __restrict__ chunk_off,
                  int B, int T, int N, int Hqk, int Hv, int max_chunks,
-                 float scale, float lower_bound, int gate_mode, uint8_t* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[INTRA_LDS];
-  float* sG = reinterpret_cast<float*>(smem + L_SG);
-  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + L_SQ);
-  uint16_t* sK = reinterpret_cast<uint16_t*>(smem + L_SK);
-  float* sA = reinterpret_cast<float*>(smem + L_SA);
-  float* sAq = reinterpret_cast<float*>(smem + L_SAQ);
-  float* sT = reinterpret_cast<float*>(smem + L_ST);
-  _Float16* sKEt = reinterpret_cast<_Float16*>(smem + L_SKE);
-  _Float16* sW = sKEt;  // staging for -W after the W products
-  float* sRq = reinterpret_cast<float*>(smem + L_VEC);
-  float* sRk = sRq + 64;
-  float* sBeta = sRk + 64;
+                 float scale, float lower_bound, uint8_t* __restrict__ ws) {
+  constexpr int LDS = (MODE == KDA_GATE_SOFTPLUS) ? L_END_SP : L_END;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+  uint8_t* sX = smem + L_X;                                          // mailbox / Kd staging / Akk / W staging
+  float* sA = reinterpret_cast<float*>(smem + L_X);
+  _Float16* sW = reinterpret_cast<_Float16*>(smem + L_X);
+  _Float16* sKd = reinterpret_cast<_Float16*>(smem + L_X);
+  float* sT = reinterpret_cast<float*>(smem + L_T);
+  _Float16* sKEt = reinterpret_cast<_Float16*>(smem + L_KE);
+  _Float16* sAq = reinterpret_cast<_Float16*>(smem + L_AQ);
+  float* sTot = reinterpret_cast<float*>(smem + L_TOT);
+  float* sMid = reinterpret_cast<float*>(smem + L_MID);
+  float* sVec = reinterpret_cast<float*>(smem + L_VEC);
+  float* sRq = reinterpret_cast<float*>(smem + L_RQ);
+  float* sRk = reinterpret_cast<float*>(smem + L_RK);
+  float* sBeta = reinterpret_cast<float*>(smem + L_BETA);
 
   const int x = blockIdx.x, h = blockIdx.y;
   ChunkPos cp;
@@ -197,165 +278,233 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int hq = h / (Hv / Hqk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
+  const int I = wave;
+  const int r = 16 * I + li;
+  const bool valid = r < cp.len;
   uint8_t* blk = ws + ((size_t)h * max_chunks + x) * BLOCK;
 
-  // ---- S1: load g -> log2 decay; q, k raw; row norms; beta
+  // ---- phase 1: loads, gate, norms, beta, in-register 16-row scan
+  // G holds the scan local to the sub-chunk: G = Gamma_r - Gamma_p.
+  float G[4][8];
+  uint4 qraw[4], kraw[4];
   {
-    const int cg = tid & 15, rg = tid >> 4;
     const float A_exp = expf(A_log[h]);
-    float dtb[8];
+    const float lb_log2e = lower_bound * kLog2e;
+    const int64_t row = cp.row0 + r;
+    float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dtb[e] = dt_bias[(size_t)h * DK + cg * 8 + e];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int r = rg + 16 * rr;
-      float gv[8];
-      uint4 qr = make_uint4(0, 0, 0, 0), kr = make_uint4(0, 0, 0, 0);
-      if (r < cp.len) {
-        const int64_t row = cp.row0 + r;
-        uint4 gr = *reinterpret_cast<const uint4*>(g + ((size_t)row * Hv + h) * DK + cg * 8);
-        unpack_bf16x8(gr, gv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gv[e] = gate_log2(gate_mode, gv[e] + dtb[e], A_exp, lower_bound);
-        qr = *reinterpret_cast<const uint4*>(q + ((size_t)row * Hqk + hq) * DK + cg * 8);
-        kr = *reinterpret_cast<const uint4*>(k + ((size_t)row * Hqk + hq) * DK + cg * 8);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gv[e] = 0.0f;
+    for (int kb = 0; kb < 4; ++kb) {
+      const int c0 = 32 * kb + 8 * lg;
+      uint4 gr = make_uint4(0, 0, 0, 0);
+      qraw[kb] = gr;
+      kraw[kb] = gr;
+      if (valid) {
+        gr = *reinterpret_cast<const uint4*>(g + ((size_t)row * Hv + h) * DK + c0);
+        qraw[kb] = *reinterpret_cast<const uint4*>(q + ((size_t)row * Hqk + hq) * DK + c0);
+        kraw[kb] = *reinterpret_cast<const uint4*>(k + ((size_t)row * Hqk + hq) * DK + c0);
       }
-      float4* gdst = reinterpret_cast<float4*>(sG + r * GS + cg * 8);
-      gdst[0] = make_float4(gv[0], gv[1], gv[2], gv[3]);
-      gdst[1] = make_float4(gv[4], gv[5], gv[6], gv[7]);
-      *reinterpret_cast<uint4*>(sQ + r * QS + cg * 8) = qr;
-      *reinterpret_cast<uint4*>(sK + r * QS + cg * 8) = kr;
       float qf[8], kf[8];
-      unpack_bf16x8(qr, qf);
-      unpack_bf16x8(kr, kf);
-      float sq = 0.f, sk = 0.f;
+      unpack_bf16x8(gr, G[kb]);
+      unpack_bf16x8(qraw[kb], qf);
+      unpack_bf16x8(kraw[kb], kf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) { sq += qf[e] * qf[e]; sk += kf[e] * kf[e]; }
-      sq = wave_xor_sum16(sq);
-      sk = wave_xor_sum16(sk);
-      if (cg == 0) {
-        sRq[r] = 1.0f / sqrtf(sq + kL2Eps);
-        sRk[r] = 1.0f / sqrtf(sk + kL2Eps);
+      const float4 d0 = *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + c0);
+      const float4 d1 = *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + c0 + 4);
+      const float dtb[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) G[kb][e] = valid ? gate2<MODE>(G[kb][e] + dtb[e], A_exp, lb_log2e) : 0.0f;
+    }
+    sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
+    sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
+    if (lg == 0) {
+      sRq[r] = rsqrtf(sq + kL2Eps);
+      sRk[r] = rsqrtf(sk + kL2Eps);
+      float bt = 0.0f;
+      if (valid) bt = fast_rcp(1.0f + fast_exp2(-kLog2e * bf2f(beta[(size_t)row * Hv + h])));
+      sBeta[r] = bt;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) G[kb][e] = scan16(G[kb][e]);
+    // sub-chunk totals (row 15) and midpoint values (row 8), both local
+    if (li == 15 || li == 8) {
+      float* dst = (li == 15 ? sTot : sMid) + I * 128;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float4* p4 = reinterpret_cast<float4*>(dst + 32 * kb + 8 * lg);
+        p4[0] = make_float4(G[kb][0], G[kb][1], G[kb][2], G[kb][3]);
+        p4[1] = make_float4(G[kb][4], G[kb][5], G[kb][6], G[kb][7]);
+      }
+    }
+    if (MODE == KDA_GATE_SOFTPLUS) {
+      // local Gamma and raw q, k rows for the pairwise diagonal
+      float* sPG = reinterpret_cast<float*>(smem + L_PG);
+      uint16_t* sPQb = reinterpret_cast<uint16_t*>(smem + L_PQ);
+      uint16_t* sPKb = reinterpret_cast<uint16_t*>(smem + L_PK);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float4* p4 = reinterpret_cast<float4*>(sPG + r * GS + 32 * kb + 8 * lg);
+        p4[0] = make_float4(G[kb][0], G[kb][1], G[kb][2], G[kb][3]);
+        p4[1] = make_float4(G[kb][4], G[kb][5], G[kb][6], G[kb][7]);
+        *reinterpret_cast<uint4*>(sPQb + r * QS + 32 * kb + 8 * lg) = qraw[kb];
+        *reinterpret_cast<uint4*>(sPKb + r * QS + 32 * kb + 8 * lg) = kraw[kb];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: per-channel vectors from the sub-chunk totals T_J and local
+  // midpoints M_J (every exponent is a sum of totals, so none is a difference
+  // of large cumulative values):
+  //   P_I = 2^(T_0+..+T_{I-1}), L_I = 2^(T_{I+1}+..+T_3), D_IJ = 2^(T_{J+1}+..+T_{I-1}),
+  //   Mr_I = 2^(-M_I), Mc_I = 2^(M_I - T_I), 2^Gamma_63 = 2^(T_0+..+T_3)
+  {
+    const int c = tid & 127, half = tid >> 7;
+    const float T0 = sTot[c], T1 = sTot[128 + c], T2 = sTot[256 + c], T3 = sTot[384 + c];
+    if (half == 0) {
+      sVec[(V_P + 0) * 128 + c] = 1.0f;
+      sVec[(V_P + 1) * 128 + c] = fast_exp2(T0);
+      sVec[(V_P + 2) * 128 + c] = fast_exp2(T0 + T1);
+      sVec[(V_P + 3) * 128 + c] = fast_exp2((T0 + T1) + T2);
+      reinterpret_cast<float*>(blk + OFF_GN)[c] = fast_exp2(((T0 + T1) + T2) + T3);
+      sVec[V_D20 * 128 + c] = fast_exp2(T1);
+      sVec[V_D30 * 128 + c] = fast_exp2(T1 + T2);
+      sVec[V_D31 * 128 + c] = fast_exp2(T2);
+    } else {
+      sVec[(V_L + 0) * 128 + c] = fast_exp2((T1 + T2) + T3);
+      sVec[(V_L + 1) * 128 + c] = fast_exp2(T2 + T3);
+      sVec[(V_L + 2) * 128 + c] = fast_exp2(T3);
+      sVec[(V_L + 3) * 128 + c] = 1.0f;
+      const float Tj[4] = {T0, T1, T2, T3};
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        const float m = sMid[J * 128 + c];
+        sVec[(V_MR + J) * 128 + c] = fast_exp2(-m);
+        sVec[(V_MC + J) * 128 + c] = fast_exp2(m - Tj[J]);
       }
     }
     if (tid < 64) {
-      float bt = 0.0f;
-      if (tid < cp.len) {
-        const int64_t row = cp.row0 + tid;
-        float bl = bf2f(beta[(size_t)row * Hv + h]);
-        bt = 1.0f / (1.0f + __expf(-bl));
-      }
-      sBeta[tid] = bt;
-    }
-  }
-  __syncthreads();
-  // ---- S2: chunk-local cumulative sum down each channel (two halves of 32 rows)
-  {
-    const int c = tid & 127, hf = tid >> 7;
-    float acc = 0.0f;
-    for (int r = 32 * hf; r < 32 * hf + 32; ++r) {
-      acc += sG[r * GS + c];
-      sG[r * GS + c] = acc;
-    }
-    __syncthreads();
-    if (hf == 1) {
-      const float base = sG[31 * GS + c];
-      for (int r = 32; r < 64; ++r) sG[r * GS + c] += base;
+      reinterpret_cast<float*>(blk + OFF_QS)[tid] = scale * sRq[tid];
+      reinterpret_cast<float*>(blk + OFF_RK)[tid] = sRk[tid];
     }
   }
   __syncthreads();
 
-  // ---- S3: Akk / Aqk sub-chunk blocks for row block I = wave
-  const int I = wave;
-  f32x4 acc_kk[4], acc_qk[4];
+  // ---- phase 3: per-element factors R = 2^G, C = 2^(T_I - G); outputs that
+  // need no other row; column operands for the later row blocks
+  // accumulators: the diagonal block, and off-diagonal blocks J = 0..2 (J < I);
+  // all register arrays are indexed by compile-time values only
+  f32x4 dkk = f32x4{0, 0, 0, 0}, dqk = f32x4{0, 0, 0, 0};
+  f32x4 okk[3], oqk[3];
 #pragma unroll
-  for (int J = 0; J < 4; ++J) { acc_kk[J] = f32x4{0, 0, 0, 0}; acc_qk[J] = f32x4{0, 0, 0, 0}; }
+  for (int J = 0; J < 3; ++J) { okk[J] = f32x4{0, 0, 0, 0}; oqk[J] = f32x4{0, 0, 0, 0}; }
+  half8 aK[4], aQ[4], kdh[4], kdl[4];
   {
-    const int r = 16 * I + li;  // this lane's row (A operand) / column row (B operand)
+    const float* vP = sVec + (V_P + I) * 128;
+    const float* vL = sVec + (V_L + I) * 128;
+    const float* vMr = sVec + (V_MR + I) * 128;
+    const float* vMc = sVec + (V_MC + I) * 128;
+    const float* vT = sTot + I * 128;
+#pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int c0 = 32 * kb + 8 * lg;
-      float Gr[8], kr[8], qr[8];
+      float kR[8], qR[8], kC[8];
       {
-        const float4* p = reinterpret_cast<const float4*>(sG + r * GS + c0);
-        float4 a0 = p[0], a1 = p[1];
-        Gr[0] = a0.x; Gr[1] = a0.y; Gr[2] = a0.z; Gr[3] = a0.w;
-        Gr[4] = a1.x; Gr[5] = a1.y; Gr[6] = a1.z; Gr[7] = a1.w;
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + r * QS + c0), kr);
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(sQ + r * QS + c0), qr);
-      }
-      if (gate_mode == KDA_GATE_SAFE_SIGMOID) {
-        // diagonal block through the sub-chunk midpoint row m
-        const int m = 16 * I + 8;
-        bf16x8 dKh, dKl, dQ, bKh, bKl;
+        float qf[8], kf[8];
+        unpack_bf16x8(qraw[kb], qf);
+        unpack_bf16x8(kraw[kb], kf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float d = Gr[e] - sG[m * GS + c0 + e];
-          const float df = fast_exp2(d), cf = fast_exp2(-d);
-          const float xk = kr[e] * df, xq = qr[e] * df, xb = kr[e] * cf;
-          const __bf16 hk = (__bf16)xk, hb = (__bf16)xb;
-          dKh[e] = hk; dKl[e] = (__bf16)(xk - (float)hk);
-          dQ[e] = (__bf16)xq;
-          bKh[e] = hb; bKl[e] = (__bf16)(xb - (float)hb);
+          const float R = fast_exp2(G[kb][e]);
+          const float C = fast_exp2(vT[c0 + e] - G[kb][e]);
+          kR[e] = kf[e] * R;
+          qR[e] = qf[e] * R;
+          kC[e] = kf[e] * C;
         }
-        f32x4 a = acc_kk[I];
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dKh, bKh, a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dKh, bKl, a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dKl, bKh, a, 0, 0, 0);
-        acc_kk[I] = a;
-        acc_qk[I] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dQ, bKh, acc_qk[I], 0, 0, 0);
       }
-      if (I > 0) {
-        // off-diagonal blocks (I, J<I) through p = last row of block I-1
-        const int p = 16 * I - 1;
-        half8 aK, aQ;
-        float Gp[8];
+      aK[kb] = to_half8(kR);
+      aQ[kb] = to_half8(qR);
+      {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = qR[e] * vP[c0 + e];
+        *reinterpret_cast<half8*>(blk + OFF_QG + ((size_t)r * DK + c0) * 2) = to_half8(o);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sKEt[(c0 + e) * KES + r] = (_Float16)(kR[e] * vP[c0 + e]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float kd = kC[e] * vL[c0 + e];
+        const _Float16 hh = (_Float16)kd;
+        kdh[kb][e] = hh;
+        kdl[kb][e] = (_Float16)(kd - (float)hh);
+      }
+#pragma unroll
+      for (int Ip = 1; Ip < 4; ++Ip) {
+        if (Ip <= I) continue;
+        const int pair = (Ip * (Ip - 1)) / 2 + I;  // (1,0)=0 (2,0)=1 (2,1)=2 (3,0)=3 (3,1)=4 (3,2)=5
+        float b[8];
+        if (Ip == I + 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) b[e] = kC[e];
+        } else {
+          const float* vD = sVec + (Ip == 2 ? V_D20 : (I == 0 ? V_D30 : V_D31)) * 128;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) b[e] = kC[e] * vD[c0 + e];
+        }
+        *reinterpret_cast<half8*>(sX + ((pair * 4 + kb) * 64 + lane) * 16) = to_half8(b);
+      }
+      if (MODE == KDA_GATE_SAFE_SIGMOID) {
+        // diagonal block on the fp32 MFMA, both sides offset by the midpoint
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          Gp[e] = sG[p * GS + c0 + e];
-          const float rf = fast_exp2(Gr[e] - Gp[e]);
-          aK[e] = (_Float16)(kr[e] * rf);
-          aQ[e] = (_Float16)(qr[e] * rf);
-        }
-        for (int J = 0; J < I; ++J) {
-          const int s = 16 * J + li;
-          float Gs[8], ks[8];
-          const float4* ps = reinterpret_cast<const float4*>(sG + s * GS + c0);
-          float4 b0 = ps[0], b1 = ps[1];
-          Gs[0] = b0.x; Gs[1] = b0.y; Gs[2] = b0.z; Gs[3] = b0.w;
-          Gs[4] = b1.x; Gs[5] = b1.y; Gs[6] = b1.z; Gs[7] = b1.w;
-          unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + s * QS + c0), ks);
-          half8 bK;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bK[e] = (_Float16)(ks[e] * fast_exp2(Gp[e] - Gs[e]));
-          acc_kk[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aK, bK, acc_kk[J], 0, 0, 0);
-          acc_qk[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aQ, bK, acc_qk[J], 0, 0, 0);
+          const float db = kC[e] * vMc[c0 + e];
+          dkk = __builtin_amdgcn_mfma_f32_16x16x4f32(kR[e] * vMr[c0 + e], db, dkk, 0, 0, 0);
+          dqk = __builtin_amdgcn_mfma_f32_16x16x4f32(qR[e] * vMr[c0 + e], db, dqk, 0, 0, 0);
         }
       }
     }
-    if (gate_mode == KDA_GATE_SOFTPLUS) {
-      // diagonal block pairwise: rows i = 16I + 4*lg + rr, column row s = 16I + li
+  }
+  __syncthreads();
+
+  // ---- phase 4: off-diagonal blocks from the mailbox; softplus pairwise diagonal
+  {
+#pragma unroll
+    for (int J = 0; J < 3; ++J) {
+      if (J >= I) continue;
+      const int pair = (I * (I - 1)) / 2 + J;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const half8 b = *reinterpret_cast<const half8*>(sX + ((pair * 4 + kb) * 64 + lane) * 16);
+        okk[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aK[kb], b, okk[J], 0, 0, 0);
+        oqk[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aQ[kb], b, oqk[J], 0, 0, 0);
+      }
+    }
+    if (MODE == KDA_GATE_SOFTPLUS) {
+      const float* sPG = reinterpret_cast<const float*>(smem + L_PG);
+      const uint16_t* sPQb = reinterpret_cast<const uint16_t*>(smem + L_PQ);
+      const uint16_t* sPKb = reinterpret_cast<const uint16_t*>(smem + L_PK);
       const int s = 16 * I + li;
       float kk[4] = {0, 0, 0, 0}, qk[4] = {0, 0, 0, 0};
       for (int c0 = 0; c0 < DK; c0 += 8) {
         float Gs[8], ks[8];
-        const float4* ps = reinterpret_cast<const float4*>(sG + s * GS + c0);
+        const float4* ps = reinterpret_cast<const float4*>(sPG + s * GS + c0);
         float4 b0 = ps[0], b1 = ps[1];
         Gs[0] = b0.x; Gs[1] = b0.y; Gs[2] = b0.z; Gs[3] = b0.w;
         Gs[4] = b1.x; Gs[5] = b1.y; Gs[6] = b1.z; Gs[7] = b1.w;
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + s * QS + c0), ks);
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(sPKb + s * QS + c0), ks);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int ri = 16 * I + 4 * lg + rr;
           float Gi[8], ki[8], qi[8];
-          const float4* pi = reinterpret_cast<const float4*>(sG + ri * GS + c0);
+          const float4* pi = reinterpret_cast<const float4*>(sPG + ri * GS + c0);
           float4 a0 = pi[0], a1 = pi[1];
           Gi[0] = a0.x; Gi[1] = a0.y; Gi[2] = a0.z; Gi[3] = a0.w;
           Gi[4] = a1.x; Gi[5] = a1.y; Gi[6] = a1.z; Gi[7] = a1.w;
-          unpack_bf16x8(*reinterpret_cast<const uint4*>(sK + ri * QS + c0), ki);
-          unpack_bf16x8(*reinterpret_cast<const uint4*>(sQ + ri * QS + c0), qi);
+          unpack_bf16x8(*reinterpret_cast<const uint4*>(sPKb + ri * QS + c0), ki);
+          unpack_bf16x8(*reinterpret_cast<const uint4*>(sPQb + ri * QS + c0), qi);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float ex = fast_exp2(fminf(Gi[e] - Gs[e], 0.0f));
@@ -365,85 +514,54 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           }
         }
       }
-      acc_kk[I] = f32x4{kk[0], kk[1], kk[2], kk[3]};
-      acc_qk[I] = f32x4{qk[0], qk[1], qk[2], qk[3]};
+      dkk = f32x4{kk[0], kk[1], kk[2], kk[3]};
+      dqk = f32x4{qk[0], qk[1], qk[2], qk[3]};
     }
   }
+  __syncthreads();  // mailbox is dead
 
-  // ---- S4: elementwise products straight from Gamma: Q . 2^G (row-major),
-  //          K . 2^G (kept for W), (K . 2^(G_last - G))^T hi/lo, 2^G_last
-  half8 keReg[4];
-  {
-    // Qg rows: item (t, 8 channels)
-    for (int it = 0; it < 4; ++it) {
-      const int item = tid + 256 * it;        // 0..1023
-      const int t = item >> 4, c0 = (item & 15) * 8;
-      float Gt[8], qf[8];
-      const float4* p = reinterpret_cast<const float4*>(sG + t * GS + c0);
-      float4 a0 = p[0], a1 = p[1];
-      Gt[0] = a0.x; Gt[1] = a0.y; Gt[2] = a0.z; Gt[3] = a0.w;
-      Gt[4] = a1.x; Gt[5] = a1.y; Gt[6] = a1.z; Gt[7] = a1.w;
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(sQ + t * QS + c0), qf);
-      half8 o;
+  // ---- phase 4b: (K . 2^(G_63 - G))^T hi then lo through LDS to global [k][t]
+  for (int part = 0; part < 2; ++part) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = (_Float16)(qf[e] * fast_exp2(Gt[e]));
-      *reinterpret_cast<half8*>(blk + OFF_QG + ((size_t)t * DK + c0) * 2) = o;
-    }
-    // transposed items (channel c, 8 consecutive t)
-    for (int it = 0; it < 4; ++it) {
-      const int c = tid & 127, tb = (tid >> 7) + 2 * it;  // tb 0..7
-      const float GL = sG[63 * GS + c];
-      half8 ke, kdh, kdl;
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = tb * 8 + e;
-        const float Gt = sG[t * GS + c];
-        const float kf = bf2f(sK[t * QS + c]);
-        ke[e] = (_Float16)(kf * fast_exp2(Gt));
-        const float kd = kf * fast_exp2(GL - Gt);
-        const _Float16 hi = (_Float16)kd;
-        kdh[e] = hi;
-        kdl[e] = (_Float16)(kd - (float)hi);
-      }
-      keReg[it] = ke;
-      *reinterpret_cast<half8*>(blk + OFF_KDH + ((size_t)c * CH + tb * 8) * 2) = kdh;
-      *reinterpret_cast<half8*>(blk + OFF_KDL + ((size_t)c * CH + tb * 8) * 2) = kdl;
+      for (int e = 0; e < 8; ++e)
+        sKd[(32 * kb + 8 * lg + e) * KES + r] = part == 0 ? kdh[kb][e] : kdl[kb][e];
+    __syncthreads();
+    for (int it = 0; it < 4; ++it) {
+      const int item = tid + 256 * it;  // (k row, 8 t)
+      const int c = item >> 3, t0 = (item & 7) * 8;
+      *reinterpret_cast<half8*>(blk + (part == 0 ? OFF_KDH : OFF_KDL) + ((size_t)c * CH + t0) * 2) =
+          *reinterpret_cast<const half8*>(sKd + c * KES + t0);
     }
-    if (tid < 128) reinterpret_cast<float*>(blk + OFF_GN)[tid] = fast_exp2(sG[63 * GS + tid]);
-    if (tid < 64) {
-      reinterpret_cast<float*>(blk + OFF_QS)[tid] = scale * sRq[tid];
-      reinterpret_cast<float*>(blk + OFF_RK)[tid] = sRk[tid];
-    }
+    __syncthreads();
   }
-  __syncthreads();  // phase A LDS is dead from here
 
-  // ---- S5: Akk, Aqk into LDS (masks, beta, norms); K . 2^G transposed; T = 0
+  // ---- phase 5: Akk (fp32) and Aqk (fp16) into LDS with masks, beta, norms; T = 0
   {
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int row = 16 * I + 4 * lg + rr, col = 16 * J + li;
+        float vkk = 0.0f, vqk = 0.0f;
+        if (J < 3 && J < I) { vkk = okk[J < 3 ? J : 0][rr]; vqk = oqk[J < 3 ? J : 0][rr]; }
+        if (J == I) { vkk = dkk[rr]; vqk = dqk[rr]; }
         float akk = 0.0f, aqk = 0.0f;
         if (J <= I) {
-          if (row > col) akk = acc_kk[J][rr] * sBeta[row] * sRk[row] * sRk[col];
-          if (row >= col) aqk = acc_qk[J][rr] * scale * sRq[row];
+          if (row > col) akk = vkk * sBeta[row] * sRk[row] * sRk[col];
+          if (row >= col) aqk = vqk * scale * sRq[row];
         }
         sA[row * AS + col] = akk;
-        sAq[row * AS + col] = aqk;
+        sAq[row * AQS + col] = (_Float16)aqk;
       }
-    }
-    for (int it = 0; it < 4; ++it) {
-      const int c = tid & 127, tb = (tid >> 7) + 2 * it;
-      *reinterpret_cast<half8*>(sKEt + c * KES + tb * 8) = keReg[it];
     }
     for (int i = tid; i < 64 * AS; i += 256) sT[i] = 0.0f;
   }
   __syncthreads();
 
-  // ---- S6: T = (I + Akk)^-1
+  // ---- phase 6: T = (I + Akk)^-1
   if (lane < 16) {
-    // forward substitution on the diagonal block of this wave, column j = lane
     const int j = lane, o = 16 * wave;
     float xcol[16];
 #pragma unroll
@@ -471,9 +589,9 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
       f32x4 y = f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float a = sT[(16 * Ib + li) * AS + 16 * Ib + 4 * lg + r];
-        y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, z[r], y, 0, 0, 0);
+      for (int rr = 0; rr < 4; ++rr) {
+        const float a = sT[(16 * Ib + li) * AS + 16 * Ib + 4 * lg + rr];
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, z[rr], y, 0, 0, 0);
       }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) sT[(16 * Ib + 4 * lg + rr) * AS + 16 * Jb + li] = -y[rr];
@@ -481,7 +599,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     __syncthreads();
   }
 
-  // ---- S7: W = T diag(b rk) (K . 2^G); T diag(b) hi/lo; Aqk
+  // ---- phase 7: W = T diag(b rk) (K . 2^G); T diag(b) hi/lo; Aqk
   {
     f32x4 accw[8];
 #pragma unroll
@@ -499,25 +617,23 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         accw[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, accw[nt], 0, 0, 0);
       }
     }
-    // T diag(b) and Aqk to global while the products drain
     for (int it = 0; it < 2; ++it) {
-      const int item = tid + 256 * it;  // 0..511 : (row, 8 columns)
+      const int item = tid + 256 * it;  // (row, 8 columns)
       const int row = item >> 3, c0 = (item & 7) * 8;
       bf16x8 th, tl;
-      half8 aq;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = sT[row * AS + c0 + e] * sBeta[c0 + e];
         const __bf16 hv = (__bf16)v;
         th[e] = hv;
         tl[e] = (__bf16)(v - (float)hv);
-        aq[e] = (_Float16)sAq[row * AS + c0 + e];
       }
       *reinterpret_cast<bf16x8*>(blk + OFF_TBH + ((size_t)row * CH + c0) * 2) = th;
       *reinterpret_cast<bf16x8*>(blk + OFF_TBL + ((size_t)row * CH + c0) * 2) = tl;
-      *reinterpret_cast<half8*>(blk + OFF_AQK + ((size_t)row * CH + c0) * 2) = aq;
+      *reinterpret_cast<half8*>(blk + OFF_AQK + ((size_t)row * CH + c0) * 2) =
+          *reinterpret_cast<const half8*>(sAq + row * AQS + c0);
     }
-    __syncthreads();  // all waves are done reading K . 2^G
+    // sA (region X) is dead after the solve: stage -W there
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
@@ -525,7 +641,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         sW[(16 * wave + 4 * lg + rr) * WSS + 16 * nt + li] = (_Float16)(-accw[nt][rr]);
     __syncthreads();
     for (int it = 0; it < 4; ++it) {
-      const int item = tid + 256 * it;  // (row, 8 columns) of 64 x 128
+      const int item = tid + 256 * it;
       const int row = item >> 4, c0 = (item & 15) * 8;
       *reinterpret_cast<half8*>(blk + OFF_WN + ((size_t)row * DK + c0) * 2) =
           *reinterpret_cast<const half8*>(sW + row * WSS + c0);
@@ -601,9 +717,31 @@ struct StateCtx {
   uint16_t* sVt;
 };
 
-// One chunk of the state chain: consumes `cur`, prefetches chunk c+1 into `nxt`.
+// Output rows of a finished chunk, held in registers until the next chunk has
+// waited for its own operands: stores are counted by vmcnt like loads, so a
+// store issued behind the prefetch would make every operand wait include a
+// store round trip.
+struct PendingOut {
+  uint16_t o[2][4];
+  int64_t row0;
+  int len;
+};
+
+__device__ __forceinline__ void store_pending(const PendingOut& pd, uint16_t* __restrict__ out, int Hv, int h,
+                                              int v0, int wave, int li, int lg) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int t = 16 * wave + 4 * lg + rr;
+      if (t < pd.len) out[((size_t)(pd.row0 + t) * Hv + h) * DV + v0 + 16 * nt + li] = pd.o[nt][rr];
+    }
+}
+
+// One chunk of the state chain: consumes `cur`, prefetches chunk c+1 into `nxt`,
+// stores the previous chunk's outputs and leaves this chunk's in `pd`.
 __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2], StateOps& cur, StateOps& nxt,
-                                            const int c) {
+                                            const int c, PendingOut& pd) {
   const uint16_t* __restrict__ v = x.v;
   uint16_t* __restrict__ out = x.out;
   const int64_t bos = x.bos, seqlen = x.seqlen;
@@ -615,6 +753,14 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
   const uint8_t* wsh = x.wsh;
     const int64_t row0 = bos + (int64_t)c * CH;
     const int len = (int)min((int64_t)CH, seqlen - (int64_t)c * CH);
+    // This chunk's V slice -> LDS (transposed).  Its last readers were before
+    // the previous chunk's B2 and its readers here come after B1.  Waiting for
+    // this load here, a whole chunk after it was issued, keeps the prefetch of
+    // the next chunk in flight.
+    store_vt(sVt, cur.vraw, tid);
+    if (c > 0) store_pending(pd, out, Hv, h, v0, wave, li, lg);
+    // prefetch chunk c+1 (issued after the wait above, so nothing waits on it
+    // until the next chunk)
     if (c + 1 < nc) {
       const int64_t r1 = row0 + CH;
       load_ops(nxt, wsh + (size_t)(x0 + c + 1) * BLOCK, wave, li, lg, v, r1,
@@ -670,7 +816,6 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
       *reinterpret_cast<half4*>(sUl + vv * SUS + tt) = lo;
     }
     __syncthreads();  // B2
-    if (c + 1 < nc) store_vt(sVt, nxt.vraw, tid);
     // S <- S Diag(2^G_last) + U'^T (K . 2^(G_last - G))
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -695,16 +840,14 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
       f32x4 o = O[nt] * cur.qs;
       const int nkb = (wave >= 2) ? 2 : 1;
       for (int kb = 0; kb < nkb; ++kb) o = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.aq[kb], uh[kb], o, 0, 0, 0);
-      // store valid rows
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int t = 16 * wave + 4 * lg + rr;
-        if (t < len) {
-          const __bf16 ob = (__bf16)o[rr];
-          out[((size_t)(row0 + t) * Hv + h) * DV + v0 + 16 * nt + li] = *reinterpret_cast<const uint16_t*>(&ob);
-        }
+        const __bf16 ob = (__bf16)o[rr];
+        pd.o[nt][rr] = *reinterpret_cast<const uint16_t*>(&ob);
       }
     }
+    pd.row0 = row0;
+    pd.len = len;
 }
 
 __global__ void __launch_bounds__(256)
@@ -762,13 +905,14 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
   StateOps opA, opB;
   if (nc > 0) {
     load_ops(opA, wsh + (size_t)x0 * BLOCK, wave, li, lg, v, bos, (int)min((int64_t)CH, seqlen), Hv, h, v0, tid);
-    store_vt(sVt, opA.vraw, tid);
   }
   StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, li, lg, sS, sUh, sUl, sVt};
+  PendingOut pd;
   for (int c = 0; c < nc; c += 2) {
-    state_chunk(ctx, S, opA, opB, c);
-    if (c + 1 < nc) state_chunk(ctx, S, opB, opA, c + 1);
+    state_chunk(ctx, S, opA, opB, c, pd);
+    if (c + 1 < nc) state_chunk(ctx, S, opB, opA, c + 1, pd);
   }
+  if (nc > 0) store_pending(pd, out, Hv, h, v0, wave, li, lg);
 
   if (final_dtype != KDA_STATE_NONE) {
 #pragma unroll
@@ -879,9 +1023,9 @@ kda_status kda_fwd_check(const kda_fwd_params* p, const void* q, const void* k, 
     const char* names[] = {"q", "k", "v", "g", "beta", "A_log", "dt_bias", "out"};
     for (int i = 0; i < 8; ++i)
       if (!req[i]) return fail(KDA_ERR_NULL, "%s is NULL", names[i]);
-    const void* al[] = {q, k, v, g, out};
-    const char* aln[] = {"q", "k", "v", "g", "out"};
-    for (int i = 0; i < 5; ++i)
+    const void* al[] = {q, k, v, g, out, dt_bias};
+    const char* aln[] = {"q", "k", "v", "g", "out", "dt_bias"};
+    for (int i = 0; i < 6; ++i)
       if (!aligned16(al[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", aln[i]);
   }
   if (p->init_state_dtype != KDA_STATE_NONE) {
@@ -900,6 +1044,55 @@ kda_status kda_fwd_check(const kda_fwd_params* p, const void* q, const void* k, 
   return KDA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+kda_status launch_intra(const kda_fwd_params* p, const void* q, const void* k, const void* g, const void* beta,
+                        const float* A_log, const float* dt_bias, const int64_t* cu_seqlens, void* workspace,
+                        hipStream_t st) {
+  const bool packed = cu_seqlens != nullptr;
+  const int64_t mc = max_chunks_of(p, packed);
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
+  int* chunk_off = reinterpret_cast<int*>(wsb);
+  uint8_t* blocks = wsb + header_bytes(p);
+  if (packed) hipLaunchKernelGGL(kda_chunk_map_kernel, dim3(1), dim3(64), 0, st, cu_seqlens, p->num_seqs, chunk_off);
+  if (mc > 0) {
+    auto kern = p->gate_mode == KDA_GATE_SAFE_SIGMOID ? kda_intra_kernel<KDA_GATE_SAFE_SIGMOID>
+                                                      : kda_intra_kernel<KDA_GATE_SOFTPLUS>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)mc, (unsigned)p->H_v), dim3(256), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)g, (const uint16_t*)beta,
+                       A_log, dt_bias, cu_seqlens, chunk_off, p->B, p->T, p->num_seqs, p->H_qk, p->H_v,
+                       (int)mc, p->scale, p->lower_bound, blocks);
+  }
+  return KDA_OK;
+}
+
+kda_status launch_state(const kda_fwd_params* p, const void* v, const int64_t* cu_seqlens,
+                        const void* initial_state, void* final_state, void* out, void* workspace, hipStream_t st) {
+  const bool packed = cu_seqlens != nullptr;
+  const int64_t mc = max_chunks_of(p, packed);
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
+  const int* chunk_off = reinterpret_cast<const int*>(wsb);
+  const uint8_t* blocks = wsb + header_bytes(p);
+  const int chains = p->num_seqs * p->H_v;
+  const int groups = (chains + 7) / 8;
+  hipLaunchKernelGGL(kda_state_kernel, dim3((unsigned)(groups * 8 * NSLICE)), dim3(256), 0, st,
+                     (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out,
+                     blocks, p->B, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype, p->final_state_dtype);
+  return KDA_OK;
+}
+
+kda_status launch_status() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 kda_status kda_fwd(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
                    const void* beta, const float* A_log, const float* dt_bias, const int64_t* cu_seqlens,
                    const void* initial_state, void* final_state, void* out, void* workspace,
@@ -908,30 +1101,34 @@ kda_status kda_fwd(const kda_fwd_params* p, const void* q, const void* k, const 
                                out, workspace, workspace_bytes);
   if (s != KDA_OK) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const bool packed = cu_seqlens != nullptr;
-  const int64_t mc = max_chunks_of(p, packed);
-  uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
-  int* chunk_off = reinterpret_cast<int*>(wsb);
-  uint8_t* blocks = wsb + header_bytes(p);
   (void)hipGetLastError();
-  if (packed) {
-    hipLaunchKernelGGL(kda_chunk_map_kernel, dim3(1), dim3(64), 0, st, cu_seqlens, p->num_seqs, chunk_off);
-  }
-  if (mc > 0) {
-    hipLaunchKernelGGL(kda_intra_kernel, dim3((unsigned)mc, (unsigned)p->H_v), dim3(256), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)g, (const uint16_t*)beta,
-                       A_log, dt_bias, cu_seqlens, chunk_off, p->B, p->T, p->num_seqs, p->H_qk, p->H_v,
-                       (int)mc, p->scale, p->lower_bound, p->gate_mode, blocks);
-  }
-  const int chains = p->num_seqs * p->H_v;
-  const int groups = (chains + 7) / 8;
-  hipLaunchKernelGGL(kda_state_kernel, dim3((unsigned)(groups * 8 * NSLICE)), dim3(256), 0, st,
-                     (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out,
-                     (const uint8_t*)blocks, p->B, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype,
-                     p->final_state_dtype);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(KDA_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
-  return KDA_OK;
+  launch_intra(p, q, k, g, beta, A_log, dt_bias, cu_seqlens, workspace, st);
+  launch_state(p, v, cu_seqlens, initial_state, final_state, out, workspace, st);
+  return launch_status();
+}
+
+kda_status kda_fwd_intra(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* A_log, const float* dt_bias, const int64_t* cu_seqlens,
+                         const void* initial_state, void* final_state, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  kda_status s = kda_fwd_check(p, q, k, v, g, beta, A_log, dt_bias, cu_seqlens, initial_state, final_state,
+                               out, workspace, workspace_bytes);
+  if (s != KDA_OK) return s;
+  (void)hipGetLastError();
+  launch_intra(p, q, k, g, beta, A_log, dt_bias, cu_seqlens, workspace, reinterpret_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+kda_status kda_fwd_state(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* A_log, const float* dt_bias, const int64_t* cu_seqlens,
+                         const void* initial_state, void* final_state, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  kda_status s = kda_fwd_check(p, q, k, v, g, beta, A_log, dt_bias, cu_seqlens, initial_state, final_state,
+                               out, workspace, workspace_bytes);
+  if (s != KDA_OK) return s;
+  (void)hipGetLastError();
+  launch_state(p, v, cu_seqlens, initial_state, final_state, out, workspace, reinterpret_cast<hipStream_t>(stream));
+  return launch_status();
 }
 
 const char* kda_status_string(kda_status s) {

@@ -119,7 +119,7 @@ def test_null_pointers(lib, name):
     assert code == (-6 if name == "ws" else -1)
 
 
-@pytest.mark.parametrize("name", ["q", "k", "v", "g", "out", "h0", "hT"])
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "out", "dt_bias", "h0", "hT"])
 def test_misaligned(lib, name):
     assert check(lib, base_params(), shift=name) == -5
 
