@@ -36,6 +36,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "kda.h"
 
 namespace {
@@ -43,6 +45,8 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int CH = 64;      // chunk length
 constexpr int DK = 128;     // key dim
@@ -56,23 +60,33 @@ constexpr float kL2Eps = 1e-6f;
 constexpr float kMinLog2Decay = -1.0e4f;
 
 // Per (v-head, chunk) workspace block, written by the intra kernel and read by
-// the state kernel.  All matrices are row-major in the orientation the state
-// kernel feeds to the MFMA, so its operand loads are 16-byte vectors.
-constexpr size_t OFF_WN = 0;        // -W          fp16 [64 t][128 k]
-constexpr size_t OFF_QG = 16384;    // Q . 2^G     fp16 [64 t][128 k]   (raw q)
-constexpr size_t OFF_KDH = 32768;   // (K . 2^(GL-G))^T hi fp16 [128 k][64 t]  (raw k)
-constexpr size_t OFF_KDL = 49152;   // ... lo
-constexpr size_t OFF_TBH = 65536;   // T diag(b)   bf16 [64 t][64 s] hi
-constexpr size_t OFF_TBL = 73728;   // ... lo
-constexpr size_t OFF_AQK = 81920;   // scale rq_t (Q Kt . 2^(Gt-Gs)) fp16 [64][64], lower incl diag
-constexpr size_t OFF_GN = 90112;    // 2^G_last    fp32 [128]
-constexpr size_t OFF_QS = 90624;    // scale rq_t  fp32 [64]
-constexpr size_t OFF_RK = 90880;    // rk_t        fp32 [64]
-constexpr size_t BLOCK = 91136;
+// the state kernel: 89 fragments of 1 KB.  A fragment is one 16 x 32 tile of
+// a 16-bit MFMA operand in lane order -- lane l = (i = l & 15, g = l >> 4)
+// holds row i and contraction columns 8g..8g+7 (16 bytes) -- so every
+// fragment moves as one contiguous 1 KB load, store or LDS access.
+constexpr int FRAG = 1024;
+constexpr int F_WN = 0;       // -W             (ta 0..3, kb 0..3) fp16  rows t, columns k
+constexpr int F_QG = 16;      // Q . 2^G        (ta, kb)           fp16  raw q
+constexpr int F_TBH = 32;     // T diag(b) hi   (ta, kb 0..1)      bf16  rows t, columns s
+constexpr int F_TBL = 40;     //           lo
+constexpr int F_AQK = 48;     // scale rq_t (Q K^T . 2^(G_t - G_s)), lower incl. diagonal (ta, kb 0..1) fp16
+constexpr int F_VEC = 56;     // 2^G_last f32[128] | scale rq f32[64] | rk f32[64]
+constexpr int F_SHARED = 57;  // fragments 0..56 are shared by all V slices of a chain
+constexpr int F_KD = 57;      // (K . 2^(G_last - G))^T (km 0..7, kb 0..1, hi/lo) fp16 rows k, columns t
+constexpr int NFRAG = 89;
+constexpr size_t BLOCK = (size_t)NFRAG * FRAG;
 static_assert(BLOCK % 256 == 0, "workspace block alignment");
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer resource over [base, base + bytes): loads beyond the range return
+// zero and stores beyond it are dropped by the hardware range check, so tail
+// rows need no branches (and no branch-dependent wait counts).
+constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer descriptor
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
 
 __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -368,7 +382,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       sVec[(V_P + 1) * 128 + c] = fast_exp2(T0);
       sVec[(V_P + 2) * 128 + c] = fast_exp2(T0 + T1);
       sVec[(V_P + 3) * 128 + c] = fast_exp2((T0 + T1) + T2);
-      reinterpret_cast<float*>(blk + OFF_GN)[c] = fast_exp2(((T0 + T1) + T2) + T3);
+      reinterpret_cast<float*>(blk + F_VEC * FRAG)[c] = fast_exp2(((T0 + T1) + T2) + T3);
       sVec[V_D20 * 128 + c] = fast_exp2(T1);
       sVec[V_D30 * 128 + c] = fast_exp2(T1 + T2);
       sVec[V_D31 * 128 + c] = fast_exp2(T2);
@@ -386,8 +400,8 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
     if (tid < 64) {
-      reinterpret_cast<float*>(blk + OFF_QS)[tid] = scale * sRq[tid];
-      reinterpret_cast<float*>(blk + OFF_RK)[tid] = sRk[tid];
+      reinterpret_cast<float*>(blk + F_VEC * FRAG)[128 + tid] = scale * sRq[tid];
+      reinterpret_cast<float*>(blk + F_VEC * FRAG)[192 + tid] = sRk[tid];
     }
   }
   __syncthreads();
@@ -430,7 +444,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = qR[e] * vP[c0 + e];
-        *reinterpret_cast<half8*>(blk + OFF_QG + ((size_t)r * DK + c0) * 2) = to_half8(o);
+        *reinterpret_cast<half8*>(blk + (F_QG + I * 4 + kb) * FRAG + lane * 16) = to_half8(o);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) sKEt[(c0 + e) * KES + r] = (_Float16)(kR[e] * vP[c0 + e]);
@@ -529,10 +543,11 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         sKd[(32 * kb + 8 * lg + e) * KES + r] = part == 0 ? kdh[kb][e] : kdl[kb][e];
     __syncthreads();
     for (int it = 0; it < 4; ++it) {
-      const int item = tid + 256 * it;  // (k row, 8 t)
-      const int c = item >> 3, t0 = (item & 7) * 8;
-      *reinterpret_cast<half8*>(blk + (part == 0 ? OFF_KDH : OFF_KDL) + ((size_t)c * CH + t0) * 2) =
-          *reinterpret_cast<const half8*>(sKd + c * KES + t0);
+      const int item = tid + 256 * it;  // fragment (km, kb) x lane
+      const int fr = item >> 6, ln = item & 63;
+      const int krow = 16 * (fr >> 1) + (ln & 15), t0 = 32 * (fr & 1) + 8 * (ln >> 4);
+      *reinterpret_cast<half8*>(blk + (F_KD + fr * 2 + part) * FRAG + ln * 16) =
+          *reinterpret_cast<const half8*>(sKd + krow * KES + t0);
     }
     __syncthreads();
   }
@@ -618,8 +633,9 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
     for (int it = 0; it < 2; ++it) {
-      const int item = tid + 256 * it;  // (row, 8 columns)
-      const int row = item >> 3, c0 = (item & 7) * 8;
+      const int item = tid + 256 * it;  // fragment (ta, kb) x lane
+      const int fr = item >> 6, ln = item & 63;
+      const int row = 16 * (fr >> 1) + (ln & 15), c0 = 32 * (fr & 1) + 8 * (ln >> 4);
       bf16x8 th, tl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -628,9 +644,9 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         th[e] = hv;
         tl[e] = (__bf16)(v - (float)hv);
       }
-      *reinterpret_cast<bf16x8*>(blk + OFF_TBH + ((size_t)row * CH + c0) * 2) = th;
-      *reinterpret_cast<bf16x8*>(blk + OFF_TBL + ((size_t)row * CH + c0) * 2) = tl;
-      *reinterpret_cast<half8*>(blk + OFF_AQK + ((size_t)row * CH + c0) * 2) =
+      *reinterpret_cast<bf16x8*>(blk + (F_TBH + fr) * FRAG + ln * 16) = th;
+      *reinterpret_cast<bf16x8*>(blk + (F_TBL + fr) * FRAG + ln * 16) = tl;
+      *reinterpret_cast<half8*>(blk + (F_AQK + fr) * FRAG + ln * 16) =
           *reinterpret_cast<const half8*>(sAq + row * AQS + c0);
     }
     // sA (region X) is dead after the solve: stage -W there
@@ -641,9 +657,10 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         sW[(16 * wave + 4 * lg + rr) * WSS + 16 * nt + li] = (_Float16)(-accw[nt][rr]);
     __syncthreads();
     for (int it = 0; it < 4; ++it) {
-      const int item = tid + 256 * it;
-      const int row = item >> 4, c0 = (item & 15) * 8;
-      *reinterpret_cast<half8*>(blk + OFF_WN + ((size_t)row * DK + c0) * 2) =
+      const int item = tid + 256 * it;  // fragment (ta, kb) x lane
+      const int fr = item >> 6, ln = item & 63;
+      const int row = 16 * (fr >> 2) + (ln & 15), c0 = 32 * (fr & 3) + 8 * (ln >> 4);
+      *reinterpret_cast<half8*>(blk + (F_WN + fr) * FRAG + ln * 16) =
           *reinterpret_cast<const half8*>(sW + row * WSS + c0);
     }
   }
@@ -651,58 +668,79 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
 // ---------------------------------------------------------------------------
 // inter-chunk state kernel
+//
+// One workgroup of 8 waves per (sequence, v-head, 32-wide V slice), sequential
+// over the sequence's chunks with the fp32 state slice S^T[k][v] in registers
+// (wave w owns key rows 16w..16w+15).  Per chunk:
+//     U = T diag(b) V - W S^T          (wave w: rows 16*(w>>1).., V tile w&1)
+//     O = qs . (Q . 2^G) S^T + Aqk U'   with U' = rk . U
+//     S <- S Diag(2^G_last) + U'^T (K . 2^(G_last - G))
+// The 57 shared fragments of a chunk (W, Q . 2^G, T diag(b), Aqk, vectors) are
+// loaded two chunks ahead, one eighth per wave, into registers and published
+// through one LDS buffer at the start of the chunk; each wave keeps its own
+// four (K . 2^(G_last - G))^T fragments in registers.  Streaming from 8 waves
+// keeps enough requests in flight per CU for the L2-shared operands of the V
+// slices of one chain (dispatched to the same XCD).
+constexpr int SWAVES = 8;
 constexpr int SSS = 136;  // sS row stride (fp16), S^T slice stored as [v][k]
-constexpr int SUS = 72;   // sU / sVt row stride
+constexpr int SUS = 72;   // sU / sVt row stride (16-bit)
+constexpr int RING_FR = 8;  // shared fragments loaded per wave (the 57 spread over 8 waves)
 
-struct StateOps {
-  half8 wn[4], qg[4], aq[2];
-  half8 kdh[2][2], kdl[2][2];
-  bf16x8 tbh[2], tbl[2];
-  f32x4 gn[2], qs, rk;
-  uint4 vraw;
+struct ChunkRegs {
+  // shared fragments f = min(wave + 8 j, 56), j = 0..7 (named members: register
+  // arrays indexed before unrolling would be left in scratch memory)
+  u32x4 r0, r1, r2, r3, r4, r5, r6, r7;
+  u32x4 kd0, kd1, kd2, kd3;  // this wave's Kd^T fragments: (kb 0, hi) (kb 0, lo) (kb 1, hi) (kb 1, lo)
+  u32x2 vraw;                // 4 values of the V slice: row tid >> 3, columns 4 (tid & 7) ..
+  template <int J> __device__ __forceinline__ u32x4& ring() {
+    static_assert(J >= 0 && J < RING_FR, "ring index");
+    if constexpr (J == 0) return r0; else if constexpr (J == 1) return r1; else if constexpr (J == 2) return r2;
+    else if constexpr (J == 3) return r3; else if constexpr (J == 4) return r4; else if constexpr (J == 5) return r5;
+    else if constexpr (J == 6) return r6; else return r7;
+  }
 };
 
-__device__ __forceinline__ void load_ops(StateOps& o, const uint8_t* blk, int wave, int li, int lg,
-                                         const uint16_t* __restrict__ v, int64_t row0, int len,
-                                         int Hv, int h, int v0, int tid) {
-  const int t = 16 * wave + li;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    o.wn[kb] = *reinterpret_cast<const half8*>(blk + OFF_WN + ((size_t)t * DK + 32 * kb + 8 * lg) * 2);
-    o.qg[kb] = *reinterpret_cast<const half8*>(blk + OFF_QG + ((size_t)t * DK + 32 * kb + 8 * lg) * 2);
+template <int J = 0, typename F>
+__device__ __forceinline__ void for_ring(F&& f) {
+  if constexpr (J < RING_FR) {
+    f(std::integral_constant<int, J>{});
+    for_ring<J + 1>(f);
   }
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    o.aq[kb] = *reinterpret_cast<const half8*>(blk + OFF_AQK + ((size_t)t * CH + 32 * kb + 8 * lg) * 2);
-    o.tbh[kb] = *reinterpret_cast<const bf16x8*>(blk + OFF_TBH + ((size_t)t * CH + 32 * kb + 8 * lg) * 2);
-    o.tbl[kb] = *reinterpret_cast<const bf16x8*>(blk + OFF_TBL + ((size_t)t * CH + 32 * kb + 8 * lg) * 2);
-  }
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int kr = 32 * wave + 16 * mt + li;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      o.kdh[mt][kb] = *reinterpret_cast<const half8*>(blk + OFF_KDH + ((size_t)kr * CH + 32 * kb + 8 * lg) * 2);
-      o.kdl[mt][kb] = *reinterpret_cast<const half8*>(blk + OFF_KDL + ((size_t)kr * CH + 32 * kb + 8 * lg) * 2);
-    }
-    o.gn[mt] = *reinterpret_cast<const f32x4*>(blk + OFF_GN + (size_t)(32 * wave + 16 * mt + 4 * lg) * 4);
-  }
-  o.qs = *reinterpret_cast<const f32x4*>(blk + OFF_QS + (size_t)(16 * wave + 4 * lg) * 4);
-  o.rk = *reinterpret_cast<const f32x4*>(blk + OFF_RK + (size_t)(16 * wave + 4 * lg) * 4);
-  // V slice: thread -> (row s = tid >> 2, 8 columns)
-  const int s = tid >> 2, cq = tid & 3;
-  if (s < len) o.vraw = *reinterpret_cast<const uint4*>(v + ((size_t)(row0 + s) * Hv + h) * DV + v0 + 8 * cq);
-  else o.vraw = make_uint4(0, 0, 0, 0);
 }
 
-__device__ __forceinline__ void store_vt(uint16_t* sVt, const uint4& vr, int tid) {
-  const int s = tid >> 2, cq = tid & 3;
-  const uint32_t w[4] = {vr.x, vr.y, vr.z, vr.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sVt[(8 * cq + 2 * i) * SUS + s] = (uint16_t)(w[i] & 0xffffu);
-    sVt[(8 * cq + 2 * i + 1) * SUS + s] = (uint16_t)(w[i] >> 16);
+// The prefetch of one chunk, issued in three parts spread over the previous
+// chunk's work so the memory pipeline drains while the wave computes.
+template <int PART>
+__device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk, int wave, int lane,
+                                                const uint16_t* __restrict__ v, int64_t row0, int len, int Hv, int h,
+                                                int v0, int tid) {
+  if constexpr (PART == 0 || PART == 1) {
+    for_ring([&](auto J) {
+      if constexpr ((int)J / 4 == PART) {
+        const int fr = min(wave + 8 * (int)J, F_SHARED - 1);
+        o.template ring<J>() = *reinterpret_cast<const u32x4*>(blk + fr * FRAG + lane * 16);
+      }
+    });
+  } else {
+    const uint8_t* kdb = blk + (F_KD + wave * 4) * FRAG + lane * 16;
+    o.kd0 = *reinterpret_cast<const u32x4*>(kdb);
+    o.kd1 = *reinterpret_cast<const u32x4*>(kdb + FRAG);
+    o.kd2 = *reinterpret_cast<const u32x4*>(kdb + 2 * FRAG);
+    o.kd3 = *reinterpret_cast<const u32x4*>(kdb + 3 * FRAG);
+    // rows s >= len lie beyond the buffer range and read as zero
+    const int s = tid >> 3, cq = tid & 7;
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + ((size_t)row0 * Hv + h) * DV + v0, (uint32_t)len * Hv * DV * 2);
+    const auto vv = __builtin_amdgcn_raw_buffer_load_b64(rv, (s * Hv * DV + 4 * cq) * 2, 0, 0);
+    o.vraw = __builtin_bit_cast(u32x2, vv);
   }
+}
+
+__device__ __forceinline__ void load_chunk(ChunkRegs& o, const uint8_t* blk, int wave, int lane,
+                                           const uint16_t* __restrict__ v, int64_t row0, int len, int Hv, int h,
+                                           int v0, int tid) {
+  load_chunk_part<0>(o, blk, wave, lane, v, row0, len, Hv, h, v0, tid);
+  load_chunk_part<1>(o, blk, wave, lane, v, row0, len, Hv, h, v0, tid);
+  load_chunk_part<2>(o, blk, wave, lane, v, row0, len, Hv, h, v0, tid);
 }
 
 struct StateCtx {
@@ -710,151 +748,185 @@ struct StateCtx {
   uint16_t* __restrict__ out;
   const uint8_t* wsh;
   int64_t bos, seqlen;
-  int x0, nc, Hv, h, v0, tid, wave, li, lg;
+  int x0, nc, Hv, h, v0, tid, wave, lane, li, lg;
+  uint8_t* ring;
   _Float16* sS;
   _Float16* sUh;
   _Float16* sUl;
   uint16_t* sVt;
 };
 
-// Output rows of a finished chunk, held in registers until the next chunk has
-// waited for its own operands: stores are counted by vmcnt like loads, so a
-// store issued behind the prefetch would make every operand wait include a
-// store round trip.
+// Output tile of a finished chunk, held in registers and stored at the start
+// of the next chunk, before that chunk's prefetch: stores count in vmcnt like
+// loads, so a store queued behind a prefetch would lengthen the operand wait.
 struct PendingOut {
-  uint16_t o[2][4];
+  uint16_t o[4];
   int64_t row0;
   int len;
 };
 
 __device__ __forceinline__ void store_pending(const PendingOut& pd, uint16_t* __restrict__ out, int Hv, int h,
-                                              int v0, int wave, int li, int lg) {
+                                              int v0, int ta, int vb, int li, int lg) {
+  // rows t >= len fall outside the buffer range and are dropped
+  const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(out + ((size_t)pd.row0 * Hv + h) * DV + v0, (uint32_t)pd.len * Hv * DV * 2);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int rr = 0; rr < 4; ++rr) {
+    const int t = 16 * ta + 4 * lg + rr;
+    __builtin_amdgcn_raw_buffer_store_b16((short)pd.o[rr], ro, (t * Hv * DV + 16 * vb + li) * 2, 0, 0);
+  }
+}
+
+__device__ __forceinline__ int chunk_len(const StateCtx& x, int c) {
+  return (int)min((int64_t)CH, x.seqlen - (int64_t)c * CH);
+}
+
+template <typename V8>
+__device__ __forceinline__ V8 ring_frag(const uint8_t* ring, int fr, int lane) {
+  return *reinterpret_cast<const V8*>(ring + fr * FRAG + lane * 16);
+}
+
+// One chunk of the state chain: `cur` holds chunk c (loaded two chunks ago),
+// `n2` receives chunk c+2.
+__device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2], ChunkRegs& cur, ChunkRegs& n2,
+                                            const int c, PendingOut& pd) {
+  const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
+  const int ta = wave >> 1, vb = wave & 1;
+  const int64_t row0 = x.bos + (int64_t)c * CH;
+  // 1. publish this chunk's shared fragments, V slice and the current state.
+  // Every reader of these buffers in the previous chunk was before its B2.
+  for_ring([&](auto J) {
+    const int fr = min(wave + 8 * (int)J, F_SHARED - 1);
+    *reinterpret_cast<u32x4*>(x.ring + fr * FRAG + lane * 16) = cur.template ring<J>();
+  });
+  {
+    const int s = tid >> 3, cq = tid & 7;
+    const uint32_t w2[2] = {cur.vraw[0], cur.vraw[1]};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      x.sVt[(4 * cq + 2 * i) * SUS + s] = (uint16_t)(w2[i] & 0xffffu);
+      x.sVt[(4 * cq + 2 * i + 1) * SUS + s] = (uint16_t)(w2[i] >> 16);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int kk = 16 * wave + 4 * lg, vv = 16 * nt + li;
+    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+    half4 hv = {(_Float16)S[nt][0], (_Float16)S[nt][1], (_Float16)S[nt][2], (_Float16)S[nt][3]};
+    *reinterpret_cast<half4*>(x.sS + vv * SSS + kk) = hv;
+  }
+  // 2. the previous chunk's outputs (none before the first chunk: len 0), then
+  //    the first part of the prefetch of chunk c+2 (clamped, so every chunk
+  //    queues the same operations)
+  store_pending(pd, x.out, x.Hv, x.h, x.v0, ta, vb, li, lg);
+  const int cp2 = min(c + 2, x.nc - 1);
+  const uint8_t* blk2 = x.wsh + (size_t)(x.x0 + cp2) * BLOCK;
+  const int64_t row2 = x.bos + (int64_t)cp2 * CH;
+  const int len2 = chunk_len(x, cp2);
+  load_chunk_part<0>(n2, blk2, wave, lane, x.v, row2, len2, x.Hv, x.h, x.v0, tid);
+  __syncthreads();  // B1
+  // 3. everything this wave needs from the shared buffer, read before B2
+  half8 wn[4], qg[4], aq[2];
+  bf16x8 tbh[2], tbl[2];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    wn[kb] = ring_frag<half8>(x.ring, F_WN + ta * 4 + kb, lane);
+    qg[kb] = ring_frag<half8>(x.ring, F_QG + ta * 4 + kb, lane);
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    tbh[kb] = ring_frag<bf16x8>(x.ring, F_TBH + ta * 2 + kb, lane);
+    tbl[kb] = ring_frag<bf16x8>(x.ring, F_TBL + ta * 2 + kb, lane);
+    aq[kb] = ring_frag<half8>(x.ring, F_AQK + ta * 2 + kb, lane);
+  }
+  const float* vec = reinterpret_cast<const float*>(x.ring + F_VEC * FRAG);
+  const f32x4 gn = *reinterpret_cast<const f32x4*>(vec + 16 * wave + 4 * lg);
+  const f32x4 qs = *reinterpret_cast<const f32x4*>(vec + 128 + 16 * ta + 4 * lg);
+  const f32x4 rk = *reinterpret_cast<const f32x4*>(vec + 192 + 16 * ta + 4 * lg);
+  // U = T diag(b) V - W S^T ; O = (Q . 2^G) S^T   (rows 16 ta.., V tile vb)
+  f32x4 U, O;
+  {
+    f32x4 u0 = f32x4{0, 0, 0, 0}, u1 = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 vbf = *reinterpret_cast<const bf16x8*>(x.sVt + (16 * vb + li) * SUS + 32 * kb + 8 * lg);
+      u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tbh[kb], vbf, u0, 0, 0, 0);
+      u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tbl[kb], vbf, u1, 0, 0, 0);
+    }
+    half8 sb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vb + li) * SSS + 32 * kb + 8 * lg);
+    u0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wn[0], sb[0], u0, 0, 0, 0);
+    u1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wn[1], sb[1], u1, 0, 0, 0);
+    u0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wn[2], sb[2], u0, 0, 0, 0);
+    u1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wn[3], sb[3], u1, 0, 0, 0);
+    U = u0 + u1;
+    f32x4 o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
+    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qg[0], sb[0], o0, 0, 0, 0);
+    o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qg[1], sb[1], o1, 0, 0, 0);
+    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qg[2], sb[2], o0, 0, 0, 0);
+    o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qg[3], sb[3], o1, 0, 0, 0);
+    O = (o0 + o1) * qs;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load_chunk_part<1>(n2, blk2, wave, lane, x.v, row2, len2, x.Hv, x.h, x.v0, tid);
+  __builtin_amdgcn_sched_barrier(0);
+  // 4. U' = rk . U -> LDS hi/lo, transposed [v][t]
+  {
+    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+    half4 hi, lo;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int t = 16 * wave + 4 * lg + rr;
-      if (t < pd.len) out[((size_t)(pd.row0 + t) * Hv + h) * DV + v0 + 16 * nt + li] = pd.o[nt][rr];
+      const float up = U[rr] * rk[rr];
+      const _Float16 hh = (_Float16)up;
+      hi[rr] = hh;
+      lo[rr] = (_Float16)(up - (float)hh);
     }
+    const int vv = 16 * vb + li, tt = 16 * ta + 4 * lg;
+    *reinterpret_cast<half4*>(x.sUh + vv * SUS + tt) = hi;
+    *reinterpret_cast<half4*>(x.sUl + vv * SUS + tt) = lo;
+  }
+  __syncthreads();  // B2
+  // 5. S <- S Diag(2^G_last) + U'^T Kd ;  O += Aqk U'
+  __builtin_amdgcn_sched_barrier(0);
+  load_chunk_part<2>(n2, blk2, wave, lane, x.v, row2, len2, x.Hv, x.h, x.v0, tid);
+  __builtin_amdgcn_sched_barrier(0);
+  const half8 kdh0 = __builtin_bit_cast(half8, cur.kd0);
+  const half8 kdl0 = __builtin_bit_cast(half8, cur.kd1);
+  const half8 kdh1 = __builtin_bit_cast(half8, cur.kd2);
+  const half8 kdl1 = __builtin_bit_cast(half8, cur.kd3);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const half8 uh0 = *reinterpret_cast<const half8*>(x.sUh + (16 * nt + li) * SUS + 8 * lg);
+    const half8 uh1 = *reinterpret_cast<const half8*>(x.sUh + (16 * nt + li) * SUS + 32 + 8 * lg);
+    const half8 ul0 = *reinterpret_cast<const half8*>(x.sUl + (16 * nt + li) * SUS + 8 * lg);
+    const half8 ul1 = *reinterpret_cast<const half8*>(x.sUl + (16 * nt + li) * SUS + 32 + 8 * lg);
+    f32x4 sa = S[nt] * gn, sb2 = f32x4{0, 0, 0, 0};
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdh0, uh0, sa, 0, 0, 0);
+    sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdh1, uh1, sb2, 0, 0, 0);
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdh0, ul0, sa, 0, 0, 0);
+    sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdh1, ul1, sb2, 0, 0, 0);
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdl0, uh0, sa, 0, 0, 0);
+    sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdl1, uh1, sb2, 0, 0, 0);
+    S[nt] = sa + sb2;
+    if (nt == vb) {
+      O = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[0], uh0, O, 0, 0, 0);
+      if (ta >= 2) O = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[1], uh1, O, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    pd.o[rr] = __builtin_bit_cast(uint16_t, (__bf16)O[rr]);
+  }
+  pd.row0 = row0;
+  pd.len = chunk_len(x, c);
 }
 
-// One chunk of the state chain: consumes `cur`, prefetches chunk c+1 into `nxt`,
-// stores the previous chunk's outputs and leaves this chunk's in `pd`.
-__device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2], StateOps& cur, StateOps& nxt,
-                                            const int c, PendingOut& pd) {
-  const uint16_t* __restrict__ v = x.v;
-  uint16_t* __restrict__ out = x.out;
-  const int64_t bos = x.bos, seqlen = x.seqlen;
-  const int x0 = x.x0, nc = x.nc, Hv = x.Hv, h = x.h, v0 = x.v0, tid = x.tid, wave = x.wave, li = x.li, lg = x.lg;
-  _Float16* sS = x.sS;
-  _Float16* sUh = x.sUh;
-  _Float16* sUl = x.sUl;
-  uint16_t* sVt = x.sVt;
-  const uint8_t* wsh = x.wsh;
-    const int64_t row0 = bos + (int64_t)c * CH;
-    const int len = (int)min((int64_t)CH, seqlen - (int64_t)c * CH);
-    // This chunk's V slice -> LDS (transposed).  Its last readers were before
-    // the previous chunk's B2 and its readers here come after B1.  Waiting for
-    // this load here, a whole chunk after it was issued, keeps the prefetch of
-    // the next chunk in flight.
-    store_vt(sVt, cur.vraw, tid);
-    if (c > 0) store_pending(pd, out, Hv, h, v0, wave, li, lg);
-    // prefetch chunk c+1 (issued after the wait above, so nothing waits on it
-    // until the next chunk)
-    if (c + 1 < nc) {
-      const int64_t r1 = row0 + CH;
-      load_ops(nxt, wsh + (size_t)(x0 + c + 1) * BLOCK, wave, li, lg, v, r1,
-               (int)min((int64_t)CH, seqlen - (int64_t)(c + 1) * CH), Hv, h, v0, tid);
-    }
-    // S^T slice -> LDS as fp16 [v][k]
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int kk = 32 * wave + 16 * mt + 4 * lg, vv = 16 * nt + li;
-        _Float16* d = sS + vv * SSS + kk;
-        typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-        half4 hv = {(_Float16)S[mt][nt][0], (_Float16)S[mt][nt][1], (_Float16)S[mt][nt][2], (_Float16)S[mt][nt][3]};
-        *reinterpret_cast<half4*>(d) = hv;
-      }
-    __syncthreads();  // B1
-    // U = T diag(b) V - W S^T ;  O = (Q . 2^G) S^T   for rows t = 16*wave + ...
-    f32x4 U[2], O[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      f32x4 u = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(sVt + (16 * nt + li) * SUS + 32 * kb + 8 * lg);
-        u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.tbh[kb], b, u, 0, 0, 0);
-        u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.tbl[kb], b, u, 0, 0, 0);
-      }
-      f32x4 o = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const half8 b = *reinterpret_cast<const half8*>(sS + (16 * nt + li) * SSS + 32 * kb + 8 * lg);
-        u = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.wn[kb], b, u, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.qg[kb], b, o, 0, 0, 0);
-      }
-      U[nt] = u;
-      O[nt] = o;
-    }
-    // U' = rk . U  -> LDS hi/lo, transposed [v][t]
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-      half4 hi, lo;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float up = U[nt][rr] * cur.rk[rr];
-        const _Float16 hh = (_Float16)up;
-        hi[rr] = hh;
-        lo[rr] = (_Float16)(up - (float)hh);
-      }
-      const int vv = 16 * nt + li, tt = 16 * wave + 4 * lg;
-      *reinterpret_cast<half4*>(sUh + vv * SUS + tt) = hi;
-      *reinterpret_cast<half4*>(sUl + vv * SUS + tt) = lo;
-    }
-    __syncthreads();  // B2
-    // S <- S Diag(2^G_last) + U'^T (K . 2^(G_last - G))
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      half8 uh[2], ul[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        uh[kb] = *reinterpret_cast<const half8*>(sUh + (16 * nt + li) * SUS + 32 * kb + 8 * lg);
-        ul[kb] = *reinterpret_cast<const half8*>(sUl + (16 * nt + li) * SUS + 32 * kb + 8 * lg);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x4 s = S[mt][nt] * cur.gn[mt];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.kdh[mt][kb], uh[kb], s, 0, 0, 0);
-          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.kdh[mt][kb], ul[kb], s, 0, 0, 0);
-          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.kdl[mt][kb], uh[kb], s, 0, 0, 0);
-        }
-        S[mt][nt] = s;
-      }
-      // O = qs . (Q . 2^G) S^T + Aqk U'
-      f32x4 o = O[nt] * cur.qs;
-      const int nkb = (wave >= 2) ? 2 : 1;
-      for (int kb = 0; kb < nkb; ++kb) o = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur.aq[kb], uh[kb], o, 0, 0, 0);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const __bf16 ob = (__bf16)o[rr];
-        pd.o[nt][rr] = *reinterpret_cast<const uint16_t*>(&ob);
-      }
-    }
-    pd.row0 = row0;
-    pd.len = len;
-}
-
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * SWAVES, 1)
 kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
                  const int* __restrict__ chunk_off, const void* __restrict__ h0, void* __restrict__ hT,
                  uint16_t* __restrict__ out, const uint8_t* __restrict__ ws,
                  int B, int T, int N, int Hv, int max_chunks, int init_dtype, int final_dtype) {
+  __shared__ __attribute__((aligned(16))) uint8_t sRing[F_SHARED * FRAG];
   __shared__ __attribute__((aligned(16))) _Float16 sS[VS * SSS];
   __shared__ __attribute__((aligned(16))) _Float16 sUh[VS * SUS];
   __shared__ __attribute__((aligned(16))) _Float16 sUl[VS * SUS];
@@ -882,56 +954,61 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
     x0 = chunk_off[n]; nc = chunk_off[n + 1] - x0;
   }
 
-  // state tiles: S^T[k][v], k = 32*wave + 16*mt + 4*lg + r, v = v0 + 16*nt + li
-  f32x4 S[2][2];
+  // state tiles: S^T[k][v], k = 16*wave + 4*lg + r, v = v0 + 16*nt + li
+  f32x4 S[2];
   const size_t sbase = ((size_t)n * Hv + h) * DV * DK;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int kk = 32 * wave + 16 * mt + 4 * lg, vv = v0 + 16 * nt + li;
-      f32x4 s = f32x4{0, 0, 0, 0};
-      if (init_dtype == KDA_STATE_F32) {
-        s = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(h0) + sbase + (size_t)vv * DK + kk);
-      } else if (init_dtype == KDA_STATE_BF16) {
-        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(h0) + sbase + (size_t)vv * DK + kk);
-        s = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                  __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
-      }
-      S[mt][nt] = s;
+  for (int nt = 0; nt < 2; ++nt) {
+    const int kk = 16 * wave + 4 * lg, vv = v0 + 16 * nt + li;
+    f32x4 s = f32x4{0, 0, 0, 0};
+    if (init_dtype == KDA_STATE_F32) {
+      s = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(h0) + sbase + (size_t)vv * DK + kk);
+    } else if (init_dtype == KDA_STATE_BF16) {
+      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(h0) + sbase + (size_t)vv * DK + kk);
+      s = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
     }
+    S[nt] = s;
+  }
 
   const uint8_t* wsh = ws + (size_t)h * max_chunks * BLOCK;
-  StateOps opA, opB;
+  StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, lane, li, lg, sRing, sS, sUh, sUl, sVt};
+  ChunkRegs rA, rB, rC;
   if (nc > 0) {
-    load_ops(opA, wsh + (size_t)x0 * BLOCK, wave, li, lg, v, bos, (int)min((int64_t)CH, seqlen), Hv, h, v0, tid);
+    load_chunk(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
+    const int c1 = min(1, nc - 1);
+    load_chunk(rB, wsh + (size_t)(x0 + c1) * BLOCK, wave, lane, v, bos + (int64_t)c1 * CH, chunk_len(ctx, c1), Hv,
+               h, v0, tid);
   }
-  StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, li, lg, sS, sUh, sUl, sVt};
   PendingOut pd;
-  for (int c = 0; c < nc; c += 2) {
-    state_chunk(ctx, S, opA, opB, c, pd);
-    if (c + 1 < nc) state_chunk(ctx, S, opB, opA, c + 1, pd);
+  pd.row0 = bos;
+  pd.len = 0;
+  int c = 0;
+  for (; c + 3 <= nc; c += 3) {
+    state_chunk(ctx, S, rA, rC, c, pd);
+    state_chunk(ctx, S, rB, rA, c + 1, pd);
+    state_chunk(ctx, S, rC, rB, c + 2, pd);
   }
-  if (nc > 0) store_pending(pd, out, Hv, h, v0, wave, li, lg);
+  if (c < nc) state_chunk(ctx, S, rA, rC, c, pd);
+  if (c + 1 < nc) state_chunk(ctx, S, rB, rA, c + 1, pd);
+  store_pending(pd, out, Hv, h, v0, wave >> 1, wave & 1, li, lg);
 
   if (final_dtype != KDA_STATE_NONE) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int nt = 0; nt < 2; ++nt) {
+      const int kk = 16 * wave + 4 * lg, vv = v0 + 16 * nt + li;
+      if (final_dtype == KDA_STATE_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(hT) + sbase + (size_t)vv * DK + kk) = S[nt];
+      } else {
+        __bf16 bb[4];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int kk = 32 * wave + 16 * mt + 4 * lg, vv = v0 + 16 * nt + li;
-        if (final_dtype == KDA_STATE_F32) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(hT) + sbase + (size_t)vv * DK + kk) = S[mt][nt];
-        } else {
-          __bf16 b[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) b[r] = (__bf16)S[mt][nt][r];
-          uint2 u;
-          u.x = (uint32_t)(*reinterpret_cast<uint16_t*>(&b[0])) | ((uint32_t)(*reinterpret_cast<uint16_t*>(&b[1])) << 16);
-          u.y = (uint32_t)(*reinterpret_cast<uint16_t*>(&b[2])) | ((uint32_t)(*reinterpret_cast<uint16_t*>(&b[3])) << 16);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(hT) + sbase + (size_t)vv * DK + kk) = u;
-        }
+        for (int r = 0; r < 4; ++r) bb[r] = (__bf16)S[nt][r];
+        uint2 u;
+        u.x = (uint32_t)(*reinterpret_cast<uint16_t*>(&bb[0])) | ((uint32_t)(*reinterpret_cast<uint16_t*>(&bb[1])) << 16);
+        u.y = (uint32_t)(*reinterpret_cast<uint16_t*>(&bb[2])) | ((uint32_t)(*reinterpret_cast<uint16_t*>(&bb[3])) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(hT) + sbase + (size_t)vv * DK + kk) = u;
       }
+    }
   }
 }
 
@@ -1077,7 +1154,7 @@ kda_status launch_state(const kda_fwd_params* p, const void* v, const int64_t* c
   const uint8_t* blocks = wsb + header_bytes(p);
   const int chains = p->num_seqs * p->H_v;
   const int groups = (chains + 7) / 8;
-  hipLaunchKernelGGL(kda_state_kernel, dim3((unsigned)(groups * 8 * NSLICE)), dim3(256), 0, st,
+  hipLaunchKernelGGL(kda_state_kernel, dim3((unsigned)(groups * 8 * NSLICE)), dim3(64 * SWAVES), 0, st,
                      (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out,
                      blocks, p->B, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype, p->final_state_dtype);
   return KDA_OK;
