@@ -305,27 +305,42 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const float A_exp = expf(A_log[h]);
     const float lb_log2e = lower_bound * kLog2e;
     const int64_t row = cp.row0 + r;
+    // All input loads are issued before any use, as range-checked buffer loads:
+    // rows at or beyond the chunk length read as zero, so no branch (and no
+    // exposed latency per k-block) is needed.
+    const uint32_t vrow = (uint32_t)li;
+    const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g + ((size_t)(cp.row0 + 16 * I) * Hv + h) * DK,
+                                                  (uint32_t)max(0, min(16, cp.len - 16 * I)) * Hv * DK * 2);
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + ((size_t)(cp.row0 + 16 * I) * Hqk + hq) * DK,
+                                                  (uint32_t)max(0, min(16, cp.len - 16 * I)) * Hqk * DK * 2);
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + ((size_t)(cp.row0 + 16 * I) * Hqk + hq) * DK,
+                                                  (uint32_t)max(0, min(16, cp.len - 16 * I)) * Hqk * DK * 2);
+    uint4 graw[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint32_t c0 = 32 * kb + 8 * lg;
+      graw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, (vrow * Hv * DK + c0) * 2, 0, 0));
+      qraw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, (vrow * Hqk * DK + c0) * 2, 0, 0));
+      kraw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, (vrow * Hqk * DK + c0) * 2, 0, 0));
+    }
+    float4 dtb4[8];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      dtb4[2 * kb] = *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + 32 * kb + 8 * lg);
+      dtb4[2 * kb + 1] = *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + 32 * kb + 8 * lg + 4);
+    }
+    const float blogit = valid ? bf2f(beta[(size_t)row * Hv + h]) : 0.0f;
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const int c0 = 32 * kb + 8 * lg;
-      uint4 gr = make_uint4(0, 0, 0, 0);
-      qraw[kb] = gr;
-      kraw[kb] = gr;
-      if (valid) {
-        gr = *reinterpret_cast<const uint4*>(g + ((size_t)row * Hv + h) * DK + c0);
-        qraw[kb] = *reinterpret_cast<const uint4*>(q + ((size_t)row * Hqk + hq) * DK + c0);
-        kraw[kb] = *reinterpret_cast<const uint4*>(k + ((size_t)row * Hqk + hq) * DK + c0);
-      }
       float qf[8], kf[8];
-      unpack_bf16x8(gr, G[kb]);
+      unpack_bf16x8(graw[kb], G[kb]);
       unpack_bf16x8(qraw[kb], qf);
       unpack_bf16x8(kraw[kb], kf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) { sq += qf[e] * qf[e]; sk += kf[e] * kf[e]; }
-      const float4 d0 = *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + c0);
-      const float4 d1 = *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + c0 + 4);
-      const float dtb[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      const float dtb[8] = {dtb4[2 * kb].x, dtb4[2 * kb].y, dtb4[2 * kb].z, dtb4[2 * kb].w,
+                            dtb4[2 * kb + 1].x, dtb4[2 * kb + 1].y, dtb4[2 * kb + 1].z, dtb4[2 * kb + 1].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) G[kb][e] = valid ? gate2<MODE>(G[kb][e] + dtb[e], A_exp, lb_log2e) : 0.0f;
     }
@@ -334,9 +349,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if (lg == 0) {
       sRq[r] = rsqrtf(sq + kL2Eps);
       sRk[r] = rsqrtf(sk + kL2Eps);
-      float bt = 0.0f;
-      if (valid) bt = fast_rcp(1.0f + fast_exp2(-kLog2e * bf2f(beta[(size_t)row * Hv + h])));
-      sBeta[r] = bt;
+      sBeta[r] = valid ? fast_rcp(1.0f + fast_exp2(-kLog2e * blogit)) : 0.0f;
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -411,6 +424,9 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // accumulators: the diagonal block, and off-diagonal blocks J = 0..2 (J < I);
   // all register arrays are indexed by compile-time values only
   f32x4 dkk = f32x4{0, 0, 0, 0}, dqk = f32x4{0, 0, 0, 0};
+  f32x4 dkkp[4], dqkp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { dkkp[j] = f32x4{0, 0, 0, 0}; dqkp[j] = f32x4{0, 0, 0, 0}; }
   f32x4 okk[3], oqk[3];
 #pragma unroll
   for (int J = 0; J < 3; ++J) { okk[J] = f32x4{0, 0, 0, 0}; oqk[J] = f32x4{0, 0, 0, 0}; }
@@ -471,15 +487,20 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         *reinterpret_cast<half8*>(sX + ((pair * 4 + kb) * 64 + lane) * 16) = to_half8(b);
       }
       if (MODE == KDA_GATE_SAFE_SIGMOID) {
-        // diagonal block on the fp32 MFMA, both sides offset by the midpoint
+        // diagonal block on the fp32 MFMA, both sides offset by the midpoint;
+        // four independent accumulators per product keep the chain short
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float db = kC[e] * vMc[c0 + e];
-          dkk = __builtin_amdgcn_mfma_f32_16x16x4f32(kR[e] * vMr[c0 + e], db, dkk, 0, 0, 0);
-          dqk = __builtin_amdgcn_mfma_f32_16x16x4f32(qR[e] * vMr[c0 + e], db, dqk, 0, 0, 0);
+          dkkp[e & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(kR[e] * vMr[c0 + e], db, dkkp[e & 3], 0, 0, 0);
+          dqkp[e & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(qR[e] * vMr[c0 + e], db, dqkp[e & 3], 0, 0, 0);
         }
       }
     }
+  }
+  if (MODE == KDA_GATE_SAFE_SIGMOID) {
+    dkk = (dkkp[0] + dkkp[1]) + (dkkp[2] + dkkp[3]);
+    dqk = (dqkp[0] + dqkp[1]) + (dqkp[2] + dqkp[3]);
   }
   __syncthreads();
 

@@ -29,7 +29,8 @@ _STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DT
            -5: "KDA_ERR_ALIGN", -6: "KDA_ERR_WORKSPACE", -7: "KDA_ERR_LAUNCH", -8: "KDA_ERR_UNSUPPORTED"}
 
 # Every function the header declares.
-EXPORTS = ("kda_fwd_workspace_size", "kda_fwd_check", "kda_fwd", "kda_status_string", "kda_last_error")
+EXPORTS = ("kda_fwd_workspace_size", "kda_fwd_check", "kda_fwd", "kda_fwd_intra", "kda_fwd_state",
+           "kda_status_string", "kda_last_error")
 
 
 class KdaError(RuntimeError):
@@ -64,8 +65,9 @@ def load_library(path: str = LIB_PATH):
     lib.kda_fwd_workspace_size.argtypes = [PP]
     lib.kda_fwd_check.restype = ctypes.c_int
     lib.kda_fwd_check.argtypes = [PP] + [P] * 12 + [ctypes.c_size_t]
-    lib.kda_fwd.restype = ctypes.c_int
-    lib.kda_fwd.argtypes = [PP] + [P] * 12 + [ctypes.c_size_t, P]
+    for fn in (lib.kda_fwd, lib.kda_fwd_intra, lib.kda_fwd_state):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [PP] + [P] * 12 + [ctypes.c_size_t, P]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_last_error.restype = ctypes.c_char_p
@@ -117,13 +119,15 @@ def _state_code(t: Optional[torch.Tensor]) -> int:
 
 def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GATE_SOFTPLUS,
         initial_state=None, final_state_dtype=torch.float32, cu_seqlens=None, out=None,
-        final_state=None, workspace=None):
+        final_state=None, workspace=None, stage=None):
     """Chunked KDA forward on the current HIP stream.
 
     q, k [B,T,Hqk,128] bf16; v, g [B,T,Hv,128] bf16; beta [B,T,Hv] bf16 logits;
     A_log [Hv] fp32; dt_bias [Hv,128] fp32; initial_state [N,Hv,128,128]
     fp32/bf16 or None; cu_seqlens [N+1] int64 or None (then B must be 1).
-    Returns (out bf16 [B,T,Hv,128], final_state or None).
+    Returns (out bf16 [B,T,Hv,128], final_state or None).  ``stage`` = "intra"
+    or "state" runs only that half of the forward (kda_fwd_intra /
+    kda_fwd_state); the two halves in order are the full forward.
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
@@ -156,7 +160,8 @@ def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GAT
     if workspace is None:
         workspace = _workspace(need, q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = lib.kda_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
+    entry = {None: lib.kda_fwd, "intra": lib.kda_fwd_intra, "state": lib.kda_fwd_state}[stage]
+    rc = entry(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
                      _ptr(cu_seqlens), _ptr(initial_state), _ptr(final_state), _ptr(out), _ptr(workspace),
                      ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
     if rc != KDA_OK:

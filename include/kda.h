@@ -114,6 +114,25 @@ kda_status kda_fwd(const kda_fwd_params* p,
                    const int64_t* cu_seqlens, const void* initial_state, void* final_state,
                    void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two stages of kda_fwd, for timing each kernel on its own: kda_fwd is
+ * exactly kda_fwd_intra followed by kda_fwd_state on the same stream, with
+ * the same parameters, tensors and workspace.  kda_fwd_intra runs the
+ * per-chunk work (gate, cumulative decay, Akk/Aqk, triangular solve, WY
+ * factors) over all chunks in parallel and leaves its results in the
+ * workspace; kda_fwd_state then runs the inter-chunk state recurrence and
+ * writes out and final_state.  Arguments, validation and errors are those of
+ * kda_fwd (every pointer is checked, even ones the stage does not read). */
+kda_status kda_fwd_intra(const kda_fwd_params* p,
+                         const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* A_log, const float* dt_bias,
+                         const int64_t* cu_seqlens, const void* initial_state, void* final_state,
+                         void* out, void* workspace, size_t workspace_bytes, void* stream);
+kda_status kda_fwd_state(const kda_fwd_params* p,
+                         const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* A_log, const float* dt_bias,
+                         const int64_t* cu_seqlens, const void* initial_state, void* final_state,
+                         void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static name of a status code. */
 const char* kda_status_string(kda_status s);
 
