@@ -110,6 +110,32 @@ def test_hand_worked_example_exact():
     assert np.array_equal(s.reshape(2, 2), [[3.0, 2.0], [4.5, 4.0]])
 
 
+def _golden(name):
+    """Read a key: values fixture from tests/golden (comments start with #)."""
+    import os
+    vals = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                key, rest = line.split(":", 1)
+                vals[key.strip()] = [float(x) for x in rest.split()]
+    return vals
+
+
+def test_golden_two_token_channel_decay():
+    # exact binary-fraction example derived by hand in the fixture's comments
+    gd = _golden("two_token_channel_decay_k2v3.txt")
+    K, V = int(gd["K"][0]), int(gd["V"][0])
+    T = len(gd["beta"])
+    d = _tiny(np.reshape(gd["q"], (T, K)), np.reshape(gd["k"], (T, K)), np.reshape(gd["v"], (T, V)),
+              np.reshape(gd["a"], (T, K)), gd["beta"], h0=np.reshape(gd["S0"], (V, K)), mode=2, scale=1.0,
+              l2norm=False, beta_is_prob=True)
+    o, s = run(d)
+    assert np.array_equal(o.reshape(T * V), gd["out"])
+    assert np.array_equal(s.reshape(V * K), gd["final_state"])
+
+
 def test_single_token_zero_state_closed_form():
     # K=2, V=3 so that a transposed state cannot pass.
     q, k, v = [[3.0, 4.0]], [[0.0, 2.0]], [[1.0, -2.0, 0.5]]
