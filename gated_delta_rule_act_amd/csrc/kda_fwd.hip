@@ -210,7 +210,8 @@ constexpr int L_AQ = L_KE + 128 * KES * 2;
 constexpr int L_RQ = L_AQ + 64 * AQS * 2;
 constexpr int L_RK = L_RQ + 64 * 4;
 constexpr int L_BETA = L_RK + 64 * 4;
-constexpr int L_END = L_BETA + 64 * 4;
+constexpr int L_FW = L_BETA + 64 * 4;
+constexpr int L_END = L_FW + 64 * 4;
 // softplus only: Gamma and raw q, k rows for the pairwise diagonal
 constexpr int L_PG = L_END;
 constexpr int L_PQ = L_PG + 64 * GS * 4;
@@ -285,12 +286,15 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   float* sRq = reinterpret_cast<float*>(smem + L_RQ);
   float* sRk = reinterpret_cast<float*>(smem + L_RK);
   float* sBeta = reinterpret_cast<float*>(smem + L_BETA);
+  float* sFw = reinterpret_cast<float*>(smem + L_FW);
 
   const int x = blockIdx.x, h = blockIdx.y;
   ChunkPos cp;
   if (!chunk_pos(x, B, T, N, cu, chunk_off, cp)) return;
   const int hq = h / (Hv / Hqk);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: keeping it in a scalar register turns every
+  // test on the sub-chunk index into a scalar branch
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const int I = wave;
   const int r = 16 * I + li;
@@ -573,26 +577,44 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     __syncthreads();
   }
 
-  // ---- phase 5: Akk (fp32) and Aqk (fp16) into LDS with masks, beta, norms; T = 0
+  // ---- phase 5: Akk (fp32) and Aqk (fp16) into LDS with masks, beta, norms.
+  // Blocks above the diagonal: Aqk is written as zero (it is copied out whole);
+  // Akk is never read there, and the blocks of T above the diagonal are never
+  // written: every reader of T masks them.
   {
+    float fk[4], fq[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = 16 * I + 4 * lg + rr;
+      fk[rr] = sBeta[row] * sRk[row];
+      fq[rr] = scale * sRq[row];
+    }
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
+      if (J > I) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sAq[(16 * I + 4 * lg + rr) * AQS + 16 * J + li] = (_Float16)0.0f;
+        continue;
+      }
+      const float fc = sRk[16 * J + li];
+      f32x4 vk, vq;
+      if (J == I) { vk = dkk; vq = dqk; }
+      else { vk = okk[J < 3 ? J : 0]; vq = oqk[J < 3 ? J : 0]; }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int row = 16 * I + 4 * lg + rr, col = 16 * J + li;
-        float vkk = 0.0f, vqk = 0.0f;
-        if (J < 3 && J < I) { vkk = okk[J < 3 ? J : 0][rr]; vqk = oqk[J < 3 ? J : 0][rr]; }
-        if (J == I) { vkk = dkk[rr]; vqk = dqk[rr]; }
-        float akk = 0.0f, aqk = 0.0f;
-        if (J <= I) {
-          if (row > col) akk = vkk * sBeta[row] * sRk[row] * sRk[col];
-          if (row >= col) aqk = vqk * scale * sRq[row];
+        float akk = vk[rr] * fk[rr] * fc;
+        float aqk = vq[rr] * fq[rr];
+        if (J == I) {
+          akk = (4 * lg + rr > li) ? akk : 0.0f;
+          aqk = (4 * lg + rr >= li) ? aqk : 0.0f;
         }
         sA[row * AS + col] = akk;
         sAq[row * AQS + col] = (_Float16)aqk;
       }
     }
-    for (int i = tid; i < 64 * AS; i += 256) sT[i] = 0.0f;
+    // column factors of the WY products: beta rk for W, beta for T diag(beta)
+    if (tid < 64) sFw[tid] = sBeta[tid] * sRk[tid];
   }
   __syncthreads();
 
@@ -644,9 +666,11 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int nkb = (wave >= 2) ? 2 : 1;
     for (int kb = 0; kb < nkb; ++kb) {
       const int s0 = 32 * kb + 8 * lg;
+      // column block 2 kb + (lg >> 1) above the diagonal block I is zero
+      const bool keep = 2 * kb + (lg >> 1) <= I;
       half8 a;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = (_Float16)(sT[t * AS + s0 + e] * sBeta[s0 + e] * sRk[s0 + e]);
+      for (int e = 0; e < 8; ++e) a[e] = keep ? (_Float16)(sT[t * AS + s0 + e] * sFw[s0 + e]) : (_Float16)0.0f;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const half8 b = *reinterpret_cast<const half8*>(sKEt + (16 * nt + li) * KES + s0);
@@ -658,9 +682,10 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const int fr = item >> 6, ln = item & 63;
       const int row = 16 * (fr >> 1) + (ln & 15), c0 = 32 * (fr & 1) + 8 * (ln >> 4);
       bf16x8 th, tl;
+      const bool keep = 2 * (fr & 1) + (ln >> 5) <= (fr >> 1);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = sT[row * AS + c0 + e] * sBeta[c0 + e];
+        const float v = keep ? sT[row * AS + c0 + e] * sBeta[c0 + e] : 0.0f;
         const __bf16 hv = (__bf16)v;
         th[e] = hv;
         tl[e] = (__bf16)(v - (float)hv);
@@ -692,41 +717,35 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 //
 // One workgroup of 8 waves per (sequence, v-head, 32-wide V slice), sequential
 // over the sequence's chunks with the fp32 state slice S^T[k][v] in registers
-// (wave w owns key rows 16w..16w+15).  Per chunk:
-//     U = T diag(b) V - W S^T          (wave w: rows 16*(w>>1).., V tile w&1)
+// (wave w owns key rows 16w..16w+15, both 16-wide V tiles).  Per chunk:
+//     U = T diag(b) V - W S^T
 //     O = qs . (Q . 2^G) S^T + Aqk U'   with U' = rk . U
 //     S <- S Diag(2^G_last) + U'^T (K . 2^(G_last - G))
-// The 57 shared fragments of a chunk (W, Q . 2^G, T diag(b), Aqk, vectors) are
-// loaded two chunks ahead, one eighth per wave, into registers and published
-// through one LDS buffer at the start of the chunk; each wave keeps its own
-// four (K . 2^(G_last - G))^T fragments in registers.  Streaming from 8 waves
-// keeps enough requests in flight per CU for the L2-shared operands of the V
-// slices of one chain (dispatched to the same XCD).
+// The U and O products are split between the two waves of a pair by their
+// contraction: wave (ta, kh) takes token tile ta and key half kh of W S^T and
+// Q S^T, and token half kh of T diag(b) V.  Each wave therefore loads only its
+// own operand fragments -- the 57 shared fragments of a chunk are read once
+// per workgroup, with no copy through LDS -- and the pair exchanges one
+// partial tile each through LDS.  Operands are loaded two chunks ahead into
+// registers; 8 waves keep enough requests in flight per CU for the
+// L2-shared operands of the V slices of one chain (dispatched to one XCD).
 constexpr int SWAVES = 8;
 constexpr int SSS = 136;  // sS row stride (fp16), S^T slice stored as [v][k]
 constexpr int SUS = 72;   // sU / sVt row stride (16-bit)
-constexpr int RING_FR = 8;  // shared fragments loaded per wave (the 57 spread over 8 waves)
 
 struct ChunkRegs {
-  // shared fragments f = min(wave + 8 j, 56), j = 0..7 (named members: register
-  // arrays indexed before unrolling would be left in scratch memory)
-  u32x4 r0, r1, r2, r3, r4, r5, r6, r7;
-  u32x4 kd0, kd1, kd2, kd3;  // this wave's Kd^T fragments: (kb 0, hi) (kb 0, lo) (kb 1, hi) (kb 1, lo)
-  u32x2 vraw;                // 4 values of the V slice: row tid >> 3, columns 4 (tid & 7) ..
-  template <int J> __device__ __forceinline__ u32x4& ring() {
-    static_assert(J >= 0 && J < RING_FR, "ring index");
-    if constexpr (J == 0) return r0; else if constexpr (J == 1) return r1; else if constexpr (J == 2) return r2;
-    else if constexpr (J == 3) return r3; else if constexpr (J == 4) return r4; else if constexpr (J == 5) return r5;
-    else if constexpr (J == 6) return r6; else return r7;
-  }
+  // named members: register arrays indexed before unrolling would be left in
+  // scratch memory
+  u32x4 wn0, wn1, qg0, qg1;   // -W and Q . 2^G: token tile ta, key blocks 2kh, 2kh+1
+  u32x4 tbh, tbl;             // T diag(b) hi/lo: token tile ta, token block kh
+  u32x4 aq0, aq1;             // Aqk: token tile ta, token blocks 0, 1
+  u32x4 kd0, kd1, kd2, kd3;   // Kd^T of key tile w: (block 0, hi) (block 0, lo) (block 1, hi) (block 1, lo)
+  u32x4 vec;                  // 16 B of the vector fragment: bytes 128 w + 16 (lane & 7) ..
+  u32x2 vraw;                 // 4 values of the V slice: row tid >> 3, columns 4 (tid & 7) ..
 };
 
-template <int J = 0, typename F>
-__device__ __forceinline__ void for_ring(F&& f) {
-  if constexpr (J < RING_FR) {
-    f(std::integral_constant<int, J>{});
-    for_ring<J + 1>(f);
-  }
+__device__ __forceinline__ u32x4 ld_frag(const uint8_t* blk, int fr, int lane) {
+  return *reinterpret_cast<const u32x4*>(blk + fr * FRAG + lane * 16);
 }
 
 // The prefetch of one chunk, issued in three parts spread over the previous
@@ -735,19 +754,25 @@ template <int PART>
 __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk, int wave, int lane,
                                                 const uint16_t* __restrict__ v, int64_t row0, int len, int Hv, int h,
                                                 int v0, int tid) {
-  if constexpr (PART == 0 || PART == 1) {
-    for_ring([&](auto J) {
-      if constexpr ((int)J / 4 == PART) {
-        const int fr = min(wave + 8 * (int)J, F_SHARED - 1);
-        o.template ring<J>() = *reinterpret_cast<const u32x4*>(blk + fr * FRAG + lane * 16);
-      }
-    });
+  const int ta = wave >> 1, kh = wave & 1;
+  if constexpr (PART == 0) {
+    o.wn0 = ld_frag(blk, F_WN + ta * 4 + 2 * kh, lane);
+    o.wn1 = ld_frag(blk, F_WN + ta * 4 + 2 * kh + 1, lane);
+    o.qg0 = ld_frag(blk, F_QG + ta * 4 + 2 * kh, lane);
+    o.qg1 = ld_frag(blk, F_QG + ta * 4 + 2 * kh + 1, lane);
+  } else if constexpr (PART == 1) {
+    o.tbh = ld_frag(blk, F_TBH + ta * 2 + kh, lane);
+    o.tbl = ld_frag(blk, F_TBL + ta * 2 + kh, lane);
+    o.aq0 = ld_frag(blk, F_AQK + ta * 2, lane);
+    o.aq1 = ld_frag(blk, F_AQK + ta * 2 + 1, lane);
   } else {
-    const uint8_t* kdb = blk + (F_KD + wave * 4) * FRAG + lane * 16;
-    o.kd0 = *reinterpret_cast<const u32x4*>(kdb);
-    o.kd1 = *reinterpret_cast<const u32x4*>(kdb + FRAG);
-    o.kd2 = *reinterpret_cast<const u32x4*>(kdb + 2 * FRAG);
-    o.kd3 = *reinterpret_cast<const u32x4*>(kdb + 3 * FRAG);
+    o.kd0 = ld_frag(blk, F_KD + wave * 4, lane);
+    o.kd1 = ld_frag(blk, F_KD + wave * 4 + 1, lane);
+    o.kd2 = ld_frag(blk, F_KD + wave * 4 + 2, lane);
+    o.kd3 = ld_frag(blk, F_KD + wave * 4 + 3, lane);
+    // each wave fetches one 128-byte eighth of the vector fragment (every lane
+    // group of 8 the same bytes) and publishes it through LDS
+    o.vec = ld_frag(blk, F_VEC, 8 * wave + (lane & 7));
     // rows s >= len lie beyond the buffer range and read as zero
     const int s = tid >> 3, cq = tid & 7;
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + ((size_t)row0 * Hv + h) * DV + v0, (uint32_t)len * Hv * DV * 2);
@@ -770,7 +795,8 @@ struct StateCtx {
   const uint8_t* wsh;
   int64_t bos, seqlen;
   int x0, nc, Hv, h, v0, tid, wave, lane, li, lg;
-  uint8_t* ring;
+  f32x4* sPart;
+  float* sVec;
   _Float16* sS;
   _Float16* sUh;
   _Float16* sUl;
@@ -786,14 +812,15 @@ struct PendingOut {
   int len;
 };
 
+// wave (ta, kh) stores the 16 x 16 output tile of token tile ta, V tile kh
 __device__ __forceinline__ void store_pending(const PendingOut& pd, uint16_t* __restrict__ out, int Hv, int h,
-                                              int v0, int ta, int vb, int li, int lg) {
+                                              int v0, int ta, int vt, int li, int lg) {
   // rows t >= len fall outside the buffer range and are dropped
   const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(out + ((size_t)pd.row0 * Hv + h) * DV + v0, (uint32_t)pd.len * Hv * DV * 2);
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int t = 16 * ta + 4 * lg + rr;
-    __builtin_amdgcn_raw_buffer_store_b16((short)pd.o[rr], ro, (t * Hv * DV + 16 * vb + li) * 2, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16((short)pd.o[rr], ro, (t * Hv * DV + 16 * vt + li) * 2, 0, 0);
   }
 }
 
@@ -801,24 +828,34 @@ __device__ __forceinline__ int chunk_len(const StateCtx& x, int c) {
   return (int)min((int64_t)CH, x.seqlen - (int64_t)c * CH);
 }
 
-template <typename V8>
-__device__ __forceinline__ V8 ring_frag(const uint8_t* ring, int fr, int lane) {
-  return *reinterpret_cast<const V8*>(ring + fr * FRAG + lane * 16);
+// An empty use that forces the registers to be loaded here: issued once before
+// the chunk loop, it completes the initial state and first chunk's loads
+// there, so the loop is entered with nothing of them outstanding (otherwise
+// the wait inserted at the loop head for that path is a full drain, paid on
+// every iteration).
+__device__ __forceinline__ void settle(const u32x4& a) { asm volatile("" ::"v"(a)); }
+__device__ __forceinline__ void settle(const f32x4& a) { asm volatile("" ::"v"(a)); }
+__device__ __forceinline__ void settle(const u32x2& a) { asm volatile("" ::"v"(a)); }
+__device__ __forceinline__ void settle(const ChunkRegs& r) {
+  settle(r.wn0); settle(r.wn1); settle(r.qg0); settle(r.qg1); settle(r.tbh); settle(r.tbl);
+  settle(r.aq0); settle(r.aq1); settle(r.kd0); settle(r.kd1); settle(r.kd2); settle(r.kd3);
+  settle(r.vec); settle(r.vraw);
 }
+
+__device__ __forceinline__ half8 as_half8(const u32x4& u) { return __builtin_bit_cast(half8, u); }
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
 
 // One chunk of the state chain: `cur` holds chunk c (loaded two chunks ago),
 // `n2` receives chunk c+2.
 __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2], ChunkRegs& cur, ChunkRegs& n2,
                                             const int c, PendingOut& pd) {
   const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
-  const int ta = wave >> 1, vb = wave & 1;
+  const int ta = wave >> 1, kh = wave & 1;
   const int64_t row0 = x.bos + (int64_t)c * CH;
-  // 1. publish this chunk's shared fragments, V slice and the current state.
-  // Every reader of these buffers in the previous chunk was before its B2.
-  for_ring([&](auto J) {
-    const int fr = min(wave + 8 * (int)J, F_SHARED - 1);
-    *reinterpret_cast<u32x4*>(x.ring + fr * FRAG + lane * 16) = cur.template ring<J>();
-  });
+  // 1. publish the V slice (transposed, [v][t]), the chunk's vectors and the
+  //    current state (fp16, [v][k]).  Every reader of these buffers in the
+  //    previous chunk was before that chunk's last barrier.
+  reinterpret_cast<u32x4*>(x.sVec)[8 * wave + (lane & 7)] = cur.vec;
   {
     const int s = tid >> 3, cq = tid & 7;
     const uint32_t w2[2] = {cur.vraw[0], cur.vraw[1]};
@@ -838,61 +875,52 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2], Ch
   // 2. the previous chunk's outputs (none before the first chunk: len 0), then
   //    the first part of the prefetch of chunk c+2 (clamped, so every chunk
   //    queues the same operations)
-  store_pending(pd, x.out, x.Hv, x.h, x.v0, ta, vb, li, lg);
+  store_pending(pd, x.out, x.Hv, x.h, x.v0, ta, kh, li, lg);
   const int cp2 = min(c + 2, x.nc - 1);
   const uint8_t* blk2 = x.wsh + (size_t)(x.x0 + cp2) * BLOCK;
   const int64_t row2 = x.bos + (int64_t)cp2 * CH;
   const int len2 = chunk_len(x, cp2);
   load_chunk_part<0>(n2, blk2, wave, lane, x.v, row2, len2, x.Hv, x.h, x.v0, tid);
   __syncthreads();  // B1
-  // 3. everything this wave needs from the shared buffer, read before B2
-  half8 wn[4], qg[4], aq[2];
-  bf16x8 tbh[2], tbl[2];
+  const f32x4 gn = *reinterpret_cast<const f32x4*>(x.sVec + 16 * wave + 4 * lg);
+  const f32x4 qs = *reinterpret_cast<const f32x4*>(x.sVec + 128 + 16 * ta + 4 * lg);
+  const f32x4 rk = *reinterpret_cast<const f32x4*>(x.sVec + 192 + 16 * ta + 4 * lg);
+  // 3. this wave's halves of U and O for both V tiles:
+  //    pu = T diag(b)[ta, token half kh] V + (-W)[ta, key half kh] S^T,
+  //    po = (Q . 2^G)[ta, key half kh] S^T
+  f32x4 pu[2], po[2];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    wn[kb] = ring_frag<half8>(x.ring, F_WN + ta * 4 + kb, lane);
-    qg[kb] = ring_frag<half8>(x.ring, F_QG + ta * 4 + kb, lane);
+  for (int nt = 0; nt < 2; ++nt) {
+    const int vv = 16 * nt + li;
+    const bf16x8 vbf = *reinterpret_cast<const bf16x8*>(x.sVt + vv * SUS + 32 * kh + 8 * lg);
+    const half8 sb0 = *reinterpret_cast<const half8*>(x.sS + vv * SSS + 64 * kh + 8 * lg);
+    const half8 sb1 = *reinterpret_cast<const half8*>(x.sS + vv * SSS + 64 * kh + 32 + 8 * lg);
+    f32x4 u0 = f32x4{0, 0, 0, 0}, u1 = f32x4{0, 0, 0, 0}, o0 = f32x4{0, 0, 0, 0};
+    u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh), vbf, u0, 0, 0, 0);
+    u1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn0), sb0, u1, 0, 0, 0);
+    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg0), sb0, o0, 0, 0, 0);
+    u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl), vbf, u0, 0, 0, 0);
+    u1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn1), sb1, u1, 0, 0, 0);
+    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg1), sb1, o0, 0, 0, 0);
+    pu[nt] = u0 + u1;
+    po[nt] = o0;
   }
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    tbh[kb] = ring_frag<bf16x8>(x.ring, F_TBH + ta * 2 + kb, lane);
-    tbl[kb] = ring_frag<bf16x8>(x.ring, F_TBL + ta * 2 + kb, lane);
-    aq[kb] = ring_frag<half8>(x.ring, F_AQK + ta * 2 + kb, lane);
-  }
-  const float* vec = reinterpret_cast<const float*>(x.ring + F_VEC * FRAG);
-  const f32x4 gn = *reinterpret_cast<const f32x4*>(vec + 16 * wave + 4 * lg);
-  const f32x4 qs = *reinterpret_cast<const f32x4*>(vec + 128 + 16 * ta + 4 * lg);
-  const f32x4 rk = *reinterpret_cast<const f32x4*>(vec + 192 + 16 * ta + 4 * lg);
-  // U = T diag(b) V - W S^T ; O = (Q . 2^G) S^T   (rows 16 ta.., V tile vb)
-  f32x4 U, O;
+  // the partner (same ta, other kh) owns V tile 1 - kh: send it that tile
   {
-    f32x4 u0 = f32x4{0, 0, 0, 0}, u1 = f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 vbf = *reinterpret_cast<const bf16x8*>(x.sVt + (16 * vb + li) * SUS + 32 * kb + 8 * lg);
-      u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tbh[kb], vbf, u0, 0, 0, 0);
-      u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tbl[kb], vbf, u1, 0, 0, 0);
-    }
-    half8 sb[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vb + li) * SSS + 32 * kb + 8 * lg);
-    u0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wn[0], sb[0], u0, 0, 0, 0);
-    u1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wn[1], sb[1], u1, 0, 0, 0);
-    u0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wn[2], sb[2], u0, 0, 0, 0);
-    u1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(wn[3], sb[3], u1, 0, 0, 0);
-    U = u0 + u1;
-    f32x4 o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
-    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qg[0], sb[0], o0, 0, 0, 0);
-    o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qg[1], sb[1], o1, 0, 0, 0);
-    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qg[2], sb[2], o0, 0, 0, 0);
-    o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qg[3], sb[3], o1, 0, 0, 0);
-    O = (o0 + o1) * qs;
+    f32x4* mine = x.sPart + (size_t)wave * 2 * 64;
+    mine[lane] = kh ? pu[0] : pu[1];
+    mine[64 + lane] = kh ? po[0] : po[1];
   }
   __builtin_amdgcn_sched_barrier(0);
   load_chunk_part<1>(n2, blk2, wave, lane, x.v, row2, len2, x.Hv, x.h, x.v0, tid);
   __builtin_amdgcn_sched_barrier(0);
-  // 4. U' = rk . U -> LDS hi/lo, transposed [v][t]
+  __syncthreads();  // B2
+  // 4. U and O of (ta, V tile kh); U' = rk . U -> LDS hi/lo, transposed [v][t]
+  f32x4 O;
   {
+    const f32x4* theirs = x.sPart + (size_t)(wave ^ 1) * 2 * 64;
+    const f32x4 U = (kh ? pu[1] : pu[0]) + theirs[lane];
+    O = ((kh ? po[1] : po[0]) + theirs[64 + lane]) * qs;
     typedef _Float16 half4 __attribute__((ext_vector_type(4)));
     half4 hi, lo;
 #pragma unroll
@@ -902,19 +930,18 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2], Ch
       hi[rr] = hh;
       lo[rr] = (_Float16)(up - (float)hh);
     }
-    const int vv = 16 * vb + li, tt = 16 * ta + 4 * lg;
+    const int vv = 16 * kh + li, tt = 16 * ta + 4 * lg;
     *reinterpret_cast<half4*>(x.sUh + vv * SUS + tt) = hi;
     *reinterpret_cast<half4*>(x.sUl + vv * SUS + tt) = lo;
   }
-  __syncthreads();  // B2
+  __syncthreads();  // B3
   // 5. S <- S Diag(2^G_last) + U'^T Kd ;  O += Aqk U'
   __builtin_amdgcn_sched_barrier(0);
   load_chunk_part<2>(n2, blk2, wave, lane, x.v, row2, len2, x.Hv, x.h, x.v0, tid);
   __builtin_amdgcn_sched_barrier(0);
-  const half8 kdh0 = __builtin_bit_cast(half8, cur.kd0);
-  const half8 kdl0 = __builtin_bit_cast(half8, cur.kd1);
-  const half8 kdh1 = __builtin_bit_cast(half8, cur.kd2);
-  const half8 kdl1 = __builtin_bit_cast(half8, cur.kd3);
+  const half8 kdh0 = as_half8(cur.kd0), kdl0 = as_half8(cur.kd1);
+  const half8 kdh1 = as_half8(cur.kd2), kdl1 = as_half8(cur.kd3);
+  half8 ua0, ua1;  // U' hi of V tile kh, token blocks 0 and 1
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const half8 uh0 = *reinterpret_cast<const half8*>(x.sUh + (16 * nt + li) * SUS + 8 * lg);
@@ -929,11 +956,13 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2], Ch
     sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdl0, uh0, sa, 0, 0, 0);
     sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdl1, uh1, sb2, 0, 0, 0);
     S[nt] = sa + sb2;
-    if (nt == vb) {
-      O = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[0], uh0, O, 0, 0, 0);
-      if (ta >= 2) O = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[1], uh1, O, 0, 0, 0);
-    }
+    if (nt == 0) { ua0 = uh0; ua1 = uh1; }
+    else { ua0 = kh ? uh0 : ua0; ua1 = kh ? uh1 : ua1; }
   }
+  // V tile kh; Aqk of token tiles 0, 1 is zero in token block 1, so the second
+  // product adds nothing there
+  O = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq0), ua0, O, 0, 0, 0);
+  O = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq1), ua1, O, 0, 0, 0);
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     pd.o[rr] = __builtin_bit_cast(uint16_t, (__bf16)O[rr]);
@@ -947,7 +976,8 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
                  const int* __restrict__ chunk_off, const void* __restrict__ h0, void* __restrict__ hT,
                  uint16_t* __restrict__ out, const uint8_t* __restrict__ ws,
                  int B, int T, int N, int Hv, int max_chunks, int init_dtype, int final_dtype) {
-  __shared__ __attribute__((aligned(16))) uint8_t sRing[F_SHARED * FRAG];
+  __shared__ __attribute__((aligned(16))) f32x4 sPart[SWAVES * 2 * 64];
+  __shared__ __attribute__((aligned(16))) float sVec[256];
   __shared__ __attribute__((aligned(16))) _Float16 sS[VS * SSS];
   __shared__ __attribute__((aligned(16))) _Float16 sUh[VS * SUS];
   __shared__ __attribute__((aligned(16))) _Float16 sUl[VS * SUS];
@@ -961,7 +991,7 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
   if (chain >= N * Hv) return;
   const int n = chain / Hv, h = chain % Hv;
   const int v0 = VS * slice;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
 
   int64_t bos, seqlen;
@@ -993,7 +1023,7 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
   }
 
   const uint8_t* wsh = ws + (size_t)h * max_chunks * BLOCK;
-  StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, lane, li, lg, sRing, sS, sUh, sUl, sVt};
+  StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, lane, li, lg, sPart, sVec, sS, sUh, sUl, sVt};
   ChunkRegs rA, rB, rC;
   if (nc > 0) {
     load_chunk(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
@@ -1001,6 +1031,9 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
     load_chunk(rB, wsh + (size_t)(x0 + c1) * BLOCK, wave, lane, v, bos + (int64_t)c1 * CH, chunk_len(ctx, c1), Hv,
                h, v0, tid);
   }
+  settle(S[0]);
+  settle(S[1]);
+  settle(rA);
   PendingOut pd;
   pd.row0 = bos;
   pd.len = 0;
