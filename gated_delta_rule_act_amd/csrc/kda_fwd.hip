@@ -187,8 +187,8 @@ __device__ __forceinline__ bool chunk_pos(int x, int B, int T, int N, const int6
 // so the 136 pairs of the block are evaluated pairwise on the VALU.
 constexpr int AS = 68;      // fp32 row stride of Akk / T
 constexpr int AQS = 72;     // fp16 row stride of Aqk
-constexpr int KES = 72;     // fp16 row stride of the transposed K . 2^G / Kd tiles
-constexpr int WSS = 136;    // fp16 row stride of the W staging tile
+constexpr int KER = 144;    // fp16 row stride of the row-major [t][k] K . 2^G and Kd tiles
+constexpr int WTS = 80;     // fp16 row stride of the [k][t] W staging tile
 constexpr int GS = 132;     // fp32 row stride of Gamma (softplus pairwise only)
 constexpr int QS = 136;     // bf16 row stride of raw q, k (softplus pairwise only)
 constexpr int NVEC = 19;    // per-channel vectors: P0..3, L0..3, D20, D30, D31, Mr0..3, Mc0..3
@@ -206,7 +206,7 @@ constexpr int L_TOT = L_T;                              // [4][128] f32, inside 
 constexpr int L_MID = L_TOT + 4 * 128 * 4;              // [4][128] f32
 constexpr int L_VEC = L_MID + 4 * 128 * 4;              // [NVEC][128] f32
 constexpr int L_KE = L_T + T_BYTES;
-constexpr int L_AQ = L_KE + 128 * KES * 2;
+constexpr int L_AQ = L_KE + 64 * KER * 2;
 constexpr int L_RQ = L_AQ + 64 * AQS * 2;
 constexpr int L_RK = L_RQ + 64 * 4;
 constexpr int L_BETA = L_RK + 64 * 4;
@@ -219,8 +219,8 @@ constexpr int L_PK = L_PQ + 64 * QS * 2;
 constexpr int L_END_SP = L_PK + 64 * QS * 2;
 static_assert(L_VEC + NVEC * 128 * 4 <= L_T + T_BYTES, "vectors fit in region T");
 static_assert(64 * AS * 4 <= X_BYTES, "Akk fits in region X");
-static_assert(64 * WSS * 2 <= X_BYTES, "W staging fits in region X");
-static_assert(X_BYTES >= 128 * KES * 2, "Kd staging fits in region X");
+static_assert(128 * WTS * 2 <= X_BYTES, "W staging fits in region X");
+static_assert(64 * KER * 2 <= X_BYTES, "Kd staging fits in region X");
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_row_shr(float x) {
@@ -263,6 +263,26 @@ __device__ __forceinline__ half8 to_half8(const float* v) {
   return h;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes
+// the 16 addresses are read as a 16 x 4 block M[s][e] of 16-bit values (4 at
+// each address) and lane i receives M[4e + (i >> 2)][i & 3], e = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const _Float16* p) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_t;
+  auto lp = (__attribute__((address_space(3))) fp16x4_t*)(p);
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16(lp));
+}
+
+// One 16 x 32 MFMA operand fragment with the contraction index contiguous per
+// lane, read from a row-major [k][n] tile of 16-bit values (row stride ld):
+// lane (i, g) receives column n0 + i, rows k0 + 8g .. k0 + 8g + 7.  Source
+// lane s of a group points at row k0 + 8g + (s >> 2), columns n0 + 4 (s & 3).
+__device__ __forceinline__ u32x4 lds_frag_tr(const _Float16* tile, int ld, int k0, int n0, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const _Float16* p = tile + (k0 + 8 * g + (i >> 2)) * ld + n0 + 4 * (i & 3);
+  const u32x2 a = lds_read_tr16(p), b = lds_read_tr16(p + 4 * ld);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(256)
 kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -278,7 +298,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   _Float16* sW = reinterpret_cast<_Float16*>(smem + L_X);
   _Float16* sKd = reinterpret_cast<_Float16*>(smem + L_X);
   float* sT = reinterpret_cast<float*>(smem + L_T);
-  _Float16* sKEt = reinterpret_cast<_Float16*>(smem + L_KE);
+  _Float16* sKE = reinterpret_cast<_Float16*>(smem + L_KE);
   _Float16* sAq = reinterpret_cast<_Float16*>(smem + L_AQ);
   float* sTot = reinterpret_cast<float*>(smem + L_TOT);
   float* sMid = reinterpret_cast<float*>(smem + L_MID);
@@ -466,8 +486,12 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int e = 0; e < 8; ++e) o[e] = qR[e] * vP[c0 + e];
         *reinterpret_cast<half8*>(blk + (F_QG + I * 4 + kb) * FRAG + lane * 16) = to_half8(o);
       }
+      {
+        float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sKEt[(c0 + e) * KES + r] = (_Float16)(kR[e] * vP[c0 + e]);
+        for (int e = 0; e < 8; ++e) o[e] = kR[e] * vP[c0 + e];
+        *reinterpret_cast<half8*>(sKE + r * KER + c0) = to_half8(o);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float kd = kC[e] * vL[c0 + e];
@@ -559,20 +583,17 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
   __syncthreads();  // mailbox is dead
 
-  // ---- phase 4b: (K . 2^(G_63 - G))^T hi then lo through LDS to global [k][t]
+  // ---- phase 4b: (K . 2^(G_63 - G))^T hi then lo to global: staged row-major
+  // [t][k] in LDS and read back transposed into fragment (key tile, token block)
   for (int part = 0; part < 2; ++part) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sKd[(32 * kb + 8 * lg + e) * KES + r] = part == 0 ? kdh[kb][e] : kdl[kb][e];
+      *reinterpret_cast<half8*>(sKd + r * KER + 32 * kb + 8 * lg) = part == 0 ? kdh[kb] : kdl[kb];
     __syncthreads();
     for (int it = 0; it < 4; ++it) {
-      const int item = tid + 256 * it;  // fragment (km, kb) x lane
-      const int fr = item >> 6, ln = item & 63;
-      const int krow = 16 * (fr >> 1) + (ln & 15), t0 = 32 * (fr & 1) + 8 * (ln >> 4);
-      *reinterpret_cast<half8*>(blk + (F_KD + fr * 2 + part) * FRAG + ln * 16) =
-          *reinterpret_cast<const half8*>(sKd + krow * KES + t0);
+      const int fr = wave + 4 * it;  // fragment (km = fr >> 1, kb = fr & 1)
+      *reinterpret_cast<u32x4*>(blk + (F_KD + fr * 2 + part) * FRAG + lane * 16) =
+          lds_frag_tr(sKd, KER, 32 * (fr & 1), 16 * (fr >> 1), lane);
     }
     __syncthreads();
   }
@@ -673,7 +694,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       for (int e = 0; e < 8; ++e) a[e] = keep ? (_Float16)(sT[t * AS + s0 + e] * sFw[s0 + e]) : (_Float16)0.0f;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const half8 b = *reinterpret_cast<const half8*>(sKEt + (16 * nt + li) * KES + s0);
+        const half8 b = __builtin_bit_cast(half8, lds_frag_tr(sKE, KER, 32 * kb, 16 * nt, lane));
         accw[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, accw[nt], 0, 0, 0);
       }
     }
@@ -697,17 +718,17 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     // sA (region X) is dead after the solve: stage -W there
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        sW[(16 * wave + 4 * lg + rr) * WSS + 16 * nt + li] = (_Float16)(-accw[nt][rr]);
+    for (int nt = 0; nt < 8; ++nt) {
+      typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+      const half4 hv = {(_Float16)(-accw[nt][0]), (_Float16)(-accw[nt][1]), (_Float16)(-accw[nt][2]),
+                        (_Float16)(-accw[nt][3])};
+      *reinterpret_cast<half4*>(sW + (16 * nt + li) * WTS + 16 * wave + 4 * lg) = hv;
+    }
     __syncthreads();
     for (int it = 0; it < 4; ++it) {
-      const int item = tid + 256 * it;  // fragment (ta, kb) x lane
-      const int fr = item >> 6, ln = item & 63;
-      const int row = 16 * (fr >> 2) + (ln & 15), c0 = 32 * (fr & 3) + 8 * (ln >> 4);
-      *reinterpret_cast<half8*>(blk + (F_WN + fr) * FRAG + ln * 16) =
-          *reinterpret_cast<const half8*>(sW + row * WSS + c0);
+      const int fr = wave + 4 * it;  // fragment (ta = fr >> 2, kb = fr & 3)
+      *reinterpret_cast<u32x4*>(blk + (F_WN + fr) * FRAG + lane * 16) =
+          lds_frag_tr(sW, WTS, 32 * (fr & 3), 16 * (fr >> 2), lane);
     }
   }
 }
@@ -731,7 +752,8 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // L2-shared operands of the V slices of one chain (dispatched to one XCD).
 constexpr int SWAVES = 8;
 constexpr int SSS = 136;  // sS row stride (fp16), S^T slice stored as [v][k]
-constexpr int SUS = 72;   // sU / sVt row stride (16-bit)
+constexpr int SUS = 72;   // sU row stride (16-bit)
+constexpr int SVS = 48;   // sV row stride (16-bit): V slice row-major [t][v]
 
 struct ChunkRegs {
   // named members: register arrays indexed before unrolling would be left in
@@ -800,7 +822,7 @@ struct StateCtx {
   _Float16* sS;
   _Float16* sUh;
   _Float16* sUl;
-  uint16_t* sVt;
+  _Float16* sV;
 };
 
 // Output tile of a finished chunk, held in registers and stored at the start
@@ -852,19 +874,11 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2], Ch
   const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
   const int ta = wave >> 1, kh = wave & 1;
   const int64_t row0 = x.bos + (int64_t)c * CH;
-  // 1. publish the V slice (transposed, [v][t]), the chunk's vectors and the
+  // 1. publish the V slice (row-major [t][v]), the chunk's vectors and the
   //    current state (fp16, [v][k]).  Every reader of these buffers in the
   //    previous chunk was before that chunk's last barrier.
   reinterpret_cast<u32x4*>(x.sVec)[8 * wave + (lane & 7)] = cur.vec;
-  {
-    const int s = tid >> 3, cq = tid & 7;
-    const uint32_t w2[2] = {cur.vraw[0], cur.vraw[1]};
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      x.sVt[(4 * cq + 2 * i) * SUS + s] = (uint16_t)(w2[i] & 0xffffu);
-      x.sVt[(4 * cq + 2 * i + 1) * SUS + s] = (uint16_t)(w2[i] >> 16);
-    }
-  }
+  *reinterpret_cast<u32x2*>(x.sV + (tid >> 3) * SVS + 4 * (tid & 7)) = cur.vraw;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int kk = 16 * wave + 4 * lg, vv = 16 * nt + li;
@@ -892,7 +906,7 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2], Ch
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int vv = 16 * nt + li;
-    const bf16x8 vbf = *reinterpret_cast<const bf16x8*>(x.sVt + vv * SUS + 32 * kh + 8 * lg);
+    const bf16x8 vbf = __builtin_bit_cast(bf16x8, lds_frag_tr(x.sV, SVS, 32 * kh, 16 * nt, lane));
     const half8 sb0 = *reinterpret_cast<const half8*>(x.sS + vv * SSS + 64 * kh + 8 * lg);
     const half8 sb1 = *reinterpret_cast<const half8*>(x.sS + vv * SSS + 64 * kh + 32 + 8 * lg);
     f32x4 u0 = f32x4{0, 0, 0, 0}, u1 = f32x4{0, 0, 0, 0}, o0 = f32x4{0, 0, 0, 0};
@@ -981,7 +995,7 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
   __shared__ __attribute__((aligned(16))) _Float16 sS[VS * SSS];
   __shared__ __attribute__((aligned(16))) _Float16 sUh[VS * SUS];
   __shared__ __attribute__((aligned(16))) _Float16 sUl[VS * SUS];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[VS * SUS];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[CH * SVS];
 
   // XCD-aware decode: the NSLICE slices of one chain share (id mod 8), so they
   // are dispatched to the same XCD and share its L2 for the chain's operands.
@@ -1023,7 +1037,7 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
   }
 
   const uint8_t* wsh = ws + (size_t)h * max_chunks * BLOCK;
-  StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, lane, li, lg, sPart, sVec, sS, sUh, sUl, sVt};
+  StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, lane, li, lg, sPart, sVec, sS, sUh, sUl, sV};
   ChunkRegs rA, rB, rC;
   if (nc > 0) {
     load_chunk(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
