@@ -736,79 +736,72 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // ---------------------------------------------------------------------------
 // inter-chunk state kernel
 //
-// One workgroup of 8 waves per (sequence, v-head, 32-wide V slice), sequential
-// over the sequence's chunks with the fp32 state slice S^T[k][v] in registers
-// (wave w owns key rows 16w..16w+15, both 16-wide V tiles).  Per chunk:
+// One workgroup of 4 waves (one per SIMD) per (sequence, v-head, 32-wide V
+// slice), sequential over the sequence's chunks with the fp32 state slice
+// S^T[k][v] in registers.  Wave w owns key rows 32w..32w+31 (key tiles 2w and
+// 2w+1) of the state, for both 16-wide V tiles, and token tile w of U and O.
+// Per chunk:
 //     U = T diag(b) V - W S^T
 //     O = qs . (Q . 2^G) S^T + Aqk U'   with U' = rk . U
 //     S <- S Diag(2^G_last) + U'^T (K . 2^(G_last - G))
-// The U and O products are split between the two waves of a pair by their
-// contraction: wave (ta, kh) takes token tile ta and key half kh of W S^T and
-// Q S^T, and token half kh of T diag(b) V.  Each wave therefore loads only its
-// own operand fragments -- the 57 shared fragments of a chunk are read once
-// per workgroup, with no copy through LDS -- and the pair exchanges one
-// partial tile each through LDS.  Operands are loaded two chunks ahead into
-// registers; 8 waves keep enough requests in flight per CU for the
-// L2-shared operands of the V slices of one chain (dispatched to one XCD).
-constexpr int SWAVES = 8;
-constexpr int SSS = 136;  // sS row stride (fp16), S^T slice stored as [v][k]
-constexpr int SUS = 72;   // sU row stride (16-bit)
+// Every wave contracts over the full key (or token) range itself, so the only
+// exchanges are the state (fp16, for W S^T and Q S^T) and U' (hi/lo, for the
+// state update): two barriers per chunk.  Each operand fragment of a chunk is
+// loaded by exactly one wave, straight into registers: the token-tile
+// operands (W, Q . 2^G, T diag(b), Aqk) two chunks ahead, the key-tile
+// operands (Kd) one chunk ahead -- they are needed only after the second
+// barrier.  The V slices of one chain run on one XCD and share its L2.
+constexpr int SWAVES = 4;
+constexpr int SSS = 136;  // sS row stride (fp16): state slice stored as [v][k]
+constexpr int SUS = 72;   // sU row stride (fp16): U' stored as [v][t]
 constexpr int SVS = 48;   // sV row stride (16-bit): V slice row-major [t][v]
 
 struct ChunkRegs {
-  // named members: register arrays indexed before unrolling would be left in
-  // scratch memory
-  u32x4 wn0, wn1, qg0, qg1;   // -W and Q . 2^G: token tile ta, key blocks 2kh, 2kh+1
-  u32x4 tbh, tbl;             // T diag(b) hi/lo: token tile ta, token block kh
-  u32x4 aq0, aq1;             // Aqk: token tile ta, token blocks 0, 1
-  u32x4 kd0, kd1, kd2, kd3;   // Kd^T of key tile w: (block 0, hi) (block 0, lo) (block 1, hi) (block 1, lo)
-  u32x4 vec;                  // 16 B of the vector fragment: bytes 128 w + 16 (lane & 7) ..
-  u32x2 vraw;                 // 4 values of the V slice: row tid >> 3, columns 4 (tid & 7) ..
+  // arrays indexed only by compile-time values (fully unrolled loops)
+  u32x4 wn[4], qg[4];        // -W, Q . 2^G: token tile w, key blocks 0..3
+  u32x4 tbh[2], tbl[2];      // T diag(b) hi/lo: token tile w, token blocks 0, 1
+  u32x4 aq[2];               // Aqk: token tile w, token blocks 0, 1
+  u32x4 vec;                 // bytes 256 w + 16 (lane & 15) of the vector fragment
+  u32x4 vraw;                // V slice: row tid >> 2, columns 8 (tid & 3) ..
+  u32x4 kd[2][2][2];         // Kd^T: key tile 2w + j, token block b, hi/lo
 };
 
 __device__ __forceinline__ u32x4 ld_frag(const uint8_t* blk, int fr, int lane) {
   return *reinterpret_cast<const u32x4*>(blk + fr * FRAG + lane * 16);
 }
 
-// The prefetch of one chunk, issued in three parts spread over the previous
-// chunk's work so the memory pipeline drains while the wave computes.
+// PART 0: token-tile operands, vectors and V (issued two chunks ahead);
+// PART 1: key-tile operands (issued one chunk ahead).
 template <int PART>
 __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk, int wave, int lane,
                                                 const uint16_t* __restrict__ v, int64_t row0, int len, int Hv, int h,
                                                 int v0, int tid) {
-  const int ta = wave >> 1, kh = wave & 1;
   if constexpr (PART == 0) {
-    o.wn0 = ld_frag(blk, F_WN + ta * 4 + 2 * kh, lane);
-    o.wn1 = ld_frag(blk, F_WN + ta * 4 + 2 * kh + 1, lane);
-    o.qg0 = ld_frag(blk, F_QG + ta * 4 + 2 * kh, lane);
-    o.qg1 = ld_frag(blk, F_QG + ta * 4 + 2 * kh + 1, lane);
-  } else if constexpr (PART == 1) {
-    o.tbh = ld_frag(blk, F_TBH + ta * 2 + kh, lane);
-    o.tbl = ld_frag(blk, F_TBL + ta * 2 + kh, lane);
-    o.aq0 = ld_frag(blk, F_AQK + ta * 2, lane);
-    o.aq1 = ld_frag(blk, F_AQK + ta * 2 + 1, lane);
-  } else {
-    o.kd0 = ld_frag(blk, F_KD + wave * 4, lane);
-    o.kd1 = ld_frag(blk, F_KD + wave * 4 + 1, lane);
-    o.kd2 = ld_frag(blk, F_KD + wave * 4 + 2, lane);
-    o.kd3 = ld_frag(blk, F_KD + wave * 4 + 3, lane);
-    // each wave fetches one 128-byte eighth of the vector fragment (every lane
-    // group of 8 the same bytes) and publishes it through LDS
-    o.vec = ld_frag(blk, F_VEC, 8 * wave + (lane & 7));
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      o.wn[kb] = ld_frag(blk, F_WN + wave * 4 + kb, lane);
+      o.qg[kb] = ld_frag(blk, F_QG + wave * 4 + kb, lane);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      o.tbh[kb] = ld_frag(blk, F_TBH + wave * 2 + kb, lane);
+      o.tbl[kb] = ld_frag(blk, F_TBL + wave * 2 + kb, lane);
+      o.aq[kb] = ld_frag(blk, F_AQK + wave * 2 + kb, lane);
+    }
+    o.vec = ld_frag(blk, F_VEC, 16 * wave + (lane & 15));
     // rows s >= len lie beyond the buffer range and read as zero
-    const int s = tid >> 3, cq = tid & 7;
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + ((size_t)row0 * Hv + h) * DV + v0, (uint32_t)len * Hv * DV * 2);
-    const auto vv = __builtin_amdgcn_raw_buffer_load_b64(rv, (s * Hv * DV + 4 * cq) * 2, 0, 0);
-    o.vraw = __builtin_bit_cast(u32x2, vv);
+    o.vraw = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ((tid >> 2) * Hv * DV + 8 * (tid & 3)) * 2, 0, 0));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int part = 0; part < 2; ++part)
+          o.kd[j][b][part] = ld_frag(blk, F_KD + ((2 * wave + j) * 2 + b) * 2 + part, lane);
   }
-}
-
-__device__ __forceinline__ void load_chunk(ChunkRegs& o, const uint8_t* blk, int wave, int lane,
-                                           const uint16_t* __restrict__ v, int64_t row0, int len, int Hv, int h,
-                                           int v0, int tid) {
-  load_chunk_part<0>(o, blk, wave, lane, v, row0, len, Hv, h, v0, tid);
-  load_chunk_part<1>(o, blk, wave, lane, v, row0, len, Hv, h, v0, tid);
-  load_chunk_part<2>(o, blk, wave, lane, v, row0, len, Hv, h, v0, tid);
 }
 
 struct StateCtx {
@@ -817,7 +810,6 @@ struct StateCtx {
   const uint8_t* wsh;
   int64_t bos, seqlen;
   int x0, nc, Hv, h, v0, tid, wave, lane, li, lg;
-  f32x4* sPart;
   float* sVec;
   _Float16* sS;
   _Float16* sUh;
@@ -825,30 +817,35 @@ struct StateCtx {
   _Float16* sV;
 };
 
-// Output tile of a finished chunk, held in registers and stored at the start
+// Output tiles of a finished chunk, held in registers and stored at the start
 // of the next chunk, before that chunk's prefetch: stores count in vmcnt like
 // loads, so a store queued behind a prefetch would lengthen the operand wait.
 struct PendingOut {
-  uint16_t o[4];
+  uint16_t o[2][4];
   int64_t row0;
   int len;
 };
 
-// wave (ta, kh) stores the 16 x 16 output tile of token tile ta, V tile kh
+// wave w stores the output tiles of token tile w, V tiles 0 and 1
 __device__ __forceinline__ void store_pending(const PendingOut& pd, uint16_t* __restrict__ out, int Hv, int h,
-                                              int v0, int ta, int vt, int li, int lg) {
+                                              int v0, int wave, int li, int lg) {
   // rows t >= len fall outside the buffer range and are dropped
   const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(out + ((size_t)pd.row0 * Hv + h) * DV + v0, (uint32_t)pd.len * Hv * DV * 2);
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int t = 16 * ta + 4 * lg + rr;
-    __builtin_amdgcn_raw_buffer_store_b16((short)pd.o[rr], ro, (t * Hv * DV + 16 * vt + li) * 2, 0, 0);
-  }
+  for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int t = 16 * wave + 4 * lg + rr;
+      __builtin_amdgcn_raw_buffer_store_b16((short)pd.o[vt][rr], ro, (t * Hv * DV + 16 * vt + li) * 2, 0, 0);
+    }
 }
 
 __device__ __forceinline__ int chunk_len(const StateCtx& x, int c) {
   return (int)min((int64_t)CH, x.seqlen - (int64_t)c * CH);
 }
+
+__device__ __forceinline__ half8 as_half8(const u32x4& u) { return __builtin_bit_cast(half8, u); }
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
 
 // An empty use that forces the registers to be loaded here: issued once before
 // the chunk loop, it completes the initial state and first chunk's loads
@@ -857,130 +854,126 @@ __device__ __forceinline__ int chunk_len(const StateCtx& x, int c) {
 // every iteration).
 __device__ __forceinline__ void settle(const u32x4& a) { asm volatile("" ::"v"(a)); }
 __device__ __forceinline__ void settle(const f32x4& a) { asm volatile("" ::"v"(a)); }
-__device__ __forceinline__ void settle(const u32x2& a) { asm volatile("" ::"v"(a)); }
 __device__ __forceinline__ void settle(const ChunkRegs& r) {
-  settle(r.wn0); settle(r.wn1); settle(r.qg0); settle(r.qg1); settle(r.tbh); settle(r.tbl);
-  settle(r.aq0); settle(r.aq1); settle(r.kd0); settle(r.kd1); settle(r.kd2); settle(r.kd3);
-  settle(r.vec); settle(r.vraw);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) { settle(r.wn[kb]); settle(r.qg[kb]); }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) { settle(r.tbh[kb]); settle(r.tbl[kb]); settle(r.aq[kb]); }
+  settle(r.vec);
+  settle(r.vraw);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) { settle(r.kd[j][b][0]); settle(r.kd[j][b][1]); }
 }
 
-__device__ __forceinline__ half8 as_half8(const u32x4& u) { return __builtin_bit_cast(half8, u); }
-__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
-
-// One chunk of the state chain: `cur` holds chunk c (loaded two chunks ago),
-// `n2` receives chunk c+2.
-__device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2], ChunkRegs& cur, ChunkRegs& n2,
-                                            const int c, PendingOut& pd) {
+// One chunk of the state chain: `cur` holds chunk c, `n1` receives the key-tile
+// operands of chunk c+1, `n2` the token-tile operands of chunk c+2.
+__device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2], ChunkRegs& cur, ChunkRegs& n1,
+                                            ChunkRegs& n2, const int c, PendingOut& pd) {
   const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
-  const int ta = wave >> 1, kh = wave & 1;
   const int64_t row0 = x.bos + (int64_t)c * CH;
-  // 1. publish the V slice (row-major [t][v]), the chunk's vectors and the
-  //    current state (fp16, [v][k]).  Every reader of these buffers in the
-  //    previous chunk was before that chunk's last barrier.
-  reinterpret_cast<u32x4*>(x.sVec)[8 * wave + (lane & 7)] = cur.vec;
-  *reinterpret_cast<u32x2*>(x.sV + (tid >> 3) * SVS + 4 * (tid & 7)) = cur.vraw;
+  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+  // 1. publish the chunk's vectors, the V slice and the current state.  Every
+  //    reader of these buffers in the previous chunk was before its B2.
+  reinterpret_cast<u32x4*>(x.sVec)[16 * wave + (lane & 15)] = cur.vec;
+  *reinterpret_cast<u32x4*>(x.sV + (tid >> 2) * SVS + 8 * (tid & 3)) = cur.vraw;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int kk = 16 * wave + 4 * lg, vv = 16 * nt + li;
-    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-    half4 hv = {(_Float16)S[nt][0], (_Float16)S[nt][1], (_Float16)S[nt][2], (_Float16)S[nt][3]};
-    *reinterpret_cast<half4*>(x.sS + vv * SSS + kk) = hv;
-  }
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt) {
+      const half4 hv = {(_Float16)S[j][vt][0], (_Float16)S[j][vt][1], (_Float16)S[j][vt][2], (_Float16)S[j][vt][3]};
+      *reinterpret_cast<half4*>(x.sS + (16 * vt + li) * SSS + 32 * wave + 16 * j + 4 * lg) = hv;
+    }
   // 2. the previous chunk's outputs (none before the first chunk: len 0), then
-  //    the first part of the prefetch of chunk c+2 (clamped, so every chunk
-  //    queues the same operations)
-  store_pending(pd, x.out, x.Hv, x.h, x.v0, ta, kh, li, lg);
-  const int cp2 = min(c + 2, x.nc - 1);
-  const uint8_t* blk2 = x.wsh + (size_t)(x.x0 + cp2) * BLOCK;
-  const int64_t row2 = x.bos + (int64_t)cp2 * CH;
-  const int len2 = chunk_len(x, cp2);
-  load_chunk_part<0>(n2, blk2, wave, lane, x.v, row2, len2, x.Hv, x.h, x.v0, tid);
+  //    the token-tile prefetch of chunk c+2 (clamped, so every chunk queues the
+  //    same operations)
+  store_pending(pd, x.out, x.Hv, x.h, x.v0, wave, li, lg);
+  {
+    const int cp = min(c + 2, x.nc - 1);
+    load_chunk_part<0>(n2, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, x.bos + (int64_t)cp * CH,
+                       chunk_len(x, cp), x.Hv, x.h, x.v0, tid);
+  }
   __syncthreads();  // B1
-  const f32x4 gn = *reinterpret_cast<const f32x4*>(x.sVec + 16 * wave + 4 * lg);
-  const f32x4 qs = *reinterpret_cast<const f32x4*>(x.sVec + 128 + 16 * ta + 4 * lg);
-  const f32x4 rk = *reinterpret_cast<const f32x4*>(x.sVec + 192 + 16 * ta + 4 * lg);
-  // 3. this wave's halves of U and O for both V tiles:
-  //    pu = T diag(b)[ta, token half kh] V + (-W)[ta, key half kh] S^T,
-  //    po = (Q . 2^G)[ta, key half kh] S^T
-  f32x4 pu[2], po[2];
+  // 3. U and O of token tile w for both V tiles, full contractions
+  const f32x4 qs = *reinterpret_cast<const f32x4*>(x.sVec + 128 + 16 * wave + 4 * lg);
+  const f32x4 rk = *reinterpret_cast<const f32x4*>(x.sVec + 192 + 16 * wave + 4 * lg);
+  const f32x4 gn0 = *reinterpret_cast<const f32x4*>(x.sVec + 32 * wave + 4 * lg);
+  const f32x4 gn1 = *reinterpret_cast<const f32x4*>(x.sVec + 32 * wave + 16 + 4 * lg);
+  f32x4 U[2], O[2];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int vv = 16 * nt + li;
-    const bf16x8 vbf = __builtin_bit_cast(bf16x8, lds_frag_tr(x.sV, SVS, 32 * kh, 16 * nt, lane));
-    const half8 sb0 = *reinterpret_cast<const half8*>(x.sS + vv * SSS + 64 * kh + 8 * lg);
-    const half8 sb1 = *reinterpret_cast<const half8*>(x.sS + vv * SSS + 64 * kh + 32 + 8 * lg);
-    f32x4 u0 = f32x4{0, 0, 0, 0}, u1 = f32x4{0, 0, 0, 0}, o0 = f32x4{0, 0, 0, 0};
-    u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh), vbf, u0, 0, 0, 0);
-    u1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn0), sb0, u1, 0, 0, 0);
-    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg0), sb0, o0, 0, 0, 0);
-    u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl), vbf, u0, 0, 0, 0);
-    u1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn1), sb1, u1, 0, 0, 0);
-    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg1), sb1, o0, 0, 0, 0);
-    pu[nt] = u0 + u1;
-    po[nt] = o0;
+  for (int vt = 0; vt < 2; ++vt) {
+    const bf16x8 vb0 = __builtin_bit_cast(bf16x8, lds_frag_tr(x.sV, SVS, 0, 16 * vt, lane));
+    const bf16x8 vb1 = __builtin_bit_cast(bf16x8, lds_frag_tr(x.sV, SVS, 32, 16 * vt, lane));
+    half8 sb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
+    f32x4 u0 = f32x4{0, 0, 0, 0}, u1 = f32x4{0, 0, 0, 0}, o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
+    u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[0]), vb0, u0, 0, 0, 0);
+    u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[0]), vb0, u1, 0, 0, 0);
+    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[0]), sb[0], o0, 0, 0, 0);
+    o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[1]), sb[1], o1, 0, 0, 0);
+    u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[1]), vb1, u0, 0, 0, 0);
+    u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[1]), vb1, u1, 0, 0, 0);
+    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[2]), sb[2], o0, 0, 0, 0);
+    o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[3]), sb[3], o1, 0, 0, 0);
+#pragma unroll
+    for (int kb = 0; kb < 4; kb += 2) {
+      u0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[kb]), sb[kb], u0, 0, 0, 0);
+      u1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[kb + 1]), sb[kb + 1], u1, 0, 0, 0);
+    }
+    U[vt] = u0 + u1;
+    O[vt] = (o0 + o1) * qs;
   }
-  // the partner (same ta, other kh) owns V tile 1 - kh: send it that tile
+  // 4. the key-tile prefetch of chunk c+1
+  __builtin_amdgcn_sched_barrier(0);
   {
-    f32x4* mine = x.sPart + (size_t)wave * 2 * 64;
-    mine[lane] = kh ? pu[0] : pu[1];
-    mine[64 + lane] = kh ? po[0] : po[1];
+    const int cp = min(c + 1, x.nc - 1);
+    load_chunk_part<1>(n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
   }
   __builtin_amdgcn_sched_barrier(0);
-  load_chunk_part<1>(n2, blk2, wave, lane, x.v, row2, len2, x.Hv, x.h, x.v0, tid);
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();  // B2
-  // 4. U and O of (ta, V tile kh); U' = rk . U -> LDS hi/lo, transposed [v][t]
-  f32x4 O;
-  {
-    const f32x4* theirs = x.sPart + (size_t)(wave ^ 1) * 2 * 64;
-    const f32x4 U = (kh ? pu[1] : pu[0]) + theirs[lane];
-    O = ((kh ? po[1] : po[0]) + theirs[64 + lane]) * qs;
-    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+  // 5. U' = rk . U -> LDS hi/lo, transposed [v][t]
+#pragma unroll
+  for (int vt = 0; vt < 2; ++vt) {
     half4 hi, lo;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const float up = U[rr] * rk[rr];
+      const float up = U[vt][rr] * rk[rr];
       const _Float16 hh = (_Float16)up;
       hi[rr] = hh;
       lo[rr] = (_Float16)(up - (float)hh);
     }
-    const int vv = 16 * kh + li, tt = 16 * ta + 4 * lg;
+    const int vv = 16 * vt + li, tt = 16 * wave + 4 * lg;
     *reinterpret_cast<half4*>(x.sUh + vv * SUS + tt) = hi;
     *reinterpret_cast<half4*>(x.sUl + vv * SUS + tt) = lo;
   }
-  __syncthreads();  // B3
-  // 5. S <- S Diag(2^G_last) + U'^T Kd ;  O += Aqk U'
-  __builtin_amdgcn_sched_barrier(0);
-  load_chunk_part<2>(n2, blk2, wave, lane, x.v, row2, len2, x.Hv, x.h, x.v0, tid);
-  __builtin_amdgcn_sched_barrier(0);
-  const half8 kdh0 = as_half8(cur.kd0), kdl0 = as_half8(cur.kd1);
-  const half8 kdh1 = as_half8(cur.kd2), kdl1 = as_half8(cur.kd3);
-  half8 ua0, ua1;  // U' hi of V tile kh, token blocks 0 and 1
+  __syncthreads();  // B2
+  // 6. S <- S Diag(2^G_last) + U'^T Kd ;  O += Aqk U'  (Aqk of token tiles 0,
+  //    1 is zero in token block 1, so that product adds nothing there)
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const half8 uh0 = *reinterpret_cast<const half8*>(x.sUh + (16 * nt + li) * SUS + 8 * lg);
-    const half8 uh1 = *reinterpret_cast<const half8*>(x.sUh + (16 * nt + li) * SUS + 32 + 8 * lg);
-    const half8 ul0 = *reinterpret_cast<const half8*>(x.sUl + (16 * nt + li) * SUS + 8 * lg);
-    const half8 ul1 = *reinterpret_cast<const half8*>(x.sUl + (16 * nt + li) * SUS + 32 + 8 * lg);
-    f32x4 sa = S[nt] * gn, sb2 = f32x4{0, 0, 0, 0};
-    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdh0, uh0, sa, 0, 0, 0);
-    sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdh1, uh1, sb2, 0, 0, 0);
-    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdh0, ul0, sa, 0, 0, 0);
-    sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdh1, ul1, sb2, 0, 0, 0);
-    sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdl0, uh0, sa, 0, 0, 0);
-    sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdl1, uh1, sb2, 0, 0, 0);
-    S[nt] = sa + sb2;
-    if (nt == 0) { ua0 = uh0; ua1 = uh1; }
-    else { ua0 = kh ? uh0 : ua0; ua1 = kh ? uh1 : ua1; }
-  }
-  // V tile kh; Aqk of token tiles 0, 1 is zero in token block 1, so the second
-  // product adds nothing there
-  O = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq0), ua0, O, 0, 0, 0);
-  O = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq1), ua1, O, 0, 0, 0);
+  for (int vt = 0; vt < 2; ++vt) {
+    const half8 uh0 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 8 * lg);
+    const half8 uh1 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 32 + 8 * lg);
+    const half8 ul0 = *reinterpret_cast<const half8*>(x.sUl + (16 * vt + li) * SUS + 8 * lg);
+    const half8 ul1 = *reinterpret_cast<const half8*>(x.sUl + (16 * vt + li) * SUS + 32 + 8 * lg);
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    pd.o[rr] = __builtin_bit_cast(uint16_t, (__bf16)O[rr]);
+    for (int j = 0; j < 2; ++j) {
+      f32x4 sa = S[j][vt] * (j == 0 ? gn0 : gn1), sb2 = f32x4{0, 0, 0, 0};
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0][0]), uh0, sa, 0, 0, 0);
+      sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1][0]), uh1, sb2, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0][0]), ul0, sa, 0, 0, 0);
+      sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1][0]), ul1, sb2, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0][1]), uh0, sa, 0, 0, 0);
+      sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1][1]), uh1, sb2, 0, 0, 0);
+      S[j][vt] = sa + sb2;
+    }
+    O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[0]), uh0, O[vt], 0, 0, 0);
+    O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[1]), uh1, O[vt], 0, 0, 0);
   }
+#pragma unroll
+  for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) pd.o[vt][rr] = __builtin_bit_cast(uint16_t, (__bf16)O[vt][rr]);
   pd.row0 = row0;
   pd.len = chunk_len(x, c);
 }
@@ -990,7 +983,6 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
                  const int* __restrict__ chunk_off, const void* __restrict__ h0, void* __restrict__ hT,
                  uint16_t* __restrict__ out, const uint8_t* __restrict__ ws,
                  int B, int T, int N, int Hv, int max_chunks, int init_dtype, int final_dtype) {
-  __shared__ __attribute__((aligned(16))) f32x4 sPart[SWAVES * 2 * 64];
   __shared__ __attribute__((aligned(16))) float sVec[256];
   __shared__ __attribute__((aligned(16))) _Float16 sS[VS * SSS];
   __shared__ __attribute__((aligned(16))) _Float16 sUh[VS * SUS];
@@ -1019,64 +1011,69 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
     x0 = chunk_off[n]; nc = chunk_off[n + 1] - x0;
   }
 
-  // state tiles: S^T[k][v], k = 16*wave + 4*lg + r, v = v0 + 16*nt + li
-  f32x4 S[2];
+  // state tiles S^T[k][v]: k = 32 wave + 16 j + 4 lg + r, v = v0 + 16 vt + li
+  f32x4 S[2][2];
   const size_t sbase = ((size_t)n * Hv + h) * DV * DK;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int kk = 16 * wave + 4 * lg, vv = v0 + 16 * nt + li;
-    f32x4 s = f32x4{0, 0, 0, 0};
-    if (init_dtype == KDA_STATE_F32) {
-      s = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(h0) + sbase + (size_t)vv * DK + kk);
-    } else if (init_dtype == KDA_STATE_BF16) {
-      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(h0) + sbase + (size_t)vv * DK + kk);
-      s = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt) {
+      const int kk = 32 * wave + 16 * j + 4 * lg, vv = v0 + 16 * vt + li;
+      f32x4 s = f32x4{0, 0, 0, 0};
+      if (init_dtype == KDA_STATE_F32) {
+        s = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(h0) + sbase + (size_t)vv * DK + kk);
+      } else if (init_dtype == KDA_STATE_BF16) {
+        const uint2 u =
+            *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(h0) + sbase + (size_t)vv * DK + kk);
+        s = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                  __uint_as_float(u.y & 0xffff0000u)};
+      }
+      S[j][vt] = s;
     }
-    S[nt] = s;
-  }
 
   const uint8_t* wsh = ws + (size_t)h * max_chunks * BLOCK;
-  StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, lane, li, lg, sPart, sVec, sS, sUh, sUl, sV};
+  StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, lane, li, lg, sVec, sS, sUh, sUl, sV};
   ChunkRegs rA, rB, rC;
   if (nc > 0) {
-    load_chunk(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
+    load_chunk_part<0>(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
+    load_chunk_part<1>(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, 0, 0, Hv, h, v0, tid);
     const int c1 = min(1, nc - 1);
-    load_chunk(rB, wsh + (size_t)(x0 + c1) * BLOCK, wave, lane, v, bos + (int64_t)c1 * CH, chunk_len(ctx, c1), Hv,
-               h, v0, tid);
+    load_chunk_part<0>(rB, wsh + (size_t)(x0 + c1) * BLOCK, wave, lane, v, bos + (int64_t)c1 * CH,
+                       chunk_len(ctx, c1), Hv, h, v0, tid);
   }
-  settle(S[0]);
-  settle(S[1]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) { settle(S[j][0]); settle(S[j][1]); }
   settle(rA);
   PendingOut pd;
   pd.row0 = bos;
   pd.len = 0;
   int c = 0;
   for (; c + 3 <= nc; c += 3) {
-    state_chunk(ctx, S, rA, rC, c, pd);
-    state_chunk(ctx, S, rB, rA, c + 1, pd);
-    state_chunk(ctx, S, rC, rB, c + 2, pd);
+    state_chunk(ctx, S, rA, rB, rC, c, pd);
+    state_chunk(ctx, S, rB, rC, rA, c + 1, pd);
+    state_chunk(ctx, S, rC, rA, rB, c + 2, pd);
   }
-  if (c < nc) state_chunk(ctx, S, rA, rC, c, pd);
-  if (c + 1 < nc) state_chunk(ctx, S, rB, rA, c + 1, pd);
-  store_pending(pd, out, Hv, h, v0, wave >> 1, wave & 1, li, lg);
+  if (c < nc) state_chunk(ctx, S, rA, rB, rC, c, pd);
+  if (c + 1 < nc) state_chunk(ctx, S, rB, rC, rA, c + 1, pd);
+  store_pending(pd, out, Hv, h, v0, wave, li, lg);
 
   if (final_dtype != KDA_STATE_NONE) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int kk = 16 * wave + 4 * lg, vv = v0 + 16 * nt + li;
-      if (final_dtype == KDA_STATE_F32) {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(hT) + sbase + (size_t)vv * DK + kk) = S[nt];
-      } else {
-        __bf16 bb[4];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bb[r] = (__bf16)S[nt][r];
-        uint2 u;
-        u.x = (uint32_t)(*reinterpret_cast<uint16_t*>(&bb[0])) | ((uint32_t)(*reinterpret_cast<uint16_t*>(&bb[1])) << 16);
-        u.y = (uint32_t)(*reinterpret_cast<uint16_t*>(&bb[2])) | ((uint32_t)(*reinterpret_cast<uint16_t*>(&bb[3])) << 16);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(hT) + sbase + (size_t)vv * DK + kk) = u;
+      for (int vt = 0; vt < 2; ++vt) {
+        const int kk = 32 * wave + 16 * j + 4 * lg, vv = v0 + 16 * vt + li;
+        if (final_dtype == KDA_STATE_F32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(hT) + sbase + (size_t)vv * DK + kk) = S[j][vt];
+        } else {
+          uint2 u;
+          u.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][0]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][1]) << 16);
+          u.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][2]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][3]) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(hT) + sbase + (size_t)vv * DK + kk) = u;
+        }
       }
-    }
   }
 }
 
