@@ -189,8 +189,6 @@ constexpr int AS = 68;      // fp32 row stride of Akk / T
 constexpr int AQS = 72;     // fp16 row stride of Aqk
 constexpr int KER = 144;    // fp16 row stride of the row-major [t][k] K . 2^G and Kd tiles
 constexpr int WTS = 80;     // fp16 row stride of the [k][t] W staging tile
-constexpr int GS = 132;     // fp32 row stride of Gamma (softplus pairwise only)
-constexpr int QS = 136;     // bf16 row stride of raw q, k (softplus pairwise only)
 constexpr int NVEC = 19;    // per-channel vectors: P0..3, L0..3, D20, D30, D31, Mr0..3, Mc0..3
 constexpr int V_P = 0, V_L = 4, V_D20 = 8, V_D30 = 9, V_D31 = 10, V_MR = 11, V_MC = 15;
 
@@ -211,12 +209,8 @@ constexpr int L_RQ = L_AQ + 64 * AQS * 2;
 constexpr int L_RK = L_RQ + 64 * 4;
 constexpr int L_BETA = L_RK + 64 * 4;
 constexpr int L_FW = L_BETA + 64 * 4;
-constexpr int L_END = L_FW + 64 * 4;
-// softplus only: Gamma and raw q, k rows for the pairwise diagonal
-constexpr int L_PG = L_END;
-constexpr int L_PQ = L_PG + 64 * GS * 4;
-constexpr int L_PK = L_PQ + 64 * QS * 2;
-constexpr int L_END_SP = L_PK + 64 * QS * 2;
+constexpr int L_QD = L_FW + 64 * 4;    // softplus: q_i . k_i per row [64] f32
+constexpr int L_END = L_QD + 64 * 4;
 static_assert(L_VEC + NVEC * 128 * 4 <= L_T + T_BYTES, "vectors fit in region T");
 static_assert(64 * AS * 4 <= X_BYTES, "Akk fits in region X");
 static_assert(128 * WTS * 2 <= X_BYTES, "W staging fits in region X");
@@ -263,6 +257,52 @@ __device__ __forceinline__ half8 to_half8(const float* v) {
   return h;
 }
 
+// Softplus diagonal block.  The per-token decay is unbounded, so no single
+// reference row keeps both factors of every pair in range.  Instead the block
+// is split by levels: at level L the rows form blocks of 2^(4-L) with halves
+// of 2^(3-L); every pair i > j lies in exactly one (lower half, upper half)
+// rectangle -- the level of the highest bit where i and j differ -- and with
+// the reference p = last row of the upper half both factors
+// 2^(Gamma_i - Gamma_p) and 2^(Gamma_p - Gamma_j) are <= 1.  Each row is in
+// the lower half (a row operand) or the upper half (a column operand) of its
+// level block, so one factor 2^-|Gamma_r - Gamma_p| per element and level
+// suffices, and a level is one fp16 product over the channels; products of
+// rows and columns from different level blocks are discarded afterwards.
+// The reference value sits in another lane of the same 16-lane row.
+template <int L>
+__device__ __forceinline__ float level_ref(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  int r;
+  if constexpr (L == 0) {
+    r = __builtin_amdgcn_ds_swizzle(xi, 0xF0);  // lane (i & 0x10) | 7 of each 32: row 7
+  } else if constexpr (L == 1) {
+    const int t = __builtin_amdgcn_update_dpp(0, xi, 0xFF, 0xf, 0xf, false);  // quad_perm 3,3,3,3
+    r = __builtin_amdgcn_update_dpp(t, t, 0x114, 0xf, 0xA, false);            // row_shr:4 into lanes 4-7, 12-15
+  } else if constexpr (L == 2) {
+    r = __builtin_amdgcn_update_dpp(0, xi, 0x55, 0xf, 0xf, false);  // quad_perm 1,1,1,1
+  } else {
+    r = __builtin_amdgcn_update_dpp(0, xi, 0xA0, 0xf, 0xf, false);  // quad_perm 0,0,2,2
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+template <int L>
+__device__ __forceinline__ void diag_level(const float (&Gk)[8], const float (&kf)[8], const float (&qf)[8], int li,
+                                           f32x4& akk, f32x4& aqk) {
+  const bool lower = (li >> (3 - L)) & 1;
+  float a[8], aq[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float F = fast_exp2(-fabsf(Gk[e] - level_ref<L>(Gk[e])));
+    a[e] = kf[e] * F;
+    aq[e] = qf[e] * F;
+  }
+  const half8 ha = to_half8(a), hq = to_half8(aq), z = {};
+  const half8 A = lower ? ha : z, Aq = lower ? hq : z, Bc = lower ? z : ha;
+  akk = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bc, akk, 0, 0, 0);
+  aqk = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq, Bc, aqk, 0, 0, 0);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes
 // the 16 addresses are read as a 16 x 4 block M[s][e] of 16-bit values (4 at
 // each address) and lane i receives M[4e + (i >> 2)][i & 3], e = 0..3.
@@ -284,14 +324,14 @@ __device__ __forceinline__ u32x4 lds_frag_tr(const _Float16* tile, int ld, int k
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta,
                  const float* __restrict__ A_log, const float* __restrict__ dt_bias,
                  const int64_t* __restrict__ cu, const int* __restrict__ chunk_off,
                  int B, int T, int N, int Hqk, int Hv, int max_chunks,
                  float scale, float lower_bound, uint8_t* __restrict__ ws) {
-  constexpr int LDS = (MODE == KDA_GATE_SOFTPLUS) ? L_END_SP : L_END;
+  constexpr int LDS = L_END;
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
   uint8_t* sX = smem + L_X;                                          // mailbox / Kd staging / Akk / W staging
   float* sA = reinterpret_cast<float*>(smem + L_X);
@@ -307,6 +347,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   float* sRk = reinterpret_cast<float*>(smem + L_RK);
   float* sBeta = reinterpret_cast<float*>(smem + L_BETA);
   float* sFw = reinterpret_cast<float*>(smem + L_FW);
+  float* sQd = reinterpret_cast<float*>(smem + L_QD);
 
   const int x = blockIdx.x, h = blockIdx.y;
   ChunkPos cp;
@@ -389,20 +430,37 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         p4[1] = make_float4(G[kb][4], G[kb][5], G[kb][6], G[kb][7]);
       }
     }
-    if (MODE == KDA_GATE_SOFTPLUS) {
-      // local Gamma and raw q, k rows for the pairwise diagonal
-      float* sPG = reinterpret_cast<float*>(smem + L_PG);
-      uint16_t* sPQb = reinterpret_cast<uint16_t*>(smem + L_PQ);
-      uint16_t* sPKb = reinterpret_cast<uint16_t*>(smem + L_PK);
+  }
+  // safe gate: four partial accumulators of the diagonal block; softplus:
+  // one accumulator per level of the diagonal block
+  f32x4 dkkp[4], dqkp[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        float4* p4 = reinterpret_cast<float4*>(sPG + r * GS + 32 * kb + 8 * lg);
-        p4[0] = make_float4(G[kb][0], G[kb][1], G[kb][2], G[kb][3]);
-        p4[1] = make_float4(G[kb][4], G[kb][5], G[kb][6], G[kb][7]);
-        *reinterpret_cast<uint4*>(sPQb + r * QS + 32 * kb + 8 * lg) = qraw[kb];
-        *reinterpret_cast<uint4*>(sPKb + r * QS + 32 * kb + 8 * lg) = kraw[kb];
-      }
+  for (int j = 0; j < 4; ++j) { dkkp[j] = f32x4{0, 0, 0, 0}; dqkp[j] = f32x4{0, 0, 0, 0}; }
+  float qkd = 0.0f;
+  if constexpr (MODE == KDA_GATE_SOFTPLUS) {
+    // diagonal block by levels (see diag_level); its diagonal is q_i . k_i
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float qf[8], kf[8];
+      unpack_bf16x8(qraw[kb], qf);
+      unpack_bf16x8(kraw[kb], kf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qkd += qf[e] * kf[e];
+      // one level at a time keeps the temporaries of only one level live
+      diag_level<0>(G[kb], kf, qf, li, dkkp[0], dqkp[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      diag_level<1>(G[kb], kf, qf, li, dkkp[1], dqkp[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      diag_level<2>(G[kb], kf, qf, li, dkkp[2], dqkp[2]);
+      __builtin_amdgcn_sched_barrier(0);
+      diag_level<3>(G[kb], kf, qf, li, dkkp[3], dqkp[3]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  if constexpr (MODE == KDA_GATE_SOFTPLUS) {
+    qkd += __shfl_xor(qkd, 16);
+    qkd += __shfl_xor(qkd, 32);
+    if (lg == 0) sQd[r] = qkd;
   }
   __syncthreads();
 
@@ -448,9 +506,6 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // accumulators: the diagonal block, and off-diagonal blocks J = 0..2 (J < I);
   // all register arrays are indexed by compile-time values only
   f32x4 dkk = f32x4{0, 0, 0, 0}, dqk = f32x4{0, 0, 0, 0};
-  f32x4 dkkp[4], dqkp[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) { dkkp[j] = f32x4{0, 0, 0, 0}; dqkp[j] = f32x4{0, 0, 0, 0}; }
   f32x4 okk[3], oqk[3];
 #pragma unroll
   for (int J = 0; J < 3; ++J) { okk[J] = f32x4{0, 0, 0, 0}; oqk[J] = f32x4{0, 0, 0, 0}; }
@@ -546,39 +601,15 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
     if (MODE == KDA_GATE_SOFTPLUS) {
-      const float* sPG = reinterpret_cast<const float*>(smem + L_PG);
-      const uint16_t* sPQb = reinterpret_cast<const uint16_t*>(smem + L_PQ);
-      const uint16_t* sPKb = reinterpret_cast<const uint16_t*>(smem + L_PK);
-      const int s = 16 * I + li;
-      float kk[4] = {0, 0, 0, 0}, qk[4] = {0, 0, 0, 0};
-      for (int c0 = 0; c0 < DK; c0 += 8) {
-        float Gs[8], ks[8];
-        const float4* ps = reinterpret_cast<const float4*>(sPG + s * GS + c0);
-        float4 b0 = ps[0], b1 = ps[1];
-        Gs[0] = b0.x; Gs[1] = b0.y; Gs[2] = b0.z; Gs[3] = b0.w;
-        Gs[4] = b1.x; Gs[5] = b1.y; Gs[6] = b1.z; Gs[7] = b1.w;
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(sPKb + s * QS + c0), ks);
+      // pair (i, j), i > j, of the diagonal block belongs to the level of the
+      // highest bit in which i and j differ
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int ri = 16 * I + 4 * lg + rr;
-          float Gi[8], ki[8], qi[8];
-          const float4* pi = reinterpret_cast<const float4*>(sPG + ri * GS + c0);
-          float4 a0 = pi[0], a1 = pi[1];
-          Gi[0] = a0.x; Gi[1] = a0.y; Gi[2] = a0.z; Gi[3] = a0.w;
-          Gi[4] = a1.x; Gi[5] = a1.y; Gi[6] = a1.z; Gi[7] = a1.w;
-          unpack_bf16x8(*reinterpret_cast<const uint4*>(sPKb + ri * QS + c0), ki);
-          unpack_bf16x8(*reinterpret_cast<const uint4*>(sPQb + ri * QS + c0), qi);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float ex = fast_exp2(fminf(Gi[e] - Gs[e], 0.0f));
-            const float kse = ks[e] * ex;
-            kk[rr] += ki[e] * kse;
-            qk[rr] += qi[e] * kse;
-          }
-        }
+      for (int rr = 0; rr < 4; ++rr) {
+        const int xd = (4 * lg + rr) ^ li;
+        dkk[rr] = xd >= 8 ? dkkp[0][rr] : xd >= 4 ? dkkp[1][rr] : xd >= 2 ? dkkp[2][rr] : dkkp[3][rr];
+        const float vq = xd >= 8 ? dqkp[0][rr] : xd >= 4 ? dqkp[1][rr] : xd >= 2 ? dqkp[2][rr] : dqkp[3][rr];
+        dqk[rr] = xd == 0 ? sQd[16 * I + 4 * lg + rr] : vq;
       }
-      dkk = f32x4{kk[0], kk[1], kk[2], kk[3]};
-      dqk = f32x4{qk[0], qk[1], qk[2], qk[3]};
     }
   }
   __syncthreads();  // mailbox is dead
