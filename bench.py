@@ -91,8 +91,9 @@ def cpu_baseline(inp, out_gpu, state_gpu, budget_s=30.0):
         import dataclasses
         sub = dataclasses.replace(inp, q=np.ascontiguousarray(inp.q[:, :, :hq]), k=np.ascontiguousarray(inp.k[:, :, :hq]),
                                   v=np.ascontiguousarray(inp.v[:, :, :heads]), g=np.ascontiguousarray(inp.g[:, :, :heads]),
-                                  beta=np.ascontiguousarray(inp.beta[:, :, :heads]), A_log=inp.A_log[:heads],
-                                  dt_bias=inp.dt_bias[:heads],
+                                  beta=np.ascontiguousarray(inp.beta[:, :, :heads]),
+                                  A_log=None if inp.A_log is None else inp.A_log[:heads],
+                                  dt_bias=None if inp.dt_bias is None else inp.dt_bias[:heads],
                                   initial_state=None if inp.initial_state is None else
                                   np.ascontiguousarray(inp.initial_state[:, :heads]))
     t0 = time.perf_counter()

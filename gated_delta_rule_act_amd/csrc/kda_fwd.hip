@@ -15,9 +15,9 @@
 //       Akk = diag(b) (K Kt . 2^(Gi-Gj)) strictly lower and
 //       Aqk = (Q Kt . 2^(Gi-Gj)) lower incl. diagonal, on 16x16 sub-chunk
 //       blocks: off-diagonal blocks factor through the last row before the
-//       row block (both exponents <= 0), diagonal blocks either through the
-//       sub-chunk midpoint (safe gate: exponent span bounded by 8*|lb|) or
-//       pairwise on the VALU (softplus gate: unbounded per-token decay);
+//       row block (both exponents <= 0); diagonal blocks either through the
+//       sub-chunk midpoint (safe gate: exponent span bounded by 8*|lb|) or by
+//       binary levels with a reference row per level (unbounded decays);
 //       T = (I + Akk)^-1 by 16x16 forward substitution plus fp32-MFMA block
 //       merges; WY factors W = T diag(b) (K . 2^G) and T diag(b) for u.
 //   kda_state_kernel  one workgroup per (sequence, v-head, 32-wide V slice),
@@ -25,11 +25,12 @@
 //       registers:  U = T diag(b) V - W S^T,  O = (Q . 2^G) S^T + Aqk U,
 //       S <- S Diag(2^G_last) + U^T (K . 2^(G_last - G)).
 //
-// Precision: 16-bit MFMA operands with fp32 accumulation; the contraction that
-// writes the state (U^T Kd) uses a 3-product fp16 hi/lo split, the diagonal
-// midpoint blocks (exponents up to 2^58) use bf16 with a hi/lo split on Akk,
-// and T is computed in fp32.  The exp2 operands are always differences of
-// Gamma values, never ratios of exponentials.
+// Precision: 16-bit MFMA operands with fp32 accumulation.  The contraction
+// that writes the state (U^T Kd) uses a 3-product fp16 hi/lo split, T diag(b)
+// enters U as bf16 hi/lo against exact bf16 V, the midpoint diagonal blocks
+// (factors up to 2^58) run on the fp32 MFMA, and T is computed in fp32.  The
+// exp2 operands are always differences of Gamma values, never ratios of
+// exponentials.
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdint.h>
@@ -183,8 +184,8 @@ __device__ __forceinline__ bool chunk_pos(int x, int B, int T, int N, const int6
 // factors <= 1, fp16 MFMA.  Diagonal block, safe gate: rows kR Mr against
 // columns kC Mc, i.e. both sides offset by the sub-chunk midpoint, with
 // exponents within 8 * |lower_bound| * log2(e) of zero (at most 2^58), on the
-// fp32 MFMA.  Diagonal block, softplus gate: the per-token decay is unbounded,
-// so the 136 pairs of the block are evaluated pairwise on the VALU.
+// fp32 MFMA.  Diagonal block, unbounded decays (softplus gate, pre-gated
+// decay): split into binary levels, one fp16 product per level (diag_level).
 constexpr int AS = 68;      // fp32 row stride of Akk / T
 constexpr int AQS = 72;     // fp16 row stride of Aqk
 constexpr int KER = 144;    // fp16 row stride of the row-major [t][k] K . 2^G and Kd tiles
@@ -209,7 +210,7 @@ constexpr int L_RQ = L_AQ + 64 * AQS * 2;
 constexpr int L_RK = L_RQ + 64 * 4;
 constexpr int L_BETA = L_RK + 64 * 4;
 constexpr int L_FW = L_BETA + 64 * 4;
-constexpr int L_QD = L_FW + 64 * 4;    // softplus: q_i . k_i per row [64] f32
+constexpr int L_QD = L_FW + 64 * 4;    // unbounded decays: q_i . k_i per row [64] f32
 constexpr int L_END = L_QD + 64 * 4;
 static_assert(L_VEC + NVEC * 128 * 4 <= L_T + T_BYTES, "vectors fit in region T");
 static_assert(64 * AS * 4 <= X_BYTES, "Akk fits in region X");
@@ -234,10 +235,13 @@ __device__ __forceinline__ float scan16(float x) {
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// log2-domain gate activation of x = g + dt_bias (A_exp = exp(A_log)).
+// log2-domain gate activation of x = g + dt_bias (A_exp = exp(A_log)); with a
+// pre-gated decay, x = g is the natural-log decay itself.
 template <int MODE>
 __device__ __forceinline__ float gate2(float x, float A_exp, float lb_log2e) {
-  if (MODE == KDA_GATE_SAFE_SIGMOID) {
+  if (MODE == KDA_GATE_PREGATED) {
+    return fmaxf(kLog2e * x, kMinLog2Decay);
+  } else if (MODE == KDA_GATE_SAFE_SIGMOID) {
     // lb * sigmoid(A x) * log2(e)
     return lb_log2e * fast_rcp(1.0f + fast_exp2(-(A_exp * kLog2e) * x));
   } else {
@@ -257,7 +261,8 @@ __device__ __forceinline__ half8 to_half8(const float* v) {
   return h;
 }
 
-// Softplus diagonal block.  The per-token decay is unbounded, so no single
+// Diagonal block for unbounded decays (softplus gate, pre-gated decay): the
+// per-token decay has no bound, so no single
 // reference row keeps both factors of every pair in range.  Instead the block
 // is split by levels: at level L the rows form blocks of 2^(4-L) with halves
 // of 2^(3-L); every pair i > j lies in exactly one (lower half, upper half)
@@ -330,7 +335,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const float* __restrict__ A_log, const float* __restrict__ dt_bias,
                  const int64_t* __restrict__ cu, const int* __restrict__ chunk_off,
                  int B, int T, int N, int Hqk, int Hv, int max_chunks,
-                 float scale, float lower_bound, uint8_t* __restrict__ ws) {
+                 float scale, float lower_bound, int flags, uint8_t* __restrict__ ws) {
   constexpr int LDS = L_END;
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
   uint8_t* sX = smem + L_X;                                          // mailbox / Kd staging / Akk / W staging
@@ -367,7 +372,8 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   float G[4][8];
   uint4 qraw[4], kraw[4];
   {
-    const float A_exp = expf(A_log[h]);
+    // a missing A_log means a multiplier of one (unused for pre-gated decay)
+    const float A_exp = (MODE == KDA_GATE_PREGATED || A_log == nullptr) ? 1.0f : expf(A_log[h]);
     const float lb_log2e = lower_bound * kLog2e;
     const int64_t row = cp.row0 + r;
     // All input loads are issued before any use, as range-checked buffer loads:
@@ -390,9 +396,13 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     float4 dtb4[8];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      dtb4[2 * kb] = *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + 32 * kb + 8 * lg);
-      dtb4[2 * kb + 1] = *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + 32 * kb + 8 * lg + 4);
+    for (int kb = 0; kb < 8; ++kb) dtb4[kb] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (dt_bias != nullptr) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        dtb4[2 * kb] = *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + 32 * kb + 8 * lg);
+        dtb4[2 * kb + 1] = *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + 32 * kb + 8 * lg + 4);
+      }
     }
     const float blogit = valid ? bf2f(beta[(size_t)row * Hv + h]) : 0.0f;
     float sq = 0.f, sk = 0.f;
@@ -412,9 +422,11 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
     sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
     if (lg == 0) {
-      sRq[r] = rsqrtf(sq + kL2Eps);
-      sRk[r] = rsqrtf(sk + kL2Eps);
-      sBeta[r] = valid ? fast_rcp(1.0f + fast_exp2(-kLog2e * blogit)) : 0.0f;
+      const bool norm = flags & KDA_FLAG_QK_L2NORM;
+      sRq[r] = norm ? rsqrtf(sq + kL2Eps) : 1.0f;
+      sRk[r] = norm ? rsqrtf(sk + kL2Eps) : 1.0f;
+      const float bp = (flags & KDA_FLAG_BETA_IS_PROB) ? blogit : fast_rcp(1.0f + fast_exp2(-kLog2e * blogit));
+      sBeta[r] = valid ? bp : 0.0f;
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -431,13 +443,13 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
   }
-  // safe gate: four partial accumulators of the diagonal block; softplus:
-  // one accumulator per level of the diagonal block
+  // safe gate: four partial accumulators of the diagonal block; unbounded
+  // decays: one accumulator per level of the diagonal block
   f32x4 dkkp[4], dqkp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) { dkkp[j] = f32x4{0, 0, 0, 0}; dqkp[j] = f32x4{0, 0, 0, 0}; }
   float qkd = 0.0f;
-  if constexpr (MODE == KDA_GATE_SOFTPLUS) {
+  if constexpr (MODE != KDA_GATE_SAFE_SIGMOID) {
     // diagonal block by levels (see diag_level); its diagonal is q_i . k_i
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -457,7 +469,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if constexpr (MODE == KDA_GATE_SOFTPLUS) {
+  if constexpr (MODE != KDA_GATE_SAFE_SIGMOID) {
     qkd += __shfl_xor(qkd, 16);
     qkd += __shfl_xor(qkd, 32);
     if (lg == 0) sQd[r] = qkd;
@@ -587,7 +599,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
   __syncthreads();
 
-  // ---- phase 4: off-diagonal blocks from the mailbox; softplus pairwise diagonal
+  // ---- phase 4: off-diagonal blocks from the mailbox; diagonal levels combined
   {
 #pragma unroll
     for (int J = 0; J < 3; ++J) {
@@ -600,7 +612,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         oqk[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aQ[kb], b, oqk[J], 0, 0, 0);
       }
     }
-    if (MODE == KDA_GATE_SOFTPLUS) {
+    if (MODE != KDA_GATE_SAFE_SIGMOID) {
       // pair (i, j), i > j, of the diagonal block belongs to the level of the
       // highest bit in which i and j differ
 #pragma unroll
@@ -1149,10 +1161,11 @@ kda_status check_params(const kda_fwd_params* p, bool packed) {
     return fail(KDA_ERR_SHAPE, "too many chunks");
   if ((int64_t)p->num_seqs * p->H_v > ((int64_t)1 << 26))
     return fail(KDA_ERR_SHAPE, "too many (sequence, head) pairs");
-  if (p->gate_mode != KDA_GATE_SOFTPLUS && p->gate_mode != KDA_GATE_SAFE_SIGMOID)
+  if (p->gate_mode != KDA_GATE_SOFTPLUS && p->gate_mode != KDA_GATE_SAFE_SIGMOID &&
+      p->gate_mode != KDA_GATE_PREGATED)
     return fail(KDA_ERR_UNSUPPORTED, "unknown gate_mode %d", p->gate_mode);
-  if (p->flags != KDA_FLAG_QK_L2NORM)
-    return fail(KDA_ERR_UNSUPPORTED, "flags must be KDA_FLAG_QK_L2NORM (got %d)", p->flags);
+  if (p->flags & ~(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_IS_PROB))
+    return fail(KDA_ERR_UNSUPPORTED, "unknown flag bits in %d", p->flags);
   if (p->gate_mode == KDA_GATE_SAFE_SIGMOID && !(p->lower_bound >= -5.0f && p->lower_bound < 0.0f))
     return fail(KDA_ERR_RANGE, "safe gate needs -5 <= lower_bound < 0 (got %g)", (double)p->lower_bound);
   if (!(p->scale == p->scale) || p->scale > 3.0e38f || p->scale < -3.0e38f)
@@ -1190,16 +1203,21 @@ kda_status kda_fwd_check(const kda_fwd_params* p, const void* q, const void* k, 
   const bool packed = cu_seqlens != nullptr;
   kda_status s = check_params(p, packed);
   if (s != KDA_OK) return s;
+  if (p->gate_mode == KDA_GATE_PREGATED && dt_bias)
+    return fail(KDA_ERR_UNSUPPORTED, "dt_bias must be NULL with pre-gated decay");
   const bool empty = (int64_t)p->B * p->T == 0;
   if (!empty) {
-    const void* req[] = {q, k, v, g, beta, A_log, dt_bias, out};
-    const char* names[] = {"q", "k", "v", "g", "beta", "A_log", "dt_bias", "out"};
-    for (int i = 0; i < 8; ++i)
-      if (!req[i]) return fail(KDA_ERR_NULL, "%s is NULL", names[i]);
-    const void* al[] = {q, k, v, g, out, dt_bias};
-    const char* aln[] = {"q", "k", "v", "g", "out", "dt_bias"};
+    const void* req[] = {q, k, v, g, beta, out};
+    const char* names[] = {"q", "k", "v", "g", "beta", "out"};
     for (int i = 0; i < 6; ++i)
+      if (!req[i]) return fail(KDA_ERR_NULL, "%s is NULL", names[i]);
+    if (p->gate_mode == KDA_GATE_SOFTPLUS && !A_log)
+      return fail(KDA_ERR_NULL, "A_log is NULL (required by the softplus gate)");
+    const void* al[] = {q, k, v, g, out};
+    const char* aln[] = {"q", "k", "v", "g", "out"};
+    for (int i = 0; i < 5; ++i)
       if (!aligned16(al[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", aln[i]);
+    if (dt_bias && !aligned16(dt_bias)) return fail(KDA_ERR_ALIGN, "dt_bias is not 16-byte aligned");
   }
   if (p->init_state_dtype != KDA_STATE_NONE) {
     if (!initial_state) return fail(KDA_ERR_NULL, "initial_state is NULL but init_state_dtype is set");
@@ -1232,11 +1250,12 @@ kda_status launch_intra(const kda_fwd_params* p, const void* q, const void* k, c
   if (packed) hipLaunchKernelGGL(kda_chunk_map_kernel, dim3(1), dim3(64), 0, st, cu_seqlens, p->num_seqs, chunk_off);
   if (mc > 0) {
     auto kern = p->gate_mode == KDA_GATE_SAFE_SIGMOID ? kda_intra_kernel<KDA_GATE_SAFE_SIGMOID>
+                : p->gate_mode == KDA_GATE_PREGATED   ? kda_intra_kernel<KDA_GATE_PREGATED>
                                                       : kda_intra_kernel<KDA_GATE_SOFTPLUS>;
     hipLaunchKernelGGL(kern, dim3((unsigned)mc, (unsigned)p->H_v), dim3(256), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)g, (const uint16_t*)beta,
                        A_log, dt_bias, cu_seqlens, chunk_off, p->B, p->T, p->num_seqs, p->H_qk, p->H_v,
-                       (int)mc, p->scale, p->lower_bound, blocks);
+                       (int)mc, p->scale, p->lower_bound, p->flags, blocks);
   }
   return KDA_OK;
 }

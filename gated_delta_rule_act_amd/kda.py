@@ -20,10 +20,12 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 KDA_OK = 0
 GATE_SOFTPLUS = 0
 GATE_SAFE_SIGMOID = 1
+GATE_PREGATED = 2
 STATE_NONE = 0
 STATE_F32 = 1
 STATE_BF16 = 2
 FLAG_QK_L2NORM = 1
+FLAG_BETA_IS_PROB = 2
 
 _STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTYPE", -4: "KDA_ERR_RANGE",
            -5: "KDA_ERR_ALIGN", -6: "KDA_ERR_WORKSPACE", -7: "KDA_ERR_LAUNCH", -8: "KDA_ERR_UNSUPPORTED"}
@@ -119,12 +121,15 @@ def _state_code(t: Optional[torch.Tensor]) -> int:
 
 def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GATE_SOFTPLUS,
         initial_state=None, final_state_dtype=torch.float32, cu_seqlens=None, out=None,
-        final_state=None, workspace=None, stage=None):
+        final_state=None, workspace=None, stage=None, qk_l2norm=True, beta_is_prob=False):
     """Chunked KDA forward on the current HIP stream.
 
-    q, k [B,T,Hqk,128] bf16; v, g [B,T,Hv,128] bf16; beta [B,T,Hv] bf16 logits;
-    A_log [Hv] fp32; dt_bias [Hv,128] fp32; initial_state [N,Hv,128,128]
-    fp32/bf16 or None; cu_seqlens [N+1] int64 or None (then B must be 1).
+    q, k [B,T,Hqk,128] bf16; v, g [B,T,Hv,128] bf16; beta [B,T,Hv] bf16 logits
+    (probabilities with ``beta_is_prob``); A_log [Hv] fp32 or None (required
+    by the softplus gate; None means a multiplier of one for the safe gate);
+    dt_bias [Hv,128] fp32 or None (zero bias; must be None with pre-gated g,
+    where g is the log-space decay); initial_state [N,Hv,128,128] fp32/bf16
+    or None; cu_seqlens [N+1] int64 or None (then B must be 1).
     Returns (out bf16 [B,T,Hv,128], final_state or None).  ``stage`` = "intra"
     or "state" runs only that half of the forward (kda_fwd_intra /
     kda_fwd_state); the two halves in order are the full forward.
@@ -134,12 +139,13 @@ def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GAT
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
             raise TypeError(f"{name} must be a contiguous bf16 device tensor")
     for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
-        if t.dtype != torch.float32 or not t.is_contiguous() or t.device != q.device:
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.device != q.device):
             raise TypeError(f"{name} must be a contiguous fp32 tensor on the same device")
     B, T, Hqk, K = q.shape
     Hv, V = v.shape[2], v.shape[3]
     if k.shape != q.shape or g.shape != (B, T, Hv, K) or tuple(v.shape[:2]) != (B, T) or \
-            beta.shape != (B, T, Hv) or A_log.shape != (Hv,) or dt_bias.shape != (Hv, K):
+            beta.shape != (B, T, Hv) or (A_log is not None and A_log.shape != (Hv,)) or \
+            (dt_bias is not None and dt_bias.shape != (Hv, K)):
         raise ValueError("inconsistent tensor shapes")
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int64 or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous():
@@ -155,7 +161,8 @@ def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GAT
         final_state = torch.empty((N, Hv, V, K), dtype=final_state_dtype, device=q.device)
     p = make_params(B=B, T=T, H_qk=Hqk, H_v=Hv, K=K, V=V, num_seqs=N, scale=float(scale),
                     lower_bound=float(lower_bound), gate_mode=int(gate_mode),
-                    init_state_dtype=_state_code(initial_state), final_state_dtype=_state_code(final_state))
+                    init_state_dtype=_state_code(initial_state), final_state_dtype=_state_code(final_state),
+                    flags=(FLAG_QK_L2NORM if qk_l2norm else 0) | (FLAG_BETA_IS_PROB if beta_is_prob else 0))
     need = int(lib.kda_fwd_workspace_size(ctypes.byref(p)))
     if workspace is None:
         workspace = _workspace(need, q.device)

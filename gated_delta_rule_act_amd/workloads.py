@@ -23,6 +23,10 @@ import numpy as np
 
 GATE_SOFTPLUS = 0
 GATE_SAFE_SIGMOID = 1
+GATE_PREGATED = 2
+
+FLAG_QK_L2NORM = 1
+FLAG_BETA_IS_PROB = 2
 
 STATE_NONE = 0
 STATE_F32 = 1
@@ -53,8 +57,8 @@ class KdaInputs:
     v: np.ndarray            # [B,T,Hv,V]  uint16
     g: np.ndarray            # [B,T,Hv,K]  uint16
     beta: np.ndarray         # [B,T,Hv]    uint16
-    A_log: np.ndarray        # [Hv] float32
-    dt_bias: np.ndarray      # [Hv,K] float32
+    A_log: Optional[np.ndarray]    # [Hv] float32, or None
+    dt_bias: Optional[np.ndarray]  # [Hv,K] float32, or None
     scale: float
     lower_bound: float
     gate_mode: int
@@ -62,6 +66,7 @@ class KdaInputs:
     initial_state: Optional[np.ndarray] = None   # [N,Hv,V,K] float32 or uint16 (bf16)
     init_state_dtype: int = STATE_NONE
     final_state_dtype: int = STATE_F32
+    flags: int = FLAG_QK_L2NORM
     name: str = "custom"
 
     @property
@@ -100,10 +105,17 @@ def _normal_bf16(rng, shape, std=1.0, mean=0.0):
 def make_inputs(*, B, T, Hqk, Hv=None, K=128, V=128, gate_mode=GATE_SOFTPLUS, lower_bound=-1.0,
                 seed=0, g_std=1.0, A_log_range=(0.0, math.log(16.0)), dt_bias_std=0.1,
                 lengths=None, init_state_dtype=STATE_NONE, final_state_dtype=STATE_F32,
-                h0_std=0.05, scale=None, name="custom", rng=None) -> KdaInputs:
+                h0_std=0.05, scale=None, name="custom", rng=None, qk_std=1.0, pregated_range=(-1.0, 0.0),
+                beta_prob=False, with_A_log=True, with_dt_bias=True, flags=FLAG_QK_L2NORM) -> KdaInputs:
     """Draw one seeded input set.  With ``lengths`` the sequences are packed
     (B must be 1 and T is their sum) and int64 cu_seqlens is returned.  A
-    generator passed as ``rng`` is used as is (``seed`` is then ignored)."""
+    generator passed as ``rng`` is used as is (``seed`` is then ignored).
+
+    Contract variants keep the draw order: with ``gate_mode`` pre-gated, g is
+    drawn U(pregated_range) as the log-space decay itself; ``beta_prob`` draws
+    beta U(0, 1) as probabilities; ``qk_std`` scales q and k (for runs without
+    the L2 norm); A_log and dt_bias are still drawn when ``with_A_log`` /
+    ``with_dt_bias`` is false, then dropped."""
     Hv = Hqk if Hv is None else Hv
     rng = np.random.default_rng(seed) if rng is None else rng
     cu = None
@@ -114,11 +126,18 @@ def make_inputs(*, B, T, Hqk, Hv=None, K=128, V=128, gate_mode=GATE_SOFTPLUS, lo
         cu = np.zeros(lengths.size + 1, np.int64)
         cu[1:] = np.cumsum(lengths)
         T = int(cu[-1])
-    q = _normal_bf16(rng, (B, T, Hqk, K))
-    k = _normal_bf16(rng, (B, T, Hqk, K))
+    q = _normal_bf16(rng, (B, T, Hqk, K), std=qk_std)
+    k = _normal_bf16(rng, (B, T, Hqk, K), std=qk_std)
     v = _normal_bf16(rng, (B, T, Hv, V))
-    g = _normal_bf16(rng, (B, T, Hv, K), std=g_std)
-    beta = _normal_bf16(rng, (B, T, Hv))
+    if gate_mode == GATE_PREGATED:
+        lo, hi = pregated_range
+        g = f32_to_bf16_bits(rng.uniform(lo, hi, size=(B, T, Hv, K)).astype(np.float32))
+    else:
+        g = _normal_bf16(rng, (B, T, Hv, K), std=g_std)
+    if beta_prob:
+        beta = f32_to_bf16_bits(rng.uniform(0.0, 1.0, size=(B, T, Hv)).astype(np.float32))
+    else:
+        beta = _normal_bf16(rng, (B, T, Hv))
     A_log = rng.uniform(A_log_range[0], A_log_range[1], size=Hv).astype(np.float32)
     dt_bias = (rng.standard_normal(size=(Hv, K), dtype=np.float32) * np.float32(dt_bias_std)).astype(np.float32)
     N = B if cu is None else cu.size - 1
@@ -126,7 +145,13 @@ def make_inputs(*, B, T, Hqk, Hv=None, K=128, V=128, gate_mode=GATE_SOFTPLUS, lo
     if init_state_dtype != STATE_NONE:
         x = rng.standard_normal(size=(N, Hv, V, K), dtype=np.float32) * np.float32(h0_std)
         h0 = f32_to_bf16_bits(x) if init_state_dtype == STATE_BF16 else x.astype(np.float32)
-    return KdaInputs(q=q, k=k, v=v, g=g, beta=beta, A_log=A_log, dt_bias=dt_bias,
+    if not with_A_log or gate_mode == GATE_PREGATED:
+        A_log = None
+    if not with_dt_bias or gate_mode == GATE_PREGATED:
+        dt_bias = None
+    if beta_prob:
+        flags |= FLAG_BETA_IS_PROB
+    return KdaInputs(q=q, k=k, v=v, g=g, beta=beta, A_log=A_log, dt_bias=dt_bias, flags=flags,
                      scale=(1.0 / math.sqrt(K)) if scale is None else float(scale),
                      lower_bound=float(lower_bound), gate_mode=gate_mode, cu_seqlens=cu,
                      initial_state=h0, init_state_dtype=init_state_dtype,

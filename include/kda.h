@@ -20,12 +20,19 @@
  * Gate activations ("fla-kda" skill listing and fla-kda SKILL.md, "Gate
  * contracts"):
  *   KDA_GATE_SOFTPLUS     a = -exp(A_log[h]) * softplus(g + dt_bias[h])
+ *                         (A_log required)
  *   KDA_GATE_SAFE_SIGMOID a = lower_bound * sigmoid(exp(A_log[h]) * (g + dt_bias[h])),
- *                         with -5 <= lower_bound < 0
- * The recurrence (per sequence and v-head, state S in R^{V x K}, q and k
- * L2-normalised in the kernel):
- *   S <- S Diag(e^{a_t});  S <- S + sigmoid(beta_t) (v_t - S k_t) k_t^T;
- *   o_t = scale * S q_t.
+ *                         with -5 <= lower_bound < 0; A_log may be NULL, which
+ *                         means a multiplier of one
+ *   KDA_GATE_PREGATED     a = g: the caller passes the log-space decay itself
+ *                         (natural log, per token and key channel); it must be
+ *                         <= 0 (device data, not validated).  A_log is unused
+ *                         and dt_bias must be NULL.
+ * dt_bias may be NULL for the two activated gates (zero bias).
+ * The recurrence (per sequence and v-head, state S in R^{V x K}):
+ *   S <- S Diag(e^{a_t});  S <- S + b_t (v_t - S k_t) k_t^T;  o_t = scale * S q_t
+ * with b_t = sigmoid(beta_t) (beta_t itself with KDA_FLAG_BETA_IS_PROB) and q,
+ * k L2-normalised in the kernel with KDA_FLAG_QK_L2NORM.
  *
  * Ownership: every buffer is allocated and owned by the caller.  The library
  * allocates no device memory, keeps no mutable global state except a
@@ -60,12 +67,13 @@ typedef enum {
   KDA_ERR_UNSUPPORTED = -8  /* unknown gate mode or flag */
 } kda_status;
 
-typedef enum { KDA_GATE_SOFTPLUS = 0, KDA_GATE_SAFE_SIGMOID = 1 } kda_gate_mode;
+typedef enum { KDA_GATE_SOFTPLUS = 0, KDA_GATE_SAFE_SIGMOID = 1, KDA_GATE_PREGATED = 2 } kda_gate_mode;
 typedef enum { KDA_STATE_NONE = 0, KDA_STATE_F32 = 1, KDA_STATE_BF16 = 2 } kda_state_dtype;
 
-/* flags: the only supported configuration normalises q and k in the kernel,
- * so KDA_FLAG_QK_L2NORM must be set. */
-enum { KDA_FLAG_QK_L2NORM = 1 };
+/* flags (any combination; other bits are rejected):
+ *   KDA_FLAG_QK_L2NORM     normalise q and k (eps 1e-6 inside the root) in the kernel
+ *   KDA_FLAG_BETA_IS_PROB  beta holds probabilities: no sigmoid is applied */
+enum { KDA_FLAG_QK_L2NORM = 1, KDA_FLAG_BETA_IS_PROB = 2 };
 
 typedef struct {
   int32_t B, T;               /* batch rows and tokens per row (total tokens when packed) */
@@ -77,7 +85,7 @@ typedef struct {
   int32_t gate_mode;          /* kda_gate_mode */
   int32_t init_state_dtype;   /* kda_state_dtype of initial_state (NONE: zero state) */
   int32_t final_state_dtype;  /* kda_state_dtype of final_state (NONE: not written) */
-  int32_t flags;              /* must be KDA_FLAG_QK_L2NORM */
+  int32_t flags;              /* KDA_FLAG_* bits */
 } kda_fwd_params;
 
 /* Bytes of device workspace kda_fwd needs for these parameters; host only,
@@ -98,8 +106,9 @@ kda_status kda_fwd_check(const kda_fwd_params* p,
 
 /* Chunked KDA forward.  All pointers are device pointers:
  *   q, k      bf16 [B, T, H_qk, 128]       v, g  bf16 [B, T, H_v, 128]
- *   beta      bf16 [B, T, H_v] (logits)
- *   A_log     fp32 [H_v]                    dt_bias fp32 [H_v, 128]
+ *   beta      bf16 [B, T, H_v] (logits, or probabilities with KDA_FLAG_BETA_IS_PROB)
+ *   A_log     fp32 [H_v] or NULL (see the gate modes)
+ *   dt_bias   fp32 [H_v, 128] or NULL (see the gate modes)
  *   cu_seqlens int64 [num_seqs + 1] or NULL (dense: sequence n is batch row n)
  *   initial_state [num_seqs, H_v, 128, 128] of init_state_dtype, or NULL
  *   final_state   [num_seqs, H_v, 128, 128] of final_state_dtype, or NULL

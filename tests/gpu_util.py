@@ -33,8 +33,9 @@ def bf16_dev(a: np.ndarray, dev="cuda"):
 
 def to_device(inp: W.KdaInputs, dev="cuda"):
     d = dict(q=bf16_dev(inp.q, dev), k=bf16_dev(inp.k, dev), v=bf16_dev(inp.v, dev), g=bf16_dev(inp.g, dev),
-             beta=bf16_dev(inp.beta, dev), A_log=torch.from_numpy(inp.A_log).to(dev),
-             dt_bias=torch.from_numpy(inp.dt_bias).to(dev))
+             beta=bf16_dev(inp.beta, dev),
+             A_log=None if inp.A_log is None else torch.from_numpy(inp.A_log).to(dev),
+             dt_bias=None if inp.dt_bias is None else torch.from_numpy(inp.dt_bias).to(dev))
     d["cu_seqlens"] = None if inp.cu_seqlens is None else torch.from_numpy(inp.cu_seqlens).to(dev)
     if inp.initial_state is None:
         d["h0"] = None
@@ -63,14 +64,15 @@ def run_gpu(inp: W.KdaInputs, dev_inputs=None, poison=True):
             fs.fill_(float("nan"))
     o, s = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"], inp.scale,
                    inp.lower_bound, inp.gate_mode, initial_state=d["h0"], cu_seqlens=d["cu_seqlens"],
-                   out=out, final_state=fs, final_state_dtype=fdt)
+                   out=out, final_state=fs, final_state_dtype=fdt,
+                   qk_l2norm=bool(inp.flags & W.FLAG_QK_L2NORM), beta_is_prob=bool(inp.flags & W.FLAG_BETA_IS_PROB))
     torch.cuda.synchronize()
     return o, s
 
 
 def run_oracle(inp: W.KdaInputs, nthreads=0):
     return oracle.fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.A_log, inp.dt_bias, scale=inp.scale,
-                      lower_bound=inp.lower_bound, gate_mode=inp.gate_mode, flags=oracle.FLAG_QK_L2NORM,
+                      lower_bound=inp.lower_bound, gate_mode=inp.gate_mode, flags=inp.flags,
                       initial_state=inp.initial_state_f64(), cu_seqlens=inp.cu_seqlens, nthreads=nthreads)
 
 
@@ -85,9 +87,11 @@ def oracle_pair(inp: W.KdaInputs, n: int, h: int, h0_f64=None):
     sl = lambda x, hh: np.ascontiguousarray(x[b:b + 1, a:e, hh:hh + 1])
     h0 = None if h0_f64 is None else h0_f64[n:n + 1, h:h + 1]
     o, s = oracle.fwd(sl(inp.q, hq), sl(inp.k, hq), sl(inp.v, h), sl(inp.g, h),
-                      np.ascontiguousarray(inp.beta[b:b + 1, a:e, h:h + 1]), inp.A_log[h:h + 1],
-                      inp.dt_bias[h:h + 1], scale=inp.scale, lower_bound=inp.lower_bound,
-                      gate_mode=inp.gate_mode, flags=oracle.FLAG_QK_L2NORM, initial_state=h0, nthreads=1)
+                      np.ascontiguousarray(inp.beta[b:b + 1, a:e, h:h + 1]),
+                      None if inp.A_log is None else inp.A_log[h:h + 1],
+                      None if inp.dt_bias is None else inp.dt_bias[h:h + 1], scale=inp.scale,
+                      lower_bound=inp.lower_bound, gate_mode=inp.gate_mode, flags=inp.flags, initial_state=h0,
+                      nthreads=1)
     return o[0, :, 0], s[0, 0]
 
 

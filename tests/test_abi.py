@@ -52,8 +52,8 @@ def check(lib, p, ws=None, cu=None, drop=None, shift=None):
     ptrs = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, cu=cu,
                 h0=FAKE if p.init_state_dtype else None, hT=FAKE if p.final_state_dtype else None,
                 out=FAKE, ws=FAKE)
-    if drop:
-        ptrs[drop] = None
+    for name in ((drop,) if isinstance(drop, str) else (drop or ())):
+        ptrs[name] = None
     if shift:
         ptrs[shift] = ptrs[shift] + 2
     need = lib.kda_fwd_workspace_size(ctypes.byref(p))
@@ -70,7 +70,7 @@ def test_valid_dense_and_packed(lib):
 
 @pytest.mark.parametrize("field,bad,code", [
     ("K", 64, -2), ("V", 256, -2), ("K", 129, -2), ("H_v", 6, -2), ("B", 0, -2), ("T", -1, -2),
-    ("num_seqs", 3, -2), ("gate_mode", 2, -8), ("flags", 0, -8), ("flags", 3, -8),
+    ("num_seqs", 3, -2), ("gate_mode", 3, -8), ("gate_mode", -1, -8), ("flags", 4, -8), ("flags", -1, -8),
     ("init_state_dtype", 3, -3), ("final_state_dtype", -1, -3),
 ])
 def test_shape_dtype_mode_rejections(lib, field, bad, code):
@@ -113,10 +113,39 @@ def test_state_dtypes_must_match(lib):
     assert check(lib, base_params(init_state_dtype=1, final_state_dtype=0)) == kda.KDA_OK
 
 
-@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "A_log", "dt_bias", "out", "h0", "hT", "ws"])
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "A_log", "out", "h0", "hT", "ws"])
 def test_null_pointers(lib, name):
+    # softplus gate: A_log is required
     code = check(lib, base_params(), drop=name)
     assert code == (-6 if name == "ws" else -1)
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+def test_flag_combinations_accepted(lib, flags):
+    assert check(lib, base_params(flags=flags)) == kda.KDA_OK
+
+
+def test_optional_gate_parameters(lib):
+    # dt_bias is optional for both activated gates
+    assert check(lib, base_params(), drop="dt_bias") == kda.KDA_OK
+    safe = dict(gate_mode=kda.GATE_SAFE_SIGMOID, lower_bound=-5.0)
+    assert check(lib, base_params(**safe), drop="dt_bias") == kda.KDA_OK
+    # a missing A_log means a multiplier of one for the safe gate only
+    assert check(lib, base_params(**safe), drop="A_log") == kda.KDA_OK
+    assert check(lib, base_params(**safe), drop=("A_log", "dt_bias")) == kda.KDA_OK
+    assert check(lib, base_params(), drop="A_log") == -1
+
+
+def test_pregated_contract(lib):
+    pre = dict(gate_mode=kda.GATE_PREGATED)
+    # the decay is given directly: no bias may accompany it, A_log is unused
+    assert check(lib, base_params(**pre), drop="dt_bias") == kda.KDA_OK
+    assert check(lib, base_params(**pre), drop=("dt_bias", "A_log")) == kda.KDA_OK
+    assert check(lib, base_params(**pre)) == -8
+    # lower_bound belongs to the safe activation and is not range-checked here
+    assert check(lib, base_params(lower_bound=3.0, **pre), drop="dt_bias") == kda.KDA_OK
+    # the bias rule holds for empty inputs too
+    assert check(lib, base_params(T=0, **pre)) == -8
 
 
 @pytest.mark.parametrize("name", ["q", "k", "v", "g", "out", "dt_bias", "h0", "hT"])

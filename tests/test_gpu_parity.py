@@ -40,6 +40,17 @@ CASES = {
     "safe_lb_tiny": dict(gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-1e-30, T=140),
     "softplus_long_memory": dict(A_log_range=(-8.0, -6.0), T=400, B=1),
     "softplus_strong_decay": dict(A_log_range=(3.0, 6.0), g_std=3.0, T=200),
+    # contract variants: pre-gated log-space decay, optional A_log / dt_bias,
+    # beta given as probabilities, q/k used without the L2 norm
+    "pregated_mild": dict(gate_mode=W.GATE_PREGATED, pregated_range=(-0.5, 0.0)),
+    "pregated_bounded_5": dict(gate_mode=W.GATE_PREGATED, pregated_range=(-5.0, 0.0), T=1000, B=1),
+    "pregated_zero_decay": dict(gate_mode=W.GATE_PREGATED, pregated_range=(0.0, 0.0), T=200),
+    "safe_no_A_log": dict(gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-5.0, with_A_log=False, g_std=3.0),
+    "softplus_no_dt_bias": dict(with_dt_bias=False, T=200),
+    "beta_prob": dict(beta_prob=True, T=200),
+    "no_l2norm": dict(flags=0, qk_std=1.0 / math.sqrt(128), T=260),
+    "pregated_no_l2norm_beta_prob_gva": dict(gate_mode=W.GATE_PREGATED, pregated_range=(-1.0, 0.0), flags=0,
+                                              qk_std=1.0 / math.sqrt(128), beta_prob=True, Hqk=2, Hv=4, T=300),
 }
 
 
@@ -58,15 +69,16 @@ def test_small_elementwise(name):
                              state_bf16=(inp.final_state_dtype == W.STATE_BF16)), name)
 
 
-@pytest.mark.parametrize("lengths,state", [
-    ([1, 63, 64, 65, 200, 130], W.STATE_F32),
-    ([0, 5, 0, 129], W.STATE_F32),
-    ([70, 1, 1, 300, 64], W.STATE_BF16),
+@pytest.mark.parametrize("lengths,state,extra", [
+    ([1, 63, 64, 65, 200, 130], W.STATE_F32, {}),
+    ([0, 5, 0, 129], W.STATE_F32, {}),
+    ([70, 1, 1, 300, 64], W.STATE_BF16, {}),
+    ([100, 3, 250], W.STATE_F32, dict(gate_mode=W.GATE_PREGATED, pregated_range=(-2.0, 0.0))),
 ])
-def test_packed_elementwise(lengths, state):
+def test_packed_elementwise(lengths, state, extra):
     inp = W.make_inputs(B=1, T=None, Hqk=2, Hv=4, seed=7, lengths=lengths, init_state_dtype=state,
-                        final_state_dtype=state)
-    U.log(f"[gpu] packed lengths={lengths} state={state}")
+                        final_state_dtype=state, **extra)
+    U.log(f"[gpu] packed lengths={lengths} state={state} {extra}")
     o, s = U.run_gpu(inp)
     o_ref, s_ref = U.run_oracle(inp)
     U.assert_parity(U.errors(U.as_f64(o), o_ref, U.as_f64(s), s_ref, state_bf16=(state == W.STATE_BF16)),
