@@ -116,8 +116,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, help="measured workload index (the bench line is 3)")
+    ap.add_argument("--workload", type=int, default=None,
+                    help="workload index (chunked: 1-5, the bench line is 3; recurrent: 1-2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("chunked", "recurrent"), default="chunked",
+                    help="chunked: the headline forward; recurrent: the token-recurrent entry on a decode workload")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="instead of the forward, run N plain 1 GiB device copies (traffic counter scale)")
     args = ap.parse_args()
@@ -142,8 +145,11 @@ def main():
                           "copies": args.copy_calibration}))
         return
 
+    if args.mode == "recurrent":
+        return run_recurrent(args, dev)
+
     t_gen = time.perf_counter()
-    inp = W.workload(args.workload)
+    inp = W.workload(3 if args.workload is None else args.workload)
     d = U.to_device(inp)
     fdt = U.final_dtype_of(inp)
     out = torch.empty((inp.B, inp.T, inp.Hv, inp.V), dtype=torch.bfloat16, device=dev)
@@ -202,7 +208,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded numpy PCG64, see DESIGN.md)",
         "config": {"workload": inp.name, "B": inp.B, "T": inp.T, "H_qk": inp.Hqk, "H_v": inp.Hv, "K": inp.K,
-                   "V": inp.V, "gate": ["softplus", "safe_sigmoid"][inp.gate_mode],
+                   "V": inp.V, "gate": ["softplus", "safe_sigmoid", "pregated"][inp.gate_mode],
                    "lower_bound": inp.lower_bound, "chunk": 64, "sub_chunk": 16,
                    "initial_state": ["none", "fp32", "bf16"][inp.init_state_dtype],
                    "final_state": ["none", "fp32", "bf16"][inp.final_state_dtype],
@@ -223,6 +229,68 @@ def main():
         cpu, parity = cpu_baseline(inp, out, fs)
         rec["cpu_baseline"] = cpu
         rec["parity"] = parity
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+def run_recurrent(args, dev):
+    """The token-recurrent entry on a decode workload: one launch per step,
+    HBM-bound on the state (read and written once per (sequence, head))."""
+    import torch
+    from gated_delta_rule_act_amd import kda, workloads as W
+    from tests import gpu_util as U
+
+    inp = W.recurrent_workload(1 if args.workload is None else args.workload)
+    d = U.to_device(inp)
+    out = torch.empty((inp.B, inp.T, inp.Hv, inp.V), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((inp.N, inp.Hv, inp.V, inp.K), dtype=torch.float32, device=dev)
+
+    def step():
+        kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"], inp.scale, inp.lower_bound,
+                inp.gate_mode, initial_state=d["h0"], out=out, final_state=fs, recurrent=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tok = inp.B * inp.T
+    st = {0: 0, 1: 4, 2: 2}
+    # algorithmic bytes: q, k per (token, qk-head); v, g, beta, out per (token, v-head);
+    # the state read and written once per (sequence, v-head); dt_bias and A_log
+    nbytes = (tok * inp.Hqk * inp.K * 2 * 2 + tok * inp.Hv * (inp.K * 2 + inp.V * 2 + 2 + inp.V * 2)
+              + inp.N * inp.Hv * inp.V * inp.K * (st[inp.init_state_dtype] + st[inp.final_state_dtype])
+              + inp.Hv * (inp.K + 1) * 4)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "fused_recurrent_kda tokens/s (decode, fp32 state in and out), 1 MI355X",
+        "value": tok / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded numpy PCG64, see DESIGN.md)",
+        "config": {"workload": inp.name, "B": inp.B, "T": inp.T, "H_qk": inp.Hqk, "H_v": inp.Hv, "K": inp.K,
+                   "V": inp.V, "gate": ["softplus", "safe_sigmoid", "pregated"][inp.gate_mode],
+                   "lower_bound": inp.lower_bound, "initial_state": "fp32", "final_state": "fp32"},
+        "roofline": {"bound": "hbm", "kernel": "kda_recurrent_kernel", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms},
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+        t0 = time.perf_counter()
+        o_ref, s_ref = U.run_oracle(inp, nthreads=threads)
+        dt = time.perf_counter() - t0
+        e = U.errors(U.as_f64(out), o_ref, U.as_f64(fs), s_ref)
+        rec["cpu_baseline"] = {"value": tok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"{inp.name}: the whole workload ({dt:.2f} s)", "seconds": dt}
+        rec["parity"] = {"out_max_abs": e["out_max_abs"], "out_rel_rms": e["out_rel_rms"],
+                         "state_rel": e["state_rel"], "tol_out_max_abs": U.OUT_MAX_ABS, "tol_state_rel": U.STATE_REL}
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

@@ -1121,6 +1121,205 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
 }
 
 // ---------------------------------------------------------------------------
+// token-recurrent forward (decode and short sequences)
+//
+// One workgroup of 256 threads per (sequence, v-head, 32-row V slice): thread
+// t owns state row v0 + (t >> 3), key columns 16 (t & 7) .. +15, as 16 fp32
+// values in registers.  Tokens go in blocks of RTB: the inputs of a block are
+// fetched into registers one block ahead, then written to a double-buffered
+// LDS slot where the gates (exp of the activation) and the q, k norms of all
+// the block's tokens are formed in parallel; the tokens of the block then run
+// with no barrier -- every state row is independent: decay its columns,
+// r = S k (an 8-lane reduction), the delta write, o = S q.
+constexpr int RSLICE = 32;                 // V rows per workgroup
+constexpr int RNSLICE = DV / RSLICE;
+// Tokens per block: RTB for sequences, 1 for decode steps (one token each).
+constexpr int RTB = 8;
+
+template <int TB>
+struct RecurrentIn {
+  static constexpr int NE = (TB * DK + 255) / 256;
+  float q[NE], k[NE], g[NE];  // element e = tid + 256 i: token e >> 7, channel e & 127
+  float vv;                   // v: token tid >> 5, row tid & 31
+  float braw;                 // beta of token tid (tid < TB)
+};
+
+// Issue the loads of the block starting at token s0 (tokens >= len read
+// nothing; the conditions are uniform per wave).
+template <int TB>
+__device__ __forceinline__ void recurrent_load(RecurrentIn<TB>& in, int64_t s0, int64_t len, int64_t bos,
+                                               const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                               const uint16_t* g, const uint16_t* beta, int Hqk, int Hv, int h,
+                                               int hq, int v0, int tid) {
+#pragma unroll
+  for (int i = 0; i < RecurrentIn<TB>::NE; ++i) {
+    const int e = tid + 256 * i, tk = e >> 7, c = e & 127;
+    in.q[i] = in.k[i] = in.g[i] = 0.0f;
+    if (tk < TB && s0 + tk < len) {
+      const size_t tok = (size_t)(bos + s0 + tk);
+      in.q[i] = bf2f(q[(tok * Hqk + hq) * DK + c]);
+      in.k[i] = bf2f(k[(tok * Hqk + hq) * DK + c]);
+      in.g[i] = bf2f(g[(tok * Hv + h) * DK + c]);
+    }
+  }
+  in.vv = 0.0f;
+  if ((tid >> 5) < TB && s0 + (tid >> 5) < len)
+    in.vv = bf2f(v[((size_t)(bos + s0 + (tid >> 5)) * Hv + h) * DV + v0 + (tid & 31)]);
+  in.braw = 0.0f;
+  if (tid < TB && s0 + tid < len) in.braw = bf2f(beta[(size_t)(bos + s0 + tid) * Hv + h]);
+}
+
+// Sums by DPP moves within a 16-lane row (no LDS permute round trips): lanes
+// paired by quad_perm [1,0,3,2] and [2,3,0,1], then the 4-lane halves of each
+// 8 by row_half_mirror, then the 8-lane halves of the row by row_mirror.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  return x;
+}
+// Sum over the 64 lanes of a wave, in a fixed order: row sums, then rows 0..3.
+__device__ __forceinline__ float sum64(float x) {
+  x = sum8(x);
+  x += dpp_f<0x140>(x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
+template <int MODE, int TB>
+__global__ void __launch_bounds__(256)
+kda_recurrent_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                     const uint16_t* __restrict__ v, const uint16_t* __restrict__ g,
+                     const uint16_t* __restrict__ beta, const float* __restrict__ A_log,
+                     const float* __restrict__ dt_bias, const int64_t* __restrict__ cu,
+                     const void* h0, void* hT, uint16_t* __restrict__ out,
+                     int T, int N, int Hqk, int Hv, float scale, float lower_bound, int flags,
+                     int init_dtype, int final_dtype) {
+  __shared__ __attribute__((aligned(16))) float sK[2][TB][DK];
+  __shared__ __attribute__((aligned(16))) float sQ[2][TB][DK];
+  __shared__ __attribute__((aligned(16))) float sD[2][TB][DK];
+  __shared__ __attribute__((aligned(16))) float sVv[2][TB][RSLICE];
+  __shared__ float sB[2][TB];
+  __shared__ float sN[2][TB][4];  // per token: sum q^2 of its two waves, then sum k^2
+
+  const int chain = blockIdx.x / RNSLICE, slice = blockIdx.x % RNSLICE;
+  if (chain >= N * Hv) return;
+  const int n = chain / Hv, h = chain % Hv, hq = h / (Hv / Hqk);
+  const int v0 = RSLICE * slice;
+  const int tid = threadIdx.x;
+  const int row = tid >> 3, kc = 16 * (tid & 7);
+  int64_t bos, len;
+  if (cu == nullptr) { bos = (int64_t)n * T; len = T; }
+  else { bos = cu[n]; len = cu[n + 1] - cu[n]; }
+
+  // state row v0 + row, columns kc .. kc + 15
+  float S[16];
+  const size_t sidx = (((size_t)n * Hv + h) * DV + v0 + row) * DK + kc;
+#pragma unroll
+  for (int j = 0; j < 16; j += 4) {
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (init_dtype == KDA_STATE_F32) {
+      x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(h0) + sidx + j);
+    } else if (init_dtype == KDA_STATE_BF16) {
+      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(h0) + sidx + j);
+      x = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                      __uint_as_float(u.y & 0xffff0000u));
+    }
+    S[j] = x.x; S[j + 1] = x.y; S[j + 2] = x.z; S[j + 3] = x.w;
+  }
+
+  const float A_exp = (MODE == KDA_GATE_PREGATED || A_log == nullptr) ? 1.0f : expf(A_log[h]);
+  const float lb_log2e = lower_bound * kLog2e;
+  const float dtb = dt_bias != nullptr ? dt_bias[(size_t)h * DK + (tid & 127)] : 0.0f;
+  const bool norm = flags & KDA_FLAG_QK_L2NORM;
+  const bool beta_prob = flags & KDA_FLAG_BETA_IS_PROB;
+
+  RecurrentIn<TB> cur;
+  recurrent_load<TB>(cur, 0, len, bos, q, k, v, g, beta, Hqk, Hv, h, hq, v0, tid);
+  for (int64_t s0 = 0; s0 < len; s0 += TB) {
+    const int buf = (int)((s0 / TB) & 1);
+    const int nb = (int)min((int64_t)TB, len - s0);
+    RecurrentIn<TB> nxt;
+    recurrent_load<TB>(nxt, s0 + TB, len, bos, q, k, v, g, beta, Hqk, Hv, h, hq, v0, tid);
+    // 1. the block into LDS: raw q, k; the decay factor of every (token,
+    //    channel); the q, k norms; v of the slice rows; beta.  This buffer was
+    //    last read two blocks ago, before the previous block's barrier.
+    // Each token's 128 channels sit in two waves (lane = channel & 63), so its
+    // norms are two 64-lane butterflies and one sum -- the same order for any
+    // block length, hence bit-identical results for any split of a sequence.
+#pragma unroll
+    for (int i = 0; i < RecurrentIn<TB>::NE; ++i) {
+      const int e = tid + 256 * i, tk = e >> 7, c = e & 127;
+      if (tk < TB) {  // uniform per wave
+        sQ[buf][tk][c] = cur.q[i];
+        sK[buf][tk][c] = cur.k[i];
+        sD[buf][tk][c] = fast_exp2(gate2<MODE>(cur.g[i] + dtb, A_exp, lb_log2e));
+        const float q2 = sum64(cur.q[i] * cur.q[i]), k2 = sum64(cur.k[i] * cur.k[i]);
+        if ((tid & 63) == 0) {
+          sN[buf][tk][(tid >> 6) & 1] = q2;
+          sN[buf][tk][2 + ((tid >> 6) & 1)] = k2;
+        }
+      }
+    }
+    if ((tid >> 5) < TB) sVv[buf][tid >> 5][tid & 31] = cur.vv;
+    if (tid < TB) sB[buf][tid] = beta_prob ? cur.braw : fast_rcp(1.0f + fast_exp2(-kLog2e * cur.braw));
+    __syncthreads();
+    // 3. the block's tokens, in order, with no barrier
+    for (int j = 0; j < nb; ++j) {
+      const float rq = norm ? rsqrtf(sN[buf][j][0] + sN[buf][j][1] + kL2Eps) : 1.0f;
+      const float rk = norm ? rsqrtf(sN[buf][j][2] + sN[buf][j][3] + kL2Eps) : 1.0f;
+      const float b = sB[buf][j];
+      const float vv = sVv[buf][j][row];
+      float Kc[16], Qc[16], Dc[16];
+#pragma unroll
+      for (int jj = 0; jj < 16; jj += 4) {
+        const float4 kk = *reinterpret_cast<const float4*>(&sK[buf][j][kc + jj]);
+        const float4 qq = *reinterpret_cast<const float4*>(&sQ[buf][j][kc + jj]);
+        const float4 dd = *reinterpret_cast<const float4*>(&sD[buf][j][kc + jj]);
+        Kc[jj] = kk.x; Kc[jj + 1] = kk.y; Kc[jj + 2] = kk.z; Kc[jj + 3] = kk.w;
+        Qc[jj] = qq.x; Qc[jj + 1] = qq.y; Qc[jj + 2] = qq.z; Qc[jj + 3] = qq.w;
+        Dc[jj] = dd.x; Dc[jj + 1] = dd.y; Dc[jj + 2] = dd.z; Dc[jj + 3] = dd.w;
+      }
+      float r = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) { S[jj] *= Dc[jj]; r += S[jj] * Kc[jj]; }
+      r = sum8(r) * rk;
+      const float coef = b * (vv - r) * rk;
+      float o = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) { S[jj] += coef * Kc[jj]; o += S[jj] * Qc[jj]; }
+      o = sum8(o) * (rq * scale);
+      if ((tid & 7) == 0)
+        out[((size_t)(bos + s0 + j) * Hv + h) * DV + v0 + row] = __builtin_bit_cast(uint16_t, (__bf16)o);
+    }
+    cur = nxt;
+  }
+
+  if (final_dtype == KDA_STATE_F32) {
+#pragma unroll
+    for (int j = 0; j < 16; j += 4)
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(hT) + sidx + j) = make_float4(S[j], S[j + 1], S[j + 2], S[j + 3]);
+  } else if (final_dtype == KDA_STATE_BF16) {
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      uint2 u;
+      u.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j]) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j + 1]) << 16);
+      u.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j + 2]) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j + 3]) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(hT) + sidx + j) = u;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 thread_local char g_last_error[512] = "";
 
@@ -1195,10 +1394,14 @@ size_t kda_fwd_workspace_size(const kda_fwd_params* p) {
   return header_bytes(p) + (size_t)p->H_v * (size_t)mc * BLOCK;
 }
 
-kda_status kda_fwd_check(const kda_fwd_params* p, const void* q, const void* k, const void* v,
-                         const void* g, const void* beta, const float* A_log, const float* dt_bias,
-                         const int64_t* cu_seqlens, const void* initial_state, const void* final_state,
-                         const void* out, const void* workspace, size_t workspace_bytes) {
+}  // extern "C"
+
+namespace {
+// The predicates of kda_fwd_check; the workspace ones only when it is used.
+kda_status check_call(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                      const void* beta, const float* A_log, const float* dt_bias, const int64_t* cu_seqlens,
+                      const void* initial_state, const void* final_state, const void* out,
+                      const void* workspace, size_t workspace_bytes, bool uses_workspace) {
   g_last_error[0] = 0;
   const bool packed = cu_seqlens != nullptr;
   kda_status s = check_params(p, packed);
@@ -1227,12 +1430,24 @@ kda_status kda_fwd_check(const kda_fwd_params* p, const void* q, const void* k, 
     if (!final_state) return fail(KDA_ERR_NULL, "final_state is NULL but final_state_dtype is set");
     if (!aligned16(final_state)) return fail(KDA_ERR_ALIGN, "final_state is not 16-byte aligned");
   }
+  if (!uses_workspace) return KDA_OK;
   const size_t need = kda_fwd_workspace_size(p);
   if (!workspace || workspace_bytes < need)
     return fail(KDA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
                 workspace ? "" : ", NULL");
   if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_ALIGN, "workspace is not 256-byte aligned");
   return KDA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kda_status kda_fwd_check(const kda_fwd_params* p, const void* q, const void* k, const void* v,
+                         const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                         const int64_t* cu_seqlens, const void* initial_state, const void* final_state,
+                         const void* out, const void* workspace, size_t workspace_bytes) {
+  return check_call(p, q, k, v, g, beta, A_log, dt_bias, cu_seqlens, initial_state, final_state, out, workspace,
+                    workspace_bytes, true);
 }
 
 }  // extern "C"
@@ -1294,8 +1509,8 @@ kda_status kda_fwd(const kda_fwd_params* p, const void* q, const void* k, const 
   if (s != KDA_OK) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  launch_intra(p, q, k, g, beta, A_log, dt_bias, cu_seqlens, workspace, st);
-  launch_state(p, v, cu_seqlens, initial_state, final_state, out, workspace, st);
+  if ((s = launch_intra(p, q, k, g, beta, A_log, dt_bias, cu_seqlens, workspace, st)) != KDA_OK) return s;
+  if ((s = launch_state(p, v, cu_seqlens, initial_state, final_state, out, workspace, st)) != KDA_OK) return s;
   return launch_status();
 }
 
@@ -1320,6 +1535,32 @@ kda_status kda_fwd_state(const kda_fwd_params* p, const void* q, const void* k, 
   if (s != KDA_OK) return s;
   (void)hipGetLastError();
   launch_state(p, v, cu_seqlens, initial_state, final_state, out, workspace, reinterpret_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+kda_status kda_fused_recurrent_fwd(const kda_fwd_params* p, const void* q, const void* k, const void* v,
+                                   const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                                   const int64_t* cu_seqlens, const void* initial_state, void* final_state,
+                                   void* out, void* stream) {
+  kda_status s = check_call(p, q, k, v, g, beta, A_log, dt_bias, cu_seqlens, initial_state, final_state, out,
+                            nullptr, 0, false);
+  if (s != KDA_OK) return s;
+  const int64_t chains = (int64_t)p->num_seqs * p->H_v;
+  if (chains == 0) return KDA_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  // decode steps (at most one token per sequence): one-token blocks
+  const bool decode = (int64_t)p->B * p->T <= (int64_t)p->num_seqs;
+  auto kern = decode ? (p->gate_mode == KDA_GATE_SAFE_SIGMOID ? kda_recurrent_kernel<KDA_GATE_SAFE_SIGMOID, 1>
+                        : p->gate_mode == KDA_GATE_PREGATED   ? kda_recurrent_kernel<KDA_GATE_PREGATED, 1>
+                                                              : kda_recurrent_kernel<KDA_GATE_SOFTPLUS, 1>)
+                     : (p->gate_mode == KDA_GATE_SAFE_SIGMOID ? kda_recurrent_kernel<KDA_GATE_SAFE_SIGMOID, RTB>
+                        : p->gate_mode == KDA_GATE_PREGATED   ? kda_recurrent_kernel<KDA_GATE_PREGATED, RTB>
+                                                              : kda_recurrent_kernel<KDA_GATE_SOFTPLUS, RTB>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(chains * RNSLICE)), dim3(256), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)g, (const uint16_t*)beta, A_log,
+                     dt_bias, cu_seqlens, initial_state, final_state, (uint16_t*)out, p->T, p->num_seqs, p->H_qk,
+                     p->H_v, p->scale, p->lower_bound, p->flags, p->init_state_dtype, p->final_state_dtype);
   return launch_status();
 }
 

@@ -32,7 +32,7 @@ _STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DT
 
 # Every function the header declares.
 EXPORTS = ("kda_fwd_workspace_size", "kda_fwd_check", "kda_fwd", "kda_fwd_intra", "kda_fwd_state",
-           "kda_status_string", "kda_last_error")
+           "kda_fused_recurrent_fwd", "kda_status_string", "kda_last_error")
 
 
 class KdaError(RuntimeError):
@@ -70,6 +70,8 @@ def load_library(path: str = LIB_PATH):
     for fn in (lib.kda_fwd, lib.kda_fwd_intra, lib.kda_fwd_state):
         fn.restype = ctypes.c_int
         fn.argtypes = [PP] + [P] * 12 + [ctypes.c_size_t, P]
+    lib.kda_fused_recurrent_fwd.restype = ctypes.c_int
+    lib.kda_fused_recurrent_fwd.argtypes = [PP] + [P] * 11 + [P]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_last_error.restype = ctypes.c_char_p
@@ -121,7 +123,7 @@ def _state_code(t: Optional[torch.Tensor]) -> int:
 
 def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GATE_SOFTPLUS,
         initial_state=None, final_state_dtype=torch.float32, cu_seqlens=None, out=None,
-        final_state=None, workspace=None, stage=None, qk_l2norm=True, beta_is_prob=False):
+        final_state=None, workspace=None, stage=None, qk_l2norm=True, beta_is_prob=False, recurrent=False):
     """Chunked KDA forward on the current HIP stream.
 
     q, k [B,T,Hqk,128] bf16; v, g [B,T,Hv,128] bf16; beta [B,T,Hv] bf16 logits
@@ -133,6 +135,8 @@ def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GAT
     Returns (out bf16 [B,T,Hv,128], final_state or None).  ``stage`` = "intra"
     or "state" runs only that half of the forward (kda_fwd_intra /
     kda_fwd_state); the two halves in order are the full forward.
+    ``recurrent`` runs the token-recurrent entry (kda_fused_recurrent_fwd)
+    instead: no workspace, and ``final_state`` may be ``initial_state``.
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
@@ -163,10 +167,19 @@ def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GAT
                     lower_bound=float(lower_bound), gate_mode=int(gate_mode),
                     init_state_dtype=_state_code(initial_state), final_state_dtype=_state_code(final_state),
                     flags=(FLAG_QK_L2NORM if qk_l2norm else 0) | (FLAG_BETA_IS_PROB if beta_is_prob else 0))
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    if recurrent:
+        if stage is not None or workspace is not None:
+            raise ValueError("the recurrent entry has no stages and no workspace")
+        rc = lib.kda_fused_recurrent_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+                                         _ptr(dt_bias), _ptr(cu_seqlens), _ptr(initial_state), _ptr(final_state),
+                                         _ptr(out), ctypes.c_void_p(stream))
+        if rc != KDA_OK:
+            raise KdaError(rc, lib.kda_last_error().decode())
+        return out, final_state
     need = int(lib.kda_fwd_workspace_size(ctypes.byref(p)))
     if workspace is None:
         workspace = _workspace(need, q.device)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
     entry = {None: lib.kda_fwd, "intra": lib.kda_fwd_intra, "state": lib.kda_fwd_state}[stage]
     rc = entry(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
                      _ptr(cu_seqlens), _ptr(initial_state), _ptr(final_state), _ptr(out), _ptr(workspace),

@@ -171,6 +171,21 @@ WORKLOADS = {
 }
 
 
+# Token-recurrent (decode) workloads: one decode step, and a short-sequence
+# batch, with the distributions of the safe-gate workload and fp32 state.
+RECURRENT_WORKLOADS = {
+    1: dict(name="decode_b64_t1_h32_lb-5", B=64, T=1, Hqk=32, gate_mode=GATE_SAFE_SIGMOID, lower_bound=-5.0,
+            A_log_range=(-4.0, 6.0), g_std=3.0, init_state_dtype=STATE_F32),
+    2: dict(name="short_b16_t64_h32_lb-5", B=16, T=64, Hqk=32, gate_mode=GATE_SAFE_SIGMOID, lower_bound=-5.0,
+            A_log_range=(-4.0, 6.0), g_std=3.0, init_state_dtype=STATE_F32),
+}
+
+
+def recurrent_workload(idx: int) -> KdaInputs:
+    """Draw token-recurrent workload ``idx`` (1..2) with seed = 100 + idx."""
+    return make_inputs(seed=100 + idx, **RECURRENT_WORKLOADS[idx])
+
+
 def workload(idx: int, **override) -> KdaInputs:
     """Draw measured workload ``idx`` (1..5) with seed = idx."""
     spec = dict(WORKLOADS[idx])

@@ -142,6 +142,22 @@ kda_status kda_fwd_state(const kda_fwd_params* p,
                          const int64_t* cu_seqlens, const void* initial_state, void* final_state,
                          void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Token-recurrent forward, for decode steps and short sequences: the second
+ * public entry point (fused recurrent, beside the chunked one) that the
+ * fla-kda SKILL.md names in its opening paragraph.
+ * Same parameters, tensors and validation as kda_fwd, minus the workspace: it
+ * evaluates the recurrence token by token with the fp32 state in registers,
+ * one workgroup per (sequence, v-head, 32-row slice of V), so its cost grows
+ * with the longest sequence; for long sequences kda_fwd is the faster path.
+ * initial_state and final_state may be the same buffer (an in-place state
+ * update), since every element is read before any is written by the same
+ * workgroup.  Returns after enqueueing. */
+kda_status kda_fused_recurrent_fwd(const kda_fwd_params* p,
+                                   const void* q, const void* k, const void* v, const void* g,
+                                   const void* beta, const float* A_log, const float* dt_bias,
+                                   const int64_t* cu_seqlens, const void* initial_state, void* final_state,
+                                   void* out, void* stream);
+
 /* Static name of a status code. */
 const char* kda_status_string(kda_status s);
 

@@ -173,3 +173,29 @@ def test_workspace_size_monotone(lib):
 def test_empty_input_needs_no_tensors(lib):
     p = base_params(T=0)
     assert check(lib, p, drop="q") == kda.KDA_OK
+
+
+def recurrent_call(lib, p, drop=None):
+    ptrs = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, cu=None,
+                h0=FAKE if p.init_state_dtype else None, hT=FAKE if p.final_state_dtype else None, out=FAKE)
+    for name in ((drop,) if isinstance(drop, str) else (drop or ())):
+        ptrs[name] = None
+    order = ["q", "k", "v", "g", "beta", "A_log", "dt_bias", "cu", "h0", "hT", "out"]
+    args = [None if ptrs[n] is None else ctypes.c_void_p(ptrs[n]) for n in order]
+    return lib.kda_fused_recurrent_fwd(ctypes.byref(p), *args, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(params=dict(K=64)), -2),
+    (dict(params=dict(gate_mode=3)), -8),
+    (dict(params=dict(gate_mode=kda.GATE_SAFE_SIGMOID, lower_bound=0.0)), -4),
+    (dict(params=dict(gate_mode=kda.GATE_PREGATED)), -8),
+    (dict(drop="q"), -1),
+    (dict(drop="A_log"), -1),
+    (dict(drop="hT"), -1),
+    (dict(params=dict(init_state_dtype=1, final_state_dtype=2)), -3),
+])
+def test_recurrent_entry_rejects_before_launch(lib, case, code):
+    # only rejections: a valid call would launch, and these tests run without a GPU
+    p = base_params(**case.get("params", {}))
+    assert recurrent_call(lib, p, case.get("drop")) == code, kda.last_error()
