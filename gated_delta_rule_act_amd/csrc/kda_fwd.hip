@@ -1124,13 +1124,16 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
 // token-recurrent forward (decode and short sequences)
 //
 // One workgroup of 256 threads per (sequence, v-head, 32-row V slice): thread
-// t owns state row v0 + (t >> 3), key columns 16 (t & 7) .. +15, as 16 fp32
-// values in registers.  Tokens go in blocks of RTB: the inputs of a block are
-// fetched into registers one block ahead, then written to a double-buffered
-// LDS slot where the gates (exp of the activation) and the q, k norms of all
-// the block's tokens are formed in parallel; the tokens of the block then run
-// with no barrier -- every state row is independent: decay its columns,
-// r = S k (an 8-lane reduction), the delta write, o = S q.
+// t owns state row v0 + (t >> 3) and the key columns 32 m + 4 (t & 7) + i
+// (m, i = 0..3), as 16 fp32 values in registers, so that each 16-byte load or
+// store instruction of a wave covers whole 128-byte row segments.  Tokens go
+// in blocks of RTB.  The inputs of a block are fetched into registers one
+// block ahead; wave w then prepares tokens w, w + 4, ... of the block (lane l
+// holds channels 2l, 2l + 1, so a token's norms are one wave reduction) and
+// writes scale q/|q|, k/|k| and the per-channel decay factor exp(a) to a
+// double-buffered LDS slot.  After one barrier the tokens of the block run
+// with no further barrier -- every state row is independent: decay its
+// columns, r = S k (an 8-lane reduction), the delta write, o = S q.
 constexpr int RSLICE = 32;                 // V rows per workgroup
 constexpr int RNSLICE = DV / RSLICE;
 // Tokens per block: RTB for sequences, 1 for decode steps (one token each).
@@ -1138,10 +1141,10 @@ constexpr int RTB = 8;
 
 template <int TB>
 struct RecurrentIn {
-  static constexpr int NE = (TB * DK + 255) / 256;
-  float q[NE], k[NE], g[NE];  // element e = tid + 256 i: token e >> 7, channel e & 127
-  float vv;                   // v: token tid >> 5, row tid & 31
-  float braw;                 // beta of token tid (tid < TB)
+  static constexpr int TPW = (TB + 3) / 4;  // tokens per wave
+  uint32_t q[TPW], k[TPW], g[TPW];          // bf16 pairs: token wave + 4 i, channels 2 lane, 2 lane + 1
+  float vv;                                 // v: token tid >> 5, row tid & 31
+  float braw;                               // beta of token tid (tid < TB)
 };
 
 // Issue the loads of the block starting at token s0 (tokens >= len read
@@ -1150,16 +1153,17 @@ template <int TB>
 __device__ __forceinline__ void recurrent_load(RecurrentIn<TB>& in, int64_t s0, int64_t len, int64_t bos,
                                                const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                                const uint16_t* g, const uint16_t* beta, int Hqk, int Hv, int h,
-                                               int hq, int v0, int tid) {
+                                               int hq, int v0, int tid, int wave) {
+  const int c = 2 * (tid & 63);
 #pragma unroll
-  for (int i = 0; i < RecurrentIn<TB>::NE; ++i) {
-    const int e = tid + 256 * i, tk = e >> 7, c = e & 127;
-    in.q[i] = in.k[i] = in.g[i] = 0.0f;
+  for (int i = 0; i < RecurrentIn<TB>::TPW; ++i) {
+    const int tk = wave + 4 * i;
+    in.q[i] = in.k[i] = in.g[i] = 0u;
     if (tk < TB && s0 + tk < len) {
       const size_t tok = (size_t)(bos + s0 + tk);
-      in.q[i] = bf2f(q[(tok * Hqk + hq) * DK + c]);
-      in.k[i] = bf2f(k[(tok * Hqk + hq) * DK + c]);
-      in.g[i] = bf2f(g[(tok * Hv + h) * DK + c]);
+      in.q[i] = *reinterpret_cast<const uint32_t*>(q + (tok * Hqk + hq) * DK + c);
+      in.k[i] = *reinterpret_cast<const uint32_t*>(k + (tok * Hqk + hq) * DK + c);
+      in.g[i] = *reinterpret_cast<const uint32_t*>(g + (tok * Hv + h) * DK + c);
     }
   }
   in.vv = 0.0f;
@@ -1207,28 +1211,28 @@ kda_recurrent_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   __shared__ __attribute__((aligned(16))) float sD[2][TB][DK];
   __shared__ __attribute__((aligned(16))) float sVv[2][TB][RSLICE];
   __shared__ float sB[2][TB];
-  __shared__ float sN[2][TB][4];  // per token: sum q^2 of its two waves, then sum k^2
 
   const int chain = blockIdx.x / RNSLICE, slice = blockIdx.x % RNSLICE;
   if (chain >= N * Hv) return;
   const int n = chain / Hv, h = chain % Hv, hq = h / (Hv / Hqk);
   const int v0 = RSLICE * slice;
   const int tid = threadIdx.x;
-  const int row = tid >> 3, kc = 16 * (tid & 7);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = tid >> 3, kc = 4 * (tid & 7);
   int64_t bos, len;
   if (cu == nullptr) { bos = (int64_t)n * T; len = T; }
   else { bos = cu[n]; len = cu[n + 1] - cu[n]; }
 
-  // state row v0 + row, columns kc .. kc + 15
+  // state row v0 + row, columns kc + 32 m + i (m, i = 0..3)
   float S[16];
   const size_t sidx = (((size_t)n * Hv + h) * DV + v0 + row) * DK + kc;
 #pragma unroll
   for (int j = 0; j < 16; j += 4) {
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
     if (init_dtype == KDA_STATE_F32) {
-      x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(h0) + sidx + j);
+      x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(h0) + sidx + 8 * j);
     } else if (init_dtype == KDA_STATE_BF16) {
-      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(h0) + sidx + j);
+      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(h0) + sidx + 8 * j);
       x = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
                       __uint_as_float(u.y & 0xffff0000u));
     }
@@ -1237,35 +1241,41 @@ kda_recurrent_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   const float A_exp = (MODE == KDA_GATE_PREGATED || A_log == nullptr) ? 1.0f : expf(A_log[h]);
   const float lb_log2e = lower_bound * kLog2e;
-  const float dtb = dt_bias != nullptr ? dt_bias[(size_t)h * DK + (tid & 127)] : 0.0f;
+  const float2 dtb = dt_bias != nullptr ? *reinterpret_cast<const float2*>(dt_bias + (size_t)h * DK + 2 * (tid & 63))
+                                        : make_float2(0.0f, 0.0f);
   const bool norm = flags & KDA_FLAG_QK_L2NORM;
   const bool beta_prob = flags & KDA_FLAG_BETA_IS_PROB;
 
   RecurrentIn<TB> cur;
-  recurrent_load<TB>(cur, 0, len, bos, q, k, v, g, beta, Hqk, Hv, h, hq, v0, tid);
+  recurrent_load<TB>(cur, 0, len, bos, q, k, v, g, beta, Hqk, Hv, h, hq, v0, tid, wave);
   for (int64_t s0 = 0; s0 < len; s0 += TB) {
     const int buf = (int)((s0 / TB) & 1);
     const int nb = (int)min((int64_t)TB, len - s0);
     RecurrentIn<TB> nxt;
-    recurrent_load<TB>(nxt, s0 + TB, len, bos, q, k, v, g, beta, Hqk, Hv, h, hq, v0, tid);
-    // 1. the block into LDS: raw q, k; the decay factor of every (token,
-    //    channel); the q, k norms; v of the slice rows; beta.  This buffer was
-    //    last read two blocks ago, before the previous block's barrier.
-    // Each token's 128 channels sit in two waves (lane = channel & 63), so its
-    // norms are two 64-lane butterflies and one sum -- the same order for any
-    // block length, hence bit-identical results for any split of a sequence.
+    recurrent_load<TB>(nxt, s0 + TB, len, bos, q, k, v, g, beta, Hqk, Hv, h, hq, v0, tid, wave);
+    // 1. the block into LDS: scale q/|q|, k/|k| and the decay factors of
+    //    wave w's tokens; v of the slice rows; beta.  This buffer was last read
+    //    two blocks ago, before the previous block's barrier.  A token's norms
+    //    are one reduction over its wave in a fixed order, so any split of a
+    //    sequence into calls gives bit-identical results.
+    const int c = 2 * (tid & 63);
 #pragma unroll
-    for (int i = 0; i < RecurrentIn<TB>::NE; ++i) {
-      const int e = tid + 256 * i, tk = e >> 7, c = e & 127;
+    for (int i = 0; i < RecurrentIn<TB>::TPW; ++i) {
+      const int tk = wave + 4 * i;
       if (tk < TB) {  // uniform per wave
-        sQ[buf][tk][c] = cur.q[i];
-        sK[buf][tk][c] = cur.k[i];
-        sD[buf][tk][c] = fast_exp2(gate2<MODE>(cur.g[i] + dtb, A_exp, lb_log2e));
-        const float q2 = sum64(cur.q[i] * cur.q[i]), k2 = sum64(cur.k[i] * cur.k[i]);
-        if ((tid & 63) == 0) {
-          sN[buf][tk][(tid >> 6) & 1] = q2;
-          sN[buf][tk][2 + ((tid >> 6) & 1)] = k2;
+        const float q0 = __uint_as_float(cur.q[i] << 16), q1 = __uint_as_float(cur.q[i] & 0xffff0000u);
+        const float k0 = __uint_as_float(cur.k[i] << 16), k1 = __uint_as_float(cur.k[i] & 0xffff0000u);
+        const float g0 = __uint_as_float(cur.g[i] << 16), g1 = __uint_as_float(cur.g[i] & 0xffff0000u);
+        float rq = scale, rk = 1.0f;
+        if (norm) {
+          rq *= rsqrtf(sum64(q0 * q0 + q1 * q1) + kL2Eps);
+          rk = rsqrtf(sum64(k0 * k0 + k1 * k1) + kL2Eps);
         }
+        *reinterpret_cast<float2*>(&sQ[buf][tk][c]) = make_float2(q0 * rq, q1 * rq);
+        *reinterpret_cast<float2*>(&sK[buf][tk][c]) = make_float2(k0 * rk, k1 * rk);
+        *reinterpret_cast<float2*>(&sD[buf][tk][c]) =
+            make_float2(fast_exp2(gate2<MODE>(g0 + dtb.x, A_exp, lb_log2e)),
+                        fast_exp2(gate2<MODE>(g1 + dtb.y, A_exp, lb_log2e)));
       }
     }
     if ((tid >> 5) < TB) sVv[buf][tid >> 5][tid & 31] = cur.vv;
@@ -1273,16 +1283,14 @@ kda_recurrent_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     __syncthreads();
     // 3. the block's tokens, in order, with no barrier
     for (int j = 0; j < nb; ++j) {
-      const float rq = norm ? rsqrtf(sN[buf][j][0] + sN[buf][j][1] + kL2Eps) : 1.0f;
-      const float rk = norm ? rsqrtf(sN[buf][j][2] + sN[buf][j][3] + kL2Eps) : 1.0f;
       const float b = sB[buf][j];
       const float vv = sVv[buf][j][row];
       float Kc[16], Qc[16], Dc[16];
 #pragma unroll
       for (int jj = 0; jj < 16; jj += 4) {
-        const float4 kk = *reinterpret_cast<const float4*>(&sK[buf][j][kc + jj]);
-        const float4 qq = *reinterpret_cast<const float4*>(&sQ[buf][j][kc + jj]);
-        const float4 dd = *reinterpret_cast<const float4*>(&sD[buf][j][kc + jj]);
+        const float4 kk = *reinterpret_cast<const float4*>(&sK[buf][j][kc + 8 * jj]);
+        const float4 qq = *reinterpret_cast<const float4*>(&sQ[buf][j][kc + 8 * jj]);
+        const float4 dd = *reinterpret_cast<const float4*>(&sD[buf][j][kc + 8 * jj]);
         Kc[jj] = kk.x; Kc[jj + 1] = kk.y; Kc[jj + 2] = kk.z; Kc[jj + 3] = kk.w;
         Qc[jj] = qq.x; Qc[jj + 1] = qq.y; Qc[jj + 2] = qq.z; Qc[jj + 3] = qq.w;
         Dc[jj] = dd.x; Dc[jj + 1] = dd.y; Dc[jj + 2] = dd.z; Dc[jj + 3] = dd.w;
@@ -1290,12 +1298,12 @@ kda_recurrent_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       float r = 0.f;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) { S[jj] *= Dc[jj]; r += S[jj] * Kc[jj]; }
-      r = sum8(r) * rk;
-      const float coef = b * (vv - r) * rk;
+      r = sum8(r);
+      const float coef = b * (vv - r);
       float o = 0.f;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) { S[jj] += coef * Kc[jj]; o += S[jj] * Qc[jj]; }
-      o = sum8(o) * (rq * scale);
+      o = sum8(o);
       if ((tid & 7) == 0)
         out[((size_t)(bos + s0 + j) * Hv + h) * DV + v0 + row] = __builtin_bit_cast(uint16_t, (__bf16)o);
     }
@@ -1305,7 +1313,8 @@ kda_recurrent_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   if (final_dtype == KDA_STATE_F32) {
 #pragma unroll
     for (int j = 0; j < 16; j += 4)
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(hT) + sidx + j) = make_float4(S[j], S[j + 1], S[j + 2], S[j + 3]);
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(hT) + sidx + 8 * j) =
+          make_float4(S[j], S[j + 1], S[j + 2], S[j + 3]);
   } else if (final_dtype == KDA_STATE_BF16) {
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
@@ -1314,7 +1323,7 @@ kda_recurrent_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j + 1]) << 16);
       u.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j + 2]) |
             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j + 3]) << 16);
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(hT) + sidx + j) = u;
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(hT) + sidx + 8 * j) = u;
     }
   }
 }
