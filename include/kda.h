@@ -70,7 +70,9 @@ typedef enum {
 typedef enum { KDA_GATE_SOFTPLUS = 0, KDA_GATE_SAFE_SIGMOID = 1, KDA_GATE_PREGATED = 2 } kda_gate_mode;
 typedef enum { KDA_STATE_NONE = 0, KDA_STATE_F32 = 1, KDA_STATE_BF16 = 2 } kda_state_dtype;
 
-/* flags (any combination; other bits are rejected):
+/* flags (any combination; other bits are rejected).  Raw and post-sigmoid
+ * beta, and the in-kernel q/k norm on and off, are among the variants the
+ * "fla-kda" skill listing names as test axes:
  *   KDA_FLAG_QK_L2NORM     normalise q and k (eps 1e-6 inside the root) in the kernel
  *   KDA_FLAG_BETA_IS_PROB  beta holds probabilities: no sigmoid is applied */
 enum { KDA_FLAG_QK_L2NORM = 1, KDA_FLAG_BETA_IS_PROB = 2 };
