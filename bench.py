@@ -121,6 +121,8 @@ def main():
     ap.add_argument("--workload", type=int, default=None,
                     help="workload index (chunked: 1-5, the bench line is 3; recurrent: 1-2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--segments", type=int, default=0,
+                    help="time segments per state chain (0: the library decides, 1: none)")
     ap.add_argument("--mode", choices=("chunked", "recurrent"), default="chunked",
                     help="chunked: the headline forward; recurrent: the token-recurrent entry on a decode workload")
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -158,15 +160,17 @@ def main():
     fs = torch.empty((inp.N, inp.Hv, inp.V, inp.K), dtype=fdt, device=dev)
     p = kda.make_params(B=inp.B, T=inp.T, H_qk=inp.Hqk, H_v=inp.Hv, num_seqs=inp.N, scale=inp.scale,
                         lower_bound=inp.lower_bound, gate_mode=inp.gate_mode,
-                        init_state_dtype=inp.init_state_dtype, final_state_dtype=inp.final_state_dtype)
+                        init_state_dtype=inp.init_state_dtype, final_state_dtype=inp.final_state_dtype,
+                        segments=args.segments)
     ws = torch.empty(kda.workspace_size(p), dtype=torch.uint8, device=dev)
+    nseg = kda.segments_of(p, packed=inp.cu_seqlens is not None)
     print(f"[bench] workload {inp.name} ready in {time.perf_counter() - t_gen:.1f} s; "
           f"workspace {ws.numel() / 2**30:.2f} GiB", file=sys.stderr, flush=True)
 
     def step(stage=None):
         kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"], inp.scale, inp.lower_bound,
                 inp.gate_mode, initial_state=d["h0"], cu_seqlens=d["cu_seqlens"], out=out, final_state=fs,
-                final_state_dtype=fdt, workspace=ws, stage=stage)
+                final_state_dtype=fdt, workspace=ws, stage=stage, segments=args.segments)
 
     for _ in range(args.warmup):
         step()
@@ -214,7 +218,7 @@ def main():
                    "lower_bound": inp.lower_bound, "chunk": 64, "sub_chunk": 16,
                    "initial_state": ["none", "fp32", "bf16"][inp.init_state_dtype],
                    "final_state": ["none", "fp32", "bf16"][inp.final_state_dtype],
-                   "packed": inp.cu_seqlens is not None},
+                   "packed": inp.cu_seqlens is not None, "state_segments": nseg},
         "roofline": {"bound": "hbm", "kernel": f"kda_{dom}_kernel", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": bm[dom],

@@ -37,6 +37,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "kda.h"
@@ -795,6 +796,14 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // operands (Kd) one chunk ahead -- they are needed only after the second
 // barrier.  The V slices of one chain run on one XCD and share its L2.
 constexpr int SWAVES = 4;
+// What one state workgroup computes over its range of chunks:
+//   ST_FULL   outputs and the state (the whole chain, or one segment of it
+//             from that segment's true entry state);
+//   ST_CARRY  the state only, no outputs (a segment carried from zero, or
+//             the first segment from the initial state);
+//   ST_TRANS  the segment's linear map P: the same recurrence with v = 0
+//             started from the identity, on key rows instead of value rows.
+constexpr int ST_FULL = 0, ST_CARRY = 1, ST_TRANS = 2;
 constexpr int SSS = 136;  // sS row stride (fp16): state slice stored as [v][k]
 constexpr int SUS = 72;   // sU row stride (fp16): U' stored as [v][t]
 constexpr int SVS = 48;   // sV row stride (16-bit): V slice row-major [t][v]
@@ -815,7 +824,8 @@ __device__ __forceinline__ u32x4 ld_frag(const uint8_t* blk, int fr, int lane) {
 
 // PART 0: token-tile operands, vectors and V (issued two chunks ahead);
 // PART 1: key-tile operands (issued one chunk ahead).
-template <int PART>
+// Operands a kind does not use are neither loaded nor kept.
+template <int PART, int KIND>
 __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk, int wave, int lane,
                                                 const uint16_t* __restrict__ v, int64_t row0, int len, int Hv, int h,
                                                 int v0, int tid) {
@@ -823,19 +833,24 @@ __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       o.wn[kb] = ld_frag(blk, F_WN + wave * 4 + kb, lane);
-      o.qg[kb] = ld_frag(blk, F_QG + wave * 4 + kb, lane);
+      if constexpr (KIND == ST_FULL) o.qg[kb] = ld_frag(blk, F_QG + wave * 4 + kb, lane);
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      o.tbh[kb] = ld_frag(blk, F_TBH + wave * 2 + kb, lane);
-      o.tbl[kb] = ld_frag(blk, F_TBL + wave * 2 + kb, lane);
-      o.aq[kb] = ld_frag(blk, F_AQK + wave * 2 + kb, lane);
+      if constexpr (KIND != ST_TRANS) {
+        o.tbh[kb] = ld_frag(blk, F_TBH + wave * 2 + kb, lane);
+        o.tbl[kb] = ld_frag(blk, F_TBL + wave * 2 + kb, lane);
+      }
+      if constexpr (KIND == ST_FULL) o.aq[kb] = ld_frag(blk, F_AQK + wave * 2 + kb, lane);
     }
     o.vec = ld_frag(blk, F_VEC, 16 * wave + (lane & 15));
-    // rows s >= len lie beyond the buffer range and read as zero
-    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + ((size_t)row0 * Hv + h) * DV + v0, (uint32_t)len * Hv * DV * 2);
-    o.vraw = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ((tid >> 2) * Hv * DV + 8 * (tid & 3)) * 2, 0, 0));
+    if constexpr (KIND != ST_TRANS) {
+      // rows s >= len lie beyond the buffer range and read as zero
+      const __amdgpu_buffer_rsrc_t rv =
+          buffer_rsrc(v + ((size_t)row0 * Hv + h) * DV + v0, (uint32_t)len * Hv * DV * 2);
+      o.vraw = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ((tid >> 2) * Hv * DV + 8 * (tid & 3)) * 2, 0, 0));
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -897,13 +912,20 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_b
 // every iteration).
 __device__ __forceinline__ void settle(const u32x4& a) { asm volatile("" ::"v"(a)); }
 __device__ __forceinline__ void settle(const f32x4& a) { asm volatile("" ::"v"(a)); }
+template <int KIND>
 __device__ __forceinline__ void settle(const ChunkRegs& r) {
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) { settle(r.wn[kb]); settle(r.qg[kb]); }
+  for (int kb = 0; kb < 4; ++kb) {
+    settle(r.wn[kb]);
+    if constexpr (KIND == ST_FULL) settle(r.qg[kb]);
+  }
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) { settle(r.tbh[kb]); settle(r.tbl[kb]); settle(r.aq[kb]); }
+  for (int kb = 0; kb < 2; ++kb) {
+    if constexpr (KIND != ST_TRANS) { settle(r.tbh[kb]); settle(r.tbl[kb]); }
+    if constexpr (KIND == ST_FULL) settle(r.aq[kb]);
+  }
   settle(r.vec);
-  settle(r.vraw);
+  if constexpr (KIND != ST_TRANS) settle(r.vraw);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -912,6 +934,7 @@ __device__ __forceinline__ void settle(const ChunkRegs& r) {
 
 // One chunk of the state chain: `cur` holds chunk c, `n1` receives the key-tile
 // operands of chunk c+1, `n2` the token-tile operands of chunk c+2.
+template <int KIND>
 __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2], ChunkRegs& cur, ChunkRegs& n1,
                                             ChunkRegs& n2, const int c, PendingOut& pd) {
   const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
@@ -920,7 +943,7 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
   // 1. publish the chunk's vectors, the V slice and the current state.  Every
   //    reader of these buffers in the previous chunk was before its B2.
   reinterpret_cast<u32x4*>(x.sVec)[16 * wave + (lane & 15)] = cur.vec;
-  *reinterpret_cast<u32x4*>(x.sV + (tid >> 2) * SVS + 8 * (tid & 3)) = cur.vraw;
+  if constexpr (KIND != ST_TRANS) *reinterpret_cast<u32x4*>(x.sV + (tid >> 2) * SVS + 8 * (tid & 3)) = cur.vraw;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -931,10 +954,10 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
   // 2. the previous chunk's outputs (none before the first chunk: len 0), then
   //    the token-tile prefetch of chunk c+2 (clamped, so every chunk queues the
   //    same operations)
-  store_pending(pd, x.out, x.Hv, x.h, x.v0, wave, li, lg);
+  if constexpr (KIND == ST_FULL) store_pending(pd, x.out, x.Hv, x.h, x.v0, wave, li, lg);
   {
     const int cp = min(c + 2, x.nc - 1);
-    load_chunk_part<0>(n2, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, x.bos + (int64_t)cp * CH,
+    load_chunk_part<0, KIND>(n2, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, x.bos + (int64_t)cp * CH,
                        chunk_len(x, cp), x.Hv, x.h, x.v0, tid);
   }
   __syncthreads();  // B1
@@ -946,33 +969,39 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
   f32x4 U[2], O[2];
 #pragma unroll
   for (int vt = 0; vt < 2; ++vt) {
-    const bf16x8 vb0 = __builtin_bit_cast(bf16x8, lds_frag_tr(x.sV, SVS, 0, 16 * vt, lane));
-    const bf16x8 vb1 = __builtin_bit_cast(bf16x8, lds_frag_tr(x.sV, SVS, 32, 16 * vt, lane));
     half8 sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
     f32x4 u0 = f32x4{0, 0, 0, 0}, u1 = f32x4{0, 0, 0, 0}, o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
-    u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[0]), vb0, u0, 0, 0, 0);
-    u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[0]), vb0, u1, 0, 0, 0);
-    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[0]), sb[0], o0, 0, 0, 0);
-    o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[1]), sb[1], o1, 0, 0, 0);
-    u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[1]), vb1, u0, 0, 0, 0);
-    u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[1]), vb1, u1, 0, 0, 0);
-    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[2]), sb[2], o0, 0, 0, 0);
-    o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[3]), sb[3], o1, 0, 0, 0);
+    if constexpr (KIND != ST_TRANS) {
+      const bf16x8 vb0 = __builtin_bit_cast(bf16x8, lds_frag_tr(x.sV, SVS, 0, 16 * vt, lane));
+      const bf16x8 vb1 = __builtin_bit_cast(bf16x8, lds_frag_tr(x.sV, SVS, 32, 16 * vt, lane));
+      u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[0]), vb0, u0, 0, 0, 0);
+      u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[0]), vb0, u1, 0, 0, 0);
+      if constexpr (KIND == ST_FULL) {
+        o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[0]), sb[0], o0, 0, 0, 0);
+        o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[1]), sb[1], o1, 0, 0, 0);
+      }
+      u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[1]), vb1, u0, 0, 0, 0);
+      u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[1]), vb1, u1, 0, 0, 0);
+      if constexpr (KIND == ST_FULL) {
+        o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[2]), sb[2], o0, 0, 0, 0);
+        o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[3]), sb[3], o1, 0, 0, 0);
+      }
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; kb += 2) {
       u0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[kb]), sb[kb], u0, 0, 0, 0);
       u1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[kb + 1]), sb[kb + 1], u1, 0, 0, 0);
     }
     U[vt] = u0 + u1;
-    O[vt] = (o0 + o1) * qs;
+    if constexpr (KIND == ST_FULL) O[vt] = (o0 + o1) * qs;
   }
   // 4. the key-tile prefetch of chunk c+1
   __builtin_amdgcn_sched_barrier(0);
   {
     const int cp = min(c + 1, x.nc - 1);
-    load_chunk_part<1>(n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+    load_chunk_part<1, KIND>(n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
   }
   __builtin_amdgcn_sched_barrier(0);
   // 5. U' = rk . U -> LDS hi/lo, transposed [v][t]
@@ -1010,34 +1039,60 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
       sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1][1]), uh1, sb2, 0, 0, 0);
       S[j][vt] = sa + sb2;
     }
-    O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[0]), uh0, O[vt], 0, 0, 0);
-    O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[1]), uh1, O[vt], 0, 0, 0);
+    if constexpr (KIND == ST_FULL) {
+      O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[0]), uh0, O[vt], 0, 0, 0);
+      O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[1]), uh1, O[vt], 0, 0, 0);
+    }
   }
+  if constexpr (KIND == ST_FULL) {
 #pragma unroll
-  for (int vt = 0; vt < 2; ++vt)
+    for (int vt = 0; vt < 2; ++vt)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) pd.o[vt][rr] = __builtin_bit_cast(uint16_t, (__bf16)O[vt][rr]);
-  pd.row0 = row0;
-  pd.len = chunk_len(x, c);
+      for (int rr = 0; rr < 4; ++rr) pd.o[vt][rr] = __builtin_bit_cast(uint16_t, (__bf16)O[vt][rr]);
+    pd.row0 = row0;
+    pd.len = chunk_len(x, c);
+  }
 }
 
+// Segment scratch (fp32 [V][K] matrices, one per (chain, segment)): entry
+// states, states carried from zero, and segment maps, in three planes.
+constexpr int SEG_SIN = 0, SEG_F = 1, SEG_P = 2;
+__device__ __forceinline__ float* seg_mat(float* seg, int chains, int nseg, int plane, int chain, int r) {
+  return seg + (((size_t)plane * chains + chain) * nseg + r) * (size_t)(DV * DK);
+}
+
+// One workgroup per (job, V slice).  A job is a whole chain (nseg == 1) or one
+// segment of it; seg_len chunks per segment (dense input only).
+//   ST_FULL  jobs (chain, r), r = 0..nseg-1: entry state h0 (nseg == 1) or
+//            S_in[r]; outputs; the final state from the last segment.
+//   ST_CARRY jobs (chain, r), r = 0..nseg-2: r = 0 copies h0 to S_in[0] and
+//            carries it into S_in[1], r >= 1 carries zero into F[r].
+// With segments, h0 is read only by the carry launch and the final state is
+// written only by the full launch, so the two may share one buffer.
+//   ST_TRANS jobs (chain, r), r = 1..nseg-2: from the identity into P[r];
+//            the "V slice" is then a range of key rows.
+template <int KIND>
 __global__ void __launch_bounds__(64 * SWAVES, 1)
 kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
                  const int* __restrict__ chunk_off, const void* __restrict__ h0, void* __restrict__ hT,
-                 uint16_t* __restrict__ out, const uint8_t* __restrict__ ws,
-                 int B, int T, int N, int Hv, int max_chunks, int init_dtype, int final_dtype) {
+                 uint16_t* __restrict__ out, const uint8_t* __restrict__ ws, float* __restrict__ seg,
+                 int B, int T, int N, int Hv, int max_chunks, int init_dtype, int final_dtype, int nseg,
+                 int seg_len) {
   __shared__ __attribute__((aligned(16))) float sVec[256];
   __shared__ __attribute__((aligned(16))) _Float16 sS[VS * SSS];
   __shared__ __attribute__((aligned(16))) _Float16 sUh[VS * SUS];
   __shared__ __attribute__((aligned(16))) _Float16 sUl[VS * SUS];
   __shared__ __attribute__((aligned(16))) _Float16 sV[CH * SVS];
 
-  // XCD-aware decode: the NSLICE slices of one chain share (id mod 8), so they
-  // are dispatched to the same XCD and share its L2 for the chain's operands.
+  // XCD-aware decode: the NSLICE slices of one job share (id mod 8), so they
+  // are dispatched to the same XCD and share its L2 for the job's operands.
+  const int jpc = KIND == ST_FULL ? nseg : KIND == ST_CARRY ? nseg - 1 : nseg - 2;  // jobs per chain
+  const int chains = N * Hv;
   const int id = blockIdx.x;
-  const int chain = (id / (8 * NSLICE)) * 8 + (id & 7);
+  const int job = (id / (8 * NSLICE)) * 8 + (id & 7);
   const int slice = (id >> 3) % NSLICE;
-  if (chain >= N * Hv) return;
+  if (job >= chains * jpc) return;
+  const int chain = job / jpc, r = job % jpc + (KIND == ST_TRANS ? 1 : 0);
   const int n = chain / Hv, h = chain % Hv;
   const int v0 = VS * slice;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1046,77 +1101,139 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
   int64_t bos, seqlen;
   int x0, nc;
   if (cu == nullptr) {
-    bos = (int64_t)n * T; seqlen = T;
     const int ncs = (T + CH - 1) / CH;
-    x0 = n * ncs; nc = ncs;
+    const int cs = r * seg_len;
+    bos = (int64_t)n * T + (int64_t)cs * CH; seqlen = (int64_t)T - (int64_t)cs * CH;
+    x0 = n * ncs + cs; nc = max(0, min(seg_len, ncs - cs));
   } else {
     bos = cu[n]; seqlen = cu[n + 1] - cu[n];
     x0 = chunk_off[n]; nc = chunk_off[n + 1] - x0;
   }
 
-  // state tiles S^T[k][v]: k = 32 wave + 16 j + 4 lg + r, v = v0 + 16 vt + li
+  // entry state: tiles S^T[k][v]: k = 32 wave + 16 j + 4 lg + rr, v = v0 + 16 vt + li
+  const void* src = nullptr;
+  int src_dtype = KDA_STATE_NONE;
+  size_t src_base = 0;
+  if ((KIND == ST_CARRY && r == 0) || (KIND == ST_FULL && nseg == 1)) {
+    src = h0; src_dtype = init_dtype; src_base = ((size_t)n * Hv + h) * DV * DK;
+  } else if (KIND == ST_FULL) {
+    src = seg_mat(seg, chains, nseg, SEG_SIN, chain, r); src_dtype = KDA_STATE_F32;
+  }
   f32x4 S[2][2];
-  const size_t sbase = ((size_t)n * Hv + h) * DV * DK;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int vt = 0; vt < 2; ++vt) {
       const int kk = 32 * wave + 16 * j + 4 * lg, vv = v0 + 16 * vt + li;
-      f32x4 s = f32x4{0, 0, 0, 0};
-      if (init_dtype == KDA_STATE_F32) {
-        s = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(h0) + sbase + (size_t)vv * DK + kk);
-      } else if (init_dtype == KDA_STATE_BF16) {
+      f32x4 st = f32x4{0, 0, 0, 0};
+      if constexpr (KIND == ST_TRANS) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) st[rr] = kk + rr == vv ? 1.0f : 0.0f;
+      } else if (src_dtype == KDA_STATE_F32) {
+        st = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(src) + src_base + (size_t)vv * DK + kk);
+      } else if (src_dtype == KDA_STATE_BF16) {
         const uint2 u =
-            *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(h0) + sbase + (size_t)vv * DK + kk);
-        s = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                  __uint_as_float(u.y & 0xffff0000u)};
+            *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + src_base + (size_t)vv * DK + kk);
+        st = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                   __uint_as_float(u.y & 0xffff0000u)};
       }
-      S[j][vt] = s;
+      S[j][vt] = st;
+      if (KIND == ST_CARRY && r == 0)
+        *reinterpret_cast<f32x4*>(seg_mat(seg, chains, nseg, SEG_SIN, chain, 0) + (size_t)vv * DK + kk) = st;
     }
 
   const uint8_t* wsh = ws + (size_t)h * max_chunks * BLOCK;
   StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, lane, li, lg, sVec, sS, sUh, sUl, sV};
   ChunkRegs rA, rB, rC;
   if (nc > 0) {
-    load_chunk_part<0>(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
-    load_chunk_part<1>(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, 0, 0, Hv, h, v0, tid);
+    load_chunk_part<0, KIND>(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
+    load_chunk_part<1, KIND>(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, 0, 0, Hv, h, v0, tid);
     const int c1 = min(1, nc - 1);
-    load_chunk_part<0>(rB, wsh + (size_t)(x0 + c1) * BLOCK, wave, lane, v, bos + (int64_t)c1 * CH,
-                       chunk_len(ctx, c1), Hv, h, v0, tid);
+    load_chunk_part<0, KIND>(rB, wsh + (size_t)(x0 + c1) * BLOCK, wave, lane, v, bos + (int64_t)c1 * CH,
+                             chunk_len(ctx, c1), Hv, h, v0, tid);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) { settle(S[j][0]); settle(S[j][1]); }
-  settle(rA);
+  settle<KIND>(rA);
   PendingOut pd;
   pd.row0 = bos;
   pd.len = 0;
   int c = 0;
   for (; c + 3 <= nc; c += 3) {
-    state_chunk(ctx, S, rA, rB, rC, c, pd);
-    state_chunk(ctx, S, rB, rC, rA, c + 1, pd);
-    state_chunk(ctx, S, rC, rA, rB, c + 2, pd);
+    state_chunk<KIND>(ctx, S, rA, rB, rC, c, pd);
+    state_chunk<KIND>(ctx, S, rB, rC, rA, c + 1, pd);
+    state_chunk<KIND>(ctx, S, rC, rA, rB, c + 2, pd);
   }
-  if (c < nc) state_chunk(ctx, S, rA, rB, rC, c, pd);
-  if (c + 1 < nc) state_chunk(ctx, S, rB, rC, rA, c + 1, pd);
-  store_pending(pd, out, Hv, h, v0, wave, li, lg);
+  if (c < nc) state_chunk<KIND>(ctx, S, rA, rB, rC, c, pd);
+  if (c + 1 < nc) state_chunk<KIND>(ctx, S, rB, rC, rA, c + 1, pd);
+  if constexpr (KIND == ST_FULL) store_pending(pd, out, Hv, h, v0, wave, li, lg);
 
-  if (final_dtype != KDA_STATE_NONE) {
+  // exit state
+  void* dst = nullptr;
+  int dst_dtype = KDA_STATE_NONE;
+  size_t dst_base = 0;
+  if constexpr (KIND == ST_FULL) {
+    if (r == nseg - 1) { dst = hT; dst_dtype = final_dtype; dst_base = ((size_t)n * Hv + h) * DV * DK; }
+  } else {
+    dst = KIND == ST_TRANS ? seg_mat(seg, chains, nseg, SEG_P, chain, r)
+          : r == 0         ? seg_mat(seg, chains, nseg, SEG_SIN, chain, 1)
+                           : seg_mat(seg, chains, nseg, SEG_F, chain, r);
+    dst_dtype = KDA_STATE_F32;
+  }
+  if (dst_dtype != KDA_STATE_NONE) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int vt = 0; vt < 2; ++vt) {
         const int kk = 32 * wave + 16 * j + 4 * lg, vv = v0 + 16 * vt + li;
-        if (final_dtype == KDA_STATE_F32) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(hT) + sbase + (size_t)vv * DK + kk) = S[j][vt];
+        if (dst_dtype == KDA_STATE_F32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dst) + dst_base + (size_t)vv * DK + kk) = S[j][vt];
         } else {
           uint2 u;
           u.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][0]) |
                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][1]) << 16);
           u.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][2]) |
                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][3]) << 16);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(hT) + sbase + (size_t)vv * DK + kk) = u;
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dst) + dst_base + (size_t)vv * DK + kk) = u;
         }
       }
+  }
+}
+
+// Entry states of the segments: S_in[r + 1] = S_in[r] P[r] + F[r] for
+// r = 1..nseg-2 (S_in[1] is the first segment's exit state).  One workgroup
+// per (chain, 8 value rows); P[r] is staged in LDS, the 8 rows of S_in stay
+// in LDS from step to step.
+constexpr int CMB_ROWS = 8;
+constexpr int CMB_XS = DK + 4;  // sX row stride: the two rows a wave reads sit on different banks
+__global__ void __launch_bounds__(256)
+kda_segment_combine_kernel(float* __restrict__ seg, int chains, int nseg) {
+  __shared__ __attribute__((aligned(16))) float sP[DK * DK];
+  __shared__ __attribute__((aligned(16))) float sX[CMB_ROWS * CMB_XS];
+  const int chain = blockIdx.x / (DV / CMB_ROWS), rb = blockIdx.x % (DV / CMB_ROWS);
+  if (chain >= chains) return;
+  const int tid = threadIdx.x, row = tid >> 5, c0 = 4 * (tid & 31);
+  const size_t off = (size_t)(rb * CMB_ROWS + row) * DK + c0;
+  *reinterpret_cast<float4*>(&sX[row * CMB_XS + c0]) =
+      *reinterpret_cast<const float4*>(seg_mat(seg, chains, nseg, SEG_SIN, chain, 1) + off);
+  for (int r = 1; r + 1 < nseg; ++r) {
+    const float* P = seg_mat(seg, chains, nseg, SEG_P, chain, r);
+#pragma unroll
+    for (int i = 0; i < DK * DK / 4 / 256; ++i) {
+      const int e = tid + 256 * i;
+      *reinterpret_cast<float4*>(&sP[4 * e]) = *reinterpret_cast<const float4*>(P + 4 * e);
+    }
+    float4 acc = *reinterpret_cast<const float4*>(seg_mat(seg, chains, nseg, SEG_F, chain, r) + off);
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < DK; ++k) {
+      const float xk = sX[row * CMB_XS + k];
+      const float4 pk = *reinterpret_cast<const float4*>(&sP[k * DK + c0]);
+      acc.x += xk * pk.x; acc.y += xk * pk.y; acc.z += xk * pk.z; acc.w += xk * pk.w;
+    }
+    __syncthreads();  // every read of sX and sP of this step is done
+    *reinterpret_cast<float4*>(&sX[row * CMB_XS + c0]) = acc;
+    *reinterpret_cast<float4*>(seg_mat(seg, chains, nseg, SEG_SIN, chain, r + 1) + off) = acc;
   }
 }
 
@@ -1351,6 +1468,32 @@ size_t header_bytes(const kda_fwd_params* p) {
   return (b + 255) & ~(size_t)255;
 }
 
+// Time segments per state chain (dense input only) and chunks per segment.
+// Automatic (segments == 0): split only when the state launch has at most
+// half as many workgroups as the GPU has CUs (one state workgroup fills a
+// CU), into up to 256 / workgroups segments of at least 16 chunks each.
+constexpr int kMaxSegments = 256;
+int seg_plan(const kda_fwd_params* p, bool packed, int* seg_len) {
+  const int ncs = (int)(((int64_t)p->T + CH - 1) / CH);
+  int nseg = 1;
+  if (!packed && ncs > 1) {
+    if (p->segments >= 2) {
+      nseg = p->segments;
+    } else if (p->segments == 0) {
+      const int64_t wgs = (int64_t)p->num_seqs * p->H_v * NSLICE;
+      if (wgs <= 128) nseg = (int)std::min<int64_t>(256 / wgs, ncs / 16);
+    }
+    nseg = std::max(1, std::min(nseg, std::min(ncs, kMaxSegments)));
+  }
+  const int len = ncs > 0 ? (ncs + nseg - 1) / nseg : 0;
+  *seg_len = len;
+  return len > 0 ? (ncs + len - 1) / len : 1;
+}
+
+size_t seg_scratch_bytes(const kda_fwd_params* p, int nseg) {
+  return nseg > 1 ? (size_t)3 * p->num_seqs * p->H_v * nseg * DV * DK * sizeof(float) : 0;
+}
+
 kda_status check_params(const kda_fwd_params* p, bool packed) {
   if (!p) return fail(KDA_ERR_NULL, "params is NULL");
   if (p->K != DK || p->V != DV) return fail(KDA_ERR_SHAPE, "K and V must both be 128 (got K=%d, V=%d)", p->K, p->V);
@@ -1385,6 +1528,8 @@ kda_status check_params(const kda_fwd_params* p, bool packed) {
   if (p->init_state_dtype != KDA_STATE_NONE && p->final_state_dtype != KDA_STATE_NONE &&
       p->init_state_dtype != p->final_state_dtype)
     return fail(KDA_ERR_DTYPE, "initial_state and final_state dtypes must match when both are given");
+  if (p->segments < 0 || p->segments > kMaxSegments)
+    return fail(KDA_ERR_RANGE, "segments must be in [0, %d] (got %d)", kMaxSegments, p->segments);
   return KDA_OK;
 }
 
@@ -1400,7 +1545,18 @@ size_t kda_fwd_workspace_size(const kda_fwd_params* p) {
   const bool packed = p->B == 1 && p->num_seqs >= 1;
   if (check_params(p, false) != KDA_OK && check_params(p, true) != KDA_OK) return 0;
   const int64_t mc = max_chunks_of(p, packed);
-  return header_bytes(p) + (size_t)p->H_v * (size_t)mc * BLOCK;
+  size_t seg = 0;
+  if (check_params(p, false) == KDA_OK) {
+    int len;
+    seg = seg_scratch_bytes(p, seg_plan(p, false, &len));
+  }
+  return header_bytes(p) + (size_t)p->H_v * (size_t)mc * BLOCK + seg;
+}
+
+int kda_fwd_segments(const kda_fwd_params* p, int packed) {
+  if (!p || check_params(p, packed != 0) != KDA_OK) return 0;
+  int len;
+  return seg_plan(p, packed != 0, &len);
 }
 
 }  // extern "C"
@@ -1491,11 +1647,31 @@ kda_status launch_state(const kda_fwd_params* p, const void* v, const int64_t* c
   uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
   const int* chunk_off = reinterpret_cast<const int*>(wsb);
   const uint8_t* blocks = wsb + header_bytes(p);
+  float* seg = reinterpret_cast<float*>(wsb + header_bytes(p) + (size_t)p->H_v * (size_t)mc * BLOCK);
   const int chains = p->num_seqs * p->H_v;
-  const int groups = (chains + 7) / 8;
-  hipLaunchKernelGGL(kda_state_kernel, dim3((unsigned)(groups * 8 * NSLICE)), dim3(64 * SWAVES), 0, st,
-                     (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out,
-                     blocks, p->B, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype, p->final_state_dtype);
+  int seg_len;
+  const int nseg = seg_plan(p, packed, &seg_len);
+  // grid of a launch with `jobs` jobs: groups of 8 jobs, NSLICE workgroups each
+  auto grid = [](int64_t jobs) { return dim3((unsigned)(((jobs + 7) / 8) * 8 * NSLICE)); };
+  if (nseg > 1) {
+    // entry states of the segments from their zero-state carries and maps
+    hipLaunchKernelGGL(kda_state_kernel<ST_CARRY>, grid((int64_t)chains * (nseg - 1)), dim3(64 * SWAVES), 0, st,
+                       (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out,
+                       blocks, seg, p->B, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype,
+                       p->final_state_dtype, nseg, seg_len);
+    if (nseg > 2) {
+      hipLaunchKernelGGL(kda_state_kernel<ST_TRANS>, grid((int64_t)chains * (nseg - 2)), dim3(64 * SWAVES), 0, st,
+                         (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out,
+                         blocks, seg, p->B, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype,
+                         p->final_state_dtype, nseg, seg_len);
+      hipLaunchKernelGGL(kda_segment_combine_kernel, dim3((unsigned)(chains * (DV / CMB_ROWS))), dim3(256), 0, st,
+                         seg, chains, nseg);
+    }
+  }
+  hipLaunchKernelGGL(kda_state_kernel<ST_FULL>, grid((int64_t)chains * nseg), dim3(64 * SWAVES), 0, st,
+                     (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out, blocks,
+                     seg, p->B, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype, p->final_state_dtype, nseg,
+                     seg_len);
   return KDA_OK;
 }
 

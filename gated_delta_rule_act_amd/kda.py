@@ -31,7 +31,7 @@ _STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DT
            -5: "KDA_ERR_ALIGN", -6: "KDA_ERR_WORKSPACE", -7: "KDA_ERR_LAUNCH", -8: "KDA_ERR_UNSUPPORTED"}
 
 # Every function the header declares.
-EXPORTS = ("kda_fwd_workspace_size", "kda_fwd_check", "kda_fwd", "kda_fwd_intra", "kda_fwd_state",
+EXPORTS = ("kda_fwd_workspace_size", "kda_fwd_segments", "kda_fwd_check", "kda_fwd", "kda_fwd_intra", "kda_fwd_state",
            "kda_fused_recurrent_fwd", "kda_status_string", "kda_last_error")
 
 
@@ -47,7 +47,7 @@ class Params(ctypes.Structure):
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("lower_bound", ctypes.c_float), ("gate_mode", ctypes.c_int32),
                 ("init_state_dtype", ctypes.c_int32), ("final_state_dtype", ctypes.c_int32),
-                ("flags", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("segments", ctypes.c_int32)]
 
 
 _lib = None
@@ -65,6 +65,8 @@ def load_library(path: str = LIB_PATH):
     PP = ctypes.POINTER(Params)
     lib.kda_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_fwd_workspace_size.argtypes = [PP]
+    lib.kda_fwd_segments.restype = ctypes.c_int
+    lib.kda_fwd_segments.argtypes = [PP, ctypes.c_int]
     lib.kda_fwd_check.restype = ctypes.c_int
     lib.kda_fwd_check.argtypes = [PP] + [P] * 12 + [ctypes.c_size_t]
     for fn in (lib.kda_fwd, lib.kda_fwd_intra, lib.kda_fwd_state):
@@ -82,13 +84,18 @@ def load_library(path: str = LIB_PATH):
 
 def make_params(*, B, T, H_qk, H_v, K=128, V=128, num_seqs=None, scale, lower_bound=-1.0,
                 gate_mode=GATE_SOFTPLUS, init_state_dtype=STATE_NONE, final_state_dtype=STATE_F32,
-                flags=FLAG_QK_L2NORM) -> Params:
+                flags=FLAG_QK_L2NORM, segments=0) -> Params:
     return Params(B, T, H_qk, H_v, K, V, B if num_seqs is None else num_seqs, scale, lower_bound, gate_mode,
-                  init_state_dtype, final_state_dtype, flags)
+                  init_state_dtype, final_state_dtype, flags, segments)
 
 
 def workspace_size(p: Params) -> int:
     return int(load_library().kda_fwd_workspace_size(ctypes.byref(p)))
+
+
+def segments_of(p: Params, packed: bool = False) -> int:
+    """Time segments per state chain kda_fwd uses for these parameters (0 if invalid)."""
+    return int(load_library().kda_fwd_segments(ctypes.byref(p), int(packed)))
 
 
 def last_error() -> str:
@@ -123,7 +130,8 @@ def _state_code(t: Optional[torch.Tensor]) -> int:
 
 def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GATE_SOFTPLUS,
         initial_state=None, final_state_dtype=torch.float32, cu_seqlens=None, out=None,
-        final_state=None, workspace=None, stage=None, qk_l2norm=True, beta_is_prob=False, recurrent=False):
+        final_state=None, workspace=None, stage=None, qk_l2norm=True, beta_is_prob=False, recurrent=False,
+        segments=0):
     """Chunked KDA forward on the current HIP stream.
 
     q, k [B,T,Hqk,128] bf16; v, g [B,T,Hv,128] bf16; beta [B,T,Hv] bf16 logits
@@ -136,7 +144,9 @@ def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GAT
     or "state" runs only that half of the forward (kda_fwd_intra /
     kda_fwd_state); the two halves in order are the full forward.
     ``recurrent`` runs the token-recurrent entry (kda_fused_recurrent_fwd)
-    instead: no workspace, and ``final_state`` may be ``initial_state``.
+    instead: no workspace.  ``final_state`` may be ``initial_state`` in both
+    entries.  ``segments`` splits each state chain of dense input into that
+    many parallel time segments (0: the library decides, 1: never).
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
@@ -166,7 +176,8 @@ def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GAT
     p = make_params(B=B, T=T, H_qk=Hqk, H_v=Hv, K=K, V=V, num_seqs=N, scale=float(scale),
                     lower_bound=float(lower_bound), gate_mode=int(gate_mode),
                     init_state_dtype=_state_code(initial_state), final_state_dtype=_state_code(final_state),
-                    flags=(FLAG_QK_L2NORM if qk_l2norm else 0) | (FLAG_BETA_IS_PROB if beta_is_prob else 0))
+                    flags=(FLAG_QK_L2NORM if qk_l2norm else 0) | (FLAG_BETA_IS_PROB if beta_is_prob else 0),
+                    segments=int(segments))
     stream = torch.cuda.current_stream(q.device).cuda_stream
     if recurrent:
         if stage is not None or workspace is not None:

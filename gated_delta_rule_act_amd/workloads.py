@@ -168,6 +168,11 @@ WORKLOADS = {
             init_state_dtype=STATE_BF16, final_state_dtype=STATE_BF16, packed=16),
     5: dict(name="gva_t131072_hqk16_hv32_lb-1", B=1, T=131072, Hqk=16, Hv=32,
             gate_mode=GATE_SAFE_SIGMOID, lower_bound=-1.0),
+    # one GPU's share of workload 5 when its 32 v-heads are split over 8 GPUs
+    # (2 qk-heads with their 4 v-heads): few (sequence, head) chains, each of
+    # 2,048 chunks -- the case time segments of the state chain are for
+    6: dict(name="gva_share_t131072_hqk2_hv4_lb-1", B=1, T=131072, Hqk=2, Hv=4,
+            gate_mode=GATE_SAFE_SIGMOID, lower_bound=-1.0),
 }
 
 
@@ -187,7 +192,7 @@ def recurrent_workload(idx: int) -> KdaInputs:
 
 
 def workload(idx: int, **override) -> KdaInputs:
-    """Draw measured workload ``idx`` (1..5) with seed = idx."""
+    """Draw measured workload ``idx`` (1..6) with seed = idx."""
     spec = dict(WORKLOADS[idx])
     spec.update(override)
     packed = spec.pop("packed", None)

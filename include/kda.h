@@ -88,11 +88,28 @@ typedef struct {
   int32_t init_state_dtype;   /* kda_state_dtype of initial_state (NONE: zero state) */
   int32_t final_state_dtype;  /* kda_state_dtype of final_state (NONE: not written) */
   int32_t flags;              /* KDA_FLAG_* bits */
+  int32_t segments;           /* time segments per state chain; dense input only (ignored
+                                 with cu_seqlens).  The chunk chain of each (sequence, v-head)
+                                 is cut into runs that proceed in parallel: each run's state
+                                 carried from zero and its linear map give its entry state,
+                                 then every run emits its outputs -- the one-GPU form of the
+                                 context parallelism the fla-kda SKILL.md "Validation" section
+                                 lists.  0 = automatic (split only when there are few
+                                 (sequence, v-head) pairs), 1 = never, n in [2, 256] = up to n
+                                 (at most one per 64-token chunk).  Other values are rejected
+                                 with KDA_ERR_RANGE.  Results agree with the unsplit chain
+                                 within rounding, not bit for bit. */
 } kda_fwd_params;
 
 /* Bytes of device workspace kda_fwd needs for these parameters; host only,
  * no HIP calls.  Returns 0 if the parameters are invalid. */
 size_t kda_fwd_workspace_size(const kda_fwd_params* p);
+
+/* Time segments per state chain that kda_fwd uses for these parameters (1:
+ * the chain is not split), for dense input (packed == 0) or input with
+ * cu_seqlens (packed != 0, always 1); host only.  Returns 0 if the
+ * parameters are invalid. */
+int kda_fwd_segments(const kda_fwd_params* p, int packed);
 
 /* Validates parameters and pointers exactly as kda_fwd does, without
  * launching anything; host only, no HIP calls.  Pointers are device
@@ -117,8 +134,11 @@ kda_status kda_fwd_check(const kda_fwd_params* p,
  *   out       bf16 [B, T, H_v, 128] -- every element is written
  *   workspace at least kda_fwd_workspace_size(p) bytes, 256-byte aligned
  *   stream    a hipStream_t (NULL: the default stream)
- * Tensors are dense row-major.  Returns after enqueueing; KDA_ERR_LAUNCH if
- * the runtime reports a launch error. */
+ * Tensors are dense row-major.  initial_state and final_state may be the
+ * same buffer (an in-place state update): every element of the initial state
+ * is read before the launch that writes the final state, or by the workgroup
+ * that later writes it.  Returns after enqueueing; KDA_ERR_LAUNCH if the
+ * runtime reports a launch error. */
 kda_status kda_fwd(const kda_fwd_params* p,
                    const void* q, const void* k, const void* v, const void* g,
                    const void* beta, const float* A_log, const float* dt_bias,

@@ -50,22 +50,24 @@ def final_dtype_of(inp):
     return {W.STATE_NONE: None, W.STATE_F32: torch.float32, W.STATE_BF16: torch.bfloat16}[inp.final_state_dtype]
 
 
-def run_gpu(inp: W.KdaInputs, dev_inputs=None, poison=True):
+def run_gpu(inp: W.KdaInputs, dev_inputs=None, poison=True, segments=0, final_state=None, initial_state=None):
     d = dev_inputs or to_device(inp)
     B, T, Hv, V = inp.B, inp.T, inp.Hv, inp.V
     out = torch.empty((B, T, Hv, V), dtype=torch.bfloat16, device="cuda")
-    fs = None
+    fs = final_state
     fdt = final_dtype_of(inp)
-    if fdt is not None:
+    if fs is None and fdt is not None:
         fs = torch.empty((inp.N, Hv, V, inp.K), dtype=fdt, device="cuda")
+        if poison:
+            fs.fill_(float("nan"))
     if poison:
         out.fill_(float("nan"))
-        if fs is not None:
-            fs.fill_(float("nan"))
+    h0 = d["h0"] if initial_state is None else initial_state
     o, s = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"], inp.scale,
-                   inp.lower_bound, inp.gate_mode, initial_state=d["h0"], cu_seqlens=d["cu_seqlens"],
+                   inp.lower_bound, inp.gate_mode, initial_state=h0, cu_seqlens=d["cu_seqlens"],
                    out=out, final_state=fs, final_state_dtype=fdt,
-                   qk_l2norm=bool(inp.flags & W.FLAG_QK_L2NORM), beta_is_prob=bool(inp.flags & W.FLAG_BETA_IS_PROB))
+                   qk_l2norm=bool(inp.flags & W.FLAG_QK_L2NORM), beta_is_prob=bool(inp.flags & W.FLAG_BETA_IS_PROB),
+                   segments=segments)
     torch.cuda.synchronize()
     return o, s
 

@@ -199,3 +199,38 @@ def test_recurrent_entry_rejects_before_launch(lib, case, code):
     # only rejections: a valid call would launch, and these tests run without a GPU
     p = base_params(**case.get("params", {}))
     assert recurrent_call(lib, p, case.get("drop")) == code, kda.last_error()
+
+
+@pytest.mark.parametrize("segments,code", [(-1, -4), (257, -4), (0, 0), (1, 0), (2, 0), (256, 0)])
+def test_segments_range(lib, segments, code):
+    p = base_params(segments=segments)
+    assert check(lib, p) == code, kda.last_error()
+
+
+def segs(lib, packed=False, **kw):
+    return lib.kda_fwd_segments(ctypes.byref(base_params(**kw)), int(packed))
+
+
+def test_segment_plan(lib):
+    # automatic: split only when the state launch has <= 128 workgroups (4 per chain)
+    assert segs(lib, B=1, T=131072, H_qk=2, H_v=4) == 16
+    assert segs(lib, B=1, T=131072, H_qk=16, H_v=32) == 2
+    assert segs(lib, B=2, T=8192, H_qk=32, H_v=32) == 1
+    assert segs(lib, B=1, T=2048, H_qk=1, H_v=1) == 2       # 32 chunks: segments of at least 16
+    assert segs(lib, B=1, T=1024, H_qk=1, H_v=1) == 1
+    # forced: at most one per chunk, and no empty segment
+    assert segs(lib, B=1, T=200, H_qk=1, H_v=1, segments=7) == 4
+    assert segs(lib, B=1, T=64 * 10, H_qk=1, H_v=1, segments=4) == 4     # 3 + 3 + 3 + 1 chunks
+    assert segs(lib, B=1, T=64 * 9, H_qk=1, H_v=1, segments=6) == 5      # 2 chunks each: 5 segments
+    assert segs(lib, B=2, T=4096, segments=1) == 1
+    assert segs(lib, B=1, T=0, H_qk=1, H_v=1, segments=8) == 1
+    # packed input never splits; invalid parameters give 0
+    assert segs(lib, packed=True, B=1, T=131072, H_qk=2, H_v=4, segments=8) == 1
+    assert segs(lib, B=2, T=100, segments=-3) == 0
+
+
+def test_workspace_holds_segment_scratch(lib):
+    p1 = base_params(B=1, T=4096, H_qk=2, H_v=2, segments=1)
+    p4 = base_params(B=1, T=4096, H_qk=2, H_v=2, segments=4)
+    extra = lib.kda_fwd_workspace_size(ctypes.byref(p4)) - lib.kda_fwd_workspace_size(ctypes.byref(p1))
+    assert extra == 3 * 2 * 4 * 128 * 128 * 4    # entry states, carries, maps: fp32 per (chain, segment)

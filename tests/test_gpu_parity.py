@@ -2,7 +2,7 @@
 
 Small cases are compared element by element (several 64-token chunks plus a
 ragged tail, every gate mode, packed sequences, grouped heads, state dtypes);
-the five measured workloads are run at full size in the same launch
+the six measured workloads are run at full size in the same launch
 configuration the benchmark times, and compared on sampled (sequence, head)
 pairs that the oracle evaluates one by one, plus properties that hold at any
 size (every output written, finite).
@@ -191,10 +191,11 @@ def test_long_cumulative_decay_no_write():
 
 # ---------------------------------------------------------------- the five measured workloads
 SAMPLES = {1: None, 2: [(0, 0), (1, 5), (3, 15), (2, 9)], 3: [(0, 0), (1, 31), (0, 17), (1, 6)],
-           4: [(0, 0), (5, 31), (11, 7), (15, 20)], 5: [(0, 0), (0, 1), (0, 17), (0, 30)]}
+           4: [(0, 0), (5, 31), (11, 7), (15, 20)], 5: [(0, 0), (0, 1), (0, 17), (0, 30)],
+           6: [(0, 0), (0, 1), (0, 2), (0, 3)]}
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6])
 def test_measured_workload(idx):
     inp = W.workload(idx)
     U.log(f"[gpu] workload {idx} {inp.name}: B={inp.B} T={inp.T} Hqk={inp.Hqk} Hv={inp.Hv} N={inp.N}")
