@@ -33,6 +33,44 @@ MUTATIONS = {
 }
 
 
+# mistakes planted in the gradient code, caught by tests/test_oracle_bwd.py
+MUTATIONS_BWD = {
+    "bwd_no_decay_carry": ("dS[(size_t)i * K + c] *= tk.ea[c];", "dS[(size_t)i * K + c] *= 1.0;"),
+    "bwd_read_sign": ("const double dr = -tk.bt * du[i];", "const double dr = tk.bt * du[i];"),
+    "bwd_no_read_key_term": ("dkn[c] += Sd[(size_t)i * K + c] * dr;", "dkn[c] += 0.0 * dr;"),
+    "bwd_output_state_before_write": ("acc += St[(size_t)i * K + c] * dot[i];", "acc += Sp[(size_t)i * K + c] * dot[i];"),
+    "bwd_decay_grad_no_exp": ("da[c] = tk.ea[c] * acc;", "da[c] = acc;"),
+    "bwd_norm_no_projection": ("dqt[c] = tk.rq * (dqn[c] - tk.qn[c] * yq);", "dqt[c] = tk.rq * dqn[c];"),
+    "bwd_beta_no_sigmoid_grad": ("dbt * tk.bt * (1.0 - tk.bt);", "dbt;"),
+    "bwd_softplus_grad_sign": ("dadx = -Aexp * orc_sigmoid(x);", "dadx = Aexp * orc_sigmoid(x);"),
+    "bwd_safe_grad_missing_exp": ("dadx = lower_bound * s * (1.0 - s) * Aexp;", "dadx = lower_bound * s * (1.0 - s);"),
+    "bwd_gva_sum_one_head": ("for (int j = 0; j < G; ++j) {", "for (int j = 0; j < 1; ++j) {"),
+    "bwd_dbeta_uses_v": ("dbt += acc * (tk.vv[i] - r[i]);", "dbt += acc * tk.vv[i];"),
+    "bwd_checkpoint_off_by_one": ("memcpy(Sbuf, Sck + (size_t)blk * VK", "memcpy(Sbuf, Sck + (size_t)(blk > 0 ? blk - 1 : 0) * VK"),
+}
+
+
+def _run_pins(name, old, new, tmp_path, pin_file):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old}"
+    mutated = tmp_path / "kda_oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / "libkda_oracle_mut.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-w",
+                           "-o", str(lib), str(mutated), "-lm"])
+    env = dict(os.environ, KDA_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", pin_file)],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutation {name} survived every pin:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS_BWD))
+def test_gradient_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTATIONS_BWD[name]
+    _run_pins(name, old, new, tmp_path, "test_oracle_bwd.py")
+
+
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_catch_planted_mistake(name, tmp_path):
     old, new = MUTATIONS[name]
