@@ -6,7 +6,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "kda_fwd.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "kda_fwd.hip"), os.path.join(PKG, "csrc", "kda_bwd.hip")]
 LIB = os.path.join(PKG, "libkda.so")
 
 HIPCC_FLAGS = [

@@ -1,0 +1,1287 @@
+// Chunked Kimi Delta Attention backward for MI355X (gfx950, CDNA4).
+//
+// Gradients of the forward in include/kda.h with respect to q, k, v, g, beta,
+// A_log, dt_bias and the initial state, given the gradients of out and of the
+// final state.  The fla-kda SKILL.md lists backward passes in its "Code map"
+// and asks for forward, final-state and gradient coverage in "Validation";
+// the pages do not print the backward, so it is derived here from the chunked
+// forward (64-token chunks, per chunk with entry state S):
+//     Akk = diag(b) (K K^T . E) strictly lower,  Aqk = (Q K^T . E) lower,
+//     E_ij = e^(G_i - G_j) per key channel,  T = (I + Akk)^-1,  M = T diag(b),
+//     W = M (K . e^G),  Ubar = M V,  U = Ubar - W S^T,
+//     O = (Q . e^G) S^T + Aqk U,  S' = S Diag(e^G_last) + U^T (K . e^(G_last - G))
+// (Q carries the output scale).  Reverse mode, with dO and dS' given:
+//     dU  = Aqk^T dO + Kd dS'^T            dS  = dS' Diag(gn) + dO^T Qg - dU^T W
+//     dQg = dO S      dKd = U dS'          dgn = colsum(dS' . S)
+//     dAqk = dO U^T (lower)                dW  = -dU S
+//     dM  = dU V^T + dW Kg^T               dV  = M^T dU      dKg = M^T dW
+//     dT  = dM diag(b), db += colsum(dM . T),  dAkk = -(T^T dT T^T) (strictly lower)
+// and the pairwise terms of Akk and Aqk into dK, dQ and dG, then dG to the
+// per-token decay by a reverse cumulative sum, through the gate activation,
+// the L2 norms and the beta sigmoid to the raw inputs.
+//
+// Five launches (plus the chunk map for packed input), all fp32:
+//   kda_bwd_prep_kernel    per (chunk, v-head): norms, G, Akk and Aqk from
+//                          pairwise factors e^(G_i - G_j) (i >= j, so every
+//                          exponent is <= 0), T by blocked substitution, W,
+//                          Ubar, Kd, Qg, Kg, gn -> workspace.
+//   kda_bwd_fstate_kernel  per (sequence, v-head, 32-row V slice), forward
+//                          over chunks: stores each chunk's entry state S and U.
+//   kda_bwd_bstate_kernel  per (sequence, v-head, V slice), backward over
+//                          chunks: stores dS' and dU, writes dS of the initial state.
+//   kda_bwd_dense_kernel   per (chunk, v-head): the dense products above.
+//   kda_bwd_pair_kernel    per (chunk, v-head): the pairwise terms, the
+//                          elementwise factors, the decay cumulative sum, gate,
+//                          norm and beta derivatives -> dq, dk, dv, dg, dbeta
+//                          and per-chunk partials of dA_log and ddt_bias.
+//   kda_bwd_reduce_kernel  sums q/k gradients over grouped v-heads and the
+//                          per-chunk gate-parameter partials.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+using namespace kda_internal;
+
+constexpr int CH = 64;
+constexpr int DK = 128;
+constexpr int DV = 128;
+constexpr int RS = 132;  // LDS row stride of 128-wide fp32 tiles (rows 4 banks apart)
+constexpr int QS = 68;   // LDS row stride of 64-wide fp32 tiles
+constexpr int BV = 32;   // V rows per state workgroup
+constexpr int BNS = DV / BV;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kL2Eps = 1e-6f;
+constexpr float kMinLog2Decay = -1.0e4f;
+
+// Workspace, per (v-head, chunk) "chunk-head", all fp32 row-major:
+// prep block (written by prep)
+constexpr int PB_T = 0;                // T = (I + Akk)^-1       [64][64]
+constexpr int PB_AQK = PB_T + 4096;    // Aqk (lower)            [64][64]
+constexpr int PB_W = PB_AQK + 4096;    // W = M Kg               [64][128]
+constexpr int PB_UB = PB_W + 8192;     // Ubar = M V             [64][128]
+constexpr int PB_KD = PB_UB + 8192;    // Kd = K . e^(G_last-G)  [64][128]
+constexpr int PB_QG = PB_KD + 8192;    // Qg = Q . e^G           [64][128]
+constexpr int PB_KG = PB_QG + 8192;    // Kg = K . e^G           [64][128]
+constexpr int PB_GN = PB_KG + 8192;    // gn = e^G_last          [128]
+constexpr int PB_FLOATS = PB_GN + 128;
+// state block (written by the two state passes)
+constexpr int SB_H = 0;                // S entering the chunk   [128 v][128 k]
+constexpr int SB_DH = SB_H + 16384;    // dS' after the chunk    [128][128]
+constexpr int SB_U = SB_DH + 16384;    // U                      [64 t][128 v]
+constexpr int SB_DU = SB_U + 8192;     // dU                     [64][128]
+constexpr int SB_FLOATS = SB_DU + 8192;
+// gradient block (written by dense, read by pair)
+constexpr int GB_DQG = 0;              // dQg                    [64][128]
+constexpr int GB_DKG = GB_DQG + 8192;  // dKg
+constexpr int GB_DKD = GB_DKG + 8192;  // dKd
+constexpr int GB_DAQK = GB_DKD + 8192; // dAqk (lower)           [64][64]
+constexpr int GB_DAKK = GB_DAQK + 4096;// dAkk (strictly lower)  [64][64]
+constexpr int GB_DGN = GB_DAKK + 4096; // dgn                    [128]
+constexpr int GB_DB = GB_DGN + 128;    // db from dM . T         [64]
+constexpr int GB_FLOATS = GB_DB + 64;
+constexpr int GP_FLOATS = 192;         // gate partials per chunk-head: ddt_bias [128], dA_log [1], pad
+constexpr size_t CHUNK_HEAD_FLOATS = (size_t)PB_FLOATS + SB_FLOATS + GB_FLOATS + GP_FLOATS;
+static_assert(CHUNK_HEAD_FLOATS % 64 == 0, "chunk-head block alignment");
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float softplus(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
+
+// Gate activation a (natural log) and its derivatives d a / d x and
+// d a / d A_log, for x = g + dt_bias.
+template <int MODE>
+__device__ __forceinline__ void gate_fwd_bwd(float x, float A_exp, float lb, float& a, float& dadx, float& dadA) {
+  if constexpr (MODE == KDA_GATE_SOFTPLUS) {
+    a = -A_exp * softplus(x);
+    dadx = -A_exp * sigm(x);
+    dadA = a;
+  } else if constexpr (MODE == KDA_GATE_SAFE_SIGMOID) {
+    const float z = A_exp * x, s = sigm(z);
+    a = lb * s;
+    dadx = lb * s * (1.0f - s) * A_exp;
+    dadA = lb * s * (1.0f - s) * z;
+  } else {
+    a = x;
+    dadx = 1.0f;
+    dadA = 0.0f;
+  }
+}
+
+struct ChunkLoc {
+  int n;        // sequence
+  int64_t row0; // first token row (b*T + t, or packed offset)
+  int len;      // valid tokens (0 if the chunk index is past the last chunk)
+};
+
+// Global chunk x -> (sequence, first row, length).  Packed input: chunk_off
+// holds each sequence's first global chunk (binary search).
+__device__ __forceinline__ ChunkLoc chunk_loc(int x, const int64_t* cu, const int* chunk_off, int T, int N) {
+  ChunkLoc L;
+  if (cu == nullptr) {
+    const int ncs = (T + CH - 1) / CH;
+    L.n = ncs > 0 ? x / ncs : 0;
+    const int c = ncs > 0 ? x % ncs : 0;
+    L.row0 = (int64_t)L.n * T + (int64_t)c * CH;
+    L.len = (L.n < N && ncs > 0) ? min(CH, T - c * CH) : 0;
+  } else {
+    if (x >= chunk_off[N]) { L.n = 0; L.row0 = 0; L.len = 0; return L; }
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (chunk_off[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    L.n = lo;
+    const int c = x - chunk_off[lo];
+    L.row0 = cu[lo] + (int64_t)c * CH;
+    L.len = (int)min((int64_t)CH, cu[lo + 1] - L.row0);
+  }
+  return L;
+}
+
+// acc[4][8] += A(r0 + i, k) B(k, c0 + j) over k < K4*4, A and B fp32 in LDS.
+//   A(r, k) = AT ? sA[k * lda + r] : sA[r * lda + k]
+//   B(k, c) = BT ? sB[c * ldb + k] : sB[k * ldb + c]
+template <bool AT, bool BT, int NC>
+__device__ __forceinline__ void mm_tile(float (&acc)[4][NC], const float* sA, int lda, const float* sB, int ldb,
+                                        int r0, int c0, int kdim) {
+  for (int k = 0; k < kdim; k += 4) {
+    float a[4][4];  // a[i][kk]
+    if constexpr (AT) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const float4 x = *reinterpret_cast<const float4*>(sA + (k + kk) * lda + r0);
+        a[0][kk] = x.x; a[1][kk] = x.y; a[2][kk] = x.z; a[3][kk] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 x = *reinterpret_cast<const float4*>(sA + (r0 + i) * lda + k);
+        a[i][0] = x.x; a[i][1] = x.y; a[i][2] = x.z; a[i][3] = x.w;
+      }
+    }
+    float b[4][NC];  // b[kk][j]
+    if constexpr (BT) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const float4 x = *reinterpret_cast<const float4*>(sB + (c0 + j) * ldb + k);
+        b[0][j] = x.x; b[1][j] = x.y; b[2][j] = x.z; b[3][j] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int j = 0; j < NC; j += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(sB + (k + kk) * ldb + c0 + j);
+          b[kk][j] = x.x; b[kk][j + 1] = x.y; b[kk][j + 2] = x.z; b[kk][j + 3] = x.w;
+        }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NC; ++j) acc[i][j] += a[i][kk] * b[kk][j];
+  }
+}
+
+template <int NC>
+__device__ __forceinline__ void zero_tile(float (&acc)[4][NC]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NC; ++j) acc[i][j] = 0.0f;
+}
+
+// 64 x 128 fp32 global tile (row stride gs floats) -> LDS rows of stride RS.
+__device__ __forceinline__ void load_tile128(float* s, const float* g, int gs, int tid) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = tid + 256 * i, r = e >> 5, c = 4 * (e & 31);
+    *reinterpret_cast<float4*>(s + r * RS + c) = *reinterpret_cast<const float4*>(g + (size_t)r * gs + c);
+  }
+}
+// 64 x 64 fp32 global tile (dense, stride 64) -> LDS rows of stride QS.
+__device__ __forceinline__ void load_tile64(float* s, const float* g, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i, r = e >> 4, c = 4 * (e & 15);
+    *reinterpret_cast<float4*>(s + r * QS + c) = *reinterpret_cast<const float4*>(g + r * 64 + c);
+  }
+}
+// 64 rows x 128 bf16 (row stride gs elements; rows >= len read as zero) -> fp32 LDS.
+__device__ __forceinline__ void load_bf16_tile128(float* s, const uint16_t* g, size_t gs, int len, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i, r = e >> 4, c = 8 * (e & 15);
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (r < len) u = *reinterpret_cast<const uint4*>(g + (size_t)r * gs + c);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float* d = s + r * RS + c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      d[2 * q] = __uint_as_float(w[q] << 16);
+      d[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+  }
+}
+
+// Per chunk: q, k normalised (the output scale is applied by the callers),
+// beta, and G = cumulative
+// log2-decay of the chunk (rows past the sequence end: zero inputs, beta 0,
+// zero decay).  Thread t: row t >> 2, channels 32 (t & 3) .. +31.
+template <int MODE>
+__device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* sG, float* sB, const uint16_t* q,
+                                                  const uint16_t* k, const uint16_t* g, const uint16_t* beta,
+                                                  const float* A_log, const float* dt_bias, int Hqk, int Hv, int h,
+                                                  int hq, int64_t row0, int len, float scale, float lb, int flags,
+                                                  int tid, float* rq_out, float* rk_out) {
+  const int r = tid >> 2, c0 = 32 * (tid & 3);
+  const bool ok = r < len;
+  const size_t row = (size_t)(row0 + r);
+  float qv[32], kv[32], gv[32];
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) {
+    uint4 uq = make_uint4(0, 0, 0, 0), uk = uq, ug = uq;
+    if (ok) {
+      uq = *reinterpret_cast<const uint4*>(q + (row * Hqk + hq) * DK + c0 + i);
+      uk = *reinterpret_cast<const uint4*>(k + (row * Hqk + hq) * DK + c0 + i);
+      ug = *reinterpret_cast<const uint4*>(g + (row * Hv + h) * DK + c0 + i);
+    }
+    const uint32_t wq[4] = {uq.x, uq.y, uq.z, uq.w}, wk[4] = {uk.x, uk.y, uk.z, uk.w}, wg[4] = {ug.x, ug.y, ug.z, ug.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qv[i + 2 * j] = __uint_as_float(wq[j] << 16); qv[i + 2 * j + 1] = __uint_as_float(wq[j] & 0xffff0000u);
+      kv[i + 2 * j] = __uint_as_float(wk[j] << 16); kv[i + 2 * j + 1] = __uint_as_float(wk[j] & 0xffff0000u);
+      gv[i + 2 * j] = __uint_as_float(wg[j] << 16); gv[i + 2 * j + 1] = __uint_as_float(wg[j] & 0xffff0000u);
+    }
+  }
+  float sq = 0.0f, sk = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) { sq += qv[i] * qv[i]; sk += kv[i] * kv[i]; }
+  sq += __shfl_xor(sq, 1); sq += __shfl_xor(sq, 2);
+  sk += __shfl_xor(sk, 1); sk += __shfl_xor(sk, 2);
+  const bool norm = flags & KDA_FLAG_QK_L2NORM;
+  const float rq = norm ? rsqrtf(sq + kL2Eps) : 1.0f, rk = norm ? rsqrtf(sk + kL2Eps) : 1.0f;
+  if (rq_out) { rq_out[0] = rq; rk_out[0] = rk; }
+  const float A_exp = (MODE == KDA_GATE_PREGATED || A_log == nullptr) ? 1.0f : __expf(A_log[h]);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int c = c0 + i;
+    sQ[r * RS + c] = qv[i] * rq;
+    sK[r * RS + c] = kv[i] * rk;
+    float a = 0.0f, d1, d2;
+    if (ok) gate_fwd_bwd<MODE>(gv[i] + (dt_bias ? dt_bias[(size_t)h * DK + c] : 0.0f), A_exp, lb, a, d1, d2);
+    sG[r * RS + c] = fmaxf(a * kLog2e, kMinLog2Decay);
+  }
+  if ((tid & 3) == 0) {
+    float b = 0.0f;
+    if (ok) {
+      const float braw = bf2f(beta[row * Hv + h]);
+      b = (flags & KDA_FLAG_BETA_IS_PROB) ? braw : sigm(braw);
+    }
+    sB[r] = b;
+  }
+  __syncthreads();
+  // inclusive cumulative sum over the 64 rows of each channel: thread t owns
+  // channel t & 127 and rows 32 (t >> 7) .. +31, then the second half adds
+  // the first half's total
+  {
+    const int c = tid & 127, half = tid >> 7;
+    float run = 0.0f;
+    for (int rr = 32 * half; rr < 32 * half + 32; ++rr) { run += sG[rr * RS + c]; sG[rr * RS + c] = run; }
+    __syncthreads();
+    if (half == 1) {
+      const float base = sG[31 * RS + c];
+      for (int rr = 32; rr < 64; ++rr) sG[rr * RS + c] += base;
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// prep: per (chunk, v-head) forward quantities in fp32
+template <int MODE>
+__global__ void __launch_bounds__(256)
+kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                    const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta, const float* __restrict__ A_log,
+                    const float* __restrict__ dt_bias, const int64_t* __restrict__ cu, const int* __restrict__ chunk_off,
+                    int T, int N, int Hqk, int Hv, int mc, float scale, float lb, int flags, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) float sK[CH * RS];
+  __shared__ __attribute__((aligned(16))) float sQ[CH * RS];
+  __shared__ __attribute__((aligned(16))) float sG[CH * RS];
+  __shared__ __attribute__((aligned(16))) float sA[CH * QS];
+  __shared__ __attribute__((aligned(16))) float sAq[CH * QS];
+  __shared__ __attribute__((aligned(16))) float sT[CH * QS];
+  __shared__ float sB[CH];
+  __shared__ float sX[16 * 17];
+  const int x = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const ChunkLoc L = chunk_loc(x, cu, chunk_off, T, N);
+  if (L.len == 0) return;
+  const int hq = h / (Hv / Hqk);
+  float* pb = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS;
+
+  for (int e = tid; e < CH * QS; e += 256) { sA[e] = 0.0f; sAq[e] = 0.0f; sT[e] = 0.0f; }
+  load_chunk_inputs<MODE>(sK, sQ, sG, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, scale, lb,
+                          flags, tid, nullptr, nullptr);
+
+  // Akk and Aqk: 4 x 4 pair blocks (I >= J) of the 64 x 64 lower triangle,
+  // each split over two adjacent threads by channel half.
+  for (int item = tid; item < 272; item += 256) {
+    const int b = item >> 1, half = item & 1;
+    int I = (int)((sqrtf(8.0f * b + 1.0f) - 1.0f) * 0.5f);
+    while ((I + 1) * (I + 2) / 2 <= b) ++I;
+    while (I * (I + 1) / 2 > b) --I;
+    const int J = b - I * (I + 1) / 2, i0 = 4 * I, j0 = 4 * J;
+    float akk[4][4], aqk[4][4];
+    zero_tile(akk);
+    zero_tile(aqk);
+    for (int c = 64 * half; c < 64 * half + 64; c += 4) {
+      float Ki[4][4], Qi[4][4], Gi[4][4], Kj[4][4], Gj[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4 a0 = *reinterpret_cast<const float4*>(sK + (i0 + r) * RS + c);
+        const float4 a1 = *reinterpret_cast<const float4*>(sQ + (i0 + r) * RS + c);
+        const float4 a2 = *reinterpret_cast<const float4*>(sG + (i0 + r) * RS + c);
+        const float4 b0 = *reinterpret_cast<const float4*>(sK + (j0 + r) * RS + c);
+        const float4 b1 = *reinterpret_cast<const float4*>(sG + (j0 + r) * RS + c);
+        Ki[r][0] = a0.x; Ki[r][1] = a0.y; Ki[r][2] = a0.z; Ki[r][3] = a0.w;
+        Qi[r][0] = a1.x; Qi[r][1] = a1.y; Qi[r][2] = a1.z; Qi[r][3] = a1.w;
+        Gi[r][0] = a2.x; Gi[r][1] = a2.y; Gi[r][2] = a2.z; Gi[r][3] = a2.w;
+        Kj[r][0] = b0.x; Kj[r][1] = b0.y; Kj[r][2] = b0.z; Kj[r][3] = b0.w;
+        Gj[r][0] = b1.x; Gj[r][1] = b1.y; Gj[r][2] = b1.z; Gj[r][3] = b1.w;
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            // i >= j gives an exponent <= 0; the upper half of a diagonal
+            // block is masked below, so its exponent is only kept finite
+            const float e = ex2(fminf(Gi[ii][cc] - Gj[jj][cc], 0.0f)) * Kj[jj][cc];
+            akk[ii][jj] += Ki[ii][cc] * e;
+            aqk[ii][jj] += Qi[ii][cc] * e;
+          }
+    }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        akk[ii][jj] += __shfl_xor(akk[ii][jj], 1);
+        aqk[ii][jj] += __shfl_xor(aqk[ii][jj], 1);
+      }
+    if (half == 0) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int i = i0 + ii, j = j0 + jj;
+          sA[i * QS + j] = j < i ? sB[i] * akk[ii][jj] : 0.0f;
+          sAq[i * QS + j] = j <= i ? scale * aqk[ii][jj] : 0.0f;
+        }
+    }
+  }
+  __syncthreads();
+
+  // T = (I + Akk)^-1: the four 16 x 16 diagonal blocks by forward
+  // substitution (one wave each, lane = column), then block rows 1..3
+  {
+    const int w = tid >> 6, lane = tid & 63;
+    if (lane < 16) {
+      const int base = 16 * w, cc = lane;
+      for (int i = 0; i < 16; ++i) {
+        float acc = i == cc ? 1.0f : 0.0f;
+        for (int j = cc; j < i; ++j) acc -= sA[(base + i) * QS + base + j] * sT[(base + j) * QS + base + cc];
+        sT[(base + i) * QS + base + cc] = i >= cc ? acc : 0.0f;
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int r = tid >> 4, c = tid & 15;
+    for (int I = 1; I < 4; ++I)
+      for (int J = 0; J < I; ++J) {
+        // X = sum_{K=J}^{I-1} A_IK T_KJ;  T_IJ = -T_II X
+        float xacc = 0.0f;
+        for (int kk = 16 * J; kk < 16 * I; ++kk) xacc += sA[(16 * I + r) * QS + kk] * sT[kk * QS + 16 * J + c];
+        sX[r * 17 + c] = xacc;
+        __syncthreads();
+        float t = 0.0f;
+        for (int m = 0; m < 16; ++m) t += sT[(16 * I + r) * QS + 16 * I + m] * sX[m * 17 + c];
+        sT[(16 * I + r) * QS + 16 * J + c] = -t;
+        __syncthreads();
+      }
+  }
+
+  // store T and Aqk
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i, r = e >> 4, c = 4 * (e & 15);
+    *reinterpret_cast<float4*>(pb + PB_T + r * 64 + c) = *reinterpret_cast<const float4*>(sT + r * QS + c);
+    *reinterpret_cast<float4*>(pb + PB_AQK + r * 64 + c) = *reinterpret_cast<const float4*>(sAq + r * QS + c);
+  }
+  // Kd, Qg, Kg, gn (own elements: row tid >> 2, channels 32 (tid & 3) ..)
+  {
+    const int r = tid >> 2, c0 = 32 * (tid & 3);
+    for (int i = 0; i < 32; i += 4) {
+      const int c = c0 + i;
+      const float4 kk = *reinterpret_cast<const float4*>(sK + r * RS + c);
+      const float4 qq = *reinterpret_cast<const float4*>(sQ + r * RS + c);
+      const float4 gg = *reinterpret_cast<const float4*>(sG + r * RS + c);
+      const float4 gl = *reinterpret_cast<const float4*>(sG + 63 * RS + c);
+      const float4 eg = make_float4(ex2(gg.x), ex2(gg.y), ex2(gg.z), ex2(gg.w));
+      const float4 kd = make_float4(kk.x * ex2(gl.x - gg.x), kk.y * ex2(gl.y - gg.y), kk.z * ex2(gl.z - gg.z),
+                                    kk.w * ex2(gl.w - gg.w));
+      const float4 kg = make_float4(kk.x * eg.x, kk.y * eg.y, kk.z * eg.z, kk.w * eg.w);
+      *reinterpret_cast<float4*>(pb + PB_KD + r * DK + c) = kd;
+      *reinterpret_cast<float4*>(pb + PB_QG + r * DK + c) =
+          make_float4(scale * qq.x * eg.x, scale * qq.y * eg.y, scale * qq.z * eg.z, scale * qq.w * eg.w);
+      *reinterpret_cast<float4*>(pb + PB_KG + r * DK + c) = kg;
+      *reinterpret_cast<float4*>(sK + r * RS + c) = kg;  // sK now holds Kg
+      if (r == 0) *reinterpret_cast<float4*>(pb + PB_GN + c) = make_float4(ex2(gl.x), ex2(gl.y), ex2(gl.z), ex2(gl.w));
+    }
+  }
+  __syncthreads();
+  // sQ <- V; sT <- M = T diag(b)
+  load_bf16_tile128(sQ, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
+  for (int e = tid; e < CH * CH; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    sT[r * QS + c] *= sB[c];
+  }
+  __syncthreads();
+  // W = M Kg, Ubar = M V (4 x 8 tiles)
+  {
+    const int r0 = 4 * (tid >> 4), c0 = 8 * (tid & 15);
+    float w[4][8], u[4][8];
+    zero_tile(w);
+    zero_tile(u);
+    mm_tile<false, false, 8>(w, sT, QS, sK, RS, r0, c0, CH);
+    mm_tile<false, false, 8>(u, sT, QS, sQ, RS, r0, c0, CH);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; j += 4) {
+        *reinterpret_cast<float4*>(pb + PB_W + (r0 + i) * DK + c0 + j) =
+            make_float4(w[i][j], w[i][j + 1], w[i][j + 2], w[i][j + 3]);
+        *reinterpret_cast<float4*>(pb + PB_UB + (r0 + i) * DV + c0 + j) =
+            make_float4(u[i][j], u[i][j + 1], u[i][j + 2], u[i][j + 3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// state passes: one workgroup per (sequence, v-head, 32-row V slice); thread
+// t owns row v0 + (t >> 3), key columns 4 (t & 7) + 32 m + i (m, i < 4)
+constexpr int SV = 36;  // LDS row stride of 32-wide slices
+
+__device__ __forceinline__ void chain_chunks(int n, const int* chunk_off, const int64_t* cu, int T, int& x0, int& nc,
+                                             int64_t& bos) {
+  if (cu == nullptr) {
+    const int ncs = (T + CH - 1) / CH;
+    x0 = n * ncs; nc = ncs; bos = (int64_t)n * T;
+  } else {
+    x0 = chunk_off[n]; nc = chunk_off[n + 1] - x0; bos = cu[n];
+  }
+}
+
+// 32 x 128 slice of a [128][128] fp32 matrix (rows v0..) <-> per-thread registers
+__device__ __forceinline__ void slice_store(const float (&S)[16], float* g, int v0, int tid) {
+  const int row = tid >> 3, kc = 4 * (tid & 7);
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    *reinterpret_cast<float4*>(g + (size_t)(v0 + row) * DK + kc + 32 * m) =
+        make_float4(S[4 * m], S[4 * m + 1], S[4 * m + 2], S[4 * m + 3]);
+}
+
+__global__ void __launch_bounds__(256)
+kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ chunk_off, const void* __restrict__ h0,
+                      int init_dtype, int T, int N, int Hv, int mc, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) float sW[CH * RS];
+  __shared__ __attribute__((aligned(16))) float sKd[CH * RS];
+  __shared__ __attribute__((aligned(16))) float sUb[CH * SV];
+  __shared__ __attribute__((aligned(16))) float sU[CH * SV];
+  __shared__ __attribute__((aligned(16))) float sS[BV * RS];
+  __shared__ __attribute__((aligned(16))) float sGn[DK];
+  const int chain = blockIdx.x / BNS, slice = blockIdx.x % BNS;
+  if (chain >= N * Hv) return;
+  const int n = chain / Hv, h = chain % Hv, v0 = BV * slice, tid = threadIdx.x;
+  const int row = tid >> 3, kc = 4 * (tid & 7);
+  int x0, nc;
+  int64_t bos;
+  chain_chunks(n, chunk_off, cu, T, x0, nc, bos);
+  float S[16];
+  const size_t sbase = (((size_t)n * Hv + h) * DV + v0 + row) * DK + kc;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (init_dtype == KDA_STATE_F32) {
+      x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(h0) + sbase + 32 * m);
+    } else if (init_dtype == KDA_STATE_BF16) {
+      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(h0) + sbase + 32 * m);
+      x = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                      __uint_as_float(u.y & 0xffff0000u));
+    }
+    S[4 * m] = x.x; S[4 * m + 1] = x.y; S[4 * m + 2] = x.z; S[4 * m + 3] = x.w;
+  }
+  for (int c = 0; c < nc; ++c) {
+    const float* pb = ws + ((size_t)h * mc + x0 + c) * CHUNK_HEAD_FLOATS;
+    float* sb = const_cast<float*>(pb) + PB_FLOATS;
+    slice_store(S, sb + SB_H, v0, tid);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<float4*>(sS + row * RS + kc + 32 * m) =
+          make_float4(S[4 * m], S[4 * m + 1], S[4 * m + 2], S[4 * m + 3]);
+    load_tile128(sW, pb + PB_W, DK, tid);
+    load_tile128(sKd, pb + PB_KD, DK, tid);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + 256 * i, t = e >> 3, j = 4 * (e & 7);
+      *reinterpret_cast<float4*>(sUb + t * SV + j) = *reinterpret_cast<const float4*>(pb + PB_UB + t * DV + v0 + j);
+    }
+    if (tid < 32) *reinterpret_cast<float4*>(sGn + 4 * tid) = *reinterpret_cast<const float4*>(pb + PB_GN + 4 * tid);
+    __syncthreads();
+    // U[t][v] = Ubar[t][v] - sum_k W[t][k] S[v][k]   (thread: t = tid >> 2, v = 8 (tid & 3) + j)
+    {
+      const int t = tid >> 2, vq = 8 * (tid & 3);
+      float acc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+      for (int k = 0; k < DK; k += 4) {
+        const float4 w = *reinterpret_cast<const float4*>(sW + t * RS + k);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float4 sv = *reinterpret_cast<const float4*>(sS + (vq + j) * RS + k);
+          acc[j] += w.x * sv.x + w.y * sv.y + w.z * sv.z + w.w * sv.w;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = sUb[t * SV + vq + j] - acc[j];
+#pragma unroll
+      for (int j = 0; j < 8; j += 4) {
+        const float4 u4 = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+        *reinterpret_cast<float4*>(sU + t * SV + vq + j) = u4;
+        *reinterpret_cast<float4*>(sb + SB_U + t * DV + v0 + vq + j) = u4;
+      }
+    }
+    __syncthreads();
+    // S[v][k] <- S[v][k] gn[k] + sum_t U[t][v] Kd[t][k]
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[4 * m + i] *= sGn[kc + 32 * m + i];
+    for (int t = 0; t < CH; ++t) {
+      const float u = sU[t * SV + row];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float4 kd = *reinterpret_cast<const float4*>(sKd + t * RS + kc + 32 * m);
+        S[4 * m] += u * kd.x; S[4 * m + 1] += u * kd.y; S[4 * m + 2] += u * kd.z; S[4 * m + 3] += u * kd.w;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(256)
+kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restrict__ dhT, float* __restrict__ dh0,
+                      const int64_t* __restrict__ cu, const int* __restrict__ chunk_off, int T, int N, int Hv, int mc,
+                      float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) float sAq[CH * QS];
+  __shared__ __attribute__((aligned(16))) float sKd[CH * RS];
+  __shared__ __attribute__((aligned(16))) float sQg[CH * RS];
+  __shared__ __attribute__((aligned(16))) float sW[CH * RS];
+  __shared__ __attribute__((aligned(16))) float sdO[CH * SV];
+  __shared__ __attribute__((aligned(16))) float sdU[CH * SV];
+  __shared__ __attribute__((aligned(16))) float sdh[BV * RS];
+  __shared__ __attribute__((aligned(16))) float sGn[DK];
+  const int chain = blockIdx.x / BNS, slice = blockIdx.x % BNS;
+  if (chain >= N * Hv) return;
+  const int n = chain / Hv, h = chain % Hv, v0 = BV * slice, tid = threadIdx.x;
+  const int row = tid >> 3, kc = 4 * (tid & 7);
+  int x0, nc;
+  int64_t bos;
+  chain_chunks(n, chunk_off, cu, T, x0, nc, bos);
+  const int64_t seqlen = cu == nullptr ? (int64_t)T : cu[n + 1] - cu[n];
+  float D[16];
+  const size_t sbase = (((size_t)n * Hv + h) * DV + v0 + row) * DK + kc;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (dhT) x = *reinterpret_cast<const float4*>(dhT + sbase + 32 * m);
+    D[4 * m] = x.x; D[4 * m + 1] = x.y; D[4 * m + 2] = x.z; D[4 * m + 3] = x.w;
+  }
+  for (int c = nc - 1; c >= 0; --c) {
+    const float* pb = ws + ((size_t)h * mc + x0 + c) * CHUNK_HEAD_FLOATS;
+    float* sb = const_cast<float*>(pb) + PB_FLOATS;
+    const int64_t row0 = bos + (int64_t)c * CH;
+    const int len = (int)min((int64_t)CH, seqlen - (int64_t)c * CH);
+    slice_store(D, sb + SB_DH, v0, tid);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<float4*>(sdh + row * RS + kc + 32 * m) =
+          make_float4(D[4 * m], D[4 * m + 1], D[4 * m + 2], D[4 * m + 3]);
+    load_tile64(sAq, pb + PB_AQK, tid);
+    load_tile128(sKd, pb + PB_KD, DK, tid);
+    load_tile128(sQg, pb + PB_QG, DK, tid);
+    load_tile128(sW, pb + PB_W, DK, tid);
+    {
+      // dO slice: token t = tid >> 2, columns 8 (tid & 3) .. +7 (bf16)
+      const int t = tid >> 2, j = 8 * (tid & 3);
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (t < len) u = *reinterpret_cast<const uint4*>(d_out + ((size_t)(row0 + t) * Hv + h) * DV + v0 + j);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sdO[t * SV + j + 2 * q] = __uint_as_float(w[q] << 16);
+        sdO[t * SV + j + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+      }
+    }
+    if (tid < 32) *reinterpret_cast<float4*>(sGn + 4 * tid) = *reinterpret_cast<const float4*>(pb + PB_GN + 4 * tid);
+    __syncthreads();
+    // dU[t][v] = sum_s Aqk[s][t] dO[s][v] + sum_k Kd[t][k] dS'[v][k]
+    {
+      const int t = tid >> 2, vq = 8 * (tid & 3);
+      float acc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+      for (int s2 = 0; s2 < CH; ++s2) {
+        const float a = sAq[s2 * QS + t];
+        const float4 o0 = *reinterpret_cast<const float4*>(sdO + s2 * SV + vq);
+        const float4 o1 = *reinterpret_cast<const float4*>(sdO + s2 * SV + vq + 4);
+        acc[0] += a * o0.x; acc[1] += a * o0.y; acc[2] += a * o0.z; acc[3] += a * o0.w;
+        acc[4] += a * o1.x; acc[5] += a * o1.y; acc[6] += a * o1.z; acc[7] += a * o1.w;
+      }
+      for (int k = 0; k < DK; k += 4) {
+        const float4 kd = *reinterpret_cast<const float4*>(sKd + t * RS + k);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float4 d = *reinterpret_cast<const float4*>(sdh + (vq + j) * RS + k);
+          acc[j] += kd.x * d.x + kd.y * d.y + kd.z * d.z + kd.w * d.w;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j += 4) {
+        const float4 u4 = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+        *reinterpret_cast<float4*>(sdU + t * SV + vq + j) = u4;
+        *reinterpret_cast<float4*>(sb + SB_DU + t * DV + v0 + vq + j) = u4;
+      }
+    }
+    __syncthreads();
+    // dS[v][k] = dS'[v][k] gn[k] + sum_t dO[t][v] Qg[t][k] - sum_t dU[t][v] W[t][k]
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) D[4 * m + i] *= sGn[kc + 32 * m + i];
+    for (int t = 0; t < CH; ++t) {
+      const float o = sdO[t * SV + row], du = sdU[t * SV + row];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float4 qg = *reinterpret_cast<const float4*>(sQg + t * RS + kc + 32 * m);
+        const float4 w = *reinterpret_cast<const float4*>(sW + t * RS + kc + 32 * m);
+        D[4 * m] += o * qg.x - du * w.x;
+        D[4 * m + 1] += o * qg.y - du * w.y;
+        D[4 * m + 2] += o * qg.z - du * w.z;
+        D[4 * m + 3] += o * qg.w - du * w.w;
+      }
+    }
+    __syncthreads();
+  }
+  if (dh0) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      *reinterpret_cast<float4*>(dh0 + sbase + 32 * m) = make_float4(D[4 * m], D[4 * m + 1], D[4 * m + 2], D[4 * m + 3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dense products per (chunk, v-head).  4 x 8 tiles of 64 x 128 results:
+// rows 4 (tid >> 4) .., columns 8 (tid & 15) ..; 4 x 4 tiles of 64 x 64
+// results: rows 4 (tid >> 4) .., columns 4 (tid & 15) ..
+__device__ __forceinline__ void store_tile8(float* g, int gs, const float (&a)[4][8], int r0, int c0, float sc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; j += 4)
+      *reinterpret_cast<float4*>(g + (size_t)(r0 + i) * gs + c0 + j) =
+          make_float4(sc * a[i][j], sc * a[i][j + 1], sc * a[i][j + 2], sc * a[i][j + 3]);
+}
+
+__global__ void __launch_bounds__(256)
+kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_out,
+                     const uint16_t* __restrict__ beta, const int64_t* __restrict__ cu,
+                     const int* __restrict__ chunk_off, int T, int N, int Hv, int mc, int flags,
+                     float* __restrict__ dv, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) float B0[CH * RS];
+  __shared__ __attribute__((aligned(16))) float B1[CH * RS];
+  __shared__ __attribute__((aligned(16))) float B2[CH * RS];
+  __shared__ __attribute__((aligned(16))) float B3[CH * RS];
+  __shared__ __attribute__((aligned(16))) float sT[CH * QS];
+  __shared__ float sB[CH];
+  __shared__ float sRed[2 * DK];
+  const int x = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const ChunkLoc L = chunk_loc(x, cu, chunk_off, T, N);
+  if (L.len == 0) return;
+  float* pb = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS;
+  float* sb = pb + PB_FLOATS;
+  float* gb = sb + SB_FLOATS;
+  const int r0 = 4 * (tid >> 4), c0 = 8 * (tid & 15), q0 = 4 * (tid & 15);
+
+  // 1. dO, dU, U and the first half of S (rows v < 64)
+  load_bf16_tile128(B0, d_out + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
+  load_tile128(B1, sb + SB_DU, DV, tid);
+  load_tile128(B2, sb + SB_U, DV, tid);
+  load_tile128(B3, sb + SB_H, DK, tid);
+  __syncthreads();
+  // 2. dQg = dO S and dW = -dU S, contracting over v in two halves
+  float dqg[4][8], dw[4][8];
+  zero_tile(dqg);
+  zero_tile(dw);
+  mm_tile<false, false, 8>(dqg, B0, RS, B3, RS, r0, c0, 64);
+  mm_tile<false, false, 8>(dw, B1, RS, B3, RS, r0, c0, 64);
+  __syncthreads();
+  load_tile128(B3, sb + SB_H + 64 * DK, DK, tid);
+  __syncthreads();
+  mm_tile<false, false, 8>(dqg, B0 + 64, RS, B3, RS, r0, c0, 64);
+  mm_tile<false, false, 8>(dw, B1 + 64, RS, B3, RS, r0, c0, 64);
+  store_tile8(gb + GB_DQG, DK, dqg, r0, c0, 1.0f);
+  // 3. dAqk = dO U^T, lower triangle including the diagonal
+  {
+    float a[4][4];
+    zero_tile(a);
+    mm_tile<false, true, 4>(a, B0, RS, B2, RS, r0, q0, DV);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(gb + GB_DAQK + (r0 + i) * 64 + q0) =
+          make_float4(q0 <= r0 + i ? a[i][0] : 0.0f, q0 + 1 <= r0 + i ? a[i][1] : 0.0f,
+                      q0 + 2 <= r0 + i ? a[i][2] : 0.0f, q0 + 3 <= r0 + i ? a[i][3] : 0.0f);
+  }
+  __syncthreads();
+  // 4. dKd = U dS', contracting over v in two halves; dgn = colsum(dS' . S)
+  {
+    float dkd[4][8];
+    zero_tile(dkd);
+    load_tile128(B3, sb + SB_DH, DK, tid);
+    __syncthreads();
+    mm_tile<false, false, 8>(dkd, B2, RS, B3, RS, r0, c0, 64);
+    __syncthreads();
+    load_tile128(B3, sb + SB_DH + 64 * DK, DK, tid);
+    __syncthreads();
+    mm_tile<false, false, 8>(dkd, B2 + 64, RS, B3, RS, r0, c0, 64);
+    store_tile8(gb + GB_DKD, DK, dkd, r0, c0, 1.0f);
+    const int c = tid & 127, half = tid >> 7;
+    float acc = 0.0f;
+    for (int vv = 64 * half; vv < 64 * half + 64; ++vv) acc += sb[SB_DH + vv * DK + c] * sb[SB_H + vv * DK + c];
+    sRed[half * DK + c] = acc;
+  }
+  __syncthreads();
+  if (tid < DK) gb[GB_DGN + tid] = sRed[tid] + sRed[DK + tid];
+  // 5. B3 <- dW, B0 <- Kg, B2 <- V, sT <- T, sB <- beta
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; j += 4)
+      *reinterpret_cast<float4*>(B3 + (r0 + i) * RS + c0 + j) =
+          make_float4(-dw[i][j], -dw[i][j + 1], -dw[i][j + 2], -dw[i][j + 3]);
+  load_tile128(B0, pb + PB_KG, DK, tid);
+  load_bf16_tile128(B2, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
+  load_tile64(sT, pb + PB_T, tid);
+  if (tid < CH) {
+    float b = 0.0f;
+    if (tid < L.len) {
+      const float braw = bf2f(beta[(size_t)(L.row0 + tid) * Hv + h]);
+      b = (flags & KDA_FLAG_BETA_IS_PROB) ? braw : sigm(braw);
+    }
+    sB[tid] = b;
+  }
+  __syncthreads();
+  // 6. dM = dU V^T + dW Kg^T;  dV = M^T dU;  dKg = M^T dW  (M = T diag(b))
+  float dm[4][4];
+  zero_tile(dm);
+  mm_tile<false, true, 4>(dm, B1, RS, B2, RS, r0, q0, DV);
+  mm_tile<false, true, 4>(dm, B3, RS, B0, RS, r0, q0, DK);
+  {
+    float a[4][8];
+    zero_tile(a);
+    mm_tile<true, false, 8>(a, sT, QS, B1, RS, r0, c0, CH);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = r0 + i;
+      if (t < L.len) {
+        float* d = dv + ((size_t)(L.row0 + t) * Hv + h) * DV + c0;
+        *reinterpret_cast<float4*>(d) = make_float4(sB[t] * a[i][0], sB[t] * a[i][1], sB[t] * a[i][2], sB[t] * a[i][3]);
+        *reinterpret_cast<float4*>(d + 4) =
+            make_float4(sB[t] * a[i][4], sB[t] * a[i][5], sB[t] * a[i][6], sB[t] * a[i][7]);
+      }
+    }
+    zero_tile(a);
+    mm_tile<true, false, 8>(a, sT, QS, B3, RS, r0, c0, CH);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[i][j] *= sB[r0 + i];
+    store_tile8(gb + GB_DKG, DK, a, r0, c0, 1.0f);
+  }
+  __syncthreads();
+  // 7. db_j = sum_i dM[i][j] T[i][j];  dT = dM diag(b);  dAkk = -(T^T dT T^T) strictly lower
+  float* sDM = B0;  // [64][QS]
+  float* sDT = B2;  // [64][QS]
+  float* sX = B3;   // [64][QS]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sDM[(r0 + i) * QS + q0 + j] = dm[i][j];
+      sDT[(r0 + i) * QS + q0 + j] = dm[i][j] * sB[q0 + j];
+    }
+  __syncthreads();
+  if (tid < CH) {
+    float acc = 0.0f;
+    for (int i = 0; i < CH; ++i) acc += sDM[i * QS + tid] * sT[i * QS + tid];
+    gb[GB_DB + tid] = acc;
+  }
+  {
+    float a[4][4];
+    zero_tile(a);
+    mm_tile<true, false, 4>(a, sT, QS, sDT, QS, r0, q0, CH);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sX[(r0 + i) * QS + q0 + j] = a[i][j];
+    __syncthreads();
+    zero_tile(a);
+    mm_tile<false, true, 4>(a, sX, QS, sT, QS, r0, q0, CH);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<float4*>(gb + GB_DAKK + (r0 + i) * 64 + q0) =
+          make_float4(q0 < r0 + i ? -a[i][0] : 0.0f, q0 + 1 < r0 + i ? -a[i][1] : 0.0f,
+                      q0 + 2 < r0 + i ? -a[i][2] : 0.0f, q0 + 3 < r0 + i ? -a[i][3] : 0.0f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pairwise terms, elementwise factors, decay sum, gate, norms and beta.
+// Thread tile: rows 4 (tid >> 4) .. +3, channels 8 (tid & 15) .. +7; the 16
+// threads of a row group are 16 consecutive lanes of one wave.
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(256)
+kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ g,
+                    const uint16_t* __restrict__ beta, const float* __restrict__ A_log,
+                    const float* __restrict__ dt_bias, const int64_t* __restrict__ cu,
+                    const int* __restrict__ chunk_off, int T, int N, int Hqk, int Hv, int mc, float scale, float lb,
+                    int flags, float* __restrict__ dq, float* __restrict__ dk, int qk_heads_out,
+                    float* __restrict__ dg, float* __restrict__ dbeta, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) float sK[CH * RS];
+  __shared__ __attribute__((aligned(16))) float sQ[CH * RS];
+  __shared__ __attribute__((aligned(16))) float sG[CH * RS];
+  __shared__ __attribute__((aligned(16))) float sDA[CH * QS];  // dAkk
+  __shared__ __attribute__((aligned(16))) float sDQ[CH * QS];  // dAqk
+  __shared__ float sB[CH];
+  __shared__ float sRq[CH], sRk[CH];
+  __shared__ float sCol[16 * DK];
+  __shared__ float sRed[8];
+  const int x = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const ChunkLoc L = chunk_loc(x, cu, chunk_off, T, N);
+  float* pb = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS;
+  float* gb = pb + PB_FLOATS + SB_FLOATS;
+  float* gp = gb + GB_FLOATS;
+  if (L.len == 0) {  // past the last chunk: zero gate partials
+    if (tid < GP_FLOATS) gp[tid] = 0.0f;
+    return;
+  }
+  const int hq = h / (Hv / Hqk);
+  float rq, rk;
+  load_chunk_inputs<MODE>(sK, sQ, sG, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, scale, lb,
+                          flags, tid, &rq, &rk);
+  if ((tid & 3) == 0) { sRq[tid >> 2] = rq; sRk[tid >> 2] = rk; }
+  load_tile64(sDA, gb + GB_DAKK, tid);
+  load_tile64(sDQ, gb + GB_DAQK, tid);
+  __syncthreads();
+
+  const int r0 = 4 * (tid >> 4), c0 = 8 * (tid & 15);
+  float Ko[4][8], Qo[4][8], Go[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      Ko[i][j] = sK[(r0 + i) * RS + c0 + j];
+      Qo[i][j] = sQ[(r0 + i) * RS + c0 + j];
+      Go[i][j] = sG[(r0 + i) * RS + c0 + j];
+    }
+  float dK[4][8], dQ[4][8], dG[4][8], dbk[4];
+  zero_tile(dK);
+  zero_tile(dQ);
+  zero_tile(dG);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dbk[i] = 0.0f;
+  const float bo[4] = {sB[r0], sB[r0 + 1], sB[r0 + 2], sB[r0 + 3]};
+
+  // row side: own rows i, partners j <= i
+  for (int j = 0; j < r0 + 4; ++j) {
+    float Kj[8], Gj[8];
+#pragma unroll
+    for (int c = 0; c < 8; c += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(sK + j * RS + c0 + c);
+      const float4 b = *reinterpret_cast<const float4*>(sG + j * RS + c0 + c);
+      Kj[c] = a.x; Kj[c + 1] = a.y; Kj[c + 2] = a.z; Kj[c + 3] = a.w;
+      Gj[c] = b.x; Gj[c + 1] = b.y; Gj[c + 2] = b.z; Gj[c + 3] = b.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float dak = sDA[(r0 + i) * QS + j], daq = sDQ[(r0 + i) * QS + j];  // zero where j > i (or j >= i for Akk)
+      const float a = bo[i] * dak;
+      float sb = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float t1 = Kj[c] * ex2(fminf(Go[i][c] - Gj[c], 0.0f));
+        dK[i][c] += a * t1;
+        dQ[i][c] += daq * t1;
+        dG[i][c] += (a * Ko[i][c] + daq * scale * Qo[i][c]) * t1;
+        sb += Ko[i][c] * t1;
+      }
+      dbk[i] += dak * sb;
+    }
+  }
+  // column side: own rows j, partners i >= j
+  for (int i = r0; i < CH; ++i) {
+    float Ki[8], Qi[8], Gi[8];
+#pragma unroll
+    for (int c = 0; c < 8; c += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(sK + i * RS + c0 + c);
+      const float4 b = *reinterpret_cast<const float4*>(sQ + i * RS + c0 + c);
+      const float4 d = *reinterpret_cast<const float4*>(sG + i * RS + c0 + c);
+      Ki[c] = a.x; Ki[c + 1] = a.y; Ki[c + 2] = a.z; Ki[c + 3] = a.w;
+      Qi[c] = b.x; Qi[c + 1] = b.y; Qi[c + 2] = b.z; Qi[c + 3] = b.w;
+      Gi[c] = d.x; Gi[c + 1] = d.y; Gi[c + 2] = d.z; Gi[c + 3] = d.w;
+    }
+    const float bi = sB[i];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float a = bi * sDA[i * QS + r0 + jj], daq = sDQ[i * QS + r0 + jj];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float t2 = (a * Ki[c] + daq * scale * Qi[c]) * ex2(fminf(Gi[c] - Go[jj][c], 0.0f));
+        dK[jj][c] += t2;
+        dG[jj][c] -= t2 * Ko[jj][c];
+      }
+    }
+  }
+
+  // elementwise factors: Qg = Q e^G, Kg = K e^G, Kd = K e^(G_last - G), gn = e^G_last
+  float colKd[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) colKd[c] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + i;
+#pragma unroll
+    for (int c = 0; c < 8; c += 4) {
+      const float4 dqg = *reinterpret_cast<const float4*>(gb + GB_DQG + r * DK + c0 + c);
+      const float4 dkg = *reinterpret_cast<const float4*>(gb + GB_DKG + r * DK + c0 + c);
+      const float4 dkd = *reinterpret_cast<const float4*>(gb + GB_DKD + r * DK + c0 + c);
+      const float vq[4] = {dqg.x, dqg.y, dqg.z, dqg.w}, vg[4] = {dkg.x, dkg.y, dkg.z, dkg.w},
+                  vd[4] = {dkd.x, dkd.y, dkd.z, dkd.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int cc = c + e;
+        const float eg = ex2(Go[i][cc]), ed = ex2(sG[63 * RS + c0 + cc] - Go[i][cc]);
+        dQ[i][cc] += vq[e] * eg;
+        dK[i][cc] += vg[e] * eg + vd[e] * ed;
+        const float kd = vd[e] * Ko[i][cc] * ed;
+        dG[i][cc] += (vq[e] * scale * Qo[i][cc] + vg[e] * Ko[i][cc]) * eg - kd;
+        colKd[cc] += kd;
+      }
+    }
+  }
+  // dG of the chunk's last row gains sum_t dKd . Kd and dgn . gn (column sums
+  // over the 16 row groups through LDS)
+#pragma unroll
+  for (int c = 0; c < 8; ++c) sCol[(tid >> 4) * DK + c0 + c] = colKd[c];
+  __syncthreads();  // also: every read of sQ and sK above is done
+  // dG -> sQ, then the reverse cumulative sum over rows gives d a per token
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) sQ[(r0 + i) * RS + c0 + c] = dG[i][c];
+  __syncthreads();
+  if (tid < DK) {
+    float sum = gb[GB_DGN + tid] * ex2(sG[63 * RS + tid]);
+    for (int rg = 0; rg < 16; ++rg) sum += sCol[rg * DK + tid];
+    sQ[63 * RS + tid] += sum;
+  }
+  __syncthreads();
+  {
+    const int c = tid & 127, half = tid >> 7;
+    float run = 0.0f;
+    for (int rr = 32 * half + 31; rr >= 32 * half; --rr) { run += sQ[rr * RS + c]; sQ[rr * RS + c] = run; }
+    __syncthreads();
+    if (half == 0) {
+      const float base = sQ[32 * RS + c];
+      for (int rr = 0; rr < 32; ++rr) sQ[rr * RS + c] += base;
+    }
+  }
+  __syncthreads();
+
+  // gate: a = f(x), x = g + dt_bias;  norms;  beta
+  const float A_exp = (MODE == KDA_GATE_PREGATED || A_log == nullptr) ? 1.0f : __expf(A_log[h]);
+  float colDt[8], dA = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) colDt[c] = 0.0f;
+  const bool norm = flags & KDA_FLAG_QK_L2NORM;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + i;
+    const bool ok = r < L.len;  // uniform over the 16 lanes of the row group
+    const size_t row = (size_t)(L.row0 + r);
+    float gv[8];
+    {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (ok) u = *reinterpret_cast<const uint4*>(g + (row * Hv + h) * DK + c0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { gv[2 * e] = __uint_as_float(w[e] << 16); gv[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u); }
+    }
+    float dgo[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float da = sQ[r * RS + c0 + c];
+      float a, dadx, dadA;
+      gate_fwd_bwd<MODE>(gv[c] + (dt_bias ? dt_bias[(size_t)h * DK + c0 + c] : 0.0f), A_exp, lb, a, dadx, dadA);
+      // below the decay floor the factor e^a is exactly zero in fp32
+      if (a * kLog2e < kMinLog2Decay) dadx = dadA = 0.0f;
+      dgo[c] = ok ? da * dadx : 0.0f;
+      colDt[c] += dgo[c];
+      if (ok) dA += da * dadA;
+    }
+    // y = q/|q| (the operand is scale y): dq = r (dy - y (y . dy)), dy = scale dQ
+    float yq = 0.0f, yk = 0.0f;
+    const float rqi = sRq[r], rki = sRk[r];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      yq += Qo[i][c] * (scale * dQ[i][c]);
+      yk += Ko[i][c] * dK[i][c];
+    }
+    yq = norm ? sum16(yq) : 0.0f;
+    yk = norm ? sum16(yk) : 0.0f;
+    float dbsum = sum16(dbk[i]);
+    if (ok) {
+      float dqo[8], dko[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        dqo[c] = rqi * (scale * dQ[i][c] - Qo[i][c] * yq);
+        dko[c] = rki * (dK[i][c] - Ko[i][c] * yk);
+      }
+      // with grouped heads the q/k gradients go to a per-v-head buffer
+      const int hh = qk_heads_out == Hqk ? hq : h;
+      float* pq = dq + (row * qk_heads_out + hh) * DK + c0;
+      float* pk = dk + (row * qk_heads_out + hh) * DK + c0;
+      *reinterpret_cast<float4*>(pq) = make_float4(dqo[0], dqo[1], dqo[2], dqo[3]);
+      *reinterpret_cast<float4*>(pq + 4) = make_float4(dqo[4], dqo[5], dqo[6], dqo[7]);
+      *reinterpret_cast<float4*>(pk) = make_float4(dko[0], dko[1], dko[2], dko[3]);
+      *reinterpret_cast<float4*>(pk + 4) = make_float4(dko[4], dko[5], dko[6], dko[7]);
+      float* pg = dg + (row * Hv + h) * DK + c0;
+      *reinterpret_cast<float4*>(pg) = make_float4(dgo[0], dgo[1], dgo[2], dgo[3]);
+      *reinterpret_cast<float4*>(pg + 4) = make_float4(dgo[4], dgo[5], dgo[6], dgo[7]);
+      if ((tid & 15) == 0) {
+        const float db = gb[GB_DB + r] + dbsum;
+        const float b = sB[r];
+        dbeta[row * Hv + h] = (flags & KDA_FLAG_BETA_IS_PROB) ? db : db * b * (1.0f - b);
+      }
+    }
+  }
+  // per-chunk partials of ddt_bias (column sums) and dA_log
+#pragma unroll
+  for (int c = 0; c < 8; ++c) sCol[(tid >> 4) * DK + c0 + c] = colDt[c];
+  dA += __shfl_xor(dA, 1); dA += __shfl_xor(dA, 2); dA += __shfl_xor(dA, 4); dA += __shfl_xor(dA, 8);
+  dA += __shfl_xor(dA, 16); dA += __shfl_xor(dA, 32);
+  if ((tid & 63) == 0) sRed[tid >> 6] = dA;
+  __syncthreads();
+  if (tid < DK) {
+    float sum = 0.0f;
+    for (int rg = 0; rg < 16; ++rg) sum += sCol[rg * DK + tid];
+    gp[tid] = sum;
+  }
+  if (tid == 0) gp[DK] = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+}
+
+// q/k gradients summed over the v-heads sharing a q/k head; gate-parameter
+// partials summed over chunks.
+__global__ void __launch_bounds__(256)
+kda_bwd_reduce_qk_kernel(const float* __restrict__ dqv, const float* __restrict__ dkv, float* __restrict__ dq,
+                         float* __restrict__ dk, int64_t rows, int Hqk, int G) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one float4 of (row, hq)
+  const int64_t total = rows * Hqk * (DK / 4);
+  if (e >= total) return;
+  const int c4 = (int)(e % (DK / 4));
+  const int64_t rh = e / (DK / 4);
+  const int hq = (int)(rh % Hqk);
+  const int64_t row = rh / Hqk;
+  float4 sq = make_float4(0.f, 0.f, 0.f, 0.f), sk = sq;
+  for (int j = 0; j < G; ++j) {
+    const size_t o = ((size_t)row * Hqk * G + (size_t)hq * G + j) * DK + 4 * c4;
+    const float4 a = *reinterpret_cast<const float4*>(dqv + o), b = *reinterpret_cast<const float4*>(dkv + o);
+    sq.x += a.x; sq.y += a.y; sq.z += a.z; sq.w += a.w;
+    sk.x += b.x; sk.y += b.y; sk.z += b.z; sk.w += b.w;
+  }
+  *reinterpret_cast<float4*>(dq + ((size_t)row * Hqk + hq) * DK + 4 * c4) = sq;
+  *reinterpret_cast<float4*>(dk + ((size_t)row * Hqk + hq) * DK + 4 * c4) = sk;
+}
+
+__global__ void __launch_bounds__(256)
+kda_bwd_reduce_gate_kernel(const float* __restrict__ ws, int mc, float* __restrict__ dA_log,
+                           float* __restrict__ ddt_bias) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  __shared__ float sPart[2][DK + 1];
+  const int c = tid & 127, half = tid >> 7;
+  float sum = 0.0f, sa = 0.0f;
+  for (int x = half; x < mc; x += 2) {
+    const float* gp = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS + PB_FLOATS + SB_FLOATS + GB_FLOATS;
+    sum += gp[c];
+    if (c == 0) sa += gp[DK];
+  }
+  sPart[half][c] = sum;
+  if (c == 0) sPart[half][DK] = sa;
+  __syncthreads();
+  if (tid < DK && ddt_bias) ddt_bias[(size_t)h * DK + tid] = sPart[0][tid] + sPart[1][tid];
+  if (tid == 0 && dA_log) dA_log[h] = sPart[0][DK] + sPart[1][DK];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// host side
+namespace {
+
+size_t bwd_bytes(const kda_fwd_params* p, int64_t mc) {
+  size_t b = header_bytes(p) + (size_t)p->H_v * (size_t)mc * CHUNK_HEAD_FLOATS * sizeof(float);
+  if (p->H_v != p->H_qk) b += 2 * (size_t)p->B * (size_t)p->T * p->H_v * DK * sizeof(float);
+  return b;
+}
+
+template <int MODE>
+void launch_bwd(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g, const void* beta,
+                const float* A_log, const float* dt_bias, const int64_t* cu, const void* h0, const void* d_out,
+                const float* dhT, float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dA_log,
+                float* ddt_bias, float* dh0, void* workspace, hipStream_t st) {
+  const bool packed = cu != nullptr;
+  const int64_t mc = max_chunks_of(p, packed);
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
+  int* chunk_off = reinterpret_cast<int*>(wsb);
+  float* ws = reinterpret_cast<float*>(wsb + header_bytes(p));
+  const int G = p->H_v / p->H_qk;
+  float* dqv = dq;
+  float* dkv = dk;
+  if (G > 1) {
+    dqv = ws + (size_t)p->H_v * mc * CHUNK_HEAD_FLOATS;
+    dkv = dqv + (size_t)p->B * p->T * p->H_v * DK;
+  }
+  const int chains = p->num_seqs * p->H_v;
+  const uint16_t* qq = (const uint16_t*)q;
+  const uint16_t* kk = (const uint16_t*)k;
+  const uint16_t* vv = (const uint16_t*)v;
+  const uint16_t* gg = (const uint16_t*)g;
+  const uint16_t* bb = (const uint16_t*)beta;
+  const uint16_t* dd = (const uint16_t*)d_out;
+  if (packed) launch_chunk_map(cu, p->num_seqs, chunk_off, st);
+  const dim3 cg((unsigned)mc, (unsigned)p->H_v);
+  if (mc > 0)
+    hipLaunchKernelGGL(kda_bwd_prep_kernel<MODE>, cg, dim3(256), 0, st, qq, kk, vv, gg, bb, A_log, dt_bias, cu,
+                       chunk_off, p->T, p->num_seqs, p->H_qk, p->H_v, (int)mc, p->scale, p->lower_bound, p->flags, ws);
+  if (chains > 0) {
+    hipLaunchKernelGGL(kda_bwd_fstate_kernel, dim3((unsigned)(chains * BNS)), dim3(256), 0, st, cu, chunk_off, h0,
+                       p->init_state_dtype, p->T, p->num_seqs, p->H_v, (int)mc, ws);
+    hipLaunchKernelGGL(kda_bwd_bstate_kernel, dim3((unsigned)(chains * BNS)), dim3(256), 0, st, dd, dhT, dh0, cu,
+                       chunk_off, p->T, p->num_seqs, p->H_v, (int)mc, ws);
+  }
+  if (mc > 0) {
+    hipLaunchKernelGGL(kda_bwd_dense_kernel, cg, dim3(256), 0, st, vv, dd, bb, cu, chunk_off, p->T, p->num_seqs,
+                       p->H_v, (int)mc, p->flags, dv, ws);
+    hipLaunchKernelGGL(kda_bwd_pair_kernel<MODE>, cg, dim3(256), 0, st, qq, kk, gg, bb, A_log, dt_bias, cu, chunk_off,
+                       p->T, p->num_seqs, p->H_qk, p->H_v, (int)mc, p->scale, p->lower_bound, p->flags, dqv, dkv,
+                       G > 1 ? p->H_v : p->H_qk, dg, dbeta, ws);
+    if (G > 1) {
+      const int64_t rows = (int64_t)p->B * p->T;
+      const int64_t n4 = rows * p->H_qk * (DK / 4);
+      hipLaunchKernelGGL(kda_bwd_reduce_qk_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, dqv, dkv,
+                         dq, dk, rows, p->H_qk, G);
+    }
+  }
+  if (dA_log || ddt_bias)
+    hipLaunchKernelGGL(kda_bwd_reduce_gate_kernel, dim3((unsigned)p->H_v), dim3(256), 0, st, ws, (int)mc, dA_log,
+                       ddt_bias);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_bwd_workspace_size(const kda_fwd_params* p) {
+  if (!p) return 0;
+  // packed or dense cannot be told from params alone; size for the larger
+  const bool packed = p->B == 1 && p->num_seqs >= 1;
+  if (check_params(p, false) != KDA_OK && check_params(p, true) != KDA_OK) return 0;
+  return bwd_bytes(p, max_chunks_of(p, packed));
+}
+
+kda_status kda_bwd(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                   const void* beta, const float* A_log, const float* dt_bias, const int64_t* cu_seqlens,
+                   const void* initial_state, const void* d_out, const float* d_final_state, float* dq, float* dk,
+                   float* dv, float* dg, float* dbeta, float* dA_log, float* ddt_bias, float* d_initial_state,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  const bool packed = cu_seqlens != nullptr;
+  kda_status s = check_params(p, packed);
+  if (s != KDA_OK) return s;
+  if (p->gate_mode == KDA_GATE_PREGATED && (dt_bias || ddt_bias || dA_log))
+    return fail(KDA_ERR_UNSUPPORTED, "dt_bias, ddt_bias and dA_log must be NULL with pre-gated decay");
+  if (p->gate_mode == KDA_GATE_SOFTPLUS && !A_log)
+    return fail(KDA_ERR_NULL, "A_log is NULL (required by the softplus gate)");
+  if (dA_log && !A_log) return fail(KDA_ERR_UNSUPPORTED, "dA_log needs A_log");
+  if ((int64_t)p->B * p->T > 0) {
+    const void* req[] = {q, k, v, g, beta, d_out, dq, dk, dv, dg, dbeta};
+    const char* names[] = {"q", "k", "v", "g", "beta", "d_out", "dq", "dk", "dv", "dg", "dbeta"};
+    for (int i = 0; i < 11; ++i)
+      if (!req[i]) return fail(KDA_ERR_NULL, "%s is NULL", names[i]);
+    const void* al[] = {q, k, v, g, d_out, dq, dk, dv, dg};
+    const char* aln[] = {"q", "k", "v", "g", "d_out", "dq", "dk", "dv", "dg"};
+    for (int i = 0; i < 9; ++i)
+      if (!aligned16(al[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", aln[i]);
+    if (dt_bias && !aligned16(dt_bias)) return fail(KDA_ERR_ALIGN, "dt_bias is not 16-byte aligned");
+    if (ddt_bias && !aligned16(ddt_bias)) return fail(KDA_ERR_ALIGN, "ddt_bias is not 16-byte aligned");
+  }
+  if (p->init_state_dtype != KDA_STATE_NONE) {
+    if (!initial_state) return fail(KDA_ERR_NULL, "initial_state is NULL but init_state_dtype is set");
+    if (!aligned16(initial_state)) return fail(KDA_ERR_ALIGN, "initial_state is not 16-byte aligned");
+  }
+  if (d_final_state && !aligned16(d_final_state)) return fail(KDA_ERR_ALIGN, "d_final_state is not 16-byte aligned");
+  if (d_initial_state && !aligned16(d_initial_state))
+    return fail(KDA_ERR_ALIGN, "d_initial_state is not 16-byte aligned");
+  const size_t need = kda_bwd_workspace_size(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(KDA_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(KDA_ERR_ALIGN, "workspace is not 256-byte aligned");
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  auto run = p->gate_mode == KDA_GATE_SAFE_SIGMOID ? launch_bwd<KDA_GATE_SAFE_SIGMOID>
+             : p->gate_mode == KDA_GATE_PREGATED   ? launch_bwd<KDA_GATE_PREGATED>
+                                                   : launch_bwd<KDA_GATE_SOFTPLUS>;
+  run(p, q, k, v, g, beta, A_log, dt_bias, cu_seqlens, initial_state, d_out, d_final_state, dq, dk, dv, dg, dbeta,
+      dA_log, ddt_bias, d_initial_state, workspace, st);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -41,8 +41,10 @@
 #include <type_traits>
 
 #include "kda.h"
+#include "kda_internal.h"
 
 namespace {
+using namespace kda_internal;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -1447,9 +1449,12 @@ kda_recurrent_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // host side
+}  // namespace
+
+namespace kda_internal {
+
 thread_local char g_last_error[512] = "";
 
-kda_status fail(kda_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 kda_status fail(kda_status s, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -1467,6 +1472,22 @@ size_t header_bytes(const kda_fwd_params* p) {
   size_t b = (size_t)(p->num_seqs + 1) * sizeof(int);
   return (b + 255) & ~(size_t)255;
 }
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+void launch_chunk_map(const int64_t* cu, int N, int* chunk_off, hipStream_t st) {
+  hipLaunchKernelGGL(kda_chunk_map_kernel, dim3(1), dim3(64), 0, st, cu, N, chunk_off);
+}
+
+kda_status launch_status() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+}  // namespace kda_internal
+
+namespace {
 
 // Time segments per state chain (dense input only) and chunks per segment.
 // Automatic (segments == 0): split only when the state launch has at most
@@ -1493,6 +1514,10 @@ int seg_plan(const kda_fwd_params* p, bool packed, int* seg_len) {
 size_t seg_scratch_bytes(const kda_fwd_params* p, int nseg) {
   return nseg > 1 ? (size_t)3 * p->num_seqs * p->H_v * nseg * DV * DK * sizeof(float) : 0;
 }
+
+}  // namespace
+
+namespace kda_internal {
 
 kda_status check_params(const kda_fwd_params* p, bool packed) {
   if (!p) return fail(KDA_ERR_NULL, "params is NULL");
@@ -1533,9 +1558,7 @@ kda_status check_params(const kda_fwd_params* p, bool packed) {
   return KDA_OK;
 }
 
-bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
-
-}  // namespace
+}  // namespace kda_internal
 
 extern "C" {
 
@@ -1627,7 +1650,7 @@ kda_status launch_intra(const kda_fwd_params* p, const void* q, const void* k, c
   uint8_t* wsb = reinterpret_cast<uint8_t*>(workspace);
   int* chunk_off = reinterpret_cast<int*>(wsb);
   uint8_t* blocks = wsb + header_bytes(p);
-  if (packed) hipLaunchKernelGGL(kda_chunk_map_kernel, dim3(1), dim3(64), 0, st, cu_seqlens, p->num_seqs, chunk_off);
+  if (packed) launch_chunk_map(cu_seqlens, p->num_seqs, chunk_off, st);
   if (mc > 0) {
     auto kern = p->gate_mode == KDA_GATE_SAFE_SIGMOID ? kda_intra_kernel<KDA_GATE_SAFE_SIGMOID>
                 : p->gate_mode == KDA_GATE_PREGATED   ? kda_intra_kernel<KDA_GATE_PREGATED>
@@ -1672,12 +1695,6 @@ kda_status launch_state(const kda_fwd_params* p, const void* v, const int64_t* c
                      (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out, blocks,
                      seg, p->B, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype, p->final_state_dtype, nseg,
                      seg_len);
-  return KDA_OK;
-}
-
-kda_status launch_status() {
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(KDA_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return KDA_OK;
 }
 

@@ -32,7 +32,7 @@ _STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DT
 
 # Every function the header declares.
 EXPORTS = ("kda_fwd_workspace_size", "kda_fwd_segments", "kda_fwd_check", "kda_fwd", "kda_fwd_intra", "kda_fwd_state",
-           "kda_fused_recurrent_fwd", "kda_status_string", "kda_last_error")
+           "kda_fused_recurrent_fwd", "kda_bwd_workspace_size", "kda_bwd", "kda_status_string", "kda_last_error")
 
 
 class KdaError(RuntimeError):
@@ -74,6 +74,10 @@ def load_library(path: str = LIB_PATH):
         fn.argtypes = [PP] + [P] * 12 + [ctypes.c_size_t, P]
     lib.kda_fused_recurrent_fwd.restype = ctypes.c_int
     lib.kda_fused_recurrent_fwd.argtypes = [PP] + [P] * 11 + [P]
+    lib.kda_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.kda_bwd_workspace_size.argtypes = [PP]
+    lib.kda_bwd.restype = ctypes.c_int
+    lib.kda_bwd.argtypes = [PP] + [P] * 20 + [ctypes.c_size_t, P]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_last_error.restype = ctypes.c_char_p
@@ -198,3 +202,51 @@ def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GAT
     if rc != KDA_OK:
         raise KdaError(rc, lib.kda_last_error().decode())
     return out, final_state
+
+
+def bwd(q, k, v, g, beta, A_log, dt_bias, scale, d_out, lower_bound=-1.0, gate_mode=GATE_SOFTPLUS,
+        initial_state=None, d_final_state=None, cu_seqlens=None, qk_l2norm=True, beta_is_prob=False,
+        workspace=None):
+    """Gradients of ``fwd`` (kda_bwd) on the current HIP stream.
+
+    Inputs as for ``fwd`` plus d_out bf16 [B,T,Hv,128] and d_final_state fp32
+    [N,Hv,128,128] or None.  Returns a dict of fp32 tensors: dq, dk
+    [B,T,Hqk,128], dv, dg [B,T,Hv,128], dbeta [B,T,Hv], dA_log [Hv] (None
+    without A_log or with pre-gated decay), ddt_bias [Hv,128] (None with
+    pre-gated decay) and dh0 [N,Hv,128,128].
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("d_out", d_out)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bf16 device tensor")
+    B, T, Hqk, K = q.shape
+    Hv, V = v.shape[2], v.shape[3]
+    if d_out.shape != (B, T, Hv, V):
+        raise ValueError("d_out must be [B, T, Hv, V]")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if d_final_state is not None and (d_final_state.dtype != torch.float32 or not d_final_state.is_contiguous()
+                                      or tuple(d_final_state.shape) != (N, Hv, V, K)):
+        raise ValueError("d_final_state must be contiguous fp32 [N, Hv, V, K]")
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    r = dict(dq=torch.empty((B, T, Hqk, K), **f32), dk=torch.empty((B, T, Hqk, K), **f32),
+             dv=torch.empty((B, T, Hv, V), **f32), dg=torch.empty((B, T, Hv, K), **f32),
+             dbeta=torch.empty((B, T, Hv), **f32), dh0=torch.empty((N, Hv, V, K), **f32),
+             dA_log=None if (A_log is None or gate_mode == GATE_PREGATED) else torch.empty((Hv,), **f32),
+             ddt_bias=None if gate_mode == GATE_PREGATED else torch.empty((Hv, K), **f32))
+    p = make_params(B=B, T=T, H_qk=Hqk, H_v=Hv, K=K, V=V, num_seqs=N, scale=float(scale),
+                    lower_bound=float(lower_bound), gate_mode=int(gate_mode),
+                    init_state_dtype=_state_code(initial_state), final_state_dtype=STATE_NONE,
+                    flags=(FLAG_QK_L2NORM if qk_l2norm else 0) | (FLAG_BETA_IS_PROB if beta_is_prob else 0))
+    need = int(lib.kda_bwd_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
+                     _ptr(cu_seqlens), _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), _ptr(r["dq"]),
+                     _ptr(r["dk"]), _ptr(r["dv"]), _ptr(r["dg"]), _ptr(r["dbeta"]), _ptr(r["dA_log"]),
+                     _ptr(r["ddt_bias"]), _ptr(r["dh0"]), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                     ctypes.c_void_p(stream))
+    if rc != KDA_OK:
+        raise KdaError(rc, lib.kda_last_error().decode())
+    return r

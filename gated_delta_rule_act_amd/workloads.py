@@ -204,3 +204,14 @@ def workload(idx: int, **override) -> KdaInputs:
         spec["lengths"] = lengths
         spec["T"] = int(lengths.sum())
     return make_inputs(rng=rng, **spec)
+
+
+def make_grads(inp: KdaInputs, seed: int, d_out_std: float = 0.1, dhT_std: Optional[float] = 0.01):
+    """Seeded upstream gradients for a backward run on ``inp``: d_out as bf16
+    bits [B,T,Hv,V] and d_final_state fp32 [N,Hv,V,K] (None if dhT_std is None)."""
+    rng = np.random.default_rng(seed)
+    d_out = _normal_bf16(rng, (inp.B, inp.T, inp.Hv, inp.V), std=d_out_std)
+    dhT = None
+    if dhT_std is not None:
+        dhT = (rng.standard_normal(size=(inp.N, inp.Hv, inp.V, inp.K), dtype=np.float32) * np.float32(dhT_std))
+    return d_out, dhT

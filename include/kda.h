@@ -180,6 +180,40 @@ kda_status kda_fused_recurrent_fwd(const kda_fwd_params* p,
                                    const int64_t* cu_seqlens, const void* initial_state, void* final_state,
                                    void* out, void* stream);
 
+/* Bytes of device workspace kda_bwd needs for these parameters; host only,
+ * no HIP calls.  Returns 0 if the parameters are invalid. */
+size_t kda_bwd_workspace_size(const kda_fwd_params* p);
+
+/* Gradients of kda_fwd: the backward pass that the fla-kda SKILL.md lists in
+ * its "Code map" (backward passes) and "Validation" (supported gradients)
+ * sections.  Inputs are those of kda_fwd (the forward is recomputed, so no
+ * forward output is needed) plus
+ *   d_out          bf16 [B, T, H_v, 128]  gradient of out
+ *   d_final_state  fp32 [num_seqs, H_v, 128, 128] gradient of the final state,
+ *                  or NULL (zero)
+ * and writes fp32 gradients, every element of each:
+ *   dq, dk  [B, T, H_qk, 128] (summed over the v-heads of each q/k head)
+ *   dv      [B, T, H_v, 128]     dg [B, T, H_v, 128]     dbeta [B, T, H_v]
+ *           (with respect to the logits, or the probabilities with
+ *           KDA_FLAG_BETA_IS_PROB)
+ *   dA_log  [H_v] or NULL (must be NULL when A_log is NULL or the decay is
+ *           pre-gated)
+ *   ddt_bias [H_v, 128] or NULL (the bias gradient, also when dt_bias is
+ *           NULL; must be NULL with pre-gated decay)
+ *   d_initial_state fp32 [num_seqs, H_v, 128, 128] or NULL
+ * params->final_state_dtype and params->segments are not used.  The
+ * workspace (kda_bwd_workspace_size bytes, 256-byte aligned) holds fp32
+ * per-chunk intermediates; the library allocates nothing.  Every predicate
+ * is checked before anything is enqueued; returns after enqueueing. */
+kda_status kda_bwd(const kda_fwd_params* p,
+                   const void* q, const void* k, const void* v, const void* g,
+                   const void* beta, const float* A_log, const float* dt_bias,
+                   const int64_t* cu_seqlens, const void* initial_state,
+                   const void* d_out, const float* d_final_state,
+                   float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                   float* dA_log, float* ddt_bias, float* d_initial_state,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static name of a status code. */
 const char* kda_status_string(kda_status s);
 

@@ -1,0 +1,124 @@
+"""GPU parity of the backward (kda_bwd, through the C ABI) against the fp64
+oracle's gradients (the token-by-token adjoint, itself pinned by finite
+differences and autograd).
+
+Bar: for every gradient tensor, ||g_gpu - g_ref||_F / ||g_ref||_F <= 1e-3 --
+the relative bar of the fp32 final state, since the backward computes in
+fp32 throughout -- and every element finite.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_act_amd import kda
+from gated_delta_rule_act_amd import workloads as W
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+GRAD_REL = 1e-3
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dA_log", "ddt_bias", "dh0")
+
+
+def run_gpu_bwd(inp, d_out, dhT):
+    d = U.to_device(inp)
+    dev_dout = U.bf16_dev(d_out)
+    dev_dhT = None if dhT is None else torch.from_numpy(dhT).cuda()
+    r = kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"], inp.scale, dev_dout,
+                lower_bound=inp.lower_bound, gate_mode=inp.gate_mode, initial_state=d["h0"], d_final_state=dev_dhT,
+                cu_seqlens=d["cu_seqlens"], qk_l2norm=bool(inp.flags & W.FLAG_QK_L2NORM),
+                beta_is_prob=bool(inp.flags & W.FLAG_BETA_IS_PROB))
+    torch.cuda.synchronize()
+    return {n: (None if t is None else t.cpu().numpy().astype(np.float64)) for n, t in r.items()}
+
+
+def run_oracle_bwd(inp, d_out, dhT):
+    f = oracle.bf16_to_f64
+    return oracle.bwd(f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta), inp.A_log, inp.dt_bias, f(d_out),
+                      None if dhT is None else dhT.astype(np.float64), scale=inp.scale,
+                      lower_bound=inp.lower_bound, gate_mode=inp.gate_mode, flags=inp.flags,
+                      initial_state=inp.initial_state_f64(), cu_seqlens=inp.cu_seqlens)
+
+
+def compare(gpu, ref, what):
+    errs = {}
+    for n in NAMES:
+        if gpu.get(n) is None:
+            continue
+        a, b = gpu[n], ref[n]
+        assert np.isfinite(a).all(), (what, n, "non-finite")
+        nb = np.linalg.norm(b)
+        errs[n] = float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
+    U.log(f"    {what} {errs}")
+    for n, e in errs.items():
+        assert e <= GRAD_REL, (what, n, e)
+
+
+def small(**kw):
+    base = dict(B=2, T=300, Hqk=4, seed=301, init_state_dtype=W.STATE_F32)
+    base.update(kw)
+    return W.make_inputs(**base)
+
+
+CASES = {
+    "softplus": dict(),
+    "safe_lb5_extremes": dict(gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-5.0, A_log_range=(-4.0, 6.0), g_std=3.0),
+    "safe_lb1_gva": dict(gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-1.0, Hqk=2, Hv=6, T=200),
+    "pregated": dict(gate_mode=W.GATE_PREGATED, pregated_range=(-1.0, 0.0)),
+    "softplus_no_state": dict(init_state_dtype=W.STATE_NONE, T=257),
+    "bf16_state": dict(init_state_dtype=W.STATE_BF16, T=150),
+    "one_token": dict(T=1, B=3),
+    "exact_chunks": dict(T=128, B=1, Hqk=2),
+    "long_memory": dict(A_log_range=(-8.0, -6.0), T=400, B=1),
+    "strong_decay": dict(A_log_range=(3.0, 6.0), g_std=3.0, T=200),
+    "no_l2norm": dict(flags=0, qk_std=1.0 / np.sqrt(128), T=260),
+    "beta_prob": dict(beta_prob=True, T=200),
+    "safe_no_A_log": dict(gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-5.0, with_A_log=False, g_std=3.0, T=200),
+    "softplus_no_dt_bias": dict(with_dt_bias=False, T=200),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_bwd_elementwise(name):
+    inp = small(**CASES[name])
+    d_out, dhT = W.make_grads(inp, seed=77)
+    U.log(f"[gpu] bwd {name}: B={inp.B} T={inp.T} Hqk={inp.Hqk} Hv={inp.Hv} gate={inp.gate_mode}")
+    compare(run_gpu_bwd(inp, d_out, dhT), run_oracle_bwd(inp, d_out, dhT), name)
+
+
+def test_bwd_without_final_state_gradient():
+    inp = small(T=200)
+    d_out, _ = W.make_grads(inp, seed=5, dhT_std=None)
+    U.log("[gpu] bwd with d_final_state = None")
+    compare(run_gpu_bwd(inp, d_out, None), run_oracle_bwd(inp, d_out, None), "no dhT")
+
+
+def test_bwd_packed():
+    lengths = [1, 63, 64, 0, 65, 200]
+    inp = W.make_inputs(B=1, T=None, Hqk=2, Hv=4, seed=19, lengths=lengths, init_state_dtype=W.STATE_F32)
+    d_out, dhT = W.make_grads(inp, seed=8)
+    U.log(f"[gpu] bwd packed {lengths}")
+    gpu = run_gpu_bwd(inp, d_out, dhT)
+    compare(gpu, run_oracle_bwd(inp, d_out, dhT), "packed")
+    # the empty sequence passes its final-state gradient straight through
+    assert np.array_equal(gpu["dh0"][3], dhT[3].astype(np.float64))
+
+
+def test_bwd_empty_input():
+    inp = small(T=0, B=2)
+    d_out, dhT = W.make_grads(inp, seed=3)
+    gpu = run_gpu_bwd(inp, d_out, dhT)
+    assert np.array_equal(gpu["dh0"], dhT.astype(np.float64))
+    assert not gpu["dA_log"].any() and not gpu["ddt_bias"].any()
+
+
+def test_bwd_medium_sampled():
+    # several chunks per sequence at the model's head count, sampled pairs
+    inp = W.make_inputs(B=2, T=2048, Hqk=8, seed=23, gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-5.0,
+                        A_log_range=(-4.0, 6.0), g_std=3.0, init_state_dtype=W.STATE_F32)
+    d_out, dhT = W.make_grads(inp, seed=29)
+    U.log("[gpu] bwd B=2 T=2048 H=8")
+    gpu = run_gpu_bwd(inp, d_out, dhT)
+    ref = run_oracle_bwd(inp, d_out, dhT)
+    compare(gpu, ref, "medium")
