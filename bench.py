@@ -123,7 +123,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--segments", type=int, default=0,
                     help="time segments per state chain (0: the library decides, 1: none)")
-    ap.add_argument("--mode", choices=("chunked", "recurrent"), default="chunked",
+    ap.add_argument("--mode", choices=("chunked", "recurrent", "backward"), default="chunked",
                     help="chunked: the headline forward; recurrent: the token-recurrent entry on a decode workload")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="instead of the forward, run N plain 1 GiB device copies (traffic counter scale)")
@@ -151,6 +151,8 @@ def main():
 
     if args.mode == "recurrent":
         return run_recurrent(args, dev)
+    if args.mode == "backward":
+        return run_backward(args, dev)
 
     t_gen = time.perf_counter()
     inp = W.workload(3 if args.workload is None else args.workload)
@@ -312,6 +314,87 @@ def run_recurrent(args, dev):
                                "sample": f"{inp.name}: the whole workload, {reps} times ({dt:.2f} s)", "seconds": dt}
         rec["parity"] = {"out_max_abs": e["out_max_abs"], "out_rel_rms": e["out_rel_rms"],
                          "state_rel": e["state_rel"], "tol_out_max_abs": U.OUT_MAX_ABS, "tol_state_rel": U.STATE_REL}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+def run_backward(args, dev):
+    """The backward (kda_bwd) on a chunked workload: one call per step, which
+    recomputes the forward quantities it needs and writes every gradient."""
+    import numpy as np
+    import torch
+    import oracle
+    from gated_delta_rule_act_amd import kda, workloads as W
+    from tests import gpu_util as U
+
+    inp = W.workload(3 if args.workload is None else args.workload)
+    d = U.to_device(inp)
+    d_out, dhT = W.make_grads(inp, seed=1000 + (3 if args.workload is None else args.workload))
+    dev_dout = U.bf16_dev(d_out)
+    dev_dhT = torch.from_numpy(dhT).to(dev)
+    res = {}
+
+    def step():
+        res.update(kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"], inp.scale, dev_dout,
+                           lower_bound=inp.lower_bound, gate_mode=inp.gate_mode, initial_state=d["h0"],
+                           d_final_state=dev_dhT, cu_seqlens=d["cu_seqlens"]))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tok = inp.B * inp.T
+    # the method's contractions for the gradients: the forward's 180,224 flop per
+    # token-head recomputed, plus twice that for the reverse products
+    flops = 3 * FLOP_PER_TOKEN_HEAD * tok * inp.Hv
+    rec = {
+        "metric": "chunk_kda bwd tokens/s (all input gradients), 1 MI355X",
+        "value": tok / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64, see DESIGN.md)",
+        "config": {"workload": inp.name, "B": inp.B, "T": inp.T, "H_qk": inp.Hqk, "H_v": inp.Hv, "K": inp.K,
+                   "V": inp.V, "gate": ["softplus", "safe_sigmoid", "pregated"][inp.gate_mode]},
+        "roofline": {"bound": "alu", "kernel": "kda_bwd (all launches)",
+                     "achieved": flops / (ms * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": ms},
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+        # a bounded sample: the first sequence's first G v-heads (one q/k head), whole length
+        G = inp.Hv // inp.Hqk
+        nh = max(G, 2 if G == 1 else G)
+        hs, hqs = slice(0, nh), slice(0, max(1, nh // G))
+        f = oracle.bf16_to_f64
+        sl = lambda a, hh: np.ascontiguousarray(a[:1, :, hh])
+        t0 = time.perf_counter()
+        ref = oracle.bwd(f(sl(inp.q, hqs)), f(sl(inp.k, hqs)), f(sl(inp.v, hs)), f(sl(inp.g, hs)),
+                         f(np.ascontiguousarray(inp.beta[:1, :, hs])),
+                         None if inp.A_log is None else inp.A_log[hs],
+                         None if inp.dt_bias is None else inp.dt_bias[hs], f(sl(d_out, hs)),
+                         dhT[:1, hs].astype(np.float64), scale=inp.scale, lower_bound=inp.lower_bound,
+                         gate_mode=inp.gate_mode, flags=inp.flags,
+                         initial_state=None if inp.initial_state is None else inp.initial_state_f64()[:1, hs],
+                         nthreads=threads)
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": inp.T * nh / inp.Hv / dt, "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle", "seconds": dt,
+                               "sample": f"{inp.name}: sequence 0, v-heads 0-{nh - 1} with their q/k heads, all "
+                                         f"{inp.T} tokens ({dt:.2f} s); tokens/s scaled to all {inp.Hv} heads"}
+        errs = {}
+        for n, sel in (("dq", hqs), ("dk", hqs), ("dv", hs), ("dg", hs), ("dbeta", hs), ("dh0", hs)):
+            a = res[n][:1, :, sel].double().cpu().numpy() if n != "dh0" else res[n][:1, sel].double().cpu().numpy()
+            b = ref[n]
+            errs[n] = float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+        rec["parity"] = {"sampled_rel_fro": errs, "tol": 1e-3}
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

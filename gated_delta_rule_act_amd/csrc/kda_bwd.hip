@@ -304,6 +304,52 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
 }
 
 // ---------------------------------------------------------------------------
+// fp32 MFMA (16x16x4) blocks with operands in LDS.  Lane (li = lane & 15,
+// lg = lane >> 4) feeds A[li][k + lg] and B[k + lg][li] and receives
+// C[4 lg + r][li] (r < 4) of each 16 x 16 tile.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// acc[m][n] += the (16 m, 16 n) tile of A B over k < kdim, operands fp32 in LDS:
+//   A(r, k) = AT ? sA[k * lda + r] : sA[r * lda + k]
+//   B(k, c) = BT ? sB[c * ldb + k] : sB[k * ldb + c]
+template <bool AT, bool BT, int MT, int NT>
+__device__ __forceinline__ void mfma_block(f32x4 (&acc)[MT][NT], const float* sA, int lda, const float* sB, int ldb,
+                                           int row0, int col0, int kdim, int lane) {
+  const int li = lane & 15, lg = lane >> 4;
+#pragma unroll 8
+  for (int k = 0; k < kdim; k += 4) {
+    const int kk = k + lg;
+    float a[MT], b[NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int r = row0 + 16 * m + li;
+      a[m] = AT ? sA[kk * lda + r] : sA[r * lda + kk];
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int c = col0 + 16 * n + li;
+      b[n] = BT ? sB[c * ldb + kk] : sB[kk * ldb + c];
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], b[n], acc[m][n], 0, 0, 0);
+  }
+}
+
+template <int MT, int NT>
+__device__ __forceinline__ void zero_block(f32x4 (&acc)[MT][NT]) {
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// element (row, col) of block tile (m, n, r): the lane's layout above
+#define BLK_ROW(row0, m, r) ((row0) + 16 * (m) + 4 * lg + (r))
+#define BLK_COL(col0, n) ((col0) + 16 * (n) + li)
+
+// ---------------------------------------------------------------------------
 // prep: per (chunk, v-head) forward quantities in fp32
 template <int MODE>
 __global__ void __launch_bounds__(256)
@@ -454,29 +500,33 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     sT[r * QS + c] *= sB[c];
   }
   __syncthreads();
-  // W = M Kg, Ubar = M V (4 x 8 tiles)
+  // W = M Kg, Ubar = M V (fp32 MFMA; wave w: rows 32 (w >> 1) .., columns 64 (w & 1) ..)
   {
-    const int r0 = 4 * (tid >> 4), c0 = 8 * (tid & 15);
-    float w[4][8], u[4][8];
-    zero_tile(w);
-    zero_tile(u);
-    mm_tile<false, false, 8>(w, sT, QS, sK, RS, r0, c0, CH);
-    mm_tile<false, false, 8>(u, sT, QS, sQ, RS, r0, c0, CH);
+    const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
+    const int R0 = 32 * (wv >> 1), C0 = 64 * (wv & 1);
+    f32x4 w[2][4], u[2][4];
+    zero_block(w);
+    zero_block(u);
+    mfma_block<false, false, 2, 4>(w, sT, QS, sK, RS, R0, C0, CH, lane);
+    mfma_block<false, false, 2, 4>(u, sT, QS, sQ, RS, R0, C0, CH, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int j = 0; j < 8; j += 4) {
-        *reinterpret_cast<float4*>(pb + PB_W + (r0 + i) * DK + c0 + j) =
-            make_float4(w[i][j], w[i][j + 1], w[i][j + 2], w[i][j + 3]);
-        *reinterpret_cast<float4*>(pb + PB_UB + (r0 + i) * DV + c0 + j) =
-            make_float4(u[i][j], u[i][j + 1], u[i][j + 2], u[i][j + 3]);
-      }
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = R0 + 16 * m + 4 * lg + r, c = C0 + 16 * n + li;
+          pb[PB_W + t * DK + c] = w[m][n][r];
+          pb[PB_UB + t * DV + c] = u[m][n][r];
+        }
   }
 }
 
 // ---------------------------------------------------------------------------
-// state passes: one workgroup per (sequence, v-head, 32-row V slice); thread
-// t owns row v0 + (t >> 3), key columns 4 (t & 7) + 32 m + i (m, i < 4)
+// state passes: one workgroup per (sequence, v-head, 32-row V slice).  The
+// 32 x 128 slice of the state (or of its gradient) lives in MFMA accumulator
+// layout: wave w holds key columns 32 w .. +31 for all 32 rows, element
+// (v = 16 m + 4 lg + r, k = 32 w + 16 n + li) in acc[m][n][r].
 constexpr int SV = 36;  // LDS row stride of 32-wide slices
 
 __device__ __forceinline__ void chain_chunks(int n, const int* chunk_off, const int64_t* cu, int T, int& x0, int& nc,
@@ -489,13 +539,22 @@ __device__ __forceinline__ void chain_chunks(int n, const int* chunk_off, const 
   }
 }
 
-// 32 x 128 slice of a [128][128] fp32 matrix (rows v0..) <-> per-thread registers
-__device__ __forceinline__ void slice_store(const float (&S)[16], float* g, int v0, int tid) {
-  const int row = tid >> 3, kc = 4 * (tid & 7);
+// slice <-> [128][128] fp32 matrix g (rows v0 ..), and <-> LDS [32][RS]
+__device__ __forceinline__ void slice_to_global(const f32x4 (&S)[2][2], float* g, int v0, int w, int li, int lg) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    *reinterpret_cast<float4*>(g + (size_t)(v0 + row) * DK + kc + 32 * m) =
-        make_float4(S[4 * m], S[4 * m + 1], S[4 * m + 2], S[4 * m + 3]);
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) g[(size_t)(v0 + 16 * m + 4 * lg + r) * DK + 32 * w + 16 * n + li] = S[m][n][r];
+}
+__device__ __forceinline__ void slice_to_lds(const f32x4 (&S)[2][2], float* s, int w, int li, int lg) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[(16 * m + 4 * lg + r) * RS + 32 * w + 16 * n + li] = S[m][n][r];
 }
 
 __global__ void __launch_bounds__(256)
@@ -503,85 +562,64 @@ kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ ch
                       int init_dtype, int T, int N, int Hv, int mc, float* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) float sW[CH * RS];
   __shared__ __attribute__((aligned(16))) float sKd[CH * RS];
-  __shared__ __attribute__((aligned(16))) float sUb[CH * SV];
   __shared__ __attribute__((aligned(16))) float sU[CH * SV];
   __shared__ __attribute__((aligned(16))) float sS[BV * RS];
-  __shared__ __attribute__((aligned(16))) float sGn[DK];
   const int chain = blockIdx.x / BNS, slice = blockIdx.x % BNS;
   if (chain >= N * Hv) return;
   const int n = chain / Hv, h = chain % Hv, v0 = BV * slice, tid = threadIdx.x;
-  const int row = tid >> 3, kc = 4 * (tid & 7);
+  const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
   int x0, nc;
   int64_t bos;
   chain_chunks(n, chunk_off, cu, T, x0, nc, bos);
-  float S[16];
-  const size_t sbase = (((size_t)n * Hv + h) * DV + v0 + row) * DK + kc;
+  f32x4 S[2][2];
+  const size_t sbase = ((size_t)n * Hv + h) * DV * DK;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (init_dtype == KDA_STATE_F32) {
-      x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(h0) + sbase + 32 * m);
-    } else if (init_dtype == KDA_STATE_BF16) {
-      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(h0) + sbase + 32 * m);
-      x = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                      __uint_as_float(u.y & 0xffff0000u));
-    }
-    S[4 * m] = x.x; S[4 * m + 1] = x.y; S[4 * m + 2] = x.z; S[4 * m + 3] = x.w;
-  }
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const size_t e = sbase + (size_t)(v0 + 16 * m + 4 * lg + r) * DK + 32 * w + 16 * nn + li;
+        float x = 0.0f;
+        if (init_dtype == KDA_STATE_F32) x = reinterpret_cast<const float*>(h0)[e];
+        else if (init_dtype == KDA_STATE_BF16) x = bf2f(reinterpret_cast<const uint16_t*>(h0)[e]);
+        S[m][nn][r] = x;
+      }
   for (int c = 0; c < nc; ++c) {
     const float* pb = ws + ((size_t)h * mc + x0 + c) * CHUNK_HEAD_FLOATS;
     float* sb = const_cast<float*>(pb) + PB_FLOATS;
-    slice_store(S, sb + SB_H, v0, tid);
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      *reinterpret_cast<float4*>(sS + row * RS + kc + 32 * m) =
-          make_float4(S[4 * m], S[4 * m + 1], S[4 * m + 2], S[4 * m + 3]);
+    slice_to_global(S, sb + SB_H, v0, w, li, lg);
+    slice_to_lds(S, sS, w, li, lg);
     load_tile128(sW, pb + PB_W, DK, tid);
     load_tile128(sKd, pb + PB_KD, DK, tid);
+    // U rows 16 w .. +15 start from Ubar (lane layout of the product below)
+    f32x4 U[1][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid + 256 * i, t = e >> 3, j = 4 * (e & 7);
-      *reinterpret_cast<float4*>(sUb + t * SV + j) = *reinterpret_cast<const float4*>(pb + PB_UB + t * DV + v0 + j);
-    }
-    if (tid < 32) *reinterpret_cast<float4*>(sGn + 4 * tid) = *reinterpret_cast<const float4*>(pb + PB_GN + 4 * tid);
+    for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) U[0][nn][r] = -pb[PB_UB + (16 * w + 4 * lg + r) * DV + v0 + 16 * nn + li];
+    float gn[2];
+#pragma unroll
+    for (int nn = 0; nn < 2; ++nn) gn[nn] = pb[PB_GN + 32 * w + 16 * nn + li];
     __syncthreads();
-    // U[t][v] = Ubar[t][v] - sum_k W[t][k] S[v][k]   (thread: t = tid >> 2, v = 8 (tid & 3) + j)
-    {
-      const int t = tid >> 2, vq = 8 * (tid & 3);
-      float acc[8];
+    // -U = W S^T - Ubar:  A(t, k) = W[t][k],  B(k, v) = S[v][k]
+    mfma_block<false, true, 1, 2>(U, sW + 16 * w * RS, RS, sS, RS, 0, 0, DK, lane);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-      for (int k = 0; k < DK; k += 4) {
-        const float4 w = *reinterpret_cast<const float4*>(sW + t * RS + k);
+    for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float4 sv = *reinterpret_cast<const float4*>(sS + (vq + j) * RS + k);
-          acc[j] += w.x * sv.x + w.y * sv.y + w.z * sv.z + w.w * sv.w;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * lg + r, vv = 16 * nn + li;
+        const float u = -U[0][nn][r];
+        sU[t * SV + vv] = u;
+        sb[SB_U + t * DV + v0 + vv] = u;
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = sUb[t * SV + vq + j] - acc[j];
-#pragma unroll
-      for (int j = 0; j < 8; j += 4) {
-        const float4 u4 = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
-        *reinterpret_cast<float4*>(sU + t * SV + vq + j) = u4;
-        *reinterpret_cast<float4*>(sb + SB_U + t * DV + v0 + vq + j) = u4;
-      }
-    }
     __syncthreads();
-    // S[v][k] <- S[v][k] gn[k] + sum_t U[t][v] Kd[t][k]
+    // S <- S Diag(gn) + U^T Kd:  A(v, t) = U[t][v],  B(t, k) = Kd[t][k]
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[4 * m + i] *= sGn[kc + 32 * m + i];
-    for (int t = 0; t < CH; ++t) {
-      const float u = sU[t * SV + row];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float4 kd = *reinterpret_cast<const float4*>(sKd + t * RS + kc + 32 * m);
-        S[4 * m] += u * kd.x; S[4 * m + 1] += u * kd.y; S[4 * m + 2] += u * kd.z; S[4 * m + 3] += u * kd.w;
-      }
-    }
+      for (int nn = 0; nn < 2; ++nn) S[m][nn] *= gn[nn];
+    mfma_block<true, false, 2, 2>(S, sU, SV, sKd, RS, 0, 32 * w, CH, lane);
     __syncthreads();
   }
 }
@@ -597,33 +635,30 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
   __shared__ __attribute__((aligned(16))) float sdO[CH * SV];
   __shared__ __attribute__((aligned(16))) float sdU[CH * SV];
   __shared__ __attribute__((aligned(16))) float sdh[BV * RS];
-  __shared__ __attribute__((aligned(16))) float sGn[DK];
   const int chain = blockIdx.x / BNS, slice = blockIdx.x % BNS;
   if (chain >= N * Hv) return;
   const int n = chain / Hv, h = chain % Hv, v0 = BV * slice, tid = threadIdx.x;
-  const int row = tid >> 3, kc = 4 * (tid & 7);
+  const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
   int x0, nc;
   int64_t bos;
   chain_chunks(n, chunk_off, cu, T, x0, nc, bos);
   const int64_t seqlen = cu == nullptr ? (int64_t)T : cu[n + 1] - cu[n];
-  float D[16];
-  const size_t sbase = (((size_t)n * Hv + h) * DV + v0 + row) * DK + kc;
+  f32x4 D[2][2];
+  const size_t sbase = ((size_t)n * Hv + h) * DV * DK;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (dhT) x = *reinterpret_cast<const float4*>(dhT + sbase + 32 * m);
-    D[4 * m] = x.x; D[4 * m + 1] = x.y; D[4 * m + 2] = x.z; D[4 * m + 3] = x.w;
-  }
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        D[m][nn][r] = dhT ? dhT[sbase + (size_t)(v0 + 16 * m + 4 * lg + r) * DK + 32 * w + 16 * nn + li] : 0.0f;
   for (int c = nc - 1; c >= 0; --c) {
     const float* pb = ws + ((size_t)h * mc + x0 + c) * CHUNK_HEAD_FLOATS;
     float* sb = const_cast<float*>(pb) + PB_FLOATS;
     const int64_t row0 = bos + (int64_t)c * CH;
     const int len = (int)min((int64_t)CH, seqlen - (int64_t)c * CH);
-    slice_store(D, sb + SB_DH, v0, tid);
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      *reinterpret_cast<float4*>(sdh + row * RS + kc + 32 * m) =
-          make_float4(D[4 * m], D[4 * m + 1], D[4 * m + 2], D[4 * m + 3]);
+    slice_to_global(D, sb + SB_DH, v0, w, li, lg);
+    slice_to_lds(D, sdh, w, li, lg);
     load_tile64(sAq, pb + PB_AQK, tid);
     load_tile128(sKd, pb + PB_KD, DK, tid);
     load_tile128(sQg, pb + PB_QG, DK, tid);
@@ -633,83 +668,49 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
       const int t = tid >> 2, j = 8 * (tid & 3);
       uint4 u = make_uint4(0, 0, 0, 0);
       if (t < len) u = *reinterpret_cast<const uint4*>(d_out + ((size_t)(row0 + t) * Hv + h) * DV + v0 + j);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        sdO[t * SV + j + 2 * q] = __uint_as_float(w[q] << 16);
-        sdO[t * SV + j + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        sdO[t * SV + j + 2 * q] = __uint_as_float(wv[q] << 16);
+        sdO[t * SV + j + 2 * q + 1] = __uint_as_float(wv[q] & 0xffff0000u);
       }
     }
-    if (tid < 32) *reinterpret_cast<float4*>(sGn + 4 * tid) = *reinterpret_cast<const float4*>(pb + PB_GN + 4 * tid);
+    float gn[2];
+#pragma unroll
+    for (int nn = 0; nn < 2; ++nn) gn[nn] = pb[PB_GN + 32 * w + 16 * nn + li];
     __syncthreads();
-    // dU[t][v] = sum_s Aqk[s][t] dO[s][v] + sum_k Kd[t][k] dS'[v][k]
-    {
-      const int t = tid >> 2, vq = 8 * (tid & 3);
-      float acc[8];
+    // dU rows 16 w .. +15:  Aqk^T dO  +  Kd dS'^T
+    f32x4 dU[1][2];
+    zero_block(dU);
+    mfma_block<true, false, 1, 2>(dU, sAq + 16 * w, QS, sdO, SV, 0, 0, CH, lane);
+    mfma_block<false, true, 1, 2>(dU, sKd + 16 * w * RS, RS, sdh, RS, 0, 0, DK, lane);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-      for (int s2 = 0; s2 < CH; ++s2) {
-        const float a = sAq[s2 * QS + t];
-        const float4 o0 = *reinterpret_cast<const float4*>(sdO + s2 * SV + vq);
-        const float4 o1 = *reinterpret_cast<const float4*>(sdO + s2 * SV + vq + 4);
-        acc[0] += a * o0.x; acc[1] += a * o0.y; acc[2] += a * o0.z; acc[3] += a * o0.w;
-        acc[4] += a * o1.x; acc[5] += a * o1.y; acc[6] += a * o1.z; acc[7] += a * o1.w;
-      }
-      for (int k = 0; k < DK; k += 4) {
-        const float4 kd = *reinterpret_cast<const float4*>(sKd + t * RS + k);
+    for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float4 d = *reinterpret_cast<const float4*>(sdh + (vq + j) * RS + k);
-          acc[j] += kd.x * d.x + kd.y * d.y + kd.z * d.z + kd.w * d.w;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * lg + r, vv = 16 * nn + li;
+        sdU[t * SV + vv] = -dU[0][nn][r];
+        sb[SB_DU + t * DV + v0 + vv] = dU[0][nn][r];
       }
-#pragma unroll
-      for (int j = 0; j < 8; j += 4) {
-        const float4 u4 = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
-        *reinterpret_cast<float4*>(sdU + t * SV + vq + j) = u4;
-        *reinterpret_cast<float4*>(sb + SB_DU + t * DV + v0 + vq + j) = u4;
-      }
-    }
     __syncthreads();
-    // dS[v][k] = dS'[v][k] gn[k] + sum_t dO[t][v] Qg[t][k] - sum_t dU[t][v] W[t][k]
+    // dS = dS' Diag(gn) + dO^T Qg - dU^T W:  A(v, t) = dO[t][v] (then -dU[t][v])
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) D[4 * m + i] *= sGn[kc + 32 * m + i];
-    for (int t = 0; t < CH; ++t) {
-      const float o = sdO[t * SV + row], du = sdU[t * SV + row];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float4 qg = *reinterpret_cast<const float4*>(sQg + t * RS + kc + 32 * m);
-        const float4 w = *reinterpret_cast<const float4*>(sW + t * RS + kc + 32 * m);
-        D[4 * m] += o * qg.x - du * w.x;
-        D[4 * m + 1] += o * qg.y - du * w.y;
-        D[4 * m + 2] += o * qg.z - du * w.z;
-        D[4 * m + 3] += o * qg.w - du * w.w;
-      }
-    }
+      for (int nn = 0; nn < 2; ++nn) D[m][nn] *= gn[nn];
+    mfma_block<true, false, 2, 2>(D, sdO, SV, sQg, RS, 0, 32 * w, CH, lane);
+    mfma_block<true, false, 2, 2>(D, sdU, SV, sW, RS, 0, 32 * w, CH, lane);
     __syncthreads();
   }
-  if (dh0) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      *reinterpret_cast<float4*>(dh0 + sbase + 32 * m) = make_float4(D[4 * m], D[4 * m + 1], D[4 * m + 2], D[4 * m + 3]);
-  }
+  if (dh0) slice_to_global(D, dh0 + sbase, v0, w, li, lg);
 }
 
 // ---------------------------------------------------------------------------
-// dense products per (chunk, v-head).  4 x 8 tiles of 64 x 128 results:
-// rows 4 (tid >> 4) .., columns 8 (tid & 15) ..; 4 x 4 tiles of 64 x 64
-// results: rows 4 (tid >> 4) .., columns 4 (tid & 15) ..
-__device__ __forceinline__ void store_tile8(float* g, int gs, const float (&a)[4][8], int r0, int c0, float sc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; j += 4)
-      *reinterpret_cast<float4*>(g + (size_t)(r0 + i) * gs + c0 + j) =
-          make_float4(sc * a[i][j], sc * a[i][j + 1], sc * a[i][j + 2], sc * a[i][j + 3]);
-}
-
+// dense products per (chunk, v-head), on the fp32 MFMA (16x16x4).  Lane
+// (li = lane & 15, lg = lane >> 4) feeds A[li][k + lg] and B[k + lg][li] and
+// receives C[4 lg + r][li] (r < 4) of each 16 x 16 tile.  Wave w computes
+// rows 32 (w >> 1) .. +31 of every product: columns 64 (w & 1) .. +63 of the
+// 128-wide ones, 32 (w & 1) .. +31 of the 64-wide ones.
 __global__ void __launch_bounds__(256)
 kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_out,
                      const uint16_t* __restrict__ beta, const int64_t* __restrict__ cu,
@@ -728,7 +729,8 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   float* pb = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS;
   float* sb = pb + PB_FLOATS;
   float* gb = sb + SB_FLOATS;
-  const int r0 = 4 * (tid >> 4), c0 = 8 * (tid & 15), q0 = 4 * (tid & 15);
+  const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int R0 = 32 * (w >> 1), C0 = 64 * (w & 1), Q0 = 32 * (w & 1);
 
   // 1. dO, dU, U and the first half of S (rows v < 64)
   load_bf16_tile128(B0, d_out + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
@@ -737,41 +739,55 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   load_tile128(B3, sb + SB_H, DK, tid);
   __syncthreads();
   // 2. dQg = dO S and dW = -dU S, contracting over v in two halves
-  float dqg[4][8], dw[4][8];
-  zero_tile(dqg);
-  zero_tile(dw);
-  mm_tile<false, false, 8>(dqg, B0, RS, B3, RS, r0, c0, 64);
-  mm_tile<false, false, 8>(dw, B1, RS, B3, RS, r0, c0, 64);
+  f32x4 dqg[2][4], dw[2][4];
+  zero_block(dqg);
+  zero_block(dw);
+  mfma_block<false, false, 2, 4>(dqg, B0, RS, B3, RS, R0, C0, 64, lane);
+  mfma_block<false, false, 2, 4>(dw, B1, RS, B3, RS, R0, C0, 64, lane);
   __syncthreads();
   load_tile128(B3, sb + SB_H + 64 * DK, DK, tid);
   __syncthreads();
-  mm_tile<false, false, 8>(dqg, B0 + 64, RS, B3, RS, r0, c0, 64);
-  mm_tile<false, false, 8>(dw, B1 + 64, RS, B3, RS, r0, c0, 64);
-  store_tile8(gb + GB_DQG, DK, dqg, r0, c0, 1.0f);
+  mfma_block<false, false, 2, 4>(dqg, B0 + 64, RS, B3, RS, R0, C0, 64, lane);
+  mfma_block<false, false, 2, 4>(dw, B1 + 64, RS, B3, RS, R0, C0, 64, lane);
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gb[GB_DQG + BLK_ROW(R0, m, r) * DK + BLK_COL(C0, n)] = dqg[m][n][r];
   // 3. dAqk = dO U^T, lower triangle including the diagonal
   {
-    float a[4][4];
-    zero_tile(a);
-    mm_tile<false, true, 4>(a, B0, RS, B2, RS, r0, q0, DV);
+    f32x4 a[2][2];
+    zero_block(a);
+    mfma_block<false, true, 2, 2>(a, B0, RS, B2, RS, R0, Q0, DV, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<float4*>(gb + GB_DAQK + (r0 + i) * 64 + q0) =
-          make_float4(q0 <= r0 + i ? a[i][0] : 0.0f, q0 + 1 <= r0 + i ? a[i][1] : 0.0f,
-                      q0 + 2 <= r0 + i ? a[i][2] : 0.0f, q0 + 3 <= r0 + i ? a[i][3] : 0.0f);
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = BLK_ROW(R0, m, r), j = BLK_COL(Q0, n);
+          gb[GB_DAQK + i * 64 + j] = j <= i ? a[m][n][r] : 0.0f;
+        }
   }
   __syncthreads();
   // 4. dKd = U dS', contracting over v in two halves; dgn = colsum(dS' . S)
   {
-    float dkd[4][8];
-    zero_tile(dkd);
+    f32x4 dkd[2][4];
+    zero_block(dkd);
     load_tile128(B3, sb + SB_DH, DK, tid);
     __syncthreads();
-    mm_tile<false, false, 8>(dkd, B2, RS, B3, RS, r0, c0, 64);
+    mfma_block<false, false, 2, 4>(dkd, B2, RS, B3, RS, R0, C0, 64, lane);
     __syncthreads();
     load_tile128(B3, sb + SB_DH + 64 * DK, DK, tid);
     __syncthreads();
-    mm_tile<false, false, 8>(dkd, B2 + 64, RS, B3, RS, r0, c0, 64);
-    store_tile8(gb + GB_DKD, DK, dkd, r0, c0, 1.0f);
+    mfma_block<false, false, 2, 4>(dkd, B2 + 64, RS, B3, RS, R0, C0, 64, lane);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gb[GB_DKD + BLK_ROW(R0, m, r) * DK + BLK_COL(C0, n)] = dkd[m][n][r];
     const int c = tid & 127, half = tid >> 7;
     float acc = 0.0f;
     for (int vv = 64 * half; vv < 64 * half + 64; ++vv) acc += sb[SB_DH + vv * DK + c] * sb[SB_H + vv * DK + c];
@@ -781,11 +797,11 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   if (tid < DK) gb[GB_DGN + tid] = sRed[tid] + sRed[DK + tid];
   // 5. B3 <- dW, B0 <- Kg, B2 <- V, sT <- T, sB <- beta
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int j = 0; j < 8; j += 4)
-      *reinterpret_cast<float4*>(B3 + (r0 + i) * RS + c0 + j) =
-          make_float4(-dw[i][j], -dw[i][j + 1], -dw[i][j + 2], -dw[i][j + 3]);
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) B3[BLK_ROW(R0, m, r) * RS + BLK_COL(C0, n)] = -dw[m][n][r];
   load_tile128(B0, pb + PB_KG, DK, tid);
   load_bf16_tile128(B2, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
   load_tile64(sT, pb + PB_T, tid);
@@ -799,31 +815,36 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   }
   __syncthreads();
   // 6. dM = dU V^T + dW Kg^T;  dV = M^T dU;  dKg = M^T dW  (M = T diag(b))
-  float dm[4][4];
-  zero_tile(dm);
-  mm_tile<false, true, 4>(dm, B1, RS, B2, RS, r0, q0, DV);
-  mm_tile<false, true, 4>(dm, B3, RS, B0, RS, r0, q0, DK);
+  f32x4 dm[2][2];
+  zero_block(dm);
+  mfma_block<false, true, 2, 2>(dm, B1, RS, B2, RS, R0, Q0, DV, lane);
+  mfma_block<false, true, 2, 2>(dm, B3, RS, B0, RS, R0, Q0, DK, lane);
   {
-    float a[4][8];
-    zero_tile(a);
-    mm_tile<true, false, 8>(a, sT, QS, B1, RS, r0, c0, CH);
+    f32x4 a[2][4];
+    zero_block(a);
+    mfma_block<true, false, 2, 4>(a, sT, QS, B1, RS, R0, C0, CH, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = r0 + i;
-      if (t < L.len) {
-        float* d = dv + ((size_t)(L.row0 + t) * Hv + h) * DV + c0;
-        *reinterpret_cast<float4*>(d) = make_float4(sB[t] * a[i][0], sB[t] * a[i][1], sB[t] * a[i][2], sB[t] * a[i][3]);
-        *reinterpret_cast<float4*>(d + 4) =
-            make_float4(sB[t] * a[i][4], sB[t] * a[i][5], sB[t] * a[i][6], sB[t] * a[i][7]);
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = BLK_ROW(R0, m, r);
+        if (t < L.len) {
+          float* d = dv + ((size_t)(L.row0 + t) * Hv + h) * DV;
+#pragma unroll
+          for (int n = 0; n < 4; ++n) d[BLK_COL(C0, n)] = sB[t] * a[m][n][r];
+        }
       }
-    }
-    zero_tile(a);
-    mm_tile<true, false, 8>(a, sT, QS, B3, RS, r0, c0, CH);
+    zero_block(a);
+    mfma_block<true, false, 2, 4>(a, sT, QS, B3, RS, R0, C0, CH, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) a[i][j] *= sB[r0 + i];
-    store_tile8(gb + GB_DKG, DK, a, r0, c0, 1.0f);
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = BLK_ROW(R0, m, r);
+          gb[GB_DKG + t * DK + BLK_COL(C0, n)] = sB[t] * a[m][n][r];
+        }
   }
   __syncthreads();
   // 7. db_j = sum_i dM[i][j] T[i][j];  dT = dM diag(b);  dAkk = -(T^T dT T^T) strictly lower
@@ -831,12 +852,15 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   float* sDT = B2;  // [64][QS]
   float* sX = B3;   // [64][QS]
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sDM[(r0 + i) * QS + q0 + j] = dm[i][j];
-      sDT[(r0 + i) * QS + q0 + j] = dm[i][j] * sB[q0 + j];
-    }
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = BLK_ROW(R0, m, r), j = BLK_COL(Q0, n);
+        sDM[i * QS + j] = dm[m][n][r];
+        sDT[i * QS + j] = dm[m][n][r] * sB[j];
+      }
   __syncthreads();
   if (tid < CH) {
     float acc = 0.0f;
@@ -844,22 +868,28 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
     gb[GB_DB + tid] = acc;
   }
   {
-    float a[4][4];
-    zero_tile(a);
-    mm_tile<true, false, 4>(a, sT, QS, sDT, QS, r0, q0, CH);
+    f32x4 a[2][2];
+    zero_block(a);
+    mfma_block<true, false, 2, 2>(a, sT, QS, sDT, QS, R0, Q0, CH, lane);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sX[(r0 + i) * QS + q0 + j] = a[i][j];
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sX[BLK_ROW(R0, m, r) * QS + BLK_COL(Q0, n)] = a[m][n][r];
     __syncthreads();
-    zero_tile(a);
-    mm_tile<false, true, 4>(a, sX, QS, sT, QS, r0, q0, CH);
+    zero_block(a);
+    mfma_block<false, true, 2, 2>(a, sX, QS, sT, QS, R0, Q0, CH, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<float4*>(gb + GB_DAKK + (r0 + i) * 64 + q0) =
-          make_float4(q0 < r0 + i ? -a[i][0] : 0.0f, q0 + 1 < r0 + i ? -a[i][1] : 0.0f,
-                      q0 + 2 < r0 + i ? -a[i][2] : 0.0f, q0 + 3 < r0 + i ? -a[i][3] : 0.0f);
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = BLK_ROW(R0, m, r), j = BLK_COL(Q0, n);
+          gb[GB_DAKK + i * 64 + j] = j < i ? -a[m][n][r] : 0.0f;
+        }
   }
 }
 
