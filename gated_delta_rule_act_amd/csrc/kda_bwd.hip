@@ -231,11 +231,13 @@ __device__ __forceinline__ void load_bf16_tile128(float* s, const uint16_t* g, s
 }
 
 // Per chunk: q, k normalised (the output scale is applied by the callers),
-// beta, and G = cumulative
-// log2-decay of the chunk (rows past the sequence end: zero inputs, beta 0,
-// zero decay).  Thread t: row t >> 2, channels 32 (t & 3) .. +31.
+// beta, and the chunk's cumulative log2-decay G, kept as a 16-row block-local
+// inclusive sum sG plus the four block totals sBt[4][128]: every exponent is
+// then composed from sums of nearby decays, never formed as the difference of
+// two large cumulative values.  Rows past the sequence end: zero inputs,
+// beta 0, zero decay.  Thread t: row t >> 2, channels 32 (t & 3) .. +31.
 template <int MODE>
-__device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* sG, float* sB, const uint16_t* q,
+__device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* sG, float* sBt, float* sB, const uint16_t* q,
                                                   const uint16_t* k, const uint16_t* g, const uint16_t* beta,
                                                   const float* A_log, const float* dt_bias, int Hqk, int Hv, int h,
                                                   int hq, int64_t row0, int len, float scale, float lb, int flags,
@@ -287,20 +289,40 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
     sB[r] = b;
   }
   __syncthreads();
-  // inclusive cumulative sum over the 64 rows of each channel: thread t owns
-  // channel t & 127 and rows 32 (t >> 7) .. +31, then the second half adds
-  // the first half's total
+  // block-local inclusive sums: thread t owns channel t & 127 and the two
+  // 16-row blocks 2 (t >> 7), 2 (t >> 7) + 1
   {
-    const int c = tid & 127, half = tid >> 7;
-    float run = 0.0f;
-    for (int rr = 32 * half; rr < 32 * half + 32; ++rr) { run += sG[rr * RS + c]; sG[rr * RS + c] = run; }
-    __syncthreads();
-    if (half == 1) {
-      const float base = sG[31 * RS + c];
-      for (int rr = 32; rr < 64; ++rr) sG[rr * RS + c] += base;
+    const int c = tid & 127;
+    for (int B = 2 * (tid >> 7); B < 2 * (tid >> 7) + 2; ++B) {
+      float run = 0.0f;
+      for (int rr = 16 * B; rr < 16 * B + 16; ++rr) { run += sG[rr * RS + c]; sG[rr * RS + c] = run; }
+      sBt[B * DK + c] = run;
     }
   }
   __syncthreads();
+}
+
+// Exponents from the block-local form (all in log2 units, all <= 0):
+//   G_i - G_j, i >= j, i in block I, j in block J
+__device__ __forceinline__ float gdiff(const float* sG, const float* sBt, int i, int j, int c) {
+  const int I = i >> 4, J = j >> 4;
+  float d = sG[i * RS + c];
+  if (I == J) return d - sG[j * RS + c];
+  d += sBt[J * DK + c] - sG[j * RS + c];
+  for (int B = J + 1; B < I; ++B) d += sBt[B * DK + c];
+  return d;
+}
+//   G_i (from the chunk start) and G_last - G_i
+__device__ __forceinline__ float gabs(const float* sG, const float* sBt, int i, int c) {
+  float d = sG[i * RS + c];
+  for (int B = 0; B < (i >> 4); ++B) d += sBt[B * DK + c];
+  return d;
+}
+__device__ __forceinline__ float gtail(const float* sG, const float* sBt, int i, int c) {
+  const int I = i >> 4;
+  float d = sBt[I * DK + c] - sG[i * RS + c];
+  for (int B = I + 1; B < 4; ++B) d += sBt[B * DK + c];
+  return d;
 }
 
 // ---------------------------------------------------------------------------
@@ -365,6 +387,7 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   __shared__ __attribute__((aligned(16))) float sT[CH * QS];
   __shared__ float sB[CH];
   __shared__ float sX[16 * 17];
+  __shared__ __attribute__((aligned(16))) float sBt[4 * DK];
   const int x = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const ChunkLoc L = chunk_loc(x, cu, chunk_off, T, N);
   if (L.len == 0) return;
@@ -372,64 +395,68 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   float* pb = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS;
 
   for (int e = tid; e < CH * QS; e += 256) { sA[e] = 0.0f; sAq[e] = 0.0f; sT[e] = 0.0f; }
-  load_chunk_inputs<MODE>(sK, sQ, sG, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, scale, lb,
-                          flags, tid, nullptr, nullptr);
+  load_chunk_inputs<MODE>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, scale,
+                          lb, flags, tid, nullptr, nullptr);
 
-  // Akk and Aqk: 4 x 4 pair blocks (I >= J) of the 64 x 64 lower triangle,
-  // each split over two adjacent threads by channel half.
-  for (int item = tid; item < 272; item += 256) {
-    const int b = item >> 1, half = item & 1;
-    int I = (int)((sqrtf(8.0f * b + 1.0f) - 1.0f) * 0.5f);
-    while ((I + 1) * (I + 2) / 2 <= b) ++I;
-    while (I * (I + 1) / 2 > b) --I;
-    const int J = b - I * (I + 1) / 2, i0 = 4 * I, j0 = 4 * J;
-    float akk[4][4], aqk[4][4];
-    zero_tile(akk);
-    zero_tile(aqk);
-    for (int c = 64 * half; c < 64 * half + 64; c += 4) {
-      float Ki[4][4], Qi[4][4], Gi[4][4], Kj[4][4], Gj[4][4];
+  // Akk and Aqk.  Wave w owns row block w.  Blocks J < w factor through the
+  // row before block w: e^(G_i - G_j) = e^(sG_i) e^(Bt_J - sG_j + sum_{J<B<w} Bt_B),
+  // both exponents <= 0, so each is one fp32 MFMA product over the channels
+  // (A = K or Q times the row factor, B = K times the column factor); the
+  // diagonal block is summed pair by pair.
+  {
+    const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
+    if (w > 0) {
+      f32x4 akk[3], aqk[3];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float4 a0 = *reinterpret_cast<const float4*>(sK + (i0 + r) * RS + c);
-        const float4 a1 = *reinterpret_cast<const float4*>(sQ + (i0 + r) * RS + c);
-        const float4 a2 = *reinterpret_cast<const float4*>(sG + (i0 + r) * RS + c);
-        const float4 b0 = *reinterpret_cast<const float4*>(sK + (j0 + r) * RS + c);
-        const float4 b1 = *reinterpret_cast<const float4*>(sG + (j0 + r) * RS + c);
-        Ki[r][0] = a0.x; Ki[r][1] = a0.y; Ki[r][2] = a0.z; Ki[r][3] = a0.w;
-        Qi[r][0] = a1.x; Qi[r][1] = a1.y; Qi[r][2] = a1.z; Qi[r][3] = a1.w;
-        Gi[r][0] = a2.x; Gi[r][1] = a2.y; Gi[r][2] = a2.z; Gi[r][3] = a2.w;
-        Kj[r][0] = b0.x; Kj[r][1] = b0.y; Kj[r][2] = b0.z; Kj[r][3] = b0.w;
-        Gj[r][0] = b1.x; Gj[r][1] = b1.y; Gj[r][2] = b1.z; Gj[r][3] = b1.w;
+      for (int J = 0; J < 3; ++J) { akk[J] = f32x4{0.f, 0.f, 0.f, 0.f}; aqk[J] = akk[J]; }
+      const int i = 16 * w + li;
+      for (int kc = 0; kc < DK; kc += 4) {
+        const int c = kc + lg;
+        const float fr = ex2(sG[i * RS + c]);
+        const float xa = sK[i * RS + c] * fr, ya = sQ[i * RS + c] * fr;
+#pragma unroll
+        for (int J = 0; J < 3; ++J) {
+          if (J < w) {  // uniform per wave
+            const int j = 16 * J + li;
+            float mid = sBt[J * DK + c];
+            for (int B = J + 1; B < w; ++B) mid += sBt[B * DK + c];
+            const float zb = sK[j * RS + c] * ex2(mid - sG[j * RS + c]);
+            akk[J] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, zb, akk[J], 0, 0, 0);
+            aqk[J] = __builtin_amdgcn_mfma_f32_16x16x4f32(ya, zb, aqk[J], 0, 0, 0);
+          }
+        }
       }
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
+      for (int J = 0; J < 3; ++J)
+        if (J < w)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            // i >= j gives an exponent <= 0; the upper half of a diagonal
-            // block is masked below, so its exponent is only kept finite
-            const float e = ex2(fminf(Gi[ii][cc] - Gj[jj][cc], 0.0f)) * Kj[jj][cc];
-            akk[ii][jj] += Ki[ii][cc] * e;
-            aqk[ii][jj] += Qi[ii][cc] * e;
+          for (int r = 0; r < 4; ++r) {
+            const int ii = 16 * w + 4 * lg + r, jj = 16 * J + li;
+            sA[ii * QS + jj] = sB[ii] * akk[J][r];
+            sAq[ii * QS + jj] = scale * aqk[J][r];
           }
     }
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        akk[ii][jj] += __shfl_xor(akk[ii][jj], 1);
-        aqk[ii][jj] += __shfl_xor(aqk[ii][jj], 1);
+    // diagonal block: the 136 pairs i >= j of block w, two or three per lane
+    for (int pr = lane; pr < 136; pr += 64) {
+      int ii = (int)((sqrtf(8.0f * pr + 1.0f) - 1.0f) * 0.5f);
+      while ((ii + 1) * (ii + 2) / 2 <= pr) ++ii;
+      while (ii * (ii + 1) / 2 > pr) --ii;
+      const int jj = pr - ii * (ii + 1) / 2;
+      const int i = 16 * w + ii, j = 16 * w + jj;
+      float akk = 0.0f, aqk = 0.0f;
+      for (int c = 0; c < DK; c += 4) {
+        const float4 ki = *reinterpret_cast<const float4*>(sK + i * RS + c);
+        const float4 qi = *reinterpret_cast<const float4*>(sQ + i * RS + c);
+        const float4 gi = *reinterpret_cast<const float4*>(sG + i * RS + c);
+        const float4 kj = *reinterpret_cast<const float4*>(sK + j * RS + c);
+        const float4 gj = *reinterpret_cast<const float4*>(sG + j * RS + c);
+        const float e0 = kj.x * ex2(fminf(gi.x - gj.x, 0.0f)), e1 = kj.y * ex2(fminf(gi.y - gj.y, 0.0f));
+        const float e2 = kj.z * ex2(fminf(gi.z - gj.z, 0.0f)), e3 = kj.w * ex2(fminf(gi.w - gj.w, 0.0f));
+        akk += ki.x * e0 + ki.y * e1 + ki.z * e2 + ki.w * e3;
+        aqk += qi.x * e0 + qi.y * e1 + qi.z * e2 + qi.w * e3;
       }
-    if (half == 0) {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int i = i0 + ii, j = j0 + jj;
-          sA[i * QS + j] = j < i ? sB[i] * akk[ii][jj] : 0.0f;
-          sAq[i * QS + j] = j <= i ? scale * aqk[ii][jj] : 0.0f;
-        }
+      sA[i * QS + j] = jj < ii ? sB[i] * akk : 0.0f;
+      sAq[i * QS + j] = scale * aqk;
     }
   }
   __syncthreads();
@@ -478,11 +505,12 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       const int c = c0 + i;
       const float4 kk = *reinterpret_cast<const float4*>(sK + r * RS + c);
       const float4 qq = *reinterpret_cast<const float4*>(sQ + r * RS + c);
-      const float4 gg = *reinterpret_cast<const float4*>(sG + r * RS + c);
-      const float4 gl = *reinterpret_cast<const float4*>(sG + 63 * RS + c);
-      const float4 eg = make_float4(ex2(gg.x), ex2(gg.y), ex2(gg.z), ex2(gg.w));
-      const float4 kd = make_float4(kk.x * ex2(gl.x - gg.x), kk.y * ex2(gl.y - gg.y), kk.z * ex2(gl.z - gg.z),
-                                    kk.w * ex2(gl.w - gg.w));
+      const float4 eg = make_float4(ex2(gabs(sG, sBt, r, c)), ex2(gabs(sG, sBt, r, c + 1)),
+                                    ex2(gabs(sG, sBt, r, c + 2)), ex2(gabs(sG, sBt, r, c + 3)));
+      const float4 kd = make_float4(kk.x * ex2(gtail(sG, sBt, r, c)), kk.y * ex2(gtail(sG, sBt, r, c + 1)),
+                                    kk.z * ex2(gtail(sG, sBt, r, c + 2)), kk.w * ex2(gtail(sG, sBt, r, c + 3)));
+      const float4 gl = make_float4(gabs(sG, sBt, 63, c), gabs(sG, sBt, 63, c + 1), gabs(sG, sBt, 63, c + 2),
+                                    gabs(sG, sBt, 63, c + 3));
       const float4 kg = make_float4(kk.x * eg.x, kk.y * eg.y, kk.z * eg.z, kk.w * eg.w);
       *reinterpret_cast<float4*>(pb + PB_KD + r * DK + c) = kd;
       *reinterpret_cast<float4*>(pb + PB_QG + r * DK + c) =
@@ -895,8 +923,17 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // pairwise terms, elementwise factors, decay sum, gate, norms and beta.
-// Thread tile: rows 4 (tid >> 4) .. +3, channels 8 (tid & 15) .. +7; the 16
-// threads of a row group are 16 consecutive lanes of one wave.
+// Wave w owns row block w (rows 16 w .. +15) in MFMA accumulator layout:
+// element (row 16 w + 4 lg + r, channel 16 n + li) in acc[n][r].  With
+// a = dAkk, b = dAqk (masked), E_ij = e^(G_i - G_j) per channel:
+//   R1_i = sum_j a_ij K_j E_ij,   R2_i = sum_j b_ij K_j E_ij      (row side)
+//   C_j  = sum_i (beta_i a_ij K_i + b_ij scale Q_i) E_ij           (column side)
+//   dK = beta R1 + C,  d(scale Q) = R2,  dG = beta K R1 + scale Q R2 - K C,
+//   dbeta_i (from Akk) = sum_c K_ic R1_ic.
+// Pairs in different 16-row blocks I > J factor through p = 16 I - 1, the
+// row before block I: E_ij = e^(G_i - G_p) e^(G_p - G_j), both exponents <= 0,
+// so those sums are fp32 MFMA products with one factor on each operand;
+// pairs inside a block are summed directly.
 __device__ __forceinline__ float sum16(float x) {
   x += __shfl_xor(x, 1);
   x += __shfl_xor(x, 2);
@@ -922,6 +959,7 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   __shared__ float sRq[CH], sRk[CH];
   __shared__ float sCol[16 * DK];
   __shared__ float sRed[8];
+  __shared__ __attribute__((aligned(16))) float sBt[4 * DK];
   const int x = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const ChunkLoc L = chunk_loc(x, cu, chunk_off, T, N);
   float* pb = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS;
@@ -933,121 +971,169 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
   const int hq = h / (Hv / Hqk);
   float rq, rk;
-  load_chunk_inputs<MODE>(sK, sQ, sG, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, scale, lb,
-                          flags, tid, &rq, &rk);
+  load_chunk_inputs<MODE>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, scale,
+                          lb, flags, tid, &rq, &rk);
   if ((tid & 3) == 0) { sRq[tid >> 2] = rq; sRk[tid >> 2] = rk; }
   load_tile64(sDA, gb + GB_DAKK, tid);
   load_tile64(sDQ, gb + GB_DAQK, tid);
   __syncthreads();
 
-  const int r0 = 4 * (tid >> 4), c0 = 8 * (tid & 15);
-  float Ko[4][8], Qo[4][8], Go[4][8];
+  const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int rbase = 16 * w + 4 * lg;  // own rows rbase + r
+  float Ko[8][4], Qo[8][4], Go[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int n = 0; n < 8; ++n)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      Ko[i][j] = sK[(r0 + i) * RS + c0 + j];
-      Qo[i][j] = sQ[(r0 + i) * RS + c0 + j];
-      Go[i][j] = sG[(r0 + i) * RS + c0 + j];
+    for (int r = 0; r < 4; ++r) {
+      const int e = (rbase + r) * RS + 16 * n + li;
+      Ko[n][r] = sK[e];
+      Qo[n][r] = sQ[e];
+      Go[n][r] = sG[e];
     }
-  float dK[4][8], dQ[4][8], dG[4][8], dbk[4];
-  zero_tile(dK);
-  zero_tile(dQ);
-  zero_tile(dG);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dbk[i] = 0.0f;
-  const float bo[4] = {sB[r0], sB[r0 + 1], sB[r0 + 2], sB[r0 + 3]};
 
-  // row side: own rows i, partners j <= i
-  for (int j = 0; j < r0 + 4; ++j) {
-    float Kj[8], Gj[8];
+  // ---- row side: R1, R2 for own rows
+  f32x4 R1[8], R2[8];
 #pragma unroll
-    for (int c = 0; c < 8; c += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(sK + j * RS + c0 + c);
-      const float4 b = *reinterpret_cast<const float4*>(sG + j * RS + c0 + c);
-      Kj[c] = a.x; Kj[c + 1] = a.y; Kj[c + 2] = a.z; Kj[c + 3] = a.w;
-      Gj[c] = b.x; Gj[c + 1] = b.y; Gj[c + 2] = b.z; Gj[c + 3] = b.w;
+  for (int n = 0; n < 8; ++n) { R1[n] = f32x4{0.f, 0.f, 0.f, 0.f}; R2[n] = R1[n]; }
+  if (w > 0) {
+    // p = 16 w - 1: G_i - G_p = sG_i;  G_p - G_j = Bt_J - sG_j + sum_{J<B<w} Bt_B
+    for (int J = 0; J < w; ++J) {
+      float mid[8];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        float o = sBt[J * DK + 16 * n + li];
+        for (int B = J + 1; B < w; ++B) o += sBt[B * DK + 16 * n + li];
+        mid[n] = o;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int j = 16 * J + 4 * kk + lg;
+        const float a = sDA[(16 * w + li) * QS + j], b = sDQ[(16 * w + li) * QS + j];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const int c = 16 * n + li;
+          const float z = sK[j * RS + c] * ex2(mid[n] - sG[j * RS + c]);
+          R1[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, z, R1[n], 0, 0, 0);
+          R2[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(b, z, R2[n], 0, 0, 0);
+        }
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float dak = sDA[(r0 + i) * QS + j], daq = sDQ[(r0 + i) * QS + j];  // zero where j > i (or j >= i for Akk)
-      const float a = bo[i] * dak;
-      float sb = 0.0f;
+    for (int n = 0; n < 8; ++n)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float t1 = Kj[c] * ex2(fminf(Go[i][c] - Gj[c], 0.0f));
-        dK[i][c] += a * t1;
-        dQ[i][c] += daq * t1;
-        dG[i][c] += (a * Ko[i][c] + daq * scale * Qo[i][c]) * t1;
-        sb += Ko[i][c] * t1;
+      for (int r = 0; r < 4; ++r) {
+        const float f = ex2(Go[n][r]);
+        R1[n][r] *= f;
+        R2[n][r] *= f;
       }
-      dbk[i] += dak * sb;
+  }
+  for (int jj = 0; jj < 16; ++jj) {
+    const int j = 16 * w + jj;
+    float a[4], b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { a[r] = sDA[(rbase + r) * QS + j]; b[r] = sDQ[(rbase + r) * QS + j]; }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int c = 16 * n + li;
+      const float kj = sK[j * RS + c], gj = sG[j * RS + c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = kj * ex2(fminf(Go[n][r] - gj, 0.0f));
+        R1[n][r] += a[r] * e;
+        R2[n][r] += b[r] * e;
+      }
     }
   }
-  // column side: own rows j, partners i >= j
-  for (int i = r0; i < CH; ++i) {
-    float Ki[8], Qi[8], Gi[8];
+
+  // ---- column side: C for own rows (as j)
+  f32x4 Cc[8];
 #pragma unroll
-    for (int c = 0; c < 8; c += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(sK + i * RS + c0 + c);
-      const float4 b = *reinterpret_cast<const float4*>(sQ + i * RS + c0 + c);
-      const float4 d = *reinterpret_cast<const float4*>(sG + i * RS + c0 + c);
-      Ki[c] = a.x; Ki[c + 1] = a.y; Ki[c + 2] = a.z; Ki[c + 3] = a.w;
-      Qi[c] = b.x; Qi[c + 1] = b.y; Qi[c + 2] = b.z; Qi[c + 3] = b.w;
-      Gi[c] = d.x; Gi[c + 1] = d.y; Gi[c + 2] = d.z; Gi[c + 3] = d.w;
+  for (int n = 0; n < 8; ++n) Cc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int I = w + 1; I < 4; ++I) {
+    f32x4 X[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) X[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int i = 16 * I + 4 * kk + lg;
+      const float a = sB[i] * sDA[i * QS + 16 * w + li], b = sDQ[i * QS + 16 * w + li];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int c = 16 * n + li;
+        const float f = ex2(sG[i * RS + c]);
+        X[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sK[i * RS + c] * f, X[n], 0, 0, 0);
+        X[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(b, scale * sQ[i * RS + c] * f, X[n], 0, 0, 0);
+      }
     }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      float mid = sBt[w * DK + 16 * n + li];
+      for (int B = w + 1; B < I; ++B) mid += sBt[B * DK + 16 * n + li];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Cc[n][r] += X[n][r] * ex2(mid - Go[n][r]);
+    }
+  }
+  for (int ii = 0; ii < 16; ++ii) {
+    const int i = 16 * w + ii;
     const float bi = sB[i];
+    float a[4], b[4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const float a = bi * sDA[i * QS + r0 + jj], daq = sDQ[i * QS + r0 + jj];
+    for (int r = 0; r < 4; ++r) { a[r] = bi * sDA[i * QS + rbase + r]; b[r] = sDQ[i * QS + rbase + r]; }
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float t2 = (a * Ki[c] + daq * scale * Qi[c]) * ex2(fminf(Gi[c] - Go[jj][c], 0.0f));
-        dK[jj][c] += t2;
-        dG[jj][c] -= t2 * Ko[jj][c];
-      }
+    for (int n = 0; n < 8; ++n) {
+      const int c = 16 * n + li;
+      const float ki = sK[i * RS + c], qi = scale * sQ[i * RS + c], gi = sG[i * RS + c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Cc[n][r] += (a[r] * ki + b[r] * qi) * ex2(fminf(gi - Go[n][r], 0.0f));
     }
   }
 
-  // elementwise factors: Qg = Q e^G, Kg = K e^G, Kd = K e^(G_last - G), gn = e^G_last
+  // ---- combine: dK, dQ (w.r.t. scale q_hat), dG; dbeta from Akk
+  float dK[8][4], dQ[8][4], dG[8][4], dbk[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dbk[r] = 0.0f;
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float bo = sB[rbase + r];
+      dK[n][r] = bo * R1[n][r] + Cc[n][r];
+      dQ[n][r] = R2[n][r];
+      dG[n][r] = bo * Ko[n][r] * R1[n][r] + scale * Qo[n][r] * R2[n][r] - Ko[n][r] * Cc[n][r];
+      dbk[r] += Ko[n][r] * R1[n][r];
+    }
+
+  // ---- elementwise factors: Qg = scale Q e^G, Kg = K e^G, Kd = K e^(G_last - G), gn = e^G_last
   float colKd[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) colKd[c] = 0.0f;
+  for (int n = 0; n < 8; ++n) colKd[n] = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + i;
+  for (int n = 0; n < 8; ++n) {
+    const int c = 16 * n + li;
 #pragma unroll
-    for (int c = 0; c < 8; c += 4) {
-      const float4 dqg = *reinterpret_cast<const float4*>(gb + GB_DQG + r * DK + c0 + c);
-      const float4 dkg = *reinterpret_cast<const float4*>(gb + GB_DKG + r * DK + c0 + c);
-      const float4 dkd = *reinterpret_cast<const float4*>(gb + GB_DKD + r * DK + c0 + c);
-      const float vq[4] = {dqg.x, dqg.y, dqg.z, dqg.w}, vg[4] = {dkg.x, dkg.y, dkg.z, dkg.w},
-                  vd[4] = {dkd.x, dkd.y, dkd.z, dkd.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int cc = c + e;
-        const float eg = ex2(Go[i][cc]), ed = ex2(sG[63 * RS + c0 + cc] - Go[i][cc]);
-        dQ[i][cc] += vq[e] * eg;
-        dK[i][cc] += vg[e] * eg + vd[e] * ed;
-        const float kd = vd[e] * Ko[i][cc] * ed;
-        dG[i][cc] += (vq[e] * scale * Qo[i][cc] + vg[e] * Ko[i][cc]) * eg - kd;
-        colKd[cc] += kd;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int row = rbase + r;
+      const float vq = gb[GB_DQG + row * DK + c], vg = gb[GB_DKG + row * DK + c], vd = gb[GB_DKD + row * DK + c];
+      const float eg = ex2(gabs(sG, sBt, row, c)), ed = ex2(gtail(sG, sBt, row, c));
+      dQ[n][r] += vq * eg;
+      dK[n][r] += vg * eg + vd * ed;
+      const float kd = vd * Ko[n][r] * ed;
+      dG[n][r] += (vq * scale * Qo[n][r] + vg * Ko[n][r]) * eg - kd;
+      colKd[n] += kd;
     }
   }
-  // dG of the chunk's last row gains sum_t dKd . Kd and dgn . gn (column sums
-  // over the 16 row groups through LDS)
+  // dG of the chunk's last row gains sum_t dKd . Kd and dgn . gn
 #pragma unroll
-  for (int c = 0; c < 8; ++c) sCol[(tid >> 4) * DK + c0 + c] = colKd[c];
-  __syncthreads();  // also: every read of sQ and sK above is done
+  for (int n = 0; n < 8; ++n) sCol[(4 * w + lg) * DK + 16 * n + li] = colKd[n];
+  __syncthreads();  // also: every read of sQ above is done
   // dG -> sQ, then the reverse cumulative sum over rows gives d a per token
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int n = 0; n < 8; ++n)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) sQ[(r0 + i) * RS + c0 + c] = dG[i][c];
+    for (int r = 0; r < 4; ++r) sQ[(rbase + r) * RS + 16 * n + li] = dG[n][r];
   __syncthreads();
   if (tid < DK) {
-    float sum = gb[GB_DGN + tid] * ex2(sG[63 * RS + tid]);
+    float sum = gb[GB_DGN + tid] * ex2(gabs(sG, sBt, 63, tid));
     for (int rg = 0; rg < 16; ++rg) sum += sCol[rg * DK + tid];
     sQ[63 * RS + tid] += sum;
   }
@@ -1064,79 +1150,70 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
   __syncthreads();
 
-  // gate: a = f(x), x = g + dt_bias;  norms;  beta
+  // ---- gate: a = f(x), x = g + dt_bias;  norms;  beta
   const float A_exp = (MODE == KDA_GATE_PREGATED || A_log == nullptr) ? 1.0f : __expf(A_log[h]);
+  const bool norm = flags & KDA_FLAG_QK_L2NORM;
   float colDt[8], dA = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) colDt[c] = 0.0f;
-  const bool norm = flags & KDA_FLAG_QK_L2NORM;
+  for (int n = 0; n < 8; ++n) colDt[n] = 0.0f;
+  float dtb[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + i;
-    const bool ok = r < L.len;  // uniform over the 16 lanes of the row group
-    const size_t row = (size_t)(L.row0 + r);
-    float gv[8];
-    {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (ok) u = *reinterpret_cast<const uint4*>(g + (row * Hv + h) * DK + c0);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  for (int n = 0; n < 8; ++n) dtb[n] = dt_bias ? dt_bias[(size_t)h * DK + 16 * n + li] : 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { gv[2 * e] = __uint_as_float(w[e] << 16); gv[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u); }
-    }
+  for (int r = 0; r < 4; ++r) {
+    const int row = rbase + r;
+    const bool ok = row < L.len;  // uniform over the 16 lanes of the row
+    const size_t trow = (size_t)(L.row0 + row);
     float dgo[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float da = sQ[r * RS + c0 + c];
+    for (int n = 0; n < 8; ++n) {
+      const int c = 16 * n + li;
+      const float da = sQ[row * RS + c];
+      const float gv = ok ? bf2f(g[(trow * Hv + h) * DK + c]) : 0.0f;
       float a, dadx, dadA;
-      gate_fwd_bwd<MODE>(gv[c] + (dt_bias ? dt_bias[(size_t)h * DK + c0 + c] : 0.0f), A_exp, lb, a, dadx, dadA);
+      gate_fwd_bwd<MODE>(gv + dtb[n], A_exp, lb, a, dadx, dadA);
       // below the decay floor the factor e^a is exactly zero in fp32
       if (a * kLog2e < kMinLog2Decay) dadx = dadA = 0.0f;
-      dgo[c] = ok ? da * dadx : 0.0f;
-      colDt[c] += dgo[c];
+      dgo[n] = ok ? da * dadx : 0.0f;
+      colDt[n] += dgo[n];
       if (ok) dA += da * dadA;
     }
     // y = q/|q| (the operand is scale y): dq = r (dy - y (y . dy)), dy = scale dQ
     float yq = 0.0f, yk = 0.0f;
-    const float rqi = sRq[r], rki = sRk[r];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      yq += Qo[i][c] * (scale * dQ[i][c]);
-      yk += Ko[i][c] * dK[i][c];
+    for (int n = 0; n < 8; ++n) {
+      yq += Qo[n][r] * (scale * dQ[n][r]);
+      yk += Ko[n][r] * dK[n][r];
     }
     yq = norm ? sum16(yq) : 0.0f;
     yk = norm ? sum16(yk) : 0.0f;
-    float dbsum = sum16(dbk[i]);
+    const float dbsum = sum16(dbk[r]);
     if (ok) {
-      float dqo[8], dko[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        dqo[c] = rqi * (scale * dQ[i][c] - Qo[i][c] * yq);
-        dko[c] = rki * (dK[i][c] - Ko[i][c] * yk);
-      }
-      // with grouped heads the q/k gradients go to a per-v-head buffer
+      const float rqi = sRq[row], rki = sRk[row];
       const int hh = qk_heads_out == Hqk ? hq : h;
-      float* pq = dq + (row * qk_heads_out + hh) * DK + c0;
-      float* pk = dk + (row * qk_heads_out + hh) * DK + c0;
-      *reinterpret_cast<float4*>(pq) = make_float4(dqo[0], dqo[1], dqo[2], dqo[3]);
-      *reinterpret_cast<float4*>(pq + 4) = make_float4(dqo[4], dqo[5], dqo[6], dqo[7]);
-      *reinterpret_cast<float4*>(pk) = make_float4(dko[0], dko[1], dko[2], dko[3]);
-      *reinterpret_cast<float4*>(pk + 4) = make_float4(dko[4], dko[5], dko[6], dko[7]);
-      float* pg = dg + (row * Hv + h) * DK + c0;
-      *reinterpret_cast<float4*>(pg) = make_float4(dgo[0], dgo[1], dgo[2], dgo[3]);
-      *reinterpret_cast<float4*>(pg + 4) = make_float4(dgo[4], dgo[5], dgo[6], dgo[7]);
-      if ((tid & 15) == 0) {
-        const float db = gb[GB_DB + r] + dbsum;
-        const float b = sB[r];
-        dbeta[row * Hv + h] = (flags & KDA_FLAG_BETA_IS_PROB) ? db : db * b * (1.0f - b);
+      float* pq = dq + (trow * qk_heads_out + hh) * DK;
+      float* pk = dk + (trow * qk_heads_out + hh) * DK;
+      float* pg = dg + (trow * Hv + h) * DK;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int c = 16 * n + li;
+        pq[c] = rqi * (scale * dQ[n][r] - Qo[n][r] * yq);
+        pk[c] = rki * (dK[n][r] - Ko[n][r] * yk);
+        pg[c] = dgo[n];
+      }
+      if (li == 0) {
+        const float db = gb[GB_DB + row] + dbsum;
+        const float b = sB[row];
+        dbeta[trow * Hv + h] = (flags & KDA_FLAG_BETA_IS_PROB) ? db : db * b * (1.0f - b);
       }
     }
   }
   // per-chunk partials of ddt_bias (column sums) and dA_log
 #pragma unroll
-  for (int c = 0; c < 8; ++c) sCol[(tid >> 4) * DK + c0 + c] = colDt[c];
+  for (int n = 0; n < 8; ++n) sCol[(4 * w + lg) * DK + 16 * n + li] = colDt[n];
   dA += __shfl_xor(dA, 1); dA += __shfl_xor(dA, 2); dA += __shfl_xor(dA, 4); dA += __shfl_xor(dA, 8);
   dA += __shfl_xor(dA, 16); dA += __shfl_xor(dA, 32);
-  if ((tid & 63) == 0) sRed[tid >> 6] = dA;
+  if (lane == 0) sRed[w] = dA;
   __syncthreads();
   if (tid < DK) {
     float sum = 0.0f;
