@@ -234,3 +234,53 @@ def test_workspace_holds_segment_scratch(lib):
     p4 = base_params(B=1, T=4096, H_qk=2, H_v=2, segments=4)
     extra = lib.kda_fwd_workspace_size(ctypes.byref(p4)) - lib.kda_fwd_workspace_size(ctypes.byref(p1))
     assert extra == 3 * 2 * 4 * 128 * 128 * 4    # entry states, carries, maps: fp32 per (chain, segment)
+
+
+def bwd_call(lib, p, drop=(), shift=None, ws=None, extra=None):
+    ptrs = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, cu=None,
+                h0=FAKE if p.init_state_dtype else None, dout=FAKE, dhT=None, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE,
+                dbeta=FAKE, dA=FAKE, ddt=FAKE, dh0=FAKE, ws=FAKE)
+    ptrs.update(extra or {})
+    for name in ((drop,) if isinstance(drop, str) else drop):
+        ptrs[name] = None
+    if shift:
+        ptrs[shift] = ptrs[shift] + 2
+    need = lib.kda_bwd_workspace_size(ctypes.byref(p))
+    order = ["q", "k", "v", "g", "beta", "A_log", "dt_bias", "cu", "h0", "dout", "dhT", "dq", "dk", "dv", "dg",
+             "dbeta", "dA", "ddt", "dh0", "ws"]
+    args = [None if ptrs[n] is None else ctypes.c_void_p(ptrs[n]) for n in order]
+    return lib.kda_bwd(ctypes.byref(p), *args, ctypes.c_size_t(need if ws is None else ws), None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(params=dict(K=64)), -2),
+    (dict(params=dict(gate_mode=3)), -8),
+    (dict(params=dict(flags=4)), -8),
+    (dict(params=dict(gate_mode=kda.GATE_SAFE_SIGMOID, lower_bound=0.0)), -4),
+    (dict(params=dict(gate_mode=kda.GATE_PREGATED), drop=("dA", "ddt")), -8),          # dt_bias given
+    (dict(params=dict(gate_mode=kda.GATE_PREGATED), drop=("dt_bias", "dA")), -8),      # ddt_bias given
+    (dict(params=dict(gate_mode=kda.GATE_PREGATED), drop=("dt_bias", "ddt")), -8),     # dA_log given
+    (dict(drop="A_log"), -1),                                                          # softplus needs A_log
+    (dict(params=dict(gate_mode=kda.GATE_SAFE_SIGMOID), drop="A_log"), -8),            # dA_log without A_log
+    (dict(drop="q"), -1), (dict(drop="dout"), -1), (dict(drop="dq"), -1), (dict(drop="dk"), -1),
+    (dict(drop="dv"), -1), (dict(drop="dg"), -1), (dict(drop="dbeta"), -1), (dict(drop="h0"), -1),
+    (dict(shift="dout"), -5), (dict(shift="dg"), -5), (dict(shift="ddt"), -5),
+    (dict(extra=dict(dhT=FAKE + 4)), -5), (dict(shift="dh0"), -5),
+    (dict(ws=16), -6), (dict(drop="ws"), -6), (dict(shift="ws"), -5),
+])
+def test_bwd_entry_rejects_before_launch(lib, case, code):
+    # only rejections: a valid call would launch, and these tests run without a GPU
+    p = base_params(**case.get("params", {}))
+    assert bwd_call(lib, p, case.get("drop", ()), case.get("shift"), case.get("ws"), case.get("extra")) == code, \
+        kda.last_error()
+    assert kda.last_error() != ""
+
+
+def test_bwd_workspace_size(lib):
+    size = lambda **kw: lib.kda_bwd_workspace_size(ctypes.byref(base_params(**kw)))
+    assert size(K=64) == 0
+    a, b = size(B=1, T=1000, H_qk=2, H_v=2), size(B=1, T=2000, H_qk=2, H_v=2)
+    assert 0 < a < b
+    # per (v-head, chunk) fp32 intermediates, plus per-v-head q/k gradient buffers with grouped heads
+    mha, gva = size(B=2, T=640, H_qk=4, H_v=4), size(B=2, T=640, H_qk=2, H_v=4)
+    assert gva - mha == 2 * 2 * 640 * 4 * 128 * 4

@@ -152,3 +152,34 @@ def test_bwd_medium_sampled():
     gpu = run_gpu_bwd(inp, d_out, dhT)
     ref = run_oracle_bwd(inp, d_out, dhT)
     compare(gpu, ref, "medium", inp)
+
+
+def test_bwd_headline_workload_sampled():
+    # the bench's backward configuration (B=2, T=8192, H=32, safe gate lb=-5),
+    # checked on sampled (sequence, head) pairs: every gradient of the pair's
+    # v-head (dq, dk of its q/k head: grouped heads are 1 here) against the
+    # oracle on that pair alone, plus finiteness of every output
+    inp = W.workload(3)
+    d_out, dhT = W.make_grads(inp, seed=1003)
+    U.log("[gpu] bwd workload 3 full size")
+    gpu = run_gpu_bwd(inp, d_out, dhT)
+    for n in NAMES:
+        if gpu.get(n) is not None:
+            assert np.isfinite(gpu[n]).all(), n
+    f = oracle.bf16_to_f64
+    for n, h in ((0, 0), (1, 31), (1, 7)):
+        sl = lambda a: np.ascontiguousarray(a[n:n + 1, :, h:h + 1])
+        ref = oracle.bwd(f(sl(inp.q)), f(sl(inp.k)), f(sl(inp.v)), f(sl(inp.g)),
+                         f(np.ascontiguousarray(inp.beta[n:n + 1, :, h:h + 1])), inp.A_log[h:h + 1],
+                         inp.dt_bias[h:h + 1], f(sl(d_out)), dhT[n:n + 1, h:h + 1].astype(np.float64),
+                         scale=inp.scale, lower_bound=inp.lower_bound, gate_mode=inp.gate_mode, flags=inp.flags,
+                         initial_state=inp.initial_state_f64()[n:n + 1, h:h + 1])
+        errs = {}
+        for name, a in (("dq", gpu["dq"][n:n + 1, :, h:h + 1]), ("dk", gpu["dk"][n:n + 1, :, h:h + 1]),
+                        ("dv", gpu["dv"][n:n + 1, :, h:h + 1]), ("dg", gpu["dg"][n:n + 1, :, h:h + 1]),
+                        ("dbeta", gpu["dbeta"][n:n + 1, :, h:h + 1]), ("dh0", gpu["dh0"][n:n + 1, h:h + 1])):
+            b = ref[name]
+            errs[name] = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+        U.log(f"    pair n={n} h={h} {errs}")
+        for name, e in errs.items():
+            assert e <= GRAD_REL, (n, h, name, e)
