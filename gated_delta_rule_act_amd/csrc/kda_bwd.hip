@@ -498,27 +498,34 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     *reinterpret_cast<float4*>(pb + PB_T + r * 64 + c) = *reinterpret_cast<const float4*>(sT + r * QS + c);
     *reinterpret_cast<float4*>(pb + PB_AQK + r * 64 + c) = *reinterpret_cast<const float4*>(sAq + r * QS + c);
   }
-  // Kd, Qg, Kg, gn (own elements: row tid >> 2, channels 32 (tid & 3) ..)
-  {
-    const int r = tid >> 2, c0 = 32 * (tid & 3);
-    for (int i = 0; i < 32; i += 4) {
-      const int c = c0 + i;
-      const float4 kk = *reinterpret_cast<const float4*>(sK + r * RS + c);
-      const float4 qq = *reinterpret_cast<const float4*>(sQ + r * RS + c);
-      const float4 eg = make_float4(ex2(gabs(sG, sBt, r, c)), ex2(gabs(sG, sBt, r, c + 1)),
-                                    ex2(gabs(sG, sBt, r, c + 2)), ex2(gabs(sG, sBt, r, c + 3)));
-      const float4 kd = make_float4(kk.x * ex2(gtail(sG, sBt, r, c)), kk.y * ex2(gtail(sG, sBt, r, c + 1)),
-                                    kk.z * ex2(gtail(sG, sBt, r, c + 2)), kk.w * ex2(gtail(sG, sBt, r, c + 3)));
-      const float4 gl = make_float4(gabs(sG, sBt, 63, c), gabs(sG, sBt, 63, c + 1), gabs(sG, sBt, 63, c + 2),
-                                    gabs(sG, sBt, 63, c + 3));
-      const float4 kg = make_float4(kk.x * eg.x, kk.y * eg.y, kk.z * eg.z, kk.w * eg.w);
-      *reinterpret_cast<float4*>(pb + PB_KD + r * DK + c) = kd;
-      *reinterpret_cast<float4*>(pb + PB_QG + r * DK + c) =
-          make_float4(scale * qq.x * eg.x, scale * qq.y * eg.y, scale * qq.z * eg.z, scale * qq.w * eg.w);
-      *reinterpret_cast<float4*>(pb + PB_KG + r * DK + c) = kg;
-      *reinterpret_cast<float4*>(sK + r * RS + c) = kg;  // sK now holds Kg
-      if (r == 0) *reinterpret_cast<float4*>(pb + PB_GN + c) = make_float4(ex2(gl.x), ex2(gl.y), ex2(gl.z), ex2(gl.w));
-    }
+  // Kd, Qg, Kg, gn: element e = tid + 256 i is row e >> 5, channels 4 (e & 31)
+  // .. +3, so the 32 lanes of a row store 512 contiguous bytes
+  __syncthreads();  // Kg overwrites sK rows that other threads still read above
+  float4 kgv[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int e = tid + 256 * it, r = e >> 5, c = 4 * (e & 31);
+    const float4 kk = *reinterpret_cast<const float4*>(sK + r * RS + c);
+    const float4 qq = *reinterpret_cast<const float4*>(sQ + r * RS + c);
+    float eg[4], ed[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { eg[u] = ex2(gabs(sG, sBt, r, c + u)); ed[u] = ex2(gtail(sG, sBt, r, c + u)); }
+    *reinterpret_cast<float4*>(pb + PB_KD + r * DK + c) =
+        make_float4(kk.x * ed[0], kk.y * ed[1], kk.z * ed[2], kk.w * ed[3]);
+    *reinterpret_cast<float4*>(pb + PB_QG + r * DK + c) =
+        make_float4(scale * qq.x * eg[0], scale * qq.y * eg[1], scale * qq.z * eg[2], scale * qq.w * eg[3]);
+    kgv[it] = make_float4(kk.x * eg[0], kk.y * eg[1], kk.z * eg[2], kk.w * eg[3]);
+    *reinterpret_cast<float4*>(pb + PB_KG + r * DK + c) = kgv[it];
+  }
+  if (tid < 32)
+    *reinterpret_cast<float4*>(pb + PB_GN + 4 * tid) =
+        make_float4(ex2(gabs(sG, sBt, 63, 4 * tid)), ex2(gabs(sG, sBt, 63, 4 * tid + 1)),
+                    ex2(gabs(sG, sBt, 63, 4 * tid + 2)), ex2(gabs(sG, sBt, 63, 4 * tid + 3)));
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {  // sK now holds Kg
+    const int e = tid + 256 * it, r = e >> 5, c = 4 * (e & 31);
+    *reinterpret_cast<float4*>(sK + r * RS + c) = kgv[it];
   }
   __syncthreads();
   // sQ <- V; sT <- M = T diag(b)
@@ -585,6 +592,13 @@ __device__ __forceinline__ void slice_to_lds(const f32x4 (&S)[2][2], float* s, i
       for (int r = 0; r < 4; ++r) s[(16 * m + 4 * lg + r) * RS + 32 * w + 16 * n + li] = S[m][n][r];
 }
 
+// XCD-aware decode: the BNS slices of one chain share (id mod 8), so they run
+// on one XCD and read the chain's chunk operands through its L2.
+__device__ __forceinline__ void chain_slice(int id, int& chain, int& slice) {
+  chain = (id / (8 * BNS)) * 8 + (id & 7);
+  slice = (id >> 3) % BNS;
+}
+
 __global__ void __launch_bounds__(256)
 kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ chunk_off, const void* __restrict__ h0,
                       int init_dtype, int T, int N, int Hv, int mc, float* __restrict__ ws) {
@@ -592,7 +606,8 @@ kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ ch
   __shared__ __attribute__((aligned(16))) float sKd[CH * RS];
   __shared__ __attribute__((aligned(16))) float sU[CH * SV];
   __shared__ __attribute__((aligned(16))) float sS[BV * RS];
-  const int chain = blockIdx.x / BNS, slice = blockIdx.x % BNS;
+  int chain, slice;
+  chain_slice(blockIdx.x, chain, slice);
   if (chain >= N * Hv) return;
   const int n = chain / Hv, h = chain % Hv, v0 = BV * slice, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
@@ -663,7 +678,8 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
   __shared__ __attribute__((aligned(16))) float sdO[CH * SV];
   __shared__ __attribute__((aligned(16))) float sdU[CH * SV];
   __shared__ __attribute__((aligned(16))) float sdh[BV * RS];
-  const int chain = blockIdx.x / BNS, slice = blockIdx.x % BNS;
+  int chain, slice;
+  chain_slice(blockIdx.x, chain, slice);
   if (chain >= N * Hv) return;
   const int n = chain / Hv, h = chain % Hv, v0 = BV * slice, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
@@ -1307,10 +1323,11 @@ void launch_bwd(const kda_fwd_params* p, const void* q, const void* k, const voi
     hipLaunchKernelGGL(kda_bwd_prep_kernel<MODE>, cg, dim3(256), 0, st, qq, kk, vv, gg, bb, A_log, dt_bias, cu,
                        chunk_off, p->T, p->num_seqs, p->H_qk, p->H_v, (int)mc, p->scale, p->lower_bound, p->flags, ws);
   if (chains > 0) {
-    hipLaunchKernelGGL(kda_bwd_fstate_kernel, dim3((unsigned)(chains * BNS)), dim3(256), 0, st, cu, chunk_off, h0,
-                       p->init_state_dtype, p->T, p->num_seqs, p->H_v, (int)mc, ws);
-    hipLaunchKernelGGL(kda_bwd_bstate_kernel, dim3((unsigned)(chains * BNS)), dim3(256), 0, st, dd, dhT, dh0, cu,
-                       chunk_off, p->T, p->num_seqs, p->H_v, (int)mc, ws);
+    const dim3 sg((unsigned)(((chains + 7) / 8) * 8 * BNS));  // groups of 8 chains, BNS slices each
+    hipLaunchKernelGGL(kda_bwd_fstate_kernel, sg, dim3(256), 0, st, cu, chunk_off, h0, p->init_state_dtype, p->T,
+                       p->num_seqs, p->H_v, (int)mc, ws);
+    hipLaunchKernelGGL(kda_bwd_bstate_kernel, sg, dim3(256), 0, st, dd, dhT, dh0, cu, chunk_off, p->T, p->num_seqs,
+                       p->H_v, (int)mc, ws);
   }
   if (mc > 0) {
     hipLaunchKernelGGL(kda_bwd_dense_kernel, cg, dim3(256), 0, st, vv, dd, bb, cu, chunk_off, p->T, p->num_seqs,
