@@ -331,12 +331,95 @@ __device__ __forceinline__ float gtail(const float* sG, const float* sBt, int i,
 // C[4 lg + r][li] (r < 4) of each 16 x 16 tile.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// acc[m][n] += the (16 m, 16 n) tile of A B over k < kdim, operands fp32 in LDS:
+// acc[m][n] += the (16 m, 16 n) tile of A B over k < kdim (a multiple of
+// 32), operands fp32 in LDS:
 //   A(r, k) = AT ? sA[k * lda + r] : sA[r * lda + k]
 //   B(k, c) = BT ? sB[c * ldb + k] : sB[k * ldb + c]
+// on the bf16 MFMA (16x16x32) with each operand split as x = hi + lo (both
+// bf16, round to nearest even) and three products hi.hi + hi.lo + lo.hi:
+// fp32-level accuracy (relative ~2^-16 per product) at the bf16 matrix rate.
+// Lane (li, g = lane >> 4) feeds A[li][8 g .. 8 g + 7] and B[8 g .. +7][li].
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = (__bf16)x[e];
+    hi[e] = h;
+    lo[e] = (__bf16)(x[e] - (float)h);
+  }
+}
+
+// Which 8 of a 32-wide k step lane group g feeds is a free choice as long as
+// A and B agree.  When both operands are read along rows (A(r, k) with k
+// contiguous, B^T likewise) the group takes 8 consecutive k, two 16-byte LDS
+// reads per operand; otherwise it takes k = 4 e + g, so that the strided reads
+// of the four groups fall on different banks.
 template <bool AT, bool BT, int MT, int NT>
 __device__ __forceinline__ void mfma_block(f32x4 (&acc)[MT][NT], const float* sA, int lda, const float* sB, int ldb,
                                            int row0, int col0, int kdim, int lane) {
+  constexpr bool kContig = !AT && BT;
+  const int li = lane & 15, g = lane >> 4;
+#pragma unroll 2
+  for (int k0 = 0; k0 < kdim; k0 += 32) {
+    bf16x8_t ah[MT], al[MT], bh[NT], bl[NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int r = row0 + 16 * m + li;
+      float x[8];
+      if constexpr (kContig) {
+        const float4 u0 = *reinterpret_cast<const float4*>(sA + r * lda + k0 + 8 * g);
+        const float4 u1 = *reinterpret_cast<const float4*>(sA + r * lda + k0 + 8 * g + 4);
+        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w; x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = k0 + 4 * e + g;
+          x[e] = AT ? sA[k * lda + r] : sA[r * lda + k];
+        }
+      }
+      split8(x, ah[m], al[m]);
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int c = col0 + 16 * n + li;
+      float x[8];
+      if constexpr (kContig) {
+        const float4 u0 = *reinterpret_cast<const float4*>(sB + c * ldb + k0 + 8 * g);
+        const float4 u1 = *reinterpret_cast<const float4*>(sB + c * ldb + k0 + 8 * g + 4);
+        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w; x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = k0 + 4 * e + g;
+          x[e] = BT ? sB[c * ldb + k] : sB[k * ldb + c];
+        }
+      }
+      split8(x, bh[n], bl[n]);
+    }
+    // one product over all tiles at a time, so consecutive MFMAs write
+    // different accumulators and none waits on the previous one's result
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bh[n], acc[m][n], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bl[n], acc[m][n], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[m], bh[n], acc[m][n], 0, 0, 0);
+  }
+}
+
+// The same product on the fp32 MFMA (16x16x4): lane (li, lg) feeds
+// A[li][k + lg] and B[k + lg][li] for each 4-wide k step.  Used where the
+// operands are read across rows only and the chain of products is short.
+template <bool AT, bool BT, int MT, int NT>
+__device__ __forceinline__ void mfma_block_f32(f32x4 (&acc)[MT][NT], const float* sA, int lda, const float* sB,
+                                               int ldb, int row0, int col0, int kdim, int lane) {
   const int li = lane & 15, lg = lane >> 4;
 #pragma unroll 8
   for (int k = 0; k < kdim; k += 4) {
@@ -726,8 +809,8 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
     // dU rows 16 w .. +15:  Aqk^T dO  +  Kd dS'^T
     f32x4 dU[1][2];
     zero_block(dU);
-    mfma_block<true, false, 1, 2>(dU, sAq + 16 * w, QS, sdO, SV, 0, 0, CH, lane);
-    mfma_block<false, true, 1, 2>(dU, sKd + 16 * w * RS, RS, sdh, RS, 0, 0, DK, lane);
+    mfma_block_f32<true, false, 1, 2>(dU, sAq + 16 * w, QS, sdO, SV, 0, 0, CH, lane);
+    mfma_block_f32<false, true, 1, 2>(dU, sKd + 16 * w * RS, RS, sdh, RS, 0, 0, DK, lane);
 #pragma unroll
     for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
@@ -742,8 +825,8 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn) D[m][nn] *= gn[nn];
-    mfma_block<true, false, 2, 2>(D, sdO, SV, sQg, RS, 0, 32 * w, CH, lane);
-    mfma_block<true, false, 2, 2>(D, sdU, SV, sW, RS, 0, 32 * w, CH, lane);
+    mfma_block_f32<true, false, 2, 2>(D, sdO, SV, sQg, RS, 0, 32 * w, CH, lane);
+    mfma_block_f32<true, false, 2, 2>(D, sdU, SV, sW, RS, 0, 32 * w, CH, lane);
     __syncthreads();
   }
   if (dh0) slice_to_global(D, dh0 + sbase, v0, w, li, lg);
