@@ -20,11 +20,14 @@
 // per-token decay by a reverse cumulative sum, through the gate activation,
 // the L2 norms and the beta sigmoid to the raw inputs.
 //
-// Five launches (plus the chunk map for packed input), all fp32:
+// Six launches (plus the chunk map for packed input).  Values are fp32; the
+// contractions over LDS operands run on the bf16 MFMA with each operand split
+// into bf16 hi + lo (three products), or on the fp32 MFMA:
 //   kda_bwd_prep_kernel    per (chunk, v-head): norms, G, Akk and Aqk from
-//                          pairwise factors e^(G_i - G_j) (i >= j, so every
-//                          exponent is <= 0), T by blocked substitution, W,
-//                          Ubar, Kd, Qg, Kg, gn -> workspace.
+//                          factors e^(G_i - G_j) (i >= j, so every exponent is
+//                          <= 0; pairs in different 16-row blocks factored
+//                          through a reference row onto the MFMA), T by
+//                          blocked substitution, W, Ubar, Kd, Qg, Kg, gn -> workspace.
 //   kda_bwd_fstate_kernel  per (sequence, v-head, 32-row V slice), forward
 //                          over chunks: stores each chunk's entry state S and U.
 //   kda_bwd_bstate_kernel  per (sequence, v-head, V slice), backward over
@@ -53,7 +56,6 @@ constexpr int QS = 68;   // LDS row stride of 64-wide fp32 tiles
 constexpr int BV = 32;   // V rows per state workgroup
 constexpr int BNS = DV / BV;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kL2Eps = 1e-6f;
 constexpr float kMinLog2Decay = -1.0e4f;
 
@@ -143,60 +145,6 @@ __device__ __forceinline__ ChunkLoc chunk_loc(int x, const int64_t* cu, const in
   return L;
 }
 
-// acc[4][8] += A(r0 + i, k) B(k, c0 + j) over k < K4*4, A and B fp32 in LDS.
-//   A(r, k) = AT ? sA[k * lda + r] : sA[r * lda + k]
-//   B(k, c) = BT ? sB[c * ldb + k] : sB[k * ldb + c]
-template <bool AT, bool BT, int NC>
-__device__ __forceinline__ void mm_tile(float (&acc)[4][NC], const float* sA, int lda, const float* sB, int ldb,
-                                        int r0, int c0, int kdim) {
-  for (int k = 0; k < kdim; k += 4) {
-    float a[4][4];  // a[i][kk]
-    if constexpr (AT) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const float4 x = *reinterpret_cast<const float4*>(sA + (k + kk) * lda + r0);
-        a[0][kk] = x.x; a[1][kk] = x.y; a[2][kk] = x.z; a[3][kk] = x.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 x = *reinterpret_cast<const float4*>(sA + (r0 + i) * lda + k);
-        a[i][0] = x.x; a[i][1] = x.y; a[i][2] = x.z; a[i][3] = x.w;
-      }
-    }
-    float b[4][NC];  // b[kk][j]
-    if constexpr (BT) {
-#pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const float4 x = *reinterpret_cast<const float4*>(sB + (c0 + j) * ldb + k);
-        b[0][j] = x.x; b[1][j] = x.y; b[2][j] = x.z; b[3][j] = x.w;
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int j = 0; j < NC; j += 4) {
-          const float4 x = *reinterpret_cast<const float4*>(sB + (k + kk) * ldb + c0 + j);
-          b[kk][j] = x.x; b[kk][j + 1] = x.y; b[kk][j + 2] = x.z; b[kk][j + 3] = x.w;
-        }
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NC; ++j) acc[i][j] += a[i][kk] * b[kk][j];
-  }
-}
-
-template <int NC>
-__device__ __forceinline__ void zero_tile(float (&acc)[4][NC]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NC; ++j) acc[i][j] = 0.0f;
-}
-
 // 64 x 128 fp32 global tile (row stride gs floats) -> LDS rows of stride RS.
 __device__ __forceinline__ void load_tile128(float* s, const float* g, int gs, int tid) {
 #pragma unroll
@@ -240,7 +188,7 @@ template <int MODE>
 __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* sG, float* sBt, float* sB, const uint16_t* q,
                                                   const uint16_t* k, const uint16_t* g, const uint16_t* beta,
                                                   const float* A_log, const float* dt_bias, int Hqk, int Hv, int h,
-                                                  int hq, int64_t row0, int len, float scale, float lb, int flags,
+                                                  int hq, int64_t row0, int len, float lb, int flags,
                                                   int tid, float* rq_out, float* rk_out) {
   const int r = tid >> 2, c0 = 32 * (tid & 3);
   const bool ok = r < len;
@@ -302,16 +250,7 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
   __syncthreads();
 }
 
-// Exponents from the block-local form (all in log2 units, all <= 0):
-//   G_i - G_j, i >= j, i in block I, j in block J
-__device__ __forceinline__ float gdiff(const float* sG, const float* sBt, int i, int j, int c) {
-  const int I = i >> 4, J = j >> 4;
-  float d = sG[i * RS + c];
-  if (I == J) return d - sG[j * RS + c];
-  d += sBt[J * DK + c] - sG[j * RS + c];
-  for (int B = J + 1; B < I; ++B) d += sBt[B * DK + c];
-  return d;
-}
+// Exponents from the block-local form (log2 units):
 //   G_i (from the chunk start) and G_last - G_i
 __device__ __forceinline__ float gabs(const float* sG, const float* sBt, int i, int c) {
   float d = sG[i * RS + c];
@@ -478,8 +417,8 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   float* pb = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS;
 
   for (int e = tid; e < CH * QS; e += 256) { sA[e] = 0.0f; sAq[e] = 0.0f; sT[e] = 0.0f; }
-  load_chunk_inputs<MODE>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, scale,
-                          lb, flags, tid, nullptr, nullptr);
+  load_chunk_inputs<MODE>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, lb,
+                          flags, tid, nullptr, nullptr);
 
   // Akk and Aqk.  Wave w owns row block w.  Blocks J < w factor through the
   // row before block w: e^(G_i - G_j) = e^(sG_i) e^(Bt_J - sG_j + sum_{J<B<w} Bt_B),
@@ -1070,8 +1009,8 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
   const int hq = h / (Hv / Hqk);
   float rq, rk;
-  load_chunk_inputs<MODE>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, scale,
-                          lb, flags, tid, &rq, &rk);
+  load_chunk_inputs<MODE>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, lb,
+                          flags, tid, &rq, &rk);
   if ((tid & 3) == 0) { sRq[tid >> 2] = rq; sRk[tid >> 2] = rk; }
   load_tile64(sDA, gb + GB_DAKK, tid);
   load_tile64(sDQ, gb + GB_DAQK, tid);
