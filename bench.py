@@ -333,12 +333,16 @@ def run_backward(args, dev):
     d_out, dhT = W.make_grads(inp, seed=1000 + (3 if args.workload is None else args.workload))
     dev_dout = U.bf16_dev(d_out)
     dev_dhT = torch.from_numpy(dhT).to(dev)
+    nseg = kda.segments_of(kda.make_params(B=inp.B, T=inp.T, H_qk=inp.Hqk, H_v=inp.Hv, num_seqs=inp.N,
+                                           scale=inp.scale, lower_bound=inp.lower_bound, gate_mode=inp.gate_mode,
+                                           flags=inp.flags, segments=args.segments),
+                           packed=inp.cu_seqlens is not None)
     res = {}
 
     def step():
         res.update(kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"], inp.scale, dev_dout,
                            lower_bound=inp.lower_bound, gate_mode=inp.gate_mode, initial_state=d["h0"],
-                           d_final_state=dev_dhT, cu_seqlens=d["cu_seqlens"]))
+                           d_final_state=dev_dhT, cu_seqlens=d["cu_seqlens"], segments=args.segments))
 
     for _ in range(args.warmup):
         step()
@@ -360,7 +364,8 @@ def run_backward(args, dev):
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded numpy PCG64, see DESIGN.md)",
         "config": {"workload": inp.name, "B": inp.B, "T": inp.T, "H_qk": inp.Hqk, "H_v": inp.Hv, "K": inp.K,
-                   "V": inp.V, "gate": ["softplus", "safe_sigmoid", "pregated"][inp.gate_mode]},
+                   "V": inp.V, "gate": ["softplus", "safe_sigmoid", "pregated"][inp.gate_mode],
+                   "state_segments": nseg},
         "roofline": {"bound": "alu", "kernel": "kda_bwd (all launches)",
                      "achieved": flops / (ms * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, "traffic": None,

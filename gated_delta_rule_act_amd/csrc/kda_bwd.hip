@@ -32,6 +32,8 @@
 //                          over chunks: stores each chunk's entry state S and U.
 //   kda_bwd_bstate_kernel  per (sequence, v-head, V slice), backward over
 //                          chunks: stores dS' and dU, writes dS of the initial state.
+//                          Both state passes may cut a long chain into time
+//                          segments (carry, map and combine launches first).
 //   kda_bwd_dense_kernel   per (chunk, v-head): the dense products above.
 //   kda_bwd_pair_kernel    per (chunk, v-head): the pairwise terms, the
 //                          elementwise factors, the decay cumulative sum, gate,
@@ -42,11 +44,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "kda.h"
 #include "kda_internal.h"
+#include "kda_segment.h"
 
 namespace {
 using namespace kda_internal;
+using namespace kda_segment;
 
 constexpr int CH = 64;
 constexpr int DK = 128;
@@ -621,48 +627,140 @@ __device__ __forceinline__ void chain_slice(int id, int& chain, int& slice) {
   slice = (id >> 3) % BNS;
 }
 
+// Both state passes are affine in the carried matrix X (rows v, columns k):
+//   forward   S   -> S (Diag(gn) - W^T Kd) + Ubar^T Kd
+//   backward  dS' -> dS' (Diag(gn) - Kd^T W) + dO^T (Qg - Aqk W)
+// so a long chain is cut into time segments as in the forward state launch:
+// carries from zero, maps from the identity with zero inputs, a combine, then
+// the full pass of every segment from its true entry.  Segments are numbered
+// in processing order (the backward pass starts at the end of the sequence).
+// Jobs (chain, r), BNS workgroups per job:
+//   ST_FULL  r = 0..nseg-1 with the per-chunk stores, from the true entry
+//            (nseg == 1) or from S_in[r];
+//   ST_CARRY r = 0..nseg-2: r = 0 from the true entry (also copied to S_in[0])
+//            into S_in[1], r >= 1 from zero into F[r];
+//   ST_TRANS r = 1..nseg-2: from the identity into P[r].
+template <int KIND>
+__device__ __forceinline__ int jobs_per_chain(int nseg) {
+  return KIND == ST_FULL ? nseg : KIND == ST_CARRY ? nseg - 1 : nseg - 2;
+}
+
+struct StateJob {
+  int chain, r, n, h, v0;
+  int x0, c0, c1;  // workspace index of the chain's first chunk; this job's chunks c0 .. c1-1
+  int64_t bos;
+};
+
+// false: the workgroup has no job.  With `reverse`, processing segment r
+// covers time segment nseg-1-r.
+template <int KIND>
+__device__ __forceinline__ bool state_job(int id, const int64_t* cu, const int* chunk_off, int T, int N, int Hv,
+                                          int nseg, int seg_len, bool reverse, StateJob& j) {
+  const int jpc = jobs_per_chain<KIND>(nseg);
+  int job, slice;
+  chain_slice(id, job, slice);
+  if (job >= N * Hv * jpc) return false;
+  j.chain = job / jpc;
+  j.r = job % jpc + (KIND == ST_TRANS ? 1 : 0);
+  j.n = j.chain / Hv;
+  j.h = j.chain % Hv;
+  j.v0 = BV * slice;
+  int nc;
+  chain_chunks(j.n, chunk_off, cu, T, j.x0, nc, j.bos);
+  j.c0 = 0;
+  j.c1 = nc;
+  if (nseg > 1) {
+    const int ts = reverse ? nseg - 1 - j.r : j.r;
+    j.c0 = min(nc, ts * seg_len);
+    j.c1 = min(nc, j.c0 + seg_len);
+  }
+  return true;
+}
+
+__device__ __forceinline__ void slice_identity(f32x4 (&S)[2][2], int v0, int w, int li, int lg) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[m][n][r] = v0 + 16 * m + 4 * lg + r == 32 * w + 16 * n + li ? 1.0f : 0.0f;
+}
+
+// the slice of a [128][128] matrix: fp32, bf16, or zero (KDA_STATE_NONE / NULL)
+__device__ __forceinline__ void slice_from_global(f32x4 (&S)[2][2], const void* g, int dtype, int v0, int w, int li,
+                                                  int lg) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const size_t e = (size_t)(v0 + 16 * m + 4 * lg + r) * DK + 32 * w + 16 * n + li;
+        float x = 0.0f;
+        if (g != nullptr && dtype == KDA_STATE_F32) x = reinterpret_cast<const float*>(g)[e];
+        else if (g != nullptr && dtype == KDA_STATE_BF16) x = bf2f(reinterpret_cast<const uint16_t*>(g)[e]);
+        S[m][n][r] = x;
+      }
+}
+
+// Entry slice of a job; `entry` is the chain's true entry matrix.
+template <int KIND>
+__device__ __forceinline__ void job_entry(f32x4 (&S)[2][2], const StateJob& j, const void* entry, int dtype,
+                                          float* seg, int chains, int nseg, int w, int li, int lg) {
+  if (KIND == ST_TRANS) {
+    slice_identity(S, j.v0, w, li, lg);
+  } else if (KIND == ST_FULL && nseg > 1) {
+    slice_from_global(S, seg_mat(seg, chains, nseg, SEG_SIN, j.chain, j.r), KDA_STATE_F32, j.v0, w, li, lg);
+  } else if (KIND == ST_CARRY && j.r > 0) {
+    slice_from_global(S, nullptr, KDA_STATE_NONE, j.v0, w, li, lg);
+  } else {
+    slice_from_global(S, entry, dtype, j.v0, w, li, lg);
+    if (KIND == ST_CARRY) slice_to_global(S, seg_mat(seg, chains, nseg, SEG_SIN, j.chain, 0), j.v0, w, li, lg);
+  }
+}
+
+// where a carry or map job leaves its matrix
+template <int KIND>
+__device__ __forceinline__ float* job_exit(float* seg, int chains, int nseg, const StateJob& j) {
+  return KIND == ST_TRANS ? seg_mat(seg, chains, nseg, SEG_P, j.chain, j.r)
+         : j.r == 0       ? seg_mat(seg, chains, nseg, SEG_SIN, j.chain, 1)
+                          : seg_mat(seg, chains, nseg, SEG_F, j.chain, j.r);
+}
+
+template <int KIND>
 __global__ void __launch_bounds__(256)
 kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ chunk_off, const void* __restrict__ h0,
-                      int init_dtype, int T, int N, int Hv, int mc, float* __restrict__ ws) {
+                      int init_dtype, int T, int N, int Hv, int mc, float* __restrict__ ws, float* __restrict__ seg,
+                      int nseg, int seg_len) {
   __shared__ __attribute__((aligned(16))) float sW[CH * RS];
   __shared__ __attribute__((aligned(16))) float sKd[CH * RS];
   __shared__ __attribute__((aligned(16))) float sU[CH * SV];
   __shared__ __attribute__((aligned(16))) float sS[BV * RS];
-  int chain, slice;
-  chain_slice(blockIdx.x, chain, slice);
-  if (chain >= N * Hv) return;
-  const int n = chain / Hv, h = chain % Hv, v0 = BV * slice, tid = threadIdx.x;
+  StateJob j;
+  if (!state_job<KIND>(blockIdx.x, cu, chunk_off, T, N, Hv, nseg, seg_len, false, j)) return;
+  const int chains = N * Hv, h = j.h, v0 = j.v0, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
-  int x0, nc;
-  int64_t bos;
-  chain_chunks(n, chunk_off, cu, T, x0, nc, bos);
   f32x4 S[2][2];
-  const size_t sbase = ((size_t)n * Hv + h) * DV * DK;
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const size_t e = sbase + (size_t)(v0 + 16 * m + 4 * lg + r) * DK + 32 * w + 16 * nn + li;
-        float x = 0.0f;
-        if (init_dtype == KDA_STATE_F32) x = reinterpret_cast<const float*>(h0)[e];
-        else if (init_dtype == KDA_STATE_BF16) x = bf2f(reinterpret_cast<const uint16_t*>(h0)[e]);
-        S[m][nn][r] = x;
-      }
-  for (int c = 0; c < nc; ++c) {
-    const float* pb = ws + ((size_t)h * mc + x0 + c) * CHUNK_HEAD_FLOATS;
+  job_entry<KIND>(S, j, h0 == nullptr ? nullptr : reinterpret_cast<const char*>(h0) +
+                                                      (size_t)j.chain * DV * DK * (init_dtype == KDA_STATE_BF16 ? 2 : 4),
+                  init_dtype, seg, chains, nseg, w, li, lg);
+  for (int c = j.c0; c < j.c1; ++c) {
+    const float* pb = ws + ((size_t)h * mc + j.x0 + c) * CHUNK_HEAD_FLOATS;
     float* sb = const_cast<float*>(pb) + PB_FLOATS;
-    slice_to_global(S, sb + SB_H, v0, w, li, lg);
+    if constexpr (KIND == ST_FULL) slice_to_global(S, sb + SB_H, v0, w, li, lg);
     slice_to_lds(S, sS, w, li, lg);
     load_tile128(sW, pb + PB_W, DK, tid);
     load_tile128(sKd, pb + PB_KD, DK, tid);
-    // U rows 16 w .. +15 start from Ubar (lane layout of the product below)
+    // U rows 16 w .. +15 start from Ubar (lane layout of the product below);
+    // a map job has no inputs, Ubar = 0
     f32x4 U[1][2];
+    zero_block(U);
+    if constexpr (KIND != ST_TRANS) {
 #pragma unroll
-    for (int nn = 0; nn < 2; ++nn)
+      for (int nn = 0; nn < 2; ++nn)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) U[0][nn][r] = -pb[PB_UB + (16 * w + 4 * lg + r) * DV + v0 + 16 * nn + li];
+        for (int r = 0; r < 4; ++r) U[0][nn][r] = -pb[PB_UB + (16 * w + 4 * lg + r) * DV + v0 + 16 * nn + li];
+    }
     float gn[2];
 #pragma unroll
     for (int nn = 0; nn < 2; ++nn) gn[nn] = pb[PB_GN + 32 * w + 16 * nn + li];
@@ -676,7 +774,7 @@ kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ ch
         const int t = 16 * w + 4 * lg + r, vv = 16 * nn + li;
         const float u = -U[0][nn][r];
         sU[t * SV + vv] = u;
-        sb[SB_U + t * DV + v0 + vv] = u;
+        if constexpr (KIND == ST_FULL) sb[SB_U + t * DV + v0 + vv] = u;
       }
     __syncthreads();
     // S <- S Diag(gn) + U^T Kd:  A(v, t) = U[t][v],  B(t, k) = Kd[t][k]
@@ -687,12 +785,14 @@ kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ ch
     mfma_block<true, false, 2, 2>(S, sU, SV, sKd, RS, 0, 32 * w, CH, lane);
     __syncthreads();
   }
+  if constexpr (KIND != ST_FULL) slice_to_global(S, job_exit<KIND>(seg, chains, nseg, j), v0, w, li, lg);
 }
 
+template <int KIND>
 __global__ void __launch_bounds__(256)
 kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restrict__ dhT, float* __restrict__ dh0,
                       const int64_t* __restrict__ cu, const int* __restrict__ chunk_off, int T, int N, int Hv, int mc,
-                      float* __restrict__ ws) {
+                      float* __restrict__ ws, float* __restrict__ seg, int nseg, int seg_len) {
   __shared__ __attribute__((aligned(16))) float sAq[CH * QS];
   __shared__ __attribute__((aligned(16))) float sKd[CH * RS];
   __shared__ __attribute__((aligned(16))) float sQg[CH * RS];
@@ -700,55 +800,45 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
   __shared__ __attribute__((aligned(16))) float sdO[CH * SV];
   __shared__ __attribute__((aligned(16))) float sdU[CH * SV];
   __shared__ __attribute__((aligned(16))) float sdh[BV * RS];
-  int chain, slice;
-  chain_slice(blockIdx.x, chain, slice);
-  if (chain >= N * Hv) return;
-  const int n = chain / Hv, h = chain % Hv, v0 = BV * slice, tid = threadIdx.x;
+  StateJob j;
+  if (!state_job<KIND>(blockIdx.x, cu, chunk_off, T, N, Hv, nseg, seg_len, true, j)) return;
+  const int chains = N * Hv, h = j.h, v0 = j.v0, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
-  int x0, nc;
-  int64_t bos;
-  chain_chunks(n, chunk_off, cu, T, x0, nc, bos);
-  const int64_t seqlen = cu == nullptr ? (int64_t)T : cu[n + 1] - cu[n];
+  const int64_t seqlen = cu == nullptr ? (int64_t)T : cu[j.n + 1] - cu[j.n];
+  const size_t sbase = (size_t)j.chain * DV * DK;
   f32x4 D[2][2];
-  const size_t sbase = ((size_t)n * Hv + h) * DV * DK;
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        D[m][nn][r] = dhT ? dhT[sbase + (size_t)(v0 + 16 * m + 4 * lg + r) * DK + 32 * w + 16 * nn + li] : 0.0f;
-  for (int c = nc - 1; c >= 0; --c) {
-    const float* pb = ws + ((size_t)h * mc + x0 + c) * CHUNK_HEAD_FLOATS;
+  job_entry<KIND>(D, j, dhT == nullptr ? nullptr : dhT + sbase, KDA_STATE_F32, seg, chains, nseg, w, li, lg);
+  for (int c = j.c1 - 1; c >= j.c0; --c) {
+    const float* pb = ws + ((size_t)h * mc + j.x0 + c) * CHUNK_HEAD_FLOATS;
     float* sb = const_cast<float*>(pb) + PB_FLOATS;
-    const int64_t row0 = bos + (int64_t)c * CH;
+    const int64_t row0 = j.bos + (int64_t)c * CH;
     const int len = (int)min((int64_t)CH, seqlen - (int64_t)c * CH);
-    slice_to_global(D, sb + SB_DH, v0, w, li, lg);
+    if constexpr (KIND == ST_FULL) slice_to_global(D, sb + SB_DH, v0, w, li, lg);
     slice_to_lds(D, sdh, w, li, lg);
-    load_tile64(sAq, pb + PB_AQK, tid);
     load_tile128(sKd, pb + PB_KD, DK, tid);
-    load_tile128(sQg, pb + PB_QG, DK, tid);
     load_tile128(sW, pb + PB_W, DK, tid);
-    {
+    if constexpr (KIND != ST_TRANS) {
+      load_tile64(sAq, pb + PB_AQK, tid);
+      load_tile128(sQg, pb + PB_QG, DK, tid);
       // dO slice: token t = tid >> 2, columns 8 (tid & 3) .. +7 (bf16)
-      const int t = tid >> 2, j = 8 * (tid & 3);
+      const int t = tid >> 2, jj = 8 * (tid & 3);
       uint4 u = make_uint4(0, 0, 0, 0);
-      if (t < len) u = *reinterpret_cast<const uint4*>(d_out + ((size_t)(row0 + t) * Hv + h) * DV + v0 + j);
+      if (t < len) u = *reinterpret_cast<const uint4*>(d_out + ((size_t)(row0 + t) * Hv + h) * DV + v0 + jj);
       const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        sdO[t * SV + j + 2 * q] = __uint_as_float(wv[q] << 16);
-        sdO[t * SV + j + 2 * q + 1] = __uint_as_float(wv[q] & 0xffff0000u);
+        sdO[t * SV + jj + 2 * q] = __uint_as_float(wv[q] << 16);
+        sdO[t * SV + jj + 2 * q + 1] = __uint_as_float(wv[q] & 0xffff0000u);
       }
     }
     float gn[2];
 #pragma unroll
     for (int nn = 0; nn < 2; ++nn) gn[nn] = pb[PB_GN + 32 * w + 16 * nn + li];
     __syncthreads();
-    // dU rows 16 w .. +15:  Aqk^T dO  +  Kd dS'^T
+    // dU rows 16 w .. +15:  Aqk^T dO  +  Kd dS'^T  (a map job has dO = 0)
     f32x4 dU[1][2];
     zero_block(dU);
-    mfma_block_f32<true, false, 1, 2>(dU, sAq + 16 * w, QS, sdO, SV, 0, 0, CH, lane);
+    if constexpr (KIND != ST_TRANS) mfma_block_f32<true, false, 1, 2>(dU, sAq + 16 * w, QS, sdO, SV, 0, 0, CH, lane);
     mfma_block_f32<false, true, 1, 2>(dU, sKd + 16 * w * RS, RS, sdh, RS, 0, 0, DK, lane);
 #pragma unroll
     for (int nn = 0; nn < 2; ++nn)
@@ -756,7 +846,7 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * w + 4 * lg + r, vv = 16 * nn + li;
         sdU[t * SV + vv] = -dU[0][nn][r];
-        sb[SB_DU + t * DV + v0 + vv] = dU[0][nn][r];
+        if constexpr (KIND == ST_FULL) sb[SB_DU + t * DV + v0 + vv] = dU[0][nn][r];
       }
     __syncthreads();
     // dS = dS' Diag(gn) + dO^T Qg - dU^T W:  A(v, t) = dO[t][v] (then -dU[t][v])
@@ -764,11 +854,15 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int nn = 0; nn < 2; ++nn) D[m][nn] *= gn[nn];
-    mfma_block_f32<true, false, 2, 2>(D, sdO, SV, sQg, RS, 0, 32 * w, CH, lane);
+    if constexpr (KIND != ST_TRANS) mfma_block_f32<true, false, 2, 2>(D, sdO, SV, sQg, RS, 0, 32 * w, CH, lane);
     mfma_block_f32<true, false, 2, 2>(D, sdU, SV, sW, RS, 0, 32 * w, CH, lane);
     __syncthreads();
   }
-  if (dh0) slice_to_global(D, dh0 + sbase, v0, w, li, lg);
+  if constexpr (KIND == ST_FULL) {
+    if (dh0 && j.r == nseg - 1) slice_to_global(D, dh0 + sbase, v0, w, li, lg);
+  } else {
+    slice_to_global(D, job_exit<KIND>(seg, chains, nseg, j), v0, w, li, lg);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1263,12 +1357,10 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
 // q/k gradients summed over the v-heads sharing a q/k head; gate-parameter
 // partials summed over chunks.
-__global__ void __launch_bounds__(256)
-kda_bwd_reduce_qk_kernel(const float* __restrict__ dqv, const float* __restrict__ dkv, float* __restrict__ dq,
-                         float* __restrict__ dk, int64_t rows, int Hqk, int G) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one float4 of (row, hq)
-  const int64_t total = rows * Hqk * (DK / 4);
-  if (e >= total) return;
+// one float4 of (row, q/k head hq): the sum over its G v-heads
+__device__ __forceinline__ void reduce_qk_one(const float* __restrict__ dqv, const float* __restrict__ dkv,
+                                              float* __restrict__ dq, float* __restrict__ dk, int64_t e, int Hqk,
+                                              int G) {
   const int c4 = (int)(e % (DK / 4));
   const int64_t rh = e / (DK / 4);
   const int hq = (int)(rh % Hqk);
@@ -1282,6 +1374,15 @@ kda_bwd_reduce_qk_kernel(const float* __restrict__ dqv, const float* __restrict_
   }
   *reinterpret_cast<float4*>(dq + ((size_t)row * Hqk + hq) * DK + 4 * c4) = sq;
   *reinterpret_cast<float4*>(dk + ((size_t)row * Hqk + hq) * DK + 4 * c4) = sk;
+}
+
+// grid-stride over the float4s of dq and dk
+__global__ void __launch_bounds__(256)
+kda_bwd_reduce_qk_kernel(const float* __restrict__ dqv, const float* __restrict__ dkv, float* __restrict__ dq,
+                         float* __restrict__ dk, int64_t rows, int Hqk, int G) {
+  const int64_t total = rows * Hqk * (DK / 4);
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256)
+    reduce_qk_one(dqv, dkv, dq, dk, e, Hqk, G);
 }
 
 __global__ void __launch_bounds__(256)
@@ -1309,10 +1410,14 @@ kda_bwd_reduce_gate_kernel(const float* __restrict__ ws, int mc, float* __restri
 // host side
 namespace {
 
-size_t bwd_bytes(const kda_fwd_params* p, int64_t mc) {
-  size_t b = header_bytes(p) + (size_t)p->H_v * (size_t)mc * CHUNK_HEAD_FLOATS * sizeof(float);
-  if (p->H_v != p->H_qk) b += 2 * (size_t)p->B * (size_t)p->T * p->H_v * DK * sizeof(float);
-  return b;
+// header | per-chunk blocks | q/k gradients per v-head (grouped heads only) |
+// segment scratch (nseg > 1)
+size_t gqa_floats(const kda_fwd_params* p) {
+  return p->H_v != p->H_qk ? 2 * (size_t)p->B * (size_t)p->T * p->H_v * DK : 0;
+}
+size_t bwd_bytes(const kda_fwd_params* p, int64_t mc, int nseg) {
+  return header_bytes(p) + ((size_t)p->H_v * (size_t)mc * CHUNK_HEAD_FLOATS + gqa_floats(p)) * sizeof(float) +
+         seg_scratch_bytes(p, nseg);
 }
 
 template <int MODE>
@@ -1345,11 +1450,36 @@ void launch_bwd(const kda_fwd_params* p, const void* q, const void* k, const voi
     hipLaunchKernelGGL(kda_bwd_prep_kernel<MODE>, cg, dim3(256), 0, st, qq, kk, vv, gg, bb, A_log, dt_bias, cu,
                        chunk_off, p->T, p->num_seqs, p->H_qk, p->H_v, (int)mc, p->scale, p->lower_bound, p->flags, ws);
   if (chains > 0) {
-    const dim3 sg((unsigned)(((chains + 7) / 8) * 8 * BNS));  // groups of 8 chains, BNS slices each
-    hipLaunchKernelGGL(kda_bwd_fstate_kernel, sg, dim3(256), 0, st, cu, chunk_off, h0, p->init_state_dtype, p->T,
-                       p->num_seqs, p->H_v, (int)mc, ws);
-    hipLaunchKernelGGL(kda_bwd_bstate_kernel, sg, dim3(256), 0, st, dd, dhT, dh0, cu, chunk_off, p->T, p->num_seqs,
-                       p->H_v, (int)mc, ws);
+    float* seg = ws + (size_t)p->H_v * mc * CHUNK_HEAD_FLOATS + gqa_floats(p);
+    int seg_len;
+    const int nseg = seg_plan(p, packed, &seg_len);
+    // grid of a launch with `jobs` jobs: groups of 8 jobs, BNS slices each
+    auto grid = [](int64_t jobs) { return dim3((unsigned)(((jobs + 7) / 8) * 8 * BNS)); };
+    const dim3 cmb((unsigned)(chains * (SD / CMB_ROWS)));
+    const int N = p->num_seqs, H = p->H_v, T = p->T, idt = p->init_state_dtype;
+    if (nseg > 1) {
+      hipLaunchKernelGGL(kda_bwd_fstate_kernel<ST_CARRY>, grid((int64_t)chains * (nseg - 1)), dim3(256), 0, st, cu,
+                         chunk_off, h0, idt, T, N, H, (int)mc, ws, seg, nseg, seg_len);
+      if (nseg > 2) {
+        hipLaunchKernelGGL(kda_bwd_fstate_kernel<ST_TRANS>, grid((int64_t)chains * (nseg - 2)), dim3(256), 0, st, cu,
+                           chunk_off, h0, idt, T, N, H, (int)mc, ws, seg, nseg, seg_len);
+        hipLaunchKernelGGL(kda_segment_combine_kernel, cmb, dim3(256), 0, st, seg, chains, nseg);
+      }
+    }
+    hipLaunchKernelGGL(kda_bwd_fstate_kernel<ST_FULL>, grid((int64_t)chains * nseg), dim3(256), 0, st, cu, chunk_off,
+                       h0, idt, T, N, H, (int)mc, ws, seg, nseg, seg_len);
+    // the backward pass reuses the scratch once the forward pass is done with it
+    if (nseg > 1) {
+      hipLaunchKernelGGL(kda_bwd_bstate_kernel<ST_CARRY>, grid((int64_t)chains * (nseg - 1)), dim3(256), 0, st, dd,
+                         dhT, dh0, cu, chunk_off, T, N, H, (int)mc, ws, seg, nseg, seg_len);
+      if (nseg > 2) {
+        hipLaunchKernelGGL(kda_bwd_bstate_kernel<ST_TRANS>, grid((int64_t)chains * (nseg - 2)), dim3(256), 0, st, dd,
+                           dhT, dh0, cu, chunk_off, T, N, H, (int)mc, ws, seg, nseg, seg_len);
+        hipLaunchKernelGGL(kda_segment_combine_kernel, cmb, dim3(256), 0, st, seg, chains, nseg);
+      }
+    }
+    hipLaunchKernelGGL(kda_bwd_bstate_kernel<ST_FULL>, grid((int64_t)chains * nseg), dim3(256), 0, st, dd, dhT, dh0,
+                       cu, chunk_off, T, N, H, (int)mc, ws, seg, nseg, seg_len);
   }
   if (mc > 0) {
     hipLaunchKernelGGL(kda_bwd_dense_kernel, cg, dim3(256), 0, st, vv, dd, bb, cu, chunk_off, p->T, p->num_seqs,
@@ -1360,8 +1490,8 @@ void launch_bwd(const kda_fwd_params* p, const void* q, const void* k, const voi
     if (G > 1) {
       const int64_t rows = (int64_t)p->B * p->T;
       const int64_t n4 = rows * p->H_qk * (DK / 4);
-      hipLaunchKernelGGL(kda_bwd_reduce_qk_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, dqv, dkv,
-                         dq, dk, rows, p->H_qk, G);
+      hipLaunchKernelGGL(kda_bwd_reduce_qk_kernel, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 1 << 20)),
+                         dim3(256), 0, st, dqv, dkv, dq, dk, rows, p->H_qk, G);
     }
   }
   if (dA_log || ddt_bias)
@@ -1376,9 +1506,13 @@ extern "C" {
 size_t kda_bwd_workspace_size(const kda_fwd_params* p) {
   if (!p) return 0;
   // packed or dense cannot be told from params alone; size for the larger
+  // chunk count (packed when it can be) and the larger segment count (dense)
   const bool packed = p->B == 1 && p->num_seqs >= 1;
-  if (check_params(p, false) != KDA_OK && check_params(p, true) != KDA_OK) return 0;
-  return bwd_bytes(p, max_chunks_of(p, packed));
+  const bool dense_ok = check_params(p, false) == KDA_OK;
+  if (!dense_ok && check_params(p, true) != KDA_OK) return 0;
+  int len, nseg = 1;
+  if (dense_ok) nseg = seg_plan(p, false, &len);
+  return bwd_bytes(p, max_chunks_of(p, packed), nseg);
 }
 
 kda_status kda_bwd(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,

@@ -42,9 +42,11 @@
 
 #include "kda.h"
 #include "kda_internal.h"
+#include "kda_segment.h"
 
 namespace {
 using namespace kda_internal;
+using namespace kda_segment;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -75,8 +77,8 @@ constexpr int F_TBH = 32;     // T diag(b) hi   (ta, kb 0..1)      bf16  rows t,
 constexpr int F_TBL = 40;     //           lo
 constexpr int F_AQK = 48;     // scale rq_t (Q K^T . 2^(G_t - G_s)), lower incl. diagonal (ta, kb 0..1) fp16
 constexpr int F_VEC = 56;     // 2^G_last f32[128] | scale rq f32[64] | rk f32[64]
-constexpr int F_SHARED = 57;  // fragments 0..56 are shared by all V slices of a chain
 constexpr int F_KD = 57;      // (K . 2^(G_last - G))^T (km 0..7, kb 0..1, hi/lo) fp16 rows k, columns t
+                              // (fragments 0..56 are shared by all V slices of a chain)
 constexpr int NFRAG = 89;
 constexpr size_t BLOCK = (size_t)NFRAG * FRAG;
 static_assert(BLOCK % 256 == 0, "workspace block alignment");
@@ -99,15 +101,6 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
     f[2 * i] = __uint_as_float(w[i] << 16);
     f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
-}
-
-__device__ __forceinline__ float wave_xor_sum16(float v) {
-  // sum across the 16 lanes that share (lane >> 4)
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
-  return v;
 }
 
 struct ChunkPos {
@@ -805,7 +798,6 @@ constexpr int SWAVES = 4;
 //             the first segment from the initial state);
 //   ST_TRANS  the segment's linear map P: the same recurrence with v = 0
 //             started from the identity, on key rows instead of value rows.
-constexpr int ST_FULL = 0, ST_CARRY = 1, ST_TRANS = 2;
 constexpr int SSS = 136;  // sS row stride (fp16): state slice stored as [v][k]
 constexpr int SUS = 72;   // sU row stride (fp16): U' stored as [v][t]
 constexpr int SVS = 48;   // sV row stride (16-bit): V slice row-major [t][v]
@@ -1056,13 +1048,6 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
   }
 }
 
-// Segment scratch (fp32 [V][K] matrices, one per (chain, segment)): entry
-// states, states carried from zero, and segment maps, in three planes.
-constexpr int SEG_SIN = 0, SEG_F = 1, SEG_P = 2;
-__device__ __forceinline__ float* seg_mat(float* seg, int chains, int nseg, int plane, int chain, int r) {
-  return seg + (((size_t)plane * chains + chain) * nseg + r) * (size_t)(DV * DK);
-}
-
 // One workgroup per (job, V slice).  A job is a whole chain (nseg == 1) or one
 // segment of it; seg_len chunks per segment (dense input only).
 //   ST_FULL  jobs (chain, r), r = 0..nseg-1: entry state h0 (nseg == 1) or
@@ -1078,7 +1063,7 @@ __global__ void __launch_bounds__(64 * SWAVES, 1)
 kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
                  const int* __restrict__ chunk_off, const void* __restrict__ h0, void* __restrict__ hT,
                  uint16_t* __restrict__ out, const uint8_t* __restrict__ ws, float* __restrict__ seg,
-                 int B, int T, int N, int Hv, int max_chunks, int init_dtype, int final_dtype, int nseg,
+                 int T, int N, int Hv, int max_chunks, int init_dtype, int final_dtype, int nseg,
                  int seg_len) {
   __shared__ __attribute__((aligned(16))) float sVec[256];
   __shared__ __attribute__((aligned(16))) _Float16 sS[VS * SSS];
@@ -1199,43 +1184,6 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
           *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dst) + dst_base + (size_t)vv * DK + kk) = u;
         }
       }
-  }
-}
-
-// Entry states of the segments: S_in[r + 1] = S_in[r] P[r] + F[r] for
-// r = 1..nseg-2 (S_in[1] is the first segment's exit state).  One workgroup
-// per (chain, 8 value rows); P[r] is staged in LDS, the 8 rows of S_in stay
-// in LDS from step to step.
-constexpr int CMB_ROWS = 8;
-constexpr int CMB_XS = DK + 4;  // sX row stride: the two rows a wave reads sit on different banks
-__global__ void __launch_bounds__(256)
-kda_segment_combine_kernel(float* __restrict__ seg, int chains, int nseg) {
-  __shared__ __attribute__((aligned(16))) float sP[DK * DK];
-  __shared__ __attribute__((aligned(16))) float sX[CMB_ROWS * CMB_XS];
-  const int chain = blockIdx.x / (DV / CMB_ROWS), rb = blockIdx.x % (DV / CMB_ROWS);
-  if (chain >= chains) return;
-  const int tid = threadIdx.x, row = tid >> 5, c0 = 4 * (tid & 31);
-  const size_t off = (size_t)(rb * CMB_ROWS + row) * DK + c0;
-  *reinterpret_cast<float4*>(&sX[row * CMB_XS + c0]) =
-      *reinterpret_cast<const float4*>(seg_mat(seg, chains, nseg, SEG_SIN, chain, 1) + off);
-  for (int r = 1; r + 1 < nseg; ++r) {
-    const float* P = seg_mat(seg, chains, nseg, SEG_P, chain, r);
-#pragma unroll
-    for (int i = 0; i < DK * DK / 4 / 256; ++i) {
-      const int e = tid + 256 * i;
-      *reinterpret_cast<float4*>(&sP[4 * e]) = *reinterpret_cast<const float4*>(P + 4 * e);
-    }
-    float4 acc = *reinterpret_cast<const float4*>(seg_mat(seg, chains, nseg, SEG_F, chain, r) + off);
-    __syncthreads();
-#pragma unroll 8
-    for (int k = 0; k < DK; ++k) {
-      const float xk = sX[row * CMB_XS + k];
-      const float4 pk = *reinterpret_cast<const float4*>(&sP[k * DK + c0]);
-      acc.x += xk * pk.x; acc.y += xk * pk.y; acc.z += xk * pk.z; acc.w += xk * pk.w;
-    }
-    __syncthreads();  // every read of sX and sP of this step is done
-    *reinterpret_cast<float4*>(&sX[row * CMB_XS + c0]) = acc;
-    *reinterpret_cast<float4*>(seg_mat(seg, chains, nseg, SEG_SIN, chain, r + 1) + off) = acc;
   }
 }
 
@@ -1487,13 +1435,12 @@ kda_status launch_status() {
 
 }  // namespace kda_internal
 
-namespace {
+namespace kda_internal {
 
 // Time segments per state chain (dense input only) and chunks per segment.
 // Automatic (segments == 0): split only when the state launch has at most
 // half as many workgroups as the GPU has CUs (one state workgroup fills a
 // CU), into up to 256 / workgroups segments of at least 16 chunks each.
-constexpr int kMaxSegments = 256;
 int seg_plan(const kda_fwd_params* p, bool packed, int* seg_len) {
   const int ncs = (int)(((int64_t)p->T + CH - 1) / CH);
   int nseg = 1;
@@ -1504,7 +1451,9 @@ int seg_plan(const kda_fwd_params* p, bool packed, int* seg_len) {
       const int64_t wgs = (int64_t)p->num_seqs * p->H_v * NSLICE;
       if (wgs <= 128) nseg = (int)std::min<int64_t>(256 / wgs, ncs / 16);
     }
-    nseg = std::max(1, std::min(nseg, std::min(ncs, kMaxSegments)));
+    nseg = std::min(nseg, std::min(ncs, kMaxSegments));
+    // at most kMaxChains jobs per launch (the combine runs only for nseg >= 3)
+    nseg = std::max(1, std::min<int>(nseg, (int)(kMaxChains / std::max<int64_t>(1, (int64_t)p->num_seqs * p->H_v))));
   }
   const int len = ncs > 0 ? (ncs + nseg - 1) / nseg : 0;
   *seg_len = len;
@@ -1514,10 +1463,6 @@ int seg_plan(const kda_fwd_params* p, bool packed, int* seg_len) {
 size_t seg_scratch_bytes(const kda_fwd_params* p, int nseg) {
   return nseg > 1 ? (size_t)3 * p->num_seqs * p->H_v * nseg * DV * DK * sizeof(float) : 0;
 }
-
-}  // namespace
-
-namespace kda_internal {
 
 kda_status check_params(const kda_fwd_params* p, bool packed) {
   if (!p) return fail(KDA_ERR_NULL, "params is NULL");
@@ -1533,9 +1478,11 @@ kda_status check_params(const kda_fwd_params* p, bool packed) {
   }
   if ((int64_t)p->B * p->T * (int64_t)p->H_v > ((int64_t)1 << 40))
     return fail(KDA_ERR_SHAPE, "B*T*H_v too large");
-  if (max_chunks_of(p, packed) * (int64_t)p->H_v > ((int64_t)1 << 30))
+  // a dispatch dimension holds fewer than 2^32 work-items: one 256-thread
+  // workgroup per chunk (grid x) and 4 per (sequence, head) pair
+  if (max_chunks_of(p, packed) >= kMaxChunks || max_chunks_of(p, packed) * (int64_t)p->H_v > ((int64_t)1 << 30))
     return fail(KDA_ERR_SHAPE, "too many chunks");
-  if ((int64_t)p->num_seqs * p->H_v > ((int64_t)1 << 26))
+  if ((int64_t)p->num_seqs * p->H_v > kMaxChains)
     return fail(KDA_ERR_SHAPE, "too many (sequence, head) pairs");
   if (p->gate_mode != KDA_GATE_SOFTPLUS && p->gate_mode != KDA_GATE_SAFE_SIGMOID &&
       p->gate_mode != KDA_GATE_PREGATED)
@@ -1680,12 +1627,12 @@ kda_status launch_state(const kda_fwd_params* p, const void* v, const int64_t* c
     // entry states of the segments from their zero-state carries and maps
     hipLaunchKernelGGL(kda_state_kernel<ST_CARRY>, grid((int64_t)chains * (nseg - 1)), dim3(64 * SWAVES), 0, st,
                        (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out,
-                       blocks, seg, p->B, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype,
+                       blocks, seg, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype,
                        p->final_state_dtype, nseg, seg_len);
     if (nseg > 2) {
       hipLaunchKernelGGL(kda_state_kernel<ST_TRANS>, grid((int64_t)chains * (nseg - 2)), dim3(64 * SWAVES), 0, st,
                          (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out,
-                         blocks, seg, p->B, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype,
+                         blocks, seg, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype,
                          p->final_state_dtype, nseg, seg_len);
       hipLaunchKernelGGL(kda_segment_combine_kernel, dim3((unsigned)(chains * (DV / CMB_ROWS))), dim3(256), 0, st,
                          seg, chains, nseg);
@@ -1693,7 +1640,7 @@ kda_status launch_state(const kda_fwd_params* p, const void* v, const int64_t* c
   }
   hipLaunchKernelGGL(kda_state_kernel<ST_FULL>, grid((int64_t)chains * nseg), dim3(64 * SWAVES), 0, st,
                      (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out, blocks,
-                     seg, p->B, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype, p->final_state_dtype, nseg,
+                     seg, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype, p->final_state_dtype, nseg,
                      seg_len);
   return KDA_OK;
 }

@@ -206,14 +206,16 @@ def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GAT
 
 def bwd(q, k, v, g, beta, A_log, dt_bias, scale, d_out, lower_bound=-1.0, gate_mode=GATE_SOFTPLUS,
         initial_state=None, d_final_state=None, cu_seqlens=None, qk_l2norm=True, beta_is_prob=False,
-        workspace=None):
+        workspace=None, segments=0):
     """Gradients of ``fwd`` (kda_bwd) on the current HIP stream.
 
     Inputs as for ``fwd`` plus d_out bf16 [B,T,Hv,128] and d_final_state fp32
     [N,Hv,128,128] or None.  Returns a dict of fp32 tensors: dq, dk
     [B,T,Hqk,128], dv, dg [B,T,Hv,128], dbeta [B,T,Hv], dA_log [Hv] (None
     without A_log or with pre-gated decay), ddt_bias [Hv,128] (None with
-    pre-gated decay) and dh0 [N,Hv,128,128].
+    pre-gated decay) and dh0 [N,Hv,128,128].  ``segments`` as for ``fwd``:
+    both state passes of dense input split their chains into that many
+    parallel time segments (0: the library decides, 1: never).
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("d_out", d_out)):
@@ -237,7 +239,8 @@ def bwd(q, k, v, g, beta, A_log, dt_bias, scale, d_out, lower_bound=-1.0, gate_m
     p = make_params(B=B, T=T, H_qk=Hqk, H_v=Hv, K=K, V=V, num_seqs=N, scale=float(scale),
                     lower_bound=float(lower_bound), gate_mode=int(gate_mode),
                     init_state_dtype=_state_code(initial_state), final_state_dtype=STATE_NONE,
-                    flags=(FLAG_QK_L2NORM if qk_l2norm else 0) | (FLAG_BETA_IS_PROB if beta_is_prob else 0))
+                    flags=(FLAG_QK_L2NORM if qk_l2norm else 0) | (FLAG_BETA_IS_PROB if beta_is_prob else 0),
+                    segments=int(segments))
     need = int(lib.kda_bwd_workspace_size(ctypes.byref(p)))
     if workspace is None:
         workspace = _workspace(need, dev)

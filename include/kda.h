@@ -201,9 +201,11 @@ size_t kda_bwd_workspace_size(const kda_fwd_params* p);
  *   ddt_bias [H_v, 128] or NULL (the bias gradient, also when dt_bias is
  *           NULL; must be NULL with pre-gated decay)
  *   d_initial_state fp32 [num_seqs, H_v, 128, 128] or NULL
- * params->final_state_dtype and params->segments are not used.  The
- * workspace (kda_bwd_workspace_size bytes, 256-byte aligned) holds fp32
- * per-chunk intermediates; the library allocates nothing.  Every predicate
+ * params->final_state_dtype is not used; params->segments splits both
+ * state passes (over the chunks forward, then backward) as in kda_fwd, the
+ * segment count kda_fwd_segments reports.  The workspace
+ * (kda_bwd_workspace_size bytes, 256-byte aligned) holds fp32 per-chunk
+ * intermediates and the segment scratch; the library allocates nothing.  Every predicate
  * is checked before anything is enqueued; returns after enqueueing. */
 kda_status kda_bwd(const kda_fwd_params* p,
                    const void* q, const void* k, const void* v, const void* g,

@@ -80,6 +80,18 @@ def test_shape_dtype_mode_rejections(lib, field, bad, code):
     assert kda.last_error() != ""
 
 
+def test_launch_size_limits(lib):
+    # a dispatch dimension holds fewer than 2^32 work-items: at most 2^21
+    # (sequence, head) pairs (4 state workgroups of 256 each) and fewer than
+    # 2^24 chunks per head (one workgroup each along x)
+    assert check(lib, base_params(B=1 << 19, T=1, H_qk=4, H_v=4)) == kda.KDA_OK
+    assert check(lib, base_params(B=(1 << 19) + 1, T=1, H_qk=4, H_v=4)) == -2
+    assert "pairs" in kda.last_error()
+    assert check(lib, base_params(B=1, T=64 * ((1 << 24) - 1), H_qk=1, H_v=1)) == kda.KDA_OK
+    assert check(lib, base_params(B=1, T=64 * (1 << 24), H_qk=1, H_v=1)) == -2
+    assert "chunks" in kda.last_error()
+
+
 def test_gva_head_ratio(lib):
     assert check(lib, base_params(H_qk=2, H_v=6)) == kda.KDA_OK
     assert check(lib, base_params(H_qk=4, H_v=6)) == -2
@@ -227,6 +239,9 @@ def test_segment_plan(lib):
     # packed input never splits; invalid parameters give 0
     assert segs(lib, packed=True, B=1, T=131072, H_qk=2, H_v=4, segments=8) == 1
     assert segs(lib, B=2, T=100, segments=-3) == 0
+    # segment jobs per launch stay within the pair limit
+    assert segs(lib, B=1 << 18, T=64 * 8, H_qk=2, H_v=2, segments=8) == 4
+    assert segs(lib, B=1 << 19, T=64 * 8, H_qk=4, H_v=4, segments=8) == 1
 
 
 def test_workspace_holds_segment_scratch(lib):
@@ -234,6 +249,9 @@ def test_workspace_holds_segment_scratch(lib):
     p4 = base_params(B=1, T=4096, H_qk=2, H_v=2, segments=4)
     extra = lib.kda_fwd_workspace_size(ctypes.byref(p4)) - lib.kda_fwd_workspace_size(ctypes.byref(p1))
     assert extra == 3 * 2 * 4 * 128 * 128 * 4    # entry states, carries, maps: fp32 per (chain, segment)
+    # the backward's two state passes share one scratch of the same size
+    extra = lib.kda_bwd_workspace_size(ctypes.byref(p4)) - lib.kda_bwd_workspace_size(ctypes.byref(p1))
+    assert extra == 3 * 2 * 4 * 128 * 128 * 4
 
 
 def bwd_call(lib, p, drop=(), shift=None, ws=None, extra=None):

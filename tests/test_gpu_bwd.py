@@ -29,14 +29,14 @@ GRAD_REL = 1e-3
 NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dA_log", "ddt_bias", "dh0")
 
 
-def run_gpu_bwd(inp, d_out, dhT):
+def run_gpu_bwd(inp, d_out, dhT, segments=0):
     d = U.to_device(inp)
     dev_dout = U.bf16_dev(d_out)
     dev_dhT = None if dhT is None else torch.from_numpy(dhT).cuda()
     r = kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["A_log"], d["dt_bias"], inp.scale, dev_dout,
                 lower_bound=inp.lower_bound, gate_mode=inp.gate_mode, initial_state=d["h0"], d_final_state=dev_dhT,
                 cu_seqlens=d["cu_seqlens"], qk_l2norm=bool(inp.flags & W.FLAG_QK_L2NORM),
-                beta_is_prob=bool(inp.flags & W.FLAG_BETA_IS_PROB))
+                beta_is_prob=bool(inp.flags & W.FLAG_BETA_IS_PROB), segments=segments)
     torch.cuda.synchronize()
     return {n: (None if t is None else t.cpu().numpy().astype(np.float64)) for n, t in r.items()}
 
@@ -183,3 +183,78 @@ def test_bwd_headline_workload_sampled():
         U.log(f"    pair n={n} h={h} {errs}")
         for name, e in errs.items():
             assert e <= GRAD_REL, (n, h, name, e)
+
+
+# Time segments of both state passes (dense input): (inputs, segments)
+SEG_CASES = {
+    "safe_lb5_seg4": (dict(B=2, T=1000, Hqk=2, Hv=4, gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-5.0,
+                           A_log_range=(-4.0, 6.0), g_std=3.0), 4),
+    "softplus_seg16_one_chunk_each": (dict(B=1, T=1000, Hqk=2), 16),
+    "bf16_state_seg3": (dict(B=2, T=700, init_state_dtype=W.STATE_BF16), 3),
+    "pregated_seg5": (dict(B=1, T=1280, gate_mode=W.GATE_PREGATED, pregated_range=(-2.0, 0.0)), 5),
+    "no_state_seg2": (dict(B=2, T=513, init_state_dtype=W.STATE_NONE), 2),
+    "long_memory_seg8": (dict(B=1, T=2048, Hqk=2, A_log_range=(-8.0, -6.0)), 8),
+    "more_segments_than_chunks": (dict(B=1, T=200), 7),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SEG_CASES))
+def test_bwd_segments_elementwise(name):
+    kw, segments = SEG_CASES[name]
+    inp = small(**kw)
+    d_out, dhT = W.make_grads(inp, seed=91)
+    U.log(f"[gpu] bwd segments {name}: B={inp.B} T={inp.T} Hqk={inp.Hqk} Hv={inp.Hv} segments={segments}")
+    compare(run_gpu_bwd(inp, d_out, dhT, segments=segments), run_oracle_bwd(inp, d_out, dhT), name, inp)
+
+
+def test_bwd_segments_without_final_state_gradient():
+    inp = small(B=1, T=900)
+    d_out, _ = W.make_grads(inp, seed=6, dhT_std=None)
+    U.log("[gpu] bwd segments=3, d_final_state = None")
+    compare(run_gpu_bwd(inp, d_out, None, segments=3), run_oracle_bwd(inp, d_out, None), "seg no dhT", inp)
+
+
+@pytest.mark.parametrize("segments", [2, 5, 32])
+def test_bwd_segments_match_unsplit(segments):
+    inp = small(B=1, T=64 * 40 + 17, Hqk=2, gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-1.0)
+    d_out, dhT = W.make_grads(inp, seed=17)
+    U.log(f"[gpu] bwd segments={segments} vs unsplit, T={inp.T}")
+    a = run_gpu_bwd(inp, d_out, dhT, segments=1)
+    b = run_gpu_bwd(inp, d_out, dhT, segments=segments)
+    for n in NAMES:
+        if a.get(n) is None:
+            continue
+        e = float(np.linalg.norm(a[n] - b[n]) / max(np.linalg.norm(a[n]), 1e-30))
+        assert e <= GRAD_REL, (n, e)
+
+
+def test_bwd_long_sequence_few_heads_sampled():
+    # one GPU's share of the long grouped-head workload (T=131072, 2 q/k
+    # heads, 4 v-heads, safe gate lb=-1): 4 chains, so the library cuts both
+    # state passes into segments.  Checked on q/k head 1 with its 2 v-heads
+    # against the oracle on that group alone.
+    inp = W.workload(6)
+    lib_segments = kda.segments_of(kda.make_params(B=inp.B, T=inp.T, H_qk=inp.Hqk, H_v=inp.Hv, num_seqs=inp.N,
+                                                   scale=inp.scale, lower_bound=inp.lower_bound,
+                                                   gate_mode=inp.gate_mode, flags=inp.flags))
+    assert lib_segments > 1, lib_segments
+    d_out, dhT = W.make_grads(inp, seed=1006)
+    U.log(f"[gpu] bwd workload 6 full size, {lib_segments} segments")
+    gpu = run_gpu_bwd(inp, d_out, dhT)
+    for n in NAMES:
+        if gpu.get(n) is not None:
+            assert np.isfinite(gpu[n]).all(), n
+    f = oracle.bf16_to_f64
+    hq, hv = slice(1, 2), slice(2, 4)
+    ref = oracle.bwd(f(np.ascontiguousarray(inp.q[:, :, hq])), f(np.ascontiguousarray(inp.k[:, :, hq])),
+                     f(np.ascontiguousarray(inp.v[:, :, hv])), f(np.ascontiguousarray(inp.g[:, :, hv])),
+                     f(np.ascontiguousarray(inp.beta[:, :, hv])), inp.A_log[hv], inp.dt_bias[hv],
+                     f(np.ascontiguousarray(d_out[:, :, hv])), dhT[:, hv].astype(np.float64), scale=inp.scale,
+                     lower_bound=inp.lower_bound, gate_mode=inp.gate_mode, flags=inp.flags, initial_state=None)
+    errs = {}
+    for name, a in (("dq", gpu["dq"][:, :, hq]), ("dk", gpu["dk"][:, :, hq]), ("dv", gpu["dv"][:, :, hv]),
+                    ("dg", gpu["dg"][:, :, hv]), ("dbeta", gpu["dbeta"][:, :, hv]), ("dh0", gpu["dh0"][:, hv])):
+        errs[name] = float(np.linalg.norm(a - ref[name]) / np.linalg.norm(ref[name]))
+    U.log(f"    group hq=1 {errs}")
+    for name, e in errs.items():
+        assert e <= GRAD_REL, (name, e)
