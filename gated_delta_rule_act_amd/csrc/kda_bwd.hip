@@ -275,6 +275,7 @@ __device__ __forceinline__ float gtail(const float* sG, const float* sBt, int i,
 // lg = lane >> 4) feeds A[li][k + lg] and B[k + lg][li] and receives
 // C[4 lg + r][li] (r < 4) of each 16 x 16 tile.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // acc[m][n] += the (16 m, 16 n) tile of A B over k < kdim (a multiple of
 // 32), operands fp32 in LDS:
@@ -727,6 +728,38 @@ __device__ __forceinline__ float* job_exit(float* seg, int chains, int nseg, con
                           : seg_mat(seg, chains, nseg, SEG_F, j.chain, j.r);
 }
 
+// Register staging of a chunk's operands: the backward state pass fetches
+// the next chunk's tiles into registers while the current chunk's products
+// run, and moves them to LDS after the chunk's last barrier.
+__device__ __forceinline__ void fetch_tile128(f32x4 (&r)[8], const float* g, int tid) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = tid + 256 * i;
+    r[i] = *reinterpret_cast<const f32x4*>(g + (size_t)(e >> 5) * DK + 4 * (e & 31));
+  }
+}
+__device__ __forceinline__ void put_tile128(float* s, const f32x4 (&r)[8], int tid) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = tid + 256 * i;
+    *reinterpret_cast<f32x4*>(s + (e >> 5) * RS + 4 * (e & 31)) = r[i];
+  }
+}
+__device__ __forceinline__ void fetch_tile64(f32x4 (&r)[4], const float* g, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i;
+    r[i] = *reinterpret_cast<const f32x4*>(g + (e >> 4) * 64 + 4 * (e & 15));
+  }
+}
+__device__ __forceinline__ void put_tile64(float* s, const f32x4 (&r)[4], int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i;
+    *reinterpret_cast<f32x4*>(s + (e >> 4) * QS + 4 * (e & 15)) = r[i];
+  }
+}
+
 template <int KIND>
 __global__ void __launch_bounds__(256)
 kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ chunk_off, const void* __restrict__ h0,
@@ -751,7 +784,7 @@ kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ ch
     slice_to_lds(S, sS, w, li, lg);
     load_tile128(sW, pb + PB_W, DK, tid);
     load_tile128(sKd, pb + PB_KD, DK, tid);
-    // U rows 16 w .. +15 start from Ubar (lane layout of the product below);
+    // U rows 16 w .. +15 start from -Ubar (lane layout of the product below);
     // a map job has no inputs, Ubar = 0
     f32x4 U[1][2];
     zero_block(U);
@@ -788,6 +821,29 @@ kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ ch
   if constexpr (KIND != ST_FULL) slice_to_global(S, job_exit<KIND>(seg, chains, nseg, j), v0, w, li, lg);
 }
 
+// (native vector types: staging arrays of them stay in registers)
+struct BStage {
+  f32x4 kd[8], w[8], qg[8], aq[4];
+  u32x4 dO;  // bf16: token tid >> 2, columns v0 + 8 (tid & 3) .. +7
+  float gn[2];
+};
+
+template <int KIND>
+__device__ __forceinline__ void bstate_fetch(BStage& b, const float* pb, const uint16_t* d_out, int64_t row0, int len,
+                                             int Hv, int h, int v0, int tid, int w, int li) {
+  fetch_tile128(b.kd, pb + PB_KD, tid);
+  fetch_tile128(b.w, pb + PB_W, tid);
+  if constexpr (KIND != ST_TRANS) {
+    fetch_tile128(b.qg, pb + PB_QG, tid);
+    fetch_tile64(b.aq, pb + PB_AQK, tid);
+    const int t = tid >> 2;
+    b.dO = u32x4{0u, 0u, 0u, 0u};
+    if (t < len) b.dO = *reinterpret_cast<const u32x4*>(d_out + ((size_t)(row0 + t) * Hv + h) * DV + v0 + 8 * (tid & 3));
+  }
+#pragma unroll
+  for (int nn = 0; nn < 2; ++nn) b.gn[nn] = pb[PB_GN + 32 * w + 16 * nn + li];
+}
+
 template <int KIND>
 __global__ void __launch_bounds__(256)
 kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restrict__ dhT, float* __restrict__ dh0,
@@ -808,33 +864,36 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
   const size_t sbase = (size_t)j.chain * DV * DK;
   f32x4 D[2][2];
   job_entry<KIND>(D, j, dhT == nullptr ? nullptr : dhT + sbase, KDA_STATE_F32, seg, chains, nseg, w, li, lg);
+  const float* pb0 = ws + ((size_t)h * mc + j.x0) * CHUNK_HEAD_FLOATS;
+  auto chunk_len = [&](int c) { return (int)min((int64_t)CH, seqlen - (int64_t)c * CH); };
+  BStage b;
+  if (j.c0 < j.c1) {
+    const int c = j.c1 - 1;
+    bstate_fetch<KIND>(b, pb0 + (size_t)c * CHUNK_HEAD_FLOATS, d_out, j.bos + (int64_t)c * CH, chunk_len(c), Hv, h,
+                       v0, tid, w, li);
+  }
   for (int c = j.c1 - 1; c >= j.c0; --c) {
-    const float* pb = ws + ((size_t)h * mc + j.x0 + c) * CHUNK_HEAD_FLOATS;
-    float* sb = const_cast<float*>(pb) + PB_FLOATS;
-    const int64_t row0 = j.bos + (int64_t)c * CH;
-    const int len = (int)min((int64_t)CH, seqlen - (int64_t)c * CH);
+    float* sb = const_cast<float*>(pb0) + (size_t)c * CHUNK_HEAD_FLOATS + PB_FLOATS;
     if constexpr (KIND == ST_FULL) slice_to_global(D, sb + SB_DH, v0, w, li, lg);
     slice_to_lds(D, sdh, w, li, lg);
-    load_tile128(sKd, pb + PB_KD, DK, tid);
-    load_tile128(sW, pb + PB_W, DK, tid);
+    put_tile128(sKd, b.kd, tid);
+    put_tile128(sW, b.w, tid);
     if constexpr (KIND != ST_TRANS) {
-      load_tile64(sAq, pb + PB_AQK, tid);
-      load_tile128(sQg, pb + PB_QG, DK, tid);
-      // dO slice: token t = tid >> 2, columns 8 (tid & 3) .. +7 (bf16)
+      put_tile128(sQg, b.qg, tid);
+      put_tile64(sAq, b.aq, tid);
       const int t = tid >> 2, jj = 8 * (tid & 3);
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (t < len) u = *reinterpret_cast<const uint4*>(d_out + ((size_t)(row0 + t) * Hv + h) * DV + v0 + jj);
-      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+      const uint32_t wv[4] = {b.dO[0], b.dO[1], b.dO[2], b.dO[3]};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         sdO[t * SV + jj + 2 * q] = __uint_as_float(wv[q] << 16);
         sdO[t * SV + jj + 2 * q + 1] = __uint_as_float(wv[q] & 0xffff0000u);
       }
     }
-    float gn[2];
-#pragma unroll
-    for (int nn = 0; nn < 2; ++nn) gn[nn] = pb[PB_GN + 32 * w + 16 * nn + li];
+    const float gn[2] = {b.gn[0], b.gn[1]};
     __syncthreads();
+    if (c - 1 >= j.c0)
+      bstate_fetch<KIND>(b, pb0 + (size_t)(c - 1) * CHUNK_HEAD_FLOATS, d_out, j.bos + (int64_t)(c - 1) * CH,
+                         chunk_len(c - 1), Hv, h, v0, tid, w, li);
     // dU rows 16 w .. +15:  Aqk^T dO  +  Kd dS'^T  (a map job has dO = 0)
     f32x4 dU[1][2];
     zero_block(dU);
@@ -1385,17 +1444,78 @@ kda_bwd_reduce_qk_kernel(const float* __restrict__ dqv, const float* __restrict_
     reduce_qk_one(dqv, dkv, dq, dk, e, Hqk, G);
 }
 
+// Gate-parameter partials of a (chunk, v-head): ddt_bias [128], dA_log [1].
+constexpr int GATE_GROUP = 16;  // chunks summed by one workgroup of the first stage
+__device__ __forceinline__ float* gate_partials(float* ws, int h, int mc, int x) {
+  return ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS + PB_FLOATS + SB_FLOATS + GB_FLOATS;
+}
+
+// First stage, per (group of GATE_GROUP chunks, v-head): the group's sum
+// replaces the partials of its first chunk.  Two halves of 128 threads take
+// alternate chunks, with all their loads in flight at once.
 __global__ void __launch_bounds__(256)
-kda_bwd_reduce_gate_kernel(const float* __restrict__ ws, int mc, float* __restrict__ dA_log,
-                           float* __restrict__ ddt_bias) {
-  const int h = blockIdx.x, tid = threadIdx.x;
-  __shared__ float sPart[2][DK + 1];
+kda_bwd_reduce_gate_groups_kernel(float* __restrict__ ws, int mc) {
+  __shared__ float sPart[DK + 1];
+  const int x0 = GATE_GROUP * blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int c = tid & 127, half = tid >> 7;
+  float v[GATE_GROUP / 2], a[GATE_GROUP / 2];
+#pragma unroll
+  for (int i = 0; i < GATE_GROUP / 2; ++i) {
+    const int x = x0 + 2 * i + half;
+    v[i] = 0.0f;
+    a[i] = 0.0f;
+    if (x < mc) {
+      const float* gp = gate_partials(ws, h, mc, x);
+      v[i] = gp[c];
+      if (c == 0) a[i] = gp[DK];
+    }
+  }
   float sum = 0.0f, sa = 0.0f;
-  for (int x = half; x < mc; x += 2) {
-    const float* gp = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS + PB_FLOATS + SB_FLOATS + GB_FLOATS;
-    sum += gp[c];
-    if (c == 0) sa += gp[DK];
+#pragma unroll
+  for (int i = 0; i < GATE_GROUP / 2; ++i) {
+    sum += v[i];
+    sa += a[i];
+  }
+  if (half == 1) {
+    sPart[c] = sum;
+    if (c == 0) sPart[DK] = sa;
+  }
+  __syncthreads();
+  if (half == 0) {
+    // only this thread read these two entries of chunk x0
+    float* gp = gate_partials(ws, h, mc, x0);
+    gp[c] = sum + sPart[c];
+    if (c == 0) gp[DK] = sa + sPart[DK];
+  }
+}
+
+// Second stage, per v-head: the sums of the groups (at chunks 0, GATE_GROUP, ...).
+__global__ void __launch_bounds__(256)
+kda_bwd_reduce_gate_kernel(float* __restrict__ ws, int mc, float* __restrict__ dA_log,
+                           float* __restrict__ ddt_bias) {
+  __shared__ float sPart[2][DK + 1];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int c = tid & 127, half = tid >> 7;
+  constexpr int U = 8;  // loads in flight per thread
+  float sum = 0.0f, sa = 0.0f;
+  for (int x = GATE_GROUP * half; x < mc; x += 2 * GATE_GROUP * U) {
+    float v[U], a[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int xi = x + 2 * GATE_GROUP * i;
+      v[i] = 0.0f;
+      a[i] = 0.0f;
+      if (xi < mc) {
+        const float* gp = gate_partials(ws, h, mc, xi);
+        v[i] = gp[c];
+        if (c == 0) a[i] = gp[DK];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      sum += v[i];
+      sa += a[i];
+    }
   }
   sPart[half][c] = sum;
   if (c == 0) sPart[half][DK] = sa;
@@ -1494,9 +1614,14 @@ void launch_bwd(const kda_fwd_params* p, const void* q, const void* k, const voi
                          dim3(256), 0, st, dqv, dkv, dq, dk, rows, p->H_qk, G);
     }
   }
-  if (dA_log || ddt_bias)
+  if (dA_log || ddt_bias) {
+    if (mc > 0)
+      hipLaunchKernelGGL(kda_bwd_reduce_gate_groups_kernel,
+                         dim3((unsigned)((mc + GATE_GROUP - 1) / GATE_GROUP), (unsigned)p->H_v), dim3(256), 0, st, ws,
+                         (int)mc);
     hipLaunchKernelGGL(kda_bwd_reduce_gate_kernel, dim3((unsigned)p->H_v), dim3(256), 0, st, ws, (int)mc, dA_log,
                        ddt_bias);
+  }
 }
 
 }  // namespace

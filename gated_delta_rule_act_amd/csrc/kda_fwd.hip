@@ -1484,6 +1484,7 @@ kda_status check_params(const kda_fwd_params* p, bool packed) {
     return fail(KDA_ERR_SHAPE, "too many chunks");
   if ((int64_t)p->num_seqs * p->H_v > kMaxChains)
     return fail(KDA_ERR_SHAPE, "too many (sequence, head) pairs");
+  if (p->H_v > 65535) return fail(KDA_ERR_SHAPE, "H_v must be at most 65535 (the y extent of a launch)");
   if (p->gate_mode != KDA_GATE_SOFTPLUS && p->gate_mode != KDA_GATE_SAFE_SIGMOID &&
       p->gate_mode != KDA_GATE_PREGATED)
     return fail(KDA_ERR_UNSUPPORTED, "unknown gate_mode %d", p->gate_mode);

@@ -58,7 +58,11 @@ extern "C" {
 typedef enum {
   KDA_OK = 0,
   KDA_ERR_NULL = -1,        /* a required pointer is NULL */
-  KDA_ERR_SHAPE = -2,       /* a size is out of the supported set */
+  KDA_ERR_SHAPE = -2,       /* a size is out of the supported set; besides the rules
+                               below: fewer than 2^24 64-token chunks per head (B *
+                               ceil(T/64), or that plus num_seqs when packed), at most
+                               2^30 chunk-heads, at most 2^21 (sequence, v-head) pairs,
+                               H_v <= 65535 -- what one launch dimension holds */
   KDA_ERR_DTYPE = -3,       /* unknown or mismatched state dtype code */
   KDA_ERR_RANGE = -4,       /* scalar outside its allowed range */
   KDA_ERR_ALIGN = -5,       /* a tensor base is not 16-byte aligned */
