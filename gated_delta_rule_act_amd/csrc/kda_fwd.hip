@@ -94,6 +94,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
+// One 1 KB workspace fragment from a wave (16 bytes per lane).  Non-temporal:
+// the workspace is written once and read by the next launch; the state
+// kernel measured 5 % faster reading blocks stored this way.
+__device__ __forceinline__ void st_frag(uint8_t* blk, int fr, int lane, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(blk + fr * FRAG + lane * 16));
+}
+
 __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -547,7 +554,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = qR[e] * vP[c0 + e];
-        *reinterpret_cast<half8*>(blk + (F_QG + I * 4 + kb) * FRAG + lane * 16) = to_half8(o);
+        st_frag(blk, F_QG + I * 4 + kb, lane, __builtin_bit_cast(u32x4, to_half8(o)));
       }
       {
         float o[8];
@@ -631,8 +638,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     __syncthreads();
     for (int it = 0; it < 4; ++it) {
       const int fr = wave + 4 * it;  // fragment (km = fr >> 1, kb = fr & 1)
-      *reinterpret_cast<u32x4*>(blk + (F_KD + fr * 2 + part) * FRAG + lane * 16) =
-          lds_frag_tr(sKd, KER, 32 * (fr & 1), 16 * (fr >> 1), lane);
+      st_frag(blk, F_KD + fr * 2 + part, lane, lds_frag_tr(sKd, KER, 32 * (fr & 1), 16 * (fr >> 1), lane));
     }
     __syncthreads();
   }
@@ -750,10 +756,9 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         th[e] = hv;
         tl[e] = (__bf16)(v - (float)hv);
       }
-      *reinterpret_cast<bf16x8*>(blk + (F_TBH + fr) * FRAG + ln * 16) = th;
-      *reinterpret_cast<bf16x8*>(blk + (F_TBL + fr) * FRAG + ln * 16) = tl;
-      *reinterpret_cast<half8*>(blk + (F_AQK + fr) * FRAG + ln * 16) =
-          *reinterpret_cast<const half8*>(sAq + row * AQS + c0);
+      st_frag(blk, F_TBH + fr, ln, __builtin_bit_cast(u32x4, th));
+      st_frag(blk, F_TBL + fr, ln, __builtin_bit_cast(u32x4, tl));
+      st_frag(blk, F_AQK + fr, ln, *reinterpret_cast<const u32x4*>(sAq + row * AQS + c0));
     }
     // sA (region X) is dead after the solve: stage -W there
 #pragma unroll
@@ -766,8 +771,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     __syncthreads();
     for (int it = 0; it < 4; ++it) {
       const int fr = wave + 4 * it;  // fragment (ta = fr >> 2, kb = fr & 3)
-      *reinterpret_cast<u32x4*>(blk + (F_WN + fr) * FRAG + lane * 16) =
-          lds_frag_tr(sW, WTS, 32 * (fr & 3), 16 * (fr >> 2), lane);
+      st_frag(blk, F_WN + fr, lane, lds_frag_tr(sW, WTS, 32 * (fr & 3), 16 * (fr >> 2), lane));
     }
   }
 }
@@ -812,8 +816,11 @@ struct ChunkRegs {
   u32x4 kd[2][2][2];         // Kd^T: key tile 2w + j, token block b, hi/lo
 };
 
+// (a buffer load over the chunk-head block: the scalar base and immediate
+// offsets take less address arithmetic than a flat pointer, measured 3 % faster)
 __device__ __forceinline__ u32x4 ld_frag(const uint8_t* blk, int fr, int lane) {
-  return *reinterpret_cast<const u32x4*>(blk + fr * FRAG + lane * 16);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(blk, (uint32_t)BLOCK),
+                                                                          fr * FRAG + lane * 16, 0, 0));
 }
 
 // PART 0: token-tile operands, vectors and V (issued two chunks ahead);
