@@ -57,8 +57,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int CH = 64;      // chunk length
 constexpr int DK = 128;     // key dim
 constexpr int DV = 128;     // value dim
-constexpr int VS = 32;      // V slice per state workgroup
-constexpr int NSLICE = DV / VS;
+// V slice per state workgroup: 16 NVT columns (NVT = 2 or 4 V tiles)
+constexpr int NVT_NARROW = 2, NVT_WIDE = 4;
+constexpr int NSLICE = DV / (16 * NVT_NARROW);  // narrow slices per (sequence, head)
+constexpr int64_t kGpuCUs = 256;                 // compute units of an MI355X
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kL2Eps = 1e-6f;
 // Per-token log2 decay floor.  Any decay below 2^-1e4 is already exactly zero
@@ -804,7 +806,9 @@ constexpr int SWAVES = 4;
 //             started from the identity, on key rows instead of value rows.
 constexpr int SSS = 136;  // sS row stride (fp16): state slice stored as [v][k]
 constexpr int SUS = 72;   // sU row stride (fp16): U' stored as [v][t]
-constexpr int SVS = 48;   // sV row stride (16-bit): V slice row-major [t][v]
+// sV row stride (16-bit): V slice row-major [t][v]; the four rows a lane
+// group reads sit on different banks
+template <int NVT> constexpr int svs() { return NVT == 2 ? 48 : 80; }
 
 struct ChunkRegs {
   // arrays indexed only by compile-time values (fully unrolled loops)
@@ -812,7 +816,7 @@ struct ChunkRegs {
   u32x4 tbh[2], tbl[2];      // T diag(b) hi/lo: token tile w, token blocks 0, 1
   u32x4 aq[2];               // Aqk: token tile w, token blocks 0, 1
   u32x4 vec;                 // bytes 256 w + 16 (lane & 15) of the vector fragment
-  u32x4 vraw;                // V slice: row tid >> 2, columns 8 (tid & 3) ..
+  u32x4 vraw[2];             // V slice: row tid >> 2, columns 32 i + 8 (tid & 3) .. (i < NVT / 2)
   u32x4 kd[2][2][2];         // Kd^T: key tile 2w + j, token block b, hi/lo
 };
 
@@ -826,7 +830,7 @@ __device__ __forceinline__ u32x4 ld_frag(const uint8_t* blk, int fr, int lane) {
 // PART 0: token-tile operands, vectors and V (issued two chunks ahead);
 // PART 1: key-tile operands (issued one chunk ahead).
 // Operands a kind does not use are neither loaded nor kept.
-template <int PART, int KIND>
+template <int PART, int KIND, int NVT>
 __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk, int wave, int lane,
                                                 const uint16_t* __restrict__ v, int64_t row0, int len, int Hv, int h,
                                                 int v0, int tid) {
@@ -849,8 +853,10 @@ __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk
       // rows s >= len lie beyond the buffer range and read as zero
       const __amdgpu_buffer_rsrc_t rv =
           buffer_rsrc(v + ((size_t)row0 * Hv + h) * DV + v0, (uint32_t)len * Hv * DV * 2);
-      o.vraw = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ((tid >> 2) * Hv * DV + 8 * (tid & 3)) * 2, 0, 0));
+#pragma unroll
+      for (int i = 0; i < NVT / 2; ++i)
+        o.vraw[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ((tid >> 2) * Hv * DV + 32 * i + 8 * (tid & 3)) * 2, 0, 0));
     }
   } else {
 #pragma unroll
@@ -879,19 +885,21 @@ struct StateCtx {
 // Output tiles of a finished chunk, held in registers and stored at the start
 // of the next chunk, before that chunk's prefetch: stores count in vmcnt like
 // loads, so a store queued behind a prefetch would lengthen the operand wait.
+template <int NVT>
 struct PendingOut {
-  uint16_t o[2][4];
+  uint16_t o[NVT][4];
   int64_t row0;
   int len;
 };
 
-// wave w stores the output tiles of token tile w, V tiles 0 and 1
-__device__ __forceinline__ void store_pending(const PendingOut& pd, uint16_t* __restrict__ out, int Hv, int h,
+// wave w stores the output tiles of token tile w, V tiles 0 .. NVT-1
+template <int NVT>
+__device__ __forceinline__ void store_pending(const PendingOut<NVT>& pd, uint16_t* __restrict__ out, int Hv, int h,
                                               int v0, int wave, int li, int lg) {
   // rows t >= len fall outside the buffer range and are dropped
   const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(out + ((size_t)pd.row0 * Hv + h) * DV + v0, (uint32_t)pd.len * Hv * DV * 2);
 #pragma unroll
-  for (int vt = 0; vt < 2; ++vt)
+  for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int t = 16 * wave + 4 * lg + rr;
@@ -913,7 +921,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_b
 // every iteration).
 __device__ __forceinline__ void settle(const u32x4& a) { asm volatile("" ::"v"(a)); }
 __device__ __forceinline__ void settle(const f32x4& a) { asm volatile("" ::"v"(a)); }
-template <int KIND>
+template <int KIND, int NVT>
 __device__ __forceinline__ void settle(const ChunkRegs& r) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -926,7 +934,9 @@ __device__ __forceinline__ void settle(const ChunkRegs& r) {
     if constexpr (KIND == ST_FULL) settle(r.aq[kb]);
   }
   settle(r.vec);
-  if constexpr (KIND != ST_TRANS) settle(r.vraw);
+  if constexpr (KIND != ST_TRANS)
+#pragma unroll
+    for (int i = 0; i < NVT / 2; ++i) settle(r.vraw[i]);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -934,21 +944,27 @@ __device__ __forceinline__ void settle(const ChunkRegs& r) {
 }
 
 // One chunk of the state chain: `cur` holds chunk c, `n1` receives the key-tile
-// operands of chunk c+1, `n2` the token-tile operands of chunk c+2.
-template <int KIND>
-__device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2], ChunkRegs& cur, ChunkRegs& n1,
-                                            ChunkRegs& n2, const int c, PendingOut& pd) {
+// operands of chunk c+1, `n2` the token-tile operands of chunk c+2.  The wide
+// slices (NVT = 4) have no registers for that depth: their token-tile
+// operands of chunk c+1 go to `n1` too (`n2` unused).
+template <int KIND, int NVT>
+__device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT], ChunkRegs& cur, ChunkRegs& n1,
+                                            ChunkRegs& n2, const int c, PendingOut<NVT>& pd) {
+  constexpr int SVS = svs<NVT>();
   const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
   const int64_t row0 = x.bos + (int64_t)c * CH;
   typedef _Float16 half4 __attribute__((ext_vector_type(4)));
   // 1. publish the chunk's vectors, the V slice and the current state.  Every
   //    reader of these buffers in the previous chunk was before its B2.
   reinterpret_cast<u32x4*>(x.sVec)[16 * wave + (lane & 15)] = cur.vec;
-  if constexpr (KIND != ST_TRANS) *reinterpret_cast<u32x4*>(x.sV + (tid >> 2) * SVS + 8 * (tid & 3)) = cur.vraw;
+  if constexpr (KIND != ST_TRANS)
+#pragma unroll
+    for (int i = 0; i < NVT / 2; ++i)
+      *reinterpret_cast<u32x4*>(x.sV + (tid >> 2) * SVS + 32 * i + 8 * (tid & 3)) = cur.vraw[i];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int vt = 0; vt < 2; ++vt) {
+    for (int vt = 0; vt < NVT; ++vt) {
       const half4 hv = {(_Float16)S[j][vt][0], (_Float16)S[j][vt][1], (_Float16)S[j][vt][2], (_Float16)S[j][vt][3]};
       *reinterpret_cast<half4*>(x.sS + (16 * vt + li) * SSS + 32 * wave + 16 * j + 4 * lg) = hv;
     }
@@ -957,8 +973,9 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
   //    same operations)
   if constexpr (KIND == ST_FULL) store_pending(pd, x.out, x.Hv, x.h, x.v0, wave, li, lg);
   {
-    const int cp = min(c + 2, x.nc - 1);
-    load_chunk_part<0, KIND>(n2, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, x.bos + (int64_t)cp * CH,
+    constexpr int AHEAD = NVT == NVT_NARROW ? 2 : 1;
+    const int cp = min(c + AHEAD, x.nc - 1);
+    load_chunk_part<0, KIND, NVT>(AHEAD == 2 ? n2 : n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, x.bos + (int64_t)cp * CH,
                        chunk_len(x, cp), x.Hv, x.h, x.v0, tid);
   }
   __syncthreads();  // B1
@@ -967,9 +984,9 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
   const f32x4 rk = *reinterpret_cast<const f32x4*>(x.sVec + 192 + 16 * wave + 4 * lg);
   const f32x4 gn0 = *reinterpret_cast<const f32x4*>(x.sVec + 32 * wave + 4 * lg);
   const f32x4 gn1 = *reinterpret_cast<const f32x4*>(x.sVec + 32 * wave + 16 + 4 * lg);
-  f32x4 U[2], O[2];
+  f32x4 U[NVT], O[NVT];
 #pragma unroll
-  for (int vt = 0; vt < 2; ++vt) {
+  for (int vt = 0; vt < NVT; ++vt) {
     half8 sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
@@ -1002,12 +1019,12 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
   __builtin_amdgcn_sched_barrier(0);
   {
     const int cp = min(c + 1, x.nc - 1);
-    load_chunk_part<1, KIND>(n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+    load_chunk_part<1, KIND, NVT>(n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
   }
   __builtin_amdgcn_sched_barrier(0);
   // 5. U' = rk . U -> LDS hi/lo, transposed [v][t]
 #pragma unroll
-  for (int vt = 0; vt < 2; ++vt) {
+  for (int vt = 0; vt < NVT; ++vt) {
     half4 hi, lo;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -1024,7 +1041,7 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
   // 6. S <- S Diag(2^G_last) + U'^T Kd ;  O += Aqk U'  (Aqk of token tiles 0,
   //    1 is zero in token block 1, so that product adds nothing there)
 #pragma unroll
-  for (int vt = 0; vt < 2; ++vt) {
+  for (int vt = 0; vt < NVT; ++vt) {
     const half8 uh0 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 8 * lg);
     const half8 uh1 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 32 + 8 * lg);
     const half8 ul0 = *reinterpret_cast<const half8*>(x.sUl + (16 * vt + li) * SUS + 8 * lg);
@@ -1047,7 +1064,7 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
   }
   if constexpr (KIND == ST_FULL) {
 #pragma unroll
-    for (int vt = 0; vt < 2; ++vt)
+    for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) pd.o[vt][rr] = __builtin_bit_cast(uint16_t, (__bf16)O[vt][rr]);
     pd.row0 = row0;
@@ -1065,7 +1082,7 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][2],
 // written only by the full launch, so the two may share one buffer.
 //   ST_TRANS jobs (chain, r), r = 1..nseg-2: from the identity into P[r];
 //            the "V slice" is then a range of key rows.
-template <int KIND>
+template <int KIND, int NVT>
 __global__ void __launch_bounds__(64 * SWAVES, 1)
 kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
                  const int* __restrict__ chunk_off, const void* __restrict__ h0, void* __restrict__ hT,
@@ -1073,18 +1090,19 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
                  int T, int N, int Hv, int max_chunks, int init_dtype, int final_dtype, int nseg,
                  int seg_len) {
   __shared__ __attribute__((aligned(16))) float sVec[256];
+  constexpr int VS = 16 * NVT, NSL = DV / VS;
   __shared__ __attribute__((aligned(16))) _Float16 sS[VS * SSS];
   __shared__ __attribute__((aligned(16))) _Float16 sUh[VS * SUS];
   __shared__ __attribute__((aligned(16))) _Float16 sUl[VS * SUS];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[CH * SVS];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[CH * svs<NVT>()];
 
-  // XCD-aware decode: the NSLICE slices of one job share (id mod 8), so they
+  // XCD-aware decode: the NSL slices of one job share (id mod 8), so they
   // are dispatched to the same XCD and share its L2 for the job's operands.
   const int jpc = KIND == ST_FULL ? nseg : KIND == ST_CARRY ? nseg - 1 : nseg - 2;  // jobs per chain
   const int chains = N * Hv;
   const int id = blockIdx.x;
-  const int job = (id / (8 * NSLICE)) * 8 + (id & 7);
-  const int slice = (id >> 3) % NSLICE;
+  const int job = (id / (8 * NSL)) * 8 + (id & 7);
+  const int slice = (id >> 3) % NSL;
   if (job >= chains * jpc) return;
   const int chain = job / jpc, r = job % jpc + (KIND == ST_TRANS ? 1 : 0);
   const int n = chain / Hv, h = chain % Hv;
@@ -1113,11 +1131,11 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
   } else if (KIND == ST_FULL) {
     src = seg_mat(seg, chains, nseg, SEG_SIN, chain, r); src_dtype = KDA_STATE_F32;
   }
-  f32x4 S[2][2];
+  f32x4 S[2][NVT];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int vt = 0; vt < 2; ++vt) {
+    for (int vt = 0; vt < NVT; ++vt) {
       const int kk = 32 * wave + 16 * j + 4 * lg, vv = v0 + 16 * vt + li;
       f32x4 st = f32x4{0, 0, 0, 0};
       if constexpr (KIND == ST_TRANS) {
@@ -1140,26 +1158,39 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
   StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, lane, li, lg, sVec, sS, sUh, sUl, sV};
   ChunkRegs rA, rB, rC;
   if (nc > 0) {
-    load_chunk_part<0, KIND>(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
-    load_chunk_part<1, KIND>(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, 0, 0, Hv, h, v0, tid);
+    load_chunk_part<0, KIND, NVT>(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0,
+                                  tid);
+    load_chunk_part<1, KIND, NVT>(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, 0, 0, Hv, h, v0, tid);
+  }
+  if (nc > 0 && NVT == NVT_NARROW) {
     const int c1 = min(1, nc - 1);
-    load_chunk_part<0, KIND>(rB, wsh + (size_t)(x0 + c1) * BLOCK, wave, lane, v, bos + (int64_t)c1 * CH,
+    load_chunk_part<0, KIND, NVT>(rB, wsh + (size_t)(x0 + c1) * BLOCK, wave, lane, v, bos + (int64_t)c1 * CH,
                              chunk_len(ctx, c1), Hv, h, v0, tid);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) { settle(S[j][0]); settle(S[j][1]); }
-  settle<KIND>(rA);
-  PendingOut pd;
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt) settle(S[j][vt]);
+  settle<KIND, NVT>(rA);
+  PendingOut<NVT> pd;
   pd.row0 = bos;
   pd.len = 0;
   int c = 0;
-  for (; c + 3 <= nc; c += 3) {
-    state_chunk<KIND>(ctx, S, rA, rB, rC, c, pd);
-    state_chunk<KIND>(ctx, S, rB, rC, rA, c + 1, pd);
-    state_chunk<KIND>(ctx, S, rC, rA, rB, c + 2, pd);
+  if constexpr (NVT == NVT_NARROW) {
+    for (; c + 3 <= nc; c += 3) {
+      state_chunk<KIND, NVT>(ctx, S, rA, rB, rC, c, pd);
+      state_chunk<KIND, NVT>(ctx, S, rB, rC, rA, c + 1, pd);
+      state_chunk<KIND, NVT>(ctx, S, rC, rA, rB, c + 2, pd);
+    }
+    if (c < nc) state_chunk<KIND, NVT>(ctx, S, rA, rB, rC, c, pd);
+    if (c + 1 < nc) state_chunk<KIND, NVT>(ctx, S, rB, rC, rA, c + 1, pd);
+  } else {
+    for (; c + 2 <= nc; c += 2) {
+      state_chunk<KIND, NVT>(ctx, S, rA, rB, rB, c, pd);
+      state_chunk<KIND, NVT>(ctx, S, rB, rA, rA, c + 1, pd);
+    }
+    if (c < nc) state_chunk<KIND, NVT>(ctx, S, rA, rB, rB, c, pd);
   }
-  if (c < nc) state_chunk<KIND>(ctx, S, rA, rB, rC, c, pd);
-  if (c + 1 < nc) state_chunk<KIND>(ctx, S, rB, rC, rA, c + 1, pd);
   if constexpr (KIND == ST_FULL) store_pending(pd, out, Hv, h, v0, wave, li, lg);
 
   // exit state
@@ -1178,7 +1209,7 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int vt = 0; vt < 2; ++vt) {
+      for (int vt = 0; vt < NVT; ++vt) {
         const int kk = 32 * wave + 16 * j + 4 * lg, vv = v0 + 16 * vt + li;
         if (dst_dtype == KDA_STATE_F32) {
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dst) + dst_base + (size_t)vv * DK + kk) = S[j][vt];
@@ -1618,6 +1649,41 @@ kda_status launch_intra(const kda_fwd_params* p, const void* q, const void* k, c
   return KDA_OK;
 }
 
+struct StateArgs {
+  const uint16_t* v;
+  const int64_t* cu;
+  const int* chunk_off;
+  const void* h0;
+  void* hT;
+  uint16_t* out;
+  const uint8_t* ws;
+  float* seg;
+  int T, N, Hv, mc, init_dtype, final_dtype, nseg, seg_len;
+};
+
+// One state launch of `jobs` jobs: groups of 8 jobs, one workgroup (one per
+// CU) per V slice.  A chunk step of a 64-column slice takes about 1.85 times
+// that of a 32-column one (measured on the varlen workload), and each job
+// needs half as many of them; so the launch takes the width whose rounds of
+// 256 workgroups, weighted by step time, cost less (narrow up to 64 jobs,
+// wide for 65..128; with many jobs the two alternate, wide saving up to 7 %).
+constexpr int64_t kWideStepPct = 185;
+template <int KIND>
+void launch_state_kind(const StateArgs& a, int64_t jobs, hipStream_t st) {
+  const int64_t narrow_rounds = (jobs * NSLICE + kGpuCUs - 1) / kGpuCUs;
+  const int64_t wide_rounds = (jobs * (NSLICE / 2) + kGpuCUs - 1) / kGpuCUs;
+  if (wide_rounds * kWideStepPct >= narrow_rounds * 100) {
+    hipLaunchKernelGGL((kda_state_kernel<KIND, NVT_NARROW>), dim3((unsigned)(((jobs + 7) / 8) * 8 * NSLICE)),
+                       dim3(64 * SWAVES), 0, st, a.v, a.cu, a.chunk_off, a.h0, a.hT, a.out, a.ws, a.seg, a.T, a.N,
+                       a.Hv, a.mc, a.init_dtype, a.final_dtype, a.nseg, a.seg_len);
+  } else {
+    constexpr int nsl = DV / (16 * NVT_WIDE);
+    hipLaunchKernelGGL((kda_state_kernel<KIND, NVT_WIDE>), dim3((unsigned)(((jobs + 7) / 8) * 8 * nsl)),
+                       dim3(64 * SWAVES), 0, st, a.v, a.cu, a.chunk_off, a.h0, a.hT, a.out, a.ws, a.seg, a.T, a.N,
+                       a.Hv, a.mc, a.init_dtype, a.final_dtype, a.nseg, a.seg_len);
+  }
+}
+
 kda_status launch_state(const kda_fwd_params* p, const void* v, const int64_t* cu_seqlens,
                         const void* initial_state, void* final_state, void* out, void* workspace, hipStream_t st) {
   const bool packed = cu_seqlens != nullptr;
@@ -1629,27 +1695,18 @@ kda_status launch_state(const kda_fwd_params* p, const void* v, const int64_t* c
   const int chains = p->num_seqs * p->H_v;
   int seg_len;
   const int nseg = seg_plan(p, packed, &seg_len);
-  // grid of a launch with `jobs` jobs: groups of 8 jobs, NSLICE workgroups each
-  auto grid = [](int64_t jobs) { return dim3((unsigned)(((jobs + 7) / 8) * 8 * NSLICE)); };
+  const StateArgs a{(const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out, blocks,
+                    seg, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype, p->final_state_dtype, nseg, seg_len};
   if (nseg > 1) {
     // entry states of the segments from their zero-state carries and maps
-    hipLaunchKernelGGL(kda_state_kernel<ST_CARRY>, grid((int64_t)chains * (nseg - 1)), dim3(64 * SWAVES), 0, st,
-                       (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out,
-                       blocks, seg, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype,
-                       p->final_state_dtype, nseg, seg_len);
+    launch_state_kind<ST_CARRY>(a, (int64_t)chains * (nseg - 1), st);
     if (nseg > 2) {
-      hipLaunchKernelGGL(kda_state_kernel<ST_TRANS>, grid((int64_t)chains * (nseg - 2)), dim3(64 * SWAVES), 0, st,
-                         (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out,
-                         blocks, seg, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype,
-                         p->final_state_dtype, nseg, seg_len);
+      launch_state_kind<ST_TRANS>(a, (int64_t)chains * (nseg - 2), st);
       hipLaunchKernelGGL(kda_segment_combine_kernel, dim3((unsigned)(chains * (DV / CMB_ROWS))), dim3(256), 0, st,
                          seg, chains, nseg);
     }
   }
-  hipLaunchKernelGGL(kda_state_kernel<ST_FULL>, grid((int64_t)chains * nseg), dim3(64 * SWAVES), 0, st,
-                     (const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out, blocks,
-                     seg, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype, p->final_state_dtype, nseg,
-                     seg_len);
+  launch_state_kind<ST_FULL>(a, (int64_t)chains * nseg, st);
   return KDA_OK;
 }
 

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+from gated_delta_rule_act_amd import kda
 from gated_delta_rule_act_amd import workloads as W
 from tests import gpu_util as U
 
@@ -49,6 +50,13 @@ CASES = {
     "softplus_no_dt_bias": dict(with_dt_bias=False, T=200),
     "beta_prob": dict(beta_prob=True, T=200),
     "no_l2norm": dict(flags=0, qk_std=1.0 / math.sqrt(128), T=260),
+    # more than 64 (sequence, head) chains: the state launch takes 64-column V slices
+    "wide_slices_safe_lb5": dict(B=17, T=150, Hqk=2, Hv=4, gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-5.0,
+                                 A_log_range=(-4.0, 6.0), g_std=3.0),
+    "wide_slices_softplus_bf16_state": dict(B=20, T=100, init_state_dtype=W.STATE_BF16,
+                                            final_state_dtype=W.STATE_BF16),
+    "wide_slices_pregated_no_state": dict(B=33, T=70, Hqk=1, Hv=2, gate_mode=W.GATE_PREGATED,
+                                          pregated_range=(-1.0, 0.0), init_state_dtype=W.STATE_NONE),
     "pregated_no_l2norm_beta_prob_gva": dict(gate_mode=W.GATE_PREGATED, pregated_range=(-1.0, 0.0), flags=0,
                                               qk_std=1.0 / math.sqrt(128), beta_prob=True, Hqk=2, Hv=4, T=300),
 }
@@ -88,6 +96,31 @@ def test_packed_elementwise(lengths, state, extra):
         if L == 0:
             init = torch.from_numpy(inp.initial_state_f64()[n]).float()
             assert torch.equal(s[n].float().cpu(), init.to(s.dtype).float())
+
+
+def test_packed_wide_slices():
+    # 20 packed sequences x 4 v-heads = 80 chains: 64-column V slices
+    lengths = [1, 64, 65, 0, 130, 7, 200, 64, 3, 90, 128, 1, 33, 70, 250, 5, 64, 100, 2, 150]
+    inp = W.make_inputs(B=1, T=None, Hqk=2, Hv=4, seed=71, lengths=lengths, init_state_dtype=W.STATE_F32)
+    U.log(f"[gpu] packed wide slices, {len(lengths)} sequences")
+    o, s = U.run_gpu(inp)
+    o_ref, s_ref = U.run_oracle(inp)
+    U.assert_parity(U.errors(U.as_f64(o), o_ref, U.as_f64(s), s_ref), "packed wide")
+
+
+def test_wide_slices_match_narrow_bitwise():
+    # 64 chains take 32-column slices, 65 take 64-column ones; the per-element
+    # arithmetic is the same, so the shared sequences agree bit for bit
+    inp = small(B=17, T=333, Hqk=2, Hv=4, gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-5.0)
+    d = U.to_device(inp)
+    U.log("[gpu] wide vs narrow slices")
+    o17, s17 = U.run_gpu(inp, d)
+    sl = {k: d[k][:16].contiguous() for k in ("q", "k", "v", "g", "beta", "h0")}
+    o16, s16 = kda.fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], d["A_log"], d["dt_bias"], inp.scale,
+                       inp.lower_bound, inp.gate_mode, initial_state=sl["h0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o17[:16], o16)
+    assert torch.equal(s17[:16], s16)
 
 
 def test_empty_dense_returns_initial_state():

@@ -30,6 +30,8 @@ CASES = {
     "long_memory_seg8": (dict(B=1, T=2048, A_log_range=(-8.0, -6.0)), 8),
     "more_segments_than_chunks": (dict(B=1, T=200), 7),
     "beta_prob_no_l2norm_seg4": (dict(beta_prob=True, flags=0, qk_std=1.0 / 128 ** 0.5), 4),
+    # 4 chains x 24 segments = 96 jobs per launch: 64-column V slices in every pass
+    "wide_slices_seg24": (dict(B=1, T=2048, gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-5.0), 24),
 }
 
 
