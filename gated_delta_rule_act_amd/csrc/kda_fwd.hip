@@ -806,9 +806,22 @@ constexpr int SWAVES = 4;
 //             started from the identity, on key rows instead of value rows.
 constexpr int SSS = 136;  // sS row stride (fp16): state slice stored as [v][k]
 constexpr int SUS = 72;   // sU row stride (fp16): U' stored as [v][t]
-// sV row stride (16-bit): V slice row-major [t][v]; the four rows a lane
-// group reads sit on different banks
+// sV: the V slice row-major [t][v] (16-bit), rows in groups of 8 with a
+// 64-element gap after each group.  A transposed operand read takes rows
+// r0 + 8 g + (0..3) (g = lane >> 4): the row stride puts the four rows of
+// one lane group on different banks, and the gap shifts the next group by
+// half the banks, so the two lane groups served together do not collide.
 template <int NVT> constexpr int svs() { return NVT == 2 ? 48 : 80; }
+template <int NVT> constexpr int svg() { return 8 * svs<NVT>() + 64; }
+template <int NVT> __device__ __forceinline__ int sv_row(int t) { return (t & 7) * svs<NVT>() + (t >> 3) * svg<NVT>(); }
+// lds_frag_tr over the grouped sV rows (k0 a multiple of 8)
+template <int NVT>
+__device__ __forceinline__ u32x4 sv_frag_tr(const _Float16* sV, int k0, int n0, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const _Float16* p = sV + sv_row<NVT>(k0 + 8 * g) + (i >> 2) * svs<NVT>() + n0 + 4 * (i & 3);
+  const u32x2 a = lds_read_tr16(p), b = lds_read_tr16(p + 4 * svs<NVT>());
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
 
 struct ChunkRegs {
   // arrays indexed only by compile-time values (fully unrolled loops)
@@ -950,17 +963,17 @@ __device__ __forceinline__ void settle(const ChunkRegs& r) {
 template <int KIND, int NVT>
 __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT], ChunkRegs& cur, ChunkRegs& n1,
                                             ChunkRegs& n2, const int c, PendingOut<NVT>& pd) {
-  constexpr int SVS = svs<NVT>();
   const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
   const int64_t row0 = x.bos + (int64_t)c * CH;
   typedef _Float16 half4 __attribute__((ext_vector_type(4)));
   // 1. publish the chunk's vectors, the V slice and the current state.  Every
   //    reader of these buffers in the previous chunk was before its B2.
-  reinterpret_cast<u32x4*>(x.sVec)[16 * wave + (lane & 15)] = cur.vec;
+  // (one lane per address: four lanes writing one address stall the LDS)
+  if (lane < 16) reinterpret_cast<u32x4*>(x.sVec)[16 * wave + lane] = cur.vec;
   if constexpr (KIND != ST_TRANS)
 #pragma unroll
     for (int i = 0; i < NVT / 2; ++i)
-      *reinterpret_cast<u32x4*>(x.sV + (tid >> 2) * SVS + 32 * i + 8 * (tid & 3)) = cur.vraw[i];
+      *reinterpret_cast<u32x4*>(x.sV + sv_row<NVT>(tid >> 2) + 32 * i + 8 * (tid & 3)) = cur.vraw[i];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -992,8 +1005,8 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
     for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
     f32x4 u0 = f32x4{0, 0, 0, 0}, u1 = f32x4{0, 0, 0, 0}, o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
     if constexpr (KIND != ST_TRANS) {
-      const bf16x8 vb0 = __builtin_bit_cast(bf16x8, lds_frag_tr(x.sV, SVS, 0, 16 * vt, lane));
-      const bf16x8 vb1 = __builtin_bit_cast(bf16x8, lds_frag_tr(x.sV, SVS, 32, 16 * vt, lane));
+      const bf16x8 vb0 = __builtin_bit_cast(bf16x8, sv_frag_tr<NVT>(x.sV, 0, 16 * vt, lane));
+      const bf16x8 vb1 = __builtin_bit_cast(bf16x8, sv_frag_tr<NVT>(x.sV, 32, 16 * vt, lane));
       u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[0]), vb0, u0, 0, 0, 0);
       u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[0]), vb0, u1, 0, 0, 0);
       if constexpr (KIND == ST_FULL) {
@@ -1094,7 +1107,7 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
   __shared__ __attribute__((aligned(16))) _Float16 sS[VS * SSS];
   __shared__ __attribute__((aligned(16))) _Float16 sUh[VS * SUS];
   __shared__ __attribute__((aligned(16))) _Float16 sUl[VS * SUS];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[CH * svs<NVT>()];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[(CH / 8) * svg<NVT>()];
 
   // XCD-aware decode: the NSL slices of one job share (id mod 8), so they
   // are dispatched to the same XCD and share its L2 for the job's operands.
