@@ -195,6 +195,14 @@ constexpr int AS = 68;      // fp32 row stride of Akk / T
 constexpr int AQS = 72;     // fp16 row stride of Aqk
 constexpr int KER = 144;    // fp16 row stride of the row-major [t][k] K . 2^G and Kd tiles
 constexpr int WTS = 80;     // fp16 row stride of the [k][t] W staging tile
+// Tiles read by lds_frag_tr_grouped keep their rows in groups of 8 with a 64-element
+// gap after each group: the four rows of a lane group fall on different
+// banks through the row stride, and the gap shifts the next group of rows
+// (the other lane group served in the same pass) by half the banks.
+constexpr int KEG = 8 * KER + 64;  // group stride of the K . 2^G / Kd tiles
+constexpr int WG8 = 8 * WTS + 64;  // group stride of the W staging tile
+__device__ __forceinline__ int ke_row(int t) { return (t & 7) * KER + (t >> 3) * KEG; }
+__device__ __forceinline__ int w_row(int k) { return (k & 7) * WTS + (k >> 3) * WG8; }
 constexpr int NVEC = 19;    // per-channel vectors: P0..3, L0..3, D20, D30, D31, Mr0..3, Mc0..3
 constexpr int V_P = 0, V_L = 4, V_D20 = 8, V_D30 = 9, V_D31 = 10, V_MR = 11, V_MC = 15;
 
@@ -210,7 +218,7 @@ constexpr int L_TOT = L_T;                              // [4][128] f32, inside 
 constexpr int L_MID = L_TOT + 4 * 128 * 4;              // [4][128] f32
 constexpr int L_VEC = L_MID + 4 * 128 * 4;              // [NVEC][128] f32
 constexpr int L_KE = L_T + T_BYTES;
-constexpr int L_AQ = L_KE + 64 * KER * 2;
+constexpr int L_AQ = L_KE + 8 * KEG * 2;
 constexpr int L_RQ = L_AQ + 64 * AQS * 2;
 constexpr int L_RK = L_RQ + 64 * 4;
 constexpr int L_BETA = L_RK + 64 * 4;
@@ -219,8 +227,8 @@ constexpr int L_QD = L_FW + 64 * 4;    // unbounded decays: q_i . k_i per row [6
 constexpr int L_END = L_QD + 64 * 4;
 static_assert(L_VEC + NVEC * 128 * 4 <= L_T + T_BYTES, "vectors fit in region T");
 static_assert(64 * AS * 4 <= X_BYTES, "Akk fits in region X");
-static_assert(128 * WTS * 2 <= X_BYTES, "W staging fits in region X");
-static_assert(64 * KER * 2 <= X_BYTES, "Kd staging fits in region X");
+static_assert(16 * WG8 * 2 <= X_BYTES, "W staging fits in region X");
+static_assert(8 * KEG * 2 <= X_BYTES, "Kd staging fits in region X");
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_row_shr(float x) {
@@ -323,12 +331,14 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const _Float16* p) {
 }
 
 // One 16 x 32 MFMA operand fragment with the contraction index contiguous per
-// lane, read from a row-major [k][n] tile of 16-bit values (row stride ld):
-// lane (i, g) receives column n0 + i, rows k0 + 8g .. k0 + 8g + 7.  Source
-// lane s of a group points at row k0 + 8g + (s >> 2), columns n0 + 4 (s & 3).
-__device__ __forceinline__ u32x4 lds_frag_tr(const _Float16* tile, int ld, int k0, int n0, int lane) {
+// lane, read from a row-major [k][n] tile of 16-bit values whose rows are kept
+// in groups of 8 (row stride ld within a group, group stride gs; k0 a
+// multiple of 8): lane (i, g) receives column n0 + i, rows k0 + 8g .. k0 +
+// 8g + 7.  Source lane s of a group points at row k0 + 8g + (s >> 2),
+// columns n0 + 4 (s & 3).
+__device__ __forceinline__ u32x4 lds_frag_tr_grouped(const _Float16* tile, int ld, int gs, int k0, int n0, int lane) {
   const int i = lane & 15, g = lane >> 4;
-  const _Float16* p = tile + (k0 + 8 * g + (i >> 2)) * ld + n0 + 4 * (i & 3);
+  const _Float16* p = tile + (k0 / 8 + g) * gs + (i >> 2) * ld + n0 + 4 * (i & 3);
   const u32x2 a = lds_read_tr16(p), b = lds_read_tr16(p + 4 * ld);
   return u32x4{a[0], a[1], b[0], b[1]};
 }
@@ -562,7 +572,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = kR[e] * vP[c0 + e];
-        *reinterpret_cast<half8*>(sKE + r * KER + c0) = to_half8(o);
+        *reinterpret_cast<half8*>(sKE + ke_row(r) + c0) = to_half8(o);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -636,11 +646,12 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   for (int part = 0; part < 2; ++part) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      *reinterpret_cast<half8*>(sKd + r * KER + 32 * kb + 8 * lg) = part == 0 ? kdh[kb] : kdl[kb];
+      *reinterpret_cast<half8*>(sKd + ke_row(r) + 32 * kb + 8 * lg) = part == 0 ? kdh[kb] : kdl[kb];
     __syncthreads();
     for (int it = 0; it < 4; ++it) {
       const int fr = wave + 4 * it;  // fragment (km = fr >> 1, kb = fr & 1)
-      st_frag(blk, F_KD + fr * 2 + part, lane, lds_frag_tr(sKd, KER, 32 * (fr & 1), 16 * (fr >> 1), lane));
+      st_frag(blk, F_KD + fr * 2 + part, lane,
+              lds_frag_tr_grouped(sKd, KER, KEG, 32 * (fr & 1), 16 * (fr >> 1), lane));
     }
     __syncthreads();
   }
@@ -741,7 +752,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       for (int e = 0; e < 8; ++e) a[e] = keep ? (_Float16)(sT[t * AS + s0 + e] * sFw[s0 + e]) : (_Float16)0.0f;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const half8 b = __builtin_bit_cast(half8, lds_frag_tr(sKE, KER, 32 * kb, 16 * nt, lane));
+        const half8 b = __builtin_bit_cast(half8, lds_frag_tr_grouped(sKE, KER, KEG, 32 * kb, 16 * nt, lane));
         accw[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, accw[nt], 0, 0, 0);
       }
     }
@@ -768,12 +779,12 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       typedef _Float16 half4 __attribute__((ext_vector_type(4)));
       const half4 hv = {(_Float16)(-accw[nt][0]), (_Float16)(-accw[nt][1]), (_Float16)(-accw[nt][2]),
                         (_Float16)(-accw[nt][3])};
-      *reinterpret_cast<half4*>(sW + (16 * nt + li) * WTS + 16 * wave + 4 * lg) = hv;
+      *reinterpret_cast<half4*>(sW + w_row(16 * nt + li) + 16 * wave + 4 * lg) = hv;
     }
     __syncthreads();
     for (int it = 0; it < 4; ++it) {
       const int fr = wave + 4 * it;  // fragment (ta = fr >> 2, kb = fr & 3)
-      st_frag(blk, F_WN + fr, lane, lds_frag_tr(sW, WTS, 32 * (fr & 3), 16 * (fr >> 2), lane));
+      st_frag(blk, F_WN + fr, lane, lds_frag_tr_grouped(sW, WTS, WG8, 32 * (fr & 3), 16 * (fr >> 2), lane));
     }
   }
 }
@@ -814,14 +825,6 @@ constexpr int SUS = 72;   // sU row stride (fp16): U' stored as [v][t]
 template <int NVT> constexpr int svs() { return NVT == 2 ? 48 : 80; }
 template <int NVT> constexpr int svg() { return 8 * svs<NVT>() + 64; }
 template <int NVT> __device__ __forceinline__ int sv_row(int t) { return (t & 7) * svs<NVT>() + (t >> 3) * svg<NVT>(); }
-// lds_frag_tr over the grouped sV rows (k0 a multiple of 8)
-template <int NVT>
-__device__ __forceinline__ u32x4 sv_frag_tr(const _Float16* sV, int k0, int n0, int lane) {
-  const int i = lane & 15, g = lane >> 4;
-  const _Float16* p = sV + sv_row<NVT>(k0 + 8 * g) + (i >> 2) * svs<NVT>() + n0 + 4 * (i & 3);
-  const u32x2 a = lds_read_tr16(p), b = lds_read_tr16(p + 4 * svs<NVT>());
-  return u32x4{a[0], a[1], b[0], b[1]};
-}
 
 struct ChunkRegs {
   // arrays indexed only by compile-time values (fully unrolled loops)
@@ -1005,8 +1008,8 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
     for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
     f32x4 u0 = f32x4{0, 0, 0, 0}, u1 = f32x4{0, 0, 0, 0}, o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
     if constexpr (KIND != ST_TRANS) {
-      const bf16x8 vb0 = __builtin_bit_cast(bf16x8, sv_frag_tr<NVT>(x.sV, 0, 16 * vt, lane));
-      const bf16x8 vb1 = __builtin_bit_cast(bf16x8, sv_frag_tr<NVT>(x.sV, 32, 16 * vt, lane));
+      const bf16x8 vb0 = __builtin_bit_cast(bf16x8, lds_frag_tr_grouped(x.sV, svs<NVT>(), svg<NVT>(), 0, 16 * vt, lane));
+      const bf16x8 vb1 = __builtin_bit_cast(bf16x8, lds_frag_tr_grouped(x.sV, svs<NVT>(), svg<NVT>(), 32, 16 * vt, lane));
       u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[0]), vb0, u0, 0, 0, 0);
       u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[0]), vb0, u1, 0, 0, 0);
       if constexpr (KIND == ST_FULL) {
