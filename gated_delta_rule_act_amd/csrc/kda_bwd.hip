@@ -61,6 +61,7 @@ constexpr int RS = 132;  // LDS row stride of 128-wide fp32 tiles (rows 4 banks 
 constexpr int QS = 68;   // LDS row stride of 64-wide fp32 tiles
 constexpr int BV = 32;   // V rows per state workgroup
 constexpr int BNS = DV / BV;
+constexpr int PREP_THREADS = 512;  // 8 waves: two per SIMD beside the prep kernel's 157 KB of LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kL2Eps = 1e-6f;
 constexpr float kMinLog2Decay = -1.0e4f;
@@ -168,10 +169,11 @@ __device__ __forceinline__ void load_tile64(float* s, const float* g, int tid) {
   }
 }
 // 64 rows x 128 bf16 (row stride gs elements; rows >= len read as zero) -> fp32 LDS.
+template <int NTH = 256>
 __device__ __forceinline__ void load_bf16_tile128(float* s, const uint16_t* g, size_t gs, int len, int tid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid + 256 * i, r = e >> 4, c = 8 * (e & 15);
+  for (int i = 0; i < 1024 / NTH; ++i) {
+    const int e = tid + NTH * i, r = e >> 4, c = 8 * (e & 15);
     uint4 u = make_uint4(0, 0, 0, 0);
     if (r < len) u = *reinterpret_cast<const uint4*>(g + (size_t)r * gs + c);
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -190,18 +192,19 @@ __device__ __forceinline__ void load_bf16_tile128(float* s, const uint16_t* g, s
 // then composed from sums of nearby decays, never formed as the difference of
 // two large cumulative values.  Rows past the sequence end: zero inputs,
 // beta 0, zero decay.  Thread t: row t >> 2, channels 32 (t & 3) .. +31.
-template <int MODE>
+template <int MODE, int NTH = 256>
 __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* sG, float* sBt, float* sB, const uint16_t* q,
                                                   const uint16_t* k, const uint16_t* g, const uint16_t* beta,
                                                   const float* A_log, const float* dt_bias, int Hqk, int Hv, int h,
                                                   int hq, int64_t row0, int len, float lb, int flags,
                                                   int tid, float* rq_out, float* rk_out) {
-  const int r = tid >> 2, c0 = 32 * (tid & 3);
+  constexpr int TPR = NTH / CH, CPT = DK / TPR;  // threads per row, channels per thread
+  const int r = tid / TPR, c0 = CPT * (tid % TPR);
   const bool ok = r < len;
   const size_t row = (size_t)(row0 + r);
-  float qv[32], kv[32], gv[32];
+  float qv[CPT], kv[CPT], gv[CPT];
 #pragma unroll
-  for (int i = 0; i < 32; i += 8) {
+  for (int i = 0; i < CPT; i += 8) {
     uint4 uq = make_uint4(0, 0, 0, 0), uk = uq, ug = uq;
     if (ok) {
       uq = *reinterpret_cast<const uint4*>(q + (row * Hqk + hq) * DK + c0 + i);
@@ -218,23 +221,29 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
   }
   float sq = 0.0f, sk = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) { sq += qv[i] * qv[i]; sk += kv[i] * kv[i]; }
-  sq += __shfl_xor(sq, 1); sq += __shfl_xor(sq, 2);
-  sk += __shfl_xor(sk, 1); sk += __shfl_xor(sk, 2);
+  for (int i = 0; i < CPT; ++i) { sq += qv[i] * qv[i]; sk += kv[i] * kv[i]; }
+#pragma unroll
+  for (int m = 1; m < TPR; m *= 2) { sq += __shfl_xor(sq, m); sk += __shfl_xor(sk, m); }
   const bool norm = flags & KDA_FLAG_QK_L2NORM;
   const float rq = norm ? rsqrtf(sq + kL2Eps) : 1.0f, rk = norm ? rsqrtf(sk + kL2Eps) : 1.0f;
   if (rq_out) { rq_out[0] = rq; rk_out[0] = rk; }
   const float A_exp = (MODE == KDA_GATE_PREGATED || A_log == nullptr) ? 1.0f : __expf(A_log[h]);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int c = c0 + i;
-    sQ[r * RS + c] = qv[i] * rq;
-    sK[r * RS + c] = kv[i] * rk;
-    float a = 0.0f, d1, d2;
-    if (ok) gate_fwd_bwd<MODE>(gv[i] + (dt_bias ? dt_bias[(size_t)h * DK + c] : 0.0f), A_exp, lb, a, d1, d2);
-    sG[r * RS + c] = fmaxf(a * kLog2e, kMinLog2Decay);
+  for (int i = 0; i < CPT; i += 4) {
+    float g4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float a = 0.0f, d1, d2;
+      if (ok) gate_fwd_bwd<MODE>(gv[i + e] + (dt_bias ? dt_bias[(size_t)h * DK + c0 + i + e] : 0.0f), A_exp, lb, a, d1, d2);
+      g4[e] = fmaxf(a * kLog2e, kMinLog2Decay);
+    }
+    *reinterpret_cast<float4*>(sQ + r * RS + c0 + i) =
+        make_float4(qv[i] * rq, qv[i + 1] * rq, qv[i + 2] * rq, qv[i + 3] * rq);
+    *reinterpret_cast<float4*>(sK + r * RS + c0 + i) =
+        make_float4(kv[i] * rk, kv[i + 1] * rk, kv[i + 2] * rk, kv[i + 3] * rk);
+    *reinterpret_cast<float4*>(sG + r * RS + c0 + i) = make_float4(g4[0], g4[1], g4[2], g4[3]);
   }
-  if ((tid & 3) == 0) {
+  if (tid % TPR == 0) {
     float b = 0.0f;
     if (ok) {
       const float braw = bf2f(beta[row * Hv + h]);
@@ -243,14 +252,21 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
     sB[r] = b;
   }
   __syncthreads();
-  // block-local inclusive sums: thread t owns channel t & 127 and the two
-  // 16-row blocks 2 (t >> 7), 2 (t >> 7) + 1
+  // block-local inclusive sums: thread t owns channel t & 127 and BPT of the
+  // four 16-row blocks; all 16 rows read first, summed in registers, written back
   {
+    constexpr int BPT = 4 * DK / NTH;
     const int c = tid & 127;
-    for (int B = 2 * (tid >> 7); B < 2 * (tid >> 7) + 2; ++B) {
-      float run = 0.0f;
-      for (int rr = 16 * B; rr < 16 * B + 16; ++rr) { run += sG[rr * RS + c]; sG[rr * RS + c] = run; }
-      sBt[B * DK + c] = run;
+#pragma unroll
+    for (int B = BPT * (tid >> 7); B < BPT * (tid >> 7) + BPT; ++B) {
+      float x[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) x[rr] = sG[(16 * B + rr) * RS + c];
+#pragma unroll
+      for (int rr = 1; rr < 16; ++rr) x[rr] += x[rr - 1];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sG[(16 * B + rr) * RS + c] = x[rr];
+      sBt[B * DK + c] = x[15];
     }
   }
   __syncthreads();
@@ -403,7 +419,7 @@ __device__ __forceinline__ void zero_block(f32x4 (&acc)[MT][NT]) {
 // ---------------------------------------------------------------------------
 // prep: per (chunk, v-head) forward quantities in fp32
 template <int MODE>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(PREP_THREADS)
 kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                     const uint16_t* __restrict__ g, const uint16_t* __restrict__ beta, const float* __restrict__ A_log,
                     const float* __restrict__ dt_bias, const int64_t* __restrict__ cu, const int* __restrict__ chunk_off,
@@ -423,69 +439,68 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int hq = h / (Hv / Hqk);
   float* pb = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS;
 
-  for (int e = tid; e < CH * QS; e += 256) { sA[e] = 0.0f; sAq[e] = 0.0f; sT[e] = 0.0f; }
-  load_chunk_inputs<MODE>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, lb,
+  for (int e = tid; e < CH * QS; e += PREP_THREADS) { sA[e] = 0.0f; sAq[e] = 0.0f; sT[e] = 0.0f; }
+  load_chunk_inputs<MODE, PREP_THREADS>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, lb,
                           flags, tid, nullptr, nullptr);
 
-  // Akk and Aqk.  Wave w owns row block w.  Blocks J < w factor through the
-  // row before block w: e^(G_i - G_j) = e^(sG_i) e^(Bt_J - sG_j + sum_{J<B<w} Bt_B),
-  // both exponents <= 0, so each is one fp32 MFMA product over the channels
-  // (A = K or Q times the row factor, B = K times the column factor); the
-  // diagonal block is summed pair by pair.
+  // Akk and Aqk.  Waves 0..3 sum the diagonal block w pair by pair; waves
+  // 4..7 form the off-diagonal blocks (I, J), J < I, two, two, one and one
+  // each.  An off-diagonal block factors through the row before block I:
+  // e^(G_i - G_j) = e^(sG_i) e^(Bt_J - sG_j + sum_{J<B<I} Bt_B), both
+  // exponents <= 0, so it is one fp32 MFMA product over the channels (A = K
+  // or Q times the row factor, B = K times the column factor).
   {
     const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
-    if (w > 0) {
-      f32x4 akk[3], aqk[3];
+    if (w >= 4) {
+      const int u = w - 4;
+      const int ntask = u < 2 ? 2 : 1;
+      for (int task = 0; task < ntask; ++task) {
+        // (1,0) (2,0) | (2,1) (3,0) | (3,1) | (3,2)
+        const int I = u == 0 ? 1 + task : u == 1 ? 2 + task : 3;
+        const int J = u == 0 ? 0 : u == 1 ? 1 - task : u - 1;
+        f32x4 akk = f32x4{0.f, 0.f, 0.f, 0.f}, aqk = akk;
+        const int i = 16 * I + li, j = 16 * J + li;
+#pragma unroll 4
+        for (int kc = 0; kc < DK; kc += 4) {
+          const int c = kc + lg;
+          const float fr = ex2(sG[i * RS + c]);
+          float mid = sBt[J * DK + c];
+          for (int B = J + 1; B < I; ++B) mid += sBt[B * DK + c];
+          const float zb = sK[j * RS + c] * ex2(mid - sG[j * RS + c]);
+          akk = __builtin_amdgcn_mfma_f32_16x16x4f32(sK[i * RS + c] * fr, zb, akk, 0, 0, 0);
+          aqk = __builtin_amdgcn_mfma_f32_16x16x4f32(sQ[i * RS + c] * fr, zb, aqk, 0, 0, 0);
+        }
 #pragma unroll
-      for (int J = 0; J < 3; ++J) { akk[J] = f32x4{0.f, 0.f, 0.f, 0.f}; aqk[J] = akk[J]; }
-      const int i = 16 * w + li;
-      for (int kc = 0; kc < DK; kc += 4) {
-        const int c = kc + lg;
-        const float fr = ex2(sG[i * RS + c]);
-        const float xa = sK[i * RS + c] * fr, ya = sQ[i * RS + c] * fr;
-#pragma unroll
-        for (int J = 0; J < 3; ++J) {
-          if (J < w) {  // uniform per wave
-            const int j = 16 * J + li;
-            float mid = sBt[J * DK + c];
-            for (int B = J + 1; B < w; ++B) mid += sBt[B * DK + c];
-            const float zb = sK[j * RS + c] * ex2(mid - sG[j * RS + c]);
-            akk[J] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, zb, akk[J], 0, 0, 0);
-            aqk[J] = __builtin_amdgcn_mfma_f32_16x16x4f32(ya, zb, aqk[J], 0, 0, 0);
-          }
+        for (int r = 0; r < 4; ++r) {
+          const int ii = 16 * I + 4 * lg + r, jj = 16 * J + li;
+          sA[ii * QS + jj] = sB[ii] * akk[r];
+          sAq[ii * QS + jj] = scale * aqk[r];
         }
       }
-#pragma unroll
-      for (int J = 0; J < 3; ++J)
-        if (J < w)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int ii = 16 * w + 4 * lg + r, jj = 16 * J + li;
-            sA[ii * QS + jj] = sB[ii] * akk[J][r];
-            sAq[ii * QS + jj] = scale * aqk[J][r];
-          }
-    }
-    // diagonal block: the 136 pairs i >= j of block w, two or three per lane
-    for (int pr = lane; pr < 136; pr += 64) {
-      int ii = (int)((sqrtf(8.0f * pr + 1.0f) - 1.0f) * 0.5f);
-      while ((ii + 1) * (ii + 2) / 2 <= pr) ++ii;
-      while (ii * (ii + 1) / 2 > pr) --ii;
-      const int jj = pr - ii * (ii + 1) / 2;
-      const int i = 16 * w + ii, j = 16 * w + jj;
-      float akk = 0.0f, aqk = 0.0f;
-      for (int c = 0; c < DK; c += 4) {
-        const float4 ki = *reinterpret_cast<const float4*>(sK + i * RS + c);
-        const float4 qi = *reinterpret_cast<const float4*>(sQ + i * RS + c);
-        const float4 gi = *reinterpret_cast<const float4*>(sG + i * RS + c);
-        const float4 kj = *reinterpret_cast<const float4*>(sK + j * RS + c);
-        const float4 gj = *reinterpret_cast<const float4*>(sG + j * RS + c);
-        const float e0 = kj.x * ex2(fminf(gi.x - gj.x, 0.0f)), e1 = kj.y * ex2(fminf(gi.y - gj.y, 0.0f));
-        const float e2 = kj.z * ex2(fminf(gi.z - gj.z, 0.0f)), e3 = kj.w * ex2(fminf(gi.w - gj.w, 0.0f));
-        akk += ki.x * e0 + ki.y * e1 + ki.z * e2 + ki.w * e3;
-        aqk += qi.x * e0 + qi.y * e1 + qi.z * e2 + qi.w * e3;
+    } else {
+      // diagonal block: the 136 pairs i >= j of block w, two or three per lane
+      for (int pr = lane; pr < 136; pr += 64) {
+        int ii = (int)((sqrtf(8.0f * pr + 1.0f) - 1.0f) * 0.5f);
+        while ((ii + 1) * (ii + 2) / 2 <= pr) ++ii;
+        while (ii * (ii + 1) / 2 > pr) --ii;
+        const int jj = pr - ii * (ii + 1) / 2;
+        const int i = 16 * w + ii, j = 16 * w + jj;
+        float akk = 0.0f, aqk = 0.0f;
+#pragma unroll 4
+        for (int c = 0; c < DK; c += 4) {
+          const float4 ki = *reinterpret_cast<const float4*>(sK + i * RS + c);
+          const float4 qi = *reinterpret_cast<const float4*>(sQ + i * RS + c);
+          const float4 gi = *reinterpret_cast<const float4*>(sG + i * RS + c);
+          const float4 kj = *reinterpret_cast<const float4*>(sK + j * RS + c);
+          const float4 gj = *reinterpret_cast<const float4*>(sG + j * RS + c);
+          const float e0 = kj.x * ex2(fminf(gi.x - gj.x, 0.0f)), e1 = kj.y * ex2(fminf(gi.y - gj.y, 0.0f));
+          const float e2 = kj.z * ex2(fminf(gi.z - gj.z, 0.0f)), e3 = kj.w * ex2(fminf(gi.w - gj.w, 0.0f));
+          akk += ki.x * e0 + ki.y * e1 + ki.z * e2 + ki.w * e3;
+          aqk += qi.x * e0 + qi.y * e1 + qi.z * e2 + qi.w * e3;
+        }
+        sA[i * QS + j] = jj < ii ? sB[i] * akk : 0.0f;
+        sAq[i * QS + j] = scale * aqk;
       }
-      sA[i * QS + j] = jj < ii ? sB[i] * akk : 0.0f;
-      sAq[i * QS + j] = scale * aqk;
     }
   }
   __syncthreads();
@@ -494,7 +509,7 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // substitution (one wave each, lane = column), then block rows 1..3
   {
     const int w = tid >> 6, lane = tid & 63;
-    if (lane < 16) {
+    if (w < 4 && lane < 16) {
       const int base = 16 * w, cc = lane;
       for (int i = 0; i < 16; ++i) {
         float acc = i == cc ? 1.0f : 0.0f;
@@ -505,35 +520,42 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
   __syncthreads();
   {
-    const int r = tid >> 4, c = tid & 15;
+    // threads 0..255: one element (r, c) of the 16 x 16 block each
+    const int r = (tid >> 4) & 15, c = tid & 15;
+    const bool act = tid < 256;
     for (int I = 1; I < 4; ++I)
       for (int J = 0; J < I; ++J) {
         // X = sum_{K=J}^{I-1} A_IK T_KJ;  T_IJ = -T_II X
-        float xacc = 0.0f;
-        for (int kk = 16 * J; kk < 16 * I; ++kk) xacc += sA[(16 * I + r) * QS + kk] * sT[kk * QS + 16 * J + c];
-        sX[r * 17 + c] = xacc;
+        if (act) {
+          float xacc = 0.0f;
+          for (int kk = 16 * J; kk < 16 * I; ++kk) xacc += sA[(16 * I + r) * QS + kk] * sT[kk * QS + 16 * J + c];
+          sX[r * 17 + c] = xacc;
+        }
         __syncthreads();
-        float t = 0.0f;
-        for (int m = 0; m < 16; ++m) t += sT[(16 * I + r) * QS + 16 * I + m] * sX[m * 17 + c];
-        sT[(16 * I + r) * QS + 16 * J + c] = -t;
+        if (act) {
+          float t = 0.0f;
+          for (int m = 0; m < 16; ++m) t += sT[(16 * I + r) * QS + 16 * I + m] * sX[m * 17 + c];
+          sT[(16 * I + r) * QS + 16 * J + c] = -t;
+        }
         __syncthreads();
       }
   }
 
   // store T and Aqk
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid + 256 * i, r = e >> 4, c = 4 * (e & 15);
+  for (int i = 0; i < 1024 / PREP_THREADS; ++i) {
+    const int e = tid + PREP_THREADS * i, r = e >> 4, c = 4 * (e & 15);
     *reinterpret_cast<float4*>(pb + PB_T + r * 64 + c) = *reinterpret_cast<const float4*>(sT + r * QS + c);
     *reinterpret_cast<float4*>(pb + PB_AQK + r * 64 + c) = *reinterpret_cast<const float4*>(sAq + r * QS + c);
   }
-  // Kd, Qg, Kg, gn: element e = tid + 256 i is row e >> 5, channels 4 (e & 31)
+  // Kd, Qg, Kg, gn: element e = tid + PREP_THREADS i is row e >> 5, channels 4 (e & 31)
   // .. +3, so the 32 lanes of a row store 512 contiguous bytes
   __syncthreads();  // Kg overwrites sK rows that other threads still read above
-  float4 kgv[8];
+  constexpr int KIT = 2048 / PREP_THREADS;
+  float4 kgv[KIT];
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int e = tid + 256 * it, r = e >> 5, c = 4 * (e & 31);
+  for (int it = 0; it < KIT; ++it) {
+    const int e = tid + PREP_THREADS * it, r = e >> 5, c = 4 * (e & 31);
     const float4 kk = *reinterpret_cast<const float4*>(sK + r * RS + c);
     const float4 qq = *reinterpret_cast<const float4*>(sQ + r * RS + c);
     float eg[4], ed[4];
@@ -552,31 +574,31 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     ex2(gabs(sG, sBt, 63, 4 * tid + 2)), ex2(gabs(sG, sBt, 63, 4 * tid + 3)));
   __syncthreads();
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {  // sK now holds Kg
-    const int e = tid + 256 * it, r = e >> 5, c = 4 * (e & 31);
+  for (int it = 0; it < KIT; ++it) {  // sK now holds Kg
+    const int e = tid + PREP_THREADS * it, r = e >> 5, c = 4 * (e & 31);
     *reinterpret_cast<float4*>(sK + r * RS + c) = kgv[it];
   }
   __syncthreads();
   // sQ <- V; sT <- M = T diag(b)
-  load_bf16_tile128(sQ, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
-  for (int e = tid; e < CH * CH; e += 256) {
+  load_bf16_tile128<PREP_THREADS>(sQ, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
+  for (int e = tid; e < CH * CH; e += PREP_THREADS) {
     const int r = e >> 6, c = e & 63;
     sT[r * QS + c] *= sB[c];
   }
   __syncthreads();
-  // W = M Kg, Ubar = M V (fp32 MFMA; wave w: rows 32 (w >> 1) .., columns 64 (w & 1) ..)
+  // W = M Kg, Ubar = M V (split-bf16 MFMA; wave w: rows 32 (w >> 2) .., columns 32 (w & 3) ..)
   {
     const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
-    const int R0 = 32 * (wv >> 1), C0 = 64 * (wv & 1);
-    f32x4 w[2][4], u[2][4];
+    const int R0 = 32 * (wv >> 2), C0 = 32 * (wv & 3);
+    f32x4 w[2][2], u[2][2];
     zero_block(w);
     zero_block(u);
-    mfma_block<false, false, 2, 4>(w, sT, QS, sK, RS, R0, C0, CH, lane);
-    mfma_block<false, false, 2, 4>(u, sT, QS, sQ, RS, R0, C0, CH, lane);
+    mfma_block<false, false, 2, 2>(w, sT, QS, sK, RS, R0, C0, CH, lane);
+    mfma_block<false, false, 2, 2>(u, sT, QS, sQ, RS, R0, C0, CH, lane);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
+      for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = R0 + 16 * m + 4 * lg + r, c = C0 + 16 * n + li;
@@ -1567,7 +1589,7 @@ void launch_bwd(const kda_fwd_params* p, const void* q, const void* k, const voi
   if (packed) launch_chunk_map(cu, p->num_seqs, chunk_off, st);
   const dim3 cg((unsigned)mc, (unsigned)p->H_v);
   if (mc > 0)
-    hipLaunchKernelGGL(kda_bwd_prep_kernel<MODE>, cg, dim3(256), 0, st, qq, kk, vv, gg, bb, A_log, dt_bias, cu,
+    hipLaunchKernelGGL(kda_bwd_prep_kernel<MODE>, cg, dim3(PREP_THREADS), 0, st, qq, kk, vv, gg, bb, A_log, dt_bias, cu,
                        chunk_off, p->T, p->num_seqs, p->H_qk, p->H_v, (int)mc, p->scale, p->lower_bound, p->flags, ws);
   if (chains > 0) {
     float* seg = ws + (size_t)p->H_v * mc * CHUNK_HEAD_FLOATS + gqa_floats(p);
