@@ -62,6 +62,7 @@ constexpr int QS = 68;   // LDS row stride of 64-wide fp32 tiles
 constexpr int BV = 32;   // V rows per state workgroup
 constexpr int BNS = DV / BV;
 constexpr int PREP_THREADS = 512;  // 8 waves: two per SIMD beside the prep kernel's 157 KB of LDS
+constexpr int PAIR_THREADS = 512;  // the same for the pair kernel (147 KB)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kL2Eps = 1e-6f;
 constexpr float kMinLog2Decay = -1.0e4f;
@@ -1156,7 +1157,7 @@ __device__ __forceinline__ float sum16(float x) {
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(PAIR_THREADS)
 kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ g,
                     const uint16_t* __restrict__ beta, const float* __restrict__ A_log,
                     const float* __restrict__ dt_bias, const int64_t* __restrict__ cu,
@@ -1172,6 +1173,7 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   __shared__ float sRq[CH], sRk[CH];
   __shared__ float sCol[16 * DK];
   __shared__ float sRed[8];
+  __shared__ float sRow[3][2][CH];  // per-row partial sums of the two channel halves
   __shared__ __attribute__((aligned(16))) float sBt[4 * DK];
   const int x = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const ChunkLoc L = chunk_loc(x, cu, chunk_off, T, N);
@@ -1184,38 +1186,44 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
   const int hq = h / (Hv / Hqk);
   float rq, rk;
-  load_chunk_inputs<MODE>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, lb,
-                          flags, tid, &rq, &rk);
-  if ((tid & 3) == 0) { sRq[tid >> 2] = rq; sRk[tid >> 2] = rk; }
-  load_tile64(sDA, gb + GB_DAKK, tid);
-  load_tile64(sDQ, gb + GB_DAQK, tid);
+  load_chunk_inputs<MODE, PAIR_THREADS>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0,
+                                        L.len, lb, flags, tid, &rq, &rk);
+  constexpr int TPR = PAIR_THREADS / CH;
+  if (tid % TPR == 0) { sRq[tid / TPR] = rq; sRk[tid / TPR] = rk; }
+  if (tid < 256) {
+    load_tile64(sDA, gb + GB_DAKK, tid);
+    load_tile64(sDQ, gb + GB_DAQK, tid);
+  }
   __syncthreads();
 
-  const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
+  // wave (w, half): row block w = wave & 3, channel columns 16 (nb + n) + li,
+  // n < 4, nb = 4 (wave >> 2)
+  const int lane = tid & 63, wave = tid >> 6, w = wave & 3, half = wave >> 2, nb = 4 * half;
+  const int li = lane & 15, lg = lane >> 4;
   const int rbase = 16 * w + 4 * lg;  // own rows rbase + r
-  float Ko[8][4], Qo[8][4], Go[8][4];
+  float Ko[4][4], Qo[4][4], Go[4][4];
 #pragma unroll
-  for (int n = 0; n < 8; ++n)
+  for (int n = 0; n < 4; ++n)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int e = (rbase + r) * RS + 16 * n + li;
+      const int e = (rbase + r) * RS + 16 * (nb + n) + li;
       Ko[n][r] = sK[e];
       Qo[n][r] = sQ[e];
       Go[n][r] = sG[e];
     }
 
   // ---- row side: R1, R2 for own rows
-  f32x4 R1[8], R2[8];
+  f32x4 R1[4], R2[4];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) { R1[n] = f32x4{0.f, 0.f, 0.f, 0.f}; R2[n] = R1[n]; }
+  for (int n = 0; n < 4; ++n) { R1[n] = f32x4{0.f, 0.f, 0.f, 0.f}; R2[n] = R1[n]; }
   if (w > 0) {
     // p = 16 w - 1: G_i - G_p = sG_i;  G_p - G_j = Bt_J - sG_j + sum_{J<B<w} Bt_B
     for (int J = 0; J < w; ++J) {
-      float mid[8];
+      float mid[4];
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        float o = sBt[J * DK + 16 * n + li];
-        for (int B = J + 1; B < w; ++B) o += sBt[B * DK + 16 * n + li];
+      for (int n = 0; n < 4; ++n) {
+        float o = sBt[J * DK + 16 * (nb + n) + li];
+        for (int B = J + 1; B < w; ++B) o += sBt[B * DK + 16 * (nb + n) + li];
         mid[n] = o;
       }
 #pragma unroll
@@ -1223,8 +1231,8 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         const int j = 16 * J + 4 * kk + lg;
         const float a = sDA[(16 * w + li) * QS + j], b = sDQ[(16 * w + li) * QS + j];
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const int c = 16 * n + li;
+        for (int n = 0; n < 4; ++n) {
+          const int c = 16 * (nb + n) + li;
           const float z = sK[j * RS + c] * ex2(mid[n] - sG[j * RS + c]);
           R1[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, z, R1[n], 0, 0, 0);
           R2[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(b, z, R2[n], 0, 0, 0);
@@ -1232,7 +1240,7 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       }
     }
 #pragma unroll
-    for (int n = 0; n < 8; ++n)
+    for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float f = ex2(Go[n][r]);
@@ -1246,8 +1254,8 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
     for (int r = 0; r < 4; ++r) { a[r] = sDA[(rbase + r) * QS + j]; b[r] = sDQ[(rbase + r) * QS + j]; }
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int c = 16 * n + li;
+    for (int n = 0; n < 4; ++n) {
+      const int c = 16 * (nb + n) + li;
       const float kj = sK[j * RS + c], gj = sG[j * RS + c];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1259,29 +1267,29 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
 
   // ---- column side: C for own rows (as j)
-  f32x4 Cc[8];
+  f32x4 Cc[4];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) Cc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < 4; ++n) Cc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int I = w + 1; I < 4; ++I) {
-    f32x4 X[8];
+    f32x4 X[4];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) X[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < 4; ++n) X[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int i = 16 * I + 4 * kk + lg;
       const float a = sB[i] * sDA[i * QS + 16 * w + li], b = sDQ[i * QS + 16 * w + li];
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const int c = 16 * n + li;
+      for (int n = 0; n < 4; ++n) {
+        const int c = 16 * (nb + n) + li;
         const float f = ex2(sG[i * RS + c]);
         X[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sK[i * RS + c] * f, X[n], 0, 0, 0);
         X[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(b, scale * sQ[i * RS + c] * f, X[n], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      float mid = sBt[w * DK + 16 * n + li];
-      for (int B = w + 1; B < I; ++B) mid += sBt[B * DK + 16 * n + li];
+    for (int n = 0; n < 4; ++n) {
+      float mid = sBt[w * DK + 16 * (nb + n) + li];
+      for (int B = w + 1; B < I; ++B) mid += sBt[B * DK + 16 * (nb + n) + li];
 #pragma unroll
       for (int r = 0; r < 4; ++r) Cc[n][r] += X[n][r] * ex2(mid - Go[n][r]);
     }
@@ -1293,8 +1301,8 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
     for (int r = 0; r < 4; ++r) { a[r] = bi * sDA[i * QS + rbase + r]; b[r] = sDQ[i * QS + rbase + r]; }
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int c = 16 * n + li;
+    for (int n = 0; n < 4; ++n) {
+      const int c = 16 * (nb + n) + li;
       const float ki = sK[i * RS + c], qi = scale * sQ[i * RS + c], gi = sG[i * RS + c];
 #pragma unroll
       for (int r = 0; r < 4; ++r) Cc[n][r] += (a[r] * ki + b[r] * qi) * ex2(fminf(gi - Go[n][r], 0.0f));
@@ -1302,11 +1310,11 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
 
   // ---- combine: dK, dQ (w.r.t. scale q_hat), dG; dbeta from Akk
-  float dK[8][4], dQ[8][4], dG[8][4], dbk[4];
+  float dK[4][4], dQ[4][4], dG[4][4], dbk[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) dbk[r] = 0.0f;
 #pragma unroll
-  for (int n = 0; n < 8; ++n)
+  for (int n = 0; n < 4; ++n)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float bo = sB[rbase + r];
@@ -1317,12 +1325,12 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 
   // ---- elementwise factors: Qg = scale Q e^G, Kg = K e^G, Kd = K e^(G_last - G), gn = e^G_last
-  float colKd[8];
+  float colKd[4];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) colKd[n] = 0.0f;
+  for (int n = 0; n < 4; ++n) colKd[n] = 0.0f;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const int c = 16 * n + li;
+  for (int n = 0; n < 4; ++n) {
+    const int c = 16 * (nb + n) + li;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = rbase + r;
@@ -1337,13 +1345,13 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
   // dG of the chunk's last row gains sum_t dKd . Kd and dgn . gn
 #pragma unroll
-  for (int n = 0; n < 8; ++n) sCol[(4 * w + lg) * DK + 16 * n + li] = colKd[n];
+  for (int n = 0; n < 4; ++n) sCol[(4 * w + lg) * DK + 16 * (nb + n) + li] = colKd[n];
   __syncthreads();  // also: every read of sQ above is done
   // dG -> sQ, then the reverse cumulative sum over rows gives d a per token
 #pragma unroll
-  for (int n = 0; n < 8; ++n)
+  for (int n = 0; n < 4; ++n)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sQ[(rbase + r) * RS + 16 * n + li] = dG[n][r];
+    for (int r = 0; r < 4; ++r) sQ[(rbase + r) * RS + 16 * (nb + n) + li] = dG[n][r];
   __syncthreads();
   if (tid < DK) {
     float sum = gb[GB_DGN + tid] * ex2(gabs(sG, sBt, 63, tid));
@@ -1352,88 +1360,105 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
   __syncthreads();
   {
-    const int c = tid & 127, half = tid >> 7;
-    float run = 0.0f;
-    for (int rr = 32 * half + 31; rr >= 32 * half; --rr) { run += sQ[rr * RS + c]; sQ[rr * RS + c] = run; }
+    // thread (c, qr): suffix sums over rows 16 qr .. 16 qr + 15, then the
+    // totals of the later row quarters are added
+    const int c = tid & 127, qr = tid >> 7;
+    float x[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) x[rr] = sQ[(16 * qr + rr) * RS + c];
+#pragma unroll
+    for (int rr = 14; rr >= 0; --rr) x[rr] += x[rr + 1];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sQ[(16 * qr + rr) * RS + c] = x[rr];
     __syncthreads();
-    if (half == 0) {
-      const float base = sQ[32 * RS + c];
-      for (int rr = 0; rr < 32; ++rr) sQ[rr * RS + c] += base;
-    }
+    float base = 0.0f;
+    for (int q2 = 3; q2 > qr; --q2) base += sQ[(16 * q2) * RS + c];
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sQ[(16 * qr + rr) * RS + c] = x[rr] + base;
   }
   __syncthreads();
 
   // ---- gate: a = f(x), x = g + dt_bias;  norms;  beta
   const float A_exp = (MODE == KDA_GATE_PREGATED || A_log == nullptr) ? 1.0f : __expf(A_log[h]);
   const bool norm = flags & KDA_FLAG_QK_L2NORM;
-  float colDt[8], dA = 0.0f;
+  float colDt[4], dA = 0.0f;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) colDt[n] = 0.0f;
-  float dtb[8];
+  for (int n = 0; n < 4; ++n) colDt[n] = 0.0f;
+  float dtb[4];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) dtb[n] = dt_bias ? dt_bias[(size_t)h * DK + 16 * n + li] : 0.0f;
+  for (int n = 0; n < 4; ++n) dtb[n] = dt_bias ? dt_bias[(size_t)h * DK + 16 * (nb + n) + li] : 0.0f;
+  float dgo[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = rbase + r;
     const bool ok = row < L.len;  // uniform over the 16 lanes of the row
     const size_t trow = (size_t)(L.row0 + row);
-    float dgo[8];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int c = 16 * n + li;
+    for (int n = 0; n < 4; ++n) {
+      const int c = 16 * (nb + n) + li;
       const float da = sQ[row * RS + c];
       const float gv = ok ? bf2f(g[(trow * Hv + h) * DK + c]) : 0.0f;
       float a, dadx, dadA;
       gate_fwd_bwd<MODE>(gv + dtb[n], A_exp, lb, a, dadx, dadA);
       // below the decay floor the factor e^a is exactly zero in fp32
       if (a * kLog2e < kMinLog2Decay) dadx = dadA = 0.0f;
-      dgo[n] = ok ? da * dadx : 0.0f;
-      colDt[n] += dgo[n];
+      dgo[n][r] = ok ? da * dadx : 0.0f;
+      colDt[n] += dgo[n][r];
       if (ok) dA += da * dadA;
     }
-    // y = q/|q| (the operand is scale y): dq = r (dy - y (y . dy)), dy = scale dQ
+    // this half's share of the row sums y . dy (q and k) and of dbeta
     float yq = 0.0f, yk = 0.0f;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+    for (int n = 0; n < 4; ++n) {
       yq += Qo[n][r] * (scale * dQ[n][r]);
       yk += Ko[n][r] * dK[n][r];
     }
-    yq = norm ? sum16(yq) : 0.0f;
-    yk = norm ? sum16(yk) : 0.0f;
-    const float dbsum = sum16(dbk[r]);
-    if (ok) {
-      const float rqi = sRq[row], rki = sRk[row];
-      const int hh = qk_heads_out == Hqk ? hq : h;
-      float* pq = dq + (trow * qk_heads_out + hh) * DK;
-      float* pk = dk + (trow * qk_heads_out + hh) * DK;
-      float* pg = dg + (trow * Hv + h) * DK;
+    yq = sum16(yq);
+    yk = sum16(yk);
+    const float dbs = sum16(dbk[r]);
+    if (li == 0) { sRow[0][half][row] = yq; sRow[1][half][row] = yk; sRow[2][half][row] = dbs; }
+  }
+  __syncthreads();
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const int c = 16 * n + li;
-        pq[c] = rqi * (scale * dQ[n][r] - Qo[n][r] * yq);
-        pk[c] = rki * (dK[n][r] - Ko[n][r] * yk);
-        pg[c] = dgo[n];
-      }
-      if (li == 0) {
-        const float db = gb[GB_DB + row] + dbsum;
-        const float b = sB[row];
-        dbeta[trow * Hv + h] = (flags & KDA_FLAG_BETA_IS_PROB) ? db : db * b * (1.0f - b);
-      }
+  for (int r = 0; r < 4; ++r) {
+    const int row = rbase + r;
+    if (row >= L.len) continue;  // uniform over the 16 lanes of the row
+    const size_t trow = (size_t)(L.row0 + row);
+    // y = q/|q| (the operand is scale y): dq = r (dy - y (y . dy)), dy = scale dQ
+    const float yq = norm ? sRow[0][0][row] + sRow[0][1][row] : 0.0f;
+    const float yk = norm ? sRow[1][0][row] + sRow[1][1][row] : 0.0f;
+    const float rqi = sRq[row], rki = sRk[row];
+    const int hh = qk_heads_out == Hqk ? hq : h;
+    float* pq = dq + (trow * qk_heads_out + hh) * DK;
+    float* pk = dk + (trow * qk_heads_out + hh) * DK;
+    float* pg = dg + (trow * Hv + h) * DK;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int c = 16 * (nb + n) + li;
+      pq[c] = rqi * (scale * dQ[n][r] - Qo[n][r] * yq);
+      pk[c] = rki * (dK[n][r] - Ko[n][r] * yk);
+      pg[c] = dgo[n][r];
+    }
+    if (li == 0 && half == 0) {
+      const float db = gb[GB_DB + row] + (sRow[2][0][row] + sRow[2][1][row]);
+      const float b = sB[row];
+      dbeta[trow * Hv + h] = (flags & KDA_FLAG_BETA_IS_PROB) ? db : db * b * (1.0f - b);
     }
   }
   // per-chunk partials of ddt_bias (column sums) and dA_log
 #pragma unroll
-  for (int n = 0; n < 8; ++n) sCol[(4 * w + lg) * DK + 16 * n + li] = colDt[n];
+  for (int n = 0; n < 4; ++n) sCol[(4 * w + lg) * DK + 16 * (nb + n) + li] = colDt[n];
   dA += __shfl_xor(dA, 1); dA += __shfl_xor(dA, 2); dA += __shfl_xor(dA, 4); dA += __shfl_xor(dA, 8);
   dA += __shfl_xor(dA, 16); dA += __shfl_xor(dA, 32);
-  if (lane == 0) sRed[w] = dA;
+  if (lane == 0) sRed[wave] = dA;
   __syncthreads();
   if (tid < DK) {
     float sum = 0.0f;
     for (int rg = 0; rg < 16; ++rg) sum += sCol[rg * DK + tid];
     gp[tid] = sum;
   }
-  if (tid == 0) gp[DK] = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+  if (tid == 0) gp[DK] = ((sRed[0] + sRed[1]) + (sRed[2] + sRed[3])) + ((sRed[4] + sRed[5]) + (sRed[6] + sRed[7]));
 }
 
 // q/k gradients summed over the v-heads sharing a q/k head; gate-parameter
@@ -1626,7 +1651,7 @@ void launch_bwd(const kda_fwd_params* p, const void* q, const void* k, const voi
   if (mc > 0) {
     hipLaunchKernelGGL(kda_bwd_dense_kernel, cg, dim3(256), 0, st, vv, dd, bb, cu, chunk_off, p->T, p->num_seqs,
                        p->H_v, (int)mc, p->flags, dv, ws);
-    hipLaunchKernelGGL(kda_bwd_pair_kernel<MODE>, cg, dim3(256), 0, st, qq, kk, gg, bb, A_log, dt_bias, cu, chunk_off,
+    hipLaunchKernelGGL(kda_bwd_pair_kernel<MODE>, cg, dim3(PAIR_THREADS), 0, st, qq, kk, gg, bb, A_log, dt_bias, cu, chunk_off,
                        p->T, p->num_seqs, p->H_qk, p->H_v, (int)mc, p->scale, p->lower_bound, p->flags, dqv, dkv,
                        G > 1 ? p->H_v : p->H_qk, dg, dbeta, ws);
     if (G > 1) {
