@@ -63,6 +63,7 @@ constexpr int BV = 32;   // V rows per state workgroup
 constexpr int BNS = DV / BV;
 constexpr int PREP_THREADS = 512;  // 8 waves: two per SIMD beside the prep kernel's 157 KB of LDS
 constexpr int PAIR_THREADS = 512;  // the same for the pair kernel (147 KB)
+constexpr int DENSE_THREADS = 512;  // and for the dense kernel (152 KB)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kL2Eps = 1e-6f;
 constexpr float kMinLog2Decay = -1.0e4f;
@@ -154,18 +155,20 @@ __device__ __forceinline__ ChunkLoc chunk_loc(int x, const int64_t* cu, const in
 }
 
 // 64 x 128 fp32 global tile (row stride gs floats) -> LDS rows of stride RS.
+template <int NTH = 256>
 __device__ __forceinline__ void load_tile128(float* s, const float* g, int gs, int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = tid + 256 * i, r = e >> 5, c = 4 * (e & 31);
+  for (int i = 0; i < 2048 / NTH; ++i) {
+    const int e = tid + NTH * i, r = e >> 5, c = 4 * (e & 31);
     *reinterpret_cast<float4*>(s + r * RS + c) = *reinterpret_cast<const float4*>(g + (size_t)r * gs + c);
   }
 }
 // 64 x 64 fp32 global tile (dense, stride 64) -> LDS rows of stride QS.
+template <int NTH = 256>
 __device__ __forceinline__ void load_tile64(float* s, const float* g, int tid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid + 256 * i, r = e >> 4, c = 4 * (e & 15);
+  for (int i = 0; i < 1024 / NTH; ++i) {
+    const int e = tid + NTH * i, r = e >> 4, c = 4 * (e & 15);
     *reinterpret_cast<float4*>(s + r * QS + c) = *reinterpret_cast<const float4*>(g + r * 64 + c);
   }
 }
@@ -953,7 +956,7 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
 // receives C[4 lg + r][li] (r < 4) of each 16 x 16 tile.  Wave w computes
 // rows 32 (w >> 1) .. +31 of every product: columns 64 (w & 1) .. +63 of the
 // 128-wide ones, 32 (w & 1) .. +31 of the 64-wide ones.
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(DENSE_THREADS)
 kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_out,
                      const uint16_t* __restrict__ beta, const int64_t* __restrict__ cu,
                      const int* __restrict__ chunk_off, int T, int N, int Hv, int mc, int flags,
@@ -964,89 +967,91 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   __shared__ __attribute__((aligned(16))) float B3[CH * RS];
   __shared__ __attribute__((aligned(16))) float sT[CH * QS];
   __shared__ float sB[CH];
-  __shared__ float sRed[2 * DK];
+  __shared__ float sRed[4 * DK];
   const int x = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const ChunkLoc L = chunk_loc(x, cu, chunk_off, T, N);
   if (L.len == 0) return;
   float* pb = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS;
   float* sb = pb + PB_FLOATS;
   float* gb = sb + SB_FLOATS;
+  // wave w: rows 32 (w >> 2) .. of every output, columns 32 (w & 3) .. of the
+  // 128-wide ones and 16 (w & 3) .. of the 64-wide ones
   const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
-  const int R0 = 32 * (w >> 1), C0 = 64 * (w & 1), Q0 = 32 * (w & 1);
+  const int R0 = 32 * (w >> 2), C0 = 32 * (w & 3), Q0 = 16 * (w & 3);
+  constexpr int NTH = DENSE_THREADS;
 
   // 1. dO, dU, U and the first half of S (rows v < 64)
-  load_bf16_tile128(B0, d_out + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
-  load_tile128(B1, sb + SB_DU, DV, tid);
-  load_tile128(B2, sb + SB_U, DV, tid);
-  load_tile128(B3, sb + SB_H, DK, tid);
+  load_bf16_tile128<NTH>(B0, d_out + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
+  load_tile128<NTH>(B1, sb + SB_DU, DV, tid);
+  load_tile128<NTH>(B2, sb + SB_U, DV, tid);
+  load_tile128<NTH>(B3, sb + SB_H, DK, tid);
   __syncthreads();
   // 2. dQg = dO S and dW = -dU S, contracting over v in two halves
-  f32x4 dqg[2][4], dw[2][4];
+  f32x4 dqg[2][2], dw[2][2];
   zero_block(dqg);
   zero_block(dw);
-  mfma_block<false, false, 2, 4>(dqg, B0, RS, B3, RS, R0, C0, 64, lane);
-  mfma_block<false, false, 2, 4>(dw, B1, RS, B3, RS, R0, C0, 64, lane);
+  mfma_block<false, false, 2, 2>(dqg, B0, RS, B3, RS, R0, C0, 64, lane);
+  mfma_block<false, false, 2, 2>(dw, B1, RS, B3, RS, R0, C0, 64, lane);
   __syncthreads();
-  load_tile128(B3, sb + SB_H + 64 * DK, DK, tid);
+  load_tile128<NTH>(B3, sb + SB_H + 64 * DK, DK, tid);
   __syncthreads();
-  mfma_block<false, false, 2, 4>(dqg, B0 + 64, RS, B3, RS, R0, C0, 64, lane);
-  mfma_block<false, false, 2, 4>(dw, B1 + 64, RS, B3, RS, R0, C0, 64, lane);
+  mfma_block<false, false, 2, 2>(dqg, B0 + 64, RS, B3, RS, R0, C0, 64, lane);
+  mfma_block<false, false, 2, 2>(dw, B1 + 64, RS, B3, RS, R0, C0, 64, lane);
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) gb[GB_DQG + BLK_ROW(R0, m, r) * DK + BLK_COL(C0, n)] = dqg[m][n][r];
   // 3. dAqk = dO U^T, lower triangle including the diagonal
   {
-    f32x4 a[2][2];
+    f32x4 a[2][1];
     zero_block(a);
-    mfma_block<false, true, 2, 2>(a, B0, RS, B2, RS, R0, Q0, DV, lane);
+    mfma_block<false, true, 2, 1>(a, B0, RS, B2, RS, R0, Q0, DV, lane);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = BLK_ROW(R0, m, r), j = BLK_COL(Q0, 0);
+        gb[GB_DAQK + i * 64 + j] = j <= i ? a[m][0][r] : 0.0f;
+      }
+  }
+  __syncthreads();
+  // 4. dKd = U dS', contracting over v in two halves; dgn = colsum(dS' . S)
+  {
+    f32x4 dkd[2][2];
+    zero_block(dkd);
+    load_tile128<NTH>(B3, sb + SB_DH, DK, tid);
+    __syncthreads();
+    mfma_block<false, false, 2, 2>(dkd, B2, RS, B3, RS, R0, C0, 64, lane);
+    __syncthreads();
+    load_tile128<NTH>(B3, sb + SB_DH + 64 * DK, DK, tid);
+    __syncthreads();
+    mfma_block<false, false, 2, 2>(dkd, B2 + 64, RS, B3, RS, R0, C0, 64, lane);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = BLK_ROW(R0, m, r), j = BLK_COL(Q0, n);
-          gb[GB_DAQK + i * 64 + j] = j <= i ? a[m][n][r] : 0.0f;
-        }
-  }
-  __syncthreads();
-  // 4. dKd = U dS', contracting over v in two halves; dgn = colsum(dS' . S)
-  {
-    f32x4 dkd[2][4];
-    zero_block(dkd);
-    load_tile128(B3, sb + SB_DH, DK, tid);
-    __syncthreads();
-    mfma_block<false, false, 2, 4>(dkd, B2, RS, B3, RS, R0, C0, 64, lane);
-    __syncthreads();
-    load_tile128(B3, sb + SB_DH + 64 * DK, DK, tid);
-    __syncthreads();
-    mfma_block<false, false, 2, 4>(dkd, B2 + 64, RS, B3, RS, R0, C0, 64, lane);
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-#pragma unroll
         for (int r = 0; r < 4; ++r) gb[GB_DKD + BLK_ROW(R0, m, r) * DK + BLK_COL(C0, n)] = dkd[m][n][r];
-    const int c = tid & 127, half = tid >> 7;
+    // dgn: four quarters of the rows, one per 128 threads
+    const int c = tid & 127, qr = tid >> 7;
     float acc = 0.0f;
-    for (int vv = 64 * half; vv < 64 * half + 64; ++vv) acc += sb[SB_DH + vv * DK + c] * sb[SB_H + vv * DK + c];
-    sRed[half * DK + c] = acc;
+    for (int vv = 32 * qr; vv < 32 * qr + 32; ++vv) acc += sb[SB_DH + vv * DK + c] * sb[SB_H + vv * DK + c];
+    sRed[qr * DK + c] = acc;
   }
   __syncthreads();
-  if (tid < DK) gb[GB_DGN + tid] = sRed[tid] + sRed[DK + tid];
+  if (tid < DK) gb[GB_DGN + tid] = (sRed[tid] + sRed[DK + tid]) + (sRed[2 * DK + tid] + sRed[3 * DK + tid]);
   // 5. B3 <- dW, B0 <- Kg, B2 <- V, sT <- T, sB <- beta
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) B3[BLK_ROW(R0, m, r) * RS + BLK_COL(C0, n)] = -dw[m][n][r];
-  load_tile128(B0, pb + PB_KG, DK, tid);
-  load_bf16_tile128(B2, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
-  load_tile64(sT, pb + PB_T, tid);
+  load_tile128<NTH>(B0, pb + PB_KG, DK, tid);
+  load_bf16_tile128<NTH>(B2, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
+  load_tile64<NTH>(sT, pb + PB_T, tid);
   if (tid < CH) {
     float b = 0.0f;
     if (tid < L.len) {
@@ -1057,14 +1062,14 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   }
   __syncthreads();
   // 6. dM = dU V^T + dW Kg^T;  dV = M^T dU;  dKg = M^T dW  (M = T diag(b))
-  f32x4 dm[2][2];
+  f32x4 dm[2][1];
   zero_block(dm);
-  mfma_block<false, true, 2, 2>(dm, B1, RS, B2, RS, R0, Q0, DV, lane);
-  mfma_block<false, true, 2, 2>(dm, B3, RS, B0, RS, R0, Q0, DK, lane);
+  mfma_block<false, true, 2, 1>(dm, B1, RS, B2, RS, R0, Q0, DV, lane);
+  mfma_block<false, true, 2, 1>(dm, B3, RS, B0, RS, R0, Q0, DK, lane);
   {
-    f32x4 a[2][4];
+    f32x4 a[2][2];
     zero_block(a);
-    mfma_block<true, false, 2, 4>(a, sT, QS, B1, RS, R0, C0, CH, lane);
+    mfma_block<true, false, 2, 2>(a, sT, QS, B1, RS, R0, C0, CH, lane);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -1073,15 +1078,15 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
         if (t < L.len) {
           float* d = dv + ((size_t)(L.row0 + t) * Hv + h) * DV;
 #pragma unroll
-          for (int n = 0; n < 4; ++n) d[BLK_COL(C0, n)] = sB[t] * a[m][n][r];
+          for (int n = 0; n < 2; ++n) d[BLK_COL(C0, n)] = sB[t] * a[m][n][r];
         }
       }
     zero_block(a);
-    mfma_block<true, false, 2, 4>(a, sT, QS, B3, RS, R0, C0, CH, lane);
+    mfma_block<true, false, 2, 2>(a, sT, QS, B3, RS, R0, C0, CH, lane);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
+      for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = BLK_ROW(R0, m, r);
@@ -1096,13 +1101,11 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = BLK_ROW(R0, m, r), j = BLK_COL(Q0, n);
-        sDM[i * QS + j] = dm[m][n][r];
-        sDT[i * QS + j] = dm[m][n][r] * sB[j];
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int i = BLK_ROW(R0, m, r), j = BLK_COL(Q0, 0);
+      sDM[i * QS + j] = dm[m][0][r];
+      sDT[i * QS + j] = dm[m][0][r] * sB[j];
+    }
   __syncthreads();
   if (tid < CH) {
     float acc = 0.0f;
@@ -1110,28 +1113,24 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
     gb[GB_DB + tid] = acc;
   }
   {
-    f32x4 a[2][2];
+    f32x4 a[2][1];
     zero_block(a);
-    mfma_block<true, false, 2, 2>(a, sT, QS, sDT, QS, R0, Q0, CH, lane);
+    mfma_block<true, false, 2, 1>(a, sT, QS, sDT, QS, R0, Q0, CH, lane);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sX[BLK_ROW(R0, m, r) * QS + BLK_COL(Q0, n)] = a[m][n][r];
+      for (int r = 0; r < 4; ++r) sX[BLK_ROW(R0, m, r) * QS + BLK_COL(Q0, 0)] = a[m][0][r];
     __syncthreads();
     zero_block(a);
-    mfma_block<false, true, 2, 2>(a, sX, QS, sT, QS, R0, Q0, CH, lane);
+    mfma_block<false, true, 2, 1>(a, sX, QS, sT, QS, R0, Q0, CH, lane);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = BLK_ROW(R0, m, r), j = BLK_COL(Q0, n);
-          gb[GB_DAKK + i * 64 + j] = j < i ? -a[m][n][r] : 0.0f;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int i = BLK_ROW(R0, m, r), j = BLK_COL(Q0, 0);
+        gb[GB_DAKK + i * 64 + j] = j < i ? -a[m][0][r] : 0.0f;
+      }
   }
 }
 
@@ -1649,7 +1648,7 @@ void launch_bwd(const kda_fwd_params* p, const void* q, const void* k, const voi
                        cu, chunk_off, T, N, H, (int)mc, ws, seg, nseg, seg_len);
   }
   if (mc > 0) {
-    hipLaunchKernelGGL(kda_bwd_dense_kernel, cg, dim3(256), 0, st, vv, dd, bb, cu, chunk_off, p->T, p->num_seqs,
+    hipLaunchKernelGGL(kda_bwd_dense_kernel, cg, dim3(DENSE_THREADS), 0, st, vv, dd, bb, cu, chunk_off, p->T, p->num_seqs,
                        p->H_v, (int)mc, p->flags, dv, ws);
     hipLaunchKernelGGL(kda_bwd_pair_kernel<MODE>, cg, dim3(PAIR_THREADS), 0, st, qq, kk, gg, bb, A_log, dt_bias, cu, chunk_off,
                        p->T, p->num_seqs, p->H_qk, p->H_v, (int)mc, p->scale, p->lower_bound, p->flags, dqv, dkv,
