@@ -64,6 +64,7 @@ constexpr int BNS = DV / BV;
 constexpr int PREP_THREADS = 512;  // 8 waves: two per SIMD beside the prep kernel's 157 KB of LDS
 constexpr int PAIR_THREADS = 512;  // the same for the pair kernel (147 KB)
 constexpr int DENSE_THREADS = 512;  // and for the dense kernel (152 KB)
+constexpr int STATE_THREADS = 512;  // and for the state passes (94 and 154 KB)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kL2Eps = 1e-6f;
 constexpr float kMinLog2Decay = -1.0e4f;
@@ -296,6 +297,7 @@ __device__ __forceinline__ float gtail(const float* sG, const float* sBt, int i,
 // C[4 lg + r][li] (r < 4) of each 16 x 16 tile.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // acc[m][n] += the (16 m, 16 n) tile of A B over k < kdim (a multiple of
 // 32), operands fp32 in LDS:
@@ -630,21 +632,17 @@ __device__ __forceinline__ void chain_chunks(int n, const int* chunk_off, const 
 }
 
 // slice <-> [128][128] fp32 matrix g (rows v0 ..), and <-> LDS [32][RS]
-__device__ __forceinline__ void slice_to_global(const f32x4 (&S)[2][2], float* g, int v0, int w, int li, int lg) {
+__device__ __forceinline__ void slice_to_global(const f32x4 (&S)[2][1], float* g, int v0, int w, int li, int lg) {
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) g[(size_t)(v0 + 16 * m + 4 * lg + r) * DK + 32 * w + 16 * n + li] = S[m][n][r];
+    for (int r = 0; r < 4; ++r) g[(size_t)(v0 + 16 * m + 4 * lg + r) * DK + 16 * w + li] = S[m][0][r];
 }
-__device__ __forceinline__ void slice_to_lds(const f32x4 (&S)[2][2], float* s, int w, int li, int lg) {
+__device__ __forceinline__ void slice_to_lds(const f32x4 (&S)[2][1], float* s, int w, int li, int lg) {
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[(16 * m + 4 * lg + r) * RS + 32 * w + 16 * n + li] = S[m][n][r];
+    for (int r = 0; r < 4; ++r) s[(16 * m + 4 * lg + r) * RS + 16 * w + li] = S[m][0][r];
 }
 
 // XCD-aware decode: the BNS slices of one chain share (id mod 8), so they run
@@ -704,35 +702,31 @@ __device__ __forceinline__ bool state_job(int id, const int64_t* cu, const int* 
   return true;
 }
 
-__device__ __forceinline__ void slice_identity(f32x4 (&S)[2][2], int v0, int w, int li, int lg) {
+__device__ __forceinline__ void slice_identity(f32x4 (&S)[2][1], int v0, int w, int li, int lg) {
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[m][n][r] = v0 + 16 * m + 4 * lg + r == 32 * w + 16 * n + li ? 1.0f : 0.0f;
+    for (int r = 0; r < 4; ++r) S[m][0][r] = v0 + 16 * m + 4 * lg + r == 16 * w + li ? 1.0f : 0.0f;
 }
 
 // the slice of a [128][128] matrix: fp32, bf16, or zero (KDA_STATE_NONE / NULL)
-__device__ __forceinline__ void slice_from_global(f32x4 (&S)[2][2], const void* g, int dtype, int v0, int w, int li,
+__device__ __forceinline__ void slice_from_global(f32x4 (&S)[2][1], const void* g, int dtype, int v0, int w, int li,
                                                   int lg) {
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const size_t e = (size_t)(v0 + 16 * m + 4 * lg + r) * DK + 32 * w + 16 * n + li;
-        float x = 0.0f;
-        if (g != nullptr && dtype == KDA_STATE_F32) x = reinterpret_cast<const float*>(g)[e];
-        else if (g != nullptr && dtype == KDA_STATE_BF16) x = bf2f(reinterpret_cast<const uint16_t*>(g)[e]);
-        S[m][n][r] = x;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const size_t e = (size_t)(v0 + 16 * m + 4 * lg + r) * DK + 16 * w + li;
+      float x = 0.0f;
+      if (g != nullptr && dtype == KDA_STATE_F32) x = reinterpret_cast<const float*>(g)[e];
+      else if (g != nullptr && dtype == KDA_STATE_BF16) x = bf2f(reinterpret_cast<const uint16_t*>(g)[e]);
+      S[m][0][r] = x;
+    }
 }
 
 // Entry slice of a job; `entry` is the chain's true entry matrix.
 template <int KIND>
-__device__ __forceinline__ void job_entry(f32x4 (&S)[2][2], const StateJob& j, const void* entry, int dtype,
+__device__ __forceinline__ void job_entry(f32x4 (&S)[2][1], const StateJob& j, const void* entry, int dtype,
                                           float* seg, int chains, int nseg, int w, int li, int lg) {
   if (KIND == ST_TRANS) {
     slice_identity(S, j.v0, w, li, lg);
@@ -757,37 +751,38 @@ __device__ __forceinline__ float* job_exit(float* seg, int chains, int nseg, con
 // Register staging of a chunk's operands: the backward state pass fetches
 // the next chunk's tiles into registers while the current chunk's products
 // run, and moves them to LDS after the chunk's last barrier.
-__device__ __forceinline__ void fetch_tile128(f32x4 (&r)[8], const float* g, int tid) {
+constexpr int ST128 = 2048 / STATE_THREADS, ST64 = 1024 / STATE_THREADS;  // 16-byte pieces per thread
+__device__ __forceinline__ void fetch_tile128(f32x4 (&r)[ST128], const float* g, int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = tid + 256 * i;
+  for (int i = 0; i < ST128; ++i) {
+    const int e = tid + STATE_THREADS * i;
     r[i] = *reinterpret_cast<const f32x4*>(g + (size_t)(e >> 5) * DK + 4 * (e & 31));
   }
 }
-__device__ __forceinline__ void put_tile128(float* s, const f32x4 (&r)[8], int tid) {
+__device__ __forceinline__ void put_tile128(float* s, const f32x4 (&r)[ST128], int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = tid + 256 * i;
+  for (int i = 0; i < ST128; ++i) {
+    const int e = tid + STATE_THREADS * i;
     *reinterpret_cast<f32x4*>(s + (e >> 5) * RS + 4 * (e & 31)) = r[i];
   }
 }
-__device__ __forceinline__ void fetch_tile64(f32x4 (&r)[4], const float* g, int tid) {
+__device__ __forceinline__ void fetch_tile64(f32x4 (&r)[ST64], const float* g, int tid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid + 256 * i;
+  for (int i = 0; i < ST64; ++i) {
+    const int e = tid + STATE_THREADS * i;
     r[i] = *reinterpret_cast<const f32x4*>(g + (e >> 4) * 64 + 4 * (e & 15));
   }
 }
-__device__ __forceinline__ void put_tile64(float* s, const f32x4 (&r)[4], int tid) {
+__device__ __forceinline__ void put_tile64(float* s, const f32x4 (&r)[ST64], int tid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid + 256 * i;
+  for (int i = 0; i < ST64; ++i) {
+    const int e = tid + STATE_THREADS * i;
     *reinterpret_cast<f32x4*>(s + (e >> 4) * QS + 4 * (e & 15)) = r[i];
   }
 }
 
 template <int KIND>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(STATE_THREADS)
 kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ chunk_off, const void* __restrict__ h0,
                       int init_dtype, int T, int N, int Hv, int mc, float* __restrict__ ws, float* __restrict__ seg,
                       int nseg, int seg_len) {
@@ -799,7 +794,9 @@ kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ ch
   if (!state_job<KIND>(blockIdx.x, cu, chunk_off, T, N, Hv, nseg, seg_len, false, j)) return;
   const int chains = N * Hv, h = j.h, v0 = j.v0, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
-  f32x4 S[2][2];
+  // wave w: state columns 16 w .. +15; U rows 16 (w & 3) .., columns 16 (w >> 2) ..
+  const int ut = 16 * (w & 3), uv = 16 * (w >> 2);
+  f32x4 S[2][1];
   job_entry<KIND>(S, j, h0 == nullptr ? nullptr : reinterpret_cast<const char*>(h0) +
                                                       (size_t)j.chain * DV * DK * (init_dtype == KDA_STATE_BF16 ? 2 : 4),
                   init_dtype, seg, chains, nseg, w, li, lg);
@@ -808,40 +805,32 @@ kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ ch
     float* sb = const_cast<float*>(pb) + PB_FLOATS;
     if constexpr (KIND == ST_FULL) slice_to_global(S, sb + SB_H, v0, w, li, lg);
     slice_to_lds(S, sS, w, li, lg);
-    load_tile128(sW, pb + PB_W, DK, tid);
-    load_tile128(sKd, pb + PB_KD, DK, tid);
+    load_tile128<STATE_THREADS>(sW, pb + PB_W, DK, tid);
+    load_tile128<STATE_THREADS>(sKd, pb + PB_KD, DK, tid);
     // U rows 16 w .. +15 start from -Ubar (lane layout of the product below);
     // a map job has no inputs, Ubar = 0
-    f32x4 U[1][2];
+    f32x4 U[1][1];
     zero_block(U);
     if constexpr (KIND != ST_TRANS) {
 #pragma unroll
-      for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) U[0][nn][r] = -pb[PB_UB + (16 * w + 4 * lg + r) * DV + v0 + 16 * nn + li];
+      for (int r = 0; r < 4; ++r) U[0][0][r] = -pb[PB_UB + (ut + 4 * lg + r) * DV + v0 + uv + li];
     }
-    float gn[2];
-#pragma unroll
-    for (int nn = 0; nn < 2; ++nn) gn[nn] = pb[PB_GN + 32 * w + 16 * nn + li];
+    const float gn = pb[PB_GN + 16 * w + li];
     __syncthreads();
     // -U = W S^T - Ubar:  A(t, k) = W[t][k],  B(k, v) = S[v][k]
-    mfma_block<false, true, 1, 2>(U, sW + 16 * w * RS, RS, sS, RS, 0, 0, DK, lane);
+    mfma_block<false, true, 1, 1>(U, sW + ut * RS, RS, sS, RS, 0, uv, DK, lane);
 #pragma unroll
-    for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * lg + r, vv = 16 * nn + li;
-        const float u = -U[0][nn][r];
-        sU[t * SV + vv] = u;
-        if constexpr (KIND == ST_FULL) sb[SB_U + t * DV + v0 + vv] = u;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int t = ut + 4 * lg + r, vv = uv + li;
+      const float u = -U[0][0][r];
+      sU[t * SV + vv] = u;
+      if constexpr (KIND == ST_FULL) sb[SB_U + t * DV + v0 + vv] = u;
+    }
     __syncthreads();
     // S <- S Diag(gn) + U^T Kd:  A(v, t) = U[t][v],  B(t, k) = Kd[t][k]
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int nn = 0; nn < 2; ++nn) S[m][nn] *= gn[nn];
-    mfma_block<true, false, 2, 2>(S, sU, SV, sKd, RS, 0, 32 * w, CH, lane);
+    for (int m = 0; m < 2; ++m) S[m][0] *= gn;
+    mfma_block<true, false, 2, 1>(S, sU, SV, sKd, RS, 0, 16 * w, CH, lane);
     __syncthreads();
   }
   if constexpr (KIND != ST_FULL) slice_to_global(S, job_exit<KIND>(seg, chains, nseg, j), v0, w, li, lg);
@@ -849,9 +838,9 @@ kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ ch
 
 // (native vector types: staging arrays of them stay in registers)
 struct BStage {
-  f32x4 kd[8], w[8], qg[8], aq[4];
-  u32x4 dO;  // bf16: token tid >> 2, columns v0 + 8 (tid & 3) .. +7
-  float gn[2];
+  f32x4 kd[ST128], w[ST128], qg[ST128], aq[ST64];
+  u32x2 dO;  // bf16: token tid >> 3, columns v0 + 4 (tid & 7) .. +3
+  float gn;
 };
 
 template <int KIND>
@@ -862,16 +851,15 @@ __device__ __forceinline__ void bstate_fetch(BStage& b, const float* pb, const u
   if constexpr (KIND != ST_TRANS) {
     fetch_tile128(b.qg, pb + PB_QG, tid);
     fetch_tile64(b.aq, pb + PB_AQK, tid);
-    const int t = tid >> 2;
-    b.dO = u32x4{0u, 0u, 0u, 0u};
-    if (t < len) b.dO = *reinterpret_cast<const u32x4*>(d_out + ((size_t)(row0 + t) * Hv + h) * DV + v0 + 8 * (tid & 3));
+    const int t = tid >> 3;
+    b.dO = u32x2{0u, 0u};
+    if (t < len) b.dO = *reinterpret_cast<const u32x2*>(d_out + ((size_t)(row0 + t) * Hv + h) * DV + v0 + 4 * (tid & 7));
   }
-#pragma unroll
-  for (int nn = 0; nn < 2; ++nn) b.gn[nn] = pb[PB_GN + 32 * w + 16 * nn + li];
+  b.gn = pb[PB_GN + 16 * w + li];
 }
 
 template <int KIND>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(STATE_THREADS)
 kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restrict__ dhT, float* __restrict__ dh0,
                       const int64_t* __restrict__ cu, const int* __restrict__ chunk_off, int T, int N, int Hv, int mc,
                       float* __restrict__ ws, float* __restrict__ seg, int nseg, int seg_len) {
@@ -888,7 +876,9 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
   const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
   const int64_t seqlen = cu == nullptr ? (int64_t)T : cu[j.n + 1] - cu[j.n];
   const size_t sbase = (size_t)j.chain * DV * DK;
-  f32x4 D[2][2];
+  // wave w: gradient columns 16 w .. +15; dU rows 16 (w & 3) .., columns 16 (w >> 2) ..
+  const int ut = 16 * (w & 3), uv = 16 * (w >> 2);
+  f32x4 D[2][1];
   job_entry<KIND>(D, j, dhT == nullptr ? nullptr : dhT + sbase, KDA_STATE_F32, seg, chains, nseg, w, li, lg);
   const float* pb0 = ws + ((size_t)h * mc + j.x0) * CHUNK_HEAD_FLOATS;
   auto chunk_len = [&](int c) { return (int)min((int64_t)CH, seqlen - (int64_t)c * CH); };
@@ -907,40 +897,33 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
     if constexpr (KIND != ST_TRANS) {
       put_tile128(sQg, b.qg, tid);
       put_tile64(sAq, b.aq, tid);
-      const int t = tid >> 2, jj = 8 * (tid & 3);
-      const uint32_t wv[4] = {b.dO[0], b.dO[1], b.dO[2], b.dO[3]};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        sdO[t * SV + jj + 2 * q] = __uint_as_float(wv[q] << 16);
-        sdO[t * SV + jj + 2 * q + 1] = __uint_as_float(wv[q] & 0xffff0000u);
-      }
+      const int t = tid >> 3, jj = 4 * (tid & 7);
+      *reinterpret_cast<float4*>(sdO + t * SV + jj) =
+          make_float4(__uint_as_float(b.dO[0] << 16), __uint_as_float(b.dO[0] & 0xffff0000u),
+                      __uint_as_float(b.dO[1] << 16), __uint_as_float(b.dO[1] & 0xffff0000u));
     }
-    const float gn[2] = {b.gn[0], b.gn[1]};
+    const float gn = b.gn;
     __syncthreads();
     if (c - 1 >= j.c0)
       bstate_fetch<KIND>(b, pb0 + (size_t)(c - 1) * CHUNK_HEAD_FLOATS, d_out, j.bos + (int64_t)(c - 1) * CH,
                          chunk_len(c - 1), Hv, h, v0, tid, w, li);
     // dU rows 16 w .. +15:  Aqk^T dO  +  Kd dS'^T  (a map job has dO = 0)
-    f32x4 dU[1][2];
+    f32x4 dU[1][1];
     zero_block(dU);
-    if constexpr (KIND != ST_TRANS) mfma_block_f32<true, false, 1, 2>(dU, sAq + 16 * w, QS, sdO, SV, 0, 0, CH, lane);
-    mfma_block_f32<false, true, 1, 2>(dU, sKd + 16 * w * RS, RS, sdh, RS, 0, 0, DK, lane);
+    if constexpr (KIND != ST_TRANS) mfma_block_f32<true, false, 1, 1>(dU, sAq + ut, QS, sdO, SV, 0, uv, CH, lane);
+    mfma_block_f32<false, true, 1, 1>(dU, sKd + ut * RS, RS, sdh, RS, 0, uv, DK, lane);
 #pragma unroll
-    for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * lg + r, vv = 16 * nn + li;
-        sdU[t * SV + vv] = -dU[0][nn][r];
-        if constexpr (KIND == ST_FULL) sb[SB_DU + t * DV + v0 + vv] = dU[0][nn][r];
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int t = ut + 4 * lg + r, vv = uv + li;
+      sdU[t * SV + vv] = -dU[0][0][r];
+      if constexpr (KIND == ST_FULL) sb[SB_DU + t * DV + v0 + vv] = dU[0][0][r];
+    }
     __syncthreads();
     // dS = dS' Diag(gn) + dO^T Qg - dU^T W:  A(v, t) = dO[t][v] (then -dU[t][v])
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int nn = 0; nn < 2; ++nn) D[m][nn] *= gn[nn];
-    if constexpr (KIND != ST_TRANS) mfma_block_f32<true, false, 2, 2>(D, sdO, SV, sQg, RS, 0, 32 * w, CH, lane);
-    mfma_block_f32<true, false, 2, 2>(D, sdU, SV, sW, RS, 0, 32 * w, CH, lane);
+    for (int m = 0; m < 2; ++m) D[m][0] *= gn;
+    if constexpr (KIND != ST_TRANS) mfma_block_f32<true, false, 2, 1>(D, sdO, SV, sQg, RS, 0, 16 * w, CH, lane);
+    mfma_block_f32<true, false, 2, 1>(D, sdU, SV, sW, RS, 0, 16 * w, CH, lane);
     __syncthreads();
   }
   if constexpr (KIND == ST_FULL) {
@@ -1624,27 +1607,27 @@ void launch_bwd(const kda_fwd_params* p, const void* q, const void* k, const voi
     const dim3 cmb((unsigned)(chains * (SD / CMB_ROWS)));
     const int N = p->num_seqs, H = p->H_v, T = p->T, idt = p->init_state_dtype;
     if (nseg > 1) {
-      hipLaunchKernelGGL(kda_bwd_fstate_kernel<ST_CARRY>, grid((int64_t)chains * (nseg - 1)), dim3(256), 0, st, cu,
+      hipLaunchKernelGGL(kda_bwd_fstate_kernel<ST_CARRY>, grid((int64_t)chains * (nseg - 1)), dim3(STATE_THREADS), 0, st, cu,
                          chunk_off, h0, idt, T, N, H, (int)mc, ws, seg, nseg, seg_len);
       if (nseg > 2) {
-        hipLaunchKernelGGL(kda_bwd_fstate_kernel<ST_TRANS>, grid((int64_t)chains * (nseg - 2)), dim3(256), 0, st, cu,
+        hipLaunchKernelGGL(kda_bwd_fstate_kernel<ST_TRANS>, grid((int64_t)chains * (nseg - 2)), dim3(STATE_THREADS), 0, st, cu,
                            chunk_off, h0, idt, T, N, H, (int)mc, ws, seg, nseg, seg_len);
         hipLaunchKernelGGL(kda_segment_combine_kernel, cmb, dim3(256), 0, st, seg, chains, nseg);
       }
     }
-    hipLaunchKernelGGL(kda_bwd_fstate_kernel<ST_FULL>, grid((int64_t)chains * nseg), dim3(256), 0, st, cu, chunk_off,
+    hipLaunchKernelGGL(kda_bwd_fstate_kernel<ST_FULL>, grid((int64_t)chains * nseg), dim3(STATE_THREADS), 0, st, cu, chunk_off,
                        h0, idt, T, N, H, (int)mc, ws, seg, nseg, seg_len);
     // the backward pass reuses the scratch once the forward pass is done with it
     if (nseg > 1) {
-      hipLaunchKernelGGL(kda_bwd_bstate_kernel<ST_CARRY>, grid((int64_t)chains * (nseg - 1)), dim3(256), 0, st, dd,
+      hipLaunchKernelGGL(kda_bwd_bstate_kernel<ST_CARRY>, grid((int64_t)chains * (nseg - 1)), dim3(STATE_THREADS), 0, st, dd,
                          dhT, dh0, cu, chunk_off, T, N, H, (int)mc, ws, seg, nseg, seg_len);
       if (nseg > 2) {
-        hipLaunchKernelGGL(kda_bwd_bstate_kernel<ST_TRANS>, grid((int64_t)chains * (nseg - 2)), dim3(256), 0, st, dd,
+        hipLaunchKernelGGL(kda_bwd_bstate_kernel<ST_TRANS>, grid((int64_t)chains * (nseg - 2)), dim3(STATE_THREADS), 0, st, dd,
                            dhT, dh0, cu, chunk_off, T, N, H, (int)mc, ws, seg, nseg, seg_len);
         hipLaunchKernelGGL(kda_segment_combine_kernel, cmb, dim3(256), 0, st, seg, chains, nseg);
       }
     }
-    hipLaunchKernelGGL(kda_bwd_bstate_kernel<ST_FULL>, grid((int64_t)chains * nseg), dim3(256), 0, st, dd, dhT, dh0,
+    hipLaunchKernelGGL(kda_bwd_bstate_kernel<ST_FULL>, grid((int64_t)chains * nseg), dim3(STATE_THREADS), 0, st, dd, dhT, dh0,
                        cu, chunk_off, T, N, H, (int)mc, ws, seg, nseg, seg_len);
   }
   if (mc > 0) {
