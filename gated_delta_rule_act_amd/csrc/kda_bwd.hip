@@ -236,10 +236,13 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
 #pragma unroll
   for (int i = 0; i < CPT; i += 4) {
     float g4[4];
+    const float4 db4 = dt_bias ? *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + c0 + i)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float db[4] = {db4.x, db4.y, db4.z, db4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float a = 0.0f, d1, d2;
-      if (ok) gate_fwd_bwd<MODE>(gv[i + e] + (dt_bias ? dt_bias[(size_t)h * DK + c0 + i + e] : 0.0f), A_exp, lb, a, d1, d2);
+      if (ok) gate_fwd_bwd<MODE>(gv[i + e] + db[e], A_exp, lb, a, d1, d2);
       g4[e] = fmaxf(a * kLog2e, kMinLog2Decay);
     }
     *reinterpret_cast<float4*>(sQ + r * RS + c0 + i) =
@@ -1183,6 +1186,14 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int lane = tid & 63, wave = tid >> 6, w = wave & 3, half = wave >> 2, nb = 4 * half;
   const int li = lane & 15, lg = lane >> 4;
   const int rbase = 16 * w + 4 * lg;  // own rows rbase + r
+  // the raw gate inputs of the gate phase, loaded now so their latency hides
+  // behind the pairwise sums (bf16 bits; zero past the chunk's end)
+  uint16_t graw[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      graw[n][r] = rbase + r < L.len ? g[((size_t)(L.row0 + rbase + r) * Hv + h) * DK + 16 * (nb + n) + li] : (uint16_t)0;
   float Ko[4][4], Qo[4][4], Go[4][4];
 #pragma unroll
   for (int n = 0; n < 4; ++n)
@@ -1375,12 +1386,11 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   for (int r = 0; r < 4; ++r) {
     const int row = rbase + r;
     const bool ok = row < L.len;  // uniform over the 16 lanes of the row
-    const size_t trow = (size_t)(L.row0 + row);
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const int c = 16 * (nb + n) + li;
       const float da = sQ[row * RS + c];
-      const float gv = ok ? bf2f(g[(trow * Hv + h) * DK + c]) : 0.0f;
+      const float gv = bf2f(graw[n][r]);
       float a, dadx, dadA;
       gate_fwd_bwd<MODE>(gv + dtb[n], A_exp, lb, a, dadx, dadA);
       // below the decay floor the factor e^a is exactly zero in fp32
