@@ -486,6 +486,27 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
           sAq[ii * QS + jj] = scale * aqk[r];
         }
       }
+    } else if constexpr (MODE == KDA_GATE_SAFE_SIGMOID) {
+      // diagonal block, bounded decay: e^(G_i - G_j) = e^(sG_i - sG_m) e^(sG_m - sG_j)
+      // with m the block's row 8, each factor within 2^(8 |lb| log2 e) of one:
+      // one fp32 MFMA product over the channels, masked on store
+      f32x4 akk = f32x4{0.f, 0.f, 0.f, 0.f}, aqk = akk;
+      const int i = 16 * w + li, m = 16 * w + 8;
+#pragma unroll 4
+      for (int kc = 0; kc < DK; kc += 4) {
+        const int c = kc + lg;
+        const float gm = sG[m * RS + c], gi = sG[i * RS + c];
+        const float fr = ex2(gi - gm), fc = ex2(gm - gi);  // row i and column i of the block
+        const float zb = sK[i * RS + c] * fc;
+        akk = __builtin_amdgcn_mfma_f32_16x16x4f32(sK[i * RS + c] * fr, zb, akk, 0, 0, 0);
+        aqk = __builtin_amdgcn_mfma_f32_16x16x4f32(sQ[i * RS + c] * fr, zb, aqk, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ii = 16 * w + 4 * lg + r, jj = 16 * w + li;
+        sA[ii * QS + jj] = jj < ii ? sB[ii] * akk[r] : 0.0f;
+        sAq[ii * QS + jj] = jj <= ii ? scale * aqk[r] : 0.0f;
+      }
     } else {
       // diagonal block: the 136 pairs i >= j of block w, two or three per lane
       for (int pr = lane; pr < 136; pr += 64) {
@@ -1241,20 +1262,55 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         R2[n][r] *= f;
       }
   }
-  for (int jj = 0; jj < 16; ++jj) {
-    const int j = 16 * w + jj;
-    float a[4], b[4];
+  // the midpoint decay of the own block, per channel (safe gate only)
+  float Gm[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) { a[r] = sDA[(rbase + r) * QS + j]; b[r] = sDQ[(rbase + r) * QS + j]; }
+  for (int n = 0; n < 4; ++n) Gm[n] = sG[(16 * w + 8) * RS + 16 * (nb + n) + li];
+  if constexpr (MODE == KDA_GATE_SAFE_SIGMOID) {
+    // Diagonal block, bounded decay: e^(G_i - G_j) = e^(sG_i - sG_m) e^(sG_m - sG_j)
+    // with m the block's row 8, each factor within 2^(8 |lb| log2 e) of one.
+    // The masked dAkk / dAqk blocks (zero above the diagonal) make it one
+    // fp32 MFMA product per term.
+    f32x4 D1[4], D2[4];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int c = 16 * (nb + n) + li;
-      const float kj = sK[j * RS + c], gj = sG[j * RS + c];
+    for (int n = 0; n < 4; ++n) { D1[n] = f32x4{0.f, 0.f, 0.f, 0.f}; D2[n] = D1[n]; }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int j = 16 * w + 4 * kk + lg;
+      const float a = sDA[(16 * w + li) * QS + j], b = sDQ[(16 * w + li) * QS + j];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int c = 16 * (nb + n) + li;
+        const float z = sK[j * RS + c] * ex2(Gm[n] - sG[j * RS + c]);
+        D1[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, z, D1[n], 0, 0, 0);
+        D2[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(b, z, D2[n], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = kj * ex2(fminf(Go[n][r] - gj, 0.0f));
-        R1[n][r] += a[r] * e;
-        R2[n][r] += b[r] * e;
+        const float f = ex2(Go[n][r] - Gm[n]);
+        R1[n][r] += f * D1[n][r];
+        R2[n][r] += f * D2[n][r];
+      }
+  } else {
+    // unbounded decay: pair by pair, every exponent <= 0
+    for (int jj = 0; jj < 16; ++jj) {
+      const int j = 16 * w + jj;
+      float a[4], b[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) { a[r] = sDA[(rbase + r) * QS + j]; b[r] = sDQ[(rbase + r) * QS + j]; }
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int c = 16 * (nb + n) + li;
+        const float kj = sK[j * RS + c], gj = sG[j * RS + c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = kj * ex2(fminf(Go[n][r] - gj, 0.0f));
+          R1[n][r] += a[r] * e;
+          R2[n][r] += b[r] * e;
+        }
       }
     }
   }
@@ -1287,18 +1343,41 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       for (int r = 0; r < 4; ++r) Cc[n][r] += X[n][r] * ex2(mid - Go[n][r]);
     }
   }
-  for (int ii = 0; ii < 16; ++ii) {
-    const int i = 16 * w + ii;
-    const float bi = sB[i];
-    float a[4], b[4];
+  if constexpr (MODE == KDA_GATE_SAFE_SIGMOID) {
+    // diagonal block through the midpoint, as on the row side
+    f32x4 X[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) { a[r] = bi * sDA[i * QS + rbase + r]; b[r] = sDQ[i * QS + rbase + r]; }
+    for (int n = 0; n < 4; ++n) X[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int c = 16 * (nb + n) + li;
-      const float ki = sK[i * RS + c], qi = scale * sQ[i * RS + c], gi = sG[i * RS + c];
+    for (int kk = 0; kk < 4; ++kk) {
+      const int i = 16 * w + 4 * kk + lg;
+      const float a = sB[i] * sDA[i * QS + 16 * w + li], b = sDQ[i * QS + 16 * w + li];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Cc[n][r] += (a[r] * ki + b[r] * qi) * ex2(fminf(gi - Go[n][r], 0.0f));
+      for (int n = 0; n < 4; ++n) {
+        const int c = 16 * (nb + n) + li;
+        const float f = ex2(sG[i * RS + c] - Gm[n]);
+        X[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sK[i * RS + c] * f, X[n], 0, 0, 0);
+        X[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(b, scale * sQ[i * RS + c] * f, X[n], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Cc[n][r] += X[n][r] * ex2(Gm[n] - Go[n][r]);
+  } else {
+    for (int ii = 0; ii < 16; ++ii) {
+      const int i = 16 * w + ii;
+      const float bi = sB[i];
+      float a[4], b[4];
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) { a[r] = bi * sDA[i * QS + rbase + r]; b[r] = sDQ[i * QS + rbase + r]; }
+  #pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int c = 16 * (nb + n) + li;
+        const float ki = sK[i * RS + c], qi = scale * sQ[i * RS + c], gi = sG[i * RS + c];
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) Cc[n][r] += (a[r] * ki + b[r] * qi) * ex2(fminf(gi - Go[n][r], 0.0f));
+      }
     }
   }
 
