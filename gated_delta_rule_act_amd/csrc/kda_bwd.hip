@@ -20,14 +20,19 @@
 // per-token decay by a reverse cumulative sum, through the gate activation,
 // the L2 norms and the beta sigmoid to the raw inputs.
 //
-// Six launches (plus the chunk map for packed input).  Values are fp32; the
+// Six kernels (plus the chunk map for packed input, and the carry, map and
+// combine launches of segmented state passes).  Values are fp32; the
 // contractions over LDS operands run on the bf16 MFMA with each operand split
-// into bf16 hi + lo (three products), or on the fp32 MFMA:
+// into bf16 hi + lo (three products), or on the fp32 MFMA.  Every kernel but
+// the reductions holds most of a CU's LDS, so each runs 8 waves (two per
+// SIMD) in one workgroup:
 //   kda_bwd_prep_kernel    per (chunk, v-head): norms, G, Akk and Aqk from
-//                          factors e^(G_i - G_j) (i >= j, so every exponent is
-//                          <= 0; pairs in different 16-row blocks factored
-//                          through a reference row onto the MFMA), T by
-//                          blocked substitution, W, Ubar, Kd, Qg, Kg, gn -> workspace.
+//                          factors e^(G_i - G_j) (pairs in different 16-row
+//                          blocks factored through a reference row onto the
+//                          MFMA; diagonal blocks through the block midpoint
+//                          when the decay is bounded, else pair by pair with
+//                          every exponent <= 0), T by blocked substitution,
+//                          W, Ubar, Kd, Qg, Kg, gn -> workspace.
 //   kda_bwd_fstate_kernel  per (sequence, v-head, 32-row V slice), forward
 //                          over chunks: stores each chunk's entry state S and U.
 //   kda_bwd_bstate_kernel  per (sequence, v-head, V slice), backward over
@@ -641,8 +646,8 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 // ---------------------------------------------------------------------------
 // state passes: one workgroup per (sequence, v-head, 32-row V slice).  The
 // 32 x 128 slice of the state (or of its gradient) lives in MFMA accumulator
-// layout: wave w holds key columns 32 w .. +31 for all 32 rows, element
-// (v = 16 m + 4 lg + r, k = 32 w + 16 n + li) in acc[m][n][r].
+// layout: wave w (of 8) holds key columns 16 w .. +15 for all 32 rows,
+// element (v = 16 m + 4 lg + r, k = 16 w + li) in acc[m][0][r].
 constexpr int SV = 36;  // LDS row stride of 32-wide slices
 
 __device__ __forceinline__ void chain_chunks(int n, const int* chunk_off, const int64_t* cu, int T, int& x0, int& nc,
@@ -958,11 +963,11 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
 }
 
 // ---------------------------------------------------------------------------
-// dense products per (chunk, v-head), on the fp32 MFMA (16x16x4).  Lane
-// (li = lane & 15, lg = lane >> 4) feeds A[li][k + lg] and B[k + lg][li] and
-// receives C[4 lg + r][li] (r < 4) of each 16 x 16 tile.  Wave w computes
-// rows 32 (w >> 1) .. +31 of every product: columns 64 (w & 1) .. +63 of the
-// 128-wide ones, 32 (w & 1) .. +31 of the 64-wide ones.
+// dense products per (chunk, v-head), on the split-bf16 MFMA.  Lane
+// (li = lane & 15, lg = lane >> 4) receives C[4 lg + r][li] (r < 4) of each
+// 16 x 16 tile.  Wave w (of 8) computes rows 32 (w >> 2) .. +31 of every
+// product: columns 32 (w & 3) .. +31 of the 128-wide ones, 16 (w & 3) .. +15
+// of the 64-wide ones.
 __global__ void __launch_bounds__(DENSE_THREADS)
 kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_out,
                      const uint16_t* __restrict__ beta, const int64_t* __restrict__ cu,
@@ -974,7 +979,6 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   __shared__ __attribute__((aligned(16))) float B3[CH * RS];
   __shared__ __attribute__((aligned(16))) float sT[CH * QS];
   __shared__ float sB[CH];
-  __shared__ float sRed[4 * DK];
   const int x = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const ChunkLoc L = chunk_loc(x, cu, chunk_off, T, N);
   if (L.len == 0) return;
@@ -1041,14 +1045,27 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int r = 0; r < 4; ++r) gb[GB_DKD + BLK_ROW(R0, m, r) * DK + BLK_COL(C0, n)] = dkd[m][n][r];
-    // dgn: four quarters of the rows, one per 128 threads
-    const int c = tid & 127, qr = tid >> 7;
-    float acc = 0.0f;
-    for (int vv = 32 * qr; vv < 32 * qr + 32; ++vv) acc += sb[SB_DH + vv * DK + c] * sb[SB_H + vv * DK + c];
-    sRed[qr * DK + c] = acc;
+    // dgn = colsum(dS' . S) over the 128 rows: thread (row group rg, 4
+    // channels) sums rows 8 rg .. +7 from independent vector loads; the 16
+    // row groups meet in B0, free since step 3
+    const int rg = tid >> 5, c4 = 4 * (tid & 31);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int vv = 8 * rg + i;
+      acc += *reinterpret_cast<const f32x4*>(sb + SB_DH + vv * DK + c4) *
+             *reinterpret_cast<const f32x4*>(sb + SB_H + vv * DK + c4);
+    }
+    *reinterpret_cast<f32x4*>(B0 + rg * DK + c4) = acc;
   }
   __syncthreads();
-  if (tid < DK) gb[GB_DGN + tid] = (sRed[tid] + sRed[DK + tid]) + (sRed[2 * DK + tid] + sRed[3 * DK + tid]);
+  if (tid < DK) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int g8 = 0; g8 < 16; ++g8) sum += B0[g8 * DK + tid];
+    gb[GB_DGN + tid] = sum;
+  }
+  __syncthreads();  // B0 is reloaded below
   // 5. B3 <- dW, B0 <- Kg, B2 <- V, sT <- T, sB <- beta
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -1143,8 +1160,9 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // pairwise terms, elementwise factors, decay sum, gate, norms and beta.
-// Wave w owns row block w (rows 16 w .. +15) in MFMA accumulator layout:
-// element (row 16 w + 4 lg + r, channel 16 n + li) in acc[n][r].  With
+// Wave (w, half) owns row block w (rows 16 w .. +15) and half of the channels
+// in MFMA accumulator layout: element (row 16 w + 4 lg + r, channel 16 (nb +
+// n) + li) in acc[n][r], nb = 4 half.  With
 // a = dAkk, b = dAqk (masked), E_ij = e^(G_i - G_j) per channel:
 //   R1_i = sum_j a_ij K_j E_ij,   R2_i = sum_j b_ij K_j E_ij      (row side)
 //   C_j  = sum_i (beta_i a_ij K_i + b_ij scale Q_i) E_ij           (column side)
@@ -1152,8 +1170,9 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
 //   dbeta_i (from Akk) = sum_c K_ic R1_ic.
 // Pairs in different 16-row blocks I > J factor through p = 16 I - 1, the
 // row before block I: E_ij = e^(G_i - G_p) e^(G_p - G_j), both exponents <= 0,
-// so those sums are fp32 MFMA products with one factor on each operand;
-// pairs inside a block are summed directly.
+// so those sums are fp32 MFMA products with one factor on each operand.
+// Pairs inside a block use the block's row 8 as the reference when the decay
+// is bounded (safe gate), and are summed directly otherwise.
 __device__ __forceinline__ float sum16(float x) {
   x += __shfl_xor(x, 1);
   x += __shfl_xor(x, 2);
