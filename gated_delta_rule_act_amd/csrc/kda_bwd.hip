@@ -202,6 +202,24 @@ __device__ __forceinline__ void load_bf16_tile128(float* s, const uint16_t* g, s
 // then composed from sums of nearby decays, never formed as the difference of
 // two large cumulative values.  Rows past the sequence end: zero inputs,
 // beta 0, zero decay.  Thread t: row t >> 2, channels 32 (t & 3) .. +31.
+// Lane sums by DPP moves (no LDS): lanes paired by quad_perm [1,0,3,2] and
+// [2,3,0,1], then the 4-lane halves of each 8 by row_half_mirror, then the
+// 8-lane halves of each 16-lane row by row_mirror.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  return x;
+}
+__device__ __forceinline__ float sum16(float x) {
+  x = sum8(x);
+  return x + dpp_f<0x140>(x);
+}
+
 template <int MODE, int NTH = 256>
 __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* sG, float* sBt, float* sB, const uint16_t* q,
                                                   const uint16_t* k, const uint16_t* g, const uint16_t* beta,
@@ -232,8 +250,13 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
   float sq = 0.0f, sk = 0.0f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) { sq += qv[i] * qv[i]; sk += kv[i] * kv[i]; }
+  if constexpr (TPR == 8) {
+    sq = sum8(sq);
+    sk = sum8(sk);
+  } else {
 #pragma unroll
-  for (int m = 1; m < TPR; m *= 2) { sq += __shfl_xor(sq, m); sk += __shfl_xor(sk, m); }
+    for (int m = 1; m < TPR; m *= 2) { sq += __shfl_xor(sq, m); sk += __shfl_xor(sk, m); }
+  }
   const bool norm = flags & KDA_FLAG_QK_L2NORM;
   const float rq = norm ? rsqrtf(sq + kL2Eps) : 1.0f, rk = norm ? rsqrtf(sk + kL2Eps) : 1.0f;
   if (rq_out) { rq_out[0] = rq; rk_out[0] = rk; }
@@ -1173,13 +1196,6 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
 // so those sums are fp32 MFMA products with one factor on each operand.
 // Pairs inside a block use the block's row 8 as the reference when the decay
 // is bounded (safe gate), and are summed directly otherwise.
-__device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
-  return x;
-}
 
 template <int MODE>
 __global__ void __launch_bounds__(PAIR_THREADS)
@@ -1539,7 +1555,7 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // per-chunk partials of ddt_bias (column sums) and dA_log
 #pragma unroll
   for (int n = 0; n < 4; ++n) sCol[(4 * w + lg) * DK + 16 * (nb + n) + li] = colDt[n];
-  dA += __shfl_xor(dA, 1); dA += __shfl_xor(dA, 2); dA += __shfl_xor(dA, 4); dA += __shfl_xor(dA, 8);
+  dA = sum16(dA);
   dA += __shfl_xor(dA, 16); dA += __shfl_xor(dA, 32);
   if (lane == 0) sRed[wave] = dA;
   __syncthreads();
