@@ -468,7 +468,7 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   __shared__ __attribute__((aligned(16))) float sAq[CH * QS];
   __shared__ __attribute__((aligned(16))) float sT[CH * QS];
   __shared__ float sB[CH];
-  __shared__ float sX[16 * 17];
+  __shared__ float sX[2 * 16 * 17];
   __shared__ __attribute__((aligned(16))) float sBt[4 * DK];
   const int x = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const ChunkLoc L = chunk_loc(x, cu, chunk_off, T, N);
@@ -568,31 +568,42 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   {
     const int w = tid >> 6, lane = tid & 63;
     if (w < 4 && lane < 16) {
+      // the lane's column of the block stays in registers (zero above the
+      // diagonal: those rows only ever subtract products with zeros)
       const int base = 16 * w, cc = lane;
+      float x[16];
+#pragma unroll
       for (int i = 0; i < 16; ++i) {
         float acc = i == cc ? 1.0f : 0.0f;
-        for (int j = cc; j < i; ++j) acc -= sA[(base + i) * QS + base + j] * sT[(base + j) * QS + base + cc];
-        sT[(base + i) * QS + base + cc] = i >= cc ? acc : 0.0f;
+#pragma unroll
+        for (int j = 0; j < i; ++j) acc -= sA[(base + i) * QS + base + j] * x[j];
+        x[i] = i >= cc ? acc : 0.0f;
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sT[(base + i) * QS + base + cc] = x[i];
     }
   }
   __syncthreads();
   {
-    // threads 0..255: one element (r, c) of the 16 x 16 block each
-    const int r = (tid >> 4) & 15, c = tid & 15;
-    const bool act = tid < 256;
+    // block row I: the blocks J < I are independent given rows < I, so up
+    // to two are formed at once, 256 threads each (element (r, c))
+    const int r = (tid >> 4) & 15, c = tid & 15, half = tid >> 8;
+    float* sXh = sX + half * (16 * 17);
     for (int I = 1; I < 4; ++I)
-      for (int J = 0; J < I; ++J) {
+      for (int J0 = 0; J0 < I; J0 += 2) {
+        const int J = J0 + half;
+        const bool act = J < I;
         // X = sum_{K=J}^{I-1} A_IK T_KJ;  T_IJ = -T_II X
         if (act) {
           float xacc = 0.0f;
           for (int kk = 16 * J; kk < 16 * I; ++kk) xacc += sA[(16 * I + r) * QS + kk] * sT[kk * QS + 16 * J + c];
-          sX[r * 17 + c] = xacc;
+          sXh[r * 17 + c] = xacc;
         }
         __syncthreads();
         if (act) {
           float t = 0.0f;
-          for (int m = 0; m < 16; ++m) t += sT[(16 * I + r) * QS + 16 * I + m] * sX[m * 17 + c];
+#pragma unroll
+          for (int m = 0; m < 16; ++m) t += sT[(16 * I + r) * QS + 16 * I + m] * sXh[m * 17 + c];
           sT[(16 * I + r) * QS + 16 * J + c] = -t;
         }
         __syncthreads();
