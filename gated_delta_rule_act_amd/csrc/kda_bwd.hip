@@ -973,8 +973,8 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
     // dU rows 16 w .. +15:  Aqk^T dO  +  Kd dS'^T  (a map job has dO = 0)
     f32x4 dU[1][1];
     zero_block(dU);
-    if constexpr (KIND != ST_TRANS) mfma_block_f32<true, false, 1, 1>(dU, sAq + ut, QS, sdO, SV, 0, uv, CH, lane);
-    mfma_block_f32<false, true, 1, 1>(dU, sKd + ut * RS, RS, sdh, RS, 0, uv, DK, lane);
+    if constexpr (KIND != ST_TRANS) mfma_block<true, false, 1, 1>(dU, sAq + ut, QS, sdO, SV, 0, uv, CH, lane);
+    mfma_block<false, true, 1, 1>(dU, sKd + ut * RS, RS, sdh, RS, 0, uv, DK, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = ut + 4 * lg + r, vv = uv + li;
@@ -985,8 +985,8 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
     // dS = dS' Diag(gn) + dO^T Qg - dU^T W:  A(v, t) = dO[t][v] (then -dU[t][v])
 #pragma unroll
     for (int m = 0; m < 2; ++m) D[m][0] *= gn;
-    if constexpr (KIND != ST_TRANS) mfma_block_f32<true, false, 2, 1>(D, sdO, SV, sQg, RS, 0, 16 * w, CH, lane);
-    mfma_block_f32<true, false, 2, 1>(D, sdU, SV, sW, RS, 0, 16 * w, CH, lane);
+    if constexpr (KIND != ST_TRANS) mfma_block<true, false, 2, 1>(D, sdO, SV, sQg, RS, 0, 16 * w, CH, lane);
+    mfma_block<true, false, 2, 1>(D, sdU, SV, sW, RS, 0, 16 * w, CH, lane);
     __syncthreads();
   }
   if constexpr (KIND == ST_FULL) {
