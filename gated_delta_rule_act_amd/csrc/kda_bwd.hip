@@ -1237,15 +1237,15 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     return;
   }
   const int hq = h / (Hv / Hqk);
+  // dAkk and dAqk first: their loads overlap the chunk inputs' (the loader's
+  // barriers order the LDS writes before any read)
+  load_tile64<PAIR_THREADS>(sDA, gb + GB_DAKK, tid);
+  load_tile64<PAIR_THREADS>(sDQ, gb + GB_DAQK, tid);
   float rq, rk;
   load_chunk_inputs<MODE, PAIR_THREADS>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0,
                                         L.len, lb, flags, tid, &rq, &rk);
   constexpr int TPR = PAIR_THREADS / CH;
   if (tid % TPR == 0) { sRq[tid / TPR] = rq; sRk[tid / TPR] = rk; }
-  if (tid < 256) {
-    load_tile64(sDA, gb + GB_DAKK, tid);
-    load_tile64(sDQ, gb + GB_DAQK, tid);
-  }
   __syncthreads();
 
   // wave (w, half): row block w = wave & 3, channel columns 16 (nb + n) + li,
