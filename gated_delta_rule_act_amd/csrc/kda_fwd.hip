@@ -68,20 +68,31 @@ constexpr float kL2Eps = 1e-6f;
 constexpr float kMinLog2Decay = -1.0e4f;
 
 // Per (v-head, chunk) workspace block, written by the intra kernel and read by
-// the state kernel: 89 fragments of 1 KB.  A fragment is one 16 x 32 tile of
+// the state kernel: 83 fragments of 1 KB.  A fragment is one 16 x 32 tile of
 // a 16-bit MFMA operand in lane order -- lane l = (i = l & 15, g = l >> 4)
 // holds row i and contraction columns 8g..8g+7 (16 bytes) -- so every
 // fragment moves as one contiguous 1 KB load, store or LDS access.
 constexpr int FRAG = 1024;
 constexpr int F_WN = 0;       // -W             (ta 0..3, kb 0..3) fp16  rows t, columns k
 constexpr int F_QG = 16;      // Q . 2^G        (ta, kb)           fp16  raw q
+// The token-by-token operands are lower triangular: their token block 1
+// (columns 32..63) is zero for token tiles 0 and 1, and those two fragments
+// are neither stored nor loaded (tri_frag numbers the other six).
 constexpr int F_TBH = 32;     // T diag(b) hi   (ta, kb 0..1)      bf16  rows t, columns s
-constexpr int F_TBL = 40;     //           lo
-constexpr int F_AQK = 48;     // scale rq_t (Q K^T . 2^(G_t - G_s)), lower incl. diagonal (ta, kb 0..1) fp16
-constexpr int F_VEC = 56;     // 2^G_last f32[128] | scale rq f32[64] | rk f32[64]
-constexpr int F_KD = 57;      // (K . 2^(G_last - G))^T (km 0..7, kb 0..1, hi/lo) fp16 rows k, columns t
-                              // (fragments 0..56 are shared by all V slices of a chain)
-constexpr int NFRAG = 89;
+constexpr int F_TBL = 38;     //           lo
+constexpr int F_AQK = 44;     // scale rq_t (Q K^T . 2^(G_t - G_s)), lower incl. diagonal (ta, kb 0..1) fp16
+constexpr int F_VEC = 50;     // 2^G_last f32[128] | scale rq f32[64] | rk f32[64]
+constexpr int F_KD = 51;      // (K . 2^(G_last - G))^T (km 0..7, kb 0..1, hi/lo) fp16 rows k, columns t
+                              // (fragments 0..50 are shared by all V slices of a chain)
+constexpr int NFRAG = 83;
+constexpr int NTRI = 6;       // stored fragments of a lower-triangular token-by-token operand
+// fragment (ta, kb) of a lower-triangular operand, kb <= ta / 2
+__host__ __device__ constexpr int tri_frag(int ta, int kb) { return ta < 2 ? ta : 2 * ta - 2 + kb; }
+// and back: the stored fragment f = 0..5 is (tri_ta(f), tri_kb(f))
+__host__ __device__ constexpr int tri_ta(int f) { return f < 2 ? f : (f + 2) >> 1; }
+__host__ __device__ constexpr int tri_kb(int f) { return f < 2 ? 0 : f & 1; }
+static_assert(tri_frag(tri_ta(5), tri_kb(5)) == 5 && tri_frag(tri_ta(2), tri_kb(2)) == 2 &&
+              tri_frag(tri_ta(3), tri_kb(3)) == 3 && tri_frag(3, 1) == 5 && tri_frag(1, 0) == 1, "tri_frag");
 constexpr size_t BLOCK = (size_t)NFRAG * FRAG;
 static_assert(BLOCK % 256 == 0, "workspace block alignment");
 
@@ -757,11 +768,13 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
     for (int it = 0; it < 2; ++it) {
-      const int item = tid + 256 * it;  // fragment (ta, kb) x lane
+      const int item = tid + 256 * it;  // stored fragment x lane
+      if (item >= NTRI * 64) break;     // (waves 2, 3 in the second pass)
       const int fr = item >> 6, ln = item & 63;
-      const int row = 16 * (fr >> 1) + (ln & 15), c0 = 32 * (fr & 1) + 8 * (ln >> 4);
+      const int ta = tri_ta(fr), kb = tri_kb(fr);
+      const int row = 16 * ta + (ln & 15), c0 = 32 * kb + 8 * (ln >> 4);
       bf16x8 th, tl;
-      const bool keep = 2 * (fr & 1) + (ln >> 5) <= (fr >> 1);
+      const bool keep = 2 * kb + (ln >> 5) <= ta;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = keep ? sT[row * AS + c0 + e] * sBeta[c0 + e] : 0.0f;
@@ -858,11 +871,14 @@ __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // token block 1 of token tiles 0, 1 is not stored: a fragment index past
+      // the block reads zeros through the buffer range check, with no memory access
+      const int tf = (kb == 1 && wave < 2) ? NFRAG : tri_frag(wave, kb);
       if constexpr (KIND != ST_TRANS) {
-        o.tbh[kb] = ld_frag(blk, F_TBH + wave * 2 + kb, lane);
-        o.tbl[kb] = ld_frag(blk, F_TBL + wave * 2 + kb, lane);
+        o.tbh[kb] = ld_frag(blk, tf == NFRAG ? NFRAG : F_TBH + tf, lane);
+        o.tbl[kb] = ld_frag(blk, tf == NFRAG ? NFRAG : F_TBL + tf, lane);
       }
-      if constexpr (KIND == ST_FULL) o.aq[kb] = ld_frag(blk, F_AQK + wave * 2 + kb, lane);
+      if constexpr (KIND == ST_FULL) o.aq[kb] = ld_frag(blk, tf == NFRAG ? NFRAG : F_AQK + tf, lane);
     }
     o.vec = ld_frag(blk, F_VEC, 16 * wave + (lane & 15));
     if constexpr (KIND != ST_TRANS) {
