@@ -27,7 +27,7 @@ BF16_PEAK_TFLOPS = 2516.6
 # Method work per token-head (dense 64-token tiles): 5 x 2*64*128 for Akk, Aqk,
 # w, u, Aqk.U plus 3 x 2*128*128 for W.S, Q.S, K^T.U.
 FLOP_PER_TOKEN_HEAD = 5 * 2 * 64 * 128 + 3 * 2 * 128 * 128
-BLOCK_BYTES = 84992  # per (v-head, chunk) intermediates written by the intra kernel
+BLOCK_BYTES = 76800  # per (v-head, chunk) intermediates written by the intra kernel
 
 
 def kernel_source_hash():

@@ -68,7 +68,7 @@ constexpr float kL2Eps = 1e-6f;
 constexpr float kMinLog2Decay = -1.0e4f;
 
 // Per (v-head, chunk) workspace block, written by the intra kernel and read by
-// the state kernel: 83 fragments of 1 KB.  A fragment is one 16 x 32 tile of
+// the state kernel: 75 fragments of 1 KB.  A fragment is one 16 x 32 tile of
 // a 16-bit MFMA operand in lane order -- lane l = (i = l & 15, g = l >> 4)
 // holds row i and contraction columns 8g..8g+7 (16 bytes) -- so every
 // fragment moves as one contiguous 1 KB load, store or LDS access.
@@ -82,9 +82,18 @@ constexpr int F_TBH = 32;     // T diag(b) hi   (ta, kb 0..1)      bf16  rows t,
 constexpr int F_TBL = 38;     //           lo
 constexpr int F_AQK = 44;     // scale rq_t (Q K^T . 2^(G_t - G_s)), lower incl. diagonal (ta, kb 0..1) fp16
 constexpr int F_VEC = 50;     // 2^G_last f32[128] | scale rq f32[64] | rk f32[64]
-constexpr int F_KD = 51;      // (K . 2^(G_last - G))^T (km 0..7, kb 0..1, hi/lo) fp16 rows k, columns t
+constexpr int F_KD = 51;      // (K . 2^(G_last - G))^T hi (km 0..7, kb 0..1) fp16 rows k, columns t
+constexpr int F_KDL = 67;     // its low part, 16 half fragments of 512 B (8 B per lane, same order):
+                              // e4m3 of (Kd - hi) 2^15, within +-16
                               // (fragments 0..50 are shared by all V slices of a chain)
-constexpr int NFRAG = 83;
+constexpr int NFRAG = 75;
+constexpr int HFRAG = 512;
+// Kd = hi + lo with hi = fp16(Kd) and |lo| <= ulp(hi) / 2 <= 2^-11 |Kd| (|Kd| <= 1).
+// lo is kept as e4m3 of lo 2^15 (3 mantissa bits): Kd to about 2^-15 relative,
+// for half the bytes of an fp16 lo.  The scale keeps typical lo (|Kd| near
+// 0.05) in the normal e4m3 range; the state kernel decodes it exactly to fp16
+// and scales its product back by 2^-15 in fp32.
+constexpr float kKdLoScale = 32768.0f, kKdLoUnscale = 1.0f / 32768.0f;
 constexpr int NTRI = 6;       // stored fragments of a lower-triangular token-by-token operand
 // fragment (ta, kb) of a lower-triangular operand, kb <= ta / 2
 __host__ __device__ constexpr int tri_frag(int ta, int kb) { return ta < 2 ? ta : 2 * ta - 2 + kb; }
@@ -112,6 +121,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 // kernel measured 5 % faster reading blocks stored this way.
 __device__ __forceinline__ void st_frag(uint8_t* blk, int fr, int lane, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(blk + fr * FRAG + lane * 16));
+}
+__device__ __forceinline__ void st_half_frag(uint8_t* blk, int off, int lane, u32x2 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(blk + off + lane * 8));
+}
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef short short2v __attribute__((ext_vector_type(2)));
+// eight fp16 -> eight e4m3 bytes (round to nearest even; the values are within
+// +-16, far from the e4m3 limit), in the same element order
+__device__ __forceinline__ u32x2 pack_e4m3(u32x4 f) {
+  u32x2 r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    // (copied to scalars first: this compiler's __builtin_bit_cast of a vector
+    // element reads element 0 whatever the index)
+    const uint32_t e0 = f[2 * i], e1 = f[2 * i + 1];
+    short2v w = {0, 0};
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w, __builtin_bit_cast(half2v, e0), 1.0f, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(w, __builtin_bit_cast(half2v, e1), 1.0f, true);
+    r[i] = __builtin_bit_cast(uint32_t, w);
+  }
+  return r;
+}
+// and back: every e4m3 value is exact in fp16
+__device__ __forceinline__ half8 unpack_e4m3(u32x2 v) {
+  half8 h;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)v[i], 1.0f, false);
+    const half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)v[i], 1.0f, true);
+    h[4 * i] = a[0]; h[4 * i + 1] = a[1]; h[4 * i + 2] = b[0]; h[4 * i + 3] = b[1];
+  }
+  return h;
 }
 
 __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
@@ -590,7 +631,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const float kd = kC[e] * vL[c0 + e];
         const _Float16 hh = (_Float16)kd;
         kdh[kb][e] = hh;
-        kdl[kb][e] = (_Float16)(kd - (float)hh);
+        kdl[kb][e] = (_Float16)((kd - (float)hh) * kKdLoScale);
       }
 #pragma unroll
       for (int Ip = 1; Ip < 4; ++Ip) {
@@ -661,8 +702,9 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     __syncthreads();
     for (int it = 0; it < 4; ++it) {
       const int fr = wave + 4 * it;  // fragment (km = fr >> 1, kb = fr & 1)
-      st_frag(blk, F_KD + fr * 2 + part, lane,
-              lds_frag_tr_grouped(sKd, KER, KEG, 32 * (fr & 1), 16 * (fr >> 1), lane));
+      const u32x4 f = lds_frag_tr_grouped(sKd, KER, KEG, 32 * (fr & 1), 16 * (fr >> 1), lane);
+      if (part == 0) st_frag(blk, F_KD + fr, lane, f);
+      else st_half_frag(blk, F_KDL * FRAG + fr * HFRAG, lane, pack_e4m3(f));
     }
     __syncthreads();
   }
@@ -846,7 +888,8 @@ struct ChunkRegs {
   u32x4 aq[2];               // Aqk: token tile w, token blocks 0, 1
   u32x4 vec;                 // bytes 256 w + 16 (lane & 15) of the vector fragment
   u32x4 vraw[2];             // V slice: row tid >> 2, columns 32 i + 8 (tid & 3) .. (i < NVT / 2)
-  u32x4 kd[2][2][2];         // Kd^T: key tile 2w + j, token block b, hi/lo
+  u32x4 kd[2][2];            // Kd^T hi: key tile 2w + j, token block b
+  u32x2 kdl[2][2];           // and its e4m3 low part
 };
 
 // (a buffer load over the chunk-head block: the scalar base and immediate
@@ -894,10 +937,12 @@ __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int part = 0; part < 2; ++part)
-          o.kd[j][b][part] = ld_frag(blk, F_KD + ((2 * wave + j) * 2 + b) * 2 + part, lane);
+      for (int b = 0; b < 2; ++b) {
+        const int fr = (2 * wave + j) * 2 + b;
+        o.kd[j][b] = ld_frag(blk, F_KD + fr, lane);
+        o.kdl[j][b] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(buffer_rsrc(blk, (uint32_t)BLOCK), F_KDL * FRAG + fr * HFRAG + lane * 8, 0, 0));
+      }
   }
 }
 
@@ -952,6 +997,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_b
 // the wait inserted at the loop head for that path is a full drain, paid on
 // every iteration).
 __device__ __forceinline__ void settle(const u32x4& a) { asm volatile("" ::"v"(a)); }
+__device__ __forceinline__ void settle(const u32x2& a) { asm volatile("" ::"v"(a)); }
 __device__ __forceinline__ void settle(const f32x4& a) { asm volatile("" ::"v"(a)); }
 template <int KIND, int NVT>
 __device__ __forceinline__ void settle(const ChunkRegs& r) {
@@ -972,7 +1018,7 @@ __device__ __forceinline__ void settle(const ChunkRegs& r) {
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) { settle(r.kd[j][b][0]); settle(r.kd[j][b][1]); }
+    for (int b = 0; b < 2; ++b) { settle(r.kd[j][b]); settle(r.kdl[j][b]); }
 }
 
 // One chunk of the state chain: `cur` holds chunk c, `n1` receives the key-tile
@@ -982,6 +1028,9 @@ __device__ __forceinline__ void settle(const ChunkRegs& r) {
 template <int KIND, int NVT>
 __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT], ChunkRegs& cur, ChunkRegs& n1,
                                             ChunkRegs& n2, const int c, PendingOut<NVT>& pd) {
+  // no fused multiply-adds the source does not spell out: each instantiation
+  // then rounds every element the same way, whatever its schedule
+#pragma clang fp contract(off)
   const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
   const int64_t row0 = x.bos + (int64_t)c * CH;
   typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -1072,6 +1121,11 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
   __syncthreads();  // B2
   // 6. S <- S Diag(2^G_last) + U'^T Kd ;  O += Aqk U'  (Aqk of token tiles 0,
   //    1 is zero in token block 1, so that product adds nothing there)
+  half8 kdlo[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) kdlo[j][b] = unpack_e4m3(cur.kdl[j][b]);
 #pragma unroll
   for (int vt = 0; vt < NVT; ++vt) {
     const half8 uh0 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 8 * lg);
@@ -1080,14 +1134,14 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
     const half8 ul1 = *reinterpret_cast<const half8*>(x.sUl + (16 * vt + li) * SUS + 32 + 8 * lg);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      f32x4 sa = S[j][vt] * (j == 0 ? gn0 : gn1), sb2 = f32x4{0, 0, 0, 0};
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0][0]), uh0, sa, 0, 0, 0);
-      sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1][0]), uh1, sb2, 0, 0, 0);
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0][0]), ul0, sa, 0, 0, 0);
-      sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1][0]), ul1, sb2, 0, 0, 0);
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0][1]), uh0, sa, 0, 0, 0);
-      sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1][1]), uh1, sb2, 0, 0, 0);
-      S[j][vt] = sa + sb2;
+      f32x4 sa = S[j][vt] * (j == 0 ? gn0 : gn1), sb2 = f32x4{0, 0, 0, 0}, sl = f32x4{0, 0, 0, 0};
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0]), uh0, sa, 0, 0, 0);
+      sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1]), uh1, sb2, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0]), ul0, sa, 0, 0, 0);
+      sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1]), ul1, sb2, 0, 0, 0);
+      sl = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdlo[j][0], uh0, sl, 0, 0, 0);
+      sl = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdlo[j][1], uh1, sl, 0, 0, 0);
+      S[j][vt] = (sa + sb2) + sl * kKdLoUnscale;
     }
     if constexpr (KIND == ST_FULL) {
       O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[0]), uh0, O[vt], 0, 0, 0);
