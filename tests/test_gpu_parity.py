@@ -19,6 +19,11 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
+# Far tighter than the 1e-3 tolerance of the fp32 final state (see
+# test_state_precision_margin): measured about 2.5e-6 (safe gate) and 1.6e-5
+# (softplus gate, whose error is set by its unbounded diagonal blocks).
+STATE_MARGIN = {W.GATE_SAFE_SIGMOID: 1e-5, W.GATE_SOFTPLUS: 4e-5}
+
 
 def small(**kw):
     base = dict(B=2, T=300, Hqk=4, seed=101, init_state_dtype=W.STATE_F32)
@@ -249,3 +254,17 @@ def test_measured_workload(idx):
             og = o[0, a:b, h]
         U.assert_parity(U.errors(U.as_f64(og), o_ref, U.as_f64(s[n, h]), s_ref, state_bf16=bf),
                         f"{inp.name} pair n={n} h={h}")
+
+
+@pytest.mark.parametrize("mode", [W.GATE_SAFE_SIGMOID, W.GATE_SOFTPLUS])
+def test_state_precision_margin(mode):
+    # The final state must stay far inside its 1e-3 tolerance, so that a lost
+    # low part of a split operand cannot pass unseen (the parity tolerance
+    # alone would let it through).
+    inp = small(B=2, T=1024, Hqk=2, Hv=4, gate_mode=mode, lower_bound=-5.0 if mode == W.GATE_SAFE_SIGMOID else -1.0)
+    U.log(f"[gpu] state precision margin, gate mode {mode}")
+    o, s = U.run_gpu(inp)
+    o_ref, s_ref = U.run_oracle(inp)
+    e = U.errors(U.as_f64(o), o_ref, U.as_f64(s), s_ref)
+    U.assert_parity(e, "precision margin")
+    assert e["state_rel"] <= STATE_MARGIN[mode], e
