@@ -26,7 +26,8 @@
 //       S <- S Diag(2^G_last) + U^T (K . 2^(G_last - G)).
 //
 // Precision: 16-bit MFMA operands with fp32 accumulation.  The contraction
-// that writes the state (U^T Kd) uses a 3-product fp16 hi/lo split, T diag(b)
+// that writes the state (U^T Kd) uses a 3-product hi/lo split (U and Kd in
+// fp16 hi/lo, the low part of Kd kept in e4m3 with a 2^15 scale), T diag(b)
 // enters U as bf16 hi/lo against exact bf16 V, the midpoint diagonal blocks
 // (factors up to 2^58) run on the fp32 MFMA, and T is computed in fp32.  The
 // exp2 operands are always differences of Gamma values, never ratios of
@@ -127,7 +128,7 @@ __device__ __forceinline__ void st_half_frag(uint8_t* blk, int off, int lane, u3
 }
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef short short2v __attribute__((ext_vector_type(2)));
-// eight fp16 -> eight e4m3 bytes (round to nearest even; the values are within
+// eight fp16 -> eight e4m3 bytes (rounded to nearest; the values are within
 // +-16, far from the e4m3 limit), in the same element order
 __device__ __forceinline__ u32x2 pack_e4m3(u32x4 f) {
   u32x2 r;
