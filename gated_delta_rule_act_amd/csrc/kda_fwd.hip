@@ -81,20 +81,23 @@ constexpr int F_QG = 16;      // Q . 2^G        (ta, kb)           fp16  raw q
 // are neither stored nor loaded (tri_frag numbers the other six).
 constexpr int F_TBH = 32;     // T diag(b) hi   (ta, kb 0..1)      bf16  rows t, columns s
 constexpr int F_TBL = 38;     //           lo
-constexpr int F_AQK = 44;     // scale rq_t (Q K^T . 2^(G_t - G_s)), lower incl. diagonal (ta, kb 0..1) fp16
-constexpr int F_VEC = 50;     // 2^G_last f32[128] | scale rq f32[64] | rk f32[64]
+constexpr int F_AQK = 44;     // scale (Q K^T . 2^(G_t - G_s)), lower incl. diagonal (ta, kb 0..1) fp16
+constexpr int F_VEC = 50;     // 2^G_last f32[128] (the rest of the fragment is unused)
 constexpr int F_KD = 51;      // (K . 2^(G_last - G))^T hi (km 0..7, kb 0..1) fp16 rows k, columns t
 constexpr int F_KDL = 67;     // its low part, 16 half fragments of 512 B (8 B per lane, same order):
-                              // e4m3 of (Kd - hi) 2^15, within +-16
+                              // e4m3 of (Kd - hi) 2^18
                               // (fragments 0..50 are shared by all V slices of a chain)
 constexpr int NFRAG = 75;
 constexpr int HFRAG = 512;
-// Kd = hi + lo with hi = fp16(Kd) and |lo| <= ulp(hi) / 2 <= 2^-11 |Kd| (|Kd| <= 1).
-// lo is kept as e4m3 of lo 2^15 (3 mantissa bits): Kd to about 2^-15 relative,
-// for half the bytes of an fp16 lo.  The scale keeps typical lo (|Kd| near
-// 0.05) in the normal e4m3 range; the state kernel decodes it exactly to fp16
-// and scales its product back by 2^-15 in fp32.
-constexpr float kKdLoScale = 32768.0f, kKdLoUnscale = 1.0f / 32768.0f;
+// Q and K here are the normalised q and k (with the L2 norm on, every element
+// is at most 1 in size), so no operand depends on the scale of the raw inputs.
+// Kd = hi + lo with hi = fp16(Kd) and |lo| <= ulp(hi) / 2 <= 2^-12 for |Kd| <= 1.
+// lo is kept as e4m3 of lo 2^18 (3 mantissa bits), within +-64 for |Kd| <= 1
+// and clamped to the e4m3 range (+-448) beyond that (only without the L2 norm):
+// Kd to about 2^-15 relative, for half the bytes of an fp16 lo.  The scale
+// keeps typical lo (|Kd| near 0.01) in the normal e4m3 range; the state kernel
+// decodes it exactly to fp16 and scales its product back by 2^-18 in fp32.
+constexpr float kKdLoScale = 262144.0f, kKdLoUnscale = 1.0f / 262144.0f, kE4m3Max = 448.0f;
 constexpr int NTRI = 6;       // stored fragments of a lower-triangular token-by-token operand
 // fragment (ta, kb) of a lower-triangular operand, kb <= ta / 2
 __host__ __device__ constexpr int tri_frag(int ta, int kb) { return ta < 2 ? ta : 2 * ta - 2 + kb; }
@@ -272,11 +275,8 @@ constexpr int L_MID = L_TOT + 4 * 128 * 4;              // [4][128] f32
 constexpr int L_VEC = L_MID + 4 * 128 * 4;              // [NVEC][128] f32
 constexpr int L_KE = L_T + T_BYTES;
 constexpr int L_AQ = L_KE + 8 * KEG * 2;
-constexpr int L_RQ = L_AQ + 64 * AQS * 2;
-constexpr int L_RK = L_RQ + 64 * 4;
-constexpr int L_BETA = L_RK + 64 * 4;
-constexpr int L_FW = L_BETA + 64 * 4;
-constexpr int L_QD = L_FW + 64 * 4;    // unbounded decays: q_i . k_i per row [64] f32
+constexpr int L_BETA = L_AQ + 64 * AQS * 2;
+constexpr int L_QD = L_BETA + 64 * 4;  // unbounded decays: q_i . k_i per row [64] f32
 constexpr int L_END = L_QD + 64 * 4;
 static_assert(L_VEC + NVEC * 128 * 4 <= L_T + T_BYTES, "vectors fit in region T");
 static_assert(64 * AS * 4 <= X_BYTES, "Akk fits in region X");
@@ -416,10 +416,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   float* sTot = reinterpret_cast<float*>(smem + L_TOT);
   float* sMid = reinterpret_cast<float*>(smem + L_MID);
   float* sVec = reinterpret_cast<float*>(smem + L_VEC);
-  float* sRq = reinterpret_cast<float*>(smem + L_RQ);
-  float* sRk = reinterpret_cast<float*>(smem + L_RK);
   float* sBeta = reinterpret_cast<float*>(smem + L_BETA);
-  float* sFw = reinterpret_cast<float*>(smem + L_FW);
   float* sQd = reinterpret_cast<float*>(smem + L_QD);
 
   const int x = blockIdx.x, h = blockIdx.y;
@@ -436,9 +433,13 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   uint8_t* blk = ws + ((size_t)h * max_chunks + x) * BLOCK;
 
   // ---- phase 1: loads, gate, norms, beta, in-register 16-row scan
-  // G holds the scan local to the sub-chunk: G = Gamma_r - Gamma_p.
+  // G holds the scan local to the sub-chunk: G = Gamma_r - Gamma_p.  rq, rk
+  // are the L2-norm factors of this lane's row (1 with the norm off): q and k
+  // are scaled by them as soon as they are unpacked, before any rounding to
+  // 16 bits, so no 16-bit operand depends on the size of the raw inputs.
   float G[4][8];
   uint4 qraw[4], kraw[4];
+  float rq, rk;
   {
     // a missing A_log means a multiplier of one (unused for pre-gated decay)
     const float A_exp = (MODE == KDA_GATE_PREGATED || A_log == nullptr) ? 1.0f : expf(A_log[h]);
@@ -450,17 +451,17 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint32_t vrow = (uint32_t)li;
     const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g + ((size_t)(cp.row0 + 16 * I) * Hv + h) * DK,
                                                   (uint32_t)max(0, min(16, cp.len - 16 * I)) * Hv * DK * 2);
-    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + ((size_t)(cp.row0 + 16 * I) * Hqk + hq) * DK,
+    const __amdgpu_buffer_rsrc_t bq = buffer_rsrc(q + ((size_t)(cp.row0 + 16 * I) * Hqk + hq) * DK,
                                                   (uint32_t)max(0, min(16, cp.len - 16 * I)) * Hqk * DK * 2);
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + ((size_t)(cp.row0 + 16 * I) * Hqk + hq) * DK,
+    const __amdgpu_buffer_rsrc_t bk = buffer_rsrc(k + ((size_t)(cp.row0 + 16 * I) * Hqk + hq) * DK,
                                                   (uint32_t)max(0, min(16, cp.len - 16 * I)) * Hqk * DK * 2);
     uint4 graw[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const uint32_t c0 = 32 * kb + 8 * lg;
       graw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, (vrow * Hv * DK + c0) * 2, 0, 0));
-      qraw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, (vrow * Hqk * DK + c0) * 2, 0, 0));
-      kraw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, (vrow * Hqk * DK + c0) * 2, 0, 0));
+      qraw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bq, (vrow * Hqk * DK + c0) * 2, 0, 0));
+      kraw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bk, (vrow * Hqk * DK + c0) * 2, 0, 0));
     }
     float4 dtb4[8];
 #pragma unroll
@@ -489,10 +490,10 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
     sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
+    const bool norm = flags & KDA_FLAG_QK_L2NORM;
+    rq = norm ? rsqrtf(sq + kL2Eps) : 1.0f;
+    rk = norm ? rsqrtf(sk + kL2Eps) : 1.0f;
     if (lg == 0) {
-      const bool norm = flags & KDA_FLAG_QK_L2NORM;
-      sRq[r] = norm ? rsqrtf(sq + kL2Eps) : 1.0f;
-      sRk[r] = norm ? rsqrtf(sk + kL2Eps) : 1.0f;
       const float bp = (flags & KDA_FLAG_BETA_IS_PROB) ? blogit : fast_rcp(1.0f + fast_exp2(-kLog2e * blogit));
       sBeta[r] = valid ? bp : 0.0f;
     }
@@ -525,7 +526,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       unpack_bf16x8(qraw[kb], qf);
       unpack_bf16x8(kraw[kb], kf);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qkd += qf[e] * kf[e];
+      for (int e = 0; e < 8; ++e) { qf[e] *= rq; kf[e] *= rk; qkd += qf[e] * kf[e]; }
       // one level at a time keeps the temporaries of only one level live
       diag_level<0>(G[kb], kf, qf, li, dkkp[0], dqkp[0]);
       __builtin_amdgcn_sched_barrier(0);
@@ -574,10 +575,6 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         sVec[(V_MC + J) * 128 + c] = fast_exp2(m - Tj[J]);
       }
     }
-    if (tid < 64) {
-      reinterpret_cast<float*>(blk + F_VEC * FRAG)[128 + tid] = scale * sRq[tid];
-      reinterpret_cast<float*>(blk + F_VEC * FRAG)[192 + tid] = sRk[tid];
-    }
   }
   __syncthreads();
 
@@ -606,6 +603,8 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         unpack_bf16x8(kraw[kb], kf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
+          qf[e] *= rq;
+          kf[e] *= rk;
           const float R = fast_exp2(G[kb][e]);
           const float C = fast_exp2(vT[c0 + e] - G[kb][e]);
           kR[e] = kf[e] * R;
@@ -632,7 +631,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const float kd = kC[e] * vL[c0 + e];
         const _Float16 hh = (_Float16)kd;
         kdh[kb][e] = hh;
-        kdl[kb][e] = (_Float16)((kd - (float)hh) * kKdLoScale);
+        kdl[kb][e] = (_Float16)__builtin_amdgcn_fmed3f((kd - (float)hh) * kKdLoScale, -kE4m3Max, kE4m3Max);
       }
 #pragma unroll
       for (int Ip = 1; Ip < 4; ++Ip) {
@@ -710,18 +709,14 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     __syncthreads();
   }
 
-  // ---- phase 5: Akk (fp32) and Aqk (fp16) into LDS with masks, beta, norms.
+  // ---- phase 5: Akk (fp32) and Aqk (fp16) into LDS with masks, beta and scale.
   // Blocks above the diagonal: Aqk is written as zero (it is copied out whole);
   // Akk is never read there, and the blocks of T above the diagonal are never
   // written: every reader of T masks them.
   {
-    float fk[4], fq[4];
+    float fk[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = 16 * I + 4 * lg + rr;
-      fk[rr] = sBeta[row] * sRk[row];
-      fq[rr] = scale * sRq[row];
-    }
+    for (int rr = 0; rr < 4; ++rr) fk[rr] = sBeta[16 * I + 4 * lg + rr];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
       if (J > I) {
@@ -729,15 +724,14 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int rr = 0; rr < 4; ++rr) sAq[(16 * I + 4 * lg + rr) * AQS + 16 * J + li] = (_Float16)0.0f;
         continue;
       }
-      const float fc = sRk[16 * J + li];
       f32x4 vk, vq;
       if (J == I) { vk = dkk; vq = dqk; }
       else { vk = okk[J < 3 ? J : 0]; vq = oqk[J < 3 ? J : 0]; }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int row = 16 * I + 4 * lg + rr, col = 16 * J + li;
-        float akk = vk[rr] * fk[rr] * fc;
-        float aqk = vq[rr] * fq[rr];
+        float akk = vk[rr] * fk[rr];
+        float aqk = vq[rr] * scale;
         if (J == I) {
           akk = (4 * lg + rr > li) ? akk : 0.0f;
           aqk = (4 * lg + rr >= li) ? aqk : 0.0f;
@@ -746,8 +740,6 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         sAq[row * AQS + col] = (_Float16)aqk;
       }
     }
-    // column factors of the WY products: beta rk for W, beta for T diag(beta)
-    if (tid < 64) sFw[tid] = sBeta[tid] * sRk[tid];
   }
   __syncthreads();
 
@@ -790,7 +782,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     __syncthreads();
   }
 
-  // ---- phase 7: W = T diag(b rk) (K . 2^G); T diag(b) hi/lo; Aqk
+  // ---- phase 7: W = T diag(b) (K . 2^G); T diag(b) hi/lo; Aqk
   {
     f32x4 accw[8];
 #pragma unroll
@@ -803,7 +795,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const bool keep = 2 * kb + (lg >> 1) <= I;
       half8 a;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = keep ? (_Float16)(sT[t * AS + s0 + e] * sFw[s0 + e]) : (_Float16)0.0f;
+      for (int e = 0; e < 8; ++e) a[e] = keep ? (_Float16)(sT[t * AS + s0 + e] * sBeta[s0 + e]) : (_Float16)0.0f;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const half8 b = __builtin_bit_cast(half8, lds_frag_tr_grouped(sKE, KER, KEG, 32 * kb, 16 * nt, lane));
@@ -854,11 +846,26 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // 2w+1) of the state, for both 16-wide V tiles, and token tile w of U and O.
 // Per chunk:
 //     U = T diag(b) V - W S^T
-//     O = qs . (Q . 2^G) S^T + Aqk U'   with U' = rk . U
-//     S <- S Diag(2^G_last) + U'^T (K . 2^(G_last - G))
+//     O = scale (Q . 2^G) S^T + Aqk U
+//     S <- S Diag(2^G_last) + U^T (K . 2^(G_last - G))
 // Every wave contracts over the full key (or token) range itself, so the only
-// exchanges are the state (fp16, for W S^T and Q S^T) and U' (hi/lo, for the
-// state update): two barriers per chunk.  Each operand fragment of a chunk is
+// exchanges are the state (fp16, for W S^T and Q S^T) and U (hi/lo, for the
+// state update): two barriers per chunk.
+//
+// Range.  S and U reach the 16-bit operands as fp16, whose range is about
+// 2^-14 .. 2^16, while v and the states may hold any bf16 / fp32 value.  The
+// workgroup therefore keeps them in units of 2^E: chunk c converts S_c 2^-E_c
+// and U_c 2^-E_(c+1), with one integer E per chunk shared by all the waves.
+// Before the first barrier of chunk c each wave posts to LDS the largest
+// magnitude of its S_c, its U_(c-1) and its part of the next chunk's V (in
+// units of 2^E_c); after the barrier every wave reads the four values and
+// sets E_(c+1) so that the largest lies in [1, 2).  The shift is applied with
+// no branch: U, the state's decay factors and the output factor of the chunk
+// carry 2^(E_c - E_(c+1)), so the update lands in units of E_(c+1).  Within
+// one chunk S and U grow by far less than the 2^14 headroom this leaves under
+// the fp16 limit.  Because E follows the magnitudes exactly, scaling v and
+// the initial state by any power of two shifts E and changes nothing else:
+// the results scale exactly, bit for bit.  Each operand fragment of a chunk is
 // loaded by exactly one wave, straight into registers: the token-tile
 // operands (W, Q . 2^G, T diag(b), Aqk) two chunks ahead, the key-tile
 // operands (Kd) one chunk ahead -- they are needed only after the second
@@ -900,7 +907,20 @@ __device__ __forceinline__ u32x4 ld_frag(const uint8_t* blk, int fr, int lane) {
                                                                           fr * FRAG + lane * 16, 0, 0));
 }
 
-// PART 0: token-tile operands, vectors and V (issued two chunks ahead);
+// The V slice of one chunk: row tid >> 2, columns 32 i + 8 (tid & 3) ..;
+// rows s >= len lie beyond the buffer range and read as zero.
+template <int NVT>
+__device__ __forceinline__ void load_v(ChunkRegs& o, const uint16_t* __restrict__ v, int64_t row0, int len, int Hv,
+                                       int h, int v0, int tid) {
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + ((size_t)row0 * Hv + h) * DV + v0, (uint32_t)len * Hv * DV * 2);
+#pragma unroll
+  for (int i = 0; i < NVT / 2; ++i)
+    o.vraw[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ((tid >> 2) * Hv * DV + 32 * i + 8 * (tid & 3)) * 2, 0, 0));
+}
+
+// PART 0: token-tile operands, vectors and (narrow slices) V, issued two
+// chunks ahead (wide slices: one chunk ahead, V two chunks ahead on its own);
 // PART 1: key-tile operands (issued one chunk ahead).
 // Operands a kind does not use are neither loaded nor kept.
 template <int PART, int KIND, int NVT>
@@ -925,15 +945,7 @@ __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk
       if constexpr (KIND == ST_FULL) o.aq[kb] = ld_frag(blk, tf == NFRAG ? NFRAG : F_AQK + tf, lane);
     }
     o.vec = ld_frag(blk, F_VEC, 16 * wave + (lane & 15));
-    if constexpr (KIND != ST_TRANS) {
-      // rows s >= len lie beyond the buffer range and read as zero
-      const __amdgpu_buffer_rsrc_t rv =
-          buffer_rsrc(v + ((size_t)row0 * Hv + h) * DV + v0, (uint32_t)len * Hv * DV * 2);
-#pragma unroll
-      for (int i = 0; i < NVT / 2; ++i)
-        o.vraw[i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ((tid >> 2) * Hv * DV + 32 * i + 8 * (tid & 3)) * 2, 0, 0));
-    }
+    if constexpr (KIND != ST_TRANS && NVT == NVT_NARROW) load_v<NVT>(o, v, row0, len, Hv, h, v0, tid);
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -953,6 +965,8 @@ struct StateCtx {
   const uint8_t* wsh;
   int64_t bos, seqlen;
   int x0, nc, Hv, h, v0, tid, wave, lane, li, lg;
+  float scale;
+  uint32_t* sMx;  // [SWAVES] largest magnitude posted by each wave (|x| bit patterns)
   float* sVec;
   _Float16* sS;
   _Float16* sUh;
@@ -1022,20 +1036,77 @@ __device__ __forceinline__ void settle(const ChunkRegs& r) {
     for (int b = 0; b < 2; ++b) { settle(r.kd[j][b]); settle(r.kdl[j][b]); }
 }
 
+// Magnitudes are compared as the bit patterns of |x|: for non-negative floats
+// the unsigned integer order is the numeric order, and integer maxima need
+// none of the NaN canonicalisation a float maximum of loaded values does.
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __builtin_bit_cast(uint32_t, x) & 0x7fffffffu; }
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t x) {
+  // lanes outside ROWS, and lanes with no source, keep their own value
+  return max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, ROWS, 0xf, false));
+}
+
+// Largest value over a wave (as |x| bit patterns): row maxima by DPP shifts,
+// then rows 0+1 and 2+3 and all four by row broadcasts; lane 63 holds it.
+__device__ __forceinline__ uint32_t wave_max_bits(uint32_t x) {
+  x = dpp_max_u32<0x111, 0xf>(x);  // row_shr:1
+  x = dpp_max_u32<0x112, 0xf>(x);  // row_shr:2
+  x = dpp_max_u32<0x114, 0xf>(x);  // row_shr:4
+  x = dpp_max_u32<0x118, 0xf>(x);  // row_shr:8: lane 15 of each row holds its row
+  x = dpp_max_u32<0x142, 0xa>(x);  // row_bcast:15 into rows 1, 3
+  x = dpp_max_u32<0x143, 0xc>(x);  // row_bcast:31 into rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// largest |value| of eight bf16 values packed in four dwords, as the bit
+// pattern of that value in fp32
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x8_absmax_bits(const u32x4& w) {
+  const u16x2 a = __builtin_bit_cast(u16x2, w[0] & 0x7fff7fffu), b = __builtin_bit_cast(u16x2, w[1] & 0x7fff7fffu);
+  const u16x2 c = __builtin_bit_cast(u16x2, w[2] & 0x7fff7fffu), d = __builtin_bit_cast(u16x2, w[3] & 0x7fff7fffu);
+  const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return (uint32_t)max(m[0], m[1]) << 16;
+}
+
+// The scale exponent is kept within [-kMaxExp, kMaxExp] and moves by at most
+// kMaxStep per chunk, so that 2^E, 2^-E and the per-chunk factor 2^-d are
+// normal floats and scale 2^-d stays finite.
+constexpr int kMaxExp = 126, kMaxStep = 64;
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
+// floor(log2 m) for a normal m > 0, from its bit pattern (m >= 0)
+__device__ __forceinline__ int ilog2_bits(int mi) { return (mi >> 23) - 127; }
+
+// The shift d = E_(c+1) - E_c that brings the largest of the four posted
+// maxima (units of 2^E_c) into [1, 2); 0 when all are zero.  Every wave reads
+// the same four values, so d is uniform across the workgroup.
+__device__ __forceinline__ int scale_shift(const uint32_t* sMx, int E) {
+  const u32x4 m4 = *reinterpret_cast<const u32x4*>(sMx);
+  const int mi = __builtin_amdgcn_readfirstlane((int)max(max(m4[0], m4[1]), max(m4[2], m4[3])));
+  if (mi == 0) return 0;
+  const int d = min(max(ilog2_bits(mi), -kMaxStep), kMaxStep);
+  return min(max(E + d, -kMaxExp), kMaxExp) - E;
+}
+
 // One chunk of the state chain: `cur` holds chunk c, `n1` receives the key-tile
 // operands of chunk c+1, `n2` the token-tile operands of chunk c+2.  The wide
 // slices (NVT = 4) have no registers for that depth: their token-tile
-// operands of chunk c+1 go to `n1` too (`n2` unused).
+// operands of chunk c+1 go to `n1` too (`n2` unused), and their V of chunk
+// c+2 goes to `cur`, whose own V is in LDS by then.  On entry S holds S_c in
+// units of 2^E (E = E_c) and mu this wave's largest |U_(c-1)| in the same
+// units; on exit S holds S_(c+1), E = E_(c+1) and mu the largest |U_c|.
 template <int KIND, int NVT>
 __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT], ChunkRegs& cur, ChunkRegs& n1,
-                                            ChunkRegs& n2, const int c, PendingOut<NVT>& pd) {
+                                            ChunkRegs& n2, const int c, PendingOut<NVT>& pd, int& E, uint32_t& mu) {
   // no fused multiply-adds the source does not spell out: each instantiation
   // then rounds every element the same way, whatever its schedule
 #pragma clang fp contract(off)
   const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
   const int64_t row0 = x.bos + (int64_t)c * CH;
   typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-  // 1. publish the chunk's vectors, the V slice and the current state.  Every
+  // 1. publish the chunk's vectors, the V slice and the current state, and
+  //    this wave's largest magnitude of S_c, U_(c-1) and the next V.  Every
   //    reader of these buffers in the previous chunk was before its B2.
   // (one lane per address: four lanes writing one address stall the LDS)
   if (lane < 16) reinterpret_cast<u32x4*>(x.sVec)[16 * wave + lane] = cur.vec;
@@ -1043,13 +1114,25 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
 #pragma unroll
     for (int i = 0; i < NVT / 2; ++i)
       *reinterpret_cast<u32x4*>(x.sV + sv_row<NVT>(tid >> 2) + 32 * i + 8 * (tid & 3)) = cur.vraw[i];
+  float ms = 0.0f;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int vt = 0; vt < NVT; ++vt) {
       const half4 hv = {(_Float16)S[j][vt][0], (_Float16)S[j][vt][1], (_Float16)S[j][vt][2], (_Float16)S[j][vt][3]};
       *reinterpret_cast<half4*>(x.sS + (16 * vt + li) * SSS + 32 * wave + 16 * j + 4 * lg) = hv;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) ms = fmaxf(ms, fabsf(S[j][vt][rr]));
     }
+  uint32_t mx = max(mu, abs_bits(ms));
+  if constexpr (KIND != ST_TRANS) {
+    uint32_t mv = 0;
+#pragma unroll
+    for (int i = 0; i < NVT / 2; ++i) mv = max(mv, bf16x8_absmax_bits(n1.vraw[i]));
+    mx = max(mx, abs_bits(__uint_as_float(mv) * pow2f(-E)));
+  }
+  mx = wave_max_bits(mx);
+  if (lane == 0) x.sMx[wave] = mx;
   // 2. the previous chunk's outputs (none before the first chunk: len 0), then
   //    the token-tile prefetch of chunk c+2 (clamped, so every chunk queues the
   //    same operations)
@@ -1059,43 +1142,60 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
     const int cp = min(c + AHEAD, x.nc - 1);
     load_chunk_part<0, KIND, NVT>(AHEAD == 2 ? n2 : n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, x.bos + (int64_t)cp * CH,
                        chunk_len(x, cp), x.Hv, x.h, x.v0, tid);
+    if constexpr (KIND != ST_TRANS && NVT != NVT_NARROW) {
+      const int cv = min(c + 2, x.nc - 1);
+      load_v<NVT>(cur, x.v, x.bos + (int64_t)cv * CH, chunk_len(x, cv), x.Hv, x.h, x.v0, tid);
+    }
   }
   __syncthreads();  // B1
-  // 3. U and O of token tile w for both V tiles, full contractions
-  const f32x4 qs = *reinterpret_cast<const f32x4*>(x.sVec + 128 + 16 * wave + 4 * lg);
-  const f32x4 rk = *reinterpret_cast<const f32x4*>(x.sVec + 192 + 16 * wave + 4 * lg);
-  const f32x4 gn0 = *reinterpret_cast<const f32x4*>(x.sVec + 32 * wave + 4 * lg);
-  const f32x4 gn1 = *reinterpret_cast<const f32x4*>(x.sVec + 32 * wave + 16 + 4 * lg);
+  // the scale of the chunk's results: E_(c+1) = E_c + d
+  const int d = scale_shift(x.sMx, E);
+  const float f = pow2f(-d);
+  const int En = E + d;
+  // 3. U and O of token tile w for all V tiles, full contractions, in units
+  //    of 2^E_(c+1):
+  //    U = 2^-E_(c+1) (T diag(b) V) - 2^-d W (S 2^-E_c)^T,
+  //    O = 2^-d scale (Q . 2^G) (S 2^-E_c)^T
+  const float scn = pow2f(-En), sf = x.scale * f;
+  const f32x4 gn0 = *reinterpret_cast<const f32x4*>(x.sVec + 32 * wave + 4 * lg) * f;
+  const f32x4 gn1 = *reinterpret_cast<const f32x4*>(x.sVec + 32 * wave + 16 + 4 * lg) * f;
   f32x4 U[NVT], O[NVT];
 #pragma unroll
   for (int vt = 0; vt < NVT; ++vt) {
     half8 sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
-    f32x4 u0 = f32x4{0, 0, 0, 0}, u1 = f32x4{0, 0, 0, 0}, o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
+    f32x4 ub = f32x4{0, 0, 0, 0}, uw = f32x4{0, 0, 0, 0}, o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
     if constexpr (KIND != ST_TRANS) {
       const bf16x8 vb0 = __builtin_bit_cast(bf16x8, lds_frag_tr_grouped(x.sV, svs<NVT>(), svg<NVT>(), 0, 16 * vt, lane));
       const bf16x8 vb1 = __builtin_bit_cast(bf16x8, lds_frag_tr_grouped(x.sV, svs<NVT>(), svg<NVT>(), 32, 16 * vt, lane));
-      u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[0]), vb0, u0, 0, 0, 0);
-      u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[0]), vb0, u1, 0, 0, 0);
+      ub = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[0]), vb0, ub, 0, 0, 0);
+      uw = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[0]), sb[0], uw, 0, 0, 0);
       if constexpr (KIND == ST_FULL) {
         o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[0]), sb[0], o0, 0, 0, 0);
         o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[1]), sb[1], o1, 0, 0, 0);
       }
-      u0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[1]), vb1, u0, 0, 0, 0);
-      u1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[1]), vb1, u1, 0, 0, 0);
+      ub = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[0]), vb0, ub, 0, 0, 0);
+      uw = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[1]), sb[1], uw, 0, 0, 0);
       if constexpr (KIND == ST_FULL) {
         o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[2]), sb[2], o0, 0, 0, 0);
         o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[3]), sb[3], o1, 0, 0, 0);
       }
-    }
+      ub = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[1]), vb1, ub, 0, 0, 0);
+      uw = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[2]), sb[2], uw, 0, 0, 0);
+      ub = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[1]), vb1, ub, 0, 0, 0);
+      uw = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[3]), sb[3], uw, 0, 0, 0);
+      U[vt] = ub * scn + uw * f;
+    } else {
+      f32x4 uw2 = f32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int kb = 0; kb < 4; kb += 2) {
-      u0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[kb]), sb[kb], u0, 0, 0, 0);
-      u1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[kb + 1]), sb[kb + 1], u1, 0, 0, 0);
+      for (int kb = 0; kb < 4; kb += 2) {
+        uw = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[kb]), sb[kb], uw, 0, 0, 0);
+        uw2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[kb + 1]), sb[kb + 1], uw2, 0, 0, 0);
+      }
+      U[vt] = (uw + uw2) * f;
     }
-    U[vt] = u0 + u1;
-    if constexpr (KIND == ST_FULL) O[vt] = (o0 + o1) * qs;
+    if constexpr (KIND == ST_FULL) O[vt] = (o0 + o1) * sf;
   }
   // 4. the key-tile prefetch of chunk c+1
   __builtin_amdgcn_sched_barrier(0);
@@ -1104,23 +1204,25 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
     load_chunk_part<1, KIND, NVT>(n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // 5. U' = rk . U -> LDS hi/lo, transposed [v][t]
+  // 5. U -> LDS hi/lo, transposed [v][t]
+  float mu_n = 0.0f;  // this wave's largest |U|
 #pragma unroll
   for (int vt = 0; vt < NVT; ++vt) {
     half4 hi, lo;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const float up = U[vt][rr] * rk[rr];
+      const float up = U[vt][rr];
       const _Float16 hh = (_Float16)up;
       hi[rr] = hh;
       lo[rr] = (_Float16)(up - (float)hh);
+      mu_n = fmaxf(mu_n, fabsf(up));
     }
     const int vv = 16 * vt + li, tt = 16 * wave + 4 * lg;
     *reinterpret_cast<half4*>(x.sUh + vv * SUS + tt) = hi;
     *reinterpret_cast<half4*>(x.sUl + vv * SUS + tt) = lo;
   }
   __syncthreads();  // B2
-  // 6. S <- S Diag(2^G_last) + U'^T Kd ;  O += Aqk U'  (Aqk of token tiles 0,
+  // 6. S <- S Diag(2^G_last) + U^T Kd ;  O += Aqk U  (Aqk of token tiles 0,
   //    1 is zero in token block 1, so that product adds nothing there)
   half8 kdlo[2][2];
 #pragma unroll
@@ -1150,13 +1252,16 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
     }
   }
   if constexpr (KIND == ST_FULL) {
+    const float se = pow2f(En);
 #pragma unroll
     for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) pd.o[vt][rr] = __builtin_bit_cast(uint16_t, (__bf16)O[vt][rr]);
+      for (int rr = 0; rr < 4; ++rr) pd.o[vt][rr] = __builtin_bit_cast(uint16_t, (__bf16)(O[vt][rr] * se));
     pd.row0 = row0;
     pd.len = chunk_len(x, c);
   }
+  E = En;
+  mu = abs_bits(mu_n);
 }
 
 // One workgroup per (job, V slice).  A job is a whole chain (nseg == 1) or one
@@ -1175,8 +1280,9 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
                  const int* __restrict__ chunk_off, const void* __restrict__ h0, void* __restrict__ hT,
                  uint16_t* __restrict__ out, const uint8_t* __restrict__ ws, float* __restrict__ seg,
                  int T, int N, int Hv, int max_chunks, int init_dtype, int final_dtype, int nseg,
-                 int seg_len) {
+                 int seg_len, float scale) {
   __shared__ __attribute__((aligned(16))) float sVec[256];
+  __shared__ __attribute__((aligned(16))) uint32_t sMx[SWAVES];
   constexpr int VS = 16 * NVT, NSL = DV / VS;
   __shared__ __attribute__((aligned(16))) _Float16 sS[VS * SSS];
   __shared__ __attribute__((aligned(16))) _Float16 sUh[VS * SUS];
@@ -1242,7 +1348,7 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
     }
 
   const uint8_t* wsh = ws + (size_t)h * max_chunks * BLOCK;
-  StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, lane, li, lg, sVec, sS, sUh, sUl, sV};
+  StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, lane, li, lg, scale, sMx, sVec, sS, sUh, sUl, sV};
   ChunkRegs rA, rB, rC;
   if (nc > 0) {
     load_chunk_part<0, KIND, NVT>(rA, wsh + (size_t)x0 * BLOCK, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0,
@@ -1254,31 +1360,73 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
     load_chunk_part<0, KIND, NVT>(rB, wsh + (size_t)(x0 + c1) * BLOCK, wave, lane, v, bos + (int64_t)c1 * CH,
                              chunk_len(ctx, c1), Hv, h, v0, tid);
   }
+  if (KIND != ST_TRANS && nc > 0 && NVT != NVT_NARROW) {
+    // wide slices: V runs two chunks ahead on its own
+    const int c1 = min(1, nc - 1);
+    load_v<NVT>(rA, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
+    load_v<NVT>(rB, v, bos + (int64_t)c1 * CH, chunk_len(ctx, c1), Hv, h, v0, tid);
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int vt = 0; vt < NVT; ++vt) settle(S[j][vt]);
   settle<KIND, NVT>(rA);
+  // the entry scale: the largest magnitude of the entry state and the first
+  // chunk's V brought into [1, 2)
+  int E = 0;
+  if (nc > 0) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) mx = max(mx, abs_bits(S[j][vt][rr]));
+    if constexpr (KIND != ST_TRANS)
+#pragma unroll
+      for (int i = 0; i < NVT / 2; ++i) mx = max(mx, bf16x8_absmax_bits(rA.vraw[i]));
+    mx = wave_max_bits(mx);
+    if (lane == 0) sMx[wave] = mx;
+    __syncthreads();
+    const int mi = __builtin_amdgcn_readfirstlane((int)max(max(sMx[0], sMx[1]), max(sMx[2], sMx[3])));
+    E = mi == 0 ? 0 : min(max(ilog2_bits(mi), -kMaxExp), kMaxExp);
+    // every wave has read the entry maxima before any wave posts again
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) S[j][vt][rr] = __builtin_amdgcn_ldexpf(S[j][vt][rr], -E);
+  }
+  __syncthreads();
+  uint32_t mu = 0;  // no U before the first chunk
   PendingOut<NVT> pd;
   pd.row0 = bos;
   pd.len = 0;
   int c = 0;
   if constexpr (NVT == NVT_NARROW) {
     for (; c + 3 <= nc; c += 3) {
-      state_chunk<KIND, NVT>(ctx, S, rA, rB, rC, c, pd);
-      state_chunk<KIND, NVT>(ctx, S, rB, rC, rA, c + 1, pd);
-      state_chunk<KIND, NVT>(ctx, S, rC, rA, rB, c + 2, pd);
+      state_chunk<KIND, NVT>(ctx, S, rA, rB, rC, c, pd, E, mu);
+      state_chunk<KIND, NVT>(ctx, S, rB, rC, rA, c + 1, pd, E, mu);
+      state_chunk<KIND, NVT>(ctx, S, rC, rA, rB, c + 2, pd, E, mu);
     }
-    if (c < nc) state_chunk<KIND, NVT>(ctx, S, rA, rB, rC, c, pd);
-    if (c + 1 < nc) state_chunk<KIND, NVT>(ctx, S, rB, rC, rA, c + 1, pd);
+    if (c < nc) state_chunk<KIND, NVT>(ctx, S, rA, rB, rC, c, pd, E, mu);
+    if (c + 1 < nc) state_chunk<KIND, NVT>(ctx, S, rB, rC, rA, c + 1, pd, E, mu);
   } else {
     for (; c + 2 <= nc; c += 2) {
-      state_chunk<KIND, NVT>(ctx, S, rA, rB, rB, c, pd);
-      state_chunk<KIND, NVT>(ctx, S, rB, rA, rA, c + 1, pd);
+      state_chunk<KIND, NVT>(ctx, S, rA, rB, rB, c, pd, E, mu);
+      state_chunk<KIND, NVT>(ctx, S, rB, rA, rA, c + 1, pd, E, mu);
     }
-    if (c < nc) state_chunk<KIND, NVT>(ctx, S, rA, rB, rB, c, pd);
+    if (c < nc) state_chunk<KIND, NVT>(ctx, S, rA, rB, rB, c, pd, E, mu);
   }
   if constexpr (KIND == ST_FULL) store_pending(pd, out, Hv, h, v0, wave, li, lg);
+  // back to the state's own units
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) S[j][vt][rr] = __builtin_amdgcn_ldexpf(S[j][vt][rr], E);
 
   // exit state
   void* dst = nullptr;
@@ -1746,6 +1894,7 @@ struct StateArgs {
   const uint8_t* ws;
   float* seg;
   int T, N, Hv, mc, init_dtype, final_dtype, nseg, seg_len;
+  float scale;
 };
 
 // One state launch of `jobs` jobs: groups of 8 jobs, one workgroup (one per
@@ -1762,12 +1911,12 @@ void launch_state_kind(const StateArgs& a, int64_t jobs, hipStream_t st) {
   if (wide_rounds * kWideStepPct >= narrow_rounds * 100) {
     hipLaunchKernelGGL((kda_state_kernel<KIND, NVT_NARROW>), dim3((unsigned)(((jobs + 7) / 8) * 8 * NSLICE)),
                        dim3(64 * SWAVES), 0, st, a.v, a.cu, a.chunk_off, a.h0, a.hT, a.out, a.ws, a.seg, a.T, a.N,
-                       a.Hv, a.mc, a.init_dtype, a.final_dtype, a.nseg, a.seg_len);
+                       a.Hv, a.mc, a.init_dtype, a.final_dtype, a.nseg, a.seg_len, a.scale);
   } else {
     constexpr int nsl = DV / (16 * NVT_WIDE);
     hipLaunchKernelGGL((kda_state_kernel<KIND, NVT_WIDE>), dim3((unsigned)(((jobs + 7) / 8) * 8 * nsl)),
                        dim3(64 * SWAVES), 0, st, a.v, a.cu, a.chunk_off, a.h0, a.hT, a.out, a.ws, a.seg, a.T, a.N,
-                       a.Hv, a.mc, a.init_dtype, a.final_dtype, a.nseg, a.seg_len);
+                       a.Hv, a.mc, a.init_dtype, a.final_dtype, a.nseg, a.seg_len, a.scale);
   }
 }
 
@@ -1783,7 +1932,8 @@ kda_status launch_state(const kda_fwd_params* p, const void* v, const int64_t* c
   int seg_len;
   const int nseg = seg_plan(p, packed, &seg_len);
   const StateArgs a{(const uint16_t*)v, cu_seqlens, chunk_off, initial_state, final_state, (uint16_t*)out, blocks,
-                    seg, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype, p->final_state_dtype, nseg, seg_len};
+                    seg, p->T, p->num_seqs, p->H_v, (int)mc, p->init_state_dtype, p->final_state_dtype, nseg, seg_len,
+                    p->scale};
   if (nseg > 1) {
     // entry states of the segments from their zero-state carries and maps
     launch_state_kind<ST_CARRY>(a, (int64_t)chains * (nseg - 1), st);

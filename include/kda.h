@@ -34,6 +34,15 @@
  * with b_t = sigmoid(beta_t) (beta_t itself with KDA_FLAG_BETA_IS_PROB) and q,
  * k L2-normalised in the kernel with KDA_FLAG_QK_L2NORM.
  *
+ * Magnitudes: v and the states may hold any finite bf16 / fp32 values; both
+ * entries scale their out and final_state exactly (bit for bit) when v and
+ * initial_state are scaled together by a power of two, as long as the results
+ * stay normal in their own dtype.  With KDA_FLAG_QK_L2NORM, q and k may hold
+ * any finite values.  Without it they are used as given, and the chunked
+ * entry rounds them (times decay factors <= 1) to fp16, so their elements
+ * must stay well below 2^15 in size -- far beyond where the recurrence with
+ * beta near 1 stays bounded.
+ *
  * Ownership: every buffer is allocated and owned by the caller.  The library
  * allocates no device memory, keeps no mutable global state except a
  * thread-local error string, and never synchronises: kda_fwd returns once its

@@ -3,9 +3,9 @@
 Small cases are compared element by element (several 64-token chunks plus a
 ragged tail, every gate mode, packed sequences, grouped heads, state dtypes);
 the six measured workloads are run at full size in the same launch
-configuration the benchmark times, and compared on sampled (sequence, head)
-pairs that the oracle evaluates one by one, plus properties that hold at any
-size (every output written, finite).
+configuration the benchmark times and compared element by element on every
+(sequence, head) chain, plus properties that hold at any size (every output
+written, finite).
 """
 import math
 
@@ -113,9 +113,12 @@ def test_packed_wide_slices():
     U.assert_parity(U.errors(U.as_f64(o), o_ref, U.as_f64(s), s_ref), "packed wide")
 
 
-def test_wide_slices_match_narrow_bitwise():
-    # 64 chains take 32-column slices, 65 take 64-column ones; the per-element
-    # arithmetic is the same, so the shared sequences agree bit for bit
+def test_wide_slices_match_narrow():
+    # 64 chains take 32-column slices, 65 take 64-column ones.  The per-element
+    # arithmetic is the same, but each workgroup picks its own power-of-two
+    # operand scale from the magnitudes of its slice, so fp16 values near the
+    # bottom of the range round differently: the two agree within the parity
+    # tolerances, and far inside the fp32 state tolerance.
     inp = small(B=17, T=333, Hqk=2, Hv=4, gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-5.0)
     d = U.to_device(inp)
     U.log("[gpu] wide vs narrow slices")
@@ -124,8 +127,9 @@ def test_wide_slices_match_narrow_bitwise():
     o16, s16 = kda.fwd(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], d["A_log"], d["dt_bias"], inp.scale,
                        inp.lower_bound, inp.gate_mode, initial_state=sl["h0"])
     torch.cuda.synchronize()
-    assert torch.equal(o17[:16], o16)
-    assert torch.equal(s17[:16], s16)
+    e = U.errors(U.as_f64(o17[:16]), U.as_f64(o16), U.as_f64(s17[:16]), U.as_f64(s16))
+    U.assert_parity(e, "wide vs narrow")
+    assert e["state_rel"] <= 1e-5, e
 
 
 def test_empty_dense_returns_initial_state():
@@ -228,32 +232,27 @@ def test_long_cumulative_decay_no_write():
 
 
 # ---------------------------------------------------------------- the five measured workloads
-SAMPLES = {1: None, 2: [(0, 0), (1, 5), (3, 15), (2, 9)], 3: [(0, 0), (1, 31), (0, 17), (1, 6)],
-           4: [(0, 0), (5, 31), (11, 7), (15, 20)], 5: [(0, 0), (0, 1), (0, 17), (0, 30)],
-           6: [(0, 0), (0, 1), (0, 2), (0, 3)]}
-
-
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6])
 def test_measured_workload(idx):
+    # every (sequence, head) chain at full size, in the benchmark's launch
+    # configuration, against the oracle on all host threads
     inp = W.workload(idx)
     U.log(f"[gpu] workload {idx} {inp.name}: B={inp.B} T={inp.T} Hqk={inp.Hqk} Hv={inp.Hv} N={inp.N}")
     o, s = U.run_gpu(inp)
     assert not torch.isnan(o.float()).any(), "some output element was not written"
     assert torch.isfinite(o.float()).all() and torch.isfinite(s.float()).all()
     bf = inp.final_state_dtype == W.STATE_BF16
-    if SAMPLES[idx] is None:
-        o_ref, s_ref = U.run_oracle(inp)
-        U.assert_parity(U.errors(U.as_f64(o), o_ref, U.as_f64(s), s_ref, state_bf16=bf), inp.name)
-        return
-    refs = U.oracle_pairs(inp, SAMPLES[idx])
-    for (n, h), (o_ref, s_ref) in refs.items():
-        if inp.cu_seqlens is None:
-            og = o[n, :, h]
-        else:
-            a, b = int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
-            og = o[0, a:b, h]
-        U.assert_parity(U.errors(U.as_f64(og), o_ref, U.as_f64(s[n, h]), s_ref, state_bf16=bf),
-                        f"{inp.name} pair n={n} h={h}")
+    o_gpu, s_gpu = U.as_f64(o), U.as_f64(s)
+    del o, s
+    U.log(f"[gpu] workload {idx}: oracle on every chain")
+    o_ref, s_ref = U.run_oracle(inp)
+    U.assert_parity(U.errors(o_gpu, o_ref, s_gpu, s_ref, state_bf16=bf), inp.name)
+    if not bf:
+        # the fp32 state tolerance also holds chain by chain
+        d = (s_gpu - s_ref).reshape(inp.N * inp.Hv, -1)
+        r = np.linalg.norm(d, axis=1) / np.linalg.norm(s_ref.reshape(inp.N * inp.Hv, -1), axis=1)
+        U.log(f"    worst chain state_rel {r.max():.3e}")
+        assert r.max() <= U.STATE_REL, r.max()
 
 
 @pytest.mark.parametrize("mode", [W.GATE_SAFE_SIGMOID, W.GATE_SOFTPLUS])
