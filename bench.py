@@ -4,15 +4,20 @@
 One step = one full forward (kda_fwd: intra-chunk kernel + state-chain
 kernel) over the safe-gate workload B=2, T=8192, H=32, K=V=128 (lower_bound
 -5, fp32 initial and final state), inputs resident in HBM.  Prints one JSON
-line: tokens/s, the dominant kernel's roofline from HIP events recorded
-around each stage on the launch stream, the path's fraction of the HBM and
-bf16 MFMA peaks, and the fp64 CPU oracle timed on this host's cores.
+line: tokens/s with the median / min / max step, the dominant kernel's
+roofline from HIP events recorded around each stage on the launch stream
+(algorithmic bytes: the kernel's own share of the method's minimum HBM bytes
+per token-head), the path's fraction of the HBM and bf16 MFMA peaks, counter
+figures from the committed rocprofv3 summaries when they match the current
+source, and the fp64 CPU oracle timed on this host's cores.
 """
 import argparse
 import hashlib
 import json
 import os
 import re
+import glob
+import statistics
 import sys
 import time
 
@@ -37,23 +42,35 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(kernel, workload_name):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_name}.md")
+def profile_figure(name, kernel, workload_name, key):
+    """A figure from a committed rocprofv3 summary (profiles/<name>_<kernel>_<workload>.md),
+    if that summary was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}_{kernel}_{workload_name}.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m_src = re.search(r"source_sha:\s*([0-9a-f]+)", txt)
-    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    m_b = re.search(key + r":\s*([0-9.eE+-]+)", txt)
     if not m_src or not m_b or m_src.group(1) != kernel_source_hash():
         return None
     return float(m_b.group(1))
 
 
+def profiled_traffic(kernel, workload_name):
+    """Counted HBM bytes per launch (FETCH_SIZE and WRITE_SIZE passes scaled by a
+    plain copy's readings) from the committed summary; None if stale or absent."""
+    return profile_figure("traffic", kernel, workload_name, "hbm_bytes_per_launch")
+
+
 def bytes_model(inp):
-    """Compulsory bytes per launch of each kernel given the two-kernel dataflow,
-    and the method's own minimum for the whole path."""
+    """Algorithmic HBM bytes: the method's minimum per token-head (q, k per qk-head
+    and v, g, out at 256 B each, beta 2 B; states once per (sequence, v-head)),
+    split into each kernel's own share -- the intra kernel reads q, k, g and
+    beta (770 B per token-head with one qk-head per v-head), the state kernel
+    reads v and the initial state and writes out and the final state (512 B
+    per token-head plus the states).  The per-chunk workspace the intra kernel
+    writes and the state kernel reads is an overhead of the two-kernel
+    dataflow, reported beside these, never inside them."""
     B, T, Hqk, Hv, K, V = inp.B, inp.T, inp.Hqk, inp.Hv, inp.K, inp.V
     nchunks = B * ((T + 63) // 64) if inp.cu_seqlens is None else sum(
         (int(inp.cu_seqlens[n + 1] - inp.cu_seqlens[n]) + 63) // 64 for n in range(inp.N))
@@ -61,11 +78,36 @@ def bytes_model(inp):
     st = {0: 0, 1: 4, 2: 2}
     h0 = inp.N * Hv * V * K * st[inp.init_state_dtype]
     hT = inp.N * Hv * V * K * st[inp.final_state_dtype]
-    inter = nchunks * Hv * BLOCK_BYTES
-    intra = tok * Hqk * K * 2 * 2 + tok * Hv * K * 2 + tok * Hv * 2 + inter
-    state = inter + tok * Hv * V * 2 + tok * Hv * V * 2 + h0 + hT
-    path = tok * Hqk * K * 2 * 2 + tok * Hv * (K * 2 + V * 2 + 2 + V * 2) + h0 + hT
-    return {"intra": intra, "state": state, "path": path}
+    intra = tok * Hqk * K * 2 * 2 + tok * Hv * K * 2 + tok * Hv * 2
+    state = tok * Hv * V * 2 + tok * Hv * V * 2 + h0 + hT
+    return {"intra": intra, "state": state, "path": intra + state, "workspace": nchunks * Hv * BLOCK_BYTES,
+            "token_heads": tok * Hv}
+
+
+def host_info():
+    """CPU model and thread count of this host, and the GPU clock levels as the
+    driver's sysfs files list them (the current level is marked with *).  Read
+    from files: no program is started once the GPU is in use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    clocks = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for clk in ("sclk", "mclk", "fclk"):
+            try:
+                with open(os.path.join(dev, f"pp_dpm_{clk}")) as f:
+                    cur = [l.strip() for l in f if "*" in l]
+                if cur:
+                    clocks[f"{os.path.basename(os.path.dirname(dev))}.{clk}"] = cur[0]
+            except OSError:
+                pass
+    return {"cpu_model": model, "cpu_threads": os.cpu_count(), "gpu_clocks": clocks or None}
 
 
 def cpu_baseline(inp, out_gpu, state_gpu, budget_s=30.0):
@@ -76,6 +118,7 @@ def cpu_baseline(inp, out_gpu, state_gpu, budget_s=30.0):
     from tests import gpu_util as U
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    build = oracle.native_build_description()
     # calibrate on one head to keep the run bounded (10-30 s of CPU work)
     t0 = time.perf_counter()
     U.oracle_pair(inp, 0, 0, inp.initial_state_f64())
@@ -107,7 +150,7 @@ def cpu_baseline(inp, out_gpu, state_gpu, budget_s=30.0):
     cpu = {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
            "sample": f"{inp.name}: all {inp.B * inp.T} tokens of {heads} of {inp.Hv} v-heads "
                      f"(fp64 token recurrence, {dt:.1f} s; tokens/s scaled to all heads)",
-           "seconds": dt}
+           "seconds": dt, "build": build}
     parity = {"out_max_abs": e["out_max_abs"], "out_rel_rms": e["out_rel_rms"], "state_rel": e["state_rel"],
               "heads_checked": heads, "tol_out_max_abs": U.OUT_MAX_ABS, "tol_state_rel": U.STATE_REL}
     return cpu, parity
@@ -132,6 +175,12 @@ def main():
         print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); "
               "multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
         sys.exit(2)
+
+    if not args.no_cpu_baseline and not args.copy_calibration:
+        # the oracle for the CPU baseline, compiled for this host's CPU before
+        # anything touches the GPU (no program is started after that)
+        import oracle
+        oracle.use_native_build()
 
     import torch
     from gated_delta_rule_act_amd import kda, workloads as W
@@ -178,15 +227,16 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` full forwards
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: exactly `steps` full forwards, an event after each
+    evt = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(args.steps):
+    evt[0].record()
+    for i in range(args.steps):
         step()
-    ev1.record()
+        evt[i + 1].record()
     torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = evt[0].elapsed_time(evt[-1]) / args.steps
+    step_ms = [evt[i].elapsed_time(evt[i + 1]) for i in range(args.steps)]
 
     # per-kernel durations: events around each stage on the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -206,10 +256,17 @@ def main():
     bm = bytes_model(inp)
     kern = {"intra": t_intra, "state": t_state}
     dom = max(kern, key=kern.get)
+    kname = f"kda_{dom}_kernel"
     achieved = bm[dom] / (kern[dom] * 1e-3) / 1e9
-    traffic = profiled_traffic(dom, inp.name)
+    traffic = profiled_traffic(kname, inp.name)
     path_gbps = bm["path"] / (ms_per_step * 1e-3) / 1e9
     mfma_tflops = FLOP_PER_TOKEN_HEAD * tokens * inp.Hv / (ms_per_step * 1e-3) / 1e12
+    counters = {}
+    for k in ("intra", "state"):
+        for fig in ("mfma_busy_pct", "valu_busy_pct", "wait_pct"):
+            v = profile_figure("counters", f"kda_{k}_kernel", inp.name, fig)
+            if v is not None:
+                counters[f"kda_{k}_kernel.{fig}"] = v
 
     rec = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -221,15 +278,29 @@ def main():
                    "initial_state": ["none", "fp32", "bf16"][inp.init_state_dtype],
                    "final_state": ["none", "fp32", "bf16"][inp.final_state_dtype],
                    "packed": inp.cu_seqlens is not None, "state_segments": nseg},
-        "roofline": {"bound": "hbm", "kernel": f"kda_{dom}_kernel", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": bm[dom],
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": bm[dom],
+                     "algorithmic_bytes_per_token_head": bm[dom] / bm["token_heads"],
+                     "convention": "the kernel's own share of the method minimum (intra: q, k, g, beta; "
+                                   "state: v, out, states); the per-chunk workspace is overhead",
+                     "workspace_bytes_per_launch": bm["workspace"],
+                     "traffic_over_algorithmic": None if traffic is None else traffic / bm[dom],
                      "avg_launch_ms": kern[dom]},
         "kernels_ms": {"kda_intra_kernel": t_intra, "kda_state_kernel": t_state},
-        "path": {"min_bytes_per_step": bm["path"], "achieved_GBps": path_gbps,
-                 "hbm_frac": path_gbps / HBM_PEAK_GBPS, "mfma_algorithmic_TFLOPs": mfma_tflops,
+        "step_ms": {"mean": ms_per_step, "median": statistics.median(step_ms), "min": min(step_ms),
+                    "max": max(step_ms)},
+        "path": {"min_bytes_per_step": bm["path"], "min_bytes_per_token_head": bm["path"] / bm["token_heads"],
+                 "achieved_GBps": path_gbps, "hbm_frac": path_gbps / HBM_PEAK_GBPS,
+                 "mfma_algorithmic_TFLOPs": mfma_tflops,
                  "mfma_pct_bf16_peak": 100.0 * mfma_tflops / BF16_PEAK_TFLOPS,
-                 "flop_per_token_head": FLOP_PER_TOKEN_HEAD},
+                 "flop_per_token_head": FLOP_PER_TOKEN_HEAD,
+                 "workspace_round_trip_bytes": 2 * bm["workspace"]},
+        "counters_rocprof": counters or None,
+        "conditions": {**host_info(),
+                       "cache": "inputs resident in HBM and warm from the previous step; the working set "
+                                "(inputs, outputs, workspace) is larger than the 256 MB Infinity Cache; "
+                                "no flush between steps"},
         "kernel_source_sha": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -45,6 +45,34 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def use_native_build() -> str:
+    """For timing on the host that runs it: compile this same source with
+    -O3 -march=native into a private temporary directory and use that library
+    from now on (the shipped library stays portable, -O2 for any x86-64).
+    Floating-point contraction stays off, so the arithmetic is the same.
+    Returns the build description."""
+    global _lib
+    import tempfile
+    flags = ["-O3", "-march=native", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-std=c99"]
+    d = tempfile.mkdtemp(prefix="kda_oracle_")
+    path = os.path.join(d, "libkda_oracle_native.so")
+    subprocess.check_call(["gcc", *flags, "-o", path, _SRC, "-lm"])
+    global _LIB_OVERRIDE, _NATIVE
+    _lib = None
+    _LIB_OVERRIDE = path
+    _load()
+    _NATIVE = "gcc " + " ".join(flags)
+    return _NATIVE
+
+
+_NATIVE = None
+
+
+def native_build_description() -> str:
+    """How the library in use was built."""
+    return _NATIVE or "gcc -O2 -fopenmp (shipped build)"
+
+
 def _load():
     global _lib
     if _lib is None:
