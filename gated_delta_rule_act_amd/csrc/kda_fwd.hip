@@ -39,11 +39,18 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "kda.h"
 #include "kda_internal.h"
 #include "kda_segment.h"
+
+// Device memory of kda_fwd_noalloc: the workspace of its calls, one array per
+// GPU, allocated with the code object and held until the process ends.  Host
+// code must not use this name as an address: it takes the address the
+// runtime reports for the current device (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[KDA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 using namespace kda_internal;
@@ -1994,6 +2001,57 @@ kda_status kda_fwd_state(const kda_fwd_params* p, const void* q, const void* k, 
   if (s != KDA_OK) return s;
   (void)hipGetLastError();
   launch_state(p, v, cu_seqlens, initial_state, final_state, out, workspace, reinterpret_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+}  // extern "C"
+
+namespace {
+// The address of `scratch` on each device, looked up once per device with that
+// device current (every GPU holds its own copy of the array).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+kda_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KDA_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KDA_ERR_UNSUPPORTED, "device index %d is beyond the %d this library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(KDA_ERR_LAUNCH, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kda_status kda_fwd_noalloc(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, const float* A_log, const float* dt_bias, const int64_t* cu_seqlens,
+                           const void* initial_state, void* final_state, void* out, void* stream) {
+  kda_status s = check_call(p, q, k, v, g, beta, A_log, dt_bias, cu_seqlens, initial_state, final_state, out,
+                            nullptr, 0, false);
+  if (s != KDA_OK) return s;
+  const size_t need = kda_fwd_workspace_size(p);
+  if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
+    return fail(KDA_ERR_WORKSPACE, "kda_fwd_noalloc handles calls whose workspace fits %zu bytes; this one needs %zu "
+                "(use kda_fwd with a caller workspace)", (size_t)KDA_NOALLOC_SCRATCH_BYTES, need);
+  void* ws = nullptr;
+  if ((s = noalloc_scratch(&ws)) != KDA_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  // the same launches as kda_fwd, on the device array; nothing in the
+  // workspace needs to start at zero (every block is written before it is read)
+  if ((s = launch_intra(p, q, k, g, beta, A_log, dt_bias, cu_seqlens, ws, st)) != KDA_OK) return s;
+  if ((s = launch_state(p, v, cu_seqlens, initial_state, final_state, out, ws, st)) != KDA_OK) return s;
   return launch_status();
 }
 

@@ -18,6 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_OK = 0
+KDA_ERR_WORKSPACE = -6
 GATE_SOFTPLUS = 0
 GATE_SAFE_SIGMOID = 1
 GATE_PREGATED = 2
@@ -32,7 +33,8 @@ _STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DT
 
 # Every function the header declares.
 EXPORTS = ("kda_fwd_workspace_size", "kda_fwd_segments", "kda_fwd_check", "kda_fwd", "kda_fwd_intra", "kda_fwd_state",
-           "kda_fused_recurrent_fwd", "kda_bwd_workspace_size", "kda_bwd", "kda_status_string", "kda_last_error")
+           "kda_fwd_noalloc", "kda_fused_recurrent_fwd", "kda_bwd_workspace_size", "kda_bwd", "kda_status_string",
+           "kda_last_error")
 
 
 class KdaError(RuntimeError):
@@ -72,8 +74,9 @@ def load_library(path: str = LIB_PATH):
     for fn in (lib.kda_fwd, lib.kda_fwd_intra, lib.kda_fwd_state):
         fn.restype = ctypes.c_int
         fn.argtypes = [PP] + [P] * 12 + [ctypes.c_size_t, P]
-    lib.kda_fused_recurrent_fwd.restype = ctypes.c_int
-    lib.kda_fused_recurrent_fwd.argtypes = [PP] + [P] * 11 + [P]
+    for fn in (lib.kda_fused_recurrent_fwd, lib.kda_fwd_noalloc):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [PP] + [P] * 11 + [P]
     lib.kda_bwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_bwd_workspace_size.argtypes = [PP]
     lib.kda_bwd.restype = ctypes.c_int
@@ -135,7 +138,7 @@ def _state_code(t: Optional[torch.Tensor]) -> int:
 def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GATE_SOFTPLUS,
         initial_state=None, final_state_dtype=torch.float32, cu_seqlens=None, out=None,
         final_state=None, workspace=None, stage=None, qk_l2norm=True, beta_is_prob=False, recurrent=False,
-        segments=0):
+        segments=0, noalloc=False):
     """Chunked KDA forward on the current HIP stream.
 
     q, k [B,T,Hqk,128] bf16; v, g [B,T,Hv,128] bf16; beta [B,T,Hv] bf16 logits
@@ -148,7 +151,10 @@ def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GAT
     or "state" runs only that half of the forward (kda_fwd_intra /
     kda_fwd_state); the two halves in order are the full forward.
     ``recurrent`` runs the token-recurrent entry (kda_fused_recurrent_fwd)
-    instead: no workspace.  ``final_state`` may be ``initial_state`` in both
+    instead: no workspace.  ``noalloc`` runs kda_fwd_noalloc: the chunked
+    forward on the library's own device array, no workspace (``out`` and
+    ``final_state`` should then be passed in, as that entry is for callers
+    that allocate nothing).  ``final_state`` may be ``initial_state`` in both
     entries.  ``segments`` splits each state chain of dense input into that
     many parallel time segments (0: the library decides, 1: never).
     """
@@ -183,12 +189,12 @@ def fwd(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound=-1.0, gate_mode=GAT
                     flags=(FLAG_QK_L2NORM if qk_l2norm else 0) | (FLAG_BETA_IS_PROB if beta_is_prob else 0),
                     segments=int(segments))
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    if recurrent:
-        if stage is not None or workspace is not None:
-            raise ValueError("the recurrent entry has no stages and no workspace")
-        rc = lib.kda_fused_recurrent_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
-                                         _ptr(dt_bias), _ptr(cu_seqlens), _ptr(initial_state), _ptr(final_state),
-                                         _ptr(out), ctypes.c_void_p(stream))
+    if recurrent or noalloc:
+        if stage is not None or workspace is not None or (recurrent and noalloc):
+            raise ValueError("the recurrent and allocation-free entries have no stages and no workspace")
+        fn = lib.kda_fused_recurrent_fwd if recurrent else lib.kda_fwd_noalloc
+        rc = fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
+                _ptr(cu_seqlens), _ptr(initial_state), _ptr(final_state), _ptr(out), ctypes.c_void_p(stream))
         if rc != KDA_OK:
             raise KdaError(rc, lib.kda_last_error().decode())
         return out, final_state

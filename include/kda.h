@@ -44,8 +44,10 @@
  * beta near 1 stays bounded.
  *
  * Ownership: every buffer is allocated and owned by the caller.  The library
- * allocates no device memory, keeps no mutable global state except a
- * thread-local error string, and never synchronises: kda_fwd returns once its
+ * allocates no device memory of its own (the one exception is the fixed
+ * device array of kda_fwd_noalloc, part of the loaded code object), keeps no
+ * mutable global state except a thread-local error string and that array's
+ * address per device, and never synchronises: kda_fwd returns once its
  * kernels are enqueued on `stream`.  Calls that use distinct workspaces are
  * independent; two calls in flight must not share a workspace.
  *
@@ -176,6 +178,26 @@ kda_status kda_fwd_state(const kda_fwd_params* p,
                          const void* beta, const float* A_log, const float* dt_bias,
                          const int64_t* cu_seqlens, const void* initial_state, void* final_state,
                          void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free form of kda_fwd, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same parameters, tensors,
+ * validation and results as kda_fwd (the same kernels, bit for bit), minus the
+ * workspace: its calls use a device array of KDA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on from the first such call until the
+ * process ends.  It calls no allocating routine.  Calls whose workspace
+ * (kda_fwd_workspace_size) exceeds that size are rejected with
+ * KDA_ERR_WORKSPACE before anything is enqueued.  All calls on one GPU share
+ * its array: two calls whose work overlaps in time on the same GPU (different
+ * streams, or host threads) race and corrupt each other's results; serialise
+ * them (one stream, or one call in flight per GPU).  Nothing in the array
+ * needs to start at zero.  Returns after enqueueing. */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+kda_status kda_fwd_noalloc(const kda_fwd_params* p,
+                           const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, const float* A_log, const float* dt_bias,
+                           const int64_t* cu_seqlens, const void* initial_state, void* final_state,
+                           void* out, void* stream);
 
 /* Token-recurrent forward, for decode steps and short sequences: the second
  * public entry point (fused recurrent, beside the chunked one) that the
