@@ -305,14 +305,6 @@ __device__ __forceinline__ float dpp_row_shr(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float scan16(float x) {
-  x += dpp_row_shr<0x111>(x);
-  x += dpp_row_shr<0x112>(x);
-  x += dpp_row_shr<0x114>(x);
-  x += dpp_row_shr<0x118>(x);
-  return x;
-}
-
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -512,10 +504,24 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const float bp = (flags & KDA_FLAG_BETA_IS_PROB) ? blogit : fast_rcp(1.0f + fast_exp2(-kLog2e * blogit));
       sBeta[r] = valid ? bp : 0.0f;
     }
+    // the 32 scans of a lane advance together, one shift at a time: each DPP
+    // step then reads a value written many instructions earlier (no hazard wait)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) G[kb][e] = scan16(G[kb][e]);
+      for (int e = 0; e < 8; ++e) G[kb][e] += dpp_row_shr<0x111>(G[kb][e]);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) G[kb][e] += dpp_row_shr<0x112>(G[kb][e]);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) G[kb][e] += dpp_row_shr<0x114>(G[kb][e]);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) G[kb][e] += dpp_row_shr<0x118>(G[kb][e]);
     // sub-chunk totals (row 15) and midpoint values (row 8), both local
     if (li == 15 || li == 8) {
       float* dst = (li == 15 ? sTot : sMid) + I * 128;
@@ -1200,7 +1206,8 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
       uw = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[2]), sb[2], uw, 0, 0, 0);
       ub = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[1]), vb1, ub, 0, 0, 0);
       uw = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[3]), sb[3], uw, 0, 0, 0);
-      U[vt] = ub * scn + uw * f;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) U[vt][rr] = __builtin_fmaf(ub[rr], scn, uw[rr] * f);
     } else {
       f32x4 uw2 = f32x4{0, 0, 0, 0};
 #pragma unroll
@@ -1252,14 +1259,16 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
     const half8 ul1 = *reinterpret_cast<const half8*>(x.sUl + (16 * vt + li) * SUS + 32 + 8 * lg);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      f32x4 sa = S[j][vt] * (j == 0 ? gn0 : gn1), sb2 = f32x4{0, 0, 0, 0}, sl = f32x4{0, 0, 0, 0};
+      // one chain for the fp16 parts, one for the scaled low part of Kd
+      f32x4 sa = S[j][vt] * (j == 0 ? gn0 : gn1), sl = f32x4{0, 0, 0, 0};
       sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0]), uh0, sa, 0, 0, 0);
-      sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1]), uh1, sb2, 0, 0, 0);
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0]), ul0, sa, 0, 0, 0);
-      sb2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1]), ul1, sb2, 0, 0, 0);
       sl = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdlo[j][0], uh0, sl, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1]), uh1, sa, 0, 0, 0);
       sl = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdlo[j][1], uh1, sl, 0, 0, 0);
-      S[j][vt] = (sa + sb2) + sl * kKdLoUnscale;
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0]), ul0, sa, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1]), ul1, sa, 0, 0, 0);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) S[j][vt][rr] = __builtin_fmaf(sl[rr], kKdLoUnscale, sa[rr]);
     }
     if constexpr (KIND == ST_FULL) {
       O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[0]), uh0, O[vt], 0, 0, 0);
