@@ -890,7 +890,10 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // loaded by exactly one wave, straight into registers: the token-tile
 // operands (W, Q . 2^G, T diag(b), Aqk) two chunks ahead, the key-tile
 // operands (Kd) one chunk ahead -- they are needed only after the second
-// barrier.  The V slices of one chain run on one XCD and share its L2.
+// barrier.  The loads are issued in groups between the MFMA products of each
+// half of the step rather than in one burst before a barrier: a wave whose
+// loads find the memory queue full stalls at issue, and before a barrier that
+// holds up all four.  The V slices of one chain run on one XCD and share its L2.
 constexpr int SWAVES = 4;
 // What one state workgroup computes over its range of chunks:
 //   ST_FULL   outputs and the state (the whole chain, or one segment of it
@@ -941,19 +944,23 @@ __device__ __forceinline__ void load_v(ChunkRegs& o, const uint16_t* __restrict_
 }
 
 // PART 0: token-tile operands, vectors and (narrow slices) V, issued two
-// chunks ahead (wide slices: one chunk ahead, V two chunks ahead on its own);
-// PART 1: key-tile operands (issued one chunk ahead).
+// chunks ahead (wide slices: one chunk ahead, V two chunks ahead on its own),
+// also in groups: PART 2 the W fragments, PART 4 the Q fragments, PART 3 the
+// rest; PART 1: key-tile operands (issued one chunk ahead).
 // Operands a kind does not use are neither loaded nor kept.
 template <int PART, int KIND, int NVT>
 __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk, int wave, int lane,
                                                 const uint16_t* __restrict__ v, int64_t row0, int len, int Hv, int h,
                                                 int v0, int tid) {
-  if constexpr (PART == 0) {
+  if constexpr (PART == 0 || PART == 2) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      o.wn[kb] = ld_frag(blk, F_WN + wave * 4 + kb, lane);
-      if constexpr (KIND == ST_FULL) o.qg[kb] = ld_frag(blk, F_QG + wave * 4 + kb, lane);
-    }
+    for (int kb = 0; kb < 4; ++kb) o.wn[kb] = ld_frag(blk, F_WN + wave * 4 + kb, lane);
+  }
+  if constexpr ((PART == 0 || PART == 4) && KIND == ST_FULL) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) o.qg[kb] = ld_frag(blk, F_QG + wave * 4 + kb, lane);
+  }
+  if constexpr (PART == 0 || PART == 3) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // token block 1 of token tiles 0, 1 is not stored: a fragment index past
@@ -967,7 +974,8 @@ __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk
     }
     o.vec = ld_frag(blk, F_VEC, 16 * wave + (lane & 15));
     if constexpr (KIND != ST_TRANS && NVT == NVT_NARROW) load_v<NVT>(o, v, row0, len, Hv, h, v0, tid);
-  } else {
+  }
+  if constexpr (PART == 1) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1154,20 +1162,15 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
   }
   mx = wave_max_bits(mx);
   if (lane == 0) x.sMx[wave] = mx;
-  // 2. the previous chunk's outputs (none before the first chunk: len 0), then
-  //    the token-tile prefetch of chunk c+2 (clamped, so every chunk queues the
-  //    same operations)
+  // 2. the previous chunk's outputs (none before the first chunk: len 0); the
+  //    prefetches are issued between the MFMA groups below, a few loads at a
+  //    time, so no wave stalls on a full memory queue before a barrier.
+  //    Prefetch indices are clamped, so every chunk queues the same operations.
   if constexpr (KIND == ST_FULL) store_pending(pd, x.out, x.Hv, x.h, x.v0, wave, li, lg);
-  {
-    constexpr int AHEAD = NVT == NVT_NARROW ? 2 : 1;
-    const int cp = min(c + AHEAD, x.nc - 1);
-    load_chunk_part<0, KIND, NVT>(AHEAD == 2 ? n2 : n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, x.bos + (int64_t)cp * CH,
-                       chunk_len(x, cp), x.Hv, x.h, x.v0, tid);
-    if constexpr (KIND != ST_TRANS && NVT != NVT_NARROW) {
-      const int cv = min(c + 2, x.nc - 1);
-      load_v<NVT>(cur, x.v, x.bos + (int64_t)cv * CH, chunk_len(x, cv), x.Hv, x.h, x.v0, tid);
-    }
-  }
+  constexpr int AHEAD = NVT == NVT_NARROW ? 2 : 1;
+  ChunkRegs& nt = AHEAD == 2 ? n2 : n1;  // receives the token-tile operands of chunk c + AHEAD
+  const int ct = min(c + AHEAD, x.nc - 1);
+  const uint8_t* blk_t = x.wsh + (size_t)(x.x0 + ct) * BLOCK;
   __syncthreads();  // B1
   // the scale of the chunk's results: E_(c+1) = E_c + d
   const int d = scale_shift(x.sMx, E);
@@ -1218,14 +1221,24 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
       U[vt] = (uw + uw2) * f;
     }
     if constexpr (KIND == ST_FULL) O[vt] = (o0 + o1) * sf;
+    // 4. the token-tile prefetch: the W and Q fragments after the first V
+    //    tile's products, the rest after the second
+    if (vt < 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (vt == 0) {
+        load_chunk_part<2, KIND, NVT>(nt, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+        load_chunk_part<4, KIND, NVT>(nt, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+      } else {
+        load_chunk_part<3, KIND, NVT>(nt, blk_t, wave, lane, x.v, x.bos + (int64_t)ct * CH, chunk_len(x, ct), x.Hv,
+                                      x.h, x.v0, tid);
+        if constexpr (KIND != ST_TRANS && NVT != NVT_NARROW) {
+          const int cv = min(c + 2, x.nc - 1);
+          load_v<NVT>(cur, x.v, x.bos + (int64_t)cv * CH, chunk_len(x, cv), x.Hv, x.h, x.v0, tid);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  // 4. the key-tile prefetch of chunk c+1
-  __builtin_amdgcn_sched_barrier(0);
-  {
-    const int cp = min(c + 1, x.nc - 1);
-    load_chunk_part<1, KIND, NVT>(n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
-  }
-  __builtin_amdgcn_sched_barrier(0);
   // 5. U -> LDS hi/lo, transposed [v][t]
   float mu_n = 0.0f;  // this wave's largest |U|
 #pragma unroll
@@ -1273,6 +1286,14 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
     if constexpr (KIND == ST_FULL) {
       O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[0]), uh0, O[vt], 0, 0, 0);
       O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[1]), uh1, O[vt], 0, 0, 0);
+    }
+    // 7. the key-tile prefetch of chunk c+1, after the first V tile's update products
+    if (vt == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int cp = min(c + 1, x.nc - 1);
+      load_chunk_part<1, KIND, NVT>(n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0,
+                                    tid);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if constexpr (KIND == ST_FULL) {

@@ -38,7 +38,8 @@
  * entries scale their out and final_state exactly (bit for bit) when v and
  * initial_state are scaled together by a power of two, as long as the results
  * stay normal in their own dtype.  With KDA_FLAG_QK_L2NORM, q and k may hold
- * any finite values.  Without it they are used as given, and the chunked
+ * any values whose squares still sum within fp32 (elements below about 2^60
+ * in size).  Without it they are used as given, and the chunked
  * entry rounds them (times decay factors <= 1) to fp16, so their elements
  * must stay well below 2^15 in size -- far beyond where the recurrence with
  * beta near 1 stays bounded.
