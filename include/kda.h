@@ -39,7 +39,15 @@
  * initial_state are scaled together by a power of two, as long as the results
  * stay normal in their own dtype.  With KDA_FLAG_QK_L2NORM, q and k may hold
  * any values whose squares still sum within fp32 (elements below about 2^60
- * in size).  Without it they are used as given, and the chunked
+ * in size).  One limit is particular to the chunked entries: within a
+ * 64-token chunk they carry the decay factors of the chunk in 16-bit operands,
+ * so a contribution decayed below about 2^-24 of its source within one chunk
+ * is dropped.  That is negligible whenever the state is within about 2^20 of
+ * the size of the values written next, which the delta rule keeps unless v
+ * falls by more than about 2^20 from one chunk to the next (tested down to
+ * steps of 2^12 over a total range of 2^88); kda_fused_recurrent_fwd, fp32
+ * throughout, has no such limit.  Without the L2 norm q and k are used as
+ * given, and the chunked
  * entry rounds them (times decay factors <= 1) to fp16, so their elements
  * must stay well below 2^15 in size -- far beyond where the recurrence with
  * beta near 1 stays bounded.
