@@ -878,9 +878,14 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // workgroup therefore keeps them in units of 2^E: chunk c converts S_c 2^-E_c
 // and U_c 2^-E_(c+1), with one integer E per chunk shared by all the waves.
 // Before the first barrier of chunk c each wave posts to LDS the largest
-// magnitude of its S_c, its U_(c-1) and its part of the next chunk's V (in
+// magnitude of its S_c, its U_(c-1) and its token tile of T diag(b) V_c (in
 // units of 2^E_c); after the barrier every wave reads the four values and
-// sets E_(c+1) so that the largest lies in [1, 2).  The shift is applied with
+// sets E_(c+1) so that the largest lies in [1, 2).  T diag(b) V_c is formed
+// at the start of chunk c for that purpose, from the V slice that chunk c - 1
+// put in LDS (two V buffers alternate), so the scale follows what is written
+// into the state this chunk, not the size of v: a chunk whose v is far larger
+// than the state's stays in range, and writes with tiny beta keep their
+// precision instead of flushing to zero.  The shift is applied with
 // no branch: U, the state's decay factors and the output factor of the chunk
 // carry 2^(E_c - E_(c+1)), so the update lands in units of E_(c+1).  Within
 // one chunk S and U grow by far less than the 2^14 headroom this leaves under
@@ -912,6 +917,8 @@ constexpr int SUS = 72;   // sU row stride (fp16): U' stored as [v][t]
 template <int NVT> constexpr int svs() { return NVT == 2 ? 48 : 80; }
 template <int NVT> constexpr int svg() { return 8 * svs<NVT>() + 64; }
 template <int NVT> __device__ __forceinline__ int sv_row(int t) { return (t & 7) * svs<NVT>() + (t >> 3) * svg<NVT>(); }
+// one V buffer; two alternate by chunk parity
+template <int NVT> constexpr int SV_HALFS = (CH / 8) * svg<NVT>();
 
 struct ChunkRegs {
   // arrays indexed only by compile-time values (fully unrolled loops)
@@ -1134,15 +1141,35 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
   const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
   const int64_t row0 = x.bos + (int64_t)c * CH;
   typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-  // 1. publish the chunk's vectors, the V slice and the current state, and
-  //    this wave's largest magnitude of S_c, U_(c-1) and the next V.  Every
-  //    reader of these buffers in the previous chunk was before its B2.
+  // 0. Ub = T diag(b) V_c of token tile w (real units), from the V slice the
+  //    previous chunk step put in LDS, so that its magnitude can set the
+  //    scale of U_c below
+  _Float16* const sVc = x.sV + (c & 1) * SV_HALFS<NVT>;
+  f32x4 ub[NVT];
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt) {
+    ub[vt] = f32x4{0, 0, 0, 0};
+    if constexpr (KIND != ST_TRANS) {
+      const bf16x8 vb0 = __builtin_bit_cast(bf16x8, lds_frag_tr_grouped(sVc, svs<NVT>(), svg<NVT>(), 0, 16 * vt, lane));
+      const bf16x8 vb1 = __builtin_bit_cast(bf16x8, lds_frag_tr_grouped(sVc, svs<NVT>(), svg<NVT>(), 32, 16 * vt, lane));
+      ub[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[0]), vb0, ub[vt], 0, 0, 0);
+      ub[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[0]), vb0, ub[vt], 0, 0, 0);
+      ub[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[1]), vb1, ub[vt], 0, 0, 0);
+      ub[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[1]), vb1, ub[vt], 0, 0, 0);
+    }
+  }
+  // 1. publish the chunk's vectors, the next chunk's V slice and the current
+  //    state, and this wave's largest magnitude of S_c, U_(c-1) and Ub.
+  //    Every reader of these buffers in the previous chunk was before its B2
+  //    (the other V buffer: before B1 of the previous chunk).
   // (one lane per address: four lanes writing one address stall the LDS)
   if (lane < 16) reinterpret_cast<u32x4*>(x.sVec)[16 * wave + lane] = cur.vec;
-  if constexpr (KIND != ST_TRANS)
+  if constexpr (KIND != ST_TRANS) {
+    _Float16* const sVn = x.sV + ((c + 1) & 1) * SV_HALFS<NVT>;
 #pragma unroll
     for (int i = 0; i < NVT / 2; ++i)
-      *reinterpret_cast<u32x4*>(x.sV + sv_row<NVT>(tid >> 2) + 32 * i + 8 * (tid & 3)) = cur.vraw[i];
+      *reinterpret_cast<u32x4*>(sVn + sv_row<NVT>(tid >> 2) + 32 * i + 8 * (tid & 3)) = n1.vraw[i];
+  }
   float ms = 0.0f;
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -1155,10 +1182,12 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
     }
   uint32_t mx = max(mu, abs_bits(ms));
   if constexpr (KIND != ST_TRANS) {
-    uint32_t mv = 0;
+    float mb = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NVT / 2; ++i) mv = max(mv, bf16x8_absmax_bits(n1.vraw[i]));
-    mx = max(mx, abs_bits(__uint_as_float(mv) * pow2f(-E)));
+    for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) mb = fmaxf(mb, fabsf(ub[vt][rr]));
+    mx = max(mx, abs_bits(mb * pow2f(-E)));
   }
   mx = wave_max_bits(mx);
   if (lane == 0) x.sMx[wave] = mx;
@@ -1189,28 +1218,22 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
     half8 sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
-    f32x4 ub = f32x4{0, 0, 0, 0}, uw = f32x4{0, 0, 0, 0}, o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
+    f32x4 uw = f32x4{0, 0, 0, 0}, o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
     if constexpr (KIND != ST_TRANS) {
-      const bf16x8 vb0 = __builtin_bit_cast(bf16x8, lds_frag_tr_grouped(x.sV, svs<NVT>(), svg<NVT>(), 0, 16 * vt, lane));
-      const bf16x8 vb1 = __builtin_bit_cast(bf16x8, lds_frag_tr_grouped(x.sV, svs<NVT>(), svg<NVT>(), 32, 16 * vt, lane));
-      ub = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[0]), vb0, ub, 0, 0, 0);
       uw = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[0]), sb[0], uw, 0, 0, 0);
       if constexpr (KIND == ST_FULL) {
         o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[0]), sb[0], o0, 0, 0, 0);
         o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[1]), sb[1], o1, 0, 0, 0);
       }
-      ub = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[0]), vb0, ub, 0, 0, 0);
       uw = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[1]), sb[1], uw, 0, 0, 0);
       if constexpr (KIND == ST_FULL) {
         o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[2]), sb[2], o0, 0, 0, 0);
         o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[3]), sb[3], o1, 0, 0, 0);
       }
-      ub = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[1]), vb1, ub, 0, 0, 0);
       uw = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[2]), sb[2], uw, 0, 0, 0);
-      ub = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[1]), vb1, ub, 0, 0, 0);
       uw = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[3]), sb[3], uw, 0, 0, 0);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) U[vt][rr] = __builtin_fmaf(ub[rr], scn, uw[rr] * f);
+      for (int rr = 0; rr < 4; ++rr) U[vt][rr] = __builtin_fmaf(ub[vt][rr], scn, uw[rr] * f);
     } else {
       f32x4 uw2 = f32x4{0, 0, 0, 0};
 #pragma unroll
@@ -1332,7 +1355,7 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
   __shared__ __attribute__((aligned(16))) _Float16 sS[VS * SSS];
   __shared__ __attribute__((aligned(16))) _Float16 sUh[VS * SUS];
   __shared__ __attribute__((aligned(16))) _Float16 sUl[VS * SUS];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[(CH / 8) * svg<NVT>()];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[2 * SV_HALFS<NVT>];
 
   // XCD-aware decode: the NSL slices of one job share (id mod 8), so they
   // are dispatched to the same XCD and share its L2 for the job's operands.
@@ -1416,6 +1439,11 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
 #pragma unroll
     for (int vt = 0; vt < NVT; ++vt) settle(S[j][vt]);
   settle<KIND, NVT>(rA);
+  // the first chunk's V slice into V buffer 0 (visible after the barrier below)
+  if (KIND != ST_TRANS && nc > 0)
+#pragma unroll
+    for (int i = 0; i < NVT / 2; ++i)
+      *reinterpret_cast<u32x4*>(sV + sv_row<NVT>(tid >> 2) + 32 * i + 8 * (tid & 3)) = rA.vraw[i];
   // the entry scale: the largest magnitude of the entry state and the first
   // chunk's V brought into [1, 2)
   int E = 0;

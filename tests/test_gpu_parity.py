@@ -219,16 +219,20 @@ def test_extreme_A_log(A):
         U.assert_parity(U.errors(U.as_f64(o), o_ref, U.as_f64(s), s_ref), f"A_log={A} gate={mode}")
 
 
-def test_long_cumulative_decay_no_write():
-    # lb = -1 over 131072 tokens (Sum a ~ -6.5e4) with beta ~ 0: the state decays to
-    # zero without NaN; checked on one head at full length
+def test_long_cumulative_decay_tiny_beta():
+    # lb = -1 over 131072 tokens (Sum a ~ -6.5e4): the initial state decays to
+    # exactly zero, and what is left are the last tokens' writes with beta =
+    # sigmoid(-30) ~ 9.4e-14, a final state of order 1e-13 that must match the
+    # oracle rather than underflow; checked on one head at full length
     inp = W.make_inputs(B=1, T=131072, Hqk=1, seed=5, gate_mode=W.GATE_SAFE_SIGMOID, lower_bound=-1.0,
                         init_state_dtype=W.STATE_F32, h0_std=1.0)
     inp.beta = W.f32_to_bf16_bits(np.full(inp.beta.shape, -30.0, np.float32))
-    U.log("[gpu] long cumulative decay")
+    U.log("[gpu] long cumulative decay, tiny beta")
     o, s = U.run_gpu(inp)
     assert torch.isfinite(o.float()).all() and torch.isfinite(s).all()
-    assert s.abs().max().item() < 1e-30
+    o_ref, s_ref = U.run_oracle(inp)
+    assert 1e-14 < np.abs(s_ref).max() < 1e-12
+    U.assert_parity(U.errors(U.as_f64(o), o_ref, U.as_f64(s), s_ref), "long decay, tiny beta")
 
 
 # ---------------------------------------------------------------- the five measured workloads

@@ -13,7 +13,7 @@ token-recurrent path is fp32 throughout), and must match the oracle on the
 scaled inputs within the parity tolerances, measured in units of 2^s.
 Raw q and k scaled far up or down (beyond the fp16 range, 2^20) must still
 match the oracle, and so must v whose size changes from chunk to chunk by up to
-2^12 over a total range of 2^88.  The chunked path keeps the decay factors of a
+2^12 over a total range of 2^88, or jumps for a single chunk by up to 2^18.  The chunked path keeps the decay factors of a
 chunk in fp16 operands, so a contribution decayed within one chunk below about
 2^-24 of its source is dropped; that is far below the tolerance unless v falls
 by more than about 2^20 from one chunk to the next, so a fall of 2^40 is run
@@ -133,6 +133,8 @@ RAMP_UP = [8 * c for c in range(12)]
 RAMP_DOWN = [-8 * c for c in range(12)]
 MIXED = [0, 8, -4, 10, 2, -6, 6, 12, 4, -4, 8, 0]
 EXTREME = [0, 20, -20, 20, -20, 0, 16, -16, 20, 0, -20, 4]
+# single chunks far above their neighbours and the state
+SPIKES = [0, 0, 16, 0, 0, 0, 12, 0, 0, 18, 0, 0]
 
 
 def jumping_v(inp: W.KdaInputs, jumps) -> W.KdaInputs:
@@ -179,6 +181,17 @@ def test_value_magnitude_changes_between_chunks(gate, pattern, recurrent):
     jumps = {"ramp_up": RAMP_UP, "ramp_down": RAMP_DOWN, "mixed": MIXED}[pattern]
     U.log(f"[gpu] v magnitude {pattern} {jumps}, gate={gate}, recurrent={recurrent}")
     check_tokenwise(jump_inputs(gate, jumps), recurrent, pattern)
+
+
+@pytest.mark.parametrize("recurrent", [False, True])
+def test_single_chunk_spikes(recurrent):
+    # one chunk's v 2^12 .. 2^18 above the state and the chunks around it: the
+    # chunked path must scale U_c by the size of that chunk's T diag(b) V (in
+    # fp16 at the size of the state, U_c would overflow); softplus decay, so
+    # that the state written by a spike is still the larger part of the next
+    # chunks' outputs
+    U.log(f"[gpu] single-chunk spikes {SPIKES}, recurrent={recurrent}")
+    check_tokenwise(jump_inputs(W.GATE_SOFTPLUS, SPIKES), recurrent, "spikes")
 
 
 @pytest.mark.parametrize("gate", [W.GATE_SAFE_SIGMOID, W.GATE_SOFTPLUS])
