@@ -41,12 +41,16 @@
  * any values whose squares still sum within fp32 (elements below about 2^60
  * in size).  One limit is particular to the chunked entries: within a
  * 64-token chunk they carry the decay factors of the chunk in 16-bit operands,
- * so a contribution decayed below about 2^-24 of its source within one chunk
- * is dropped.  That is negligible whenever the state is within about 2^20 of
- * the size of the values written next, which the delta rule keeps unless v
- * falls by more than about 2^20 from one chunk to the next (tested down to
- * steps of 2^12 over a total range of 2^88); kda_fused_recurrent_fwd, fp32
- * throughout, has no such limit.  Without the L2 norm q and k are used as
+ * so a state decayed within one chunk below about 2^-24 of its size (fp16
+ * subnormals lose precision from 2^-14) drops out of that chunk's outputs.
+ * That is far below the output tolerance while the state and the values
+ * written next are of similar size, which the delta rule keeps, unless v
+ * changes by a large factor from one chunk to the next while strong decays
+ * act: with a per-token decay down to e^-1 (safe gate, lower bound -1) a
+ * change by 2^14 costs the following outputs about 1 % relative, 2^16 about
+ * 3 %; with mild decays a change by 2^18 stays at 0.2 %.  Tested down to
+ * steps of 2^12 per chunk over a total range of 2^88.  kda_fused_recurrent_fwd,
+ * fp32 throughout, has no such limit.  Without the L2 norm q and k are used as
  * given, and the chunked
  * entry rounds them (times decay factors <= 1) to fp16, so their elements
  * must stay well below 2^15 in size -- far beyond where the recurrence with
