@@ -319,9 +319,12 @@ __device__ __forceinline__ float gate2(float x, float A_exp, float lb_log2e) {
     return lb_log2e * fast_rcp(1.0f + fast_exp2(-(A_exp * kLog2e) * x));
   } else {
     // -A * softplus(x) * log2(e), softplus(x) = max(x, 0) + log1p(e^-|x|)
+    // (both forms are evaluated and one is selected: the choice differs from
+    // lane to lane, and a branch would run both sides anyway)
     const float ex = fast_exp2(-kLog2e * fabsf(x));
-    const float l1p = (ex < 0.0078125f) ? ex * (1.0f - ex * (0.5f - ex * (1.0f / 3.0f)))
-                                        : fast_log2(1.0f + ex) * 0.6931471805599453f;
+    const float l1p_series = ex * (1.0f - ex * (0.5f - ex * (1.0f / 3.0f)));
+    const float l1p_log = fast_log2(1.0f + ex) * 0.6931471805599453f;
+    const float l1p = (ex < 0.0078125f) ? l1p_series : l1p_log;
     const float a2 = -(A_exp * kLog2e) * (fmaxf(x, 0.0f) + l1p);
     return fmaxf(a2, kMinLog2Decay);
   }
@@ -481,6 +484,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
     const float blogit = valid ? bf2f(beta[(size_t)row * Hv + h]) : 0.0f;
+    const float vmask = valid ? 1.0f : 0.0f;
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -493,7 +497,10 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const float dtb[8] = {dtb4[2 * kb].x, dtb4[2 * kb].y, dtb4[2 * kb].z, dtb4[2 * kb].w,
                             dtb4[2 * kb + 1].x, dtb4[2 * kb + 1].y, dtb4[2 * kb + 1].z, dtb4[2 * kb + 1].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) G[kb][e] = valid ? gate2<MODE>(G[kb][e] + dtb[e], A_exp, lb_log2e) : 0.0f;
+      // the gate of a row past the chunk end (zero inputs, finite) times 0:
+      // a product, where a select had the compiler branch around each
+      // element's exponential
+      for (int e = 0; e < 8; ++e) G[kb][e] = gate2<MODE>(G[kb][e] + dtb[e], A_exp, lb_log2e) * vmask;
     }
     sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
     sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
@@ -705,10 +712,17 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       // highest bit in which i and j differ
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
+        // (a chain of selects on scalars: nested conditionals on the vector
+        // elements were compiled into branches)
         const int xd = (4 * lg + rr) ^ li;
-        dkk[rr] = xd >= 8 ? dkkp[0][rr] : xd >= 4 ? dkkp[1][rr] : xd >= 2 ? dkkp[2][rr] : dkkp[3][rr];
-        const float vq = xd >= 8 ? dqkp[0][rr] : xd >= 4 ? dqkp[1][rr] : xd >= 2 ? dqkp[2][rr] : dqkp[3][rr];
-        dqk[rr] = xd == 0 ? sQd[16 * I + 4 * lg + rr] : vq;
+        const float k0 = dkkp[0][rr], k1 = dkkp[1][rr], k2 = dkkp[2][rr], k3 = dkkp[3][rr];
+        const float q0 = dqkp[0][rr], q1 = dqkp[1][rr], q2 = dqkp[2][rr], q3 = dqkp[3][rr];
+        float vk = xd >= 2 ? k2 : k3, vq = xd >= 2 ? q2 : q3;
+        vk = xd >= 4 ? k1 : vk; vq = xd >= 4 ? q1 : vq;
+        vk = xd >= 8 ? k0 : vk; vq = xd >= 8 ? q0 : vq;
+        const float qd = sQd[16 * I + 4 * lg + rr];  // read by every lane: no branch around the load
+        dkk[rr] = vk;
+        dqk[rr] = xd == 0 ? qd : vq;
       }
     }
   }
@@ -816,7 +830,12 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const bool keep = 2 * kb + (lg >> 1) <= I;
       half8 a;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = keep ? (_Float16)(sT[t * AS + s0 + e] * sBeta[s0 + e]) : (_Float16)0.0f;
+      // every lane reads (T above the diagonal holds stale values, dropped by
+      // the select): a load under the lane-dependent condition is a branch
+      for (int e = 0; e < 8; ++e) {
+        const float tb = sT[t * AS + s0 + e] * sBeta[s0 + e];
+        a[e] = keep ? (_Float16)tb : (_Float16)0.0f;
+      }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const half8 b = __builtin_bit_cast(half8, lds_frag_tr_grouped(sKE, KER, KEG, 32 * kb, 16 * nt, lane));
@@ -833,7 +852,8 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const bool keep = 2 * kb + (ln >> 5) <= ta;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = keep ? sT[row * AS + c0 + e] * sBeta[c0 + e] : 0.0f;
+        const float tb = sT[row * AS + c0 + e] * sBeta[c0 + e];
+        const float v = keep ? tb : 0.0f;
         const __bf16 hv = (__bf16)v;
         th[e] = hv;
         tl[e] = (__bf16)(v - (float)hv);
