@@ -52,12 +52,14 @@
 #include <algorithm>
 
 #include "kda.h"
+#include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_segment.h"
 
 namespace {
 using namespace kda_internal;
 using namespace kda_segment;
+using namespace kda_device;
 
 constexpr int CH = 64;
 constexpr int DK = 128;
@@ -179,13 +181,14 @@ __device__ __forceinline__ void load_tile64(float* s, const float* g, int tid) {
   }
 }
 // 64 rows x 128 bf16 (row stride gs elements; rows >= len read as zero) -> fp32 LDS.
+// (range-checked buffer loads: rows >= len read as zero with no branch)
 template <int NTH = 256>
 __device__ __forceinline__ void load_bf16_tile128(float* s, const uint16_t* g, size_t gs, int len, int tid) {
+  const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g, (uint32_t)((size_t)len * gs * 2));
 #pragma unroll
   for (int i = 0; i < 1024 / NTH; ++i) {
     const int e = tid + NTH * i, r = e >> 4, c = 8 * (e & 15);
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (r < len) u = *reinterpret_cast<const uint4*>(g + (size_t)r * gs + c);
+    const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, (uint32_t)(r * gs + c) * 2, 0, 0));
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
     float* d = s + r * RS + c;
 #pragma unroll
@@ -229,16 +232,19 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
   constexpr int TPR = NTH / CH, CPT = DK / TPR;  // threads per row, channels per thread
   const int r = tid / TPR, c0 = CPT * (tid % TPR);
   const bool ok = r < len;
-  const size_t row = (size_t)(row0 + r);
+  // range-checked buffer loads over the chunk's rows: rows >= len read as
+  // zero, with no branch around the loads
+  const __amdgpu_buffer_rsrc_t bq = buffer_rsrc(q + ((size_t)row0 * Hqk + hq) * DK, (uint32_t)len * Hqk * DK * 2);
+  const __amdgpu_buffer_rsrc_t bk = buffer_rsrc(k + ((size_t)row0 * Hqk + hq) * DK, (uint32_t)len * Hqk * DK * 2);
+  const __amdgpu_buffer_rsrc_t bg = buffer_rsrc(g + ((size_t)row0 * Hv + h) * DK, (uint32_t)len * Hv * DK * 2);
+  const __amdgpu_buffer_rsrc_t bb = buffer_rsrc(beta + (size_t)row0 * Hv + h, (uint32_t)len * Hv * 2);
   float qv[CPT], kv[CPT], gv[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; i += 8) {
-    uint4 uq = make_uint4(0, 0, 0, 0), uk = uq, ug = uq;
-    if (ok) {
-      uq = *reinterpret_cast<const uint4*>(q + (row * Hqk + hq) * DK + c0 + i);
-      uk = *reinterpret_cast<const uint4*>(k + (row * Hqk + hq) * DK + c0 + i);
-      ug = *reinterpret_cast<const uint4*>(g + (row * Hv + h) * DK + c0 + i);
-    }
+    const uint32_t oqk = (uint32_t)(r * Hqk * DK + c0 + i) * 2, og = (uint32_t)(r * Hv * DK + c0 + i) * 2;
+    const uint4 uq = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bq, oqk, 0, 0));
+    const uint4 uk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bk, oqk, 0, 0));
+    const uint4 ug = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bg, og, 0, 0));
     const uint32_t wq[4] = {uq.x, uq.y, uq.z, uq.w}, wk[4] = {uk.x, uk.y, uk.z, uk.w}, wg[4] = {ug.x, ug.y, ug.z, ug.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -269,9 +275,11 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
     const float db[4] = {db4.x, db4.y, db4.z, db4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float a = 0.0f, d1, d2;
-      if (ok) gate_fwd_bwd<MODE>(gv[i + e] + db[e], A_exp, lb, a, d1, d2);
-      g4[e] = fmaxf(a * kLog2e, kMinLog2Decay);
+      // every row's gate (zero inputs past the end, finite), then the select:
+      // a branch around each element's exponentials costs more
+      float a, d1, d2;
+      gate_fwd_bwd<MODE>(gv[i + e] + db[e], A_exp, lb, a, d1, d2);
+      g4[e] = fmaxf((ok ? a : 0.0f) * kLog2e, kMinLog2Decay);
     }
     *reinterpret_cast<float4*>(sQ + r * RS + c0 + i) =
         make_float4(qv[i] * rq, qv[i + 1] * rq, qv[i + 2] * rq, qv[i + 3] * rq);
@@ -280,12 +288,9 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
     *reinterpret_cast<float4*>(sG + r * RS + c0 + i) = make_float4(g4[0], g4[1], g4[2], g4[3]);
   }
   if (tid % TPR == 0) {
-    float b = 0.0f;
-    if (ok) {
-      const float braw = bf2f(beta[row * Hv + h]);
-      b = (flags & KDA_FLAG_BETA_IS_PROB) ? braw : sigm(braw);
-    }
-    sB[r] = b;
+    const float braw = bf2f((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(bb, (uint32_t)(r * Hv) * 2, 0, 0));
+    const float bp = (flags & KDA_FLAG_BETA_IS_PROB) ? braw : sigm(braw);
+    sB[r] = ok ? bp : 0.0f;
   }
   __syncthreads();
   // block-local inclusive sums: thread t owns channel t & 127 and BPT of the
@@ -487,7 +492,9 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // exponents <= 0, so it is one fp32 MFMA product over the channels (A = K
   // or Q times the row factor, B = K times the column factor).
   {
-    const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
+    // (the wave index through readfirstlane: the compiler then knows it is
+    // uniform, and tests and loops on it are scalar branches, not exec masks)
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), li = lane & 15, lg = lane >> 4;
     if (w >= 4) {
       const int u = w - 4;
       const int ntask = u < 2 ? 2 : 1;
@@ -566,7 +573,7 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // T = (I + Akk)^-1: the four 16 x 16 diagonal blocks by forward
   // substitution (one wave each, lane = column), then block rows 1..3
   {
-    const int w = tid >> 6, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     if (w < 4 && lane < 16) {
       // the lane's column of the block stays in registers (zero above the
       // diagonal: those rows only ever subtract products with zeros)
@@ -657,7 +664,7 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   __syncthreads();
   // W = M Kg, Ubar = M V (split-bf16 MFMA; wave w: rows 32 (w >> 2) .., columns 32 (w & 3) ..)
   {
-    const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), li = lane & 15, lg = lane >> 4;
     const int R0 = 32 * (wv >> 2), C0 = 32 * (wv & 3);
     f32x4 w[2][2], u[2][2];
     zero_block(w);
@@ -856,7 +863,7 @@ kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ ch
   StateJob j;
   if (!state_job<KIND>(blockIdx.x, cu, chunk_off, T, N, Hv, nseg, seg_len, false, j)) return;
   const int chains = N * Hv, h = j.h, v0 = j.v0, tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), li = lane & 15, lg = lane >> 4;
   // wave w: state columns 16 w .. +15; U rows 16 (w & 3) .., columns 16 (w >> 2) ..
   const int ut = 16 * (w & 3), uv = 16 * (w >> 2);
   f32x4 S[2][1];
@@ -936,7 +943,7 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
   StateJob j;
   if (!state_job<KIND>(blockIdx.x, cu, chunk_off, T, N, Hv, nseg, seg_len, true, j)) return;
   const int chains = N * Hv, h = j.h, v0 = j.v0, tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), li = lane & 15, lg = lane >> 4;
   const int64_t seqlen = cu == nullptr ? (int64_t)T : cu[j.n + 1] - cu[j.n];
   const size_t sbase = (size_t)j.chain * DV * DK;
   // wave w: gradient columns 16 w .. +15; dU rows 16 (w & 3) .., columns 16 (w >> 2) ..
@@ -1021,7 +1028,7 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   float* gb = sb + SB_FLOATS;
   // wave w: rows 32 (w >> 2) .. of every output, columns 32 (w & 3) .. of the
   // 128-wide ones and 16 (w & 3) .. of the 64-wide ones
-  const int lane = tid & 63, w = tid >> 6, li = lane & 15, lg = lane >> 4;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), li = lane & 15, lg = lane >> 4;
   const int R0 = 32 * (w >> 2), C0 = 32 * (w & 3), Q0 = 16 * (w & 3);
   constexpr int NTH = DENSE_THREADS;
 
@@ -1111,12 +1118,10 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   load_bf16_tile128<NTH>(B2, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
   load_tile64<NTH>(sT, pb + PB_T, tid);
   if (tid < CH) {
-    float b = 0.0f;
-    if (tid < L.len) {
-      const float braw = bf2f(beta[(size_t)(L.row0 + tid) * Hv + h]);
-      b = (flags & KDA_FLAG_BETA_IS_PROB) ? braw : sigm(braw);
-    }
-    sB[tid] = b;
+    const __amdgpu_buffer_rsrc_t bb = buffer_rsrc(beta + (size_t)L.row0 * Hv + h, (uint32_t)L.len * Hv * 2);
+    const float braw = bf2f((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(bb, (uint32_t)(tid * Hv) * 2, 0, 0));
+    const float bp = (flags & KDA_FLAG_BETA_IS_PROB) ? braw : sigm(braw);
+    sB[tid] = tid < L.len ? bp : 0.0f;
   }
   __syncthreads();
   // 6. dM = dU V^T + dW Kg^T;  dV = M^T dU;  dKg = M^T dW  (M = T diag(b))
@@ -1250,17 +1255,23 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
   // wave (w, half): row block w = wave & 3, channel columns 16 (nb + n) + li,
   // n < 4, nb = 4 (wave >> 2)
-  const int lane = tid & 63, wave = tid >> 6, w = wave & 3, half = wave >> 2, nb = 4 * half;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), w = wave & 3, half = wave >> 2, nb = 4 * half;
   const int li = lane & 15, lg = lane >> 4;
   const int rbase = 16 * w + 4 * lg;  // own rows rbase + r
   // the raw gate inputs of the gate phase, loaded now so their latency hides
   // behind the pairwise sums (bf16 bits; zero past the chunk's end)
+  // (range-checked buffer loads: a conditional load was compiled into a
+  // branch that waited for each load in turn)
   uint16_t graw[4][4];
+  {
+    const __amdgpu_buffer_rsrc_t bg = buffer_rsrc(g + ((size_t)L.row0 * Hv + h) * DK, (uint32_t)L.len * Hv * DK * 2);
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
-      graw[n][r] = rbase + r < L.len ? g[((size_t)(L.row0 + rbase + r) * Hv + h) * DK + 16 * (nb + n) + li] : (uint16_t)0;
+      for (int n = 0; n < 4; ++n)
+        graw[n][r] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
+            bg, (uint32_t)((rbase + r) * Hv * DK + 16 * (nb + n) + li) * 2, 0, 0);
+  }
   float Ko[4][4], Qo[4][4], Go[4][4];
 #pragma unroll
   for (int n = 0; n < 4; ++n)

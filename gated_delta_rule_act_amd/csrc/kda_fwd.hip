@@ -43,6 +43,7 @@
 #include <type_traits>
 
 #include "kda.h"
+#include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_segment.h"
 
@@ -55,6 +56,7 @@ static __device__ __align__(256) uint8_t scratch[KDA_NOALLOC_SCRATCH_BYTES];
 namespace {
 using namespace kda_internal;
 using namespace kda_segment;
+using namespace kda_device;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -118,22 +120,6 @@ static_assert(BLOCK % 256 == 0, "workspace block alignment");
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Raw buffer resource over [base, base + bytes): loads beyond the range return
-// zero and stores beyond it are dropped by the hardware range check, so tail
-// rows need no branches (and no branch-dependent wait counts).
-// Every caller passes workgroup-uniform values; they are read from the first
-// lane so the descriptor is built in scalar registers even where a uniform
-// value was computed by a vector instruction (a clamp has no scalar form), as
-// a descriptor in vector registers turns each load into a loop over lanes.
-constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer descriptor
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((int)b);
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(bu), (short)0,
-                                           __builtin_amdgcn_readfirstlane((int)bytes), kBufferWord3);
-}
 
 // One 1 KB workspace fragment from a wave (16 bytes per lane).  Non-temporal:
 // the workspace is written once and read by the next launch; the state
