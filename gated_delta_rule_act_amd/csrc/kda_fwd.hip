@@ -27,9 +27,10 @@
 //
 // Precision: 16-bit MFMA operands with fp32 accumulation.  The contraction
 // that writes the state (U^T Kd) uses a 3-product hi/lo split (U and Kd in
-// fp16 hi/lo, the low part of Kd kept in e4m3 with a 2^15 scale), T diag(b)
+// fp16 hi/lo, the low part of Kd kept in e4m3 with a 2^18 scale), T diag(b)
 // enters U as bf16 hi/lo against exact bf16 V, the midpoint diagonal blocks
-// (factors up to 2^58) run on the fp32 MFMA, and T is computed in fp32.  The
+// (factors up to 2^58) take both sides as bf16 hi/lo (three products), and T
+// is computed in fp32.  The
 // exp2 operands are always differences of Gamma values, never ratios of
 // exponentials.
 #include <hip/hip_runtime.h>
@@ -663,14 +664,29 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         *reinterpret_cast<half8*>(sX + ((pair * 4 + kb) * 64 + lane) * 16) = to_half8(b);
       }
       if (MODE == KDA_GATE_SAFE_SIGMOID) {
-        // diagonal block on the fp32 MFMA, both sides offset by the midpoint;
-        // four independent accumulators per product keep the chain short
+        // diagonal block, both sides offset by the midpoint.  The factors span
+        // up to 2^+-58, within bf16's exponent range but not fp16's: each
+        // operand is split into bf16 hi + lo, and three products (hi hi, hi
+        // lo, lo hi) on the bf16 MFMA give the block to about 2^-16 of its
+        // terms, for an eighth of the fp32 MFMA's issue time.  One
+        // accumulator per channel block keeps the chains short.
+        bf16x8 ah, al, qh, ql, bh, bl;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float db = kC[e] * vMc[c0 + e];
-          dkkp[e & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(kR[e] * vMr[c0 + e], db, dkkp[e & 3], 0, 0, 0);
-          dqkp[e & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(qR[e] * vMr[c0 + e], db, dqkp[e & 3], 0, 0, 0);
+          const float a = kR[e] * vMr[c0 + e], aq = qR[e] * vMr[c0 + e], b = kC[e] * vMc[c0 + e];
+          ah[e] = (__bf16)a;
+          al[e] = (__bf16)(a - (float)ah[e]);
+          qh[e] = (__bf16)aq;
+          ql[e] = (__bf16)(aq - (float)qh[e]);
+          bh[e] = (__bf16)b;
+          bl[e] = (__bf16)(b - (float)bh[e]);
         }
+        dkkp[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, dkkp[kb], 0, 0, 0);
+        dqkp[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, bh, dqkp[kb], 0, 0, 0);
+        dkkp[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, dkkp[kb], 0, 0, 0);
+        dqkp[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, bl, dqkp[kb], 0, 0, 0);
+        dkkp[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, dkkp[kb], 0, 0, 0);
+        dqkp[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, bh, dqkp[kb], 0, 0, 0);
       }
     }
   }
