@@ -293,6 +293,30 @@ __device__ __forceinline__ float dpp_row_shr(float x) {
 }
 
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Magnitudes are compared as the bit patterns of |x|: for non-negative floats
+// the unsigned integer order is the numeric order, and integer maxima need
+// none of the NaN canonicalisation a float maximum of loaded values does.
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __builtin_bit_cast(uint32_t, x) & 0x7fffffffu; }
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t x) {
+  // lanes outside ROWS, and lanes with no source, keep their own value
+  return max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, ROWS, 0xf, false));
+}
+
+// Largest value over a wave (as |x| bit patterns): row maxima by DPP shifts,
+// then rows 0+1 and 2+3 and all four by row broadcasts; lane 63 holds it.
+__device__ __forceinline__ uint32_t wave_max_bits(uint32_t x) {
+  x = dpp_max_u32<0x111, 0xf>(x);  // row_shr:1
+  x = dpp_max_u32<0x112, 0xf>(x);  // row_shr:2
+  x = dpp_max_u32<0x114, 0xf>(x);  // row_shr:4
+  x = dpp_max_u32<0x118, 0xf>(x);  // row_shr:8: lane 15 of each row holds its row
+  x = dpp_max_u32<0x142, 0xa>(x);  // row_bcast:15 into rows 1, 3
+  x = dpp_max_u32<0x143, 0xc>(x);  // row_bcast:31 into rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // log2-domain gate activation of x = g + dt_bias (A_exp = exp(A_log)); with a
@@ -527,13 +551,28 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
   }
-  // safe gate: four partial accumulators of the diagonal block; unbounded
-  // decays: one accumulator per level of the diagonal block
+  // The diagonal block: through the sub-chunk midpoint (phase 3) when the
+  // sub-chunk's decay spans at most 2^100 in every channel, so that every
+  // offset factor times a q or k element (below 2^15) is a normal bf16 --
+  // always with the safe gate, whose decay per token is bounded (a span of
+  // at most 2^58) -- else by binary levels (below).  G is non-increasing down
+  // the rows, so its largest size is the sub-chunk total.
+  bool mid_ok = true;
+  if constexpr (MODE != KDA_GATE_SAFE_SIGMOID) {
+    float mg = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mg = fmaxf(mg, -G[kb][e]);
+    mid_ok = (int)wave_max_bits(abs_bits(mg)) <= __builtin_bit_cast(int, 100.0f);
+  }
+  // four partial accumulators of the diagonal block (midpoint form), or one
+  // per level (level form)
   f32x4 dkkp[4], dqkp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) { dkkp[j] = f32x4{0, 0, 0, 0}; dqkp[j] = f32x4{0, 0, 0, 0}; }
   float qkd = 0.0f;
-  if constexpr (MODE != KDA_GATE_SAFE_SIGMOID) {
+  if (MODE != KDA_GATE_SAFE_SIGMOID && !mid_ok) {
     // diagonal block by levels (see diag_level); its diagonal is q_i . k_i
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -553,7 +592,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if constexpr (MODE != KDA_GATE_SAFE_SIGMOID) {
+  if (MODE != KDA_GATE_SAFE_SIGMOID && !mid_ok) {
     qkd += __shfl_xor(qkd, 16);
     qkd += __shfl_xor(qkd, 32);
     if (lg == 0) sQd[r] = qkd;
@@ -663,7 +702,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
         *reinterpret_cast<half8*>(sX + ((pair * 4 + kb) * 64 + lane) * 16) = to_half8(b);
       }
-      if (MODE == KDA_GATE_SAFE_SIGMOID) {
+      if (mid_ok) {
         // diagonal block, both sides offset by the midpoint.  The factors span
         // up to 2^+-58, within bf16's exponent range but not fp16's: each
         // operand is split into bf16 hi + lo, and three products (hi hi, hi
@@ -690,7 +729,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
   }
-  if (MODE == KDA_GATE_SAFE_SIGMOID) {
+  if (mid_ok) {
     dkk = (dkkp[0] + dkkp[1]) + (dkkp[2] + dkkp[3]);
     dqk = (dqkp[0] + dqkp[1]) + (dqkp[2] + dqkp[3]);
   }
@@ -709,7 +748,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         oqk[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aQ[kb], b, oqk[J], 0, 0, 0);
       }
     }
-    if (MODE != KDA_GATE_SAFE_SIGMOID) {
+    if (MODE != KDA_GATE_SAFE_SIGMOID && !mid_ok) {
       // pair (i, j), i > j, of the diagonal block belongs to the level of the
       // highest bit in which i and j differ
 #pragma unroll
@@ -1092,29 +1131,6 @@ __device__ __forceinline__ void settle(const ChunkRegs& r) {
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int b = 0; b < 2; ++b) { settle(r.kd[j][b]); settle(r.kdl[j][b]); }
-}
-
-// Magnitudes are compared as the bit patterns of |x|: for non-negative floats
-// the unsigned integer order is the numeric order, and integer maxima need
-// none of the NaN canonicalisation a float maximum of loaded values does.
-__device__ __forceinline__ uint32_t abs_bits(float x) { return __builtin_bit_cast(uint32_t, x) & 0x7fffffffu; }
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t x) {
-  // lanes outside ROWS, and lanes with no source, keep their own value
-  return max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, ROWS, 0xf, false));
-}
-
-// Largest value over a wave (as |x| bit patterns): row maxima by DPP shifts,
-// then rows 0+1 and 2+3 and all four by row broadcasts; lane 63 holds it.
-__device__ __forceinline__ uint32_t wave_max_bits(uint32_t x) {
-  x = dpp_max_u32<0x111, 0xf>(x);  // row_shr:1
-  x = dpp_max_u32<0x112, 0xf>(x);  // row_shr:2
-  x = dpp_max_u32<0x114, 0xf>(x);  // row_shr:4
-  x = dpp_max_u32<0x118, 0xf>(x);  // row_shr:8: lane 15 of each row holds its row
-  x = dpp_max_u32<0x142, 0xa>(x);  // row_bcast:15 into rows 1, 3
-  x = dpp_max_u32<0x143, 0xc>(x);  // row_bcast:31 into rows 2, 3
-  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // largest |value| of eight bf16 values packed in four dwords, as the bit
