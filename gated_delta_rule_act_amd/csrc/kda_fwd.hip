@@ -1163,6 +1163,26 @@ __device__ __forceinline__ int scale_shift(const uint32_t* sMx, int E) {
   return min(max(E + d, -kMaxExp), kMaxExp) - E;
 }
 
+// ub tile vt = T diag(b) V (real units) of token tile w, from a chunk's
+// T diag(b) fragments in `r` and its V slice in LDS at sVb
+template <int KIND, int NVT>
+__device__ __forceinline__ void ub_one(f32x4& u, const _Float16* sVb, const ChunkRegs& r, int vt, int lane) {
+  u = f32x4{0, 0, 0, 0};
+  if constexpr (KIND != ST_TRANS) {
+    const bf16x8 vb0 = __builtin_bit_cast(bf16x8, lds_frag_tr_grouped(sVb, svs<NVT>(), svg<NVT>(), 0, 16 * vt, lane));
+    const bf16x8 vb1 = __builtin_bit_cast(bf16x8, lds_frag_tr_grouped(sVb, svs<NVT>(), svg<NVT>(), 32, 16 * vt, lane));
+    u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.tbh[0]), vb0, u, 0, 0, 0);
+    u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.tbl[0]), vb0, u, 0, 0, 0);
+    u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.tbh[1]), vb1, u, 0, 0, 0);
+    u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.tbl[1]), vb1, u, 0, 0, 0);
+  }
+}
+template <int KIND, int NVT>
+__device__ __forceinline__ void ub_tile(f32x4 (&u)[NVT], const _Float16* sVb, const ChunkRegs& r, int lane) {
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt) ub_one<KIND, NVT>(u[vt], sVb, r, vt, lane);
+}
+
 // One chunk of the state chain: `cur` holds chunk c, `n1` receives the key-tile
 // operands of chunk c+1, `n2` the token-tile operands of chunk c+2.  The wide
 // slices (NVT = 4) have no registers for that depth: their token-tile
@@ -1172,30 +1192,20 @@ __device__ __forceinline__ int scale_shift(const uint32_t* sMx, int E) {
 // units; on exit S holds S_(c+1), E = E_(c+1) and mu the largest |U_c|.
 template <int KIND, int NVT>
 __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT], ChunkRegs& cur, ChunkRegs& n1,
-                                            ChunkRegs& n2, const int c, PendingOut<NVT>& pd, int& E, uint32_t& mu) {
+                                            ChunkRegs& n2, const int c, PendingOut<NVT>& pd, int& E, uint32_t& mu,
+                                            f32x4 (&ub)[NVT]) {
   // no fused multiply-adds the source does not spell out: each instantiation
   // then rounds every element the same way, whatever its schedule
 #pragma clang fp contract(off)
   const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
   const int64_t row0 = x.bos + (int64_t)c * CH;
   typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-  // 0. Ub = T diag(b) V_c of token tile w (real units), from the V slice the
+  // 0. ub = T diag(b) V_c of token tile w (real units), from the V slice the
   //    previous chunk step put in LDS, so that its magnitude can set the
-  //    scale of U_c below
-  _Float16* const sVc = x.sV + (c & 1) * SV_HALFS<NVT>;
-  f32x4 ub[NVT];
-#pragma unroll
-  for (int vt = 0; vt < NVT; ++vt) {
-    ub[vt] = f32x4{0, 0, 0, 0};
-    if constexpr (KIND != ST_TRANS) {
-      const bf16x8 vb0 = __builtin_bit_cast(bf16x8, lds_frag_tr_grouped(sVc, svs<NVT>(), svg<NVT>(), 0, 16 * vt, lane));
-      const bf16x8 vb1 = __builtin_bit_cast(bf16x8, lds_frag_tr_grouped(sVc, svs<NVT>(), svg<NVT>(), 32, 16 * vt, lane));
-      ub[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[0]), vb0, ub[vt], 0, 0, 0);
-      ub[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[0]), vb0, ub[vt], 0, 0, 0);
-      ub[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbh[1]), vb1, ub[vt], 0, 0, 0);
-      ub[vt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.tbl[1]), vb1, ub[vt], 0, 0, 0);
-    }
-  }
+  //    scale of U_c below.  The narrow slices formed it in the previous
+  //    chunk step already (their T diag(b) of chunk c+1 is in registers one
+  //    chunk early), between the barriers where it fills MFMA idle cycles.
+  if constexpr (NVT != NVT_NARROW) ub_tile<KIND, NVT>(ub, x.sV + (c & 1) * SV_HALFS<NVT>, cur, lane);
   // 1. publish the chunk's vectors, the next chunk's V slice and the current
   //    state, and this wave's largest magnitude of S_c, U_(c-1) and Ub.
   //    Every reader of these buffers in the previous chunk was before its B2
@@ -1250,9 +1260,11 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
   const float scn = pow2f(-En), sf = x.scale * f;
   const f32x4 gn0 = *reinterpret_cast<const f32x4*>(x.sVec + 32 * wave + 4 * lg) * f;
   const f32x4 gn1 = *reinterpret_cast<const f32x4*>(x.sVec + 32 * wave + 16 + 4 * lg) * f;
-  f32x4 U[NVT], O[NVT];
+  f32x4 U[NVT], O[NVT], ubn[NVT];
 #pragma unroll
   for (int vt = 0; vt < NVT; ++vt) {
+    // the next chunk's ub (narrow slices): its V slice went to LDS before B1
+    if constexpr (NVT == NVT_NARROW) ub_one<KIND, NVT>(ubn[vt], x.sV + ((c + 1) & 1) * SV_HALFS<NVT>, n1, vt, lane);
     half8 sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
@@ -1368,6 +1380,9 @@ __device__ __forceinline__ void state_chunk(const StateCtx& x, f32x4 (&S)[2][NVT
   }
   E = En;
   mu = abs_bits(mu_n);
+  if constexpr (NVT == NVT_NARROW)
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt) ub[vt] = ubn[vt];
 }
 
 // One workgroup per (job, V slice).  A job is a whole chain (nseg == 1) or one
@@ -1510,6 +1525,9 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
         for (int rr = 0; rr < 4; ++rr) S[j][vt][rr] = __builtin_amdgcn_ldexpf(S[j][vt][rr], -E);
   }
   __syncthreads();
+  // the first chunk's ub (the narrow slices carry it from one chunk step to the next)
+  f32x4 ub[NVT];
+  if (NVT == NVT_NARROW && nc > 0) ub_tile<KIND, NVT>(ub, sV, rA, lane);
   uint32_t mu = 0;  // no U before the first chunk
   PendingOut<NVT> pd;
   pd.row0 = bos;
@@ -1517,18 +1535,18 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
   int c = 0;
   if constexpr (NVT == NVT_NARROW) {
     for (; c + 3 <= nc; c += 3) {
-      state_chunk<KIND, NVT>(ctx, S, rA, rB, rC, c, pd, E, mu);
-      state_chunk<KIND, NVT>(ctx, S, rB, rC, rA, c + 1, pd, E, mu);
-      state_chunk<KIND, NVT>(ctx, S, rC, rA, rB, c + 2, pd, E, mu);
+      state_chunk<KIND, NVT>(ctx, S, rA, rB, rC, c, pd, E, mu, ub);
+      state_chunk<KIND, NVT>(ctx, S, rB, rC, rA, c + 1, pd, E, mu, ub);
+      state_chunk<KIND, NVT>(ctx, S, rC, rA, rB, c + 2, pd, E, mu, ub);
     }
-    if (c < nc) state_chunk<KIND, NVT>(ctx, S, rA, rB, rC, c, pd, E, mu);
-    if (c + 1 < nc) state_chunk<KIND, NVT>(ctx, S, rB, rC, rA, c + 1, pd, E, mu);
+    if (c < nc) state_chunk<KIND, NVT>(ctx, S, rA, rB, rC, c, pd, E, mu, ub);
+    if (c + 1 < nc) state_chunk<KIND, NVT>(ctx, S, rB, rC, rA, c + 1, pd, E, mu, ub);
   } else {
     for (; c + 2 <= nc; c += 2) {
-      state_chunk<KIND, NVT>(ctx, S, rA, rB, rB, c, pd, E, mu);
-      state_chunk<KIND, NVT>(ctx, S, rB, rA, rA, c + 1, pd, E, mu);
+      state_chunk<KIND, NVT>(ctx, S, rA, rB, rB, c, pd, E, mu, ub);
+      state_chunk<KIND, NVT>(ctx, S, rB, rA, rA, c + 1, pd, E, mu, ub);
     }
-    if (c < nc) state_chunk<KIND, NVT>(ctx, S, rA, rB, rB, c, pd, E, mu);
+    if (c < nc) state_chunk<KIND, NVT>(ctx, S, rA, rB, rB, c, pd, E, mu, ub);
   }
   if constexpr (KIND == ST_FULL) store_pending(pd, out, Hv, h, v0, wave, li, lg);
   // back to the state's own units
