@@ -301,8 +301,10 @@ __device__ __forceinline__ uint32_t abs_bits(float x) { return __builtin_bit_cas
 
 template <int CTRL, int ROWS>
 __device__ __forceinline__ uint32_t dpp_max_u32(uint32_t x) {
-  // lanes outside ROWS, and lanes with no source, keep their own value
-  return max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, ROWS, 0xf, false));
+  // lanes outside ROWS, and lanes with no source, take 0 (the identity of an
+  // unsigned maximum) and so keep their own value; with that identity the
+  // compiler fuses the move into the maximum (one DPP instruction per step)
+  return max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xf, true));
 }
 
 // Largest value over a wave (as |x| bit patterns): row maxima by DPP shifts,
