@@ -244,11 +244,13 @@ __device__ __forceinline__ bool chunk_pos(int x, int B, int T, int N, const int6
 //     D_IJ = 2^(Gamma_p(I) - Gamma_e(J)), I >= J + 2 (off-diagonal columns)
 //     Mr_I = 2^(Gamma_p - Gamma_m), Mc_I = 2^(Gamma_m - Gamma_e), m = 16I + 8
 // Off-diagonal block (I, J < I): rows qR, kR against columns kC D_IJ -- all
-// factors <= 1, fp16 MFMA.  Diagonal block, safe gate: rows kR Mr against
+// factors <= 1, fp16 MFMA (kC is posted once in fp16; the reader multiplies
+// it by D_IJ, also in fp16).  Diagonal block, safe gate: rows kR Mr against
 // columns kC Mc, i.e. both sides offset by the sub-chunk midpoint, with
-// exponents within 8 * |lower_bound| * log2(e) of zero (at most 2^58), on the
-// fp32 MFMA.  Diagonal block, unbounded decays (softplus gate, pre-gated
-// decay): split into binary levels, one fp16 product per level (diag_level).
+// exponents within 8 * |lower_bound| * log2(e) of zero (at most 2^58), as
+// bf16 hi/lo products.  Diagonal block, unbounded decays (softplus gate,
+// pre-gated decay): the same midpoint form where a sub-chunk's decay span
+// allows it, else binary levels, one fp16 product per level (diag_level).
 constexpr int AS = 68;      // fp32 row stride of Akk / T
 constexpr int AQS = 72;     // fp16 row stride of Aqk
 constexpr int KER = 144;    // fp16 row stride of the row-major [t][k] K . 2^G and Kd tiles
@@ -261,29 +263,29 @@ constexpr int KEG = 8 * KER + 64;  // group stride of the K . 2^G / Kd tiles
 constexpr int WG8 = 8 * WTS + 64;  // group stride of the W staging tile
 __device__ __forceinline__ int ke_row(int t) { return (t & 7) * KER + (t >> 3) * KEG; }
 __device__ __forceinline__ int w_row(int k) { return (k & 7) * WTS + (k >> 3) * WG8; }
-constexpr int NVEC = 19;    // per-channel vectors: P0..3, L0..3, D20, D30, D31, Mr0..3, Mc0..3
-constexpr int V_P = 0, V_L = 4, V_D20 = 8, V_D30 = 9, V_D31 = 10, V_MR = 11, V_MC = 15;
+constexpr int NVEC = 16;    // per-channel fp32 vectors: P0..3, L0..3, Mr0..3, Mc0..3
+constexpr int V_P = 0, V_L = 4, V_MR = 8, V_MC = 12;
+constexpr int NDH = 4;      // per-channel fp16 vectors D20, D30, D31 and ones (read by the off-diagonal blocks)
 
 // LDS plan (bytes).  Region X is reused: mailbox (phases 3-4), Kd staging
 // (phase 4b), then Akk fp32 / W staging (phases 5-7).  Region T holds the
-// sub-chunk totals, midpoints and per-channel vectors until phase 3, then T.
-constexpr int MB_BYTES = 6 * 4 * 64 * 16;               // 6 (I,J) pairs x 4 k-blocks x 64 lanes x 16 B
-constexpr int X_BYTES = MB_BYTES;
+// sub-chunk totals, midpoints and per-channel vectors until phase 4, then T.
+constexpr int MB_BYTES = 3 * 4 * 64 * 16;               // column sub-chunks J = 0..2 x 4 k-blocks x 64 lanes x 16 B
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int X_BYTES = cmax(cmax(MB_BYTES, 64 * AS * 4), cmax(16 * WG8 * 2, 8 * KEG * 2));
 constexpr int L_X = 0;
 constexpr int L_T = L_X + X_BYTES;
 constexpr int T_BYTES = 64 * AS * 4;
 constexpr int L_TOT = L_T;                              // [4][128] f32, inside region T
 constexpr int L_MID = L_TOT + 4 * 128 * 4;              // [4][128] f32
 constexpr int L_VEC = L_MID + 4 * 128 * 4;              // [NVEC][128] f32
+constexpr int L_DH = L_VEC + NVEC * 128 * 4;            // [NDH][128] fp16
 constexpr int L_KE = L_T + T_BYTES;
 constexpr int L_AQ = L_KE + 8 * KEG * 2;
 constexpr int L_BETA = L_AQ + 64 * AQS * 2;
 constexpr int L_QD = L_BETA + 64 * 4;  // unbounded decays: q_i . k_i per row [64] f32
 constexpr int L_END = L_QD + 64 * 4;
-static_assert(L_VEC + NVEC * 128 * 4 <= L_T + T_BYTES, "vectors fit in region T");
-static_assert(64 * AS * 4 <= X_BYTES, "Akk fits in region X");
-static_assert(16 * WG8 * 2 <= X_BYTES, "W staging fits in region X");
-static_assert(8 * KEG * 2 <= X_BYTES, "Kd staging fits in region X");
+static_assert(L_DH + NDH * 128 * 2 <= L_T + T_BYTES, "vectors fit in region T");
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_row_shr(float x) {
@@ -439,6 +441,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   float* sTot = reinterpret_cast<float*>(smem + L_TOT);
   float* sMid = reinterpret_cast<float*>(smem + L_MID);
   float* sVec = reinterpret_cast<float*>(smem + L_VEC);
+  _Float16* sDh = reinterpret_cast<_Float16*>(smem + L_DH);
   float* sBeta = reinterpret_cast<float*>(smem + L_BETA);
   float* sQd = reinterpret_cast<float*>(smem + L_QD);
 
@@ -615,9 +618,10 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       sVec[(V_P + 2) * 128 + c] = fast_exp2(T0 + T1);
       sVec[(V_P + 3) * 128 + c] = fast_exp2((T0 + T1) + T2);
       reinterpret_cast<float*>(blk + F_VEC * FRAG)[c] = fast_exp2(((T0 + T1) + T2) + T3);
-      sVec[V_D20 * 128 + c] = fast_exp2(T1);
-      sVec[V_D30 * 128 + c] = fast_exp2(T1 + T2);
-      sVec[V_D31 * 128 + c] = fast_exp2(T2);
+      sDh[0 * 128 + c] = (_Float16)fast_exp2(T1);
+      sDh[1 * 128 + c] = (_Float16)fast_exp2(T1 + T2);
+      sDh[2 * 128 + c] = (_Float16)fast_exp2(T2);
+      sDh[3 * 128 + c] = (_Float16)1.0f;  // adjacent sub-chunks: no factor
     } else {
       sVec[(V_L + 0) * 128 + c] = fast_exp2((T1 + T2) + T3);
       sVec[(V_L + 1) * 128 + c] = fast_exp2(T2 + T3);
@@ -689,21 +693,10 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         kdh[kb][e] = hh;
         kdl[kb][e] = (_Float16)__builtin_amdgcn_fmed3f((kd - (float)hh) * kKdLoScale, -kE4m3Max, kE4m3Max);
       }
-#pragma unroll
-      for (int Ip = 1; Ip < 4; ++Ip) {
-        if (Ip <= I) continue;
-        const int pair = (Ip * (Ip - 1)) / 2 + I;  // (1,0)=0 (2,0)=1 (2,1)=2 (3,0)=3 (3,1)=4 (3,2)=5
-        float b[8];
-        if (Ip == I + 1) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) b[e] = kC[e];
-        } else {
-          const float* vD = sVec + (Ip == 2 ? V_D20 : (I == 0 ? V_D30 : V_D31)) * 128;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) b[e] = kC[e] * vD[c0 + e];
-        }
-        *reinterpret_cast<half8*>(sX + ((pair * 4 + kb) * 64 + lane) * 16) = to_half8(b);
-      }
+      // the column operand of the off-diagonal blocks (I', I), I' > I; the
+      // blocks with I' >= I + 2 scale it by D_(I'I) as they read it, so every
+      // posting wave does the same work
+      if (I < 3) *reinterpret_cast<half8*>(sX + ((I * 4 + kb) * 64 + lane) * 16) = to_half8(kC);
       if (mid_ok) {
         // diagonal block, both sides offset by the midpoint.  The factors span
         // up to 2^+-58, within bf16's exponent range but not fp16's: each
@@ -742,10 +735,17 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int J = 0; J < 3; ++J) {
       if (J >= I) continue;
-      const int pair = (I * (I - 1)) / 2 + J;
+      // D_IJ in fp16 (D20, D30, D31; ones for I = J + 1): every block
+      // multiplies, so no branch separates the reads from their use
+      const _Float16* dh = sDh + (I == J + 1 ? 3 : I == 2 ? 0 : J == 0 ? 1 : 2) * 128;
+      half8 bs[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        bs[kb] = *reinterpret_cast<const half8*>(sX + ((J * 4 + kb) * 64 + lane) * 16) *
+                 *reinterpret_cast<const half8*>(dh + 32 * kb + 8 * lg);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const half8 b = *reinterpret_cast<const half8*>(sX + ((pair * 4 + kb) * 64 + lane) * 16);
+        const half8 b = bs[kb];
         okk[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aK[kb], b, okk[J], 0, 0, 0);
         oqk[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aQ[kb], b, oqk[J], 0, 0, 0);
       }
