@@ -485,42 +485,58 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   load_chunk_inputs<MODE, PREP_THREADS>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, lb,
                           flags, tid, nullptr, nullptr);
 
-  // Akk and Aqk.  Waves 0..3 sum the diagonal block w pair by pair; waves
-  // 4..7 form the off-diagonal blocks (I, J), J < I, two, two, one and one
-  // each.  An off-diagonal block factors through the row before block I:
+  // Akk and Aqk.  Each off-diagonal block (I, J), J < I, is formed in two
+  // halves over the channels, twelve tasks in all; waves 0..3 also sum the
+  // diagonal block w.  With the safe gate a diagonal block costs about half
+  // an off-diagonal one, so waves 0..3 take one half-block each and waves
+  // 4..7 two; with unbounded decays the pairwise diagonal is the heavy part,
+  // and waves 4..7 take three half-blocks each.  Waves w and w + 4 share a
+  // SIMD, so either way every SIMD gets about the same work.  An off-diagonal
+  // block factors through the row before block I:
   // e^(G_i - G_j) = e^(sG_i) e^(Bt_J - sG_j + sum_{J<B<I} Bt_B), both
   // exponents <= 0, so it is one fp32 MFMA product over the channels (A = K
-  // or Q times the row factor, B = K times the column factor).
+  // or Q times the row factor, B = K times the column factor).  The first
+  // half goes to sA / sAq, the second to sT (Akk part below the diagonal,
+  // Aqk part transposed above it, both unused until the solve), and waves
+  // 4..7 add the two while waves 0..3 solve the diagonal blocks.
   {
     // (the wave index through readfirstlane: the compiler then knows it is
     // uniform, and tests and loops on it are scalar branches, not exec masks)
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), li = lane & 15, lg = lane >> 4;
-    if (w >= 4) {
-      const int u = w - 4;
-      const int ntask = u < 2 ? 2 : 1;
-      for (int task = 0; task < ntask; ++task) {
-        // (1,0) (2,0) | (2,1) (3,0) | (3,1) | (3,2)
-        const int I = u == 0 ? 1 + task : u == 1 ? 2 + task : 3;
-        const int J = u == 0 ? 0 : u == 1 ? 1 - task : u - 1;
-        f32x4 akk = f32x4{0.f, 0.f, 0.f, 0.f}, aqk = akk;
-        const int i = 16 * I + li, j = 16 * J + li;
+    constexpr bool kSafe = MODE == KDA_GATE_SAFE_SIGMOID;
+    const int t0 = kSafe ? (w < 4 ? w : 4 + 2 * (w - 4)) : 3 * (w - 4);
+    const int ntask = kSafe ? (w < 4 ? 1 : 2) : (w < 4 ? 0 : 3);
+    for (int task = t0; task < t0 + ntask; ++task) {
+      // blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2), two channel halves each
+      const int blk = task >> 1, hc = task & 1;
+      const int I = blk == 0 ? 1 : blk < 3 ? 2 : 3;
+      const int J = blk == 0 ? 0 : blk < 3 ? blk - 1 : blk - 3;
+      f32x4 akk = f32x4{0.f, 0.f, 0.f, 0.f}, aqk = akk;
+      const int i = 16 * I + li, j = 16 * J + li;
 #pragma unroll 4
-        for (int kc = 0; kc < DK; kc += 4) {
-          const int c = kc + lg;
-          const float fr = ex2(sG[i * RS + c]);
-          float mid = sBt[J * DK + c];
-          for (int B = J + 1; B < I; ++B) mid += sBt[B * DK + c];
-          const float zb = sK[j * RS + c] * ex2(mid - sG[j * RS + c]);
-          akk = __builtin_amdgcn_mfma_f32_16x16x4f32(sK[i * RS + c] * fr, zb, akk, 0, 0, 0);
-          aqk = __builtin_amdgcn_mfma_f32_16x16x4f32(sQ[i * RS + c] * fr, zb, aqk, 0, 0, 0);
-        }
+      for (int kc = 64 * hc; kc < 64 * hc + 64; kc += 4) {
+        const int c = kc + lg;
+        const float fr = ex2(sG[i * RS + c]);
+        float mid = sBt[J * DK + c];
+        for (int B = J + 1; B < I; ++B) mid += sBt[B * DK + c];
+        const float zb = sK[j * RS + c] * ex2(mid - sG[j * RS + c]);
+        akk = __builtin_amdgcn_mfma_f32_16x16x4f32(sK[i * RS + c] * fr, zb, akk, 0, 0, 0);
+        aqk = __builtin_amdgcn_mfma_f32_16x16x4f32(sQ[i * RS + c] * fr, zb, aqk, 0, 0, 0);
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ii = 16 * I + 4 * lg + r, jj = 16 * J + li;
+      for (int r = 0; r < 4; ++r) {
+        const int ii = 16 * I + 4 * lg + r, jj = 16 * J + li;
+        if (hc == 0) {
           sA[ii * QS + jj] = sB[ii] * akk[r];
           sAq[ii * QS + jj] = scale * aqk[r];
+        } else {
+          sT[ii * QS + jj] = sB[ii] * akk[r];
+          sT[jj * QS + ii] = scale * aqk[r];
         }
       }
+    }
+    if (w >= 4) {
+      // waves 4..7: off-diagonal half-blocks only
     } else if constexpr (MODE == KDA_GATE_SAFE_SIGMOID) {
       // diagonal block, bounded decay: e^(G_i - G_j) = e^(sG_i - sG_m) e^(sG_m - sG_j)
       // with m the block's row 8, each factor within 2^(8 |lb| log2 e) of one:
@@ -574,6 +590,20 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // substitution (one wave each, lane = column), then block rows 1..3
   {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    if (w >= 4) {
+      // the second channel halves of the off-diagonal blocks, out of sT
+      const int e = tid - 256;
+#pragma unroll
+      for (int blk = 0; blk < 6; ++blk) {
+        const int I = blk == 0 ? 1 : blk < 3 ? 2 : 3;
+        const int J = blk == 0 ? 0 : blk < 3 ? blk - 1 : blk - 3;
+        const int ii = 16 * I + (e >> 4), jj = 16 * J + (e & 15);
+        sA[ii * QS + jj] += sT[ii * QS + jj];
+        sAq[ii * QS + jj] += sT[jj * QS + ii];
+        sT[ii * QS + jj] = 0.0f;
+        sT[jj * QS + ii] = 0.0f;
+      }
+    }
     if (w < 4 && lane < 16) {
       // the lane's column of the block stays in registers (zero above the
       // diagonal: those rows only ever subtract products with zeros)
