@@ -1430,6 +1430,18 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       for (int r = 0; r < 4; ++r) Cc[n][r] += X[n][r] * ex2(mid - Go[n][r]);
     }
   }
+  // the workspace gradients of the elementwise factors, issued here so their
+  // latency hides behind the column-side products
+  float eq[4][4], egk[4][4], ed4[4][4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int o = (rbase + r) * DK + 16 * (nb + n) + li;
+      eq[n][r] = gb[GB_DQG + o];
+      egk[n][r] = gb[GB_DKG + o];
+      ed4[n][r] = gb[GB_DKD + o];
+    }
   if constexpr (MODE == KDA_GATE_SAFE_SIGMOID) {
     // diagonal block through the midpoint, as on the row side
     f32x4 X[4];
@@ -1484,17 +1496,27 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 
   // ---- elementwise factors: Qg = scale Q e^G, Kg = K e^G, Kd = K e^(G_last - G), gn = e^G_last
-  float colKd[4];
-#pragma unroll
-  for (int n = 0; n < 4; ++n) colKd[n] = 0.0f;
+  // The own rows all lie in block w, so the block totals before it (Pa) and
+  // from it on (Pt) are per channel: G_abs = Go + Pa, G_last - G_abs = Pt - Go.
+  float colKd[4], Pa[4], Pt[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int c = 16 * (nb + n) + li;
+    float a = 0.0f, t = 0.0f;
+    for (int B = 0; B < 4; ++B) {
+      const float bt = sBt[B * DK + c];
+      if (B < w) a += bt; else t += bt;
+    }
+    Pa[n] = a;
+    Pt[n] = t;
+    colKd[n] = 0.0f;
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = rbase + r;
-      const float vq = gb[GB_DQG + row * DK + c], vg = gb[GB_DKG + row * DK + c], vd = gb[GB_DKD + row * DK + c];
-      const float eg = ex2(gabs(sG, sBt, row, c)), ed = ex2(gtail(sG, sBt, row, c));
+      const float vq = eq[n][r], vg = egk[n][r], vd = ed4[n][r];
+      const float eg = ex2(Go[n][r] + Pa[n]), ed = ex2(Pt[n] - Go[n][r]);
       dQ[n][r] += vq * eg;
       dK[n][r] += vg * eg + vd * ed;
       const float kd = vd * Ko[n][r] * ed;
