@@ -171,6 +171,28 @@ __device__ __forceinline__ void load_tile128(float* s, const float* g, int gs, i
     *reinterpret_cast<float4*>(s + r * RS + c) = *reinterpret_cast<const float4*>(g + (size_t)r * gs + c);
   }
 }
+// The same tile in two steps, so that the global loads can be issued ahead of
+// the products that run before the tile's LDS space is free: fetch into
+// registers, then put into LDS.  (Native vector types: with HIP's float4 and
+// uint4 classes the compiler keeps such arrays in scratch memory.)
+typedef float stage_f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t stage_u4 __attribute__((ext_vector_type(4)));
+template <int NTH>
+__device__ __forceinline__ void fetch_tile128(stage_f4 (&r4)[2048 / NTH], const float* g, int gs, int tid) {
+#pragma unroll
+  for (int i = 0; i < 2048 / NTH; ++i) {
+    const int e = tid + NTH * i, r = e >> 5, c = 4 * (e & 31);
+    r4[i] = *reinterpret_cast<const stage_f4*>(g + (size_t)r * gs + c);
+  }
+}
+template <int NTH>
+__device__ __forceinline__ void put_tile128(float* s, const stage_f4 (&r4)[2048 / NTH], int tid) {
+#pragma unroll
+  for (int i = 0; i < 2048 / NTH; ++i) {
+    const int e = tid + NTH * i, r = e >> 5, c = 4 * (e & 31);
+    *reinterpret_cast<stage_f4*>(s + r * RS + c) = r4[i];
+  }
+}
 // 64 x 64 fp32 global tile (dense, stride 64) -> LDS rows of stride QS.
 template <int NTH = 256>
 __device__ __forceinline__ void load_tile64(float* s, const float* g, int tid) {
@@ -178,6 +200,22 @@ __device__ __forceinline__ void load_tile64(float* s, const float* g, int tid) {
   for (int i = 0; i < 1024 / NTH; ++i) {
     const int e = tid + NTH * i, r = e >> 4, c = 4 * (e & 15);
     *reinterpret_cast<float4*>(s + r * QS + c) = *reinterpret_cast<const float4*>(g + r * 64 + c);
+  }
+}
+template <int NTH>
+__device__ __forceinline__ void fetch_tile64(stage_f4 (&r4)[1024 / NTH], const float* g, int tid) {
+#pragma unroll
+  for (int i = 0; i < 1024 / NTH; ++i) {
+    const int e = tid + NTH * i, r = e >> 4, c = 4 * (e & 15);
+    r4[i] = *reinterpret_cast<const stage_f4*>(g + r * 64 + c);
+  }
+}
+template <int NTH>
+__device__ __forceinline__ void put_tile64(float* s, const stage_f4 (&r4)[1024 / NTH], int tid) {
+#pragma unroll
+  for (int i = 0; i < 1024 / NTH; ++i) {
+    const int e = tid + NTH * i, r = e >> 4, c = 4 * (e & 15);
+    *reinterpret_cast<stage_f4*>(s + r * QS + c) = r4[i];
   }
 }
 // 64 rows x 128 bf16 (row stride gs elements; rows >= len read as zero) -> fp32 LDS.
@@ -190,6 +228,32 @@ __device__ __forceinline__ void load_bf16_tile128(float* s, const uint16_t* g, s
     const int e = tid + NTH * i, r = e >> 4, c = 8 * (e & 15);
     const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, (uint32_t)(r * gs + c) * 2, 0, 0));
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float* d = s + r * RS + c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      d[2 * q] = __uint_as_float(w[q] << 16);
+      d[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+  }
+}
+
+// the same in two steps (fetch the raw bf16 into registers, put into LDS)
+template <int NTH>
+__device__ __forceinline__ void fetch_bf16_tile128(stage_u4 (&u4)[1024 / NTH], const uint16_t* g, size_t gs, int len,
+                                                   int tid) {
+  const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g, (uint32_t)((size_t)len * gs * 2));
+#pragma unroll
+  for (int i = 0; i < 1024 / NTH; ++i) {
+    const int e = tid + NTH * i, r = e >> 4, c = 8 * (e & 15);
+    u4[i] = __builtin_bit_cast(stage_u4, __builtin_amdgcn_raw_buffer_load_b128(rg, (uint32_t)(r * gs + c) * 2, 0, 0));
+  }
+}
+template <int NTH>
+__device__ __forceinline__ void put_bf16_tile128(float* s, const stage_u4 (&u4)[1024 / NTH], int tid) {
+#pragma unroll
+  for (int i = 0; i < 1024 / NTH; ++i) {
+    const int e = tid + NTH * i, r = e >> 4, c = 8 * (e & 15);
+    const uint32_t w[4] = {u4[i][0], u4[i][1], u4[i][2], u4[i][3]};
     float* d = s + r * RS + c;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1067,6 +1131,12 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   load_tile128<NTH>(B1, sb + SB_DU, DV, tid);
   load_tile128<NTH>(B2, sb + SB_U, DV, tid);
   load_tile128<NTH>(B3, sb + SB_H, DK, tid);
+  // Each later single-tile reload is fetched into registers one phase early
+  // and put into LDS once its space is free, so its latency hides behind the
+  // products in between: pf holds the second half of S now, then the two
+  // halves of dS', then Kg (with pv = V and pt = T) for step 5.
+  stage_f4 pf[2048 / NTH];
+  fetch_tile128<NTH>(pf, sb + SB_H + 64 * DK, DK, tid);
   __syncthreads();
   // 2. dQg = dO S and dW = -dU S, contracting over v in two halves
   f32x4 dqg[2][2], dw[2][2];
@@ -1075,7 +1145,8 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   mfma_block<false, false, 2, 2>(dqg, B0, RS, B3, RS, R0, C0, 64, lane);
   mfma_block<false, false, 2, 2>(dw, B1, RS, B3, RS, R0, C0, 64, lane);
   __syncthreads();
-  load_tile128<NTH>(B3, sb + SB_H + 64 * DK, DK, tid);
+  put_tile128<NTH>(B3, pf, tid);
+  fetch_tile128<NTH>(pf, sb + SB_DH, DK, tid);
   __syncthreads();
   mfma_block<false, false, 2, 2>(dqg, B0 + 64, RS, B3, RS, R0, C0, 64, lane);
   mfma_block<false, false, 2, 2>(dw, B1 + 64, RS, B3, RS, R0, C0, 64, lane);
@@ -1100,14 +1171,20 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   }
   __syncthreads();
   // 4. dKd = U dS', contracting over v in two halves; dgn = colsum(dS' . S)
+  stage_u4 pv[1024 / NTH];
+  stage_f4 pt[1024 / NTH];
   {
     f32x4 dkd[2][2];
     zero_block(dkd);
-    load_tile128<NTH>(B3, sb + SB_DH, DK, tid);
+    put_tile128<NTH>(B3, pf, tid);
+    fetch_tile128<NTH>(pf, sb + SB_DH + 64 * DK, DK, tid);
     __syncthreads();
     mfma_block<false, false, 2, 2>(dkd, B2, RS, B3, RS, R0, C0, 64, lane);
     __syncthreads();
-    load_tile128<NTH>(B3, sb + SB_DH + 64 * DK, DK, tid);
+    put_tile128<NTH>(B3, pf, tid);
+    fetch_tile128<NTH>(pf, pb + PB_KG, DK, tid);
+    fetch_bf16_tile128<NTH>(pv, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
+    fetch_tile64<NTH>(pt, pb + PB_T, tid);
     __syncthreads();
     mfma_block<false, false, 2, 2>(dkd, B2 + 64, RS, B3, RS, R0, C0, 64, lane);
 #pragma unroll
@@ -1144,9 +1221,9 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) B3[BLK_ROW(R0, m, r) * RS + BLK_COL(C0, n)] = -dw[m][n][r];
-  load_tile128<NTH>(B0, pb + PB_KG, DK, tid);
-  load_bf16_tile128<NTH>(B2, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
-  load_tile64<NTH>(sT, pb + PB_T, tid);
+  put_tile128<NTH>(B0, pf, tid);
+  put_bf16_tile128<NTH>(B2, pv, tid);
+  put_tile64<NTH>(sT, pt, tid);
   if (tid < CH) {
     const __amdgpu_buffer_rsrc_t bb = buffer_rsrc(beta + (size_t)L.row0 * Hv + h, (uint32_t)L.len * Hv * 2);
     const float braw = bf2f((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(bb, (uint32_t)(tid * Hv) * 2, 0, 0));
