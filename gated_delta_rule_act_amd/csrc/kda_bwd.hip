@@ -964,22 +964,36 @@ kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ ch
   job_entry<KIND>(S, j, h0 == nullptr ? nullptr : reinterpret_cast<const char*>(h0) +
                                                       (size_t)j.chain * DV * DK * (init_dtype == KDA_STATE_BF16 ? 2 : 4),
                   init_dtype, seg, chains, nseg, w, li, lg);
+  // every global operand of a chunk (W, Kd, the Ubar tile and gn) is fetched
+  // into registers one chunk ahead, so a chunk step waits on memory only for
+  // loads issued a whole step earlier
+  f32x4 fW[ST128], fKd[ST128];
+  f32x4 fUb = f32x4{0.f, 0.f, 0.f, 0.f};
+  float fgn = 0.0f;
+  auto fetch = [&](int c) {
+    const float* pb = ws + ((size_t)h * mc + j.x0 + c) * CHUNK_HEAD_FLOATS;
+    fetch_tile128(fW, pb + PB_W, tid);
+    fetch_tile128(fKd, pb + PB_KD, tid);
+    // U rows 16 w .. +15 start from -Ubar (lane layout of the product below);
+    // a map job has no inputs, Ubar = 0
+    if constexpr (KIND != ST_TRANS) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) fUb[r] = pb[PB_UB + (ut + 4 * lg + r) * DV + v0 + uv + li];
+    }
+    fgn = pb[PB_GN + 16 * w + li];
+  };
+  if (j.c0 < j.c1) fetch(j.c0);
   for (int c = j.c0; c < j.c1; ++c) {
     const float* pb = ws + ((size_t)h * mc + j.x0 + c) * CHUNK_HEAD_FLOATS;
     float* sb = const_cast<float*>(pb) + PB_FLOATS;
     if constexpr (KIND == ST_FULL) slice_to_global(S, sb + SB_H, v0, w, li, lg);
     slice_to_lds(S, sS, w, li, lg);
-    load_tile128<STATE_THREADS>(sW, pb + PB_W, DK, tid);
-    load_tile128<STATE_THREADS>(sKd, pb + PB_KD, DK, tid);
-    // U rows 16 w .. +15 start from -Ubar (lane layout of the product below);
-    // a map job has no inputs, Ubar = 0
+    put_tile128(sW, fW, tid);
+    put_tile128(sKd, fKd, tid);
     f32x4 U[1][1];
-    zero_block(U);
-    if constexpr (KIND != ST_TRANS) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) U[0][0][r] = -pb[PB_UB + (ut + 4 * lg + r) * DV + v0 + uv + li];
-    }
-    const float gn = pb[PB_GN + 16 * w + li];
+    U[0][0] = -fUb;
+    const float gn = fgn;
+    fetch(min(c + 1, j.c1 - 1));
     __syncthreads();
     // -U = W S^T - Ubar:  A(t, k) = W[t][k],  B(k, v) = S[v][k]
     mfma_block<false, true, 1, 1>(U, sW + ut * RS, RS, sS, RS, 0, uv, DK, lane);
