@@ -1148,7 +1148,8 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   // Each later single-tile reload is fetched into registers one phase early
   // and put into LDS once its space is free, so its latency hides behind the
   // products in between: pf holds the second half of S now, then the two
-  // halves of dS', then Kg (with pv = V and pt = T) for step 5.
+  // halves of dS' (second half first), then Kg (with pv = V and pt = T) for
+  // step 5.
   stage_f4 pf[2048 / NTH];
   fetch_tile128<NTH>(pf, sb + SB_H + 64 * DK, DK, tid);
   __syncthreads();
@@ -1160,7 +1161,7 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   mfma_block<false, false, 2, 2>(dw, B1, RS, B3, RS, R0, C0, 64, lane);
   __syncthreads();
   put_tile128<NTH>(B3, pf, tid);
-  fetch_tile128<NTH>(pf, sb + SB_DH, DK, tid);
+  fetch_tile128<NTH>(pf, sb + SB_DH + 64 * DK, DK, tid);  // dS' rows 64 .. 127, first in step 4
   __syncthreads();
   mfma_block<false, false, 2, 2>(dqg, B0 + 64, RS, B3, RS, R0, C0, 64, lane);
   mfma_block<false, false, 2, 2>(dw, B1 + 64, RS, B3, RS, R0, C0, 64, lane);
@@ -1184,50 +1185,56 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
       }
   }
   __syncthreads();
-  // 4. dKd = U dS', contracting over v in two halves; dgn = colsum(dS' . S)
+  // 4. dKd = U dS', contracting over v in two halves; dgn = colsum(dS' . S).
+  //    B0 is free since step 3 and B3 still holds the second half of S, so
+  //    dS' goes to B0, second half first: that half's column sums pair B0
+  //    with B3 in LDS, and only the first half of S is read again (into
+  //    registers, issued a phase early).  Thread (row group rg, 4 channels
+  //    c4) sums rows 4 rg .. +3 of each half.
   stage_u4 pv[1024 / NTH];
   stage_f4 pt[1024 / NTH];
   {
+    const int rg = tid >> 5, c4 = 4 * (tid & 31);
     f32x4 dkd[2][2];
     zero_block(dkd);
-    put_tile128<NTH>(B3, pf, tid);
-    fetch_tile128<NTH>(pf, sb + SB_DH + 64 * DK, DK, tid);
+    put_tile128<NTH>(B0, pf, tid);  // dS' rows 64 .. 127
+    fetch_tile128<NTH>(pf, sb + SB_DH, DK, tid);
+    stage_f4 s1[4];  // S rows 4 rg .. +3 (first half), channels c4 .. +3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s1[i] = *reinterpret_cast<const stage_f4*>(sb + SB_H + (4 * rg + i) * DK + c4);
     __syncthreads();
-    mfma_block<false, false, 2, 2>(dkd, B2, RS, B3, RS, R0, C0, 64, lane);
+    mfma_block<false, false, 2, 2>(dkd, B2 + 64, RS, B0, RS, R0, C0, 64, lane);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc += *reinterpret_cast<const f32x4*>(B0 + (4 * rg + i) * RS + c4) *
+             *reinterpret_cast<const f32x4*>(B3 + (4 * rg + i) * RS + c4);
     __syncthreads();
-    put_tile128<NTH>(B3, pf, tid);
+    put_tile128<NTH>(B0, pf, tid);  // dS' rows 0 .. 63
     fetch_tile128<NTH>(pf, pb + PB_KG, DK, tid);
     fetch_bf16_tile128<NTH>(pv, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
     fetch_tile64<NTH>(pt, pb + PB_T, tid);
     __syncthreads();
-    mfma_block<false, false, 2, 2>(dkd, B2 + 64, RS, B3, RS, R0, C0, 64, lane);
+    mfma_block<false, false, 2, 2>(dkd, B2, RS, B0, RS, R0, C0, 64, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += *reinterpret_cast<const f32x4*>(B0 + (4 * rg + i) * RS + c4) * s1[i];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int r = 0; r < 4; ++r) gb[GB_DKD + BLK_ROW(R0, m, r) * DK + BLK_COL(C0, n)] = dkd[m][n][r];
-    // dgn = colsum(dS' . S) over the 128 rows: thread (row group rg, 4
-    // channels) sums rows 8 rg .. +7 from independent vector loads; the 16
-    // row groups meet in B0, free since step 3
-    const int rg = tid >> 5, c4 = 4 * (tid & 31);
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int vv = 8 * rg + i;
-      acc += *reinterpret_cast<const f32x4*>(sb + SB_DH + vv * DK + c4) *
-             *reinterpret_cast<const f32x4*>(sb + SB_H + vv * DK + c4);
-    }
-    *reinterpret_cast<f32x4*>(B0 + rg * DK + c4) = acc;
+    // the 16 row groups meet in sT, free until step 5
+    *reinterpret_cast<f32x4*>(sT + rg * DK + c4) = acc;
   }
   __syncthreads();
   if (tid < DK) {
     float sum = 0.0f;
 #pragma unroll
-    for (int g8 = 0; g8 < 16; ++g8) sum += B0[g8 * DK + tid];
+    for (int g8 = 0; g8 < 16; ++g8) sum += sT[g8 * DK + tid];
     gb[GB_DGN + tid] = sum;
   }
-  __syncthreads();  // B0 is reloaded below
+  __syncthreads();  // B0, B2, B3 and sT are refilled below
   // 5. B3 <- dW, B0 <- Kg, B2 <- V, sT <- T, sB <- beta
 #pragma unroll
   for (int m = 0; m < 2; ++m)
