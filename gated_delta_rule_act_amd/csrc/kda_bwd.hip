@@ -1391,6 +1391,10 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // (range-checked buffer loads: a conditional load was compiled into a
   // branch that waited for each load in turn)
   uint16_t graw[4][4];
+  // db from dM . T of the own rows (dense kernel), for the dbeta stores at the end
+  float dbw[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dbw[r] = gb[GB_DB + rbase + r];
   {
     const __amdgpu_buffer_rsrc_t bg = buffer_rsrc(g + ((size_t)L.row0 * Hv + h) * DK, (uint32_t)L.len * Hv * DK * 2);
 #pragma unroll
@@ -1698,30 +1702,26 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     if (li == 0) { sRow[0][half][row] = yq; sRow[1][half][row] = yk; sRow[2][half][row] = dbs; }
   }
   __syncthreads();
+  // dq, dk and dg go through LDS (sK, sQ and sG are free now), so that every
+  // thread stores whole 64-byte row segments instead of 48 scattered floats
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = rbase + r;
-    if (row >= L.len) continue;  // uniform over the 16 lanes of the row
-    const size_t trow = (size_t)(L.row0 + row);
     // y = q/|q| (the operand is scale y): dq = r (dy - y (y . dy)), dy = scale dQ
     const float yq = norm ? sRow[0][0][row] + sRow[0][1][row] : 0.0f;
     const float yk = norm ? sRow[1][0][row] + sRow[1][1][row] : 0.0f;
     const float rqi = sRq[row], rki = sRk[row];
-    const int hh = qk_heads_out == Hqk ? hq : h;
-    float* pq = dq + (trow * qk_heads_out + hh) * DK;
-    float* pk = dk + (trow * qk_heads_out + hh) * DK;
-    float* pg = dg + (trow * Hv + h) * DK;
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      const int c = 16 * (nb + n) + li;
-      pq[c] = rqi * (scale * dQ[n][r] - Qo[n][r] * yq);
-      pk[c] = rki * (dK[n][r] - Ko[n][r] * yk);
-      pg[c] = dgo[n][r];
+      const int e = row * RS + 16 * (nb + n) + li;
+      sK[e] = rqi * (scale * dQ[n][r] - Qo[n][r] * yq);
+      sQ[e] = rki * (dK[n][r] - Ko[n][r] * yk);
+      sG[e] = dgo[n][r];
     }
-    if (li == 0 && half == 0) {
-      const float db = gb[GB_DB + row] + (sRow[2][0][row] + sRow[2][1][row]);
+    if (li == 0 && half == 0 && row < L.len) {
+      const float db = dbw[r] + (sRow[2][0][row] + sRow[2][1][row]);
       const float b = sB[row];
-      dbeta[trow * Hv + h] = (flags & KDA_FLAG_BETA_IS_PROB) ? db : db * b * (1.0f - b);
+      dbeta[(size_t)(L.row0 + row) * Hv + h] = (flags & KDA_FLAG_BETA_IS_PROB) ? db : db * b * (1.0f - b);
     }
   }
   // per-chunk partials of ddt_bias (column sums) and dA_log
@@ -1731,6 +1731,24 @@ kda_bwd_pair_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   dA += __shfl_xor(dA, 16); dA += __shfl_xor(dA, 32);
   if (lane == 0) sRed[wave] = dA;
   __syncthreads();
+  {
+    // thread t: channels 4 (t & 31) .. +3 of rows (t >> 5) + 16 i, so the 32
+    // lanes of a row store its 512 bytes in order
+    const int c4 = 4 * (tid & 31);
+    const int hh = qk_heads_out == Hqk ? hq : h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 5) + 16 * i;
+      if (row < L.len) {
+        const size_t trow = (size_t)(L.row0 + row);
+        *reinterpret_cast<f32x4*>(dq + (trow * qk_heads_out + hh) * DK + c4) =
+            *reinterpret_cast<const f32x4*>(sK + row * RS + c4);
+        *reinterpret_cast<f32x4*>(dk + (trow * qk_heads_out + hh) * DK + c4) =
+            *reinterpret_cast<const f32x4*>(sQ + row * RS + c4);
+        *reinterpret_cast<f32x4*>(dg + (trow * Hv + h) * DK + c4) = *reinterpret_cast<const f32x4*>(sG + row * RS + c4);
+      }
+    }
+  }
   if (tid < DK) {
     float sum = 0.0f;
     for (int rg = 0; rg < 16; ++rg) sum += sCol[rg * DK + tid];
