@@ -68,6 +68,7 @@ constexpr int RS = 132;  // LDS row stride of 128-wide fp32 tiles (rows 4 banks 
 constexpr int QS = 68;   // LDS row stride of 64-wide fp32 tiles
 constexpr int BV = 32;   // V rows per state workgroup
 constexpr int BNS = DV / BV;
+constexpr int64_t kBwdCUs = 256;   // compute units of an MI355X (persistent grids)
 constexpr int PREP_THREADS = 512;  // 8 waves: two per SIMD beside the prep kernel's 157 KB of LDS
 constexpr int PAIR_THREADS = 512;  // the same for the pair kernel (147 KB)
 constexpr int DENSE_THREADS = 512;  // and for the dense kernel (152 KB)
@@ -287,29 +288,50 @@ __device__ __forceinline__ float sum16(float x) {
   return x + dpp_f<0x140>(x);
 }
 
-template <int MODE, int NTH = 256>
-__device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* sG, float* sBt, float* sB, const uint16_t* q,
-                                                  const uint16_t* k, const uint16_t* g, const uint16_t* beta,
-                                                  const float* A_log, const float* dt_bias, int Hqk, int Hv, int h,
-                                                  int hq, int64_t row0, int len, float lb, int flags,
-                                                  int tid, float* rq_out, float* rk_out) {
-  constexpr int TPR = NTH / CH, CPT = DK / TPR;  // threads per row, channels per thread
+// The raw inputs of one chunk for thread t (row t / TPR, CPT channels): the
+// global loads, kept apart from their processing so that a persistent
+// kernel can issue the next chunk's loads while it works on the current one.
+template <int NTH>
+struct ChunkRaw {
+  static constexpr int TPR = NTH / CH, CPT = DK / TPR;  // threads per row, channels per thread
+  stage_u4 q[CPT / 8], k[CPT / 8], g[CPT / 8];
+  uint32_t b;  // beta of the row (bf16 bits)
+};
+template <int NTH>
+__device__ __forceinline__ void fetch_chunk_raw(ChunkRaw<NTH>& raw, const uint16_t* q, const uint16_t* k,
+                                                const uint16_t* g, const uint16_t* beta, int Hqk, int Hv, int h, int hq,
+                                                int64_t row0, int len, int tid) {
+  constexpr int TPR = ChunkRaw<NTH>::TPR, CPT = ChunkRaw<NTH>::CPT;
   const int r = tid / TPR, c0 = CPT * (tid % TPR);
-  const bool ok = r < len;
   // range-checked buffer loads over the chunk's rows: rows >= len read as
   // zero, with no branch around the loads
   const __amdgpu_buffer_rsrc_t bq = buffer_rsrc(q + ((size_t)row0 * Hqk + hq) * DK, (uint32_t)len * Hqk * DK * 2);
   const __amdgpu_buffer_rsrc_t bk = buffer_rsrc(k + ((size_t)row0 * Hqk + hq) * DK, (uint32_t)len * Hqk * DK * 2);
   const __amdgpu_buffer_rsrc_t bg = buffer_rsrc(g + ((size_t)row0 * Hv + h) * DK, (uint32_t)len * Hv * DK * 2);
   const __amdgpu_buffer_rsrc_t bb = buffer_rsrc(beta + (size_t)row0 * Hv + h, (uint32_t)len * Hv * 2);
-  float qv[CPT], kv[CPT], gv[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; i += 8) {
     const uint32_t oqk = (uint32_t)(r * Hqk * DK + c0 + i) * 2, og = (uint32_t)(r * Hv * DK + c0 + i) * 2;
-    const uint4 uq = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bq, oqk, 0, 0));
-    const uint4 uk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bk, oqk, 0, 0));
-    const uint4 ug = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bg, og, 0, 0));
-    const uint32_t wq[4] = {uq.x, uq.y, uq.z, uq.w}, wk[4] = {uk.x, uk.y, uk.z, uk.w}, wg[4] = {ug.x, ug.y, ug.z, ug.w};
+    raw.q[i / 8] = __builtin_bit_cast(stage_u4, __builtin_amdgcn_raw_buffer_load_b128(bq, oqk, 0, 0));
+    raw.k[i / 8] = __builtin_bit_cast(stage_u4, __builtin_amdgcn_raw_buffer_load_b128(bk, oqk, 0, 0));
+    raw.g[i / 8] = __builtin_bit_cast(stage_u4, __builtin_amdgcn_raw_buffer_load_b128(bg, og, 0, 0));
+  }
+  raw.b = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(bb, (uint32_t)(r * Hv) * 2, 0, 0);
+}
+
+template <int MODE, int NTH>
+__device__ __forceinline__ void process_chunk_inputs(const ChunkRaw<NTH>& raw, float* sK, float* sQ, float* sG,
+                                                     float* sBt, float* sB, const float* A_log, const float* dt_bias,
+                                                     int h, int len, float lb, int flags, int tid, float* rq_out,
+                                                     float* rk_out) {
+  constexpr int TPR = ChunkRaw<NTH>::TPR, CPT = ChunkRaw<NTH>::CPT;
+  const int r = tid / TPR, c0 = CPT * (tid % TPR);
+  const bool ok = r < len;
+  float qv[CPT], kv[CPT], gv[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; i += 8) {
+    const stage_u4 uq = raw.q[i / 8], uk = raw.k[i / 8], ug = raw.g[i / 8];
+    const uint32_t wq[4] = {uq[0], uq[1], uq[2], uq[3]}, wk[4] = {uk[0], uk[1], uk[2], uk[3]}, wg[4] = {ug[0], ug[1], ug[2], ug[3]};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       qv[i + 2 * j] = __uint_as_float(wq[j] << 16); qv[i + 2 * j + 1] = __uint_as_float(wq[j] & 0xffff0000u);
@@ -352,7 +374,7 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
     *reinterpret_cast<float4*>(sG + r * RS + c0 + i) = make_float4(g4[0], g4[1], g4[2], g4[3]);
   }
   if (tid % TPR == 0) {
-    const float braw = bf2f((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(bb, (uint32_t)(r * Hv) * 2, 0, 0));
+    const float braw = bf2f((uint16_t)raw.b);
     const float bp = (flags & KDA_FLAG_BETA_IS_PROB) ? braw : sigm(braw);
     sB[r] = ok ? bp : 0.0f;
   }
@@ -375,6 +397,18 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
     }
   }
   __syncthreads();
+}
+
+// fetch and process in one go
+template <int MODE, int NTH = 256>
+__device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* sG, float* sBt, float* sB, const uint16_t* q,
+                                                  const uint16_t* k, const uint16_t* g, const uint16_t* beta,
+                                                  const float* A_log, const float* dt_bias, int Hqk, int Hv, int h,
+                                                  int hq, int64_t row0, int len, float lb, int flags,
+                                                  int tid, float* rq_out, float* rk_out) {
+  ChunkRaw<NTH> raw;
+  fetch_chunk_raw<NTH>(raw, q, k, g, beta, Hqk, Hv, h, hq, row0, len, tid);
+  process_chunk_inputs<MODE, NTH>(raw, sK, sQ, sG, sBt, sB, A_log, dt_bias, h, len, lb, flags, tid, rq_out, rk_out);
 }
 
 // Exponents from the block-local form (log2 units):
@@ -539,15 +573,43 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   __shared__ float sB[CH];
   __shared__ float sX[2 * 16 * 17];
   __shared__ __attribute__((aligned(16))) float sBt[4 * DK];
-  const int x = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  // Persistent: workgroup b takes the chunk-heads b, b + gridDim.x, ...
+  // (chunk-head id = v-head * mc + chunk), and the raw inputs of the next one
+  // are fetched into registers while the current one runs, so that their
+  // latency is not exposed at one workgroup per CU.
+  const int tid0 = threadIdx.x, total = mc * Hv;
+  ChunkRaw<PREP_THREADS> raw;
+  stage_u4 rawv[1024 / PREP_THREADS];  // the chunk's V tile (bf16)
+  auto fetch = [&](int id) {
+    const int x2 = id % mc, h2 = id / mc;
+    const ChunkLoc L2 = chunk_loc(x2, cu, chunk_off, T, N);
+    fetch_chunk_raw<PREP_THREADS>(raw, q, k, g, beta, Hqk, Hv, h2, h2 / (Hv / Hqk), L2.row0, L2.len, tid0);
+    fetch_bf16_tile128<PREP_THREADS>(rawv, v + ((size_t)L2.row0 * Hv + h2) * DV, (size_t)Hv * DV, L2.len, tid0);
+  };
+  if ((int)blockIdx.x < total) fetch(blockIdx.x);
+  for (int id = blockIdx.x; id < total; id += gridDim.x) {
+  // the thread index is renewed opaquely every chunk-head, so the compiler
+  // does not hoist the body's index arithmetic out of the loop and hold it in
+  // registers across the whole body
+  int tid = tid0;
+  asm volatile("" : "+v"(tid));
+  const int x = id % mc, h = id / mc;
   const ChunkLoc L = chunk_loc(x, cu, chunk_off, T, N);
-  if (L.len == 0) return;
+  const int nxt = id + (int)gridDim.x;
+  if (L.len == 0) {
+    if (nxt < total) fetch(nxt);
+    continue;
+  }
   const int hq = h / (Hv / Hqk);
   float* pb = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS;
 
   for (int e = tid; e < CH * QS; e += PREP_THREADS) { sA[e] = 0.0f; sAq[e] = 0.0f; sT[e] = 0.0f; }
-  load_chunk_inputs<MODE, PREP_THREADS>(sK, sQ, sG, sBt, sB, q, k, g, beta, A_log, dt_bias, Hqk, Hv, h, hq, L.row0, L.len, lb,
-                          flags, tid, nullptr, nullptr);
+  process_chunk_inputs<MODE, PREP_THREADS>(raw, sK, sQ, sG, sBt, sB, A_log, dt_bias, h, L.len, lb, flags, tid, nullptr,
+                                           nullptr);
+  stage_u4 vcur[1024 / PREP_THREADS];  // this chunk's V, kept until it goes to LDS
+#pragma unroll
+  for (int i = 0; i < 1024 / PREP_THREADS; ++i) vcur[i] = rawv[i];
+  if (nxt < total) fetch(nxt);
 
   // Akk and Aqk.  Each off-diagonal block (I, J), J < I, is formed in two
   // halves over the channels, twelve tasks in all; waves 0..3 also sum the
@@ -749,8 +811,8 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     *reinterpret_cast<float4*>(sK + r * RS + c) = kgv[it];
   }
   __syncthreads();
-  // sQ <- V; sT <- M = T diag(b)
-  load_bf16_tile128<PREP_THREADS>(sQ, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
+  // sQ <- V (fetched with the chunk's other inputs); sT <- M = T diag(b)
+  put_bf16_tile128<PREP_THREADS>(sQ, vcur, tid);
   for (int e = tid; e < CH * CH; e += PREP_THREADS) {
     const int r = e >> 6, c = e & 63;
     sT[r * QS + c] *= sB[c];
@@ -775,6 +837,8 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
           pb[PB_W + t * DK + c] = w[m][n][r];
           pb[PB_UB + t * DV + c] = u[m][n][r];
         }
+  }
+  __syncthreads();  // the next chunk-head rewrites every LDS array
   }
 }
 
@@ -1909,8 +1973,11 @@ void launch_bwd(const kda_fwd_params* p, const void* q, const void* k, const voi
   const uint16_t* dd = (const uint16_t*)d_out;
   if (packed) launch_chunk_map(cu, p->num_seqs, chunk_off, st);
   const dim3 cg((unsigned)mc, (unsigned)p->H_v);
+  // the prep kernel is persistent: one workgroup per CU (its LDS allows no
+  // more), each looping over chunk-heads
+  const dim3 pg((unsigned)std::min<int64_t>(mc * p->H_v, kBwdCUs));
   if (mc > 0)
-    hipLaunchKernelGGL(kda_bwd_prep_kernel<MODE>, cg, dim3(PREP_THREADS), 0, st, qq, kk, vv, gg, bb, A_log, dt_bias, cu,
+    hipLaunchKernelGGL(kda_bwd_prep_kernel<MODE>, pg, dim3(PREP_THREADS), 0, st, qq, kk, vv, gg, bb, A_log, dt_bias, cu,
                        chunk_off, p->T, p->num_seqs, p->H_qk, p->H_v, (int)mc, p->scale, p->lower_bound, p->flags, ws);
   if (chains > 0) {
     float* seg = ws + (size_t)p->H_v * mc * CHUNK_HEAD_FLOATS + gqa_floats(p);
