@@ -4,7 +4,9 @@
 One step = one full forward (kda_fwd: intra-chunk kernel + state-chain
 kernel) over the safe-gate workload B=2, T=8192, H=32, K=V=128 (lower_bound
 -5, fp32 initial and final state), inputs resident in HBM.  Prints one JSON
-line: tokens/s with the median / min / max step, the dominant kernel's
+line: tokens/s with the median / min / max step, the sustained rate of the
+steps that run on after the timed ones (the clocks ramp up over the first
+tens of milliseconds of load), the dominant kernel's
 roofline from HIP events recorded around each stage on the launch stream
 (algorithmic bytes: the kernel's own share of the method's minimum HBM bytes
 per token-head), the path's fraction of the HBM and bf16 MFMA peaks, counter
@@ -161,6 +163,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--sustain-steps", type=int, default=200,
+                    help="untimed-for-value steps after the timed region, for the sustained rate")
     ap.add_argument("--workload", type=int, default=None,
                     help="workload index (chunked: 1-5, the bench line is 3; recurrent: 1-2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -238,7 +242,23 @@ def main():
     ms_per_step = evt[0].elapsed_time(evt[-1]) / args.steps
     step_ms = [evt[i].elapsed_time(evt[i + 1]) for i in range(args.steps)]
 
-    # per-kernel durations: events around each stage on the launch stream
+    # Sustained rate, after the timed region (not part of `value`): the GPU
+    # raises its clocks over the first tens of milliseconds of load (workload 3:
+    # about 595 us per step at first, 521 us after some 35 steps, and back to
+    # the start after an idle of 0.1 s), so a short window right after a few
+    # warm-up steps measures part of that ramp.  This loop runs on from the
+    # timed one with no idle in between.
+    sus = [torch.cuda.Event(enable_timing=True) for _ in range(args.sustain_steps + 1)]
+    sus[0].record()
+    for i in range(args.sustain_steps):
+        step()
+        sus[i + 1].record()
+    torch.cuda.synchronize()
+    sus_ms = [sus[i].elapsed_time(sus[i + 1]) for i in range(args.sustain_steps)]
+    sus_tail = sus_ms[len(sus_ms) // 2:]  # the second half, past the ramp
+
+    # per-kernel durations: events around each stage on the launch stream,
+    # right after the sustained loop (so at the clocks of continuous load)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for e in evs:
@@ -290,6 +310,11 @@ def main():
         "kernels_ms": {"kda_intra_kernel": t_intra, "kda_state_kernel": t_state},
         "step_ms": {"mean": ms_per_step, "median": statistics.median(step_ms), "min": min(step_ms),
                     "max": max(step_ms)},
+        "sustained": None if not sus_tail else {
+            "steps": args.sustain_steps, "ms_per_step_median": statistics.median(sus_tail),
+            "ms_per_step_mean": statistics.mean(sus_tail), "min": min(sus_tail), "max": max(sus_tail),
+            "tokens_per_s": tokens / (statistics.median(sus_tail) * 1e-3),
+            "note": "steps run on right after the timed region; figures over the second half of them"},
         "path": {"min_bytes_per_step": bm["path"], "min_bytes_per_token_head": bm["path"] / bm["token_heads"],
                  "achieved_GBps": path_gbps, "hbm_frac": path_gbps / HBM_PEAK_GBPS,
                  "mfma_algorithmic_TFLOPs": mfma_tflops,
@@ -342,6 +367,18 @@ def run_recurrent(args, dev):
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    # sustained rate: five times as many steps as the chunked forward's (a decode
+    # step is about a tenth as long), run on after the timed ones in blocks of
+    # 100 with an event per block; figures over the second half of the blocks
+    nblk = args.sustain_steps * 5 // 100
+    sus = [torch.cuda.Event(enable_timing=True) for _ in range(nblk + 1)]
+    sus[0].record()
+    for b in range(nblk):
+        for _ in range(100):
+            step()
+        sus[b + 1].record()
+    torch.cuda.synchronize()
+    sus_tail = [sus[b].elapsed_time(sus[b + 1]) / 100 for b in range(nblk)][nblk // 2:]
     tok = inp.B * inp.T
     st = {0: 0, 1: 4, 2: 2}
     # algorithmic bytes: q, k per (token, qk-head); v, g, beta, out per (token, v-head);
@@ -368,6 +405,11 @@ def run_recurrent(args, dev):
                    "V": inp.V, "gate": ["softplus", "safe_sigmoid", "pregated"][inp.gate_mode],
                    "lower_bound": inp.lower_bound, "initial_state": "fp32", "final_state": "fp32"},
         "roofline": roof,
+        "sustained": None if not sus_tail else {
+            "steps": nblk * 100, "ms_per_step_median": statistics.median(sus_tail), "min": min(sus_tail),
+            "max": max(sus_tail), "tokens_per_s": tok / (statistics.median(sus_tail) * 1e-3),
+            "achieved_GBps": nbytes / (statistics.median(sus_tail) * 1e-3) / 1e9,
+            "note": "blocks of 100 steps run on right after the timed ones; per-step figures of the second half"},
         "kernel_source_sha": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
@@ -425,6 +467,16 @@ def run_backward(args, dev):
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    # sustained rate: steps run on after the timed ones (a quarter as many as the
+    # forward's, each step being about eight times longer), second half
+    ns = args.sustain_steps // 4
+    sus = [torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)]
+    sus[0].record()
+    for i in range(ns):
+        step()
+        sus[i + 1].record()
+    torch.cuda.synchronize()
+    sus_tail = [sus[i].elapsed_time(sus[i + 1]) for i in range(ns)][ns // 2:]
     tok = inp.B * inp.T
     # the method's contractions for the gradients: the forward's 180,224 flop per
     # token-head recomputed, plus twice that for the reverse products
@@ -441,6 +493,10 @@ def run_backward(args, dev):
                      "achieved": flops / (ms * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, "traffic": None,
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": ms},
+        "sustained": None if not sus_tail else {
+            "steps": ns, "ms_per_step_median": statistics.median(sus_tail), "min": min(sus_tail),
+            "max": max(sus_tail), "tokens_per_s": tok / (statistics.median(sus_tail) * 1e-3),
+            "note": "steps run on right after the timed ones; figures over the second half of them"},
         "kernel_source_sha": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
