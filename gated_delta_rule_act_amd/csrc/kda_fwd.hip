@@ -1016,7 +1016,8 @@ __device__ __forceinline__ void load_v(ChunkRegs& o, const uint16_t* __restrict_
 // PART 0: token-tile operands, vectors and (narrow slices) V, issued two
 // chunks ahead (wide slices: one chunk ahead, V two chunks ahead on its own),
 // also in groups: PART 2 the W fragments, PART 4 the Q fragments, PART 3 the
-// rest; PART 1: key-tile operands (issued one chunk ahead).
+// rest (PART 5 its vectors alone, PART 6 the rest without them); PART 1:
+// key-tile operands (issued one chunk ahead).
 // Operands a kind does not use are neither loaded nor kept.
 template <int PART, int KIND, int NVT>
 __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk, int wave, int lane,
@@ -1030,7 +1031,7 @@ __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) o.qg[kb] = ld_frag(blk, F_QG + wave * 4 + kb, lane);
   }
-  if constexpr (PART == 0 || PART == 3) {
+  if constexpr (PART == 0 || PART == 3 || PART == 6) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // token block 1 of token tiles 0, 1 is not stored: a fragment index past
@@ -1042,9 +1043,10 @@ __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk
       }
       if constexpr (KIND == ST_FULL) o.aq[kb] = ld_frag(blk, tf == NFRAG ? NFRAG : F_AQK + tf, lane);
     }
-    o.vec = ld_frag(blk, F_VEC, 16 * wave + (lane & 15));
-    if constexpr (KIND != ST_TRANS && NVT == NVT_NARROW) load_v<NVT>(o, v, row0, len, Hv, h, v0, tid);
   }
+  if constexpr (PART == 0 || PART == 3 || PART == 5) o.vec = ld_frag(blk, F_VEC, 16 * wave + (lane & 15));
+  if constexpr ((PART == 0 || PART == 3 || PART == 6) && KIND != ST_TRANS && NVT == NVT_NARROW)
+    load_v<NVT>(o, v, row0, len, Hv, h, v0, tid);
   if constexpr (PART == 1) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -1592,6 +1594,409 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
 }
 
 // ---------------------------------------------------------------------------
+// The same chain for full outputs on 32-column slices, with each chunk step
+// split over two roles of four waves, two waves per SIMD:
+//   chain waves (0..3), wave w: the recurrence itself -- S_c to LDS, U of
+//     token tile w = 2^-E_(c+1) Ub - 2^-d W (S 2^-E_c)^T to LDS, then its key
+//     rows of S <- S Diag(2^G_last) + U^T Kd; operands W, the vectors, Kd;
+//   helper waves (4..7), wave 4 + w: everything off that path for token tile
+//     w -- Ub = T diag(b) V of the next chunk, O = scale (Q . 2^G) S^T +
+//     Aqk U, its bf16 rounding and stores; operands Q . 2^G, T diag(b), Aqk, V.
+// With one wave per SIMD the step's serial instruction stream was the bound:
+// here the helper issues while the chain wave waits on an MFMA result, an LDS
+// read or a barrier.  The barriers, LDS buffers and scale rule are those of
+// kda_state_kernel (the helper posts the largest |Ub|, the chain wave those
+// of S and U, and the scale takes the largest of the eight), and every
+// product and rounding is the same, so the results are bit-identical to it.
+// Each role runs its own loop over the chunks, so the registers of the one
+// role's operands are free for the other's.
+constexpr int SPWAVES = 8;
+
+// the scale shift from the eight posted maxima (chain waves 0..3, helpers 4..7)
+__device__ __forceinline__ int scale_shift8(const uint32_t* sMx, int E) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(sMx), b = *reinterpret_cast<const u32x4*>(sMx + 4);
+  const int mi = __builtin_amdgcn_readfirstlane(
+      (int)max(max(max(a[0], a[1]), max(a[2], a[3])), max(max(b[0], b[1]), max(b[2], b[3]))));
+  if (mi == 0) return 0;
+  const int d = min(max(ilog2_bits(mi), -kMaxStep), kMaxStep);
+  return min(max(E + d, -kMaxExp), kMaxExp) - E;
+}
+
+// chain wave, chunk c: `cur` holds W, the vectors and Kd of chunk c, `n1`
+// receives Kd of chunk c+1, `n2` W and the vectors of chunk c+2.  On entry S
+// holds S_c in units of 2^E and mu this wave's largest |U_(c-1)|.
+__device__ __forceinline__ void chain_step(const StateCtx& x, f32x4 (&S)[2][NVT_NARROW], ChunkRegs& cur,
+                                           ChunkRegs& n1, ChunkRegs& n2, const int c, int& E, uint32_t& mu,
+                                           const f32x4* sUb) {
+#pragma clang fp contract(off)
+  constexpr int NVT = NVT_NARROW;
+  const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
+  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+  if (lane < 16) reinterpret_cast<u32x4*>(x.sVec)[16 * wave + lane] = cur.vec;
+  float ms = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt) {
+      const half4 hv = {(_Float16)S[j][vt][0], (_Float16)S[j][vt][1], (_Float16)S[j][vt][2], (_Float16)S[j][vt][3]};
+      *reinterpret_cast<half4*>(x.sS + (16 * vt + li) * SSS + 32 * wave + 16 * j + 4 * lg) = hv;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) ms = fmaxf(ms, fabsf(S[j][vt][rr]));
+    }
+  uint32_t mx = wave_max_bits(max(mu, abs_bits(ms)));
+  if (lane == 0) x.sMx[wave] = mx;
+  const int ct = min(c + 2, x.nc - 1);
+  const uint8_t* blk_t = x.wsh + (size_t)(x.x0 + ct) * BLOCK;
+  __syncthreads();  // B1
+  const int d = scale_shift8(x.sMx, E);
+  const float f = pow2f(-d);
+  const int En = E + d;
+  const float scn = pow2f(-En);
+  const f32x4 gn0 = *reinterpret_cast<const f32x4*>(x.sVec + 32 * wave + 4 * lg) * f;
+  const f32x4 gn1 = *reinterpret_cast<const f32x4*>(x.sVec + 32 * wave + 16 + 4 * lg) * f;
+  f32x4 U[NVT];
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt) {
+    const f32x4 ub = sUb[(wave * NVT + vt) * 64 + lane];
+    half8 sb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
+    f32x4 uw = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) uw = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.wn[kb]), sb[kb], uw, 0, 0, 0);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) U[vt][rr] = __builtin_fmaf(ub[rr], scn, uw[rr] * f);
+    __builtin_amdgcn_sched_barrier(0);
+    if (vt == 0) load_chunk_part<2, ST_FULL, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+    else load_chunk_part<5, ST_FULL, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float mu_n = 0.0f;
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt) {
+    half4 hi, lo;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float up = U[vt][rr];
+      const _Float16 hh = (_Float16)up;
+      hi[rr] = hh;
+      lo[rr] = (_Float16)(up - (float)hh);
+      mu_n = fmaxf(mu_n, fabsf(up));
+    }
+    const int vv = 16 * vt + li, tt = 16 * wave + 4 * lg;
+    *reinterpret_cast<half4*>(x.sUh + vv * SUS + tt) = hi;
+    *reinterpret_cast<half4*>(x.sUl + vv * SUS + tt) = lo;
+  }
+  __syncthreads();  // B2
+  half8 kdlo[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) kdlo[j][b] = unpack_e4m3(cur.kdl[j][b]);
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt) {
+    const half8 uh0 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 8 * lg);
+    const half8 uh1 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 32 + 8 * lg);
+    const half8 ul0 = *reinterpret_cast<const half8*>(x.sUl + (16 * vt + li) * SUS + 8 * lg);
+    const half8 ul1 = *reinterpret_cast<const half8*>(x.sUl + (16 * vt + li) * SUS + 32 + 8 * lg);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f32x4 sa = S[j][vt] * (j == 0 ? gn0 : gn1), sl = f32x4{0, 0, 0, 0};
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0]), uh0, sa, 0, 0, 0);
+      sl = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdlo[j][0], uh0, sl, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1]), uh1, sa, 0, 0, 0);
+      sl = __builtin_amdgcn_mfma_f32_16x16x32_f16(kdlo[j][1], uh1, sl, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][0]), ul0, sa, 0, 0, 0);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.kd[j][1]), ul1, sa, 0, 0, 0);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) S[j][vt][rr] = __builtin_fmaf(sl[rr], kKdLoUnscale, sa[rr]);
+    }
+    if (vt == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int cp = min(c + 1, x.nc - 1);
+      load_chunk_part<1, ST_FULL, NVT>(n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, 0, 0, x.Hv, x.h,
+                                       x.v0, tid);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  E = En;
+  mu = abs_bits(mu_n);
+}
+
+// helper wave, chunk c: `cur` holds Q . 2^G and Aqk of chunk c, `n1` T diag(b)
+// and V of chunk c+1, `n2` receives the helper operands of chunk c+2.  On
+// entry ub holds T diag(b) V_c of token tile w (real units); the outputs of
+// chunk c-1 are in pd.
+__device__ __forceinline__ void helper_step(const StateCtx& x, ChunkRegs& cur, ChunkRegs& n1, ChunkRegs& n2,
+                                            const int c, PendingOut<NVT_NARROW>& pd, int& E,
+                                            f32x4 (&ub)[NVT_NARROW], f32x4* sUb) {
+#pragma clang fp contract(off)
+  constexpr int NVT = NVT_NARROW;
+  const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
+  const int64_t row0 = x.bos + (int64_t)c * CH;
+  // the next chunk's V slice (read after B1 below; the other buffer's last
+  // reads were before B2 of the previous chunk), this chunk's Ub for the
+  // chain waves and its magnitude
+  _Float16* const sVn = x.sV + ((c + 1) & 1) * SV_HALFS<NVT>;
+  *reinterpret_cast<u32x4*>(sVn + sv_row<NVT>(tid >> 2) + 8 * (tid & 3)) = n1.vraw[0];
+  float mb = 0.0f;
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt) {
+    sUb[(wave * NVT + vt) * 64 + lane] = ub[vt];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) mb = fmaxf(mb, fabsf(ub[vt][rr]));
+  }
+  const uint32_t mx = wave_max_bits(abs_bits(mb * pow2f(-E)));
+  if (lane == 0) x.sMx[SWAVES + wave] = mx;
+  store_pending(pd, x.out, x.Hv, x.h, x.v0, wave, li, lg);
+  const int ct = min(c + 2, x.nc - 1);
+  const uint8_t* blk_t = x.wsh + (size_t)(x.x0 + ct) * BLOCK;
+  __syncthreads();  // B1
+  const int d = scale_shift8(x.sMx, E);
+  const int En = E + d;
+  const float sf = x.scale * pow2f(-d);
+  f32x4 O[NVT], ubn[NVT];
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt) {
+    ub_one<ST_FULL, NVT>(ubn[vt], sVn, n1, vt, lane);
+    half8 sb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
+    f32x4 o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
+    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[0]), sb[0], o0, 0, 0, 0);
+    o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[1]), sb[1], o1, 0, 0, 0);
+    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[2]), sb[2], o0, 0, 0, 0);
+    o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[3]), sb[3], o1, 0, 0, 0);
+    O[vt] = (o0 + o1) * sf;
+    __builtin_amdgcn_sched_barrier(0);
+    if (vt == 0) load_chunk_part<4, ST_FULL, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+    else load_chunk_part<6, ST_FULL, NVT>(n2, blk_t, wave, lane, x.v, x.bos + (int64_t)ct * CH, chunk_len(x, ct),
+                                          x.Hv, x.h, x.v0, tid);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();  // B2
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt) {
+    const half8 uh0 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 8 * lg);
+    const half8 uh1 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 32 + 8 * lg);
+    O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[0]), uh0, O[vt], 0, 0, 0);
+    O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[1]), uh1, O[vt], 0, 0, 0);
+  }
+  const float se = pow2f(En);
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) pd.o[vt][rr] = __builtin_bit_cast(uint16_t, (__bf16)(O[vt][rr] * se));
+  pd.row0 = row0;
+  pd.len = chunk_len(x, c);
+  E = En;
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt) ub[vt] = ubn[vt];
+}
+
+// One workgroup of 8 waves per (job, 32-column V slice), full outputs; jobs
+// and the XCD-aware decode as in kda_state_kernel.
+__global__ void __launch_bounds__(64 * SPWAVES, 1)
+kda_state_split_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
+                       const int* __restrict__ chunk_off, const void* __restrict__ h0, void* __restrict__ hT,
+                       uint16_t* __restrict__ out, const uint8_t* __restrict__ ws, float* __restrict__ seg,
+                       int T, int N, int Hv, int max_chunks, int init_dtype, int final_dtype, int nseg,
+                       int seg_len, float scale) {
+  constexpr int NVT = NVT_NARROW;
+  __shared__ __attribute__((aligned(16))) float sVec[256];
+  __shared__ __attribute__((aligned(16))) uint32_t sMx[SPWAVES];
+  constexpr int VS = 16 * NVT, NSL = DV / VS;
+  __shared__ __attribute__((aligned(16))) _Float16 sS[VS * SSS];
+  __shared__ __attribute__((aligned(16))) _Float16 sUh[VS * SUS];
+  __shared__ __attribute__((aligned(16))) _Float16 sUl[VS * SUS];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[2 * SV_HALFS<NVT>];
+  __shared__ __attribute__((aligned(16))) f32x4 sUb[SWAVES * NVT * 64];  // Ub of each token tile, lane order
+
+  const int chains = N * Hv;
+  const int id = blockIdx.x;
+  const int job = (id / (8 * NSL)) * 8 + (id & 7);
+  const int slice = (id >> 3) % NSL;
+  if (job >= chains * nseg) return;
+  const int chain = job / nseg, r = job % nseg;
+  const int n = chain / Hv, h = chain % Hv;
+  const int v0 = VS * slice;
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const bool helper = wv >= SWAVES;
+  // the role's own wave index and thread index (0..255)
+  const int wave = helper ? wv - SWAVES : wv, tid = (int)threadIdx.x & (64 * SWAVES - 1), lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+
+  int64_t bos, seqlen;
+  int x0, nc;
+  if (cu == nullptr) {
+    const int ncs = (T + CH - 1) / CH;
+    const int cs = r * seg_len;
+    bos = (int64_t)n * T + (int64_t)cs * CH; seqlen = (int64_t)T - (int64_t)cs * CH;
+    x0 = n * ncs + cs; nc = max(0, min(seg_len, ncs - cs));
+  } else {
+    bos = cu[n]; seqlen = cu[n + 1] - cu[n];
+    x0 = chunk_off[n]; nc = chunk_off[n + 1] - x0;
+  }
+  const uint8_t* wsh = ws + (size_t)h * max_chunks * BLOCK;
+  StateCtx ctx{v, out, wsh, bos, seqlen, x0, nc, Hv, h, v0, tid, wave, lane, li, lg, scale, sMx, sVec, sS, sUh, sUl, sV};
+
+  if (!helper) {
+    // entry state: tiles S^T[k][v]: k = 32 wave + 16 j + 4 lg + rr, v = v0 + 16 vt + li
+    const void* src = nullptr;
+    int src_dtype = KDA_STATE_NONE;
+    size_t src_base = 0;
+    if (nseg == 1) {
+      src = h0; src_dtype = init_dtype; src_base = ((size_t)n * Hv + h) * DV * DK;
+    } else {
+      src = seg_mat(seg, chains, nseg, SEG_SIN, chain, r); src_dtype = KDA_STATE_F32;
+    }
+    f32x4 S[2][NVT];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) {
+        const int kk = 32 * wave + 16 * j + 4 * lg, vv = v0 + 16 * vt + li;
+        f32x4 st = f32x4{0, 0, 0, 0};
+        if (src_dtype == KDA_STATE_F32) {
+          st = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(src) + src_base + (size_t)vv * DK + kk);
+        } else if (src_dtype == KDA_STATE_BF16) {
+          const uint2 u =
+              *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + src_base + (size_t)vv * DK + kk);
+          st = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u)};
+        }
+        S[j][vt] = st;
+      }
+    ChunkRegs rA, rB, rC;
+    if (nc > 0) {
+      const uint8_t* b0 = wsh + (size_t)x0 * BLOCK;
+      load_chunk_part<2, ST_FULL, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      load_chunk_part<5, ST_FULL, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      load_chunk_part<1, ST_FULL, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      const uint8_t* b1 = wsh + (size_t)(x0 + min(1, nc - 1)) * BLOCK;
+      load_chunk_part<2, ST_FULL, NVT>(rB, b1, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      load_chunk_part<5, ST_FULL, NVT>(rB, b1, wave, lane, v, 0, 0, Hv, h, v0, tid);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) settle(S[j][vt]);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) settle(rA.wn[kb]);
+    settle(rA.vec);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) { settle(rA.kd[j][b]); settle(rA.kdl[j][b]); }
+    // the entry scale: the largest magnitude of the entry state (chain waves)
+    // and of the first chunk's V (helpers) brought into [1, 2)
+    int E = 0;
+    if (nc > 0) {
+      uint32_t mx = 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) mx = max(mx, abs_bits(S[j][vt][rr]));
+      mx = wave_max_bits(mx);
+      if (lane == 0) sMx[wave] = mx;
+      __syncthreads();
+      const u32x4 a = *reinterpret_cast<const u32x4*>(sMx), b = *reinterpret_cast<const u32x4*>(sMx + 4);
+      const int mi = __builtin_amdgcn_readfirstlane(
+          (int)max(max(max(a[0], a[1]), max(a[2], a[3])), max(max(b[0], b[1]), max(b[2], b[3]))));
+      E = mi == 0 ? 0 : min(max(ilog2_bits(mi), -kMaxExp), kMaxExp);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) S[j][vt][rr] = __builtin_amdgcn_ldexpf(S[j][vt][rr], -E);
+    }
+    __syncthreads();  // every wave has read the entry maxima before any posts again
+    uint32_t mu = 0;
+    int c = 0;
+    for (; c + 3 <= nc; c += 3) {
+      chain_step(ctx, S, rA, rB, rC, c, E, mu, sUb);
+      chain_step(ctx, S, rB, rC, rA, c + 1, E, mu, sUb);
+      chain_step(ctx, S, rC, rA, rB, c + 2, E, mu, sUb);
+    }
+    if (c < nc) chain_step(ctx, S, rA, rB, rC, c, E, mu, sUb);
+    if (c + 1 < nc) chain_step(ctx, S, rB, rC, rA, c + 1, E, mu, sUb);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) S[j][vt][rr] = __builtin_amdgcn_ldexpf(S[j][vt][rr], E);
+    // exit state (the last segment's job holds the chain's final state)
+    if (r == nseg - 1 && final_dtype != KDA_STATE_NONE) {
+      const size_t dst_base = ((size_t)n * Hv + h) * DV * DK;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) {
+          const int kk = 32 * wave + 16 * j + 4 * lg, vv = v0 + 16 * vt + li;
+          if (final_dtype == KDA_STATE_F32) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(hT) + dst_base + (size_t)vv * DK + kk) = S[j][vt];
+          } else {
+            uint2 u;
+            u.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][0]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][1]) << 16);
+            u.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][2]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(hT) + dst_base + (size_t)vv * DK + kk) = u;
+          }
+        }
+    }
+  } else {
+    ChunkRegs rA, rB, rC;
+    if (nc > 0) {
+      const uint8_t* b0 = wsh + (size_t)x0 * BLOCK;
+      load_chunk_part<4, ST_FULL, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      load_chunk_part<6, ST_FULL, NVT>(rA, b0, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
+      const int c1 = min(1, nc - 1);
+      const uint8_t* b1 = wsh + (size_t)(x0 + c1) * BLOCK;
+      load_chunk_part<4, ST_FULL, NVT>(rB, b1, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      load_chunk_part<6, ST_FULL, NVT>(rB, b1, wave, lane, v, bos + (int64_t)c1 * CH, chunk_len(ctx, c1), Hv, h, v0,
+                                       tid);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) settle(rA.qg[kb]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) { settle(rA.tbh[kb]); settle(rA.tbl[kb]); settle(rA.aq[kb]); }
+    settle(rA.vraw[0]);
+    // the first chunk's V slice into V buffer 0 (visible after the barrier below)
+    if (nc > 0) *reinterpret_cast<u32x4*>(sV + sv_row<NVT>(tid >> 2) + 8 * (tid & 3)) = rA.vraw[0];
+    int E = 0;
+    if (nc > 0) {
+      const uint32_t mx = wave_max_bits(bf16x8_absmax_bits(rA.vraw[0]));
+      if (lane == 0) sMx[SWAVES + wave] = mx;
+      __syncthreads();
+      const u32x4 a = *reinterpret_cast<const u32x4*>(sMx), b = *reinterpret_cast<const u32x4*>(sMx + 4);
+      const int mi = __builtin_amdgcn_readfirstlane(
+          (int)max(max(max(a[0], a[1]), max(a[2], a[3])), max(max(b[0], b[1]), max(b[2], b[3]))));
+      E = mi == 0 ? 0 : min(max(ilog2_bits(mi), -kMaxExp), kMaxExp);
+    }
+    __syncthreads();
+    f32x4 ub[NVT];
+    if (nc > 0) ub_tile<ST_FULL, NVT>(ub, sV, rA, lane);
+    PendingOut<NVT> pd;
+    pd.row0 = bos;
+    pd.len = 0;
+    int c = 0;
+    for (; c + 3 <= nc; c += 3) {
+      helper_step(ctx, rA, rB, rC, c, pd, E, ub, sUb);
+      helper_step(ctx, rB, rC, rA, c + 1, pd, E, ub, sUb);
+      helper_step(ctx, rC, rA, rB, c + 2, pd, E, ub, sUb);
+    }
+    if (c < nc) helper_step(ctx, rA, rB, rC, c, pd, E, ub, sUb);
+    if (c + 1 < nc) helper_step(ctx, rB, rC, rA, c + 1, pd, E, ub, sUb);
+    store_pending(pd, out, Hv, h, v0, wave, li, lg);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // token-recurrent forward (decode and short sequences)
 //
 // One workgroup of 256 threads per (sequence, v-head, 32-row V slice): thread
@@ -2040,9 +2445,14 @@ void launch_state_kind(const StateArgs& a, int64_t jobs, hipStream_t st) {
   const int64_t narrow_rounds = (jobs * NSLICE + kGpuCUs - 1) / kGpuCUs;
   const int64_t wide_rounds = (jobs * (NSLICE / 2) + kGpuCUs - 1) / kGpuCUs;
   if (wide_rounds * kWideStepPct >= narrow_rounds * 100) {
-    hipLaunchKernelGGL((kda_state_kernel<KIND, NVT_NARROW>), dim3((unsigned)(((jobs + 7) / 8) * 8 * NSLICE)),
-                       dim3(64 * SWAVES), 0, st, a.v, a.cu, a.chunk_off, a.h0, a.hT, a.out, a.ws, a.seg, a.T, a.N,
-                       a.Hv, a.mc, a.init_dtype, a.final_dtype, a.nseg, a.seg_len, a.scale);
+    if constexpr (KIND == ST_FULL)
+      hipLaunchKernelGGL(kda_state_split_kernel, dim3((unsigned)(((jobs + 7) / 8) * 8 * NSLICE)),
+                         dim3(64 * SPWAVES), 0, st, a.v, a.cu, a.chunk_off, a.h0, a.hT, a.out, a.ws, a.seg, a.T, a.N,
+                         a.Hv, a.mc, a.init_dtype, a.final_dtype, a.nseg, a.seg_len, a.scale);
+    else
+      hipLaunchKernelGGL((kda_state_kernel<KIND, NVT_NARROW>), dim3((unsigned)(((jobs + 7) / 8) * 8 * NSLICE)),
+                         dim3(64 * SWAVES), 0, st, a.v, a.cu, a.chunk_off, a.h0, a.hT, a.out, a.ws, a.seg, a.T, a.N,
+                         a.Hv, a.mc, a.init_dtype, a.final_dtype, a.nseg, a.seg_len, a.scale);
   } else {
     constexpr int nsl = DV / (16 * NVT_WIDE);
     hipLaunchKernelGGL((kda_state_kernel<KIND, NVT_WIDE>), dim3((unsigned)(((jobs + 7) / 8) * 8 * nsl)),
