@@ -1016,8 +1016,8 @@ __device__ __forceinline__ void load_v(ChunkRegs& o, const uint16_t* __restrict_
 // PART 0: token-tile operands, vectors and (narrow slices) V, issued two
 // chunks ahead (wide slices: one chunk ahead, V two chunks ahead on its own),
 // also in groups: PART 2 the W fragments, PART 4 the Q fragments, PART 3 the
-// rest (PART 5 its vectors alone, PART 6 the rest without them); PART 1:
-// key-tile operands (issued one chunk ahead).
+// rest (PART 5 its vectors alone, PART 6 the rest without them, PART 7 that
+// without V); PART 1: key-tile operands (issued one chunk ahead).
 // Operands a kind does not use are neither loaded nor kept.
 template <int PART, int KIND, int NVT>
 __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk, int wave, int lane,
@@ -1031,7 +1031,7 @@ __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) o.qg[kb] = ld_frag(blk, F_QG + wave * 4 + kb, lane);
   }
-  if constexpr (PART == 0 || PART == 3 || PART == 6) {
+  if constexpr (PART == 0 || PART == 3 || PART == 6 || PART == 7) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // token block 1 of token tiles 0, 1 is not stored: a fragment index past
@@ -1723,10 +1723,14 @@ __device__ __forceinline__ void chain_step(const StateCtx& x, f32x4 (&S)[2][NVT_
   mu = abs_bits(mu_n);
 }
 
-// helper wave, chunk c: `cur` holds Q . 2^G and Aqk of chunk c, `n1` T diag(b)
-// and V of chunk c+1, `n2` receives the helper operands of chunk c+2.  On
-// entry ub holds T diag(b) V_c of token tile w (real units); the outputs of
-// chunk c-1 are in pd.
+// helper wave, chunk c: `cur` holds Q . 2^G and Aqk of chunk c (its V is in
+// LDS already, and the register set receives V of chunk c+3), `n1` holds
+// T diag(b) and V of chunk c+1, `n2` receives Q, T diag(b) and Aqk of chunk
+// c+2.  On entry ub holds T diag(b) V_c of token tile w (real units); the
+// outputs of chunk c-1 are in pd.  V of chunk c+1 goes to LDS between the
+// barriers and T diag(b) V_(c+1) is formed after the second: so those
+// operands are consumed a step and a half after their loads are issued (loads
+// complete in order, so a wait for a young load waits for all the older ones).
 __device__ __forceinline__ void helper_step(const StateCtx& x, ChunkRegs& cur, ChunkRegs& n1, ChunkRegs& n2,
                                             const int c, PendingOut<NVT_NARROW>& pd, int& E,
                                             f32x4 (&ub)[NVT_NARROW], f32x4* sUb) {
@@ -1734,11 +1738,7 @@ __device__ __forceinline__ void helper_step(const StateCtx& x, ChunkRegs& cur, C
   constexpr int NVT = NVT_NARROW;
   const int wave = x.wave, lane = x.lane, li = x.li, lg = x.lg, tid = x.tid;
   const int64_t row0 = x.bos + (int64_t)c * CH;
-  // the next chunk's V slice (read after B1 below; the other buffer's last
-  // reads were before B2 of the previous chunk), this chunk's Ub for the
-  // chain waves and its magnitude
-  _Float16* const sVn = x.sV + ((c + 1) & 1) * SV_HALFS<NVT>;
-  *reinterpret_cast<u32x4*>(sVn + sv_row<NVT>(tid >> 2) + 8 * (tid & 3)) = n1.vraw[0];
+  // this chunk's Ub for the chain waves, and its magnitude
   float mb = 0.0f;
 #pragma unroll
   for (int vt = 0; vt < NVT; ++vt) {
@@ -1749,16 +1749,15 @@ __device__ __forceinline__ void helper_step(const StateCtx& x, ChunkRegs& cur, C
   const uint32_t mx = wave_max_bits(abs_bits(mb * pow2f(-E)));
   if (lane == 0) x.sMx[SWAVES + wave] = mx;
   store_pending(pd, x.out, x.Hv, x.h, x.v0, wave, li, lg);
-  const int ct = min(c + 2, x.nc - 1);
+  const int ct = min(c + 2, x.nc - 1), cv = min(c + 3, x.nc - 1);
   const uint8_t* blk_t = x.wsh + (size_t)(x.x0 + ct) * BLOCK;
   __syncthreads();  // B1
   const int d = scale_shift8(x.sMx, E);
   const int En = E + d;
   const float sf = x.scale * pow2f(-d);
-  f32x4 O[NVT], ubn[NVT];
+  f32x4 O[NVT];
 #pragma unroll
   for (int vt = 0; vt < NVT; ++vt) {
-    ub_one<ST_FULL, NVT>(ubn[vt], sVn, n1, vt, lane);
     half8 sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
@@ -1769,11 +1768,18 @@ __device__ __forceinline__ void helper_step(const StateCtx& x, ChunkRegs& cur, C
     o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[3]), sb[3], o1, 0, 0, 0);
     O[vt] = (o0 + o1) * sf;
     __builtin_amdgcn_sched_barrier(0);
-    if (vt == 0) load_chunk_part<4, ST_FULL, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
-    else load_chunk_part<6, ST_FULL, NVT>(n2, blk_t, wave, lane, x.v, x.bos + (int64_t)ct * CH, chunk_len(x, ct),
-                                          x.Hv, x.h, x.v0, tid);
+    if (vt == 0) {
+      load_chunk_part<4, ST_FULL, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+    } else {
+      load_chunk_part<7, ST_FULL, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+      load_v<NVT>(cur, x.v, x.bos + (int64_t)cv * CH, chunk_len(x, cv), x.Hv, x.h, x.v0, tid);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
+  // V of chunk c+1 into the V buffer of its parity (last read before B2 of
+  // the previous chunk step but one)
+  _Float16* const sVn = x.sV + ((c + 1) & 1) * SV_HALFS<NVT>;
+  *reinterpret_cast<u32x4*>(sVn + sv_row<NVT>(tid >> 2) + 8 * (tid & 3)) = n1.vraw[0];
   __syncthreads();  // B2
 #pragma unroll
   for (int vt = 0; vt < NVT; ++vt) {
@@ -1790,8 +1796,9 @@ __device__ __forceinline__ void helper_step(const StateCtx& x, ChunkRegs& cur, C
   pd.row0 = row0;
   pd.len = chunk_len(x, c);
   E = En;
+  // the next chunk's Ub
 #pragma unroll
-  for (int vt = 0; vt < NVT; ++vt) ub[vt] = ubn[vt];
+  for (int vt = 0; vt < NVT; ++vt) ub_one<ST_FULL, NVT>(ub[vt], sVn, n1, vt, lane);
 }
 
 // One workgroup of 8 waves per (job, 32-column V slice), full outputs; jobs
@@ -1955,11 +1962,13 @@ kda_state_split_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict
       const uint8_t* b0 = wsh + (size_t)x0 * BLOCK;
       load_chunk_part<4, ST_FULL, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
       load_chunk_part<6, ST_FULL, NVT>(rA, b0, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
-      const int c1 = min(1, nc - 1);
+      const int c1 = min(1, nc - 1), c2 = min(2, nc - 1);
       const uint8_t* b1 = wsh + (size_t)(x0 + c1) * BLOCK;
       load_chunk_part<4, ST_FULL, NVT>(rB, b1, wave, lane, v, 0, 0, Hv, h, v0, tid);
       load_chunk_part<6, ST_FULL, NVT>(rB, b1, wave, lane, v, bos + (int64_t)c1 * CH, chunk_len(ctx, c1), Hv, h, v0,
                                        tid);
+      // V runs three chunks ahead: chunk 2's goes to the third register set now
+      load_v<NVT>(rC, v, bos + (int64_t)c2 * CH, chunk_len(ctx, c2), Hv, h, v0, tid);
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) settle(rA.qg[kb]);
