@@ -470,7 +470,6 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // a missing A_log means a multiplier of one (unused for pre-gated decay)
     const float A_exp = (MODE == KDA_GATE_PREGATED || A_log == nullptr) ? 1.0f : expf(A_log[h]);
     const float lb_log2e = lower_bound * kLog2e;
-    const int64_t row = cp.row0 + r;
     // All input loads are issued before any use, as range-checked buffer loads:
     // rows at or beyond the chunk length read as zero, so no branch (and no
     // exposed latency per k-block) is needed.
@@ -481,14 +480,17 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                   (uint32_t)max(0, min(16, cp.len - 16 * I)) * Hqk * DK * 2);
     const __amdgpu_buffer_rsrc_t bk = buffer_rsrc(k + ((size_t)(cp.row0 + 16 * I) * Hqk + hq) * DK,
                                                   (uint32_t)max(0, min(16, cp.len - 16 * I)) * Hqk * DK * 2);
+    // beta, then g (and dt_bias) first: loads complete in order, so the gate
+    // and the scan below, which need only those, run while q and k are in
+    // flight (beta is used only after the scan; a range-checked load, since a
+    // conditional one became a branch with a full wait after it)
+    const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(beta + (size_t)cp.row0 * Hv + h, (uint32_t)max(0, cp.len) * Hv * 2);
+    const float blogit = bf2f((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(r * Hv) * 2, 0, 0));
     uint4 graw[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const uint32_t c0 = 32 * kb + 8 * lg;
-      graw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, (vrow * Hv * DK + c0) * 2, 0, 0));
-      qraw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bq, (vrow * Hqk * DK + c0) * 2, 0, 0));
-      kraw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bk, (vrow * Hqk * DK + c0) * 2, 0, 0));
-    }
+    for (int kb = 0; kb < 4; ++kb)
+      graw[kb] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, (vrow * Hv * DK + 32 * kb + 8 * lg) * 2, 0, 0));
     float4 dtb4[8];
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) dtb4[kb] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -499,17 +501,19 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         dtb4[2 * kb + 1] = *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + 32 * kb + 8 * lg + 4);
       }
     }
-    const float blogit = valid ? bf2f(beta[(size_t)row * Hv + h]) : 0.0f;
-    const float vmask = valid ? 1.0f : 0.0f;
-    float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      float qf[8], kf[8];
-      unpack_bf16x8(graw[kb], G[kb]);
-      unpack_bf16x8(qraw[kb], qf);
-      unpack_bf16x8(kraw[kb], kf);
+      const uint32_t c0 = 32 * kb + 8 * lg;
+      qraw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bq, (vrow * Hqk * DK + c0) * 2, 0, 0));
+      kraw[kb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bk, (vrow * Hqk * DK + c0) * 2, 0, 0));
+    }
+    // (kept here: the scheduler would otherwise sink the q and k loads below
+    // the gate's first wait)
+    __builtin_amdgcn_sched_barrier(0);
+    const float vmask = valid ? 1.0f : 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { sq += qf[e] * qf[e]; sk += kf[e] * kf[e]; }
+    for (int kb = 0; kb < 4; ++kb) {
+      unpack_bf16x8(graw[kb], G[kb]);
       const float dtb[8] = {dtb4[2 * kb].x, dtb4[2 * kb].y, dtb4[2 * kb].z, dtb4[2 * kb].w,
                             dtb4[2 * kb + 1].x, dtb4[2 * kb + 1].y, dtb4[2 * kb + 1].z, dtb4[2 * kb + 1].w};
 #pragma unroll
@@ -517,15 +521,6 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       // a product, where a select had the compiler branch around each
       // element's exponential
       for (int e = 0; e < 8; ++e) G[kb][e] = gate2<MODE>(G[kb][e] + dtb[e], A_exp, lb_log2e) * vmask;
-    }
-    sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
-    sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
-    const bool norm = flags & KDA_FLAG_QK_L2NORM;
-    rq = norm ? rsqrtf(sq + kL2Eps) : 1.0f;
-    rk = norm ? rsqrtf(sk + kL2Eps) : 1.0f;
-    if (lg == 0) {
-      const float bp = (flags & KDA_FLAG_BETA_IS_PROB) ? blogit : fast_rcp(1.0f + fast_exp2(-kLog2e * blogit));
-      sBeta[r] = valid ? bp : 0.0f;
     }
     // the 32 scans of a lane advance together, one shift at a time: each DPP
     // step then reads a value written many instructions earlier (no hazard wait)
@@ -545,6 +540,25 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int e = 0; e < 8; ++e) G[kb][e] += dpp_row_shr<0x118>(G[kb][e]);
+    // the L2-norm factors, once q and k have arrived
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float qf[8], kf[8];
+      unpack_bf16x8(qraw[kb], qf);
+      unpack_bf16x8(kraw[kb], kf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { sq += qf[e] * qf[e]; sk += kf[e] * kf[e]; }
+    }
+    sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
+    sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
+    const bool norm = flags & KDA_FLAG_QK_L2NORM;
+    rq = norm ? rsqrtf(sq + kL2Eps) : 1.0f;
+    rk = norm ? rsqrtf(sk + kL2Eps) : 1.0f;
+    if (lg == 0) {
+      const float bp = (flags & KDA_FLAG_BETA_IS_PROB) ? blogit : fast_rcp(1.0f + fast_exp2(-kLog2e * blogit));
+      sBeta[r] = valid ? bp : 0.0f;
+    }
     // sub-chunk totals (row 15) and midpoint values (row 8), both local
     if (li == 15 || li == 8) {
       float* dst = (li == 15 ? sTot : sMid) + I * 128;
