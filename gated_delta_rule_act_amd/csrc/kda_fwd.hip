@@ -1608,14 +1608,16 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
 }
 
 // ---------------------------------------------------------------------------
-// The same chain for full outputs on 32-column slices, with each chunk step
-// split over two roles of four waves, two waves per SIMD:
+// The same chain on 32-column slices for full outputs (ST_FULL) or the state
+// alone (ST_CARRY), with each chunk step split over two roles of four waves,
+// two waves per SIMD:
 //   chain waves (0..3), wave w: the recurrence itself -- S_c to LDS, U of
 //     token tile w = 2^-E_(c+1) Ub - 2^-d W (S 2^-E_c)^T to LDS, then its key
 //     rows of S <- S Diag(2^G_last) + U^T Kd; operands W, the vectors, Kd;
 //   helper waves (4..7), wave 4 + w: everything off that path for token tile
-//     w -- Ub = T diag(b) V of the next chunk, O = scale (Q . 2^G) S^T +
-//     Aqk U, its bf16 rounding and stores; operands Q . 2^G, T diag(b), Aqk, V.
+//     w -- Ub = T diag(b) V of the next chunk and (ST_FULL) O = scale
+//     (Q . 2^G) S^T + Aqk U, its bf16 rounding and stores; operands
+//     T diag(b), V and (ST_FULL) Q . 2^G, Aqk.
 // With one wave per SIMD the step's serial instruction stream was the bound:
 // here the helper issues while the chain wave waits on an MFMA result, an LDS
 // read or a barrier.  The barriers, LDS buffers and scale rule are those of
@@ -1639,6 +1641,7 @@ __device__ __forceinline__ int scale_shift8(const uint32_t* sMx, int E) {
 // chain wave, chunk c: `cur` holds W, the vectors and Kd of chunk c, `n1`
 // receives Kd of chunk c+1, `n2` W and the vectors of chunk c+2.  On entry S
 // holds S_c in units of 2^E and mu this wave's largest |U_(c-1)|.
+template <int KIND>
 __device__ __forceinline__ void chain_step(const StateCtx& x, f32x4 (&S)[2][NVT_NARROW], ChunkRegs& cur,
                                            ChunkRegs& n1, ChunkRegs& n2, const int c, int& E, uint32_t& mu,
                                            const f32x4* sUb) {
@@ -1681,8 +1684,8 @@ __device__ __forceinline__ void chain_step(const StateCtx& x, f32x4 (&S)[2][NVT_
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) U[vt][rr] = __builtin_fmaf(ub[rr], scn, uw[rr] * f);
     __builtin_amdgcn_sched_barrier(0);
-    if (vt == 0) load_chunk_part<2, ST_FULL, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
-    else load_chunk_part<5, ST_FULL, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+    if (vt == 0) load_chunk_part<2, KIND, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+    else load_chunk_part<5, KIND, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
     __builtin_amdgcn_sched_barrier(0);
   }
   float mu_n = 0.0f;
@@ -1728,7 +1731,7 @@ __device__ __forceinline__ void chain_step(const StateCtx& x, f32x4 (&S)[2][NVT_
     if (vt == 0) {
       __builtin_amdgcn_sched_barrier(0);
       const int cp = min(c + 1, x.nc - 1);
-      load_chunk_part<1, ST_FULL, NVT>(n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, 0, 0, x.Hv, x.h,
+      load_chunk_part<1, KIND, NVT>(n1, x.wsh + (size_t)(x.x0 + cp) * BLOCK, wave, lane, x.v, 0, 0, x.Hv, x.h,
                                        x.v0, tid);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1737,14 +1740,15 @@ __device__ __forceinline__ void chain_step(const StateCtx& x, f32x4 (&S)[2][NVT_
   mu = abs_bits(mu_n);
 }
 
-// helper wave, chunk c: `cur` holds Q . 2^G and Aqk of chunk c (its V is in
-// LDS already, and the register set receives V of chunk c+3), `n1` holds
-// T diag(b) and V of chunk c+1, `n2` receives Q, T diag(b) and Aqk of chunk
-// c+2.  On entry ub holds T diag(b) V_c of token tile w (real units); the
+// helper wave, chunk c: `cur` holds Q . 2^G and Aqk of chunk c (ST_FULL; its
+// V is in LDS already, and the register set receives V of chunk c+3), `n1`
+// holds T diag(b) and V of chunk c+1, `n2` receives the helper operands of
+// chunk c+2.  On entry ub holds T diag(b) V_c of token tile w (real units); the
 // outputs of chunk c-1 are in pd.  V of chunk c+1 goes to LDS between the
 // barriers and T diag(b) V_(c+1) is formed after the second: so those
 // operands are consumed a step and a half after their loads are issued (loads
 // complete in order, so a wait for a young load waits for all the older ones).
+template <int KIND>
 __device__ __forceinline__ void helper_step(const StateCtx& x, ChunkRegs& cur, ChunkRegs& n1, ChunkRegs& n2,
                                             const int c, PendingOut<NVT_NARROW>& pd, int& E,
                                             f32x4 (&ub)[NVT_NARROW], f32x4* sUb) {
@@ -1762,7 +1766,7 @@ __device__ __forceinline__ void helper_step(const StateCtx& x, ChunkRegs& cur, C
   }
   const uint32_t mx = wave_max_bits(abs_bits(mb * pow2f(-E)));
   if (lane == 0) x.sMx[SWAVES + wave] = mx;
-  store_pending(pd, x.out, x.Hv, x.h, x.v0, wave, li, lg);
+  if constexpr (KIND == ST_FULL) store_pending(pd, x.out, x.Hv, x.h, x.v0, wave, li, lg);
   const int ct = min(c + 2, x.nc - 1), cv = min(c + 3, x.nc - 1);
   const uint8_t* blk_t = x.wsh + (size_t)(x.x0 + ct) * BLOCK;
   __syncthreads();  // B1
@@ -1772,20 +1776,23 @@ __device__ __forceinline__ void helper_step(const StateCtx& x, ChunkRegs& cur, C
   f32x4 O[NVT];
 #pragma unroll
   for (int vt = 0; vt < NVT; ++vt) {
-    half8 sb[4];
+    if constexpr (KIND == ST_FULL) {
+      half8 sb[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
-    f32x4 o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
-    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[0]), sb[0], o0, 0, 0, 0);
-    o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[1]), sb[1], o1, 0, 0, 0);
-    o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[2]), sb[2], o0, 0, 0, 0);
-    o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[3]), sb[3], o1, 0, 0, 0);
-    O[vt] = (o0 + o1) * sf;
+      for (int kb = 0; kb < 4; ++kb)
+        sb[kb] = *reinterpret_cast<const half8*>(x.sS + (16 * vt + li) * SSS + 32 * kb + 8 * lg);
+      f32x4 o0 = f32x4{0, 0, 0, 0}, o1 = f32x4{0, 0, 0, 0};
+      o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[0]), sb[0], o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[1]), sb[1], o1, 0, 0, 0);
+      o0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[2]), sb[2], o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.qg[3]), sb[3], o1, 0, 0, 0);
+      O[vt] = (o0 + o1) * sf;
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (vt == 0) {
-      load_chunk_part<4, ST_FULL, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+      load_chunk_part<4, KIND, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
     } else {
-      load_chunk_part<7, ST_FULL, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
+      load_chunk_part<7, KIND, NVT>(n2, blk_t, wave, lane, x.v, 0, 0, x.Hv, x.h, x.v0, tid);
       load_v<NVT>(cur, x.v, x.bos + (int64_t)cv * CH, chunk_len(x, cv), x.Hv, x.h, x.v0, tid);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1795,28 +1802,31 @@ __device__ __forceinline__ void helper_step(const StateCtx& x, ChunkRegs& cur, C
   _Float16* const sVn = x.sV + ((c + 1) & 1) * SV_HALFS<NVT>;
   *reinterpret_cast<u32x4*>(sVn + sv_row<NVT>(tid >> 2) + 8 * (tid & 3)) = n1.vraw[0];
   __syncthreads();  // B2
+  if constexpr (KIND == ST_FULL) {
 #pragma unroll
-  for (int vt = 0; vt < NVT; ++vt) {
-    const half8 uh0 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 8 * lg);
-    const half8 uh1 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 32 + 8 * lg);
-    O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[0]), uh0, O[vt], 0, 0, 0);
-    O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[1]), uh1, O[vt], 0, 0, 0);
+    for (int vt = 0; vt < NVT; ++vt) {
+      const half8 uh0 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 8 * lg);
+      const half8 uh1 = *reinterpret_cast<const half8*>(x.sUh + (16 * vt + li) * SUS + 32 + 8 * lg);
+      O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[0]), uh0, O[vt], 0, 0, 0);
+      O[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(cur.aq[1]), uh1, O[vt], 0, 0, 0);
+    }
+    const float se = pow2f(En);
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) pd.o[vt][rr] = __builtin_bit_cast(uint16_t, (__bf16)(O[vt][rr] * se));
+    pd.row0 = row0;
+    pd.len = chunk_len(x, c);
   }
-  const float se = pow2f(En);
-#pragma unroll
-  for (int vt = 0; vt < NVT; ++vt)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) pd.o[vt][rr] = __builtin_bit_cast(uint16_t, (__bf16)(O[vt][rr] * se));
-  pd.row0 = row0;
-  pd.len = chunk_len(x, c);
   E = En;
   // the next chunk's Ub
 #pragma unroll
-  for (int vt = 0; vt < NVT; ++vt) ub_one<ST_FULL, NVT>(ub[vt], sVn, n1, vt, lane);
+  for (int vt = 0; vt < NVT; ++vt) ub_one<KIND, NVT>(ub[vt], sVn, n1, vt, lane);
 }
 
-// One workgroup of 8 waves per (job, 32-column V slice), full outputs; jobs
-// and the XCD-aware decode as in kda_state_kernel.
+// One workgroup of 8 waves per (job, 32-column V slice); jobs, their entry
+// and exit states and the XCD-aware decode as in kda_state_kernel.
+template <int KIND>
 __global__ void __launch_bounds__(64 * SPWAVES, 1)
 kda_state_split_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
                        const int* __restrict__ chunk_off, const void* __restrict__ h0, void* __restrict__ hT,
@@ -1833,12 +1843,14 @@ kda_state_split_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict
   __shared__ __attribute__((aligned(16))) _Float16 sV[2 * SV_HALFS<NVT>];
   __shared__ __attribute__((aligned(16))) f32x4 sUb[SWAVES * NVT * 64];  // Ub of each token tile, lane order
 
+  static_assert(KIND == ST_FULL || KIND == ST_CARRY, "the split kernel runs full and carry jobs");
+  const int jpc = KIND == ST_FULL ? nseg : nseg - 1;  // jobs per chain
   const int chains = N * Hv;
   const int id = blockIdx.x;
   const int job = (id / (8 * NSL)) * 8 + (id & 7);
   const int slice = (id >> 3) % NSL;
-  if (job >= chains * nseg) return;
-  const int chain = job / nseg, r = job % nseg;
+  if (job >= chains * jpc) return;
+  const int chain = job / jpc, r = job % jpc;
   const int n = chain / Hv, h = chain % Hv;
   const int v0 = VS * slice;
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -1866,9 +1878,9 @@ kda_state_split_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict
     const void* src = nullptr;
     int src_dtype = KDA_STATE_NONE;
     size_t src_base = 0;
-    if (nseg == 1) {
+    if ((KIND == ST_CARRY && r == 0) || (KIND == ST_FULL && nseg == 1)) {
       src = h0; src_dtype = init_dtype; src_base = ((size_t)n * Hv + h) * DV * DK;
-    } else {
+    } else if (KIND == ST_FULL) {
       src = seg_mat(seg, chains, nseg, SEG_SIN, chain, r); src_dtype = KDA_STATE_F32;
     }
     f32x4 S[2][NVT];
@@ -1887,16 +1899,18 @@ kda_state_split_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict
                      __uint_as_float(u.y & 0xffff0000u)};
         }
         S[j][vt] = st;
+        if (KIND == ST_CARRY && r == 0)
+          *reinterpret_cast<f32x4*>(seg_mat(seg, chains, nseg, SEG_SIN, chain, 0) + (size_t)vv * DK + kk) = st;
       }
     ChunkRegs rA, rB, rC;
     if (nc > 0) {
       const uint8_t* b0 = wsh + (size_t)x0 * BLOCK;
-      load_chunk_part<2, ST_FULL, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
-      load_chunk_part<5, ST_FULL, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
-      load_chunk_part<1, ST_FULL, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      load_chunk_part<2, KIND, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      load_chunk_part<5, KIND, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      load_chunk_part<1, KIND, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
       const uint8_t* b1 = wsh + (size_t)(x0 + min(1, nc - 1)) * BLOCK;
-      load_chunk_part<2, ST_FULL, NVT>(rB, b1, wave, lane, v, 0, 0, Hv, h, v0, tid);
-      load_chunk_part<5, ST_FULL, NVT>(rB, b1, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      load_chunk_part<2, KIND, NVT>(rB, b1, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      load_chunk_part<5, KIND, NVT>(rB, b1, wave, lane, v, 0, 0, Hv, h, v0, tid);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -1938,35 +1952,44 @@ kda_state_split_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict
     uint32_t mu = 0;
     int c = 0;
     for (; c + 3 <= nc; c += 3) {
-      chain_step(ctx, S, rA, rB, rC, c, E, mu, sUb);
-      chain_step(ctx, S, rB, rC, rA, c + 1, E, mu, sUb);
-      chain_step(ctx, S, rC, rA, rB, c + 2, E, mu, sUb);
+      chain_step<KIND>(ctx, S, rA, rB, rC, c, E, mu, sUb);
+      chain_step<KIND>(ctx, S, rB, rC, rA, c + 1, E, mu, sUb);
+      chain_step<KIND>(ctx, S, rC, rA, rB, c + 2, E, mu, sUb);
     }
-    if (c < nc) chain_step(ctx, S, rA, rB, rC, c, E, mu, sUb);
-    if (c + 1 < nc) chain_step(ctx, S, rB, rC, rA, c + 1, E, mu, sUb);
+    if (c < nc) chain_step<KIND>(ctx, S, rA, rB, rC, c, E, mu, sUb);
+    if (c + 1 < nc) chain_step<KIND>(ctx, S, rB, rC, rA, c + 1, E, mu, sUb);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) S[j][vt][rr] = __builtin_amdgcn_ldexpf(S[j][vt][rr], E);
-    // exit state (the last segment's job holds the chain's final state)
-    if (r == nseg - 1 && final_dtype != KDA_STATE_NONE) {
-      const size_t dst_base = ((size_t)n * Hv + h) * DV * DK;
+    // exit state: the chain's final state from the last full job; a carry
+    // job's state into the segment scratch
+    void* dst = nullptr;
+    int dst_dtype = KDA_STATE_NONE;
+    size_t dst_base = 0;
+    if constexpr (KIND == ST_FULL) {
+      if (r == nseg - 1) { dst = hT; dst_dtype = final_dtype; dst_base = ((size_t)n * Hv + h) * DV * DK; }
+    } else {
+      dst = r == 0 ? seg_mat(seg, chains, nseg, SEG_SIN, chain, 1) : seg_mat(seg, chains, nseg, SEG_F, chain, r);
+      dst_dtype = KDA_STATE_F32;
+    }
+    if (dst_dtype != KDA_STATE_NONE) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) {
           const int kk = 32 * wave + 16 * j + 4 * lg, vv = v0 + 16 * vt + li;
-          if (final_dtype == KDA_STATE_F32) {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(hT) + dst_base + (size_t)vv * DK + kk) = S[j][vt];
+          if (dst_dtype == KDA_STATE_F32) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dst) + dst_base + (size_t)vv * DK + kk) = S[j][vt];
           } else {
             uint2 u;
             u.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][0]) |
                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][1]) << 16);
             u.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][2]) |
                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)S[j][vt][3]) << 16);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(hT) + dst_base + (size_t)vv * DK + kk) = u;
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dst) + dst_base + (size_t)vv * DK + kk) = u;
           }
         }
     }
@@ -1974,20 +1997,25 @@ kda_state_split_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict
     ChunkRegs rA, rB, rC;
     if (nc > 0) {
       const uint8_t* b0 = wsh + (size_t)x0 * BLOCK;
-      load_chunk_part<4, ST_FULL, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
-      load_chunk_part<6, ST_FULL, NVT>(rA, b0, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
+      load_chunk_part<4, KIND, NVT>(rA, b0, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      load_chunk_part<6, KIND, NVT>(rA, b0, wave, lane, v, bos, chunk_len(ctx, 0), Hv, h, v0, tid);
       const int c1 = min(1, nc - 1), c2 = min(2, nc - 1);
       const uint8_t* b1 = wsh + (size_t)(x0 + c1) * BLOCK;
-      load_chunk_part<4, ST_FULL, NVT>(rB, b1, wave, lane, v, 0, 0, Hv, h, v0, tid);
-      load_chunk_part<6, ST_FULL, NVT>(rB, b1, wave, lane, v, bos + (int64_t)c1 * CH, chunk_len(ctx, c1), Hv, h, v0,
-                                       tid);
+      load_chunk_part<4, KIND, NVT>(rB, b1, wave, lane, v, 0, 0, Hv, h, v0, tid);
+      load_chunk_part<6, KIND, NVT>(rB, b1, wave, lane, v, bos + (int64_t)c1 * CH, chunk_len(ctx, c1), Hv, h, v0,
+                                    tid);
       // V runs three chunks ahead: chunk 2's goes to the third register set now
       load_v<NVT>(rC, v, bos + (int64_t)c2 * CH, chunk_len(ctx, c2), Hv, h, v0, tid);
     }
+    if constexpr (KIND == ST_FULL)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) settle(rA.qg[kb]);
+      for (int kb = 0; kb < 4; ++kb) settle(rA.qg[kb]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) { settle(rA.tbh[kb]); settle(rA.tbl[kb]); settle(rA.aq[kb]); }
+    for (int kb = 0; kb < 2; ++kb) {
+      settle(rA.tbh[kb]);
+      settle(rA.tbl[kb]);
+      if constexpr (KIND == ST_FULL) settle(rA.aq[kb]);
+    }
     settle(rA.vraw[0]);
     // the first chunk's V slice into V buffer 0 (visible after the barrier below)
     if (nc > 0) *reinterpret_cast<u32x4*>(sV + sv_row<NVT>(tid >> 2) + 8 * (tid & 3)) = rA.vraw[0];
@@ -2003,19 +2031,19 @@ kda_state_split_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict
     }
     __syncthreads();
     f32x4 ub[NVT];
-    if (nc > 0) ub_tile<ST_FULL, NVT>(ub, sV, rA, lane);
+    if (nc > 0) ub_tile<KIND, NVT>(ub, sV, rA, lane);
     PendingOut<NVT> pd;
     pd.row0 = bos;
     pd.len = 0;
     int c = 0;
     for (; c + 3 <= nc; c += 3) {
-      helper_step(ctx, rA, rB, rC, c, pd, E, ub, sUb);
-      helper_step(ctx, rB, rC, rA, c + 1, pd, E, ub, sUb);
-      helper_step(ctx, rC, rA, rB, c + 2, pd, E, ub, sUb);
+      helper_step<KIND>(ctx, rA, rB, rC, c, pd, E, ub, sUb);
+      helper_step<KIND>(ctx, rB, rC, rA, c + 1, pd, E, ub, sUb);
+      helper_step<KIND>(ctx, rC, rA, rB, c + 2, pd, E, ub, sUb);
     }
-    if (c < nc) helper_step(ctx, rA, rB, rC, c, pd, E, ub, sUb);
-    if (c + 1 < nc) helper_step(ctx, rB, rC, rA, c + 1, pd, E, ub, sUb);
-    store_pending(pd, out, Hv, h, v0, wave, li, lg);
+    if (c < nc) helper_step<KIND>(ctx, rA, rB, rC, c, pd, E, ub, sUb);
+    if (c + 1 < nc) helper_step<KIND>(ctx, rB, rC, rA, c + 1, pd, E, ub, sUb);
+    if constexpr (KIND == ST_FULL) store_pending(pd, out, Hv, h, v0, wave, li, lg);
   }
 }
 
@@ -2468,8 +2496,8 @@ void launch_state_kind(const StateArgs& a, int64_t jobs, hipStream_t st) {
   const int64_t narrow_rounds = (jobs * NSLICE + kGpuCUs - 1) / kGpuCUs;
   const int64_t wide_rounds = (jobs * (NSLICE / 2) + kGpuCUs - 1) / kGpuCUs;
   if (wide_rounds * kWideStepPct >= narrow_rounds * 100) {
-    if constexpr (KIND == ST_FULL)
-      hipLaunchKernelGGL(kda_state_split_kernel, dim3((unsigned)(((jobs + 7) / 8) * 8 * NSLICE)),
+    if constexpr (KIND == ST_FULL || KIND == ST_CARRY)
+      hipLaunchKernelGGL(kda_state_split_kernel<KIND>, dim3((unsigned)(((jobs + 7) / 8) * 8 * NSLICE)),
                          dim3(64 * SPWAVES), 0, st, a.v, a.cu, a.chunk_off, a.h0, a.hT, a.out, a.ws, a.seg, a.T, a.N,
                          a.Hv, a.mc, a.init_dtype, a.final_dtype, a.nseg, a.seg_len, a.scale);
     else
