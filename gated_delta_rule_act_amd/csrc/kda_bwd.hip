@@ -295,12 +295,13 @@ template <int NTH>
 struct ChunkRaw {
   static constexpr int TPR = NTH / CH, CPT = DK / TPR;  // threads per row, channels per thread
   stage_u4 q[CPT / 8], k[CPT / 8], g[CPT / 8];
+  stage_f4 db[CPT / 4];  // dt_bias of the thread's channels (zero when absent)
   uint32_t b;  // beta of the row (bf16 bits)
 };
 template <int NTH>
 __device__ __forceinline__ void fetch_chunk_raw(ChunkRaw<NTH>& raw, const uint16_t* q, const uint16_t* k,
-                                                const uint16_t* g, const uint16_t* beta, int Hqk, int Hv, int h, int hq,
-                                                int64_t row0, int len, int tid) {
+                                                const uint16_t* g, const uint16_t* beta, const float* dt_bias, int Hqk,
+                                                int Hv, int h, int hq, int64_t row0, int len, int tid) {
   constexpr int TPR = ChunkRaw<NTH>::TPR, CPT = ChunkRaw<NTH>::CPT;
   const int r = tid / TPR, c0 = CPT * (tid % TPR);
   // range-checked buffer loads over the chunk's rows: rows >= len read as
@@ -317,13 +318,19 @@ __device__ __forceinline__ void fetch_chunk_raw(ChunkRaw<NTH>& raw, const uint16
     raw.g[i / 8] = __builtin_bit_cast(stage_u4, __builtin_amdgcn_raw_buffer_load_b128(bg, og, 0, 0));
   }
   raw.b = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(bb, (uint32_t)(r * Hv) * 2, 0, 0);
+  // dt_bias through a buffer of size 0 when absent: zeros, and no branch (a
+  // conditional load became a branch with a full wait after it, per load)
+  const __amdgpu_buffer_rsrc_t bd =
+      buffer_rsrc(dt_bias ? dt_bias + (size_t)h * DK : dt_bias, dt_bias ? (uint32_t)DK * 4 : 0u);
+#pragma unroll
+  for (int i = 0; i < CPT; i += 4)
+    raw.db[i / 4] = __builtin_bit_cast(stage_f4, __builtin_amdgcn_raw_buffer_load_b128(bd, (uint32_t)(c0 + i) * 4, 0, 0));
 }
 
 template <int MODE, int NTH>
 __device__ __forceinline__ void process_chunk_inputs(const ChunkRaw<NTH>& raw, float* sK, float* sQ, float* sG,
-                                                     float* sBt, float* sB, const float* A_log, const float* dt_bias,
-                                                     int h, int len, float lb, int flags, int tid, float* rq_out,
-                                                     float* rk_out) {
+                                                     float* sBt, float* sB, const float* A_log, int h, int len,
+                                                     float lb, int flags, int tid, float* rq_out, float* rk_out) {
   constexpr int TPR = ChunkRaw<NTH>::TPR, CPT = ChunkRaw<NTH>::CPT;
   const int r = tid / TPR, c0 = CPT * (tid % TPR);
   const bool ok = r < len;
@@ -356,9 +363,7 @@ __device__ __forceinline__ void process_chunk_inputs(const ChunkRaw<NTH>& raw, f
 #pragma unroll
   for (int i = 0; i < CPT; i += 4) {
     float g4[4];
-    const float4 db4 = dt_bias ? *reinterpret_cast<const float4*>(dt_bias + (size_t)h * DK + c0 + i)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float db[4] = {db4.x, db4.y, db4.z, db4.w};
+    const float db[4] = {raw.db[i / 4][0], raw.db[i / 4][1], raw.db[i / 4][2], raw.db[i / 4][3]};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       // every row's gate (zero inputs past the end, finite), then the select:
@@ -407,8 +412,8 @@ __device__ __forceinline__ void load_chunk_inputs(float* sK, float* sQ, float* s
                                                   int hq, int64_t row0, int len, float lb, int flags,
                                                   int tid, float* rq_out, float* rk_out) {
   ChunkRaw<NTH> raw;
-  fetch_chunk_raw<NTH>(raw, q, k, g, beta, Hqk, Hv, h, hq, row0, len, tid);
-  process_chunk_inputs<MODE, NTH>(raw, sK, sQ, sG, sBt, sB, A_log, dt_bias, h, len, lb, flags, tid, rq_out, rk_out);
+  fetch_chunk_raw<NTH>(raw, q, k, g, beta, dt_bias, Hqk, Hv, h, hq, row0, len, tid);
+  process_chunk_inputs<MODE, NTH>(raw, sK, sQ, sG, sBt, sB, A_log, h, len, lb, flags, tid, rq_out, rk_out);
 }
 
 // Exponents from the block-local form (log2 units):
@@ -583,7 +588,7 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   auto fetch = [&](int id) {
     const int x2 = id % mc, h2 = id / mc;
     const ChunkLoc L2 = chunk_loc(x2, cu, chunk_off, T, N);
-    fetch_chunk_raw<PREP_THREADS>(raw, q, k, g, beta, Hqk, Hv, h2, h2 / (Hv / Hqk), L2.row0, L2.len, tid0);
+    fetch_chunk_raw<PREP_THREADS>(raw, q, k, g, beta, dt_bias, Hqk, Hv, h2, h2 / (Hv / Hqk), L2.row0, L2.len, tid0);
     fetch_bf16_tile128<PREP_THREADS>(rawv, v + ((size_t)L2.row0 * Hv + h2) * DV, (size_t)Hv * DV, L2.len, tid0);
   };
   if ((int)blockIdx.x < total) fetch(blockIdx.x);
@@ -604,7 +609,7 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   float* pb = ws + ((size_t)h * mc + x) * CHUNK_HEAD_FLOATS;
 
   for (int e = tid; e < CH * QS; e += PREP_THREADS) { sA[e] = 0.0f; sAq[e] = 0.0f; sT[e] = 0.0f; }
-  process_chunk_inputs<MODE, PREP_THREADS>(raw, sK, sQ, sG, sBt, sB, A_log, dt_bias, h, L.len, lb, flags, tid, nullptr,
+  process_chunk_inputs<MODE, PREP_THREADS>(raw, sK, sQ, sG, sBt, sB, A_log, h, L.len, lb, flags, tid, nullptr,
                                            nullptr);
   stage_u4 vcur[1024 / PREP_THREADS];  // this chunk's V, kept until it goes to LDS
 #pragma unroll
@@ -937,19 +942,31 @@ __device__ __forceinline__ void slice_identity(f32x4 (&S)[2][1], int v0, int w, 
     for (int r = 0; r < 4; ++r) S[m][0][r] = v0 + 16 * m + 4 * lg + r == 16 * w + li ? 1.0f : 0.0f;
 }
 
-// the slice of a [128][128] matrix: fp32, bf16, or zero (KDA_STATE_NONE / NULL)
+// the slice of a [128][128] matrix: fp32, bf16, or zero (KDA_STATE_NONE / NULL).
+// Range-checked loads under one branch on the (uniform) dtype: an absent
+// matrix is a buffer of size 0 and reads zeros (conditional loads per element
+// became a branch with a full wait after each)
 __device__ __forceinline__ void slice_from_global(f32x4 (&S)[2][1], const void* g, int dtype, int v0, int w, int li,
                                                   int lg) {
+  const bool f32 = g != nullptr && dtype == KDA_STATE_F32, b16 = g != nullptr && dtype == KDA_STATE_BF16;
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(g, f32 ? (uint32_t)DV * DK * 4 : b16 ? (uint32_t)DV * DK * 2 : 0u);
+  if (b16) {
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const size_t e = (size_t)(v0 + 16 * m + 4 * lg + r) * DK + 16 * w + li;
-      float x = 0.0f;
-      if (g != nullptr && dtype == KDA_STATE_F32) x = reinterpret_cast<const float*>(g)[e];
-      else if (g != nullptr && dtype == KDA_STATE_BF16) x = bf2f(reinterpret_cast<const uint16_t*>(g)[e]);
-      S[m][0][r] = x;
-    }
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t e = (uint32_t)(v0 + 16 * m + 4 * lg + r) * DK + 16 * w + li;
+        S[m][0][r] = bf2f((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, e * 2, 0, 0));
+      }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t e = (uint32_t)(v0 + 16 * m + 4 * lg + r) * DK + 16 * w + li;
+        S[m][0][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, e * 4, 0, 0));
+      }
+  }
 }
 
 // Entry slice of a job; `entry` is the chain's true entry matrix.
