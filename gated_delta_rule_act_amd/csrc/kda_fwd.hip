@@ -1201,6 +1201,39 @@ __device__ __forceinline__ void ub_tile(f32x4 (&u)[NVT], const _Float16* sVb, co
   for (int vt = 0; vt < NVT; ++vt) ub_one<KIND, NVT>(u[vt], sVb, r, vt, lane);
 }
 
+// Entry tiles S^T[k][v] (k = 32 wave + 16 j + 4 lg + rr, v = v0 + 16 vt + li)
+// of a [V][K] state matrix at `src` + `base` elements: fp32, bf16, or zero
+// (KDA_STATE_NONE).  Range-checked loads under one branch on the uniform
+// dtype, where a conditional load per tile became a branch with a full memory
+// wait after each.
+template <int NVT>
+__device__ __forceinline__ void load_entry_tiles(f32x4 (&S)[2][NVT], const void* src, int dtype, size_t base, int wave,
+                                                 int v0, int li, int lg) {
+  const bool f32 = dtype == KDA_STATE_F32, b16 = dtype == KDA_STATE_BF16;
+  const void* b = f32 ? (const void*)(reinterpret_cast<const float*>(src) + base)
+                      : b16 ? (const void*)(reinterpret_cast<const uint16_t*>(src) + base) : nullptr;
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(b, f32 ? (uint32_t)DV * DK * 4 : b16 ? (uint32_t)DV * DK * 2 : 0u);
+  if (b16) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) {
+        const uint32_t e = (uint32_t)(v0 + 16 * vt + li) * DK + 32 * wave + 16 * j + 4 * lg;
+        const u32x2 u = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, e * 2, 0, 0));
+        S[j][vt] = f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+                         __uint_as_float(u[1] & 0xffff0000u)};
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt) {
+        const uint32_t e = (uint32_t)(v0 + 16 * vt + li) * DK + 32 * wave + 16 * j + 4 * lg;
+        S[j][vt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, e * 4, 0, 0));
+      }
+  }
+}
+
 // One chunk of the state chain: `cur` holds chunk c, `n1` receives the key-tile
 // operands of chunk c+1, `n2` the token-tile operands of chunk c+2.  The wide
 // slices (NVT = 4) have no registers for that depth: their token-tile
@@ -1464,26 +1497,18 @@ kda_state_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict__ cu,
     src = seg_mat(seg, chains, nseg, SEG_SIN, chain, r); src_dtype = KDA_STATE_F32;
   }
   f32x4 S[2][NVT];
+  if constexpr (KIND != ST_TRANS) load_entry_tiles<NVT>(S, src, src_dtype, src_base, wave, v0, li, lg);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int vt = 0; vt < NVT; ++vt) {
       const int kk = 32 * wave + 16 * j + 4 * lg, vv = v0 + 16 * vt + li;
-      f32x4 st = f32x4{0, 0, 0, 0};
       if constexpr (KIND == ST_TRANS) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) st[rr] = kk + rr == vv ? 1.0f : 0.0f;
-      } else if (src_dtype == KDA_STATE_F32) {
-        st = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(src) + src_base + (size_t)vv * DK + kk);
-      } else if (src_dtype == KDA_STATE_BF16) {
-        const uint2 u =
-            *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + src_base + (size_t)vv * DK + kk);
-        st = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                   __uint_as_float(u.y & 0xffff0000u)};
+        for (int rr = 0; rr < 4; ++rr) S[j][vt][rr] = kk + rr == vv ? 1.0f : 0.0f;
       }
-      S[j][vt] = st;
       if (KIND == ST_CARRY && r == 0)
-        *reinterpret_cast<f32x4*>(seg_mat(seg, chains, nseg, SEG_SIN, chain, 0) + (size_t)vv * DK + kk) = st;
+        *reinterpret_cast<f32x4*>(seg_mat(seg, chains, nseg, SEG_SIN, chain, 0) + (size_t)vv * DK + kk) = S[j][vt];
     }
 
   const uint8_t* wsh = ws + (size_t)h * max_chunks * BLOCK;
@@ -1884,24 +1909,15 @@ kda_state_split_kernel(const uint16_t* __restrict__ v, const int64_t* __restrict
       src = seg_mat(seg, chains, nseg, SEG_SIN, chain, r); src_dtype = KDA_STATE_F32;
     }
     f32x4 S[2][NVT];
+    load_entry_tiles<NVT>(S, src, src_dtype, src_base, wave, v0, li, lg);
+    if (KIND == ST_CARRY && r == 0)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) {
-        const int kk = 32 * wave + 16 * j + 4 * lg, vv = v0 + 16 * vt + li;
-        f32x4 st = f32x4{0, 0, 0, 0};
-        if (src_dtype == KDA_STATE_F32) {
-          st = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(src) + src_base + (size_t)vv * DK + kk);
-        } else if (src_dtype == KDA_STATE_BF16) {
-          const uint2 u =
-              *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + src_base + (size_t)vv * DK + kk);
-          st = f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
-                     __uint_as_float(u.y & 0xffff0000u)};
+        for (int vt = 0; vt < NVT; ++vt) {
+          const int kk = 32 * wave + 16 * j + 4 * lg, vv = v0 + 16 * vt + li;
+          *reinterpret_cast<f32x4*>(seg_mat(seg, chains, nseg, SEG_SIN, chain, 0) + (size_t)vv * DK + kk) = S[j][vt];
         }
-        S[j][vt] = st;
-        if (KIND == ST_CARRY && r == 0)
-          *reinterpret_cast<f32x4*>(seg_mat(seg, chains, nseg, SEG_SIN, chain, 0) + (size_t)vv * DK + kk) = st;
-      }
     ChunkRegs rA, rB, rC;
     if (nc > 0) {
       const uint8_t* b0 = wsh + (size_t)x0 * BLOCK;
