@@ -64,6 +64,19 @@ def profiled_traffic(kernel, workload_name):
     return profile_figure("traffic", kernel, workload_name, "hbm_bytes_per_launch")
 
 
+def kernel_names(inp, nseg):
+    """The kernels a chunked forward of this workload runs: the intra kernel, and
+    the state pass's kernel as the library picks it (32-column slices on the
+    split chain/helper kernel when a 64-column launch would not take fewer
+    rounds of 256 workgroups weighted by its 1.85 x step time, else 64-column
+    slices on the 4-wave kernel)."""
+    jobs = inp.N * inp.Hv * nseg
+    narrow_rounds = (jobs * 4 + 255) // 256
+    wide_rounds = (jobs * 2 + 255) // 256
+    narrow = wide_rounds * 185 >= narrow_rounds * 100
+    return {"intra": "kda_intra_kernel", "state": "kda_state_split_kernel" if narrow else "kda_state_kernel"}
+
+
 def bytes_model(inp):
     """Algorithmic HBM bytes: the method's minimum per token-head (q, k per qk-head
     and v, g, out at 256 B each, beta 2 B; states once per (sequence, v-head)),
@@ -276,7 +289,8 @@ def main():
     bm = bytes_model(inp)
     kern = {"intra": t_intra, "state": t_state}
     dom = max(kern, key=kern.get)
-    kname = f"kda_{dom}_kernel"
+    names = kernel_names(inp, nseg)
+    kname = names[dom]
     achieved = bm[dom] / (kern[dom] * 1e-3) / 1e9
     traffic = profiled_traffic(kname, inp.name)
     path_gbps = bm["path"] / (ms_per_step * 1e-3) / 1e9
@@ -284,9 +298,9 @@ def main():
     counters = {}
     for k in ("intra", "state"):
         for fig in ("mfma_busy_pct", "valu_busy_pct", "wait_pct"):
-            v = profile_figure("counters", f"kda_{k}_kernel", inp.name, fig)
+            v = profile_figure("counters", names[k], inp.name, fig)
             if v is not None:
-                counters[f"kda_{k}_kernel.{fig}"] = v
+                counters[f"{names[k]}.{fig}"] = v
 
     rec = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -307,7 +321,7 @@ def main():
                      "workspace_bytes_per_launch": bm["workspace"],
                      "traffic_over_algorithmic": None if traffic is None else traffic / bm[dom],
                      "avg_launch_ms": kern[dom]},
-        "kernels_ms": {"kda_intra_kernel": t_intra, "kda_state_kernel": t_state},
+        "kernels_ms": {names["intra"]: t_intra, names["state"]: t_state},
         "step_ms": {"mean": ms_per_step, "median": statistics.median(step_ms), "min": min(step_ms),
                     "max": max(step_ms)},
         "sustained": None if not sus_tail else {
