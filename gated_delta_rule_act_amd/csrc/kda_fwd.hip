@@ -94,11 +94,11 @@ constexpr int F_TBL = 38;     //           lo
 constexpr int F_AQK = 44;     // scale (Q K^T . 2^(G_t - G_s)), lower incl. diagonal (ta, kb 0..1) fp16
 constexpr int F_VEC = 50;     // 2^G_last f32[128] (the rest of the fragment is unused)
 constexpr int F_KD = 51;      // (K . 2^(G_last - G))^T hi (km 0..7, kb 0..1) fp16 rows k, columns t
-constexpr int F_KDL = 67;     // its low part, 16 half fragments of 512 B (8 B per lane, same order):
-                              // e4m3 of (Kd - hi) 2^18
+constexpr int F_KDL = 67;     // its low part, e4m3 of (Kd - hi) 2^18, 8 B per lane and fragment;
+                              // the two token blocks of key tile km share fragment F_KDL + km,
+                              // lane l holding kb 0 at 16 l and kb 1 at 16 l + 8 (one 16-byte load)
                               // (fragments 0..50 are shared by all V slices of a chain)
 constexpr int NFRAG = 75;
-constexpr int HFRAG = 512;
 // Q and K here are the normalised q and k (with the L2 norm on, every element
 // is at most 1 in size), so no operand depends on the scale of the raw inputs.
 // Kd = hi + lo with hi = fp16(Kd) and |lo| <= ulp(hi) / 2 <= 2^-12 for |Kd| <= 1.
@@ -128,13 +128,14 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ void st_frag(uint8_t* blk, int fr, int lane, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(blk + fr * FRAG + lane * 16));
 }
+// 8 bytes per lane at a 16-byte lane stride (two such halves share a fragment)
 __device__ __forceinline__ void st_half_frag(uint8_t* blk, int off, int lane, u32x2 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(blk + off + lane * 8));
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(blk + off + lane * 16));
 }
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef short short2v __attribute__((ext_vector_type(2)));
-// eight fp16 -> eight e4m3 bytes (rounded to nearest; the values are within
-// +-16, far from the e4m3 limit), in the same element order
+// eight fp16 -> eight e4m3 bytes (rounded to nearest; the caller has clamped
+// the values to the e4m3 range), in the same element order
 __device__ __forceinline__ u32x2 pack_e4m3(u32x4 f) {
   u32x2 r;
 #pragma unroll
@@ -796,7 +797,7 @@ kda_intra_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const int fr = wave + 4 * it;  // fragment (km = fr >> 1, kb = fr & 1)
       const u32x4 f = lds_frag_tr_grouped(sKd, KER, KEG, 32 * (fr & 1), 16 * (fr >> 1), lane);
       if (part == 0) st_frag(blk, F_KD + fr, lane, f);
-      else st_half_frag(blk, F_KDL * FRAG + fr * HFRAG, lane, pack_e4m3(f));
+      else st_half_frag(blk, (F_KDL + (fr >> 1)) * FRAG + 8 * (fr & 1), lane, pack_e4m3(f));
     }
     __syncthreads();
   }
@@ -1063,14 +1064,14 @@ __device__ __forceinline__ void load_chunk_part(ChunkRegs& o, const uint8_t* blk
     load_v<NVT>(o, v, row0, len, Hv, h, v0, tid);
   if constexpr (PART == 1) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int fr = (2 * wave + j) * 2 + b;
-        o.kd[j][b] = ld_frag(blk, F_KD + fr, lane);
-        o.kdl[j][b] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(buffer_rsrc(blk, (uint32_t)BLOCK), F_KDL * FRAG + fr * HFRAG + lane * 8, 0, 0));
-      }
+      for (int b = 0; b < 2; ++b) o.kd[j][b] = ld_frag(blk, F_KD + (2 * wave + j) * 2 + b, lane);
+      // both token blocks' low parts in one load
+      const u32x4 lo = ld_frag(blk, F_KDL + 2 * wave + j, lane);
+      o.kdl[j][0] = u32x2{lo[0], lo[1]};
+      o.kdl[j][1] = u32x2{lo[2], lo[3]};
+    }
   }
 }
 
