@@ -521,6 +521,100 @@ __device__ __forceinline__ void mfma_block(f32x4 (&acc)[MT][NT], const float* sA
   }
 }
 
+// Pre-split operands.  A tile that several waves read as split-bf16 MFMA
+// operands is stored once as two bf16 tiles, hi = bf16(x) and lo = bf16(x -
+// hi) (the split of mfma_block), so that no reader splits it again.  Rows are
+// kept in groups of 8 (row stride ld, group stride gs, in elements).  A tile
+// read down its columns (the transposing LDS read) takes ld = 144 (or 48 for
+// 32 columns) and a 64-element gap between groups, so that the lane groups of
+// one read fall on different banks; a tile read only along its rows takes
+// ld = 136 and no gap.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+struct PsTile {
+  __bf16* hi;
+  __bf16* lo;
+  int ld, gs;
+  __device__ __forceinline__ int row(int r) const { return (r & 7) * ld + (r >> 3) * gs; }
+};
+constexpr int PS_ROW_LD = 136;                    // tiles read along rows
+constexpr int PS_COL_LD = 144, PS_COL_GS = 8 * PS_COL_LD + 64;  // 128-column tiles read down columns
+constexpr int PS_C32_LD = 48, PS_C32_GS = 8 * PS_C32_LD + 64;   // 32-column tiles read down columns
+
+__device__ __forceinline__ void ps_put1(const PsTile& t, int r, int c, float x) {
+  const __bf16 h = (__bf16)x;
+  t.hi[t.row(r) + c] = h;
+  t.lo[t.row(r) + c] = (__bf16)(x - (float)h);
+}
+// four consecutive values of row r from column c (a multiple of 4)
+__device__ __forceinline__ void ps_put4(const PsTile& t, int r, int c, const stage_f4& x) {
+  bf16x4_t h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = (__bf16)x[e];
+    l[e] = (__bf16)(x[e] - (float)h[e]);
+  }
+  *reinterpret_cast<bf16x4_t*>(t.hi + t.row(r) + c) = h;
+  *reinterpret_cast<bf16x4_t*>(t.lo + t.row(r) + c) = l;
+}
+// a fetched 64 x 128 fp32 tile (fetch_tile128's thread layout) into a split tile
+template <int NTH>
+__device__ __forceinline__ void put_ps_tile128(const PsTile& t, const stage_f4 (&r4)[2048 / NTH], int tid) {
+#pragma unroll
+  for (int i = 0; i < 2048 / NTH; ++i) {
+    const int e = tid + NTH * i;
+    ps_put4(t, e >> 5, 4 * (e & 31), r4[i]);
+  }
+}
+
+// acc[m][n] += the (16 m, 16 n) tile of A B over k < kdim (a multiple of 32)
+// from split tiles, A(r, k) = AT ? tA[k][r] : tA[r][k] and B(k, c) = BT ?
+// tB[c][k] : tB[k][c]: lane (li, g) feeds A[li][8 g .. +7] and B[8 g .. +7][li],
+// read along a row (16 bytes per half) or down a column (transposing reads),
+// and the three products of mfma_block.
+template <bool AT, bool BT, int MT, int NT>
+__device__ __forceinline__ void mfma_block_ps(f32x4 (&acc)[MT][NT], const PsTile& A, const PsTile& B, int row0,
+                                              int col0, int kdim, int lane) {
+  const int li = lane & 15, g = lane >> 4;
+#pragma unroll 2
+  for (int k0 = 0; k0 < kdim; k0 += 32) {
+    bf16x8_t ah[MT], al[MT], bh[NT], bl[NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if constexpr (AT) {
+        ah[m] = __builtin_bit_cast(bf16x8_t, lds_frag_tr_grouped(A.hi, A.ld, A.gs, k0, row0 + 16 * m, lane));
+        al[m] = __builtin_bit_cast(bf16x8_t, lds_frag_tr_grouped(A.lo, A.ld, A.gs, k0, row0 + 16 * m, lane));
+      } else {
+        const int o = A.row(row0 + 16 * m + li) + k0 + 8 * g;
+        ah[m] = *reinterpret_cast<const bf16x8_t*>(A.hi + o);
+        al[m] = *reinterpret_cast<const bf16x8_t*>(A.lo + o);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if constexpr (BT) {
+        const int o = B.row(col0 + 16 * n + li) + k0 + 8 * g;
+        bh[n] = *reinterpret_cast<const bf16x8_t*>(B.hi + o);
+        bl[n] = *reinterpret_cast<const bf16x8_t*>(B.lo + o);
+      } else {
+        bh[n] = __builtin_bit_cast(bf16x8_t, lds_frag_tr_grouped(B.hi, B.ld, B.gs, k0, col0 + 16 * n, lane));
+        bl[n] = __builtin_bit_cast(bf16x8_t, lds_frag_tr_grouped(B.lo, B.ld, B.gs, k0, col0 + 16 * n, lane));
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bh[n], acc[m][n], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bl[n], acc[m][n], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[m], bh[n], acc[m][n], 0, 0, 0);
+  }
+}
+
 // The same product on the fp32 MFMA (16x16x4): lane (li, lg) feeds
 // A[li][k + lg] and B[k + lg][li] for each 4-wide k step.  Used where the
 // operands are read across rows only and the chain of products is short.
@@ -1031,10 +1125,14 @@ __global__ void __launch_bounds__(STATE_THREADS)
 kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ chunk_off, const void* __restrict__ h0,
                       int init_dtype, int T, int N, int Hv, int mc, float* __restrict__ ws, float* __restrict__ seg,
                       int nseg, int seg_len) {
-  __shared__ __attribute__((aligned(16))) float sW[CH * RS];
-  __shared__ __attribute__((aligned(16))) float sKd[CH * RS];
-  __shared__ __attribute__((aligned(16))) float sU[CH * SV];
-  __shared__ __attribute__((aligned(16))) float sS[BV * RS];
+  // pre-split operand tiles: W and the state slice read along rows, U and Kd
+  // down columns
+  __shared__ __attribute__((aligned(16))) __bf16 sWh[CH * PS_ROW_LD], sWl[CH * PS_ROW_LD];
+  __shared__ __attribute__((aligned(16))) __bf16 sKdh[CH / 8 * PS_COL_GS], sKdl[CH / 8 * PS_COL_GS];
+  __shared__ __attribute__((aligned(16))) __bf16 sUh[CH / 8 * PS_C32_GS], sUl[CH / 8 * PS_C32_GS];
+  __shared__ __attribute__((aligned(16))) __bf16 sSh[BV * PS_ROW_LD], sSl[BV * PS_ROW_LD];
+  const PsTile tW{sWh, sWl, PS_ROW_LD, 8 * PS_ROW_LD}, tKd{sKdh, sKdl, PS_COL_LD, PS_COL_GS};
+  const PsTile tU{sUh, sUl, PS_C32_LD, PS_C32_GS}, tS{sSh, sSl, PS_ROW_LD, 8 * PS_ROW_LD};
   StateJob j;
   if (!state_job<KIND>(blockIdx.x, cu, chunk_off, T, N, Hv, nseg, seg_len, false, j)) return;
   const int chains = N * Hv, h = j.h, v0 = j.v0, tid = threadIdx.x;
@@ -1068,28 +1166,32 @@ kda_bwd_fstate_kernel(const int64_t* __restrict__ cu, const int* __restrict__ ch
     const float* pb = ws + ((size_t)h * mc + j.x0 + c) * CHUNK_HEAD_FLOATS;
     float* sb = const_cast<float*>(pb) + PB_FLOATS;
     if constexpr (KIND == ST_FULL) slice_to_global(S, sb + SB_H, v0, w, li, lg);
-    slice_to_lds(S, sS, w, li, lg);
-    put_tile128(sW, fW, tid);
-    put_tile128(sKd, fKd, tid);
+    // the state slice S[v][k] (v = 16 m + 4 lg + r, k = 16 w + li)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ps_put1(tS, 16 * m + 4 * lg + r, 16 * w + li, S[m][0][r]);
+    put_ps_tile128<STATE_THREADS>(tW, fW, tid);
+    put_ps_tile128<STATE_THREADS>(tKd, fKd, tid);
     f32x4 U[1][1];
     U[0][0] = -fUb;
     const float gn = fgn;
     fetch(min(c + 1, j.c1 - 1));
     __syncthreads();
     // -U = W S^T - Ubar:  A(t, k) = W[t][k],  B(k, v) = S[v][k]
-    mfma_block<false, true, 1, 1>(U, sW + ut * RS, RS, sS, RS, 0, uv, DK, lane);
+    mfma_block_ps<false, true, 1, 1>(U, tW, tS, ut, uv, DK, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = ut + 4 * lg + r, vv = uv + li;
       const float u = -U[0][0][r];
-      sU[t * SV + vv] = u;
+      ps_put1(tU, t, vv, u);
       if constexpr (KIND == ST_FULL) sb[SB_U + t * DV + v0 + vv] = u;
     }
     __syncthreads();
     // S <- S Diag(gn) + U^T Kd:  A(v, t) = U[t][v],  B(t, k) = Kd[t][k]
 #pragma unroll
     for (int m = 0; m < 2; ++m) S[m][0] *= gn;
-    mfma_block<true, false, 2, 1>(S, sU, SV, sKd, RS, 0, 16 * w, CH, lane);
+    mfma_block_ps<true, false, 2, 1>(S, tU, tKd, 0, 16 * w, CH, lane);
     __syncthreads();
   }
   if constexpr (KIND != ST_FULL) slice_to_global(S, job_exit<KIND>(seg, chains, nseg, j), v0, w, li, lg);

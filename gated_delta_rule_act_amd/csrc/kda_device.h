@@ -22,5 +22,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
                                            __builtin_amdgcn_readfirstlane((int)bytes), kBufferWord3);
 }
 
+
+typedef uint32_t kd_u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t kd_u32x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes
+// the 16 addresses are read as a 16 x 4 block M[s][e] of 16-bit values (4 at
+// each address) and lane i receives M[4e + (i >> 2)][i & 3], e = 0..3.
+template <typename T>
+__device__ __forceinline__ kd_u32x2 lds_read_tr16(const T* p) {
+  static_assert(sizeof(T) == 2, "16-bit elements");
+  typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_t;
+  auto lp = (__attribute__((address_space(3))) fp16x4_t*)(p);
+  return __builtin_bit_cast(kd_u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16(lp));
+}
+
+// One 16 x 32 MFMA operand fragment with the contraction index contiguous per
+// lane, read from a row-major [k][n] tile of 16-bit values whose rows are kept
+// in groups of 8 (row stride ld within a group, group stride gs; k0 a
+// multiple of 8): lane (i, g) receives column n0 + i, rows k0 + 8g .. k0 +
+// 8g + 7.  Source lane s of a group points at row k0 + 8g + (s >> 2),
+// columns n0 + 4 (s & 3).
+template <typename T>
+__device__ __forceinline__ kd_u32x4 lds_frag_tr_grouped(const T* tile, int ld, int gs, int k0, int n0, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const T* p = tile + (k0 / 8 + g) * gs + (i >> 2) * ld + n0 + 4 * (i & 3);
+  const kd_u32x2 a = lds_read_tr16(p), b = lds_read_tr16(p + 4 * ld);
+  return kd_u32x4{a[0], a[1], b[0], b[1]};
+}
+
 }  // namespace
 }  // namespace kda_device

@@ -400,27 +400,7 @@ __device__ __forceinline__ void diag_level(const float (&Gk)[8], const float (&k
   aqk = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aq, Bc, aqk, 0, 0, 0);
 }
 
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes
-// the 16 addresses are read as a 16 x 4 block M[s][e] of 16-bit values (4 at
-// each address) and lane i receives M[4e + (i >> 2)][i & 3], e = 0..3.
-__device__ __forceinline__ u32x2 lds_read_tr16(const _Float16* p) {
-  typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_t;
-  auto lp = (__attribute__((address_space(3))) fp16x4_t*)(p);
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16(lp));
-}
-
-// One 16 x 32 MFMA operand fragment with the contraction index contiguous per
-// lane, read from a row-major [k][n] tile of 16-bit values whose rows are kept
-// in groups of 8 (row stride ld within a group, group stride gs; k0 a
-// multiple of 8): lane (i, g) receives column n0 + i, rows k0 + 8g .. k0 +
-// 8g + 7.  Source lane s of a group points at row k0 + 8g + (s >> 2),
-// columns n0 + 4 (s & 3).
-__device__ __forceinline__ u32x4 lds_frag_tr_grouped(const _Float16* tile, int ld, int gs, int k0, int n0, int lane) {
-  const int i = lane & 15, g = lane >> 4;
-  const _Float16* p = tile + (k0 / 8 + g) * gs + (i >> 2) * ld + n0 + 4 * (i & 3);
-  const u32x2 a = lds_read_tr16(p), b = lds_read_tr16(p + 4 * ld);
-  return u32x4{a[0], a[1], b[0], b[1]};
-}
+// (lds_read_tr16 and lds_frag_tr_grouped, the transposing LDS reads, are in kda_device.h)
 
 template <int MODE>
 __global__ void __launch_bounds__(256, 2)
