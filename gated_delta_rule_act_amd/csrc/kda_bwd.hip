@@ -539,6 +539,9 @@ struct PsTile {
 constexpr int PS_ROW_LD = 136;                    // tiles read along rows
 constexpr int PS_COL_LD = 144, PS_COL_GS = 8 * PS_COL_LD + 64;  // 128-column tiles read down columns
 constexpr int PS_C32_LD = 48, PS_C32_GS = 8 * PS_C32_LD + 64;   // 32-column tiles read down columns
+// 32-column tiles read down columns, unpadded: the four rows of a lane group
+// lie 16 banks apart and the next group of rows 8 banks further (64 banks)
+constexpr int PS_N32_LD = 32, PS_N32_GS = 8 * PS_N32_LD + 16;
 
 __device__ __forceinline__ void ps_put1(const PsTile& t, int r, int c, float x) {
   const __bf16 h = (__bf16)x;
@@ -600,6 +603,68 @@ __device__ __forceinline__ void mfma_block_ps(f32x4 (&acc)[MT][NT], const PsTile
         bl[n] = __builtin_bit_cast(bf16x8_t, lds_frag_tr_grouped(B.lo, B.ld, B.gs, k0, col0 + 16 * n, lane));
       }
     }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bh[n], acc[m][n], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[m], bl[n], acc[m][n], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[m], bh[n], acc[m][n], 0, 0, 0);
+  }
+}
+
+// Products with one operand pre-split and the other in fp32 (split as it is
+// read).  Every operand reader gives lane (li, g) the 8 consecutive k from
+// k0 + 8 g, so the two sides agree.  F32Tile: fp32 rows of stride ld.
+struct F32Tile {
+  const float* s;
+  int ld;
+};
+// A(r, k) or B^T(c, k) along a row (T = false) / down a column (T = true) of
+// the tile: the fragment for index x0 + li (row for T = false, column for T = true)
+template <bool T>
+__device__ __forceinline__ void opnd_frag(const F32Tile& t, int x0, int k0, int lane, bf16x8_t& hi, bf16x8_t& lo) {
+  const int li = lane & 15, g = lane >> 4;
+  float x[8];
+  if constexpr (!T) {
+    const float4 u0 = *reinterpret_cast<const float4*>(t.s + (x0 + li) * t.ld + k0 + 8 * g);
+    const float4 u1 = *reinterpret_cast<const float4*>(t.s + (x0 + li) * t.ld + k0 + 8 * g + 4);
+    x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w; x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = t.s[(k0 + 8 * g + e) * t.ld + x0 + li];
+  }
+  split8(x, hi, lo);
+}
+template <bool T>
+__device__ __forceinline__ void opnd_frag(const PsTile& t, int x0, int k0, int lane, bf16x8_t& hi, bf16x8_t& lo) {
+  if constexpr (!T) {
+    const int o = t.row(x0 + (lane & 15)) + k0 + 8 * (lane >> 4);
+    hi = *reinterpret_cast<const bf16x8_t*>(t.hi + o);
+    lo = *reinterpret_cast<const bf16x8_t*>(t.lo + o);
+  } else {
+    hi = __builtin_bit_cast(bf16x8_t, lds_frag_tr_grouped(t.hi, t.ld, t.gs, k0, x0, lane));
+    lo = __builtin_bit_cast(bf16x8_t, lds_frag_tr_grouped(t.lo, t.ld, t.gs, k0, x0, lane));
+  }
+}
+// acc[m][n] += the (16 m, 16 n) tile of A B over k < kdim (a multiple of 32):
+// A(r, k) = AT ? tA[k][r] : tA[r][k], B(k, c) = BT ? tB[c][k] : tB[k][c], each
+// tile fp32 (F32Tile) or pre-split (PsTile); the three products of mfma_block.
+template <bool AT, bool BT, int MT, int NT, class TA, class TB>
+__device__ __forceinline__ void mfma_block_mix(f32x4 (&acc)[MT][NT], const TA& A, const TB& B, int row0, int col0,
+                                               int kdim, int lane) {
+#pragma unroll 2
+  for (int k0 = 0; k0 < kdim; k0 += 32) {
+    bf16x8_t ah[MT], al[MT], bh[NT], bl[NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) opnd_frag<AT>(A, row0 + 16 * m, k0, lane, ah[m], al[m]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) opnd_frag<!BT>(B, col0 + 16 * n, k0, lane, bh[n], bl[n]);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -946,7 +1011,6 @@ kda_bwd_prep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 // 32 x 128 slice of the state (or of its gradient) lives in MFMA accumulator
 // layout: wave w (of 8) holds key columns 16 w .. +15 for all 32 rows,
 // element (v = 16 m + 4 lg + r, k = 16 w + li) in acc[m][0][r].
-constexpr int SV = 36;  // LDS row stride of 32-wide slices
 
 __device__ __forceinline__ void chain_chunks(int n, const int* chunk_off, const int64_t* cu, int T, int& x0, int& nc,
                                              int64_t& bos) {
@@ -964,12 +1028,6 @@ __device__ __forceinline__ void slice_to_global(const f32x4 (&S)[2][1], float* g
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int r = 0; r < 4; ++r) g[(size_t)(v0 + 16 * m + 4 * lg + r) * DK + 16 * w + li] = S[m][0][r];
-}
-__device__ __forceinline__ void slice_to_lds(const f32x4 (&S)[2][1], float* s, int w, int li, int lg) {
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s[(16 * m + 4 * lg + r) * RS + 16 * w + li] = S[m][0][r];
 }
 
 // XCD-aware decode: the BNS slices of one chain share (id mod 8), so they run
@@ -1228,9 +1286,14 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
   __shared__ __attribute__((aligned(16))) float sKd[CH * RS];
   __shared__ __attribute__((aligned(16))) float sQg[CH * RS];
   __shared__ __attribute__((aligned(16))) float sW[CH * RS];
-  __shared__ __attribute__((aligned(16))) float sdO[CH * SV];
-  __shared__ __attribute__((aligned(16))) float sdU[CH * SV];
-  __shared__ __attribute__((aligned(16))) float sdh[BV * RS];
+  // pre-split: dO and dU (every wave reads all of both) and the dS' slice
+  // (four waves read each part); the others are read by one or two waves
+  __shared__ __attribute__((aligned(16))) __bf16 sdOh[CH / 8 * PS_N32_GS], sdOl[CH / 8 * PS_N32_GS];
+  __shared__ __attribute__((aligned(16))) __bf16 sdUh[CH / 8 * PS_N32_GS], sdUl[CH / 8 * PS_N32_GS];
+  __shared__ __attribute__((aligned(16))) __bf16 sdhh[BV * PS_ROW_LD], sdhl[BV * PS_ROW_LD];
+  const PsTile tdO{sdOh, sdOl, PS_N32_LD, PS_N32_GS}, tdU{sdUh, sdUl, PS_N32_LD, PS_N32_GS};
+  const PsTile tdh{sdhh, sdhl, PS_ROW_LD, 8 * PS_ROW_LD};
+  const F32Tile tAq{sAq, QS}, tKd{sKd, RS}, tQg{sQg, RS}, tW{sW, RS};
   StateJob j;
   if (!state_job<KIND>(blockIdx.x, cu, chunk_off, T, N, Hv, nseg, seg_len, true, j)) return;
   const int chains = N * Hv, h = j.h, v0 = j.v0, tid = threadIdx.x;
@@ -1252,16 +1315,19 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
   for (int c = j.c1 - 1; c >= j.c0; --c) {
     float* sb = const_cast<float*>(pb0) + (size_t)c * CHUNK_HEAD_FLOATS + PB_FLOATS;
     if constexpr (KIND == ST_FULL) slice_to_global(D, sb + SB_DH, v0, w, li, lg);
-    slice_to_lds(D, sdh, w, li, lg);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ps_put1(tdh, 16 * m + 4 * lg + r, 16 * w + li, D[m][0][r]);
     put_tile128(sKd, b.kd, tid);
     put_tile128(sW, b.w, tid);
     if constexpr (KIND != ST_TRANS) {
       put_tile128(sQg, b.qg, tid);
       put_tile64(sAq, b.aq, tid);
       const int t = tid >> 3, jj = 4 * (tid & 7);
-      *reinterpret_cast<float4*>(sdO + t * SV + jj) =
-          make_float4(__uint_as_float(b.dO[0] << 16), __uint_as_float(b.dO[0] & 0xffff0000u),
-                      __uint_as_float(b.dO[1] << 16), __uint_as_float(b.dO[1] & 0xffff0000u));
+      ps_put4(tdO, t, jj,
+              stage_f4{__uint_as_float(b.dO[0] << 16), __uint_as_float(b.dO[0] & 0xffff0000u),
+                       __uint_as_float(b.dO[1] << 16), __uint_as_float(b.dO[1] & 0xffff0000u)});
     }
     const float gn = b.gn;
     __syncthreads();
@@ -1271,20 +1337,20 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
     // dU rows 16 w .. +15:  Aqk^T dO  +  Kd dS'^T  (a map job has dO = 0)
     f32x4 dU[1][1];
     zero_block(dU);
-    if constexpr (KIND != ST_TRANS) mfma_block<true, false, 1, 1>(dU, sAq + ut, QS, sdO, SV, 0, uv, CH, lane);
-    mfma_block<false, true, 1, 1>(dU, sKd + ut * RS, RS, sdh, RS, 0, uv, DK, lane);
+    if constexpr (KIND != ST_TRANS) mfma_block_mix<true, false, 1, 1>(dU, tAq, tdO, ut, uv, CH, lane);
+    mfma_block_mix<false, true, 1, 1>(dU, tKd, tdh, ut, uv, DK, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = ut + 4 * lg + r, vv = uv + li;
-      sdU[t * SV + vv] = -dU[0][0][r];
+      ps_put1(tdU, t, vv, -dU[0][0][r]);
       if constexpr (KIND == ST_FULL) sb[SB_DU + t * DV + v0 + vv] = dU[0][0][r];
     }
     __syncthreads();
     // dS = dS' Diag(gn) + dO^T Qg - dU^T W:  A(v, t) = dO[t][v] (then -dU[t][v])
 #pragma unroll
     for (int m = 0; m < 2; ++m) D[m][0] *= gn;
-    if constexpr (KIND != ST_TRANS) mfma_block<true, false, 2, 1>(D, sdO, SV, sQg, RS, 0, 16 * w, CH, lane);
-    mfma_block<true, false, 2, 1>(D, sdU, SV, sW, RS, 0, 16 * w, CH, lane);
+    if constexpr (KIND != ST_TRANS) mfma_block_mix<true, false, 2, 1>(D, tdO, tQg, 0, 16 * w, CH, lane);
+    mfma_block_mix<true, false, 2, 1>(D, tdU, tW, 0, 16 * w, CH, lane);
     __syncthreads();
   }
   if constexpr (KIND == ST_FULL) {
