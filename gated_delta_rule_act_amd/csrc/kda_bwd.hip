@@ -569,6 +569,29 @@ __device__ __forceinline__ void put_ps_tile128(const PsTile& t, const stage_f4 (
   }
 }
 
+// a 64 x 128 fp32 global tile (row stride gs floats) straight into a split tile
+template <int NTH>
+__device__ __forceinline__ void load_ps_tile128(const PsTile& t, const float* g, int gs, int tid) {
+#pragma unroll
+  for (int i = 0; i < 2048 / NTH; ++i) {
+    const int e = tid + NTH * i, r = e >> 5, c = 4 * (e & 31);
+    ps_put4(t, r, c, *reinterpret_cast<const stage_f4*>(g + (size_t)r * gs + c));
+  }
+}
+// 64 rows x 128 bf16 (row stride gs elements; rows >= len read as zero) into a
+// split tile: the values are bf16 already, so hi is the value and lo zero
+template <int NTH>
+__device__ __forceinline__ void load_ps_bf16_tile128(const PsTile& t, const uint16_t* g, size_t gs, int len, int tid) {
+  const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g, (uint32_t)((size_t)len * gs * 2));
+#pragma unroll
+  for (int i = 0; i < 1024 / NTH; ++i) {
+    const int e = tid + NTH * i, r = e >> 4, c = 8 * (e & 15);
+    const stage_u4 u = __builtin_bit_cast(stage_u4, __builtin_amdgcn_raw_buffer_load_b128(rg, (uint32_t)(r * gs + c) * 2, 0, 0));
+    *reinterpret_cast<stage_u4*>(t.hi + t.row(r) + c) = u;
+    *reinterpret_cast<stage_u4*>(t.lo + t.row(r) + c) = stage_u4{0u, 0u, 0u, 0u};
+  }
+}
+
 // acc[m][n] += the (16 m, 16 n) tile of A B over k < kdim (a multiple of 32)
 // from split tiles, A(r, k) = AT ? tA[k][r] : tA[r][k] and B(k, c) = BT ?
 // tB[c][k] : tB[k][c]: lane (li, g) feeds A[li][8 g .. +7] and B[8 g .. +7][li],
@@ -1371,12 +1394,18 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
                      const uint16_t* __restrict__ beta, const int64_t* __restrict__ cu,
                      const int* __restrict__ chunk_off, int T, int N, int Hv, int mc, int flags,
                      float* __restrict__ dv, float* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) float B0[CH * RS];
-  __shared__ __attribute__((aligned(16))) float B1[CH * RS];
+  // B0 (dO, then dS', then Kg) and B1 (dU) are read by the most waves and
+  // products: they are kept pre-split; B2, B3 and T stay fp32 (all five
+  // pre-split would not fit a CU's LDS)
+  __shared__ __attribute__((aligned(16))) __bf16 B0h[CH * PS_ROW_LD], B0l[CH * PS_ROW_LD];
+  __shared__ __attribute__((aligned(16))) __bf16 B1h[CH * PS_ROW_LD], B1l[CH * PS_ROW_LD];
   __shared__ __attribute__((aligned(16))) float B2[CH * RS];
   __shared__ __attribute__((aligned(16))) float B3[CH * RS];
   __shared__ __attribute__((aligned(16))) float sT[CH * QS];
   __shared__ float sB[CH];
+  const PsTile tB0{B0h, B0l, PS_ROW_LD, 8 * PS_ROW_LD}, tB1{B1h, B1l, PS_ROW_LD, 8 * PS_ROW_LD};
+  const PsTile tB0v{B0h + 64, B0l + 64, PS_ROW_LD, 8 * PS_ROW_LD}, tB1v{B1h + 64, B1l + 64, PS_ROW_LD, 8 * PS_ROW_LD};
+  const F32Tile fB2{B2, RS}, fB2v{B2 + 64, RS}, fB3{B3, RS}, fT{sT, QS};
   const int x = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const ChunkLoc L = chunk_loc(x, cu, chunk_off, T, N);
   if (L.len == 0) return;
@@ -1390,8 +1419,8 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   constexpr int NTH = DENSE_THREADS;
 
   // 1. dO, dU, U and the first half of S (rows v < 64)
-  load_bf16_tile128<NTH>(B0, d_out + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
-  load_tile128<NTH>(B1, sb + SB_DU, DV, tid);
+  load_ps_bf16_tile128<NTH>(tB0, d_out + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
+  load_ps_tile128<NTH>(tB1, sb + SB_DU, DV, tid);
   load_tile128<NTH>(B2, sb + SB_U, DV, tid);
   load_tile128<NTH>(B3, sb + SB_H, DK, tid);
   // Each later single-tile reload is fetched into registers one phase early
@@ -1406,14 +1435,14 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   f32x4 dqg[2][2], dw[2][2];
   zero_block(dqg);
   zero_block(dw);
-  mfma_block<false, false, 2, 2>(dqg, B0, RS, B3, RS, R0, C0, 64, lane);
-  mfma_block<false, false, 2, 2>(dw, B1, RS, B3, RS, R0, C0, 64, lane);
+  mfma_block_mix<false, false, 2, 2>(dqg, tB0, fB3, R0, C0, 64, lane);
+  mfma_block_mix<false, false, 2, 2>(dw, tB1, fB3, R0, C0, 64, lane);
   __syncthreads();
   put_tile128<NTH>(B3, pf, tid);
   fetch_tile128<NTH>(pf, sb + SB_DH + 64 * DK, DK, tid);  // dS' rows 64 .. 127, first in step 4
   __syncthreads();
-  mfma_block<false, false, 2, 2>(dqg, B0 + 64, RS, B3, RS, R0, C0, 64, lane);
-  mfma_block<false, false, 2, 2>(dw, B1 + 64, RS, B3, RS, R0, C0, 64, lane);
+  mfma_block_mix<false, false, 2, 2>(dqg, tB0v, fB3, R0, C0, 64, lane);
+  mfma_block_mix<false, false, 2, 2>(dw, tB1v, fB3, R0, C0, 64, lane);
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -1424,7 +1453,7 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   {
     f32x4 a[2][1];
     zero_block(a);
-    mfma_block<false, true, 2, 1>(a, B0, RS, B2, RS, R0, Q0, DV, lane);
+    mfma_block_mix<false, true, 2, 1>(a, tB0, fB2, R0, Q0, DV, lane);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -1436,37 +1465,35 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   __syncthreads();
   // 4. dKd = U dS', contracting over v in two halves; dgn = colsum(dS' . S).
   //    B0 is free since step 3 and B3 still holds the second half of S, so
-  //    dS' goes to B0, second half first: that half's column sums pair B0
-  //    with B3 in LDS, and only the first half of S is read again (into
-  //    registers, issued a phase early).  Thread (row group rg, 4 channels
-  //    c4) sums rows 4 rg .. +3 of each half.
+  //    dS' goes to B0, second half first.  The column sums take dS' from the
+  //    registers it is put from (B0 holds it split): thread (rows rb + 16 i,
+  //    channels c4) pairs the second half with S in B3, then the first half
+  //    with S's first half, read again into registers a phase early.
   stage_u4 pv[1024 / NTH];
   stage_f4 pt[1024 / NTH];
   {
-    const int rg = tid >> 5, c4 = 4 * (tid & 31);
+    const int rb = tid >> 5, c4 = 4 * (tid & 31);
     f32x4 dkd[2][2];
     zero_block(dkd);
-    put_tile128<NTH>(B0, pf, tid);  // dS' rows 64 .. 127
-    fetch_tile128<NTH>(pf, sb + SB_DH, DK, tid);
-    stage_f4 s1[4];  // S rows 4 rg .. +3 (first half), channels c4 .. +3
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s1[i] = *reinterpret_cast<const stage_f4*>(sb + SB_H + (4 * rg + i) * DK + c4);
-    __syncthreads();
-    mfma_block<false, false, 2, 2>(dkd, B2 + 64, RS, B0, RS, R0, C0, 64, lane);
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc += *reinterpret_cast<const f32x4*>(B0 + (4 * rg + i) * RS + c4) *
-             *reinterpret_cast<const f32x4*>(B3 + (4 * rg + i) * RS + c4);
+    for (int i = 0; i < 4; ++i) acc += pf[i] * *reinterpret_cast<const f32x4*>(B3 + (rb + 16 * i) * RS + c4);
+    put_ps_tile128<NTH>(tB0, pf, tid);  // dS' rows 64 .. 127
+    fetch_tile128<NTH>(pf, sb + SB_DH, DK, tid);
+    stage_f4 s1[4];  // S rows rb + 16 i (first half), channels c4 .. +3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s1[i] = *reinterpret_cast<const stage_f4*>(sb + SB_H + (rb + 16 * i) * DK + c4);
     __syncthreads();
-    put_tile128<NTH>(B0, pf, tid);  // dS' rows 0 .. 63
+    mfma_block_mix<false, false, 2, 2>(dkd, fB2v, tB0, R0, C0, 64, lane);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc += pf[i] * s1[i];
+    put_ps_tile128<NTH>(tB0, pf, tid);  // dS' rows 0 .. 63
     fetch_tile128<NTH>(pf, pb + PB_KG, DK, tid);
     fetch_bf16_tile128<NTH>(pv, v + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
     fetch_tile64<NTH>(pt, pb + PB_T, tid);
     __syncthreads();
-    mfma_block<false, false, 2, 2>(dkd, B2, RS, B0, RS, R0, C0, 64, lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc += *reinterpret_cast<const f32x4*>(B0 + (4 * rg + i) * RS + c4) * s1[i];
+    mfma_block_mix<false, false, 2, 2>(dkd, fB2, tB0, R0, C0, 64, lane);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -1474,7 +1501,7 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
 #pragma unroll
         for (int r = 0; r < 4; ++r) gb[GB_DKD + BLK_ROW(R0, m, r) * DK + BLK_COL(C0, n)] = dkd[m][n][r];
     // the 16 row groups meet in sT, free until step 5
-    *reinterpret_cast<f32x4*>(sT + rg * DK + c4) = acc;
+    *reinterpret_cast<f32x4*>(sT + rb * DK + c4) = acc;
   }
   __syncthreads();
   if (tid < DK) {
@@ -1491,7 +1518,7 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) B3[BLK_ROW(R0, m, r) * RS + BLK_COL(C0, n)] = -dw[m][n][r];
-  put_tile128<NTH>(B0, pf, tid);
+  put_ps_tile128<NTH>(tB0, pf, tid);
   put_bf16_tile128<NTH>(B2, pv, tid);
   put_tile64<NTH>(sT, pt, tid);
   if (tid < CH) {
@@ -1504,12 +1531,12 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   // 6. dM = dU V^T + dW Kg^T;  dV = M^T dU;  dKg = M^T dW  (M = T diag(b))
   f32x4 dm[2][1];
   zero_block(dm);
-  mfma_block<false, true, 2, 1>(dm, B1, RS, B2, RS, R0, Q0, DV, lane);
-  mfma_block<false, true, 2, 1>(dm, B3, RS, B0, RS, R0, Q0, DK, lane);
+  mfma_block_mix<false, true, 2, 1>(dm, tB1, fB2, R0, Q0, DV, lane);
+  mfma_block_mix<false, true, 2, 1>(dm, fB3, tB0, R0, Q0, DK, lane);
   {
     f32x4 a[2][2];
     zero_block(a);
-    mfma_block<true, false, 2, 2>(a, sT, QS, B1, RS, R0, C0, CH, lane);
+    mfma_block_mix<true, false, 2, 2>(a, fT, tB1, R0, C0, CH, lane);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -1535,7 +1562,8 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   }
   __syncthreads();
   // 7. db_j = sum_i dM[i][j] T[i][j];  dT = dM diag(b);  dAkk = -(T^T dT T^T) strictly lower
-  float* sDM = B0;  // [64][QS]
+  float* sDM = reinterpret_cast<float*>(B0h);  // [64][QS] (B0's hi tile is dead: same 17,408 bytes)
+  static_assert(CH * QS * sizeof(float) <= CH * PS_ROW_LD * sizeof(__bf16), "sDM fits B0's hi tile");
   float* sDT = B2;  // [64][QS]
   float* sX = B3;   // [64][QS]
 #pragma unroll
