@@ -1394,18 +1394,19 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
                      const uint16_t* __restrict__ beta, const int64_t* __restrict__ cu,
                      const int* __restrict__ chunk_off, int T, int N, int Hv, int mc, int flags,
                      float* __restrict__ dv, float* __restrict__ ws) {
-  // B0 (dO, then dS', then Kg) and B1 (dU) are read by the most waves and
-  // products: they are kept pre-split; B2, B3 and T stay fp32 (all five
-  // pre-split would not fit a CU's LDS)
+  // B0 (dO, then dS', then Kg), B1 (dU) and B3 (S, then dW) are read by the
+  // most waves and products: they are kept pre-split; B2 and T stay fp32
+  // (all five pre-split would not fit a CU's LDS)
   __shared__ __attribute__((aligned(16))) __bf16 B0h[CH * PS_ROW_LD], B0l[CH * PS_ROW_LD];
   __shared__ __attribute__((aligned(16))) __bf16 B1h[CH * PS_ROW_LD], B1l[CH * PS_ROW_LD];
   __shared__ __attribute__((aligned(16))) float B2[CH * RS];
-  __shared__ __attribute__((aligned(16))) float B3[CH * RS];
+  __shared__ __attribute__((aligned(16))) __bf16 B3h[CH * PS_ROW_LD], B3l[CH * PS_ROW_LD];
   __shared__ __attribute__((aligned(16))) float sT[CH * QS];
   __shared__ float sB[CH];
   const PsTile tB0{B0h, B0l, PS_ROW_LD, 8 * PS_ROW_LD}, tB1{B1h, B1l, PS_ROW_LD, 8 * PS_ROW_LD};
   const PsTile tB0v{B0h + 64, B0l + 64, PS_ROW_LD, 8 * PS_ROW_LD}, tB1v{B1h + 64, B1l + 64, PS_ROW_LD, 8 * PS_ROW_LD};
-  const F32Tile fB2{B2, RS}, fB2v{B2 + 64, RS}, fB3{B3, RS}, fT{sT, QS};
+  const PsTile tB3{B3h, B3l, PS_ROW_LD, 8 * PS_ROW_LD};
+  const F32Tile fB2{B2, RS}, fB2v{B2 + 64, RS}, fT{sT, QS};
   const int x = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const ChunkLoc L = chunk_loc(x, cu, chunk_off, T, N);
   if (L.len == 0) return;
@@ -1422,7 +1423,7 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   load_ps_bf16_tile128<NTH>(tB0, d_out + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
   load_ps_tile128<NTH>(tB1, sb + SB_DU, DV, tid);
   load_tile128<NTH>(B2, sb + SB_U, DV, tid);
-  load_tile128<NTH>(B3, sb + SB_H, DK, tid);
+  load_ps_tile128<NTH>(tB3, sb + SB_H, DK, tid);
   // Each later single-tile reload is fetched into registers one phase early
   // and put into LDS once its space is free, so its latency hides behind the
   // products in between: pf holds the second half of S now, then the two
@@ -1435,14 +1436,19 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   f32x4 dqg[2][2], dw[2][2];
   zero_block(dqg);
   zero_block(dw);
-  mfma_block_mix<false, false, 2, 2>(dqg, tB0, fB3, R0, C0, 64, lane);
-  mfma_block_mix<false, false, 2, 2>(dw, tB1, fB3, R0, C0, 64, lane);
+  mfma_block_mix<false, false, 2, 2>(dqg, tB0, tB3, R0, C0, 64, lane);
+  mfma_block_mix<false, false, 2, 2>(dw, tB1, tB3, R0, C0, 64, lane);
   __syncthreads();
-  put_tile128<NTH>(B3, pf, tid);
+  // the second half of S stays in registers too, for step 4's column sums
+  // (rows (tid >> 5) + 16 i, channels 4 (tid & 31): the put's layout)
+  stage_f4 s2[2048 / NTH];
+#pragma unroll
+  for (int i = 0; i < 2048 / NTH; ++i) s2[i] = pf[i];
+  put_ps_tile128<NTH>(tB3, pf, tid);
   fetch_tile128<NTH>(pf, sb + SB_DH + 64 * DK, DK, tid);  // dS' rows 64 .. 127, first in step 4
   __syncthreads();
-  mfma_block_mix<false, false, 2, 2>(dqg, tB0v, fB3, R0, C0, 64, lane);
-  mfma_block_mix<false, false, 2, 2>(dw, tB1v, fB3, R0, C0, 64, lane);
+  mfma_block_mix<false, false, 2, 2>(dqg, tB0v, tB3, R0, C0, 64, lane);
+  mfma_block_mix<false, false, 2, 2>(dw, tB1v, tB3, R0, C0, 64, lane);
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -1464,11 +1470,11 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   }
   __syncthreads();
   // 4. dKd = U dS', contracting over v in two halves; dgn = colsum(dS' . S).
-  //    B0 is free since step 3 and B3 still holds the second half of S, so
-  //    dS' goes to B0, second half first.  The column sums take dS' from the
-  //    registers it is put from (B0 holds it split): thread (rows rb + 16 i,
-  //    channels c4) pairs the second half with S in B3, then the first half
-  //    with S's first half, read again into registers a phase early.
+  //    B0 is free since step 3, so dS' goes to B0, second half first.  The
+  //    column sums take dS' from the registers it is put from (B0 holds it
+  //    split): thread (rows rb + 16 i, channels c4) pairs the second half
+  //    with S's second half kept in registers since step 2, then the first
+  //    half with S's first half, read again into registers a phase early.
   stage_u4 pv[1024 / NTH];
   stage_f4 pt[1024 / NTH];
   {
@@ -1477,7 +1483,7 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
     zero_block(dkd);
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc += pf[i] * *reinterpret_cast<const f32x4*>(B3 + (rb + 16 * i) * RS + c4);
+    for (int i = 0; i < 4; ++i) acc += pf[i] * s2[i];
     put_ps_tile128<NTH>(tB0, pf, tid);  // dS' rows 64 .. 127
     fetch_tile128<NTH>(pf, sb + SB_DH, DK, tid);
     stage_f4 s1[4];  // S rows rb + 16 i (first half), channels c4 .. +3
@@ -1517,7 +1523,7 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) B3[BLK_ROW(R0, m, r) * RS + BLK_COL(C0, n)] = -dw[m][n][r];
+      for (int r = 0; r < 4; ++r) ps_put1(tB3, BLK_ROW(R0, m, r), BLK_COL(C0, n), -dw[m][n][r]);
   put_ps_tile128<NTH>(tB0, pf, tid);
   put_bf16_tile128<NTH>(B2, pv, tid);
   put_tile64<NTH>(sT, pt, tid);
@@ -1532,7 +1538,7 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   f32x4 dm[2][1];
   zero_block(dm);
   mfma_block_mix<false, true, 2, 1>(dm, tB1, fB2, R0, Q0, DV, lane);
-  mfma_block_mix<false, true, 2, 1>(dm, fB3, tB0, R0, Q0, DK, lane);
+  mfma_block_mix<false, true, 2, 1>(dm, tB3, tB0, R0, Q0, DK, lane);
   {
     f32x4 a[2][2];
     zero_block(a);
@@ -1549,7 +1555,7 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
         }
       }
     zero_block(a);
-    mfma_block<true, false, 2, 2>(a, sT, QS, B3, RS, R0, C0, CH, lane);
+    mfma_block_mix<true, false, 2, 2>(a, fT, tB3, R0, C0, CH, lane);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -1565,7 +1571,7 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   float* sDM = reinterpret_cast<float*>(B0h);  // [64][QS] (B0's hi tile is dead: same 17,408 bytes)
   static_assert(CH * QS * sizeof(float) <= CH * PS_ROW_LD * sizeof(__bf16), "sDM fits B0's hi tile");
   float* sDT = B2;  // [64][QS]
-  float* sX = B3;   // [64][QS]
+  float* sX = reinterpret_cast<float*>(B3h);  // [64][QS] (B3's hi tile, dead by now)
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
