@@ -539,6 +539,7 @@ struct PsTile {
 constexpr int PS_ROW_LD = 136;                    // tiles read along rows
 constexpr int PS_COL_LD = 144, PS_COL_GS = 8 * PS_COL_LD + 64;  // 128-column tiles read down columns
 constexpr int PS_C32_LD = 48, PS_C32_GS = 8 * PS_C32_LD + 64;   // 32-column tiles read down columns
+constexpr int PS_C64_LD = 80, PS_C64_GS = 8 * PS_C64_LD + 64;   // 64-column tiles read down columns
 // 32-column tiles read down columns, unpadded: the four rows of a lane group
 // lie 16 banks apart and the next group of rows 8 banks further (64 banks)
 constexpr int PS_N32_LD = 32, PS_N32_GS = 8 * PS_N32_LD + 16;
@@ -589,6 +590,16 @@ __device__ __forceinline__ void load_ps_bf16_tile128(const PsTile& t, const uint
     const stage_u4 u = __builtin_bit_cast(stage_u4, __builtin_amdgcn_raw_buffer_load_b128(rg, (uint32_t)(r * gs + c) * 2, 0, 0));
     *reinterpret_cast<stage_u4*>(t.hi + t.row(r) + c) = u;
     *reinterpret_cast<stage_u4*>(t.lo + t.row(r) + c) = stage_u4{0u, 0u, 0u, 0u};
+  }
+}
+
+// a fetched 64 x 64 fp32 tile (fetch_tile64's thread layout) into a split tile
+template <int NTH>
+__device__ __forceinline__ void put_ps_tile64(const PsTile& t, const stage_f4 (&r4)[1024 / NTH], int tid) {
+#pragma unroll
+  for (int i = 0; i < 1024 / NTH; ++i) {
+    const int e = tid + NTH * i;
+    ps_put4(t, e >> 4, 4 * (e & 15), r4[i]);
   }
 }
 
@@ -1305,18 +1316,20 @@ __global__ void __launch_bounds__(STATE_THREADS)
 kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restrict__ dhT, float* __restrict__ dh0,
                       const int64_t* __restrict__ cu, const int* __restrict__ chunk_off, int T, int N, int Hv, int mc,
                       float* __restrict__ ws, float* __restrict__ seg, int nseg, int seg_len) {
-  __shared__ __attribute__((aligned(16))) float sAq[CH * QS];
-  __shared__ __attribute__((aligned(16))) float sKd[CH * RS];
   __shared__ __attribute__((aligned(16))) float sQg[CH * RS];
   __shared__ __attribute__((aligned(16))) float sW[CH * RS];
-  // pre-split: dO and dU (every wave reads all of both) and the dS' slice
-  // (four waves read each part); the others are read by one or two waves
+  // pre-split: dO and dU (every wave reads all of both), the dS' slice (four
+  // waves read each part), Kd and Aqk (two); Qg and W (one wave each) stay
+  // fp32, as the CU's LDS holds no more
   __shared__ __attribute__((aligned(16))) __bf16 sdOh[CH / 8 * PS_N32_GS], sdOl[CH / 8 * PS_N32_GS];
   __shared__ __attribute__((aligned(16))) __bf16 sdUh[CH / 8 * PS_N32_GS], sdUl[CH / 8 * PS_N32_GS];
   __shared__ __attribute__((aligned(16))) __bf16 sdhh[BV * PS_ROW_LD], sdhl[BV * PS_ROW_LD];
+  __shared__ __attribute__((aligned(16))) __bf16 sKdh[CH * PS_ROW_LD], sKdl[CH * PS_ROW_LD];
+  __shared__ __attribute__((aligned(16))) __bf16 sAqh[CH / 8 * PS_C64_GS], sAql[CH / 8 * PS_C64_GS];
   const PsTile tdO{sdOh, sdOl, PS_N32_LD, PS_N32_GS}, tdU{sdUh, sdUl, PS_N32_LD, PS_N32_GS};
-  const PsTile tdh{sdhh, sdhl, PS_ROW_LD, 8 * PS_ROW_LD};
-  const F32Tile tAq{sAq, QS}, tKd{sKd, RS}, tQg{sQg, RS}, tW{sW, RS};
+  const PsTile tdh{sdhh, sdhl, PS_ROW_LD, 8 * PS_ROW_LD}, tKd{sKdh, sKdl, PS_ROW_LD, 8 * PS_ROW_LD};
+  const PsTile tAq{sAqh, sAql, PS_C64_LD, PS_C64_GS};
+  const F32Tile tQg{sQg, RS}, tW{sW, RS};
   StateJob j;
   if (!state_job<KIND>(blockIdx.x, cu, chunk_off, T, N, Hv, nseg, seg_len, true, j)) return;
   const int chains = N * Hv, h = j.h, v0 = j.v0, tid = threadIdx.x;
@@ -1342,11 +1355,11 @@ kda_bwd_bstate_kernel(const uint16_t* __restrict__ d_out, const float* __restric
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int r = 0; r < 4; ++r) ps_put1(tdh, 16 * m + 4 * lg + r, 16 * w + li, D[m][0][r]);
-    put_tile128(sKd, b.kd, tid);
+    put_ps_tile128<STATE_THREADS>(tKd, b.kd, tid);
     put_tile128(sW, b.w, tid);
     if constexpr (KIND != ST_TRANS) {
       put_tile128(sQg, b.qg, tid);
-      put_tile64(sAq, b.aq, tid);
+      put_ps_tile64<STATE_THREADS>(tAq, b.aq, tid);
       const int t = tid >> 3, jj = 4 * (tid & 7);
       ps_put4(tdO, t, jj,
               stage_f4{__uint_as_float(b.dO[0] << 16), __uint_as_float(b.dO[0] & 0xffff0000u),
