@@ -1436,7 +1436,11 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   load_ps_bf16_tile128<NTH>(tB0, d_out + ((size_t)L.row0 * Hv + h) * DV, (size_t)Hv * DV, L.len, tid);
   load_ps_tile128<NTH>(tB1, sb + SB_DU, DV, tid);
   load_tile128<NTH>(B2, sb + SB_U, DV, tid);
-  load_ps_tile128<NTH>(tB3, sb + SB_H, DK, tid);
+  // the first half of S also stays in registers, for step 4's column sums
+  // (rows (tid >> 5) + 16 i, channels 4 (tid & 31): the put's layout)
+  stage_f4 s1[2048 / NTH];
+  fetch_tile128<NTH>(s1, sb + SB_H, DK, tid);
+  put_ps_tile128<NTH>(tB3, s1, tid);
   // Each later single-tile reload is fetched into registers one phase early
   // and put into LDS once its space is free, so its latency hides behind the
   // products in between: pf holds the second half of S now, then the two
@@ -1485,9 +1489,8 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
   // 4. dKd = U dS', contracting over v in two halves; dgn = colsum(dS' . S).
   //    B0 is free since step 3, so dS' goes to B0, second half first.  The
   //    column sums take dS' from the registers it is put from (B0 holds it
-  //    split): thread (rows rb + 16 i, channels c4) pairs the second half
-  //    with S's second half kept in registers since step 2, then the first
-  //    half with S's first half, read again into registers a phase early.
+  //    split): thread (rows rb + 16 i, channels c4) pairs each half with
+  //    the half of S it kept in registers when S went to LDS.
   stage_u4 pv[1024 / NTH];
   stage_f4 pt[1024 / NTH];
   {
@@ -1499,9 +1502,6 @@ kda_bwd_dense_kernel(const uint16_t* __restrict__ v, const uint16_t* __restrict_
     for (int i = 0; i < 4; ++i) acc += pf[i] * s2[i];
     put_ps_tile128<NTH>(tB0, pf, tid);  // dS' rows 64 .. 127
     fetch_tile128<NTH>(pf, sb + SB_DH, DK, tid);
-    stage_f4 s1[4];  // S rows rb + 16 i (first half), channels c4 .. +3
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s1[i] = *reinterpret_cast<const stage_f4*>(sb + SB_H + (rb + 16 * i) * DK + c4);
     __syncthreads();
     mfma_block_mix<false, false, 2, 2>(dkd, fB2v, tB0, R0, C0, 64, lane);
     __syncthreads();
