@@ -189,8 +189,8 @@ def main():
                     help="instead of the forward, run N plain 1 GiB device copies (traffic counter scale)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); "
-              "multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        print(f"bench.py: the path runs on exactly one GPU (asked for {args.gpus}); "
+              "sharding across GPUs is not built", file=sys.stderr)
         sys.exit(2)
 
     if not args.no_cpu_baseline and not args.copy_calibration:
@@ -305,7 +305,7 @@ def main():
     rec = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded numpy PCG64, see DESIGN.md)",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded numpy PCG64 draws of the workload's shapes and distributions)",
         "config": {"workload": inp.name, "B": inp.B, "T": inp.T, "H_qk": inp.Hqk, "H_v": inp.Hv, "K": inp.K,
                    "V": inp.V, "gate": ["softplus", "safe_sigmoid", "pregated"][inp.gate_mode],
                    "lower_bound": inp.lower_bound, "chunk": 64, "sub_chunk": 16,
@@ -414,7 +414,7 @@ def run_recurrent(args, dev):
         "metric": "fused_recurrent_kda tokens/s (fp32 state in and out), 1 MI355X",
         "value": tok / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded numpy PCG64, see DESIGN.md)",
+        "data": "synthetic (seeded numpy PCG64 draws of the workload's shapes and distributions)",
         "config": {"workload": inp.name, "B": inp.B, "T": inp.T, "H_qk": inp.Hqk, "H_v": inp.Hv, "K": inp.K,
                    "V": inp.V, "gate": ["softplus", "safe_sigmoid", "pregated"][inp.gate_mode],
                    "lower_bound": inp.lower_bound, "initial_state": "fp32", "final_state": "fp32"},
@@ -499,7 +499,7 @@ def run_backward(args, dev):
         "metric": "chunk_kda bwd tokens/s (all input gradients), 1 MI355X",
         "value": tok / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic (seeded numpy PCG64, see DESIGN.md)",
+        "data": "synthetic (seeded numpy PCG64 draws of the workload's shapes and distributions)",
         "config": {"workload": inp.name, "B": inp.B, "T": inp.T, "H_qk": inp.Hqk, "H_v": inp.Hv, "K": inp.K,
                    "V": inp.V, "gate": ["softplus", "safe_sigmoid", "pregated"][inp.gate_mode],
                    "state_segments": nseg},
