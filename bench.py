@@ -37,9 +37,9 @@ FLOP_PER_TOKEN_HEAD = 5 * 2 * 64 * 128 + 3 * 2 * 128 * 128
 BLOCK_BYTES = 76800  # per (v-head, chunk) intermediates written by the intra kernel
 
 
-def kernel_source_hash():
+def kernel_source_hash(name="kda_fwd.hip"):
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "gated_delta_rule_act_amd", "csrc", "kda_fwd.hip"), "rb") as f:
+    with open(os.path.join(ROOT, "gated_delta_rule_act_amd", "csrc", name), "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -54,6 +54,21 @@ def profile_figure(name, kernel, workload_name, key):
     m_src = re.search(r"source_sha:\s*([0-9a-f]+)", txt)
     m_b = re.search(key + r":\s*([0-9.eE+-]+)", txt)
     if not m_src or not m_b or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def profiled_bwd_traffic(workload_name):
+    """Counted HBM bytes of one backward call (every kernel's FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy's readings) from the committed backward
+    counter summary, if taken on the current backward source; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_backward_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"bwd_source_sha:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_call:\s*([0-9.eE+-]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != kernel_source_hash("kda_bwd.hip"):
         return None
     return float(m_b.group(1))
 
@@ -505,13 +520,15 @@ def run_backward(args, dev):
                    "state_segments": nseg},
         "roofline": {"bound": "alu", "kernel": "kda_bwd (all launches)",
                      "achieved": flops / (ms * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, "traffic": None,
+                     "frac": flops / (ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                     "traffic": profiled_bwd_traffic(inp.name),
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": ms},
         "sustained": None if not sus_tail else {
             "steps": ns, "ms_per_step_median": statistics.median(sus_tail), "min": min(sus_tail),
             "max": max(sus_tail), "tokens_per_s": tok / (statistics.median(sus_tail) * 1e-3),
             "note": "steps run on right after the timed ones; figures over the second half of them"},
         "kernel_source_sha": kernel_source_hash(),
+        "bwd_kernel_source_sha": kernel_source_hash("kda_bwd.hip"),
     }
     if not args.no_cpu_baseline:
         threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
